@@ -1,0 +1,270 @@
+/*
+ * sv.h -- batched speculative verification on AMD Instinct MI355X (gfx950).
+ *
+ * B sequences each carry gamma_i drafted tokens.  One target-model pass
+ * verifies all sum(gamma_i + 1) stacked tokens with a single read of the
+ * weights, rejection sampling keeps each sequence's accepted prefix plus one
+ * token of the target's own, and only the KV lengths are committed: no
+ * sequence is padded to the longest run.
+ *
+ * Source passages (pages of the method's write-ups):
+ *  - "Speculative Decoding and Batching Compete for the Same Compute Slack on
+ *    RDNA4": FAQ on the ragged tensor problem and section "The batch also goes
+ *    ragged" (per-sequence positions, masks and KV lengths; padding or
+ *    realignment are the costs to avoid); sections "The budget is fixed, and
+ *    the batch is inside it" and "What the budget says to build" (draft
+ *    length as a function of the live batch).
+ *  - "Speculative Decoding at High Batch Size: Where the 3x Speedup Turns
+ *    Into a Tax": sections "What does one speculative iteration actually
+ *    cost?" and "How does the roofline model work?" (expected tokens, step
+ *    model, crossover batch); rejection sampling keeps the output distribution
+ *    of plain decoding (section "Why do the headline speedups all come from
+ *    batch 1?").
+ *  - the speculative-decoding primer (splicedso.github.io/learn), section
+ *    "The idea": one pass checks every draft, keeps the drafts up to the first
+ *    rejection and adds one token of its own.
+ *
+ * Conventions for every call:
+ *  - Pointers are device pointers owned by the caller unless marked (host).
+ *    The library keeps no pointer after a call returns and never allocates or
+ *    frees device memory inside these calls; scratch memory comes from a
+ *    caller workspace sized by the matching *_workspace_bytes query.
+ *  - Work is enqueued on the caller's HIP stream (`stream` is a hipStream_t;
+ *    NULL is the null stream).  No call synchronises the stream or the device;
+ *    outputs are valid once the stream reaches that point.
+ *  - The return value is an sv_status.  Arguments are validated on the host
+ *    before anything is enqueued; a failing call enqueues nothing, except
+ *    SV_ERR_HIP, which reports a failed launch (hipGetLastError is consumed).
+ *  - Errors that depend on device data (a token id outside the vocabulary, a
+ *    KV length that would overflow the cache) set bits in the optional device
+ *    word *err_flag (SV_DEV_ERR_*) and never write outside caller buffers.
+ *  - Workspaces: zero-fill a workspace once after allocating it.  Each call
+ *    leaves its synchronisation counters zeroed again, so a workspace can be
+ *    reused by later calls on the same stream; calls that overlap in time
+ *    must use different workspaces.
+ *  - Thread safety: calls may come from several host threads; the only
+ *    global state is the optional kernel-timing trace (sv_trace_*).
+ */
+#ifndef SV_H
+#define SV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t sv_status;
+
+#define SV_OK 0
+#define SV_ERR_INVALID_ARG (-1) /* null pointer, negative size, inconsistent counts */
+#define SV_ERR_UNSUPPORTED (-2) /* a shape or dtype this build does not handle */
+#define SV_ERR_WORKSPACE (-3)   /* workspace missing or smaller than required */
+#define SV_ERR_HIP (-4)         /* a kernel launch failed */
+
+/* Device-side error bits, OR-ed into *err_flag. */
+#define SV_DEV_ERR_BAD_TOKEN 1   /* token id outside [0, vocab) */
+#define SV_DEV_ERR_KV_OVERFLOW 2 /* kv_len[i] + gamma_i + 1 > kv_cap */
+#define SV_DEV_ERR_CTX_BOUND 4   /* kv_len[i] > max_ctx (work beyond the bound skipped) */
+
+/* Layer kinds (sv_layer.kind). */
+#define SV_LAYER_EMBED 0   /* x[t] = E[token[t]] */
+#define SV_LAYER_DECODER 1 /* one pre-norm decoder layer */
+#define SV_LAYER_HEAD 2    /* final RMSNorm, LM head, softmax */
+
+/* Weight storage (sv_layer.wtype). */
+#define SV_W_F32 0      /* fp32 [N][K] */
+#define SV_W_BF16 1     /* bf16 [N][K] */
+#define SV_W_INT4_G32 2 /* int4, groups of 32 along K: packed uint32 [N][K/8],
+                           nibble i of word m = code + 8 for k = 8m + i,
+                           codes in [-7, 7]; bf16 scales [N][K/32];
+                           weight = code * scale */
+
+/* sv_verify_layer flags. */
+#define SV_HEAD_LOGITS 1 /* HEAD: write fp32 logits instead of probabilities */
+
+/* One weight matrix in [N][K] = [output features][reduction] layout.
+ * scale is used only for SV_W_INT4_G32. */
+typedef struct sv_matrix {
+  const void *w;
+  const void *scale;
+} sv_matrix;
+
+/* Layer description (host struct).
+ *
+ * DECODER computes, for the stacked verify tokens x[T][d] (bf16):
+ *   h = RMSNorm(x) (eps, unit gain);  q, k, v = h Wq^T, h Wk^T, h Wv^T;
+ *   RoPE on q and k at each token's position, pairs (i, i + head_dim/2)
+ *   rotated by pos * rope_theta^(-2i/head_dim);
+ *   k and v appended to the sequence's cache at that position (bf16);
+ *   o = softmax(q K^T / sqrt(head_dim)) V, query j of sequence i seeing keys
+ *   0 .. kv_len[i] + j, query head h reading KV head h / (n_q_heads/n_kv_heads);
+ *   x1 = x + o Wo^T;  y = x1 + (silu(RMSNorm(x1) Wg^T) * (RMSNorm(x1) Wu^T)) Wd^T.
+ * HEAD computes logits = RMSNorm(y) Wlm^T and p = softmax(logits) per row.
+ * EMBED copies E[token] (fp32 or bf16 table [vocab][d]) to bf16 rows.
+ *
+ * Shapes: Wq [n_q*hd][d], Wk/Wv [n_kv*hd][d], Wo [d][n_q*hd], Wg/Wu [ffn][d],
+ * Wd [d][ffn], lm_head [vocab][d], embed [vocab][d].
+ * Supported: d, ffn, n_q*hd multiples of 64; head_dim 64 or 128;
+ * n_q_heads a multiple of n_kv_heads. */
+typedef struct sv_layer {
+  int32_t kind;
+  int32_t wtype;
+  int32_t d;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t ffn;
+  int32_t vocab;
+  float eps;          /* RMSNorm epsilon (1e-6 in the reference model) */
+  float rope_theta;   /* RoPE base (1e4 in the reference model) */
+  sv_matrix wq, wk, wv, wo, w_gate, w_up, w_down; /* DECODER */
+  sv_matrix embed;    /* EMBED: table, wtype SV_W_F32 or SV_W_BF16 */
+  sv_matrix lm_head;  /* HEAD */
+} sv_layer;
+
+/* Batch description (host struct; the arrays it points to are as marked).
+ *
+ * Token map: sequence i owns stacked rows q_start[i] .. q_start[i] + gamma_i
+ * where q_start is the exclusive prefix sum of (gamma_i + 1); row j of
+ * sequence i is the token at position kv_len[i] + j (j = 0 is the last
+ * committed token, j >= 1 the drafts).  T must equal sum(gamma_i + 1).
+ *
+ * KV caches: k_cache[i] points to sequence i's keys, bf16 [n_kv][kv_cap][hd]
+ * (position-major); v_cache[i] to its values, bf16 [n_kv][hd][kv_cap]
+ * (position-minor, so one head's values for consecutive positions are
+ * contiguous).  Entries at positions < kv_len[i] are read; the pass writes
+ * positions kv_len[i] .. kv_len[i] + gamma_i.  kv_cap is a multiple of 16. */
+typedef struct sv_batch {
+  int32_t B;                 /* sequences, >= 0 */
+  int32_t T;                 /* stacked tokens = sum(gamma_i + 1) */
+  int32_t max_ctx;           /* upper bound on every kv_len[i] (sizes the grid) */
+  int32_t kv_cap;            /* cache capacity per sequence, multiple of 16 */
+  const int32_t *gamma_host; /* (host) [B] draft counts, >= 0 */
+  const int32_t *gamma;      /* [B] the same counts on the device */
+  const int32_t *kv_len;     /* [B] cached tokens before the pass */
+  void *const *k_cache;      /* [B] device pointers */
+  void *const *v_cache;      /* [B] device pointers */
+  int32_t *err_flag;         /* [1] nullable */
+} sv_batch;
+
+/* Workspace needed by sv_verify_layer for this layer, batch and flags. */
+sv_status sv_verify_layer_workspace_bytes(const sv_layer *layer, const sv_batch *batch,
+                                          int32_t flags, size_t *bytes);
+
+/* One verify pass through one layer.
+ *   DECODER: x_in bf16 [T][d] -> y_out bf16 [T][d]; appends K/V rows.
+ *   HEAD:    x_in bf16 [T][d] -> y_out fp32 [T][vocab] probabilities
+ *            (or logits with SV_HEAD_LOGITS).
+ *   EMBED:   x_in int32 token ids [T] -> y_out bf16 [T][d].
+ * x_in and y_out must not overlap.  Only B, T, gamma_host and err_flag of the
+ * batch are used by EMBED and HEAD. */
+sv_status sv_verify_layer(const sv_layer *layer, const sv_batch *batch, const void *x_in,
+                          void *y_out, int32_t flags, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
+/* Acceptance modes. */
+#define SV_ACCEPT_STOCHASTIC 0
+#define SV_ACCEPT_GREEDY 1
+
+/* Workspace needed by sv_accept_commit. */
+sv_status sv_accept_commit_workspace_bytes(int32_t B, int32_t V, int32_t mode,
+                                           const int32_t *gamma_host, size_t *bytes);
+
+/* Acceptance, resampling and commit for every sequence (rejection sampling
+ * in the sense of Leviathan, Kalman and Matias).
+ *
+ * Rows: p row q_start[i] + j (j = 0..gamma_i) is the target distribution of
+ * the (j+1)-th new token of sequence i; q row q_start[i] - i + j
+ * (j = 0..gamma_i - 1) is the draft distribution of draft token j+1, whose id
+ * is draft[q_start[i] - i + j].  p fp32 [T][V], q fp32 [sum gamma][V], with
+ * entries in [0, 1].  u_acc fp32 [sum gamma], u_samp fp32 [B] in [0, 1).
+ *
+ * Stochastic mode, per sequence:
+ *   a = number of leading drafts with fl32(u_acc * q(d)) < p(d);
+ *   r = max(0, fl32(p_{a+1} - q_{a+1})) if a < gamma_i, else p_{gamma_i+1};
+ *   R(x) = trunc(fl32(r(x) * 2^32)) as 64-bit integers, S = sum R (exact);
+ *   if S == 0 after a rejection, R is taken from p_{a+1}; if S is still 0
+ *   the token is argmax p_{a+1} (lowest index);
+ *   t = floor(fl64(u_samp * S)) (at most S - 1); next_token = least x whose
+ *   running sum of R exceeds t.
+ * Greedy mode: a = leading drafts equal to argmax p_j, next_token =
+ * argmax p_{a+1} (lowest index on ties); q, u_acc, u_samp may be NULL.
+ * Commit: accepted[i] = a, kv_len[i] += a + 1 (in place).  A sequence whose
+ * drafts contain an id outside [0, V) is left uncommitted: accepted and
+ * next_token are -1, kv_len unchanged, SV_DEV_ERR_BAD_TOKEN set. */
+sv_status sv_accept_commit(int32_t B, int32_t V, int32_t mode, const int32_t *gamma_host,
+                           const int32_t *gamma, const int32_t *draft, const float *p,
+                           const float *q, const float *u_acc, const float *u_samp,
+                           int32_t *kv_len, int32_t *accepted, int32_t *next_token,
+                           int32_t *err_flag, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/* Draft-length planning (host only). */
+#define SV_PLAN_BUDGET 0  /* keep sum(gamma_i + 1) within the compute-slack budget */
+#define SV_PLAN_SPEEDUP 1 /* maximise the step-model speedup over plain decoding */
+
+typedef struct sv_plan_params {
+  int32_t mode;
+  int32_t gamma_max;       /* cap on any gamma_i */
+  int32_t budget_tokens;   /* BUDGET: slack in tokens; 0 = floor(t_floor_ms / c_ms) */
+  int32_t fill_remainder;  /* BUDGET: give the leftover tokens to the first sequences */
+  double t_floor_ms;       /* decode step floor (BUDGET when budget_tokens == 0) */
+  double t_w_ms;           /* weight-read time per step */
+  double k_ms;             /* KV-read time per sequence */
+  double c_ms;             /* compute time per token */
+  double draft_frac;       /* drafter size relative to the target (e.g. 0.04) */
+  int32_t n_alpha;         /* 1: independent acceptance alpha[0]; >1: conditional
+                              acceptance per position (last value repeats) */
+  const double *alpha;     /* (host) [n_alpha] */
+} sv_plan_params;
+
+/* gamma_out (host) [B_live] receives the draft lengths.
+ * BUDGET: n = budget tokens; if B_live >= n every gamma is 0, otherwise the
+ *   n - B_live free tokens are split evenly (floor), the first
+ *   (n - B_live) mod B_live sequences getting one more if fill_remainder,
+ *   each capped at gamma_max.
+ * SPEEDUP: one gamma in 0..gamma_max for all sequences, maximising
+ *   E(gamma) t(B,1) / (t(B, gamma+1) + t_d(B, gamma)) with
+ *   t(B, n) = max(t_w + B k, B n c), t_d(B, g) = max(f t_w + B k, f B g c);
+ *   ties go to the smaller gamma.
+ * *bstar_out (nullable) receives the crossover batch t_w / ((g+1) c - k) for
+ * the largest planned g (infinity when the denominator is <= 0 or t_w, c
+ * are not given). */
+sv_status sv_plan_gamma(const sv_plan_params *params, int32_t B_live, int32_t *gamma_out,
+                        double *bstar_out);
+
+/* Kernel-timing trace (profiling aid).  While a trace is active, every launch
+ * of the named kernel class is bracketed by a pair of HIP events on the
+ * launch stream, up to `capacity` launches.  sv_trace_end waits for the last
+ * recorded event, writes the elapsed milliseconds of each bracketed launch to
+ * ms_out (host, capacity entries), stores their number in *count and releases
+ * the events. */
+#define SV_K_GEMM_QKV 0
+#define SV_K_ATTENTION 1
+#define SV_K_ATTN_MERGE 2
+#define SV_K_GEMM_O 3
+#define SV_K_GEMM_GATE_UP 4
+#define SV_K_GEMM_DOWN 5
+#define SV_K_GEMM_LM_HEAD 6
+#define SV_K_SOFTMAX 7
+#define SV_K_ACCEPT_SCAN 8
+#define SV_K_ACCEPT_SELECT 9
+#define SV_K_EMBED 10
+#define SV_K_COUNT 11
+
+sv_status sv_trace_begin(int32_t kernel_class, int32_t capacity);
+sv_status sv_trace_end(float *ms_out, int32_t capacity, int32_t *count);
+
+/* Message for a status code (static string). */
+const char *sv_status_string(sv_status status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t sv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SV_H */

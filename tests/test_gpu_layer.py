@@ -1,0 +1,175 @@
+"""GPU parity of the verify pass against the fp64 oracle on sizes that span
+several GEMM tiles, K splits and attention chunks with ragged tails, plus the
+tiny two-layer model end to end (embedding -> 2 layers -> head -> accept)."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import (TOL, GpuDecoder, GpuHead, OF, OV, accept_inputs, dev_bf16_to_f64,
+                         embed_weights, hidden_states, oracle_accept, rel_rows, run_accept, say,
+                         sv, tg)
+from workloads import SHAPES, Shape, custom_workload, f32_to_bf16_bits, workload
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # (name, shape, wtype, gamma, ctx)
+    ("hd128-gqa4-bf16", Shape(512, 8, 2, 128, 1024, 3000), "bf16", [2, 0, 5, 1], [300, 0, 777, 64]),
+    ("hd64-gqa1-f32", SHAPES["tiny"], "f32", [4, 0, 2], [128, 5, 260]),
+    ("hd128-gqa4-int4", Shape(512, 8, 2, 128, 1024, 3000), "int4", [3, 3, 0], [1000, 17, 513]),
+    ("hd128-gqa5-bf16-rows48", Shape(640, 10, 2, 128, 1280, 2000), "bf16", [7, 1], [400, 2]),
+    ("hd64-gqa2-bf16-tok>64", Shape(256, 4, 2, 64, 512, 1000), "bf16",
+     [6, 0, 3, 9, 2, 4, 1, 8, 5, 7, 3, 0, 6, 2], list(range(10, 150, 10))),
+]
+
+
+@pytest.mark.parametrize("name,shape,wtype,gamma,ctx", CASES, ids=[c[0] for c in CASES])
+def test_decoder_parity(name, shape, wtype, gamma, ctx):
+    wl = custom_workload(shape, wtype, gamma, ctx, seed=31)
+    say(f"decoder {name}: T={wl.T} B={wl.B}")
+    dec = GpuDecoder(wl)
+    xh = hidden_states(wl.T, shape.d, wl.seed)
+    y = dec.run(tg.to_dev(xh))
+    torch.cuda.synchronize()
+    ref = dec.oracle(xh)
+    err = rel_rows(dev_bf16_to_f64(y), ref.y)
+    say(f"  y rel err {err:.2e}")
+    assert err < TOL[wtype]
+    assert dec.batch.err.item() == 0
+    # appended cache rows (rotated keys, values) at positions ctx_i .. ctx_i + gamma_i
+    for i in range(wl.B):
+        c, n = int(wl.ctx[i]), int(wl.gamma[i]) + 1
+        kg = OF.bf16_to_f64(dec.batch.k_logical(i)[:, c:c + n])
+        vg = OF.bf16_to_f64(dec.batch.v_logical(i)[:, c:c + n])
+        assert rel_rows(kg.reshape(-1, shape.hd), ref.k_new[i].reshape(-1, shape.hd)) < TOL[wtype]
+        assert rel_rows(vg.reshape(-1, shape.hd), ref.v_new[i].reshape(-1, shape.hd)) < TOL[wtype]
+        # the cached prefix is untouched
+        np.testing.assert_array_equal(dec.batch.k_logical(i)[:, :c], dec.kc[i][:, :c])
+        np.testing.assert_array_equal(dec.batch.v_logical(i)[:, :c], dec.vc[i][:, :c])
+
+
+def test_decoder_deterministic_and_repeatable():
+    shape = Shape(512, 8, 2, 128, 1024, 3000)
+    wl = custom_workload(shape, "bf16", [3, 1, 0], [500, 20, 0], seed=4)
+    dec = GpuDecoder(wl)
+    x = tg.to_dev(hidden_states(wl.T, shape.d, wl.seed))
+    y1 = dec.run(x).clone()
+    y2 = dec.run(x).clone()   # same lengths: rewrites the same cache rows
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+def test_verify_equals_sequential_decodes_gpu():
+    """gamma+1 tokens in one pass == gamma+1 single-token passes that commit
+    one row each (spec property 1), and gamma = 0 is plain decoding."""
+    shape = Shape(256, 4, 2, 64, 512, 1000)
+    gam, ctx = [3, 5], [40, 300]
+    wl = custom_workload(shape, "bf16", gam, ctx, seed=8)
+    xh = hidden_states(wl.T, shape.d, wl.seed)
+    full = GpuDecoder(wl)
+    yf = dev_bf16_to_f64(full.run(tg.to_dev(xh)))
+    seqd = GpuDecoder(wl)     # fresh caches, same contents
+    rows = []
+    for j in range(max(gam) + 1):
+        live = [i for i in range(wl.B) if j <= gam[i]]
+        # one token per live sequence, at position ctx_i + j
+        b = tg.DeviceBatch([0] * len(live), [ctx[i] + j for i in live], wl.cap)
+        b.k = [seqd.batch.k[i] for i in live]
+        b.v = [seqd.batch.v[i] for i in live]
+        b.kptr = torch.tensor([t.data_ptr() for t in b.k], dtype=torch.int64, device="cuda")
+        b.vptr = torch.tensor([t.data_ptr() for t in b.v], dtype=torch.int64, device="cuda")
+        b.max_ctx = max(ctx) + max(gam)
+        bs = b.struct()
+        n = sv.sv_verify_layer_workspace_bytes(seqd.L, bs)
+        ws = tg.workspace(n)
+        xs = np.stack([xh[int(wl.q_start[i]) + j] for i in live])
+        y = torch.empty(len(live), shape.d, dtype=torch.bfloat16, device="cuda")
+        assert sv.sv_verify_layer(seqd.L, bs, tg.to_dev(xs), y, 0, ws, n, tg.stream_handle()) == 0
+        yh = dev_bf16_to_f64(y)
+        for k, i in enumerate(live):
+            rows.append((int(wl.q_start[i]) + j, yh[k]))
+    for r, v in rows:
+        assert rel_rows(v[None], yf[r][None]) < 1e-2, r
+
+
+def test_head_parity():
+    shape = Shape(512, 8, 2, 128, 1024, 5003)
+    for wtype in ("bf16", "int4"):
+        wl = custom_workload(shape, wtype, [2, 0, 4], [1, 1, 1], seed=12)
+        head = GpuHead(wl)
+        yh = hidden_states(wl.T, shape.d, 77)
+        yd = tg.to_dev(yh)
+        lg = head.run(yd, logits=True).cpu().numpy()
+        pr = head.run(yd).cpu().numpy()
+        ref = OV.head_logits(head.Wlm, yh)
+        err = rel_rows(lg, ref)
+        say(f"head {wtype}: logits rel err {err:.2e}")
+        assert err < TOL[wtype]
+        np.testing.assert_allclose(pr.sum(1), 1.0, rtol=1e-4)
+        np.testing.assert_allclose(pr, OV.softmax(lg), rtol=2e-5, atol=1e-9)
+
+
+def test_embed_and_bad_token():
+    sh = SHAPES["tiny"]
+    E = embed_weights(sh, 3)
+    table = tg.to_dev(E)
+    L = tg.embed_struct(sh, table)
+    b = tg.DeviceBatch([2, 0], [0, 0], 16)
+    toks = torch.tensor([5, 1023, 0, 77], dtype=torch.int32, device="cuda")
+    out = torch.empty(4, sh.d, dtype=torch.bfloat16, device="cuda")
+    assert sv.sv_verify_layer(L, b.struct(), toks, out, 0, None, 0, tg.stream_handle()) == 0
+    want = f32_to_bf16_bits(E[[5, 1023, 0, 77]])
+    np.testing.assert_array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), want)
+    assert b.err.item() == 0
+    toks = torch.tensor([5, 1024, 0, -1], dtype=torch.int32, device="cuda")
+    assert sv.sv_verify_layer(L, b.struct(), toks, out, 0, None, 0, tg.stream_handle()) == 0
+    torch.cuda.synchronize()
+    assert b.err.item() & sv.SV_DEV_ERR_BAD_TOKEN
+    assert (out[1].float() == 0).all() and (out[3].float() == 0).all()
+
+
+def test_tiny_model_end_to_end():
+    """Workload 1: embedding -> 2 fp32 layers -> head -> accept, against the
+    oracle; acceptance is bit-exact when both sides get the GPU's p."""
+    wl = workload(1)
+    sh = wl.shape
+    rng = np.random.default_rng(wl.seed)
+    acc_in = accept_inputs(wl, sh.vocab)           # drafts d_j ~ q_j (temperature 0.7)
+    x_last = int(rng.integers(0, sh.vocab))
+    tokens = np.concatenate([[x_last], acc_in["draft"]]).astype(np.int32)
+    E = embed_weights(sh, wl.seed)
+    table = tg.to_dev(E)
+    b = tg.DeviceBatch(wl.gamma, wl.ctx, wl.cap)
+    x = torch.empty(wl.T, sh.d, dtype=torch.bfloat16, device="cuda")
+    assert sv.sv_verify_layer(tg.embed_struct(sh, table), b.struct(),
+                              torch.tensor(tokens, device="cuda"), x, 0, None, 0,
+                              tg.stream_handle()) == 0
+    layers = [GpuDecoder(wl, tag=f"layer{k}") for k in range(2)]
+    h = x
+    for ly in layers:
+        h = ly.run(h)
+    head = GpuHead(wl)
+    lg = head.run(h, logits=True).cpu().numpy()
+    p_gpu = head.run(h).cpu().numpy()
+    # oracle chain in fp64
+    xo = OV.embed(E, tokens)
+    for ly in layers:
+        xo = ly.oracle(xo).y
+    ref = OV.head_logits(head.Wlm, xo)
+    err = rel_rows(lg, ref)
+    say(f"tiny model logits rel err {err:.2e}")
+    assert err < TOL["f32"]
+    # acceptance on the GPU's probabilities: bit-exact
+    inp = dict(acc_in, p=p_gpu)
+    ga, gy, gk, _ = run_accept(wl.gamma, sh.vocab, inp, wl.ctx)
+    ra, ry, rk, _ = oracle_accept(wl.gamma, inp, wl.ctx)
+    np.testing.assert_array_equal(ga, ra)
+    np.testing.assert_array_equal(gy, ry)
+    np.testing.assert_array_equal(gk, rk)
+    # against the oracle's own probabilities a flip is possible only where
+    # u * q(d) sits within the logits tolerance of p(d); report it
+    inp_o = dict(acc_in, p=OV.softmax(ref).astype(np.float32))
+    oa, oy, _, _ = oracle_accept(wl.gamma, inp_o, wl.ctx)
+    say(f"tiny model: accepted gpu={ga.tolist()} oracle-p={oa.tolist()} next {gy.tolist()}/{oy.tolist()}")
+    for ly in layers:
+        assert ly.batch.err.item() == 0

@@ -1,0 +1,531 @@
+// C-ABI entry points: argument validation, workspace layout, launch geometry
+// and kernel dispatch on the caller's stream.  No allocation, no sync.
+#include <atomic>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "sv_common.h"
+
+using namespace sv;
+
+// ---------------------------------------------------------------------------
+// Kernel-timing trace.
+namespace {
+struct TraceState {
+  std::mutex mu;
+  std::atomic<int> cls{-1};
+  int cap = 0;
+  int n = 0;
+  bool open = false;
+  std::vector<hipEvent_t> ev;
+};
+TraceState g_trace;
+}  // namespace
+
+void sv::trace_before(int kernel_class, hipStream_t s) {
+  if (g_trace.cls.load(std::memory_order_relaxed) != kernel_class) return;
+  std::lock_guard<std::mutex> lk(g_trace.mu);
+  if (g_trace.n < g_trace.cap && !g_trace.open) {
+    if (hipEventRecord(g_trace.ev[2 * g_trace.n], s) == hipSuccess) g_trace.open = true;
+  }
+}
+
+void sv::trace_after(int kernel_class, hipStream_t s) {
+  if (g_trace.cls.load(std::memory_order_relaxed) != kernel_class) return;
+  std::lock_guard<std::mutex> lk(g_trace.mu);
+  if (g_trace.open) {
+    (void)hipEventRecord(g_trace.ev[2 * g_trace.n + 1], s);
+    g_trace.open = false;
+    ++g_trace.n;
+  }
+}
+
+extern "C" sv_status sv_trace_begin(int32_t kernel_class, int32_t capacity) {
+  if (kernel_class < 0 || kernel_class >= SV_K_COUNT || capacity <= 0) return SV_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lk(g_trace.mu);
+  if (g_trace.cls.load() >= 0) return SV_ERR_INVALID_ARG;  // one trace at a time
+  g_trace.ev.assign(2 * (size_t)capacity, nullptr);
+  for (auto &e : g_trace.ev)
+    if (hipEventCreate(&e) != hipSuccess) return SV_ERR_HIP;
+  g_trace.cap = capacity;
+  g_trace.n = 0;
+  g_trace.open = false;
+  g_trace.cls.store(kernel_class);
+  return SV_OK;
+}
+
+extern "C" sv_status sv_trace_end(float *ms_out, int32_t capacity, int32_t *count) {
+  std::lock_guard<std::mutex> lk(g_trace.mu);
+  if (g_trace.cls.load() < 0) return SV_ERR_INVALID_ARG;
+  g_trace.cls.store(-1);
+  sv_status st = SV_OK;
+  const int n = g_trace.n;
+  if (n > 0 && hipEventSynchronize(g_trace.ev[2 * n - 1]) != hipSuccess) st = SV_ERR_HIP;
+  for (int i = 0; i < n && st == SV_OK; ++i) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, g_trace.ev[2 * i], g_trace.ev[2 * i + 1]) != hipSuccess) st = SV_ERR_HIP;
+    if (ms_out && i < capacity) ms_out[i] = ms;
+  }
+  for (auto &e : g_trace.ev) (void)hipEventDestroy(e);
+  g_trace.ev.clear();
+  if (count) *count = n;
+  g_trace.n = 0;
+  g_trace.cap = 0;
+  return st;
+}
+
+extern "C" const char *sv_status_string(sv_status s) {
+  switch (s) {
+    case SV_OK: return "ok";
+    case SV_ERR_INVALID_ARG: return "invalid argument";
+    case SV_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case SV_ERR_WORKSPACE: return "workspace missing or too small";
+    case SV_ERR_HIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+extern "C" int32_t sv_version(void) { return 100; }
+
+// ---------------------------------------------------------------------------
+// Planning of one verify_layer call.
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int target_workgroups() {
+  static int v = [] {
+    const char *e = std::getenv("SV_TARGET_WG");
+    const int x = e ? std::atoi(e) : 0;
+    return x > 0 ? x : 1024;
+  }();
+  return v;
+}
+
+struct GemmCfg {
+  int nblk = 0, ntblk = 0, splits = 1, tt = 1, ksteps = 0, K = 0, N = 0;
+  bool norm = false;
+  size_t partial_floats() const {
+    return splits > 1 ? (size_t)splits * nblk * ntblk * tt * 16 * 64 : 0;
+  }
+  size_t ss_floats() const { return (splits > 1 && norm) ? (size_t)nblk * splits * ntblk * 64 : 0; }
+  size_t counters() const { return splits > 1 ? (size_t)nblk * ntblk : 0; }
+};
+
+GemmCfg gemm_cfg(int nblk, int N, int T, int K, int wtype, bool norm) {
+  GemmCfg c;
+  c.nblk = nblk;
+  c.N = N;
+  c.K = K;
+  c.norm = norm;
+  c.tt = T <= 16 ? 1 : T <= 32 ? 2 : T <= 48 ? 3 : 4;
+  c.ntblk = (T + 16 * c.tt - 1) / (16 * c.tt);
+  c.ksteps = K / kstep_of(wtype);
+  const int base = std::max(1, nblk * c.ntblk);
+  const int want = (target_workgroups() + base - 1) / base;
+  const int maxs = std::max(1, std::min(32, c.ksteps / 4));
+  c.splits = std::max(1, std::min(want, maxs));
+  return c;
+}
+
+struct LayerPlan {
+  int T = 0, B = 0, G = 1, gmax = 0;
+  GemmCfg qkv, o, gu, down, head;
+  int attn_chunk = 256, attn_items = 0, attn_rpad = 16;
+  size_t off_counters = 0, off_partial = 0, off_ss = 0, off_qbuf = 0, off_po = 0, off_pml = 0;
+  size_t off_attn = 0, off_x1 = 0, off_act = 0, off_stats = 0;
+  size_t bytes = 0;
+};
+
+bool valid_wtype(int w) { return w == SV_W_F32 || w == SV_W_BF16 || w == SV_W_INT4_G32; }
+
+sv_status check_matrix(const sv_matrix &m, int wtype) {
+  if (!m.w) return SV_ERR_INVALID_ARG;
+  if (wtype == SV_W_INT4_G32 && !m.scale) return SV_ERR_INVALID_ARG;
+  return SV_OK;
+}
+
+sv_status plan_layer(const sv_layer *L, const sv_batch *b, int32_t flags, LayerPlan &pl) {
+  if (!L || !b) return SV_ERR_INVALID_ARG;
+  if (L->kind < SV_LAYER_EMBED || L->kind > SV_LAYER_HEAD) return SV_ERR_INVALID_ARG;
+  if (flags & ~SV_HEAD_LOGITS) return SV_ERR_INVALID_ARG;
+  if (b->B < 0 || b->T < 0) return SV_ERR_INVALID_ARG;
+  if (b->B > 0 && !b->gamma_host) return SV_ERR_INVALID_ARG;
+  long long T = 0;
+  int gmax = 0;
+  for (int i = 0; i < b->B; ++i) {
+    const int g = b->gamma_host[i];
+    if (g < 0) return SV_ERR_INVALID_ARG;
+    gmax = std::max(gmax, g);
+    T += g + 1;
+  }
+  if (T != b->T) return SV_ERR_INVALID_ARG;
+  if (T > (1 << 24)) return SV_ERR_UNSUPPORTED;
+  pl.T = (int)T;
+  pl.B = b->B;
+  pl.gmax = gmax;
+  if (L->d <= 0) return SV_ERR_INVALID_ARG;
+  if (pl.T == 0) {  // empty batch: nothing to plan, nothing will be enqueued
+    pl.bytes = 0;
+    return SV_OK;
+  }
+  const int w = L->wtype;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+
+  if (L->kind == SV_LAYER_EMBED) {
+    if (L->vocab <= 0 || !L->embed.w) return SV_ERR_INVALID_ARG;
+    if (w != SV_W_F32 && w != SV_W_BF16) return SV_ERR_UNSUPPORTED;
+    pl.bytes = 0;
+    return SV_OK;
+  }
+  if (!valid_wtype(w)) return SV_ERR_UNSUPPORTED;
+  const int kmul = w == SV_W_INT4_G32 ? 128 : 64;
+  if (L->d % kmul) return SV_ERR_UNSUPPORTED;
+
+  if (L->kind == SV_LAYER_HEAD) {
+    if (L->vocab <= 0) return SV_ERR_INVALID_ARG;
+    if (check_matrix(L->lm_head, w) != SV_OK) return SV_ERR_INVALID_ARG;
+    pl.head = gemm_cfg((L->vocab + 63) / 64, L->vocab, pl.T, L->d, w, true);
+    pl.off_counters = take(std::max<size_t>(pl.head.counters(), 1) * sizeof(int));
+    pl.off_partial = take(pl.head.partial_floats() * sizeof(float));
+    pl.off_ss = take(pl.head.ss_floats() * sizeof(float));
+    pl.off_stats = take((size_t)pl.head.nblk * pl.T * 2 * sizeof(float));
+    pl.bytes = off;
+    return SV_OK;
+  }
+
+  // DECODER
+  const int d = L->d, hq = L->n_q_heads, hk = L->n_kv_heads, hd = L->head_dim, F = L->ffn;
+  if (hq <= 0 || hk <= 0 || F <= 0) return SV_ERR_INVALID_ARG;
+  if (hq % hk) return SV_ERR_UNSUPPORTED;
+  if (hd != 64 && hd != 128) return SV_ERR_UNSUPPORTED;
+  if (F % kmul || (hq * hd) % kmul) return SV_ERR_UNSUPPORTED;
+  for (const sv_matrix *m : {&L->wq, &L->wk, &L->wv, &L->wo, &L->w_gate, &L->w_up, &L->w_down})
+    if (check_matrix(*m, w) != SV_OK) return SV_ERR_INVALID_ARG;
+  pl.G = hq / hk;
+  if (pl.B > kScanMaxB) return SV_ERR_UNSUPPORTED;
+  if ((long long)pl.G * (gmax + 1) > 64) return SV_ERR_UNSUPPORTED;
+  if (b->max_ctx < 0 || b->kv_cap <= 0 || b->kv_cap % 16) return SV_ERR_INVALID_ARG;
+  if ((long long)b->max_ctx + gmax + 1 > b->kv_cap) return SV_ERR_INVALID_ARG;
+  if (pl.B > 0 && (!b->gamma || !b->kv_len || !b->k_cache || !b->v_cache)) return SV_ERR_INVALID_ARG;
+
+  const int nqkv = (hq + 2 * hk) * hd;
+  pl.qkv = gemm_cfg(nqkv / 64, nqkv, pl.T, d, w, true);
+  pl.o = gemm_cfg(d / 64, d, pl.T, hq * hd, w, false);
+  pl.gu = gemm_cfg((F + 31) / 32, 2 * F, pl.T, d, w, true);
+  pl.down = gemm_cfg(d / 64, d, pl.T, F, w, false);
+  pl.attn_rpad = 16 * ((pl.G * (gmax + 1) + 15) / 16);
+  long long items = 0;
+  for (int i = 0; i < pl.B; ++i)
+    items += ((long long)b->max_ctx + b->gamma_host[i] + 1 + pl.attn_chunk - 1) / pl.attn_chunk;
+  if (items > (1 << 30)) return SV_ERR_UNSUPPORTED;
+  pl.attn_items = (int)items;
+
+  size_t counters = 1, partial = 0, ss = 0;
+  for (const GemmCfg *g : {&pl.qkv, &pl.o, &pl.gu, &pl.down}) {
+    counters = std::max(counters, g->counters());
+    partial = std::max(partial, g->partial_floats());
+    ss = std::max(ss, g->ss_floats());
+  }
+  pl.off_counters = take(counters * sizeof(int));
+  pl.off_partial = take(partial * sizeof(float));
+  pl.off_ss = take(ss * sizeof(float));
+  pl.off_qbuf = take((size_t)pl.T * hq * hd * 2);
+  pl.off_po = take((size_t)pl.attn_items * hk * pl.attn_rpad * hd * sizeof(float));
+  pl.off_pml = take((size_t)pl.attn_items * hk * pl.attn_rpad * 2 * sizeof(float));
+  pl.off_attn = take((size_t)pl.T * hq * hd * 2);
+  pl.off_x1 = take((size_t)pl.T * d * 2);
+  pl.off_act = take((size_t)pl.T * F * 2);
+  pl.bytes = off;
+  return SV_OK;
+}
+
+GemmParams base_params(const GemmCfg &c, const void *x, int T, int wtype, unsigned char *ws,
+                       const LayerPlan &pl) {
+  GemmParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.x = static_cast<const uint16_t *>(x);
+  p.T = T;
+  p.K = c.K;
+  p.N = c.N;
+  p.splits = c.splits;
+  p.ksteps = c.ksteps;
+  p.nblk = c.nblk;
+  p.ntblk = c.ntblk;
+  p.norm = c.norm ? 1 : 0;
+  p.partial = reinterpret_cast<float *>(ws + pl.off_partial);
+  p.part_ss = reinterpret_cast<float *>(ws + pl.off_ss);
+  p.counters = reinterpret_cast<int *>(ws + pl.off_counters);
+  (void)wtype;
+  return p;
+}
+
+int wt_of(int w) { return w == SV_W_F32 ? WT_F32 : w == SV_W_BF16 ? WT_BF16 : WT_INT4; }
+
+GemmMat mat_of(const sv_matrix &m, int rows) {
+  GemmMat g;
+  g.w = m.w;
+  g.s = static_cast<const uint16_t *>(m.scale);
+  g.rows = rows;
+  return g;
+}
+
+}  // namespace
+
+extern "C" sv_status sv_verify_layer_workspace_bytes(const sv_layer *layer, const sv_batch *batch,
+                                                     int32_t flags, size_t *bytes) {
+  if (!bytes) return SV_ERR_INVALID_ARG;
+  LayerPlan pl;
+  const sv_status st = plan_layer(layer, batch, flags, pl);
+  if (st != SV_OK) return st;
+  *bytes = pl.bytes;
+  return SV_OK;
+}
+
+extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const void *x_in,
+                                     void *y_out, int32_t flags, void *workspace,
+                                     size_t workspace_bytes, void *stream) {
+  LayerPlan pl;
+  sv_status st = plan_layer(L, b, flags, pl);
+  if (st != SV_OK) return st;
+  if (pl.T == 0) return SV_OK;
+  if (!x_in || !y_out) return SV_ERR_INVALID_ARG;
+  if (pl.bytes > 0 && (!workspace || workspace_bytes < pl.bytes)) return SV_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  unsigned char *ws = static_cast<unsigned char *>(workspace);
+  const int wt = wt_of(L->wtype);
+  (void)hipGetLastError();  // start from a clean launch status
+  hipError_t e = hipSuccess;
+
+  if (L->kind == SV_LAYER_EMBED) {
+    EmbedParams p;
+    p.tokens = static_cast<const int *>(x_in);
+    p.table = L->embed.w;
+    p.table_bf16 = L->wtype == SV_W_BF16;
+    p.T = pl.T;
+    p.V = L->vocab;
+    p.d = L->d;
+    p.out = static_cast<uint16_t *>(y_out);
+    p.err = b->err_flag;
+    e = launch_embed(p, s);
+    return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+  }
+
+  if (L->kind == SV_LAYER_HEAD) {
+    GemmParams p = base_params(pl.head, x_in, pl.T, wt, ws, pl);
+    p.nmat = 1;
+    p.mat[0] = mat_of(L->lm_head, L->vocab);
+    p.rowmap = RM_LINEAR;
+    p.eps = L->eps;
+    p.epi = EPI_LOGITS;
+    p.out = y_out;
+    p.ldo = L->vocab;
+    p.stats = reinterpret_cast<float *>(ws + pl.off_stats);
+    e = launch_gemm(p, wt, pl.head.tt, s, SV_K_GEMM_LM_HEAD);
+    if (e == hipSuccess && !(flags & SV_HEAD_LOGITS)) {
+      HeadSoftmaxParams h;
+      h.logits = static_cast<float *>(y_out);
+      h.stats = p.stats;
+      h.T = pl.T;
+      h.V = L->vocab;
+      h.nblk = pl.head.nblk;
+      h.cols_per_block = 16384;
+      e = launch_head_softmax(h, s);
+    }
+    return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+  }
+
+  // DECODER
+  const int d = L->d, hq = L->n_q_heads, hk = L->n_kv_heads, hd = L->head_dim, F = L->ffn;
+  uint16_t *qbuf = reinterpret_cast<uint16_t *>(ws + pl.off_qbuf);
+  uint16_t *attn = reinterpret_cast<uint16_t *>(ws + pl.off_attn);
+  uint16_t *x1 = reinterpret_cast<uint16_t *>(ws + pl.off_x1);
+  uint16_t *act = reinterpret_cast<uint16_t *>(ws + pl.off_act);
+
+  {  // QKV + RoPE + KV append
+    GemmParams p = base_params(pl.qkv, x_in, pl.T, wt, ws, pl);
+    p.nmat = 3;
+    p.mat[0] = mat_of(L->wq, hq * hd);
+    p.mat[1] = mat_of(L->wk, hk * hd);
+    p.mat[2] = mat_of(L->wv, hk * hd);
+    p.rowmap = RM_ROPE_PAIRS;
+    p.hd = hd;
+    p.eps = L->eps;
+    p.epi = EPI_QKV;
+    p.qbuf = qbuf;
+    p.hq = hq;
+    p.hkv = hk;
+    p.rope_theta = L->rope_theta;
+    p.gamma = b->gamma;
+    p.kv_len = b->kv_len;
+    p.B = pl.B;
+    p.kv_cap = b->kv_cap;
+    p.kc = b->k_cache;
+    p.vc = b->v_cache;
+    p.err = b->err_flag;
+    e = launch_gemm(p, wt, pl.qkv.tt, s, SV_K_GEMM_QKV);
+    if (e != hipSuccess) return SV_ERR_HIP;
+  }
+  {  // ragged attention + merge
+    AttnParams a;
+    std::memset(&a, 0, sizeof(a));
+    a.qbuf = qbuf;
+    a.gamma = b->gamma;
+    a.kv_len = b->kv_len;
+    a.kc = b->k_cache;
+    a.vc = b->v_cache;
+    a.B = pl.B;
+    a.T = pl.T;
+    a.hq = hq;
+    a.hkv = hk;
+    a.hd = hd;
+    a.kv_cap = b->kv_cap;
+    a.max_ctx = b->max_ctx;
+    a.chunk = pl.attn_chunk;
+    a.max_items = pl.attn_items;
+    a.rpad = pl.attn_rpad;
+    a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)hd));
+    a.part_o = reinterpret_cast<float *>(ws + pl.off_po);
+    a.part_ml = reinterpret_cast<float *>(ws + pl.off_pml);
+    a.out = attn;
+    a.err = b->err_flag;
+    e = launch_attention(a, s);
+    if (e == hipSuccess) e = launch_attn_merge(a, s);
+    if (e != hipSuccess) return SV_ERR_HIP;
+  }
+  {  // O projection + residual
+    GemmParams p = base_params(pl.o, attn, pl.T, wt, ws, pl);
+    p.nmat = 1;
+    p.mat[0] = mat_of(L->wo, d);
+    p.rowmap = RM_LINEAR;
+    p.epi = EPI_RESID;
+    p.out = x1;
+    p.ldo = d;
+    p.resid = static_cast<const uint16_t *>(x_in);
+    e = launch_gemm(p, wt, pl.o.tt, s, SV_K_GEMM_O);
+    if (e != hipSuccess) return SV_ERR_HIP;
+  }
+  {  // gate || up + SwiGLU
+    GemmParams p = base_params(pl.gu, x1, pl.T, wt, ws, pl);
+    p.nmat = 2;
+    p.mat[0] = mat_of(L->w_gate, F);
+    p.mat[1] = mat_of(L->w_up, F);
+    p.rowmap = RM_SWIGLU;
+    p.eps = L->eps;
+    p.epi = EPI_SWIGLU;
+    p.out = act;
+    p.ldo = F;
+    e = launch_gemm(p, wt, pl.gu.tt, s, SV_K_GEMM_GATE_UP);
+    if (e != hipSuccess) return SV_ERR_HIP;
+  }
+  {  // down projection + residual
+    GemmParams p = base_params(pl.down, act, pl.T, wt, ws, pl);
+    p.nmat = 1;
+    p.mat[0] = mat_of(L->w_down, d);
+    p.rowmap = RM_LINEAR;
+    p.epi = EPI_RESID;
+    p.out = y_out;
+    p.ldo = d;
+    p.resid = x1;
+    e = launch_gemm(p, wt, pl.down.tt, s, SV_K_GEMM_DOWN);
+    if (e != hipSuccess) return SV_ERR_HIP;
+  }
+  return SV_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Acceptance.
+namespace {
+constexpr int kAcceptChunk = 8192;
+
+struct AcceptPlan {
+  long long T = 0, nd = 0;
+  int nchunk = 0;
+  size_t off_parts = 0, off_acc = 0, bytes = 0;
+};
+
+sv_status plan_accept(int32_t B, int32_t V, int32_t mode, const int32_t *gamma_host, AcceptPlan &ap) {
+  if (B < 0 || V <= 0) return SV_ERR_INVALID_ARG;
+  if (mode != SV_ACCEPT_STOCHASTIC && mode != SV_ACCEPT_GREEDY) return SV_ERR_INVALID_ARG;
+  if (B > 0 && !gamma_host) return SV_ERR_INVALID_ARG;
+  if (B > kScanMaxB) return SV_ERR_UNSUPPORTED;
+  for (int i = 0; i < B; ++i) {
+    if (gamma_host[i] < 0) return SV_ERR_INVALID_ARG;
+    ap.T += gamma_host[i] + 1;
+    ap.nd += gamma_host[i];
+  }
+  if (ap.T > (1 << 24)) return SV_ERR_UNSUPPORTED;
+  ap.nchunk = (V + kAcceptChunk - 1) / kAcceptChunk;
+  const long long rows = mode == SV_ACCEPT_GREEDY ? ap.T : B;
+  size_t off = 0;
+  ap.off_parts = off;
+  off = align_up(off + (size_t)rows * ap.nchunk * sizeof(AcceptPart));
+  ap.off_acc = off;
+  off = align_up(off + (size_t)(B + ap.T) * sizeof(int));
+  ap.bytes = off;
+  return SV_OK;
+}
+}  // namespace
+
+extern "C" sv_status sv_accept_commit_workspace_bytes(int32_t B, int32_t V, int32_t mode,
+                                                      const int32_t *gamma_host, size_t *bytes) {
+  if (!bytes) return SV_ERR_INVALID_ARG;
+  AcceptPlan ap;
+  const sv_status st = plan_accept(B, V, mode, gamma_host, ap);
+  if (st != SV_OK) return st;
+  *bytes = ap.bytes;
+  return SV_OK;
+}
+
+extern "C" sv_status sv_accept_commit(int32_t B, int32_t V, int32_t mode, const int32_t *gamma_host,
+                                      const int32_t *gamma, const int32_t *draft, const float *p,
+                                      const float *q, const float *u_acc, const float *u_samp,
+                                      int32_t *kv_len, int32_t *accepted, int32_t *next_token,
+                                      int32_t *err_flag, void *workspace, size_t workspace_bytes,
+                                      void *stream) {
+  AcceptPlan ap;
+  sv_status st = plan_accept(B, V, mode, gamma_host, ap);
+  if (st != SV_OK) return st;
+  if (B == 0) return SV_OK;
+  if (!gamma || !p || !kv_len || !accepted || !next_token) return SV_ERR_INVALID_ARG;
+  if (ap.nd > 0 && !draft) return SV_ERR_INVALID_ARG;
+  if (mode == SV_ACCEPT_STOCHASTIC) {
+    if (!u_samp) return SV_ERR_INVALID_ARG;
+    if (ap.nd > 0 && (!q || !u_acc)) return SV_ERR_INVALID_ARG;
+  }
+  if (!workspace || workspace_bytes < ap.bytes) return SV_ERR_WORKSPACE;
+  unsigned char *ws = static_cast<unsigned char *>(workspace);
+  AcceptParams a;
+  std::memset(&a, 0, sizeof(a));
+  a.B = B;
+  a.V = V;
+  a.T = (int)ap.T;
+  a.nd = (int)ap.nd;
+  a.mode = mode;
+  a.chunk = kAcceptChunk;
+  a.nchunk = ap.nchunk;
+  a.gamma = gamma;
+  a.draft = draft;
+  a.p = p;
+  a.q = q;
+  a.u_acc = u_acc;
+  a.u_samp = u_samp;
+  a.kv_len = kv_len;
+  a.accepted = accepted;
+  a.next_token = next_token;
+  a.err = err_flag;
+  a.parts = reinterpret_cast<AcceptPart *>(ws + ap.off_parts);
+  a.acc_ws = reinterpret_cast<int *>(ws + ap.off_acc);
+  (void)hipGetLastError();
+  const hipError_t e = launch_accept(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+}

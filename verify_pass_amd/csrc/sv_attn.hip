@@ -1,0 +1,320 @@
+// Ragged causal attention over per-sequence KV caches, gfx950.
+//
+// Each sequence i brings G * (gamma_i + 1) query rows per KV head (the GQA
+// group times its verify tokens) and L_i = kv_len[i] + gamma_i + 1 keys.  Query
+// j of sequence i sees keys 0 .. kv_len[i] + j: the causal mask only bites on
+// the new keys, and every sequence keeps its own length -- nothing is padded
+// to the longest sequence.  Work items are (sequence, key chunk) pairs
+// enumerated by a prefix sum over per-sequence chunk counts, times KV heads.
+//
+// Per wave, 32 keys at a time:
+//   S^T[key][row] = K Q^T  (MFMA: keys are M, query rows N, head dim K)
+//   online softmax in fp32 (exp2 domain), row max across lanes by shuffles
+//   O^T[d][row] += V^T P^T (MFMA: head dim M, query rows N, keys K)
+// The key order inside an MFMA is permuted so that the S^T output a lane holds
+// (8 consecutive keys of one query row) is exactly the P^T operand it feeds to
+// the PV MFMA; values are stored position-minor (V^T per head) so that operand
+// is one contiguous 16-byte load.  Waves of a workgroup split the chunk and are
+// combined in LDS; chunks are combined by a log-sum-exp merge.
+#include "sv_common.h"
+
+namespace sv {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kKeysPerStep = 32;
+constexpr float kNegBig = -1.0e30f;
+
+// Token map and chunk map for all sequences, in LDS.
+// qs[i] = first stacked row of sequence i, cs[i] = first work item of sequence i.
+__device__ inline int build_maps(const AttnParams &p, int *qs, int *cs, int *tmp) {
+  for (int i = threadIdx.x; i < p.B; i += kThreads) {
+    const int g = p.gamma[i];
+    const int L = p.kv_len[i] + g + 1;
+    qs[i] = g + 1;
+    cs[i] = (L + p.chunk - 1) / p.chunk;
+  }
+  __syncthreads();
+  block_exscan(qs, p.B, tmp);
+  return block_exscan(cs, p.B, tmp);
+}
+
+__device__ __forceinline__ int dslice(int dg, int gq) {
+  // lane group gq covers head-dim columns [64*(dg/2) + 16*gq + 8*(dg%2), +8)
+  return 64 * (dg >> 1) + 16 * gq + 8 * (dg & 1);
+}
+
+template <int RT, int HD>
+__global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
+  constexpr int NDG = HD / 32;  // MFMA k-groups over the head dim
+  constexpr int NDT = HD / 16;  // 16-wide head-dim tiles of the output
+  extern __shared__ __align__(16) unsigned char smem[];
+  int *qs = reinterpret_cast<int *>(smem);
+  int *cs = qs + p.B + 1;
+  int *tmp = cs + p.B + 1;
+  float *red_o = reinterpret_cast<float *>(tmp + 260);  // [4][HD][16]
+  float *red_ml = red_o + 4 * HD * 16;                   // [4][16][2]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int gq = lane >> 4, l16 = lane & 15;
+  const int g = blockIdx.y;
+
+  const int total = build_maps(p, qs, cs, tmp);
+  if (blockIdx.x == 0 && g == 0 && tid == 0 && total > p.max_items) set_err(p.err, SV_DEV_ERR_CTX_BOUND);
+  const int item = blockIdx.x;
+  if (item >= total) return;
+  const int seq = upper_index(cs, p.B, item);
+  const int c = item - cs[seq];
+  const int gam = p.gamma[seq];
+  const int ctx = p.kv_len[seq];
+  const int L = ctx + gam + 1;
+  if (L > p.kv_cap) {
+    if (tid == 0) set_err(p.err, SV_DEV_ERR_KV_OVERFLOW);
+    return;
+  }
+  const int G = p.hq / p.hkv;
+  const int n1 = gam + 1;
+  const int R = G * n1;
+  const int kb = c * p.chunk, ke = min(L, kb + p.chunk);
+  const int per_wave = p.chunk / 4;
+  const int kw0 = kb + wave * per_wave, kw1 = min(ke, kw0 + per_wave);
+
+  const uint16_t *kbase = static_cast<const uint16_t *>(p.kc[seq]) + (size_t)g * p.kv_cap * HD;
+  const uint16_t *vbase = static_cast<const uint16_t *>(p.vc[seq]) + (size_t)g * HD * p.kv_cap;
+
+  // query fragments and per-row causal limits
+  bf16x8 qf[RT][NDG];
+  int lim[RT];  // last visible key of this lane's row (or -1 for padding rows)
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int rr = rt * 16 + l16;
+    if (rr < R) {
+      const int hg = rr / n1, j = rr - hg * n1;
+      const int t = qs[seq] + j;
+      const uint16_t *q = p.qbuf + ((size_t)t * p.hq + g * G + hg) * HD;
+#pragma unroll
+      for (int dg = 0; dg < NDG; ++dg) qf[rt][dg] = as_bf16x8(*reinterpret_cast<const uint4 *>(q + dslice(dg, gq)));
+      lim[rt] = ctx + j;
+    } else {
+#pragma unroll
+      for (int dg = 0; dg < NDG; ++dg) qf[rt][dg] = as_bf16x8(uint4{0u, 0u, 0u, 0u});
+      lim[rt] = -1;
+    }
+  }
+
+  floatx4 o[RT][NDT];
+  float m_run[RT], l_run[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    m_run[rt] = kNegBig;
+    l_run[rt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[rt][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  for (int k0 = kw0; k0 < kw1; k0 += kKeysPerStep) {
+    // K operand: MFMA row m of key tile kt is key k0 + 8*(m/4) + 4*kt + m%4
+    bf16x8 kf[2][NDG];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      int key = k0 + 8 * (l16 >> 2) + 4 * kt + (l16 & 3);
+      key = min(key, L - 1);
+      const uint16_t *kr = kbase + (size_t)key * HD;
+#pragma unroll
+      for (int dg = 0; dg < NDG; ++dg) kf[kt][dg] = as_bf16x8(*reinterpret_cast<const uint4 *>(kr + dslice(dg, gq)));
+    }
+    // V^T operand: lane (d = 16*dt + l16, gq) holds keys k0 + 8*gq .. +7
+    bf16x8 vf[NDT];
+    const int vk = k0 + 8 * gq;
+    const int vstart = min(vk, (L - 1) & ~7);
+    const int nvalid = L - vk;  // keys at or past L are zeroed
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      uint4 v = *reinterpret_cast<const uint4 *>(vbase + (size_t)(dt * 16 + l16) * p.kv_cap + vstart);
+      if (nvalid < 8) {
+        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (e >= nvalid) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+        v = uint4{w[0], w[1], w[2], w[3]};
+      }
+      vf[dt] = as_bf16x8(v);
+    }
+
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      floatx4 s[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        s[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dg = 0; dg < NDG; ++dg) s[kt] = mfma16x16x32(kf[kt][dg], qf[rt][dg], s[kt]);
+      }
+      float sv[8];
+      float mx = kNegBig;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int key = k0 + 8 * gq + e;
+        const bool ok = key < kw1 && key <= lim[rt];
+        sv[e] = ok ? s[e >> 2][e & 3] * p.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, sv[e]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run[rt], mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run[rt] - m_new);
+      float lsum = 0.f;
+      uint32_t pb[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pe = __builtin_amdgcn_exp2f(sv[e] - m_new);
+        lsum += pe;
+        pb[e] = f2bf(pe);
+      }
+      l_run[rt] = l_run[rt] * alpha + lsum;
+      m_run[rt] = m_new;
+      const bf16x8 pf = as_bf16x8(uint4{pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16),
+                                        pb[4] | (pb[5] << 16), pb[6] | (pb[7] << 16)});
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        o[rt][dt] *= alpha;
+        o[rt][dt] = mfma16x16x32(vf[dt], pf, o[rt][dt]);
+      }
+    }
+  }
+
+  // ---- combine the four waves, one row tile at a time ----------------------
+  const int G_items = p.hkv;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    float l = l_run[rt];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (gq == 0) {
+      red_ml[(wave * 16 + l16) * 2] = m_run[rt];
+      red_ml[(wave * 16 + l16) * 2 + 1] = l;
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red_o[(wave * HD + dt * 16 + 4 * gq + i) * 16 + l16] = o[rt][dt][i];
+    __syncthreads();
+    const size_t prow = ((size_t)item * G_items + g) * p.rpad + rt * 16;
+    for (int idx = tid; idx < HD * 16; idx += kThreads) {
+      const int row = idx / HD, d = idx - row * HD;
+      float M = kNegBig;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) M = fmaxf(M, red_ml[(w * 16 + row) * 2]);
+      float acc = 0.f, lt = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float f = __builtin_amdgcn_exp2f(red_ml[(w * 16 + row) * 2] - M);
+        acc += red_o[(w * HD + d) * 16 + row] * f;
+        lt += red_ml[(w * 16 + row) * 2 + 1] * f;
+      }
+      p.part_o[(prow + row) * HD + d] = acc;
+      if (d == 0) {
+        p.part_ml[(prow + row) * 2] = M;
+        p.part_ml[(prow + row) * 2 + 1] = lt;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// One workgroup per (token, query head): log-sum-exp merge over the chunks.
+template <int HD>
+__global__ __launch_bounds__(HD) void merge_kernel(AttnParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  int *qs = reinterpret_cast<int *>(smem);
+  int *cs = qs + p.B + 1;
+  int *tmp = cs + p.B + 1;
+  // the scan helpers assume 256 threads; HD <= 256 threads here, so build the
+  // maps with a simple strided loop and a serial scan by thread 0
+  for (int i = threadIdx.x; i < p.B; i += HD) {
+    const int g = p.gamma[i];
+    qs[i] = g + 1;
+    cs[i] = (p.kv_len[i] + g + 1 + p.chunk - 1) / p.chunk;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int a = 0, b = 0;
+    for (int i = 0; i < p.B; ++i) {
+      const int x = qs[i], y = cs[i];
+      qs[i] = a;
+      cs[i] = b;
+      a += x;
+      b += y;
+    }
+    tmp[0] = b;
+  }
+  __syncthreads();
+  const int t = blockIdx.x, qh = blockIdx.y, d = threadIdx.x;
+  const int seq = upper_index(qs, p.B, t);
+  const int j = t - qs[seq];
+  const int gam = p.gamma[seq];
+  const int G = p.hq / p.hkv;
+  const int g = qh / G, hg = qh - g * G;
+  const int row = hg * (gam + 1) + j;
+  const int L = p.kv_len[seq] + gam + 1;
+  const int nch = (L + p.chunk - 1) / p.chunk;
+  float M = kNegBig;
+  for (int c = 0; c < nch; ++c) {
+    const int item = cs[seq] + c;
+    if (item >= p.max_items) break;
+    M = fmaxf(M, p.part_ml[(((size_t)item * p.hkv + g) * p.rpad + row) * 2]);
+  }
+  float acc = 0.f, lt = 0.f;
+  for (int c = 0; c < nch; ++c) {
+    const int item = cs[seq] + c;
+    if (item >= p.max_items) break;
+    const size_t pr = ((size_t)item * p.hkv + g) * p.rpad + row;
+    const float f = __builtin_amdgcn_exp2f(p.part_ml[pr * 2] - M);
+    acc += p.part_o[pr * HD + d] * f;
+    lt += p.part_ml[pr * 2 + 1] * f;
+  }
+  const float v = lt > 0.f ? acc / lt : 0.f;
+  p.out[(size_t)t * p.hq * HD + qh * HD + d] = f2bf(v);
+}
+
+template <int RT, int HD>
+hipError_t launch_rt(const AttnParams &p, hipStream_t s) {
+  const size_t lds = (size_t)(2 * (p.B + 1) + 260) * sizeof(int) + (size_t)4 * HD * 16 * sizeof(float) +
+                     4 * 16 * 2 * sizeof(float);
+  if (lds > 65536)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_kernel<RT, HD>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  trace_before(SV_K_ATTENTION, s);
+  hipLaunchKernelGGL((attn_kernel<RT, HD>), dim3(p.max_items, p.hkv), dim3(kThreads), lds, s, p);
+  trace_after(SV_K_ATTENTION, s);
+  return hipGetLastError();
+}
+
+template <int HD>
+hipError_t launch_hd(const AttnParams &p, hipStream_t s) {
+  switch (p.rpad / 16) {
+    case 1: return launch_rt<1, HD>(p, s);
+    case 2: return launch_rt<2, HD>(p, s);
+    case 3: return launch_rt<3, HD>(p, s);
+    default: return launch_rt<4, HD>(p, s);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attention(const AttnParams &p, hipStream_t s) {
+  return p.hd == 64 ? launch_hd<64>(p, s) : launch_hd<128>(p, s);
+}
+
+hipError_t launch_attn_merge(const AttnParams &p, hipStream_t s) {
+  const size_t lds = (size_t)(2 * (p.B + 1) + 4) * sizeof(int);
+  trace_before(SV_K_ATTN_MERGE, s);
+  if (p.hd == 64)
+    hipLaunchKernelGGL((merge_kernel<64>), dim3(p.T, p.hq), dim3(64), lds, s, p);
+  else
+    hipLaunchKernelGGL((merge_kernel<128>), dim3(p.T, p.hq), dim3(128), lds, s, p);
+  trace_after(SV_K_ATTN_MERGE, s);
+  return hipGetLastError();
+}
+
+}  // namespace sv

@@ -1,0 +1,205 @@
+// Internal declarations shared by the gfx950 kernels and the host dispatch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/sv.h"
+
+namespace sv {
+
+// ---------------------------------------------------------------------------
+// Vector types for the CDNA4 matrix cores.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// D = A(16x32) * B(32x16) + C, bf16 inputs, fp32 accumulate.
+// Lane l: A row l%16, k = 8*(l/16)..+7; B column l%16, same k; D rows
+// 4*(l/16)..+3 of column l%16.
+__device__ __forceinline__ floatx4 mfma16x16x32(const bf16x8 &a, const bf16x8 &b,
+                                                const floatx4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf2f(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4 &v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// ---------------------------------------------------------------------------
+// Block-level helpers (blockDim.x == 256).
+
+// In-place exclusive prefix sum of n (<= 65536) ints in LDS; returns the total.
+// tmp: 257 ints of LDS.  Deterministic (fixed association order).
+__device__ inline int block_exscan(int *vals, int n, int *tmp) {
+  const int tid = threadIdx.x;
+  const int per = (n + 255) / 256;
+  const int lo = min(n, tid * per), hi = min(n, lo + per);
+  int s = 0;
+  for (int i = lo; i < hi; ++i) s += vals[i];
+  tmp[tid] = s;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int i = 0; i < 256; ++i) {
+      const int v = tmp[i];
+      tmp[i] = run;
+      run += v;
+    }
+    tmp[256] = run;
+  }
+  __syncthreads();
+  int run = tmp[tid];
+  for (int i = lo; i < hi; ++i) {
+    const int v = vals[i];
+    vals[i] = run;
+    run += v;
+  }
+  __syncthreads();
+  return tmp[256];
+}
+
+// Largest i in [0, n) with starts[i] <= x (starts ascending, starts[0] <= x).
+__device__ inline int upper_index(const int *starts, int n, int x) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (starts[mid] <= x) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__device__ inline void set_err(int *err, int bits) {
+  if (err) atomicOr(err, bits);
+}
+
+// ---------------------------------------------------------------------------
+// Kernel parameter blocks.
+
+constexpr int kMaxB = 65536;        // sequences per call (LDS token-map limit)
+constexpr int kScanMaxB = 4096;     // kernels that keep the full map in LDS
+
+enum RowMap { RM_LINEAR = 0, RM_ROPE_PAIRS = 1, RM_SWIGLU = 2 };
+enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
+enum WType { WT_F32 = 0, WT_BF16 = 1, WT_INT4 = 2 };
+
+struct GemmMat {
+  const void *w;
+  const uint16_t *s;
+  int rows;
+};
+
+struct GemmParams {
+  const uint16_t *x;  // activations bf16 [T][K]
+  int T, K, N;        // N = logical rows
+  int nmat;
+  GemmMat mat[3];
+  int rowmap, hd;
+  int splits, ksteps;  // ksteps = K / step size
+  int nblk, ntblk;     // 64-row blocks, token blocks
+  int norm;
+  float eps;
+  float *partial;      // [splits][nblk][ntblk][tok_tile*64]
+  float *part_ss;      // [nblk][splits][ntblk][64]
+  int *counters;       // [nblk * ntblk]
+  int epi;
+  void *out;
+  int ldo;
+  const uint16_t *resid;  // EPI_RESID
+  float *stats;           // EPI_LOGITS: [nblk][T][2] (max, sum exp)
+  // EPI_QKV
+  uint16_t *qbuf;  // [T][hq][hd]
+  int hq, hkv;
+  float rope_theta;
+  const int *gamma;
+  const int *kv_len;
+  int B, kv_cap;
+  void *const *kc;
+  void *const *vc;
+  int *err;
+};
+
+struct AttnParams {
+  const uint16_t *qbuf;  // [T][hq][hd] (rotated)
+  const int *gamma;
+  const int *kv_len;
+  void *const *kc;
+  void *const *vc;
+  int B, T, hq, hkv, hd, kv_cap, max_ctx;
+  int chunk;        // keys per work item
+  int max_items;    // grid.x
+  int rpad;         // padded query rows per (seq, kv head)
+  float scale_log2; // log2(e) / sqrt(hd)
+  float *part_o;    // [max_items][hkv][rpad][hd]
+  float *part_ml;   // [max_items][hkv][rpad][2]
+  uint16_t *out;    // [T][hq*hd]
+  int *err;
+};
+
+struct HeadSoftmaxParams {
+  float *logits;        // [T][V] in: logits, out: probabilities
+  const float *stats;   // [nblk][T][2]
+  int T, V, nblk, cols_per_block;
+};
+
+struct EmbedParams {
+  const int *tokens;
+  const void *table;  // [V][d] fp32 or bf16
+  int table_bf16;
+  int T, V, d;
+  uint16_t *out;
+  int *err;
+};
+
+struct AcceptPart {
+  unsigned long long sum_res;  // residual / bonus weights in this chunk
+  unsigned long long sum_p;    // fallback weights (target row)
+  float max_p;                 // argmax of the target row in this chunk
+  int arg_p;
+};
+
+struct AcceptParams {
+  int B, V, T, nd, mode;
+  int chunk, nchunk;
+  const int *gamma;
+  const int *draft;
+  const float *p;
+  const float *q;
+  const float *u_acc;
+  const float *u_samp;
+  int *kv_len;
+  int *accepted;
+  int *next_token;
+  int *err;
+  AcceptPart *parts;   // stochastic: [B][nchunk]; greedy: [T][nchunk]
+  int *acc_ws;         // stochastic: [B] accepted count (or -1 for a bad sequence)
+};
+
+// ---------------------------------------------------------------------------
+// Host launchers (one per kernel family).  Return hipSuccess or the launch error.
+hipError_t launch_gemm(const GemmParams &p, int wtype, int tok_tiles, hipStream_t s,
+                       int trace_class);
+hipError_t launch_attention(const AttnParams &p, hipStream_t s);
+hipError_t launch_attn_merge(const AttnParams &p, hipStream_t s);
+hipError_t launch_head_softmax(const HeadSoftmaxParams &p, hipStream_t s);
+hipError_t launch_embed(const EmbedParams &p, hipStream_t s);
+hipError_t launch_accept(const AcceptParams &p, hipStream_t s);
+
+// Kernel-timing trace hooks (host).
+void trace_before(int kernel_class, hipStream_t s);
+void trace_after(int kernel_class, hipStream_t s);
+
+// Step sizes along K per weight type.
+inline int kstep_of(int wtype) { return wtype == WT_INT4 ? 128 : 64; }
+
+}  // namespace sv
