@@ -38,10 +38,11 @@
  *  - Errors that depend on device data (a token id outside the vocabulary, a
  *    KV length that would overflow the cache) set bits in the optional device
  *    word *err_flag (SV_DEV_ERR_*) and never write outside caller buffers.
- *  - Workspaces: zero-fill a workspace once after allocating it.  Each call
- *    leaves its synchronisation counters zeroed again, so a workspace can be
- *    reused by later calls on the same stream; calls that overlap in time
- *    must use different workspaces.
+ *  - Workspaces: zero-fill a workspace once after allocating it.  Its first
+ *    256 KiB hold the library's arrival counters in every call; each call
+ *    leaves them zeroed again, so one workspace (sized for the largest call)
+ *    can serve later calls of any kind on the same stream.  Calls that overlap
+ *    in time must use different workspaces.
  *  - Thread safety: calls may come from several host threads; the only
  *    global state is the optional kernel-timing trace (sv_trace_*).
  */
@@ -139,7 +140,8 @@ typedef struct sv_layer {
 typedef struct sv_batch {
   int32_t B;                 /* sequences, >= 0 */
   int32_t T;                 /* stacked tokens = sum(gamma_i + 1) */
-  int32_t max_ctx;           /* upper bound on every kv_len[i] (sizes the grid) */
+  int32_t max_ctx;           /* upper bound on every kv_len[i] (sizes the attention grid;
+                                a larger kv_len sets SV_DEV_ERR_CTX_BOUND) */
   int32_t kv_cap;            /* cache capacity per sequence, multiple of 16 */
   const int32_t *gamma_host; /* (host) [B] draft counts, >= 0 */
   const int32_t *gamma;      /* [B] the same counts on the device */

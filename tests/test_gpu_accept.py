@@ -90,16 +90,20 @@ def test_accept_chi_square_gpu():
     from scipy import stats
     sh = SHAPES["tiny"]
     rng = np.random.default_rng(9)
-    B, V = 200000, 8
+    Bc, calls, V = 4096, 50, 8       # 204800 sequences in calls of 4096
     p1, p2 = rng.dirichlet(np.ones(V)).astype(np.float32), rng.dirichlet(np.ones(V)).astype(np.float32)
     q1 = rng.dirichlet(np.ones(V)).astype(np.float32)
-    wl = custom_workload(sh, "f32", [1] * B, [0] * B, seed=9)
-    d = rng.choice(V, size=B, p=q1 / q1.sum()).astype(np.int32)
-    inp = {"draft": d, "q": np.tile(q1, (B, 1)), "p": np.tile(np.stack([p1, p2]), (B, 1)),
-           "u_acc": (rng.integers(0, 1 << 24, B) / 2 ** 24).astype(np.float32),
-           "u_samp": (rng.integers(0, 1 << 24, B) / 2 ** 24).astype(np.float32)}
-    a, y, _, _ = run_accept(wl.gamma, V, inp, wl.ctx)
-    first = np.where(a >= 1, d, y)
+    wl = custom_workload(sh, "f32", [1] * Bc, [0] * Bc, seed=9)
+    firsts = []
+    for _ in range(calls):
+        d = rng.choice(V, size=Bc, p=q1 / q1.sum()).astype(np.int32)
+        inp = {"draft": d, "q": np.tile(q1, (Bc, 1)), "p": np.tile(np.stack([p1, p2]), (Bc, 1)),
+               "u_acc": (rng.integers(0, 1 << 24, Bc) / 2 ** 24).astype(np.float32),
+               "u_samp": (rng.integers(0, 1 << 24, Bc) / 2 ** 24).astype(np.float32)}
+        a, y, _, _ = run_accept(wl.gamma, V, inp, wl.ctx)
+        firsts.append(np.where(a >= 1, d, y))
+    first = np.concatenate(firsts)
+    B = len(first)
     counts = np.bincount(first, minlength=V).astype(np.float64)
     exp = p1.astype(np.float64) / p1.sum() * B
     chi = stats.chisquare(counts, exp)

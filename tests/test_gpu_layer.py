@@ -109,6 +109,31 @@ def test_head_parity():
         np.testing.assert_allclose(pr, OV.softmax(lg), rtol=2e-5, atol=1e-9)
 
 
+def test_decoder_then_head_shared_workspace():
+    """The chain a verify step runs: decoder layer then LM head on one stream,
+    sharing one workspace, against the oracle chain."""
+    shape = Shape(512, 8, 2, 128, 1024, 4099)
+    wl = custom_workload(shape, "bf16", [2, 0, 3], [300, 7, 64], seed=7)
+    dec = GpuDecoder(wl)
+    head = GpuHead(wl)
+    n = max(dec.ws_bytes, head.ws_bytes[sv.SV_HEAD_LOGITS])
+    ws = tg.workspace(n)
+    xh = hidden_states(wl.T, shape.d, wl.seed)
+    x = tg.to_dev(xh)
+    y = torch.empty_like(x)
+    lg = torch.empty(wl.T, shape.vocab, dtype=torch.float32, device="cuda")
+    st = tg.stream_handle()
+    assert sv.sv_verify_layer(dec.L, dec.bs, x, y, 0, ws, n, st) == 0
+    assert sv.sv_verify_layer(head.L, dec.bs, y, lg, sv.SV_HEAD_LOGITS, ws, n, st) == 0
+    torch.cuda.synchronize()
+    ref = dec.oracle(xh)
+    ey = rel_rows(dev_bf16_to_f64(y), ref.y)
+    el = rel_rows(lg.cpu().numpy(), OV.head_logits(head.Wlm, ref.y))
+    el_own = rel_rows(lg.cpu().numpy(), OV.head_logits(head.Wlm, dev_bf16_to_f64(y)))
+    say(f"chain: y {ey:.2e}  logits {el:.2e}  logits-on-gpu-y {el_own:.2e}")
+    assert ey < TOL["bf16"] and el_own < TOL["bf16"] and el < TOL["bf16"]
+
+
 def test_embed_and_bad_token():
     sh = SHAPES["tiny"]
     E = embed_weights(sh, 3)

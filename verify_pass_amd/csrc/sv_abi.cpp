@@ -96,12 +96,18 @@ namespace {
 
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+// Every workspace starts with the same fixed block of arrival counters, so a
+// workspace zero-filled once stays valid when it is shared between calls of
+// different kinds and shapes (each launch leaves the counters it used at 0).
+constexpr size_t kCounterBytes = 256 * 1024;
+constexpr size_t kMaxCounters = kCounterBytes / sizeof(int);
 
-int target_workgroups() {
+// Waves to aim for per weight GEMM: about 8 per CU on 256 CUs.
+int target_units() {
   static int v = [] {
-    const char *e = std::getenv("SV_TARGET_WG");
+    const char *e = std::getenv("SV_TARGET_UNITS");
     const int x = e ? std::atoi(e) : 0;
-    return x > 0 ? x : 1024;
+    return x > 0 ? x : 2048;
   }();
   return v;
 }
@@ -109,13 +115,12 @@ int target_workgroups() {
 struct GemmCfg {
   int nblk = 0, ntblk = 0, splits = 1, tt = 1, ksteps = 0, K = 0, N = 0;
   bool norm = false;
-  size_t partial_floats() const {
-    return splits > 1 ? (size_t)splits * nblk * ntblk * tt * 16 * 64 : 0;
-  }
-  size_t ss_floats() const { return (splits > 1 && norm) ? (size_t)nblk * splits * ntblk * 64 : 0; }
+  size_t partial_floats() const { return gemm_partial_floats(nblk, splits, ntblk, tt); }
   size_t counters() const { return splits > 1 ? (size_t)nblk * ntblk : 0; }
 };
 
+// nblk: 32-row groups (16 gate/up feature pairs for SwiGLU).  K is split only
+// when the row groups alone leave the chip short of work.
 GemmCfg gemm_cfg(int nblk, int N, int T, int K, int wtype, bool norm) {
   GemmCfg c;
   c.nblk = nblk;
@@ -126,9 +131,11 @@ GemmCfg gemm_cfg(int nblk, int N, int T, int K, int wtype, bool norm) {
   c.ntblk = (T + 16 * c.tt - 1) / (16 * c.tt);
   c.ksteps = K / kstep_of(wtype);
   const int base = std::max(1, nblk * c.ntblk);
-  const int want = (target_workgroups() + base - 1) / base;
-  const int maxs = std::max(1, std::min(32, c.ksteps / 4));
+  // split K only as far as the resident waves allow (one round of units)
+  const int want = std::max(1, target_units() / base);
+  const int maxs = std::max(1, std::min(32, c.ksteps / 2));
   c.splits = std::max(1, std::min(want, maxs));
+  if (c.splits > 1 && (size_t)base > kMaxCounters) c.splits = 1;
   return c;
 }
 
@@ -136,7 +143,7 @@ struct LayerPlan {
   int T = 0, B = 0, G = 1, gmax = 0;
   GemmCfg qkv, o, gu, down, head;
   int attn_chunk = 256, attn_items = 0, attn_rpad = 16;
-  size_t off_counters = 0, off_partial = 0, off_ss = 0, off_qbuf = 0, off_po = 0, off_pml = 0;
+  size_t off_counters = 0, off_partial = 0, off_qbuf = 0, off_po = 0, off_pml = 0;
   size_t off_attn = 0, off_x1 = 0, off_act = 0, off_stats = 0;
   size_t bytes = 0;
 };
@@ -194,10 +201,9 @@ sv_status plan_layer(const sv_layer *L, const sv_batch *b, int32_t flags, LayerP
   if (L->kind == SV_LAYER_HEAD) {
     if (L->vocab <= 0) return SV_ERR_INVALID_ARG;
     if (check_matrix(L->lm_head, w) != SV_OK) return SV_ERR_INVALID_ARG;
-    pl.head = gemm_cfg((L->vocab + 63) / 64, L->vocab, pl.T, L->d, w, true);
-    pl.off_counters = take(std::max<size_t>(pl.head.counters(), 1) * sizeof(int));
+    pl.head = gemm_cfg((L->vocab + 31) / 32, L->vocab, pl.T, L->d, w, true);
+    pl.off_counters = take(kCounterBytes);
     pl.off_partial = take(pl.head.partial_floats() * sizeof(float));
-    pl.off_ss = take(pl.head.ss_floats() * sizeof(float));
     pl.off_stats = take((size_t)pl.head.nblk * pl.T * 2 * sizeof(float));
     pl.bytes = off;
     return SV_OK;
@@ -214,15 +220,16 @@ sv_status plan_layer(const sv_layer *L, const sv_batch *b, int32_t flags, LayerP
   pl.G = hq / hk;
   if (pl.B > kScanMaxB) return SV_ERR_UNSUPPORTED;
   if ((long long)pl.G * (gmax + 1) > 64) return SV_ERR_UNSUPPORTED;
+  // per-sequence capacity (kv_len[i] + gamma_i + 1 <= kv_cap) is checked on the
+  // device, where kv_len lives; max_ctx only sizes the attention grid
   if (b->max_ctx < 0 || b->kv_cap <= 0 || b->kv_cap % 16) return SV_ERR_INVALID_ARG;
-  if ((long long)b->max_ctx + gmax + 1 > b->kv_cap) return SV_ERR_INVALID_ARG;
   if (pl.B > 0 && (!b->gamma || !b->kv_len || !b->k_cache || !b->v_cache)) return SV_ERR_INVALID_ARG;
 
   const int nqkv = (hq + 2 * hk) * hd;
-  pl.qkv = gemm_cfg(nqkv / 64, nqkv, pl.T, d, w, true);
-  pl.o = gemm_cfg(d / 64, d, pl.T, hq * hd, w, false);
-  pl.gu = gemm_cfg((F + 31) / 32, 2 * F, pl.T, d, w, true);
-  pl.down = gemm_cfg(d / 64, d, pl.T, F, w, false);
+  pl.qkv = gemm_cfg(nqkv / 32, nqkv, pl.T, d, w, true);
+  pl.o = gemm_cfg((d + 31) / 32, d, pl.T, hq * hd, w, false);
+  pl.gu = gemm_cfg((F + 15) / 16, 2 * F, pl.T, d, w, true);
+  pl.down = gemm_cfg((d + 31) / 32, d, pl.T, F, w, false);
   pl.attn_rpad = 16 * ((pl.G * (gmax + 1) + 15) / 16);
   long long items = 0;
   for (int i = 0; i < pl.B; ++i)
@@ -230,15 +237,10 @@ sv_status plan_layer(const sv_layer *L, const sv_batch *b, int32_t flags, LayerP
   if (items > (1 << 30)) return SV_ERR_UNSUPPORTED;
   pl.attn_items = (int)items;
 
-  size_t counters = 1, partial = 0, ss = 0;
-  for (const GemmCfg *g : {&pl.qkv, &pl.o, &pl.gu, &pl.down}) {
-    counters = std::max(counters, g->counters());
-    partial = std::max(partial, g->partial_floats());
-    ss = std::max(ss, g->ss_floats());
-  }
-  pl.off_counters = take(counters * sizeof(int));
+  size_t partial = 0;
+  for (const GemmCfg *g : {&pl.qkv, &pl.o, &pl.gu, &pl.down}) partial = std::max(partial, g->partial_floats());
+  pl.off_counters = take(kCounterBytes);
   pl.off_partial = take(partial * sizeof(float));
-  pl.off_ss = take(ss * sizeof(float));
   pl.off_qbuf = take((size_t)pl.T * hq * hd * 2);
   pl.off_po = take((size_t)pl.attn_items * hk * pl.attn_rpad * hd * sizeof(float));
   pl.off_pml = take((size_t)pl.attn_items * hk * pl.attn_rpad * 2 * sizeof(float));
@@ -263,7 +265,6 @@ GemmParams base_params(const GemmCfg &c, const void *x, int T, int wtype, unsign
   p.ntblk = c.ntblk;
   p.norm = c.norm ? 1 : 0;
   p.partial = reinterpret_cast<float *>(ws + pl.off_partial);
-  p.part_ss = reinterpret_cast<float *>(ws + pl.off_ss);
   p.counters = reinterpret_cast<int *>(ws + pl.off_counters);
   (void)wtype;
   return p;
@@ -338,7 +339,7 @@ extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const
       h.T = pl.T;
       h.V = L->vocab;
       h.nblk = pl.head.nblk;
-      h.cols_per_block = 16384;
+      h.cols_per_block = 4096;
       e = launch_head_softmax(h, s);
     }
     return e == hipSuccess ? SV_OK : SV_ERR_HIP;
@@ -466,7 +467,7 @@ sv_status plan_accept(int32_t B, int32_t V, int32_t mode, const int32_t *gamma_h
   if (ap.T > (1 << 24)) return SV_ERR_UNSUPPORTED;
   ap.nchunk = (V + kAcceptChunk - 1) / kAcceptChunk;
   const long long rows = mode == SV_ACCEPT_GREEDY ? ap.T : B;
-  size_t off = 0;
+  size_t off = kCounterBytes;  // shared-workspace layout: counters first
   ap.off_parts = off;
   off = align_up(off + (size_t)rows * ap.nchunk * sizeof(AcceptPart));
   ap.off_acc = off;

@@ -106,17 +106,16 @@ struct GemmParams {
   GemmMat mat[3];
   int rowmap, hd;
   int splits, ksteps;  // ksteps = K / step size
-  int nblk, ntblk;     // 64-row blocks, token blocks
+  int nblk, ntblk;     // 32-row groups (16 features for SWIGLU), token blocks
   int norm;
   float eps;
-  float *partial;      // [splits][nblk][ntblk][tok_tile*64]
-  float *part_ss;      // [nblk][splits][ntblk][64]
-  int *counters;       // [nblk * ntblk]
+  float *partial;      // K-split partial tiles (device-scope stores)
+  int *counters;       // [ntblk * nblk] arrival counters, zero between launches
   int epi;
   void *out;
   int ldo;
   const uint16_t *resid;  // EPI_RESID
-  float *stats;           // EPI_LOGITS: [nblk][T][2] (max, sum exp)
+  float *stats;           // EPI_LOGITS: [nblk][T][2] (max, sum exp of the group)
   // EPI_QKV
   uint16_t *qbuf;  // [T][hq][hd]
   int hq, hkv;
@@ -189,6 +188,8 @@ struct AcceptParams {
 // Host launchers (one per kernel family).  Return hipSuccess or the launch error.
 hipError_t launch_gemm(const GemmParams &p, int wtype, int tok_tiles, hipStream_t s,
                        int trace_class);
+// Workspace floats for the K-split partial tiles of one GEMM launch.
+size_t gemm_partial_floats(int ngroups, int splits, int ntblk, int tok_tiles);
 hipError_t launch_attention(const AttnParams &p, hipStream_t s);
 hipError_t launch_attn_merge(const AttnParams &p, hipStream_t s);
 hipError_t launch_head_softmax(const HeadSoftmaxParams &p, hipStream_t s);

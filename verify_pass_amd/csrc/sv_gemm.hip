@@ -1,24 +1,31 @@
 // Weight-streaming GEMM over the stacked verify tokens, gfx950.
 //
-// Y^T[N][T] = W[N][K] * X^T: the weight rows are the MFMA's M side and the
-// tokens its N side, so a wave streams 16 weight rows straight from HBM into
-// registers (no LDS round trip for the big operand) while the small token
-// matrix is staged in LDS and reused by every wave of the workgroup.  One
-// read of the weights serves every stacked token, which is the point of a
-// verification pass (one weight stream for all drafts of all sequences).
+// Y^T[N][T] = W[N][K] * X^T: weight rows are the MFMA's M side and tokens its
+// N side.  One read of the weights serves every stacked token of every
+// sequence -- the single weight stream a verification pass is built around.
 //
-// Work decomposition: a workgroup (4 waves) owns a 64-row block of logical
-// output rows, one token block of up to 64 tokens and one split of K.  Splits
-// write fp32 partial tiles to the workspace; the last split to finish (atomic
-// counter per tile) adds them in split order -- so results are bitwise
-// repeatable -- and runs the fused epilogue:
-//   QKV     RMSNorm scale, RoPE, q to a staging buffer, k/v appended to caches
-//   RESID   + residual, bf16 out (O and down projections)
-//   SWIGLU  RMSNorm scale, silu(gate) * up, bf16 out
-//   LOGITS  RMSNorm scale, fp32 logits, per-block softmax statistics
-// RMSNorm needs only a per-token scale r_t = 1/sqrt(mean(x^2) + eps), and
-// (r_t x) W = r_t (x W), so the norm is applied in the epilogue from sums of
-// squares gathered while the token tiles are staged.
+// Work unit = one wave: 32 weight rows (two 16-row MFMA tiles) x up to 64
+// tokens x one split of K.  The unit streams its weight rows straight from HBM
+// into registers with a rolling prefetch and reads the (small, L2-resident)
+// token rows directly as MFMA B operands: no LDS staging, no barriers, so the
+// four waves of a workgroup run independently and keep memory busy.
+//
+// The two tiles of a unit are chosen so that every epilogue is lane-local:
+//   QKV     tile 0 = rotation-pair firsts, tile 1 = their partners (i + hd/2):
+//           RMSNorm scale, RoPE, q to a staging buffer, k/v appended to caches
+//   SWIGLU  tile 0 = gate rows, tile 1 = the matching up rows: silu(g) * u
+//   RESID   + residual (O and down projections)
+//   LOGITS  fp32 logits and per-(32 rows, token) softmax statistics
+// RMSNorm only needs a per-token scale r_t = 1/sqrt(mean(x^2) + eps):
+// (r_t x) W = r_t (x W), so it is applied in the epilogue from sums of squares
+// of the token operand the unit already loads.
+//
+// K splits: when there are too few row groups to occupy the chip, units also
+// split K.  Each split stores its fp32 partial tile with device-scope (sc1)
+// stores, waits for them to complete and bumps a per-tile counter; the split
+// that arrives last reads the partials back with device-scope loads, adds
+// them in split order (bitwise repeatable) and runs the epilogue.  No
+// cache-wide fence is involved.
 #include "sv_common.h"
 
 namespace sv {
@@ -26,37 +33,31 @@ namespace sv {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRowsPerBlock = 64;
-constexpr int kYStride = 65;        // fp32 epilogue tile row stride (tokens x rows)
-constexpr int kStageBytes = 32768;  // LDS bytes for one staged token sub-chunk
+constexpr int kWaves = kThreads / 64;
+constexpr float kLog2e = 1.4426950408889634f;
 
-// Raw per-lane payload of one K step.
-template <int WT> struct Step;
-template <> struct Step<WT_BF16> { uint4 v[2]; };
-template <> struct Step<WT_F32> { uint4 v[4]; };
-template <> struct Step<WT_INT4> { uint4 v; uint32_t s; };
+// Raw per-lane payload of one K step for one 16-row tile.
+template <int WT> struct WStep;
+template <> struct WStep<WT_BF16> { uint4 v[2]; };
+template <> struct WStep<WT_F32> { uint4 v[4]; };
+template <> struct WStep<WT_INT4> { uint4 v; uint32_t s; };
 
 template <int WT> constexpr int kstep() { return WT == WT_INT4 ? 128 : 64; }
-template <int WT> constexpr int prefetch() { return WT == WT_F32 ? 2 : 4; }
-// K steps per staged token sub-chunk: about kStageBytes of LDS, rounded down
-// to whole prefetch groups (at least one group).
-template <int WT, int TT> constexpr int stage_steps() {
-  constexpr int raw = kStageBytes / (TT * 16 * 2 * kstep<WT>());
-  return raw < prefetch<WT>() ? prefetch<WT>() : raw / prefetch<WT>() * prefetch<WT>();
-}
-template <int WT, int TT> constexpr int x_lds_bytes() {
-  return TT * 16 * 2 * kstep<WT>() * stage_steps<WT, TT>();
-}
 
-// Lane (row, gq) of step ks covers reduction indices ks*KS + (KS/4)*gq + [0, KS/4).
+// Lane (row, gq) of step ks holds, for MFMA m, reduction indices
+//   bf16 : ks*64  + 32m + 8gq + [0, 8)      (each instruction: 64 contiguous
+//          bytes per row across the four lane groups)
+//   int4 : ks*128 + 32gq + 8m + [0, 8)      (one 16-byte load per lane)
+//   fp32 : ks*64  + 16gq + 8m + [0, 8)
+// and the token operand holds the same indices for its token.
 template <int WT>
-__device__ __forceinline__ Step<WT> load_step(const void *w, const uint16_t *sc, int row, int K,
-                                              int ks, int gq) {
-  Step<WT> r;
+__device__ __forceinline__ WStep<WT> load_w(const void *w, const uint16_t *sc, int row, int K, int ks,
+                                           int gq) {
+  WStep<WT> r;
   if constexpr (WT == WT_BF16) {
-    const uint16_t *b = static_cast<const uint16_t *>(w) + (size_t)row * K + ks * 64 + 16 * gq;
+    const uint16_t *b = static_cast<const uint16_t *>(w) + (size_t)row * K + ks * 64 + 8 * gq;
     r.v[0] = *reinterpret_cast<const uint4 *>(b);
-    r.v[1] = *reinterpret_cast<const uint4 *>(b + 8);
+    r.v[1] = *reinterpret_cast<const uint4 *>(b + 32);
   } else if constexpr (WT == WT_F32) {
     const float *b = static_cast<const float *>(w) + (size_t)row * K + ks * 64 + 16 * gq;
 #pragma unroll
@@ -69,20 +70,39 @@ __device__ __forceinline__ Step<WT> load_step(const void *w, const uint16_t *sc,
   return r;
 }
 
+// Token operand of one step: lane (token, gq) holds the step's reduction
+// indices in the same order as the weight operand (KS/4 bf16 values).
+template <int WT> struct XStep;
+template <> struct XStep<WT_BF16> { uint4 v[2]; };
+template <> struct XStep<WT_F32> { uint4 v[2]; };
+template <> struct XStep<WT_INT4> { uint4 v[4]; };
+
+template <int WT>
+__device__ __forceinline__ XStep<WT> load_x(const uint16_t *xrow, int ks, int gq) {
+  XStep<WT> r;
+  if constexpr (WT == WT_BF16) {
+    const uint16_t *b = xrow + ks * 64 + 8 * gq;
+    r.v[0] = *reinterpret_cast<const uint4 *>(b);
+    r.v[1] = *reinterpret_cast<const uint4 *>(b + 32);
+  } else {
+    constexpr int KS = kstep<WT>();
+    const uint16_t *b = xrow + ks * KS + (KS / 4) * gq;
+#pragma unroll
+    for (int i = 0; i < (KS / 32); ++i) r.v[i] = *reinterpret_cast<const uint4 *>(b + 8 * i);
+  }
+  return r;
+}
+
 // int4 word (8 codes, offset by 8) times the group scale, to bf16.
 __device__ __forceinline__ bf16x8 dequant8(uint32_t word, float s) {
-  uint4 o;
   uint32_t h[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const float v = static_cast<float>(static_cast<int>((word >> (4 * e)) & 15u) - 8) * s;
     h[e] = f2bf(v);
   }
-  o.x = h[0] | (h[1] << 16);
-  o.y = h[2] | (h[3] << 16);
-  o.z = h[4] | (h[5] << 16);
-  o.w = h[6] | (h[7] << 16);
-  return as_bf16x8(o);
+  return as_bf16x8(uint4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                         h[6] | (h[7] << 16)});
 }
 
 // fp32 x8 -> (hi, lo) bf16 pairs with hi + lo == v to about 2^-17 relative.
@@ -96,28 +116,40 @@ __device__ __forceinline__ void split8(const uint4 &a, const uint4 &b, bf16x8 &h
     h[e] = f2bf(f[e]);
     l[e] = f2bf(f[e] - bf2f(static_cast<uint16_t>(h[e])));
   }
-  uint4 ho{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-  uint4 lw{l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16)};
-  hi = as_bf16x8(ho);
-  lo = as_bf16x8(lw);
+  hi = as_bf16x8(uint4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)});
+  lo = as_bf16x8(uint4{l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16)});
 }
 
-// Logical row lr of block blk -> (matrix, physical row).  False past the end.
-__device__ __forceinline__ bool map_row(const GemmParams &p, int blk, int lr, int &m, int &pr) {
+__device__ __forceinline__ float sumsq8(const uint4 &v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = __uint_as_float(w[i] << 16), b = __uint_as_float(w[i] & 0xFFFF0000u);
+    s += a * a;
+    s += b * b;
+  }
+  return s;
+}
+
+// Physical (matrix, row) of row r of tile `tile` in 32-row group g.
+// Returns false past the end of the matrix (the lane then streams row 0 and
+// its results are dropped).
+__device__ __forceinline__ bool map_row(const GemmParams &p, int g, int tile, int r, int &m, int &pr) {
+  int n;
   if (p.rowmap == RM_SWIGLU) {
-    const int f = blk * 32 + (lr & 31);
+    const int f = g * 16 + r;
     if (f >= p.mat[0].rows) return false;
-    m = lr < 32 ? 0 : 1;
+    m = tile;
     pr = f;
     return true;
   }
-  int n;
   if (p.rowmap == RM_ROPE_PAIRS) {
-    const int bph = p.hd / 64;
-    const int head = blk / bph, hb = blk - head * bph;
-    n = head * p.hd + (lr < 32 ? 32 * hb + lr : p.hd / 2 + 32 * hb + lr - 32);
+    const int gph = p.hd / 32;  // groups per head
+    const int head = g / gph, c = g - head * gph;
+    n = head * p.hd + tile * (p.hd / 2) + 16 * c + r;
   } else {
-    n = blk * kRowsPerBlock + lr;
+    n = g * 32 + tile * 16 + r;
   }
   if (n >= p.N) return false;
   int k = 0;
@@ -130,275 +162,327 @@ __device__ __forceinline__ bool map_row(const GemmParams &p, int blk, int lr, in
   return true;
 }
 
-// Swizzled LDS offset (elements) of the 16-byte chunk holding column c of row r.
-__device__ __forceinline__ int xs_off(int r, int c, int cols) {
-  const int chunk = (c >> 3) ^ (r & 7);
-  return r * cols + (chunk << 3) + (c & 7);
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-
-// Bijective remap of the dispatch index so that consecutive logical tiles run
-// on the same XCD (dispatch is round-robin over the 8 XCDs).
+// Bijective remap of the dispatch index so that consecutive logical
+// workgroups run on the same XCD (dispatch is round-robin over the 8 XCDs).
 __device__ __forceinline__ int xcd_remap(int wg, int nwg) {
   const int q = nwg / 8, r = nwg % 8;
   const int x = wg % 8, k = wg / 8;
   return x * q + min(x, r) + k;
 }
 
+__device__ __forceinline__ void store_dev(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_dev(const float *p) {
+  return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// wait until this wave's outstanding vector memory operations have completed
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Sequence and position of stacked token t (each lane passes its own t).
+// The token map is the prefix sum of gamma_i + 1, built 64 sequences at a
+// time with a wave scan; the owner of t is the last sequence starting <= t.
+__device__ inline void token_pos(const GemmParams &p, int t, int lane, int &seq, int &pos) {
+  int base = 0, found = 0, fstart = 0;
+  for (int c0 = 0; c0 < p.B; c0 += 64) {
+    const int i = c0 + lane;
+    const int v = i < p.B ? p.gamma[i] + 1 : 0;
+    int inc = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(inc, o);
+      if (lane >= o) inc += y;
+    }
+    const int start = base + inc - v;
+    const int n = min(64, p.B - c0);
+    for (int j = 0; j < n; ++j) {
+      const int sj = __shfl(start, j);
+      if (sj <= t) {
+        found = c0 + j;
+        fstart = sj;
+      }
+    }
+    base += __shfl(inc, 63);
+  }
+  seq = found;
+  pos = p.kv_len[seq] + (t - fstart);
+}
+
 template <int WT, int TT>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  constexpr int KS = kstep<WT>();
-  constexpr int NTOK = TT * 16;
-  constexpr int SS = stage_steps<WT, TT>();           // steps per staged sub-chunk
-  constexpr int SCOLS = SS * KS;                      // staged columns
-  constexpr int P = prefetch<WT>();                   // weight prefetch depth (steps)
-  static_assert(SS >= 1 && SS % P == 0, "stage must hold whole prefetch groups");
+  constexpr int MPS = WT == WT_BF16 ? 2 : 4;      // MFMAs per step per tile pair member
+  constexpr int P = TT <= 2 ? 4 : 3;              // prefetch depth in K steps
 
-  __shared__ float ss4[256];
-  __shared__ float ssv[64];
-  __shared__ int flag;
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int gq = lane >> 4, l16 = lane & 15;
-  const int nwg = gridDim.x;
-  int lid = xcd_remap(blockIdx.x, nwg);
-  const int tb = lid % p.ntblk;
-  lid /= p.ntblk;
-  const int split = lid % p.splits;
-  const int blk = lid / p.splits;
-  const int t0 = tb * NTOK;
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int unit = wg * kWaves + wave;
+  const int ngrp = p.nblk;
+  const int nunits = ngrp * p.splits * p.ntblk;
+  if (unit >= nunits) return;
+  const int grp = unit % ngrp;
+  const int rest = unit / ngrp;
+  const int split = rest % p.splits;
+  const int tb = rest / p.splits;
+  const int t0 = tb * TT * 16;
   const int s0 = (int)((long long)split * p.ksteps / p.splits);
   const int s1 = (int)((long long)(split + 1) * p.ksteps / p.splits);
   const int nsteps = s1 - s0;
 
-  // This lane's weight row (loads); out-of-range rows read row 0 and are dropped.
-  int mi = 0, pr = 0;
-  if (!map_row(p, blk, wave * 16 + l16, mi, pr)) { mi = 0; pr = 0; }
-  const void *wbase = p.mat[mi].w;
-  const uint16_t *sbase = p.mat[mi].s;
-
-  floatx4 acc[TT];
+  // weight rows this lane streams (one per tile)
+  const void *wb[2];
+  const uint16_t *sb[2];
+  int prow[2];
 #pragma unroll
-  for (int i = 0; i < TT; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  Step<WT> buf[P];
-  if (nsteps > 0) {
+  for (int tile = 0; tile < 2; ++tile) {
+    int mi = 0, pr = 0;
+    if (!map_row(p, grp, tile, l16, mi, pr)) { mi = 0; pr = 0; }
+    wb[tile] = p.mat[mi].w;
+    sb[tile] = p.mat[mi].s;
+    prow[tile] = pr;
+  }
+  // token rows this lane reads (clamped; results of padding tokens are dropped)
+  const uint16_t *xr[TT];
 #pragma unroll
-    for (int j = 0; j < P; ++j) buf[j] = load_step<WT>(wbase, sbase, pr, p.K, s0 + min(j, nsteps - 1), gq);
+  for (int tt = 0; tt < TT; ++tt) xr[tt] = p.x + (size_t)min(t0 + tt * 16 + l16, p.T - 1) * p.K;
+
+  floatx4 acc[2][TT];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) acc[a][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float ss[TT];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) ss[tt] = 0.f;
+
+  WStep<WT> wbuf[P][2];
+  XStep<WT> xbuf[P][TT];
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    const int st = s0 + min(j, nsteps - 1);
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile) wbuf[j][tile] = load_w<WT>(wb[tile], sb[tile], prow[tile], p.K, st, gq);
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) xbuf[j][tt] = load_x<WT>(xr[tt], st, gq);
   }
 
-  uint16_t *xs = reinterpret_cast<uint16_t *>(smem);
-  float ssum = 0.f;  // this thread's share of one token row's sum of squares
-  const int ss_row = tid >> 2, ss_part = tid & 3;
-
-  for (int st0 = 0; st0 < nsteps; st0 += SS) {
-    const int nst = min(SS, nsteps - st0);
-    const int cols = nst * KS;
-    __syncthreads();
-    // stage X[t0 .. t0+NTOK)[ (s0+st0)*KS .. + cols ) into LDS (zero past T)
-    const int cpr = cols / 8;
-    for (int idx = tid; idx < NTOK * cpr; idx += kThreads) {
-      const int r = idx / cpr, c8 = idx - r * cpr;
-      uint4 v{0u, 0u, 0u, 0u};
-      if (t0 + r < p.T)
-        v = *reinterpret_cast<const uint4 *>(p.x + (size_t)(t0 + r) * p.K + (s0 + st0) * KS + c8 * 8);
-      *reinterpret_cast<uint4 *>(xs + xs_off(r, c8 * 8, SCOLS)) = v;
-    }
-    __syncthreads();
-    if (p.norm && ss_row < NTOK) {
-      const int q4 = cols / 4;
-      float s = 0.f;
-      for (int c = ss_part * q4; c < (ss_part + 1) * q4; ++c) {
-        const float f = bf2f(xs[xs_off(ss_row, c, SCOLS)]);
-        s += f * f;
-      }
-      ssum += s;
-    }
-    // K loop over the staged columns with a rolling prefetch of P weight steps.
-    for (int b = 0; b < nst; b += P) {
+  for (int base = 0; base < nsteps; base += P) {
 #pragma unroll
-      for (int j = 0; j < P; ++j) {
-        const int st = st0 + b + j;
-        if (b + j < nst) {
-          const int cbase = (b + j) * KS + (KS / 4) * gq;
+    for (int j = 0; j < P; ++j) {
+      if (base + j < nsteps) {
 #pragma unroll
-          for (int tt = 0; tt < TT; ++tt) {
-            const int r = tt * 16 + l16;
+        for (int tt = 0; tt < TT; ++tt) {
+          if (p.norm) {
+#pragma unroll
+            for (int i = 0; i < (kstep<WT>() / 32); ++i) ss[tt] += sumsq8(xbuf[j][tt].v[i]);
+          }
+#pragma unroll
+          for (int tile = 0; tile < 2; ++tile) {
             if constexpr (WT == WT_BF16) {
 #pragma unroll
-              for (int m = 0; m < 2; ++m) {
-                const bf16x8 bx = as_bf16x8(*reinterpret_cast<const uint4 *>(xs + xs_off(r, cbase + 8 * m, SCOLS)));
-                acc[tt] = mfma16x16x32(as_bf16x8(buf[j].v[m]), bx, acc[tt]);
-              }
+              for (int m = 0; m < 2; ++m)
+                acc[tile][tt] = mfma16x16x32(as_bf16x8(wbuf[j][tile].v[m]), as_bf16x8(xbuf[j][tt].v[m]), acc[tile][tt]);
             } else if constexpr (WT == WT_INT4) {
-              const float s = bf2f(static_cast<uint16_t>(buf[j].s));
-              const uint32_t wv[4] = {buf[j].v.x, buf[j].v.y, buf[j].v.z, buf[j].v.w};
+              const float s = bf2f(static_cast<uint16_t>(wbuf[j][tile].s));
+              const uint32_t wv[4] = {wbuf[j][tile].v.x, wbuf[j][tile].v.y, wbuf[j][tile].v.z, wbuf[j][tile].v.w};
 #pragma unroll
-              for (int m = 0; m < 4; ++m) {
-                const bf16x8 bx = as_bf16x8(*reinterpret_cast<const uint4 *>(xs + xs_off(r, cbase + 8 * m, SCOLS)));
-                acc[tt] = mfma16x16x32(dequant8(wv[m], s), bx, acc[tt]);
-              }
+              for (int m = 0; m < 4; ++m)
+                acc[tile][tt] = mfma16x16x32(dequant8(wv[m], s), as_bf16x8(xbuf[j][tt].v[m]), acc[tile][tt]);
             } else {
 #pragma unroll
               for (int m = 0; m < 2; ++m) {
-                const bf16x8 bx = as_bf16x8(*reinterpret_cast<const uint4 *>(xs + xs_off(r, cbase + 8 * m, SCOLS)));
                 bf16x8 hi, lo;
-                split8(buf[j].v[2 * m], buf[j].v[2 * m + 1], hi, lo);
-                acc[tt] = mfma16x16x32(hi, bx, acc[tt]);
-                acc[tt] = mfma16x16x32(lo, bx, acc[tt]);
+                split8(wbuf[j][tile].v[2 * m], wbuf[j][tile].v[2 * m + 1], hi, lo);
+                acc[tile][tt] = mfma16x16x32(hi, as_bf16x8(xbuf[j][tt].v[m]), acc[tile][tt]);
+                acc[tile][tt] = mfma16x16x32(lo, as_bf16x8(xbuf[j][tt].v[m]), acc[tile][tt]);
               }
             }
           }
         }
-        buf[j] = load_step<WT>(wbase, sbase, pr, p.K, s0 + min(st + P, nsteps - 1), gq);
+      }
+      const int nx = s0 + min(base + j + P, nsteps - 1);
+#pragma unroll
+      for (int tile = 0; tile < 2; ++tile) wbuf[j][tile] = load_w<WT>(wb[tile], sb[tile], prow[tile], p.K, nx, gq);
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) xbuf[j][tt] = load_x<WT>(xr[tt], nx, gq);
+    }
+  }
+  (void)MPS;
+
+  // sums of squares of this split's token slices: add the four lane groups
+  if (p.norm) {
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      ss[tt] += __shfl_xor(ss[tt], 16);
+      ss[tt] += __shfl_xor(ss[tt], 32);
+    }
+  }
+
+  // ---- K-split reduction ----------------------------------------------------
+  if (p.splits > 1) {
+    constexpr int TILE = 2 * TT * 4 * 64 + TT * 64;  // partial values + sums of squares
+    const size_t tile_id = (size_t)tb * ngrp + grp;
+    float *mine = p.partial + ((size_t)split * ngrp * p.ntblk + tile_id) * TILE;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) store_dev(mine + ((a * TT + tt) * 4 + i) * 64 + lane, acc[a][tt][i]);
+    if (p.norm) {
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) store_dev(mine + 2 * TT * 4 * 64 + tt * 64 + lane, ss[tt]);
+    }
+    wait_vmem();
+    int old = 0;
+    if (lane == 0)
+      old = __hip_atomic_fetch_add(p.counters + tile_id, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __shfl(old, 0);
+    if (old != p.splits - 1) return;
+    if (lane == 0) __hip_atomic_store(p.counters + tile_id, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) acc[a][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) ss[tt] = 0.f;
+    for (int sp = 0; sp < p.splits; ++sp) {
+      const float *src = p.partial + ((size_t)sp * ngrp * p.ntblk + tile_id) * TILE;
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[a][tt][i] += load_dev(src + ((a * TT + tt) * 4 + i) * 64 + lane);
+      if (p.norm) {
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) ss[tt] += load_dev(src + 2 * TT * 4 * 64 + tt * 64 + lane);
       }
     }
   }
-  __syncthreads();
 
-  // ---- gather this split's tile into LDS: Y[t][lr] -------------------------
-  float *ys = reinterpret_cast<float *>(smem);
+  // per-token RMSNorm scale (lane's token is t0 + tt*16 + l16)
+  float rs[TT];
 #pragma unroll
-  for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ys[(tt * 16 + l16) * kYStride + wave * 16 + 4 * gq + i] = acc[tt][i];
-  if (p.norm) {
-    ss4[tid] = ssum;
-    __syncthreads();
-    if (tid < NTOK) ssv[tid] = ((ss4[4 * tid] + ss4[4 * tid + 1]) + ss4[4 * tid + 2]) + ss4[4 * tid + 3];
-  }
-  __syncthreads();
+  for (int tt = 0; tt < TT; ++tt) rs[tt] = p.norm ? 1.f / sqrtf(ss[tt] / static_cast<float>(p.K) + p.eps) : 1.f;
 
-  if (p.splits > 1) {
-    const size_t tile = (size_t)NTOK * kRowsPerBlock;
-    float *mine = p.partial + (((size_t)split * p.nblk + blk) * p.ntblk + tb) * tile;
-    for (int idx = tid; idx < NTOK * kRowsPerBlock; idx += kThreads)
-      mine[idx] = ys[(idx >> 6) * kYStride + (idx & 63)];
-    if (p.norm && tid < NTOK)
-      p.part_ss[(((size_t)blk * p.splits + split) * p.ntblk + tb) * 64 + tid] = ssv[tid];
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-      int *ctr = p.counters + (size_t)blk * p.ntblk + tb;
-      const int old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-      flag = (old == p.splits - 1);
-      if (flag) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    if (!flag) return;
-    __threadfence();
-    for (int idx = tid; idx < NTOK * kRowsPerBlock; idx += kThreads) {
-      float s = 0.f;
-      for (int sp = 0; sp < p.splits; ++sp)
-        s += __builtin_nontemporal_load(p.partial + (((size_t)sp * p.nblk + blk) * p.ntblk + tb) * tile + idx);
-      ys[(idx >> 6) * kYStride + (idx & 63)] = s;
-    }
-    if (p.norm && tid < NTOK) {
-      float s = 0.f;
-      for (int sp = 0; sp < p.splits; ++sp)
-        s += __builtin_nontemporal_load(p.part_ss + (((size_t)blk * p.splits + sp) * p.ntblk + tb) * 64 + tid);
-      ssv[tid] = s;
-    }
-    __syncthreads();
-  }
-
-  // per-token RMSNorm scale
-  if (tid < NTOK) {
-    float r = 1.f;
-    if (p.norm) r = 1.f / sqrtf(ssv[tid] / static_cast<float>(p.K) + p.eps);
-    ss4[tid] = r;
-  }
-  __syncthreads();
-  const float *rt = ss4;
-
-  // ---- fused epilogues ------------------------------------------------------
+  // ---- fused epilogues (lane-local) -----------------------------------------
   if (p.epi == EPI_RESID) {
     uint16_t *out = static_cast<uint16_t *>(p.out);
-    for (int idx = tid; idx < NTOK * kRowsPerBlock; idx += kThreads) {
-      const int t = idx >> 6, lr = idx & 63, n = blk * kRowsPerBlock + lr;
-      if (t0 + t < p.T && n < p.N) {
-        const size_t o = (size_t)(t0 + t) * p.ldo + n;
-        out[o] = f2bf(ys[t * kYStride + lr] * rt[t] + bf2f(p.resid[o]));
-      }
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      const int t = t0 + tt * 16 + l16;
+      if (t >= p.T) continue;
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int n = grp * 32 + a * 16 + 4 * gq + i;
+          if (n < p.N) {
+            const size_t o = (size_t)t * p.ldo + n;
+            out[o] = f2bf(acc[a][tt][i] * rs[tt] + bf2f(p.resid[o]));
+          }
+        }
     }
   } else if (p.epi == EPI_SWIGLU) {
     uint16_t *out = static_cast<uint16_t *>(p.out);
-    for (int idx = tid; idx < NTOK * 32; idx += kThreads) {
-      const int t = idx >> 5, lr = idx & 31, f = blk * 32 + lr;
-      if (t0 + t < p.T && f < p.mat[0].rows) {
-        const float g = ys[t * kYStride + lr] * rt[t];
-        const float u = ys[t * kYStride + lr + 32] * rt[t];
-        const float sig = 1.f / (1.f + __builtin_amdgcn_exp2f(-g * 1.4426950408889634f));
-        out[(size_t)(t0 + t) * p.ldo + f] = f2bf(g * sig * u);
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      const int t = t0 + tt * 16 + l16;
+      if (t >= p.T) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int f = grp * 16 + 4 * gq + i;
+        if (f < p.mat[0].rows) {
+          const float g = acc[0][tt][i] * rs[tt], u = acc[1][tt][i] * rs[tt];
+          const float sig = 1.f / (1.f + __builtin_amdgcn_exp2f(-g * kLog2e));
+          out[(size_t)t * p.ldo + f] = f2bf(g * sig * u);
+        }
       }
     }
   } else if (p.epi == EPI_LOGITS) {
     float *out = static_cast<float *>(p.out);
-    const int n = blk * kRowsPerBlock + lane;
-    const bool valid = n < p.N;
-    for (int t = wave; t < NTOK; t += 4) {
-      if (t0 + t >= p.T) break;
-      const float v = ys[t * kYStride + lane] * rt[t];
-      if (valid) out[(size_t)(t0 + t) * p.ldo + n] = v;
-      const float m = wave_max(valid ? v : -INFINITY);
-      const float e = valid ? __builtin_amdgcn_exp2f((v - m) * 1.4426950408889634f) : 0.f;
-      const float s = wave_sum(e);
-      if (lane == 0) {
-        float *st = p.stats + ((size_t)blk * p.T + t0 + t) * 2;
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      const int t = t0 + tt * 16 + l16;
+      float v[8];
+      float m = -INFINITY;
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int n = grp * 32 + a * 16 + 4 * gq + i;
+          v[a * 4 + i] = n < p.N ? acc[a][tt][i] * rs[tt] : -INFINITY;
+          m = fmaxf(m, v[a * 4 + i]);
+          if (t < p.T && n < p.N) out[(size_t)t * p.ldo + n] = v[a * 4 + i];
+        }
+      m = fmaxf(m, __shfl_xor(m, 16));
+      m = fmaxf(m, __shfl_xor(m, 32));
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += __builtin_amdgcn_exp2f((v[e] - m) * kLog2e);
+      s += __shfl_xor(s, 16);
+      s += __shfl_xor(s, 32);
+      if (gq == 0 && t < p.T) {
+        float *st = p.stats + ((size_t)grp * p.T + t) * 2;
         st[0] = m;
         st[1] = s;
       }
     }
-  } else {  // EPI_QKV
-    int *gam = reinterpret_cast<int *>(smem + NTOK * kYStride * sizeof(float));
-    int *tmp = gam + (p.B + 1);
-    for (int i = tid; i < p.B; i += kThreads) gam[i] = p.gamma[i] + 1;
-    __syncthreads();
-    block_exscan(gam, p.B, tmp);
-    const int bph = p.hd / 64;
-    const int head = blk / bph, hb = blk - head * bph;
+  } else {  // EPI_QKV: tile 0 holds pair firsts i, tile 1 the partners i + hd/2
+    const int gph = p.hd / 32;
+    const int head = grp / gph, c = grp - head * gph;
     const int half = p.hd / 2;
-    for (int idx = tid; idx < NTOK * 32; idx += kThreads) {
-      const int t = idx >> 5, lr = idx & 31;
-      const int tg = t0 + t;
-      if (tg >= p.T) continue;
-      const int seq = upper_index(gam, p.B, tg);
-      const int pos = p.kv_len[seq] + (tg - gam[seq]);
-      const int i = 32 * hb + lr;  // rotation pair (i, i + hd/2)
-      const float a = ys[t * kYStride + lr] * rt[t];
-      const float b = ys[t * kYStride + lr + 32] * rt[t];
-      if (head < p.hq + p.hkv) {
-        const double inv = pow(static_cast<double>(p.rope_theta), -2.0 * i / p.hd);
-        double sn, cs;
-        sincos(static_cast<double>(pos) * inv, &sn, &cs);
-        const float c = static_cast<float>(cs), s = static_cast<float>(sn);
-        const float ra = a * c - b * s, rb = b * c + a * s;
-        if (head < p.hq) {
-          uint16_t *q = p.qbuf + ((size_t)tg * p.hq + head) * p.hd;
-          q[i] = f2bf(ra);
-          q[i + half] = f2bf(rb);
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      const int t = t0 + tt * 16 + l16;
+      int seq = 0, pos = 0;
+      token_pos(p, min(t, p.T - 1), lane, seq, pos);
+      if (t >= p.T) continue;
+      const bool kv_ok = pos >= 0 && pos < p.kv_cap;
+      if (head >= p.hq && !kv_ok) {
+        set_err(p.err, SV_DEV_ERR_KV_OVERFLOW);
+        continue;
+      }
+      float ra[4], rb[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int fi = 16 * c + 4 * gq + e;  // rotation pair (fi, fi + hd/2)
+        const float a = acc[0][tt][e] * rs[tt], b = acc[1][tt][e] * rs[tt];
+        if (head < p.hq + p.hkv) {
+          const double inv = pow(static_cast<double>(p.rope_theta), -2.0 * fi / p.hd);
+          double sn, cs;
+          sincos(static_cast<double>(pos) * inv, &sn, &cs);
+          const float cf = static_cast<float>(cs), sf = static_cast<float>(sn);
+          ra[e] = a * cf - b * sf;
+          rb[e] = b * cf + a * sf;
         } else {
-          if (pos >= p.kv_cap || pos < 0) { set_err(p.err, SV_DEV_ERR_KV_OVERFLOW); continue; }
-          uint16_t *k = static_cast<uint16_t *>(p.kc[seq]) + ((size_t)(head - p.hq) * p.kv_cap + pos) * p.hd;
-          k[i] = f2bf(ra);
-          k[i + half] = f2bf(rb);
+          ra[e] = a;
+          rb[e] = b;
+        }
+      }
+      const int fi0 = 16 * c + 4 * gq;
+      if (head < p.hq) {
+        uint16_t *q = p.qbuf + ((size_t)t * p.hq + head) * p.hd;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          q[fi0 + e] = f2bf(ra[e]);
+          q[fi0 + half + e] = f2bf(rb[e]);
+        }
+      } else if (head < p.hq + p.hkv) {
+        uint16_t *k = static_cast<uint16_t *>(p.kc[seq]) + ((size_t)(head - p.hq) * p.kv_cap + pos) * p.hd;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          k[fi0 + e] = f2bf(ra[e]);
+          k[fi0 + half + e] = f2bf(rb[e]);
         }
       } else {
-        if (pos >= p.kv_cap || pos < 0) { set_err(p.err, SV_DEV_ERR_KV_OVERFLOW); continue; }
         uint16_t *v = static_cast<uint16_t *>(p.vc[seq]) + (size_t)(head - p.hq - p.hkv) * p.hd * p.kv_cap;
-        v[(size_t)i * p.kv_cap + pos] = f2bf(a);
-        v[(size_t)(i + half) * p.kv_cap + pos] = f2bf(b);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[(size_t)(fi0 + e) * p.kv_cap + pos] = f2bf(ra[e]);
+          v[(size_t)(fi0 + half + e) * p.kv_cap + pos] = f2bf(rb[e]);
+        }
       }
     }
   }
@@ -406,17 +490,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
 
 template <int WT, int TT>
 hipError_t launch_tt(const GemmParams &p, hipStream_t s, int trace_class) {
-  const int nwg = p.nblk * p.splits * p.ntblk;
-  size_t lds = x_lds_bytes<WT, TT>();
-  const size_t ylds = (size_t)TT * 16 * kYStride * sizeof(float);
-  size_t need = ylds + (p.epi == EPI_QKV ? (size_t)(p.B + 1 + 257) * sizeof(int) : 0);
-  if (need > lds) lds = need;
-  if (lds > 65536) {
-    hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_kernel<WT, TT>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  }
+  const int nunits = p.nblk * p.splits * p.ntblk;
+  const int nwg = (nunits + kWaves - 1) / kWaves;
   trace_before(trace_class, s);
-  hipLaunchKernelGGL((gemm_kernel<WT, TT>), dim3(nwg), dim3(kThreads), lds, s, p);
+  hipLaunchKernelGGL((gemm_kernel<WT, TT>), dim3(nwg), dim3(kThreads), 0, s, p);
   trace_after(trace_class, s);
   return hipGetLastError();
 }
@@ -438,6 +515,11 @@ hipError_t launch_gemm(const GemmParams &p, int wtype, int tok_tiles, hipStream_
   if (wtype == WT_BF16) return launch_wt<WT_BF16>(p, tok_tiles, s, trace_class);
   if (wtype == WT_INT4) return launch_wt<WT_INT4>(p, tok_tiles, s, trace_class);
   return launch_wt<WT_F32>(p, tok_tiles, s, trace_class);
+}
+
+size_t gemm_partial_floats(int ngroups, int splits, int ntblk, int tok_tiles) {
+  if (splits <= 1) return 0;
+  return (size_t)splits * ngroups * ntblk * (2 * tok_tiles * 4 * 64 + tok_tiles * 64);
 }
 
 }  // namespace sv
