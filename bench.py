@@ -139,11 +139,12 @@ def main():
     xh = hidden_states(wl.T, sh.d, wl.seed)
     log(f"generated inputs in {time.perf_counter() - t0:.1f} s")
 
-    mats = {k: tg.upload_matrix(v) for k, v in W.items()}
-    lm = tg.upload_matrix(Wlm) if Wlm is not None else None
+    packed = wl.wtype != "f32"
+    mats = {k: tg.upload_matrix(v, packed=packed) for k, v in W.items()}
+    lm = tg.upload_matrix(Wlm, packed=packed) if Wlm is not None else None
     batch = tg.DeviceBatch(wl.gamma, wl.ctx, wl.cap, kcache=kc, vcache=vc)
     bs = batch.struct()
-    Ld = tg.decoder_struct(sh, wl.wtype, mats)
+    Ld = tg.decoder_struct(sh, wl.wtype, mats, packed=packed)
     nd = sv.sv_verify_layer_workspace_bytes(Ld, bs)
     ws_d = tg.workspace(nd)
     x = tg.to_dev(xh)
@@ -151,7 +152,7 @@ def main():
     V = sh.vocab
     stream = tg.stream_handle()
     if lm is not None:
-        Lh = tg.head_struct(sh, wl.wtype, lm)
+        Lh = tg.head_struct(sh, wl.wtype, lm, packed=packed)
         nh = sv.sv_verify_layer_workspace_bytes(Lh, bs)
         nhl = sv.sv_verify_layer_workspace_bytes(Lh, bs, sv.SV_HEAD_LOGITS)
         ws_h = tg.workspace(max(nh, nhl))
@@ -246,7 +247,7 @@ def main():
                  sv.SV_K_ATTN_MERGE: "attn_merge", sv.SV_K_GEMM_O: "gemm_o",
                  sv.SV_K_GEMM_GATE_UP: "gemm_gate_up", sv.SV_K_GEMM_DOWN: "gemm_down",
                  sv.SV_K_GEMM_LM_HEAD: "gemm_lm_head", sv.SV_K_SOFTMAX: "softmax",
-                 sv.SV_K_ACCEPT_SCAN: "accept_scan", sv.SV_K_ACCEPT_SELECT: "accept_select"}
+                 sv.SV_K_ACCEPT: "accept", sv.SV_K_PREP: "prep"}
         for cls, nm in names.items():
             n = 10
             assert sv.sv_trace_begin(cls, n) == 0
@@ -280,7 +281,7 @@ def main():
         "dtype": "bf16" if wl.wtype != "f32" else "f32", "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "gamma": glist if wl.B <= 16 else int(wl.gamma[0]),
                    "T": wl.T, "ctx": int(wl.ctx[0]) if len(set(wl.ctx.tolist())) == 1 else "ragged",
-                   "weights": wl.wtype, "d": sh.d, "heads": f"{sh.n_q}q/{sh.n_kv}kv x {sh.hd}",
+                   "weights": wl.wtype + (" packed" if packed else ""), "d": sh.d, "heads": f"{sh.n_q}q/{sh.n_kv}kv x {sh.hd}",
                    "ffn": sh.ffn, "vocab": V if lm is not None else None,
                    "acceptance": (wl.alphas[0] if wl.alphas else wl.draft)},
         "accepted_tok_s": round(accepted_tok_s, 2),

@@ -82,6 +82,10 @@ typedef int32_t sv_status;
                            codes in [-7, 7]; bf16 scales [N][K/32];
                            weight = code * scale */
 
+/* Weight layouts (sv_layer.layout). */
+#define SV_LAYOUT_ROWMAJOR 0 /* [N][K] as described below */
+#define SV_LAYOUT_PACKED 1   /* produced by sv_pack_matrix (bf16 and int4 only) */
+
 /* sv_verify_layer flags. */
 #define SV_HEAD_LOGITS 1 /* HEAD: write fp32 logits instead of probabilities */
 
@@ -112,6 +116,7 @@ typedef struct sv_matrix {
 typedef struct sv_layer {
   int32_t kind;
   int32_t wtype;
+  int32_t layout;     /* SV_LAYOUT_*, for every GEMM matrix of the layer */
   int32_t d;
   int32_t n_q_heads;
   int32_t n_kv_heads;
@@ -150,6 +155,25 @@ typedef struct sv_batch {
   void *const *v_cache;      /* [B] device pointers */
   int32_t *err_flag;         /* [1] nullable */
 } sv_batch;
+
+/* Packed weight layout.  The weight GEMMs read each 16-row block of a matrix
+ * as one sequential stream when it is stored fragment by fragment:
+ *   bf16: for tile t (rows 16t..16t+15), step s (k = 64s..64s+63), half m,
+ *         lane l (row 16t + l%16), the 8 values k = 64s + 32m + 8(l/16) + 0..7
+ *         are stored at element ((t * K/64 + s) * 2 + m) * 512 + l * 8;
+ *   int4: for tile t, step s (k = 128s..128s+127), lane l, the 32 codes
+ *         k = 128s + 32(l/16) + 0..31 of row 16t + l%16 (four packed words)
+ *         are stored at word ((t * K/128 + s) * 64 + l) * 4, and their group
+ *         scale at element (t * K/128 + s) * 64 + l of the scale array.
+ * Rows past N in the last tile are zero.  Packing is a one-time layout change
+ * (done when weights are loaded), not part of a verification pass. */
+sv_status sv_packed_matrix_bytes(int32_t wtype, int32_t N, int32_t K, size_t *w_bytes,
+                                 size_t *scale_bytes);
+
+/* Pack a row-major [N][K] matrix (and its int4 scales) into the packed
+ * layout on `stream`.  Destinations must not overlap the sources. */
+sv_status sv_pack_matrix(int32_t wtype, int32_t N, int32_t K, const void *w, const void *scale,
+                         void *w_packed, void *scale_packed, void *stream);
 
 /* Workspace needed by sv_verify_layer for this layer, batch and flags. */
 sv_status sv_verify_layer_workspace_bytes(const sv_layer *layer, const sv_batch *batch,
@@ -251,8 +275,8 @@ sv_status sv_plan_gamma(const sv_plan_params *params, int32_t B_live, int32_t *g
 #define SV_K_GEMM_DOWN 5
 #define SV_K_GEMM_LM_HEAD 6
 #define SV_K_SOFTMAX 7
-#define SV_K_ACCEPT_SCAN 8
-#define SV_K_ACCEPT_SELECT 9
+#define SV_K_ACCEPT 8
+#define SV_K_PREP 9
 #define SV_K_EMBED 10
 #define SV_K_COUNT 11
 

@@ -41,12 +41,12 @@ def check(st, what=""):
 class GpuDecoder:
     """One decoder layer of a workload on the device, with its caches."""
 
-    def __init__(self, wl, tag="layer0", max_ctx=None):
+    def __init__(self, wl, tag="layer0", max_ctx=None, packed=False):
         self.wl = wl
         sh = wl.shape
         self.W = layer_weights(sh, wl.wtype, wl.seed, tag)
-        self.dev = {k: tg.upload_matrix(v) for k, v in self.W.items()}
-        self.L = tg.decoder_struct(sh, wl.wtype, self.dev)
+        self.dev = {k: tg.upload_matrix(v, packed=packed) for k, v in self.W.items()}
+        self.L = tg.decoder_struct(sh, wl.wtype, self.dev, packed=packed)
         self.kc, self.vc = kv_cache(sh, wl.ctx, wl.cap, wl.seed, tag)
         self.batch = tg.DeviceBatch(wl.gamma, wl.ctx, wl.cap, max_ctx=max_ctx, kcache=self.kc,
                                     vcache=self.vc)
@@ -66,11 +66,11 @@ class GpuDecoder:
 
 
 class GpuHead:
-    def __init__(self, wl, vocab=None):
+    def __init__(self, wl, vocab=None, packed=False):
         self.wl = wl
         self.Wlm = head_weights(wl.shape, wl.wtype, wl.seed)
-        self.dev = tg.upload_matrix(self.Wlm)
-        self.L = tg.head_struct(wl.shape, wl.wtype, self.dev)
+        self.dev = tg.upload_matrix(self.Wlm, packed=packed)
+        self.L = tg.head_struct(wl.shape, wl.wtype, self.dev, packed=packed)
         self.batch = tg.DeviceBatch(wl.gamma, wl.ctx, wl.cap)
         self.bs = self.batch.struct()
         self.ws_bytes = {f: sv.sv_verify_layer_workspace_bytes(self.L, self.bs, f)

@@ -194,3 +194,22 @@ def test_plan_rejects_bad_params():
     assert sv.sv_plan_gamma(p, 4)[0] == sv.SV_ERR_INVALID_ARG
     p = sv.make_plan_params(sv.SV_PLAN_BUDGET, 8)  # no budget and no rates
     assert sv.sv_plan_gamma(p, 4)[0] == sv.SV_ERR_INVALID_ARG
+
+
+def test_packed_sizes_and_validation():
+    assert sv.sv_packed_matrix_bytes(sv.SV_W_BF16, 100, 256) == (112 * 256 * 2, 0)
+    assert sv.sv_packed_matrix_bytes(sv.SV_W_INT4_G32, 77, 384) == (80 * 384 // 2, 80 * 12 * 2)
+    with pytest.raises(sv.SvError):
+        sv.sv_packed_matrix_bytes(sv.SV_W_F32, 16, 64)
+    with pytest.raises(sv.SvError):
+        sv.sv_packed_matrix_bytes(sv.SV_W_INT4_G32, 16, 64)    # K not a multiple of 128
+    assert sv.sv_pack_matrix(sv.SV_W_BF16, 16, 64, None, None, 0x10, None, None) == sv.SV_ERR_INVALID_ARG
+    assert sv.sv_pack_matrix(sv.SV_W_INT4_G32, 16, 128, 0x10, None, 0x20, 0x30, None) == \
+        sv.SV_ERR_INVALID_ARG
+    # an fp32 layer cannot use the packed layout; an unknown layout is rejected
+    L = _layer(wtype=sv.SV_W_F32)
+    L.layout = sv.SV_LAYOUT_PACKED
+    assert _ws(L, _batch([1]))[0] == sv.SV_ERR_UNSUPPORTED
+    L = _layer()
+    L.layout = 5
+    assert _ws(L, _batch([1]))[0] == sv.SV_ERR_INVALID_ARG

@@ -23,11 +23,15 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("name,shape,wtype,gamma,ctx", CASES, ids=[c[0] for c in CASES])
+PACKED_CASES = [(c[0] + "-packed",) + c[1:] for c in CASES if c[2] != "f32"]
+
+
+@pytest.mark.parametrize("name,shape,wtype,gamma,ctx", CASES + PACKED_CASES,
+                         ids=[c[0] for c in CASES + PACKED_CASES])
 def test_decoder_parity(name, shape, wtype, gamma, ctx):
     wl = custom_workload(shape, wtype, gamma, ctx, seed=31)
     say(f"decoder {name}: T={wl.T} B={wl.B}")
-    dec = GpuDecoder(wl)
+    dec = GpuDecoder(wl, packed=name.endswith("-packed"))
     xh = hidden_states(wl.T, shape.d, wl.seed)
     y = dec.run(tg.to_dev(xh))
     torch.cuda.synchronize()
@@ -92,11 +96,12 @@ def test_verify_equals_sequential_decodes_gpu():
         assert rel_rows(v[None], yf[r][None]) < 1e-2, r
 
 
-def test_head_parity():
+@pytest.mark.parametrize("packed", [False, True])
+def test_head_parity(packed):
     shape = Shape(512, 8, 2, 128, 1024, 5003)
     for wtype in ("bf16", "int4"):
         wl = custom_workload(shape, wtype, [2, 0, 4], [1, 1, 1], seed=12)
-        head = GpuHead(wl)
+        head = GpuHead(wl, packed=packed)
         yh = hidden_states(wl.T, shape.d, 77)
         yd = tg.to_dev(yh)
         lg = head.run(yd, logits=True).cpu().numpy()
@@ -132,6 +137,38 @@ def test_decoder_then_head_shared_workspace():
     el_own = rel_rows(lg.cpu().numpy(), OV.head_logits(head.Wlm, dev_bf16_to_f64(y)))
     say(f"chain: y {ey:.2e}  logits {el:.2e}  logits-on-gpu-y {el_own:.2e}")
     assert ey < TOL["bf16"] and el_own < TOL["bf16"] and el < TOL["bf16"]
+
+
+def _pack_reference(m):
+    """Expected packed bytes, by an independent numpy re-layout of [N][K]."""
+    n, k = m.n, m.k
+    nt = (n + 15) // 16
+    if m.wtype == "bf16":
+        w = np.zeros((nt * 16, k), np.uint16)
+        w[:n] = m.data
+        ks = k // 64   # row 16t+l, k = 64s + 32m + 8g + e  ->  [t][s][m][g*16+l][e]
+        a = w.reshape(nt, 16, ks, 2, 4, 8).transpose(0, 2, 3, 4, 1, 5)
+        return a.reshape(-1).view(np.uint8), None
+    w = np.zeros((nt * 16, k // 8), np.uint32)
+    w[:n] = m.data
+    s = np.zeros((nt * 16, k // 32), np.uint16)
+    s[:n] = m.scale
+    ks = k // 128  # word 16s + 4g + j of row 16t+l -> [t][s][g*16+l][j]
+    a = w.reshape(nt, 16, ks, 4, 4).transpose(0, 2, 3, 1, 4)
+    b = s.reshape(nt, 16, ks, 4).transpose(0, 2, 3, 1)
+    return a.reshape(-1).view(np.uint8), b.reshape(-1).view(np.uint8)
+
+
+@pytest.mark.parametrize("wtype,n,k", [("bf16", 100, 256), ("bf16", 4096, 512), ("int4", 77, 384),
+                                       ("int4", 1024, 1024)])
+def test_pack_matrix_bit_exact(wtype, n, k):
+    from workloads.gen import _matrix, rng_for
+    m = _matrix(rng_for(5, f"pack/{wtype}/{n}"), n, k, 0.05, wtype)
+    dm = tg.upload_matrix(m, packed=True)
+    want_w, want_s = _pack_reference(m)
+    np.testing.assert_array_equal(dm.w.cpu().numpy(), want_w)
+    if want_s is not None:
+        np.testing.assert_array_equal(dm.scale.cpu().numpy()[:want_s.size], want_s)
 
 
 def test_embed_and_bad_token():

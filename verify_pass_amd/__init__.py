@@ -4,7 +4,7 @@ The functions below carry the names of the C entry points declared in
 include/sv.h and only marshal arguments: every step of the verification path
 runs in the library's gfx950 kernels.  Importing this package loads the
 in-tree libsv.so and fails loudly if it has not been built
-(``python -m verify_pass_amd.build``).  torch is used by the helpers in
+(``python verify_pass_amd/csrc/build.py``).  torch is used by the helpers in
 ``verify_pass_amd.torch_glue`` for device memory and streams only.
 """
 from __future__ import annotations
@@ -28,11 +28,12 @@ SV_DEV_ERR_CTX_BOUND = 4
 SV_LAYER_EMBED, SV_LAYER_DECODER, SV_LAYER_HEAD = 0, 1, 2
 SV_W_F32, SV_W_BF16, SV_W_INT4_G32 = 0, 1, 2
 SV_HEAD_LOGITS = 1
+SV_LAYOUT_ROWMAJOR, SV_LAYOUT_PACKED = 0, 1
 SV_ACCEPT_STOCHASTIC, SV_ACCEPT_GREEDY = 0, 1
 SV_PLAN_BUDGET, SV_PLAN_SPEEDUP = 0, 1
 
 (SV_K_GEMM_QKV, SV_K_ATTENTION, SV_K_ATTN_MERGE, SV_K_GEMM_O, SV_K_GEMM_GATE_UP,
- SV_K_GEMM_DOWN, SV_K_GEMM_LM_HEAD, SV_K_SOFTMAX, SV_K_ACCEPT_SCAN, SV_K_ACCEPT_SELECT,
+ SV_K_GEMM_DOWN, SV_K_GEMM_LM_HEAD, SV_K_SOFTMAX, SV_K_ACCEPT, SV_K_PREP,
  SV_K_EMBED, SV_K_COUNT) = range(12)
 
 WTYPES = {"f32": SV_W_F32, "bf16": SV_W_BF16, "int4": SV_W_INT4_G32}
@@ -43,7 +44,7 @@ class sv_matrix(C.Structure):
 
 
 class sv_layer(C.Structure):
-    _fields_ = [("kind", C.c_int32), ("wtype", C.c_int32), ("d", C.c_int32),
+    _fields_ = [("kind", C.c_int32), ("wtype", C.c_int32), ("layout", C.c_int32), ("d", C.c_int32),
                 ("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
                 ("ffn", C.c_int32), ("vocab", C.c_int32), ("eps", C.c_float),
                 ("rope_theta", C.c_float),
@@ -80,6 +81,10 @@ _SIGNATURES = [
      [C.c_int32, C.c_int32, C.c_int32, C.POINTER(C.c_int32), C.c_void_p, C.c_void_p, C.c_void_p,
       C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
       C.c_void_p, C.c_size_t, C.c_void_p]),
+    ("sv_packed_matrix_bytes", C.c_int32,
+     [C.c_int32, C.c_int32, C.c_int32, C.POINTER(C.c_size_t), C.POINTER(C.c_size_t)]),
+    ("sv_pack_matrix", C.c_int32,
+     [C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]),
     ("sv_plan_gamma", C.c_int32,
      [C.POINTER(sv_plan_params), C.c_int32, C.POINTER(C.c_int32), C.POINTER(C.c_double)]),
     ("sv_trace_begin", C.c_int32, [C.c_int32, C.c_int32]),
@@ -97,7 +102,7 @@ class SvError(RuntimeError):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m verify_pass_amd.build` "
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python verify_pass_amd/csrc/build.py` "
                           "(the verification path has no fallback)")
     try:  # bind to the HIP runtime torch already loaded, if any
         import torch  # noqa: F401
@@ -161,6 +166,20 @@ def sv_accept_commit(B, V, mode, gamma_host, gamma, draft, p, q, u_acc, u_samp, 
                                  _ptr(u_acc), _ptr(u_samp), _ptr(kv_len), _ptr(accepted),
                                  _ptr(next_token), _ptr(err_flag), _ptr(workspace),
                                  workspace_bytes, _ptr(stream))
+
+
+def sv_packed_matrix_bytes(wtype: int, N: int, K: int):
+    """Returns (w_bytes, scale_bytes) of the packed layout."""
+    w, s = C.c_size_t(0), C.c_size_t(0)
+    st = _lib.sv_packed_matrix_bytes(wtype, N, K, C.byref(w), C.byref(s))
+    if st != SV_OK:
+        raise SvError(st, "sv_packed_matrix_bytes")
+    return w.value, s.value
+
+
+def sv_pack_matrix(wtype, N, K, w, scale, w_packed, scale_packed, stream) -> int:
+    return _lib.sv_pack_matrix(wtype, N, K, _ptr(w), _ptr(scale), _ptr(w_packed),
+                               _ptr(scale_packed), _ptr(stream))
 
 
 def sv_plan_gamma(params: sv_plan_params, B_live: int):

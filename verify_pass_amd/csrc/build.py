@@ -1,6 +1,9 @@
 """Build libsv.so (the C-ABI library) for gfx950 with hipcc, in-tree.
 
-    python -m verify_pass_amd.build [-v]
+    python verify_pass_amd/csrc/build.py [-v]
+
+Runs as a plain script (it does not import the package, whose import loads
+the library being rebuilt).
 """
 from __future__ import annotations
 
@@ -9,11 +12,11 @@ import os
 import subprocess
 import sys
 
-HERE = os.path.dirname(os.path.abspath(__file__))
-CSRC = os.path.join(HERE, "csrc")
-BUILD = os.path.join(HERE, "_build")
-LIB = os.path.join(HERE, "libsv.so")
-SOURCES = ["sv_gemm.hip", "sv_attn.hip", "sv_head.hip", "sv_accept.hip", "sv_abi.cpp",
+CSRC = os.path.dirname(os.path.abspath(__file__))
+PKG = os.path.dirname(CSRC)
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libsv.so")
+SOURCES = ["sv_prep.hip", "sv_gemm.hip", "sv_attn.hip", "sv_head.hip", "sv_accept.hip", "sv_abi.cpp",
            "sv_plan.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Wall", "-Wno-unused-function",

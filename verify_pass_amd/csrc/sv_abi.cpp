@@ -2,6 +2,7 @@
 // and kernel dispatch on the caller's stream.  No allocation, no sync.
 #include <atomic>
 #include <cmath>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
@@ -102,39 +103,67 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 constexpr size_t kCounterBytes = 256 * 1024;
 constexpr size_t kMaxCounters = kCounterBytes / sizeof(int);
 
-// Waves to aim for per weight GEMM: about 8 per CU on 256 CUs.
-int target_units() {
-  static int v = [] {
-    const char *e = std::getenv("SV_TARGET_UNITS");
-    const int x = e ? std::atoi(e) : 0;
-    return x > 0 ? x : 2048;
+// GEMM kinds of one pass (for the launch policy and its tuning override).
+enum GemmKind { GK_QKV = 0, GK_O, GK_GU, GK_DOWN, GK_HEAD, GK_COUNT };
+
+// Optional override of the (splits, depth) policy for tuning sweeps:
+// SV_GEMM_TUNE="qkv:8:8,o:8:8,gu:2:8,down:16:8,head:1:2" (kind:splits:depth).
+struct Tune {
+  int splits[GK_COUNT];
+  int depth[GK_COUNT];
+};
+const Tune &tune() {
+  static Tune t = [] {
+    Tune r;
+    for (int i = 0; i < GK_COUNT; ++i) r.splits[i] = r.depth[i] = 0;
+    const char *e = std::getenv("SV_GEMM_TUNE");
+    if (!e) return r;
+    const char *names[GK_COUNT] = {"qkv", "o", "gu", "down", "head"};
+    for (int i = 0; i < GK_COUNT; ++i) {
+      const char *f = std::strstr(e, names[i]);
+      while (f && f != e && f[-1] != ',') f = std::strstr(f + 1, names[i]);
+      if (!f) continue;
+      int s = 0, d = 0;
+      if (std::sscanf(f + std::strlen(names[i]), ":%d:%d", &s, &d) == 2) {
+        r.splits[i] = s;
+        r.depth[i] = d;
+      }
+    }
+    return r;
   }();
-  return v;
+  return t;
 }
 
 struct GemmCfg {
-  int nblk = 0, ntblk = 0, splits = 1, tt = 1, ksteps = 0, K = 0, N = 0;
-  bool norm = false;
+  int nblk = 0, ntblk = 0, splits = 1, tt = 1, ksteps = 0, K = 0, N = 0, depth = 2;
   size_t partial_floats() const { return gemm_partial_floats(nblk, splits, ntblk, tt); }
   size_t counters() const { return splits > 1 ? (size_t)nblk * ntblk : 0; }
 };
 
-// nblk: 32-row groups (16 gate/up feature pairs for SwiGLU).  K is split only
-// when the row groups alone leave the chip short of work.
-GemmCfg gemm_cfg(int nblk, int N, int T, int K, int wtype, bool norm) {
+// nblk: 32-row groups (16 gate/up feature pairs for SwiGLU).
+// Enough row groups to fill the chip: no K split, a shallow prefetch and many
+// resident waves.  Too few: a deep prefetch (8 steps in flight per wave) and
+// K split into units of about 16 steps, at most one round of units.
+GemmCfg gemm_cfg(int kind, int nblk, int N, int T, int K, int wtype) {
   GemmCfg c;
   c.nblk = nblk;
   c.N = N;
   c.K = K;
-  c.norm = norm;
   c.tt = T <= 16 ? 1 : T <= 32 ? 2 : T <= 48 ? 3 : 4;
   c.ntblk = (T + 16 * c.tt - 1) / (16 * c.tt);
   c.ksteps = K / kstep_of(wtype);
   const int base = std::max(1, nblk * c.ntblk);
-  // split K only as far as the resident waves allow (one round of units)
-  const int want = std::max(1, target_units() / base);
-  const int maxs = std::max(1, std::min(32, c.ksteps / 2));
-  c.splits = std::max(1, std::min(want, maxs));
+  if (base >= 2048) {
+    c.splits = 1;
+    c.depth = 2;
+  } else {
+    // about 16 steps per unit, at most 2048 units (resident at depth 8)
+    c.splits = std::max(1, std::min(std::min(c.ksteps / 16, 32), 2048 / base));
+    c.depth = 8;
+  }
+  const Tune &tn = tune();
+  if (tn.splits[kind] > 0) c.splits = std::max(1, std::min(tn.splits[kind], c.ksteps));
+  if (tn.depth[kind] > 0) c.depth = tn.depth[kind];
   if (c.splits > 1 && (size_t)base > kMaxCounters) c.splits = 1;
   return c;
 }
@@ -145,6 +174,7 @@ struct LayerPlan {
   int attn_chunk = 256, attn_items = 0, attn_rpad = 16;
   size_t off_counters = 0, off_partial = 0, off_qbuf = 0, off_po = 0, off_pml = 0;
   size_t off_attn = 0, off_x1 = 0, off_act = 0, off_stats = 0;
+  size_t off_rnorm = 0, off_rparts = 0, off_tseq = 0, off_tpos = 0, off_qs = 0, off_cs = 0, off_rope = 0;
   size_t bytes = 0;
 };
 
@@ -195,16 +225,19 @@ sv_status plan_layer(const sv_layer *L, const sv_batch *b, int32_t flags, LayerP
     return SV_OK;
   }
   if (!valid_wtype(w)) return SV_ERR_UNSUPPORTED;
+  if (L->layout != SV_LAYOUT_ROWMAJOR && L->layout != SV_LAYOUT_PACKED) return SV_ERR_INVALID_ARG;
+  if (L->layout == SV_LAYOUT_PACKED && w == SV_W_F32) return SV_ERR_UNSUPPORTED;
   const int kmul = w == SV_W_INT4_G32 ? 128 : 64;
   if (L->d % kmul) return SV_ERR_UNSUPPORTED;
 
   if (L->kind == SV_LAYER_HEAD) {
     if (L->vocab <= 0) return SV_ERR_INVALID_ARG;
     if (check_matrix(L->lm_head, w) != SV_OK) return SV_ERR_INVALID_ARG;
-    pl.head = gemm_cfg((L->vocab + 31) / 32, L->vocab, pl.T, L->d, w, true);
+    pl.head = gemm_cfg(GK_HEAD, (L->vocab + 31) / 32, L->vocab, pl.T, L->d, w);
     pl.off_counters = take(kCounterBytes);
     pl.off_partial = take(pl.head.partial_floats() * sizeof(float));
     pl.off_stats = take((size_t)pl.head.nblk * pl.T * 2 * sizeof(float));
+    pl.off_rnorm = take((size_t)pl.T * sizeof(float));
     pl.bytes = off;
     return SV_OK;
   }
@@ -226,10 +259,10 @@ sv_status plan_layer(const sv_layer *L, const sv_batch *b, int32_t flags, LayerP
   if (pl.B > 0 && (!b->gamma || !b->kv_len || !b->k_cache || !b->v_cache)) return SV_ERR_INVALID_ARG;
 
   const int nqkv = (hq + 2 * hk) * hd;
-  pl.qkv = gemm_cfg(nqkv / 32, nqkv, pl.T, d, w, true);
-  pl.o = gemm_cfg((d + 31) / 32, d, pl.T, hq * hd, w, false);
-  pl.gu = gemm_cfg((F + 15) / 16, 2 * F, pl.T, d, w, true);
-  pl.down = gemm_cfg((d + 31) / 32, d, pl.T, F, w, false);
+  pl.qkv = gemm_cfg(GK_QKV, nqkv / 32, nqkv, pl.T, d, w);
+  pl.o = gemm_cfg(GK_O, (d + 31) / 32, d, pl.T, hq * hd, w);
+  pl.gu = gemm_cfg(GK_GU, (F + 15) / 16, 2 * F, pl.T, d, w);
+  pl.down = gemm_cfg(GK_DOWN, (d + 31) / 32, d, pl.T, F, w);
   pl.attn_rpad = 16 * ((pl.G * (gmax + 1) + 15) / 16);
   long long items = 0;
   for (int i = 0; i < pl.B; ++i)
@@ -247,6 +280,13 @@ sv_status plan_layer(const sv_layer *L, const sv_batch *b, int32_t flags, LayerP
   pl.off_attn = take((size_t)pl.T * hq * hd * 2);
   pl.off_x1 = take((size_t)pl.T * d * 2);
   pl.off_act = take((size_t)pl.T * F * 2);
+  pl.off_rnorm = take((size_t)pl.T * sizeof(float));
+  pl.off_rparts = take((size_t)pl.o.nblk * pl.T * sizeof(float));
+  pl.off_tseq = take((size_t)pl.T * sizeof(int));
+  pl.off_tpos = take((size_t)pl.T * sizeof(int));
+  pl.off_qs = take((size_t)(pl.B + 1) * sizeof(int));
+  pl.off_cs = take((size_t)(pl.B + 1) * sizeof(int));
+  pl.off_rope = take((size_t)pl.T * hd * sizeof(float));
   pl.bytes = off;
   return SV_OK;
 }
@@ -263,7 +303,7 @@ GemmParams base_params(const GemmCfg &c, const void *x, int T, int wtype, unsign
   p.ksteps = c.ksteps;
   p.nblk = c.nblk;
   p.ntblk = c.ntblk;
-  p.norm = c.norm ? 1 : 0;
+  p.packed = 0;
   p.partial = reinterpret_cast<float *>(ws + pl.off_partial);
   p.counters = reinterpret_cast<int *>(ws + pl.off_counters);
   (void)wtype;
@@ -322,7 +362,18 @@ extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const
   }
 
   if (L->kind == SV_LAYER_HEAD) {
+    PrepParams pp;
+    std::memset(&pp, 0, sizeof(pp));
+    pp.x = static_cast<const uint16_t *>(x_in);
+    pp.T = pl.T;
+    pp.d = L->d;
+    pp.eps = L->eps;
+    pp.rnorm = reinterpret_cast<float *>(ws + pl.off_rnorm);
+    e = launch_prep(pp, s);
+    if (e != hipSuccess) return SV_ERR_HIP;
     GemmParams p = base_params(pl.head, x_in, pl.T, wt, ws, pl);
+    p.rnorm = pp.rnorm;
+    p.packed = L->layout == SV_LAYOUT_PACKED;
     p.nmat = 1;
     p.mat[0] = mat_of(L->lm_head, L->vocab);
     p.rowmap = RM_LINEAR;
@@ -331,7 +382,7 @@ extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const
     p.out = y_out;
     p.ldo = L->vocab;
     p.stats = reinterpret_cast<float *>(ws + pl.off_stats);
-    e = launch_gemm(p, wt, pl.head.tt, s, SV_K_GEMM_LM_HEAD);
+    e = launch_gemm(p, wt, pl.head.tt, pl.head.depth, s, SV_K_GEMM_LM_HEAD);
     if (e == hipSuccess && !(flags & SV_HEAD_LOGITS)) {
       HeadSoftmaxParams h;
       h.logits = static_cast<float *>(y_out);
@@ -339,7 +390,7 @@ extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const
       h.T = pl.T;
       h.V = L->vocab;
       h.nblk = pl.head.nblk;
-      h.cols_per_block = 4096;
+      h.cols_per_block = 8192;
       e = launch_head_softmax(h, s);
     }
     return e == hipSuccess ? SV_OK : SV_ERR_HIP;
@@ -352,8 +403,38 @@ extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const
   uint16_t *x1 = reinterpret_cast<uint16_t *>(ws + pl.off_x1);
   uint16_t *act = reinterpret_cast<uint16_t *>(ws + pl.off_act);
 
+  float *rnorm = reinterpret_cast<float *>(ws + pl.off_rnorm);
+  float *rparts = reinterpret_cast<float *>(ws + pl.off_rparts);
+  int *tseq = reinterpret_cast<int *>(ws + pl.off_tseq);
+  int *tpos = reinterpret_cast<int *>(ws + pl.off_tpos);
+  int *qstart = reinterpret_cast<int *>(ws + pl.off_qs);
+  int *cstart = reinterpret_cast<int *>(ws + pl.off_cs);
+  {  // RMSNorm scales of x and the token map
+    PrepParams pp;
+    std::memset(&pp, 0, sizeof(pp));
+    pp.x = static_cast<const uint16_t *>(x_in);
+    pp.T = pl.T;
+    pp.d = d;
+    pp.eps = L->eps;
+    pp.rnorm = rnorm;
+    pp.gamma = b->gamma;
+    pp.kv_len = b->kv_len;
+    pp.B = pl.B;
+    pp.chunk = pl.attn_chunk;
+    pp.tok_seq = tseq;
+    pp.tok_pos = tpos;
+    pp.q_start = qstart;
+    pp.chunk_start = cstart;
+    pp.rope_cs = reinterpret_cast<float *>(ws + pl.off_rope);
+    pp.hd = hd;
+    pp.rope_theta = L->rope_theta;
+    e = launch_prep(pp, s);
+    if (e != hipSuccess) return SV_ERR_HIP;
+  }
   {  // QKV + RoPE + KV append
     GemmParams p = base_params(pl.qkv, x_in, pl.T, wt, ws, pl);
+    p.rnorm = rnorm;
+    p.packed = L->layout == SV_LAYOUT_PACKED;
     p.nmat = 3;
     p.mat[0] = mat_of(L->wq, hq * hd);
     p.mat[1] = mat_of(L->wk, hk * hd);
@@ -366,14 +447,15 @@ extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const
     p.hq = hq;
     p.hkv = hk;
     p.rope_theta = L->rope_theta;
-    p.gamma = b->gamma;
-    p.kv_len = b->kv_len;
+    p.tok_seq = tseq;
+    p.tok_pos = tpos;
+    p.rope_cs = reinterpret_cast<const float *>(ws + pl.off_rope);
     p.B = pl.B;
     p.kv_cap = b->kv_cap;
     p.kc = b->k_cache;
     p.vc = b->v_cache;
     p.err = b->err_flag;
-    e = launch_gemm(p, wt, pl.qkv.tt, s, SV_K_GEMM_QKV);
+    e = launch_gemm(p, wt, pl.qkv.tt, pl.qkv.depth, s, SV_K_GEMM_QKV);
     if (e != hipSuccess) return SV_ERR_HIP;
   }
   {  // ragged attention + merge
@@ -382,6 +464,8 @@ extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const
     a.qbuf = qbuf;
     a.gamma = b->gamma;
     a.kv_len = b->kv_len;
+    a.q_start = qstart;
+    a.chunk_start = cstart;
     a.kc = b->k_cache;
     a.vc = b->v_cache;
     a.B = pl.B;
@@ -405,6 +489,7 @@ extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const
   }
   {  // O projection + residual
     GemmParams p = base_params(pl.o, attn, pl.T, wt, ws, pl);
+    p.packed = L->layout == SV_LAYOUT_PACKED;
     p.nmat = 1;
     p.mat[0] = mat_of(L->wo, d);
     p.rowmap = RM_LINEAR;
@@ -412,24 +497,29 @@ extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const
     p.out = x1;
     p.ldo = d;
     p.resid = static_cast<const uint16_t *>(x_in);
-    e = launch_gemm(p, wt, pl.o.tt, s, SV_K_GEMM_O);
+    p.sq_out = rparts;  // sums of squares of x1 for the next RMSNorm
+    e = launch_gemm(p, wt, pl.o.tt, pl.o.depth, s, SV_K_GEMM_O);
     if (e != hipSuccess) return SV_ERR_HIP;
   }
   {  // gate || up + SwiGLU
     GemmParams p = base_params(pl.gu, x1, pl.T, wt, ws, pl);
+    p.packed = L->layout == SV_LAYOUT_PACKED;
     p.nmat = 2;
     p.mat[0] = mat_of(L->w_gate, F);
     p.mat[1] = mat_of(L->w_up, F);
     p.rowmap = RM_SWIGLU;
+    p.rparts = rparts;
+    p.nparts = pl.o.nblk;
     p.eps = L->eps;
     p.epi = EPI_SWIGLU;
     p.out = act;
     p.ldo = F;
-    e = launch_gemm(p, wt, pl.gu.tt, s, SV_K_GEMM_GATE_UP);
+    e = launch_gemm(p, wt, pl.gu.tt, pl.gu.depth, s, SV_K_GEMM_GATE_UP);
     if (e != hipSuccess) return SV_ERR_HIP;
   }
   {  // down projection + residual
     GemmParams p = base_params(pl.down, act, pl.T, wt, ws, pl);
+    p.packed = L->layout == SV_LAYOUT_PACKED;
     p.nmat = 1;
     p.mat[0] = mat_of(L->w_down, d);
     p.rowmap = RM_LINEAR;
@@ -437,10 +527,45 @@ extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const
     p.out = y_out;
     p.ldo = d;
     p.resid = x1;
-    e = launch_gemm(p, wt, pl.down.tt, s, SV_K_GEMM_DOWN);
+    e = launch_gemm(p, wt, pl.down.tt, pl.down.depth, s, SV_K_GEMM_DOWN);
     if (e != hipSuccess) return SV_ERR_HIP;
   }
   return SV_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Packed weight layout.
+extern "C" sv_status sv_packed_matrix_bytes(int32_t wtype, int32_t N, int32_t K, size_t *w_bytes,
+                                            size_t *scale_bytes) {
+  if (N <= 0 || K <= 0) return SV_ERR_INVALID_ARG;
+  const size_t rows = (size_t)(N + 15) / 16 * 16;
+  if (wtype == SV_W_BF16) {
+    if (K % 64) return SV_ERR_UNSUPPORTED;
+    if (w_bytes) *w_bytes = rows * K * 2;
+    if (scale_bytes) *scale_bytes = 0;
+    return SV_OK;
+  }
+  if (wtype == SV_W_INT4_G32) {
+    if (K % 128) return SV_ERR_UNSUPPORTED;
+    if (w_bytes) *w_bytes = rows * K / 2;
+    if (scale_bytes) *scale_bytes = rows * (K / 32) * 2;
+    return SV_OK;
+  }
+  return SV_ERR_UNSUPPORTED;
+}
+
+extern "C" sv_status sv_pack_matrix(int32_t wtype, int32_t N, int32_t K, const void *w,
+                                    const void *scale, void *w_packed, void *scale_packed,
+                                    void *stream) {
+  size_t wb = 0, sb = 0;
+  const sv_status st = sv_packed_matrix_bytes(wtype, N, K, &wb, &sb);
+  if (st != SV_OK) return st;
+  if (!w || !w_packed) return SV_ERR_INVALID_ARG;
+  if (wtype == SV_W_INT4_G32 && (!scale || !scale_packed)) return SV_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+  const hipError_t e = launch_pack(wtype == SV_W_BF16 ? WT_BF16 : WT_INT4, N, K, w, scale, w_packed,
+                                   scale_packed, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
 // ---------------------------------------------------------------------------
@@ -526,6 +651,7 @@ extern "C" sv_status sv_accept_commit(int32_t B, int32_t V, int32_t mode, const 
   a.err = err_flag;
   a.parts = reinterpret_cast<AcceptPart *>(ws + ap.off_parts);
   a.acc_ws = reinterpret_cast<int *>(ws + ap.off_acc);
+  a.counters = reinterpret_cast<int *>(ws);
   (void)hipGetLastError();
   const hipError_t e = launch_accept(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SV_OK : SV_ERR_HIP;

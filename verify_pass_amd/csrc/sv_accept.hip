@@ -7,12 +7,14 @@
 // the order in which lanes and workgroups add them, so the token drawn for a
 // given uniform is the same on any grid shape.
 //
-// Kernel 1 (grid: vocabulary chunks x sequences, or x rows in greedy mode):
-//   acceptance tests (one draft per lane, first rejection by LDS atomic min),
-//   then per-chunk weight sums of the residual / bonus row, of the fallback
-//   target row, and the chunk's argmax.
-// Kernel 2 (grid: sequences): total weight, uniform -> integer target,
-//   chunk search over the partial sums, exact scan inside the chunk, commit.
+// One kernel, grid = vocabulary chunks x sequences (x target rows in greedy
+// mode).  Every workgroup runs the sequence's acceptance tests (one draft per
+// lane, first rejection by LDS atomic min) and sums the integer weights of its
+// chunk of the resampling row, of the fallback target row, and the chunk's
+// argmax.  It publishes them with device-scope stores and bumps the
+// sequence's arrival counter; the last workgroup to arrive turns the uniform
+// into an integer target, finds the chunk holding it from the chunk sums,
+// scans that chunk exactly (staged through LDS) and commits.
 #include "sv_common.h"
 
 namespace sv {
@@ -60,28 +62,74 @@ __device__ inline void block_reduce(u64 &a, u64 &b, float &v, int &ix, u64 *sa, 
   b = sb[0];
   v = sv[0];
   ix = si[0];
-}
-
-// q_start of every sequence (exclusive scan of gamma + 1) into qs[0..B).
-__device__ inline void token_starts(const int *gamma, int B, int *qs, int *tmp) {
-  for (int i = threadIdx.x; i < B; i += kThreads) qs[i] = gamma[i] + 1;
   __syncthreads();
-  block_exscan(qs, B, tmp);
 }
 
-__global__ __launch_bounds__(kThreads) void accept_scan_kernel(AcceptParams p) {
-  extern __shared__ __align__(16) unsigned char smem[];
+// Device-scope (cross-XCD coherent) stores and loads of the chunk results.
+__device__ __forceinline__ void put_part(AcceptPart *p, const AcceptPart &v) {
+  u64 *w = reinterpret_cast<u64 *>(p);
+  __hip_atomic_store(w, v.sum_res, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(w + 1, v.sum_p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const u64 mx = (static_cast<u64>(static_cast<uint32_t>(v.arg_p)) << 32) | __float_as_uint(v.max_p);
+  __hip_atomic_store(w + 2, mx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ AcceptPart get_part(const AcceptPart *p) {
+  u64 *w = reinterpret_cast<u64 *>(const_cast<AcceptPart *>(p));
+  AcceptPart v;
+  v.sum_res = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  v.sum_p = __hip_atomic_load(w + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const u64 mx = __hip_atomic_load(w + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  v.max_p = __uint_as_float(static_cast<uint32_t>(mx));
+  v.arg_p = static_cast<int>(mx >> 32);
+  return v;
+}
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Publish, count the arrival, and tell whether this workgroup arrived last
+// (then the counter is reset for the next call).
+__device__ inline bool arrive_last(int *ctr, int expected, int *flag) {
+  wait_vmem();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = old == expected - 1;
+    if (*flag) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  return *flag != 0;
+}
+
+// q_start of sequence i (exclusive prefix sum of gamma + 1), by a block reduction.
+__device__ inline int seq_start(const int *gamma, int i, int *red) {
+  int s = 0;
+  for (int k = threadIdx.x; k < i; k += kThreads) s += gamma[k] + 1;
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int o = kThreads / 2; o > 0; o >>= 1) {
+    if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  const int r = red[0];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(kThreads) void accept_kernel(AcceptParams p) {
   __shared__ u64 sa[kThreads], sb[kThreads];
   __shared__ float sv[kThreads];
   __shared__ int si[kThreads];
-  __shared__ int first_fail, bad;
-  int *qs = reinterpret_cast<int *>(smem);
-  int *tmp = qs + p.B + 1;
+  __shared__ int red[kThreads];
+  __shared__ int first_fail, bad, flag, chosen_chunk, use_res, result;
+  __shared__ u64 target, seg[kThreads];
+  __shared__ int row_arg[64];
+  __shared__ float stage_p[8192];
+  __shared__ float stage_q[8192];
   const int tid = threadIdx.x, c = blockIdx.x;
   const int x0 = c * p.chunk, x1 = min(p.V, x0 + p.chunk);
 
   if (p.mode == SV_ACCEPT_GREEDY) {
-    // one target row per blockIdx.y: chunk argmax only
+    // blockIdx.y = target row: chunk argmax; the last of the sequence's
+    // (gamma_i + 1) * nchunk workgroups decides
     const int row = blockIdx.y;
     const float *pr = p.p + (size_t)row * p.V;
     float bv = -INFINITY;
@@ -89,14 +137,61 @@ __global__ __launch_bounds__(kThreads) void accept_scan_kernel(AcceptParams p) {
     for (int x = x0 + tid; x < x1; x += kThreads) amax(bv, bi, pr[x], x);
     u64 z0 = 0, z1 = 0;
     block_reduce(z0, z1, bv, bi, sa, sb, sv, si);
-    if (tid == 0) p.parts[(size_t)row * p.nchunk + c] = AcceptPart{0ull, 0ull, bv, bi};
+    if (tid == 0) put_part(p.parts + (size_t)row * p.nchunk + c, AcceptPart{0ull, 0ull, bv, bi});
+    // owner sequence of this row
+    if (tid == 0) {
+      int s = 0, i = 0;
+      while (i < p.B && s + p.gamma[i] + 1 <= row) s += p.gamma[i++] + 1;
+      red[0] = i;
+      red[1] = s;
+    }
+    __syncthreads();
+    const int i = red[0], qst = red[1];
+    __syncthreads();
+    const int g = p.gamma[i];
+    if (!arrive_last(p.counters + i, (g + 1) * p.nchunk, &flag)) return;
+    for (int j = tid; j <= g; j += kThreads) {
+      float v = -INFINITY;
+      int b = 0x7fffffff;
+      for (int cc = 0; cc < p.nchunk; ++cc) {
+        const AcceptPart q = get_part(p.parts + (size_t)(qst + j) * p.nchunk + cc);
+        amax(v, b, q.max_p, q.arg_p);
+      }
+      if (j < 64) row_arg[j] = b;
+      else p.acc_ws[p.B + qst + j] = b;  // rare long drafts spill to workspace
+    }
+    wait_vmem();
+    __syncthreads();
+    if (tid == 0) {
+      const int dst = qst - i;
+      auto arg = [&](int j) {
+        return j < 64 ? row_arg[j]
+                      : __hip_atomic_load(p.acc_ws + p.B + qst + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      };
+      int badtok = 0;
+      for (int j = 0; j < g; ++j) {
+        const int d = p.draft[dst + j];
+        if (d < 0 || d >= p.V) badtok = 1;
+      }
+      if (badtok) {
+        p.accepted[i] = -1;
+        p.next_token[i] = -1;
+        set_err(p.err, SV_DEV_ERR_BAD_TOKEN);
+        return;
+      }
+      int a = 0;
+      while (a < g && p.draft[dst + a] == arg(a)) ++a;
+      p.accepted[i] = a;
+      p.next_token[i] = arg(a);
+      p.kv_len[i] += a + 1;
+    }
     return;
   }
 
+  // ---- stochastic -----------------------------------------------------------
   const int i = blockIdx.y;
-  token_starts(p.gamma, p.B, qs, tmp);
   const int g = p.gamma[i];
-  const int qst = qs[i], dst = qst - i;
+  const int qst = seq_start(p.gamma, i, red), dst = qst - i;
   if (tid == 0) {
     first_fail = g;
     bad = 0;
@@ -112,83 +207,25 @@ __global__ __launch_bounds__(kThreads) void accept_scan_kernel(AcceptParams p) {
     }
   }
   __syncthreads();
-  if (bad) {
-    if (c == 0 && tid == 0) p.acc_ws[i] = -1;
-    return;
-  }
-  const int a = first_fail;
-  if (c == 0 && tid == 0) p.acc_ws[i] = a;
-  const float *prow = p.p + (size_t)(qst + a) * p.V;
-  const float *qrow = a < g ? p.q + (size_t)(dst + a) * p.V : nullptr;
+  const int a = bad ? -1 : first_fail;
+  const float *prow = p.p + (size_t)(qst + max(a, 0)) * p.V;
+  const float *qrow = (a >= 0 && a < g) ? p.q + (size_t)(dst + a) * p.V : nullptr;
   u64 sres = 0, sp = 0;
   float bv = -INFINITY;
   int bi = 0x7fffffff;
-  if (qrow) {
-    for (int x = x0 + tid; x < x1; x += kThreads) {
-      const float pv = prow[x];
-      sres += weight_of(pv - qrow[x]);
-      sp += weight_of(pv);
-      amax(bv, bi, pv, x);
-    }
-  } else {
+  if (a >= 0) {
     for (int x = x0 + tid; x < x1; x += kThreads) {
       const float pv = prow[x];
       const u64 w = weight_of(pv);
-      sres += w;
+      sres += qrow ? weight_of(pv - qrow[x]) : w;
       sp += w;
       amax(bv, bi, pv, x);
     }
   }
   block_reduce(sres, sp, bv, bi, sa, sb, sv, si);
-  if (tid == 0) p.parts[(size_t)i * p.nchunk + c] = AcceptPart{sres, sp, bv, bi};
-}
+  if (tid == 0) put_part(p.parts + (size_t)i * p.nchunk + c, AcceptPart{sres, sp, bv, bi});
+  if (!arrive_last(p.counters + i, p.nchunk, &flag)) return;
 
-__global__ __launch_bounds__(kThreads) void accept_select_kernel(AcceptParams p) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ u64 seg[kThreads + 1];
-  __shared__ int chosen_chunk, use_res, result;
-  __shared__ u64 target;
-  __shared__ int row_arg[64];
-  int *qs = reinterpret_cast<int *>(smem);
-  int *tmp = qs + p.B + 1;
-  const int tid = threadIdx.x, i = blockIdx.x;
-  token_starts(p.gamma, p.B, qs, tmp);
-  const int g = p.gamma[i];
-  const int qst = qs[i], dst = qst - i;
-
-  if (p.mode == SV_ACCEPT_GREEDY) {
-    // argmax of each of the g + 1 rows (chunks combined in fixed order)
-    for (int j = tid; j <= g; j += kThreads) {
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
-      const AcceptPart *pp = p.parts + (size_t)(qst + j) * p.nchunk;
-      for (int c = 0; c < p.nchunk; ++c) amax(bv, bi, pp[c].max_p, pp[c].arg_p);
-      if (j < 64) row_arg[j] = bi;
-      else p.acc_ws[p.B + (qst + j)] = bi;  // rare long drafts spill to workspace
-    }
-    __syncthreads();
-    if (tid == 0) {
-      auto arg = [&](int j) { return j < 64 ? row_arg[j] : p.acc_ws[p.B + qst + j]; };
-      int a = 0, badtok = 0;
-      for (int j = 0; j < g; ++j) {
-        const int d = p.draft[dst + j];
-        if (d < 0 || d >= p.V) { badtok = 1; break; }
-      }
-      if (badtok) {
-        p.accepted[i] = -1;
-        p.next_token[i] = -1;
-        set_err(p.err, SV_DEV_ERR_BAD_TOKEN);
-        return;
-      }
-      while (a < g && p.draft[dst + a] == arg(a)) ++a;
-      p.accepted[i] = a;
-      p.next_token[i] = arg(a);
-      p.kv_len[i] += a + 1;
-    }
-    return;
-  }
-
-  const int a = p.acc_ws[i];
   if (a < 0) {
     if (tid == 0) {
       p.accepted[i] = -1;
@@ -200,12 +237,13 @@ __global__ __launch_bounds__(kThreads) void accept_select_kernel(AcceptParams p)
   const AcceptPart *pp = p.parts + (size_t)i * p.nchunk;
   if (tid == 0) {
     u64 s_res = 0, s_p = 0;
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-    for (int c = 0; c < p.nchunk; ++c) {
-      s_res += pp[c].sum_res;
-      s_p += pp[c].sum_p;
-      amax(bv, bi, pp[c].max_p, pp[c].arg_p);
+    float mv = -INFINITY;
+    int mi = 0x7fffffff;
+    for (int cc = 0; cc < p.nchunk; ++cc) {
+      const AcceptPart q = get_part(pp + cc);
+      s_res += q.sum_res;
+      s_p += q.sum_p;
+      amax(mv, mi, q.max_p, q.arg_p);
     }
     int ur;
     u64 S;
@@ -215,32 +253,38 @@ __global__ __launch_bounds__(kThreads) void accept_select_kernel(AcceptParams p)
     use_res = ur;
     result = -1;
     if (ur < 0) {
-      result = bi;
+      result = mi;
     } else {
       u64 t = static_cast<u64>(floor(static_cast<double>(p.u_samp[i]) * static_cast<double>(S)));
       if (t >= S) t = S - 1;
       u64 run = 0;
-      int cc = p.nchunk - 1;
-      for (int c = 0; c < p.nchunk; ++c) {
-        const u64 v = ur ? pp[c].sum_res : pp[c].sum_p;
-        if (run + v > t) { cc = c; break; }
+      int cc_hit = p.nchunk - 1;
+      for (int cc = 0; cc < p.nchunk; ++cc) {
+        const AcceptPart q = get_part(pp + cc);
+        const u64 v = ur ? q.sum_res : q.sum_p;
+        if (run + v > t) { cc_hit = cc; break; }
         run += v;
       }
-      chosen_chunk = cc;
+      chosen_chunk = cc_hit;
       target = t - run;
     }
   }
   __syncthreads();
   if (use_res >= 0) {
-    const int c = chosen_chunk;
-    const int x0 = c * p.chunk, x1 = min(p.V, x0 + p.chunk);
-    const int n = x1 - x0;
+    // exact scan of the chosen chunk: stage it in LDS with coalesced loads,
+    // then each thread sums a contiguous segment
+    const int cx0 = chosen_chunk * p.chunk, cx1 = min(p.V, cx0 + p.chunk);
+    const int n = cx1 - cx0;
+    const bool resid = use_res && a < g;
+    for (int x = tid; x < n; x += kThreads) {
+      stage_p[x] = prow[cx0 + x];
+      if (resid) stage_q[x] = qrow[cx0 + x];
+    }
+    __syncthreads();
     const int per = (n + kThreads - 1) / kThreads;
-    const int lo = x0 + min(n, tid * per), hi = x0 + min(n, (tid + 1) * per);
-    const float *prow = p.p + (size_t)(qst + a) * p.V;
-    const float *qrow = (use_res && a < g) ? p.q + (size_t)(dst + a) * p.V : nullptr;
+    const int lo = min(n, tid * per), hi = min(n, lo + per);
     u64 s = 0;
-    for (int x = lo; x < hi; ++x) s += weight_of(qrow ? prow[x] - qrow[x] : prow[x]);
+    for (int x = lo; x < hi; ++x) s += weight_of(resid ? stage_p[x] - stage_q[x] : stage_p[x]);
     seg[tid] = s;
     __syncthreads();
     if (tid == 0) {
@@ -250,16 +294,14 @@ __global__ __launch_bounds__(kThreads) void accept_select_kernel(AcceptParams p)
         seg[k] = run;
         run += v;
       }
-      seg[kThreads] = run;
     }
     __syncthreads();
-    const u64 t = target;
-    const u64 before = seg[tid];
+    const u64 t = target, before = seg[tid];
     if (before <= t && t < before + s) {
       u64 run = before;
       for (int x = lo; x < hi; ++x) {
-        run += weight_of(qrow ? prow[x] - qrow[x] : prow[x]);
-        if (run > t) { result = x; break; }
+        run += weight_of(resid ? stage_p[x] - stage_q[x] : stage_p[x]);
+        if (run > t) { result = cx0 + x; break; }
       }
     }
     __syncthreads();
@@ -274,16 +316,10 @@ __global__ __launch_bounds__(kThreads) void accept_select_kernel(AcceptParams p)
 }  // namespace
 
 hipError_t launch_accept(const AcceptParams &p, hipStream_t s) {
-  const size_t lds = (size_t)(p.B + 1 + 260) * sizeof(int);
   const int rows = p.mode == SV_ACCEPT_GREEDY ? p.T : p.B;
-  trace_before(SV_K_ACCEPT_SCAN, s);
-  hipLaunchKernelGGL(accept_scan_kernel, dim3(p.nchunk, rows), dim3(kThreads), lds, s, p);
-  trace_after(SV_K_ACCEPT_SCAN, s);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  trace_before(SV_K_ACCEPT_SELECT, s);
-  hipLaunchKernelGGL(accept_select_kernel, dim3(p.B), dim3(kThreads), lds, s, p);
-  trace_after(SV_K_ACCEPT_SELECT, s);
+  trace_before(SV_K_ACCEPT, s);
+  hipLaunchKernelGGL(accept_kernel, dim3(p.nchunk, rows), dim3(kThreads), 0, s, p);
+  trace_after(SV_K_ACCEPT, s);
   return hipGetLastError();
 }
 

@@ -25,18 +25,15 @@ constexpr int kThreads = 256;
 constexpr int kKeysPerStep = 32;
 constexpr float kNegBig = -1.0e30f;
 
-// Token map and chunk map for all sequences, in LDS.
-// qs[i] = first stacked row of sequence i, cs[i] = first work item of sequence i.
-__device__ inline int build_maps(const AttnParams &p, int *qs, int *cs, int *tmp) {
-  for (int i = threadIdx.x; i < p.B; i += kThreads) {
-    const int g = p.gamma[i];
-    const int L = p.kv_len[i] + g + 1;
-    qs[i] = g + 1;
-    cs[i] = (L + p.chunk - 1) / p.chunk;
+// Copy the token map (q_start) and chunk map (chunk_start) of all sequences
+// into LDS; returns the total number of work items.
+__device__ inline int load_maps(const AttnParams &p, int *qs, int *cs) {
+  for (int i = threadIdx.x; i <= p.B; i += blockDim.x) {
+    qs[i] = p.q_start[i];
+    cs[i] = p.chunk_start[i];
   }
   __syncthreads();
-  block_exscan(qs, p.B, tmp);
-  return block_exscan(cs, p.B, tmp);
+  return cs[p.B];
 }
 
 __device__ __forceinline__ int dslice(int dg, int gq) {
@@ -51,15 +48,14 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   int *qs = reinterpret_cast<int *>(smem);
   int *cs = qs + p.B + 1;
-  int *tmp = cs + p.B + 1;
-  float *red_o = reinterpret_cast<float *>(tmp + 260);  // [4][HD][16]
+  float *red_o = reinterpret_cast<float *>(cs + p.B + 1 + 2);  // [4][HD][16]
   float *red_ml = red_o + 4 * HD * 16;                   // [4][16][2]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int gq = lane >> 4, l16 = lane & 15;
   const int g = blockIdx.y;
 
-  const int total = build_maps(p, qs, cs, tmp);
+  const int total = load_maps(p, qs, cs);
   if (blockIdx.x == 0 && g == 0 && tid == 0 && total > p.max_items) set_err(p.err, SV_DEV_ERR_CTX_BOUND);
   const int item = blockIdx.x;
   if (item >= total) return;
@@ -228,27 +224,7 @@ __global__ __launch_bounds__(HD) void merge_kernel(AttnParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   int *qs = reinterpret_cast<int *>(smem);
   int *cs = qs + p.B + 1;
-  int *tmp = cs + p.B + 1;
-  // the scan helpers assume 256 threads; HD <= 256 threads here, so build the
-  // maps with a simple strided loop and a serial scan by thread 0
-  for (int i = threadIdx.x; i < p.B; i += HD) {
-    const int g = p.gamma[i];
-    qs[i] = g + 1;
-    cs[i] = (p.kv_len[i] + g + 1 + p.chunk - 1) / p.chunk;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int a = 0, b = 0;
-    for (int i = 0; i < p.B; ++i) {
-      const int x = qs[i], y = cs[i];
-      qs[i] = a;
-      cs[i] = b;
-      a += x;
-      b += y;
-    }
-    tmp[0] = b;
-  }
-  __syncthreads();
+  load_maps(p, qs, cs);
   const int t = blockIdx.x, qh = blockIdx.y, d = threadIdx.x;
   const int seq = upper_index(qs, p.B, t);
   const int j = t - qs[seq];
@@ -279,7 +255,7 @@ __global__ __launch_bounds__(HD) void merge_kernel(AttnParams p) {
 
 template <int RT, int HD>
 hipError_t launch_rt(const AttnParams &p, hipStream_t s) {
-  const size_t lds = (size_t)(2 * (p.B + 1) + 260) * sizeof(int) + (size_t)4 * HD * 16 * sizeof(float) +
+  const size_t lds = (size_t)(2 * (p.B + 1) + 2) * sizeof(int) + (size_t)4 * HD * 16 * sizeof(float) +
                      4 * 16 * 2 * sizeof(float);
   if (lds > 65536)
     (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_kernel<RT, HD>),
@@ -307,7 +283,7 @@ hipError_t launch_attention(const AttnParams &p, hipStream_t s) {
 }
 
 hipError_t launch_attn_merge(const AttnParams &p, hipStream_t s) {
-  const size_t lds = (size_t)(2 * (p.B + 1) + 4) * sizeof(int);
+  const size_t lds = (size_t)(2 * (p.B + 1) + 2) * sizeof(int);
   trace_before(SV_K_ATTN_MERGE, s);
   if (p.hd == 64)
     hipLaunchKernelGGL((merge_kernel<64>), dim3(p.T, p.hq), dim3(64), lds, s, p);

@@ -105,33 +105,58 @@ struct GemmParams {
   int nmat;
   GemmMat mat[3];
   int rowmap, hd;
+  int packed;          // weights in the packed fragment layout
   int splits, ksteps;  // ksteps = K / step size
   int nblk, ntblk;     // 32-row groups (16 features for SWIGLU), token blocks
-  int norm;
+  const float *rnorm;      // per-token RMSNorm scale [T] (nullptr: see rparts / none)
+  const float *rparts;     // per-token sums of squares in nparts partials [T][nparts]
+  int nparts;
   float eps;
+  float *sq_out;           // EPI_RESID: sums of squares of the output, [T][row groups]
   float *partial;      // K-split partial tiles (device-scope stores)
   int *counters;       // [ntblk * nblk] arrival counters, zero between launches
   int epi;
   void *out;
   int ldo;
   const uint16_t *resid;  // EPI_RESID
-  float *stats;           // EPI_LOGITS: [nblk][T][2] (max, sum exp of the group)
+  float *stats;           // EPI_LOGITS: [T][nblk][2] (max, sum exp of the group)
   // EPI_QKV
   uint16_t *qbuf;  // [T][hq][hd]
   int hq, hkv;
   float rope_theta;
-  const int *gamma;
-  const int *kv_len;
+  const int *tok_seq;  // [T] sequence of each stacked token
+  const int *tok_pos;  // [T] its position
+  const float *rope_cs;  // [T][hd/2][2] rotation cos, sin
   int B, kv_cap;
   void *const *kc;
   void *const *vc;
   int *err;
 };
 
+struct PrepParams {
+  const uint16_t *x;   // [T][d] rows whose RMSNorm scale is needed
+  int T, d;
+  float eps;
+  float *rnorm;        // [T]
+  // token map (decoder calls; gamma == nullptr skips it)
+  const int *gamma;
+  const int *kv_len;
+  int B, chunk;
+  int *tok_seq;        // [T]
+  int *tok_pos;        // [T]
+  int *q_start;        // [B + 1]
+  int *chunk_start;    // [B + 1] attention work items of each sequence
+  float *rope_cs;      // [T][hd/2][2] cos, sin (nullptr: none)
+  int hd;
+  float rope_theta;
+};
+
 struct AttnParams {
   const uint16_t *qbuf;  // [T][hq][hd] (rotated)
   const int *gamma;
   const int *kv_len;
+  const int *q_start;      // [B + 1]
+  const int *chunk_start;  // [B + 1]
   void *const *kc;
   void *const *vc;
   int B, T, hq, hkv, hd, kv_cap, max_ctx;
@@ -147,7 +172,7 @@ struct AttnParams {
 
 struct HeadSoftmaxParams {
   float *logits;        // [T][V] in: logits, out: probabilities
-  const float *stats;   // [nblk][T][2]
+  const float *stats;   // [T][nblk][2]
   int T, V, nblk, cols_per_block;
 };
 
@@ -181,15 +206,19 @@ struct AcceptParams {
   int *next_token;
   int *err;
   AcceptPart *parts;   // stochastic: [B][nchunk]; greedy: [T][nchunk]
-  int *acc_ws;         // stochastic: [B] accepted count (or -1 for a bad sequence)
+  int *acc_ws;         // [B + T] ints of spill space (greedy rows past the LDS table)
+  int *counters;       // [B] arrival counters, zero between calls
 };
 
 // ---------------------------------------------------------------------------
 // Host launchers (one per kernel family).  Return hipSuccess or the launch error.
-hipError_t launch_gemm(const GemmParams &p, int wtype, int tok_tiles, hipStream_t s,
+hipError_t launch_gemm(const GemmParams &p, int wtype, int tok_tiles, int depth, hipStream_t s,
                        int trace_class);
+hipError_t launch_pack(int wtype, int N, int K, const void *w, const void *scale, void *wp,
+                       void *sp, hipStream_t s);
 // Workspace floats for the K-split partial tiles of one GEMM launch.
 size_t gemm_partial_floats(int ngroups, int splits, int ntblk, int tok_tiles);
+hipError_t launch_prep(const PrepParams &p, hipStream_t s);
 hipError_t launch_attention(const AttnParams &p, hipStream_t s);
 hipError_t launch_attn_merge(const AttnParams &p, hipStream_t s);
 hipError_t launch_head_softmax(const HeadSoftmaxParams &p, hipStream_t s);

@@ -44,28 +44,89 @@ template <> struct WStep<WT_INT4> { uint4 v; uint32_t s; };
 
 template <int WT> constexpr int kstep() { return WT == WT_INT4 ? 128 : 64; }
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+// Streaming (non-temporal) 16-byte load: weights are read once per pass and
+// should not evict the token operand from L2.
+__device__ __forceinline__ uint4 ld_nt(const void *p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  return __builtin_bit_cast(uint4, v);
+}
+
+// Per-lane weight stream of one 16-row tile.
 // Lane (row, gq) of step ks holds, for MFMA m, reduction indices
-//   bf16 : ks*64  + 32m + 8gq + [0, 8)      (each instruction: 64 contiguous
-//          bytes per row across the four lane groups)
-//   int4 : ks*128 + 32gq + 8m + [0, 8)      (one 16-byte load per lane)
+//   bf16 : ks*64  + 32m + 8gq + [0, 8)
+//   int4 : ks*128 + 32gq + 8m + [0, 8)      (one 16-byte word group per lane)
 //   fp32 : ks*64  + 16gq + 8m + [0, 8)
 // and the token operand holds the same indices for its token.
+// Row-major [N][K] storage: each load instruction reads 16 rows x 64 bytes.
+// Packed storage (see sv_pack_matrix): the 16-row tile's fragments for one
+// step are contiguous in lane order, so each load instruction reads 1 KiB of
+// contiguous memory and a tile's whole K range is one sequential stream.
 template <int WT>
-__device__ __forceinline__ WStep<WT> load_w(const void *w, const uint16_t *sc, int row, int K, int ks,
-                                           int gq) {
-  WStep<WT> r;
-  if constexpr (WT == WT_BF16) {
-    const uint16_t *b = static_cast<const uint16_t *>(w) + (size_t)row * K + ks * 64 + 8 * gq;
-    r.v[0] = *reinterpret_cast<const uint4 *>(b);
-    r.v[1] = *reinterpret_cast<const uint4 *>(b + 32);
-  } else if constexpr (WT == WT_F32) {
-    const float *b = static_cast<const float *>(w) + (size_t)row * K + ks * 64 + 16 * gq;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r.v[i] = *reinterpret_cast<const uint4 *>(b + 4 * i);
+struct WSrc {
+  const unsigned char *p;   // lane's base address for step 0
+  const uint16_t *s;        // int4 scales, lane's base for step 0
+  int step_bytes;           // byte advance per K step
+  int s_step;               // scale advance (elements) per K step
+  int m_off;                // byte offset of the second fragment (bf16)
+};
+
+template <int WT>
+__device__ __forceinline__ WSrc<WT> make_src(const GemmMat &mat, int row, int tile_row0, int K,
+                                             int ksteps, int packed, int lane, int gq) {
+  WSrc<WT> w;
+  if (packed) {
+    const size_t tile = (size_t)(tile_row0 / 16);
+    if constexpr (WT == WT_INT4) {
+      w.p = static_cast<const unsigned char *>(mat.w) + (tile * ksteps * 64 + lane) * 16;
+      w.s = mat.s + tile * ksteps * 64 + lane;
+      w.step_bytes = 64 * 16;
+      w.s_step = 64;
+      w.m_off = 0;
+    } else {
+      w.p = static_cast<const unsigned char *>(mat.w) + (tile * ksteps * 128 + lane) * 16;
+      w.s = nullptr;
+      w.step_bytes = 128 * 16;
+      w.s_step = 0;
+      w.m_off = 64 * 16;
+    }
   } else {
-    const uint32_t *b = static_cast<const uint32_t *>(w) + (size_t)row * (K / 8) + ks * 16 + 4 * gq;
-    r.v = *reinterpret_cast<const uint4 *>(b);
-    r.s = sc[(size_t)row * (K / 32) + ks * 4 + gq];
+    if constexpr (WT == WT_BF16) {
+      w.p = static_cast<const unsigned char *>(mat.w) + ((size_t)row * K + 8 * gq) * 2;
+      w.step_bytes = 128;
+      w.m_off = 64;
+      w.s = nullptr;
+      w.s_step = 0;
+    } else if constexpr (WT == WT_INT4) {
+      w.p = static_cast<const unsigned char *>(mat.w) + ((size_t)row * (K / 8) + 4 * gq) * 4;
+      w.step_bytes = 64;
+      w.m_off = 0;
+      w.s = mat.s + (size_t)row * (K / 32) + gq;
+      w.s_step = 4;
+    } else {
+      w.p = static_cast<const unsigned char *>(mat.w) + ((size_t)row * K + 16 * gq) * 4;
+      w.step_bytes = 256;
+      w.m_off = 0;
+      w.s = nullptr;
+      w.s_step = 0;
+    }
+  }
+  return w;
+}
+
+template <int WT>
+__device__ __forceinline__ WStep<WT> load_w(const WSrc<WT> &w, int ks) {
+  WStep<WT> r;
+  const unsigned char *b = w.p + (size_t)ks * w.step_bytes;
+  if constexpr (WT == WT_BF16) {
+    r.v[0] = ld_nt(b);
+    r.v[1] = ld_nt(b + w.m_off);
+  } else if constexpr (WT == WT_F32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.v[i] = ld_nt(b + 16 * i);
+  } else {
+    r.v = ld_nt(b);
+    r.s = w.s[(size_t)ks * w.s_step];
   }
   return r;
 }
@@ -120,18 +181,6 @@ __device__ __forceinline__ void split8(const uint4 &a, const uint4 &b, bf16x8 &h
   lo = as_bf16x8(uint4{l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16)});
 }
 
-__device__ __forceinline__ float sumsq8(const uint4 &v) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float a = __uint_as_float(w[i] << 16), b = __uint_as_float(w[i] & 0xFFFF0000u);
-    s += a * a;
-    s += b * b;
-  }
-  return s;
-}
-
 // Physical (matrix, row) of row r of tile `tile` in 32-row group g.
 // Returns false past the end of the matrix (the lane then streams row 0 and
 // its results are dropped).
@@ -162,6 +211,11 @@ __device__ __forceinline__ bool map_row(const GemmParams &p, int g, int tile, in
   return true;
 }
 
+__device__ __forceinline__ int rotate_step(int s, int rot, int n) {
+  const int r = s + rot;
+  return r >= n ? r - n : r;
+}
+
 // Bijective remap of the dispatch index so that consecutive logical
 // workgroups run on the same XCD (dispatch is round-robin over the 8 XCDs).
 __device__ __forceinline__ int xcd_remap(int wg, int nwg) {
@@ -179,39 +233,17 @@ __device__ __forceinline__ float load_dev(const float *p) {
 // wait until this wave's outstanding vector memory operations have completed
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// Sequence and position of stacked token t (each lane passes its own t).
-// The token map is the prefix sum of gamma_i + 1, built 64 sequences at a
-// time with a wave scan; the owner of t is the last sequence starting <= t.
-__device__ inline void token_pos(const GemmParams &p, int t, int lane, int &seq, int &pos) {
-  int base = 0, found = 0, fstart = 0;
-  for (int c0 = 0; c0 < p.B; c0 += 64) {
-    const int i = c0 + lane;
-    const int v = i < p.B ? p.gamma[i] + 1 : 0;
-    int inc = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(inc, o);
-      if (lane >= o) inc += y;
-    }
-    const int start = base + inc - v;
-    const int n = min(64, p.B - c0);
-    for (int j = 0; j < n; ++j) {
-      const int sj = __shfl(start, j);
-      if (sj <= t) {
-        found = c0 + j;
-        fstart = sj;
-      }
-    }
-    base += __shfl(inc, 63);
-  }
-  seq = found;
-  pos = p.kv_len[seq] + (t - fstart);
+// Resident workgroups per CU to aim for: the skinny bf16 shapes are latency
+// bound, so more resident waves (fewer registers each) keep more loads in flight.
+template <int WT, int TT, int G> constexpr int min_wg_per_cu() {
+  return (WT == WT_BF16 && TT <= 2 && G <= 2) ? 8 : 1;
 }
 
-template <int WT, int TT>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
-  constexpr int MPS = WT == WT_BF16 ? 2 : 4;      // MFMAs per step per tile pair member
-  constexpr int P = TT <= 2 ? 4 : 3;              // prefetch depth in K steps
+// G = K steps of weights and tokens in flight per wave: 2 for long streams
+// (many resident waves share the work), 8 for short K splits (one round of
+// loads per unit).
+template <int WT, int TT, int EPI, int G>
+__global__ __launch_bounds__(kThreads, (min_wg_per_cu<WT, TT, G>())) void gemm_kernel(GemmParams p) {
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int gq = lane >> 4, l16 = lane & 15;
@@ -229,17 +261,16 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
   const int s1 = (int)((long long)(split + 1) * p.ksteps / p.splits);
   const int nsteps = s1 - s0;
 
-  // weight rows this lane streams (one per tile)
-  const void *wb[2];
-  const uint16_t *sb[2];
-  int prow[2];
+  // weight stream of each of the unit's two tiles (rows past the end of a
+  // matrix stream its first tile; their results are dropped)
+  WSrc<WT> src[2];
 #pragma unroll
   for (int tile = 0; tile < 2; ++tile) {
-    int mi = 0, pr = 0;
-    if (!map_row(p, grp, tile, l16, mi, pr)) { mi = 0; pr = 0; }
-    wb[tile] = p.mat[mi].w;
-    sb[tile] = p.mat[mi].s;
-    prow[tile] = pr;
+    int mi = 0, pr0 = 0;
+    if (!map_row(p, grp, tile, 0, mi, pr0)) { mi = 0; pr0 = 0; }
+    int pr = pr0 + l16;
+    if (pr >= p.mat[mi].rows) pr = pr0;
+    src[tile] = make_src<WT>(p.mat[mi], pr, pr0, p.K, p.ksteps, p.packed, lane, gq);
   }
   // token rows this lane reads (clamped; results of padding tokens are dropped)
   const uint16_t *xr[TT];
@@ -251,31 +282,29 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) acc[a][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float ss[TT];
-#pragma unroll
-  for (int tt = 0; tt < TT; ++tt) ss[tt] = 0.f;
 
-  WStep<WT> wbuf[P][2];
-  XStep<WT> xbuf[P][TT];
+  const int rot = (grp * 7 + tb * 3) % max(nsteps, 1);
+  // Grouped prefetch: G steps of weights and tokens in flight per wave, then
+  // compute.  A shallow group keeps the register count low, so many waves are
+  // resident and together keep the memory system busy.
+  for (int base = 0; base < nsteps; base += G) {
+    WStep<WT> wbuf[G][2];
+    XStep<WT> xbuf[G][TT];
 #pragma unroll
-  for (int j = 0; j < P; ++j) {
-    const int st = s0 + min(j, nsteps - 1);
+    for (int j = 0; j < G; ++j) {
+      // units start at staggered steps (the order is fixed per unit) so that
+      // waves do not all read the same token-operand lines at the same time
+      const int st = s0 + rotate_step(min(base + j, nsteps - 1), rot, nsteps);
 #pragma unroll
-    for (int tile = 0; tile < 2; ++tile) wbuf[j][tile] = load_w<WT>(wb[tile], sb[tile], prow[tile], p.K, st, gq);
+      for (int tile = 0; tile < 2; ++tile) wbuf[j][tile] = load_w<WT>(src[tile], st);
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt) xbuf[j][tt] = load_x<WT>(xr[tt], st, gq);
-  }
-
-  for (int base = 0; base < nsteps; base += P) {
+      for (int tt = 0; tt < TT; ++tt) xbuf[j][tt] = load_x<WT>(xr[tt], st, gq);
+    }
 #pragma unroll
-    for (int j = 0; j < P; ++j) {
+    for (int j = 0; j < G; ++j) {
       if (base + j < nsteps) {
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) {
-          if (p.norm) {
-#pragma unroll
-            for (int i = 0; i < (kstep<WT>() / 32); ++i) ss[tt] += sumsq8(xbuf[j][tt].v[i]);
-          }
 #pragma unroll
           for (int tile = 0; tile < 2; ++tile) {
             if constexpr (WT == WT_BF16) {
@@ -300,27 +329,12 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
           }
         }
       }
-      const int nx = s0 + min(base + j + P, nsteps - 1);
-#pragma unroll
-      for (int tile = 0; tile < 2; ++tile) wbuf[j][tile] = load_w<WT>(wb[tile], sb[tile], prow[tile], p.K, nx, gq);
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt) xbuf[j][tt] = load_x<WT>(xr[tt], nx, gq);
-    }
-  }
-  (void)MPS;
-
-  // sums of squares of this split's token slices: add the four lane groups
-  if (p.norm) {
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-      ss[tt] += __shfl_xor(ss[tt], 16);
-      ss[tt] += __shfl_xor(ss[tt], 32);
     }
   }
 
   // ---- K-split reduction ----------------------------------------------------
   if (p.splits > 1) {
-    constexpr int TILE = 2 * TT * 4 * 64 + TT * 64;  // partial values + sums of squares
+    constexpr int TILE = 2 * TT * 4 * 64;  // one partial value per (tile, token tile, row, lane)
     const size_t tile_id = (size_t)tb * ngrp + grp;
     float *mine = p.partial + ((size_t)split * ngrp * p.ntblk + tile_id) * TILE;
 #pragma unroll
@@ -329,10 +343,6 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
       for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) store_dev(mine + ((a * TT + tt) * 4 + i) * 64 + lane, acc[a][tt][i]);
-    if (p.norm) {
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt) store_dev(mine + 2 * TT * 4 * 64 + tt * 64 + lane, ss[tt]);
-    }
     wait_vmem();
     int old = 0;
     if (lane == 0)
@@ -344,8 +354,6 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
     for (int a = 0; a < 2; ++a)
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) acc[a][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) ss[tt] = 0.f;
     for (int sp = 0; sp < p.splits; ++sp) {
       const float *src = p.partial + ((size_t)sp * ngrp * p.ntblk + tile_id) * TILE;
 #pragma unroll
@@ -354,37 +362,58 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
         for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[a][tt][i] += load_dev(src + ((a * TT + tt) * 4 + i) * 64 + lane);
-      if (p.norm) {
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt) ss[tt] += load_dev(src + 2 * TT * 4 * 64 + tt * 64 + lane);
-      }
     }
   }
 
-  // per-token RMSNorm scale (lane's token is t0 + tt*16 + l16)
+  // per-token RMSNorm scale of the operand rows (lane's token is t0 + tt*16 + l16):
+  // precomputed scales, or sums of squares left in partials by the producer
   float rs[TT];
 #pragma unroll
-  for (int tt = 0; tt < TT; ++tt) rs[tt] = p.norm ? 1.f / sqrtf(ss[tt] / static_cast<float>(p.K) + p.eps) : 1.f;
+  for (int tt = 0; tt < TT; ++tt) {
+    const int t = min(t0 + tt * 16 + l16, p.T - 1);
+    if (p.rnorm) {
+      rs[tt] = p.rnorm[t];
+    } else if (p.rparts) {
+      // lane group gq adds partials gq, gq+4, ... of its token; then the groups
+      float s = 0.f;
+      const float *pr = p.rparts + (size_t)t * p.nparts;
+#pragma unroll 8
+      for (int g = gq; g < p.nparts; g += 4) s += pr[g];
+      s += __shfl_xor(s, 16);
+      s += __shfl_xor(s, 32);
+      rs[tt] = 1.f / sqrtf(s / static_cast<float>(p.K) + p.eps);
+    } else {
+      rs[tt] = 1.f;
+    }
+  }
 
   // ---- fused epilogues (lane-local) -----------------------------------------
-  if (p.epi == EPI_RESID) {
+  if constexpr (EPI == EPI_RESID) {
     uint16_t *out = static_cast<uint16_t *>(p.out);
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
       const int t = t0 + tt * 16 + l16;
-      if (t >= p.T) continue;
+      float sq = 0.f;  // this lane's share of the output row's sum of squares
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int n = grp * 32 + a * 16 + 4 * gq + i;
-          if (n < p.N) {
+          if (n < p.N && t < p.T) {
             const size_t o = (size_t)t * p.ldo + n;
-            out[o] = f2bf(acc[a][tt][i] * rs[tt] + bf2f(p.resid[o]));
+            const uint16_t h = f2bf(acc[a][tt][i] * rs[tt] + bf2f(p.resid[o]));
+            out[o] = h;
+            const float f = bf2f(h);
+            sq += f * f;
           }
         }
+      if (p.sq_out) {
+        sq += __shfl_xor(sq, 16);
+        sq += __shfl_xor(sq, 32);
+        if (gq == 0 && t < p.T) p.sq_out[(size_t)t * p.nblk + grp] = sq;
+      }
     }
-  } else if (p.epi == EPI_SWIGLU) {
+  } else if constexpr (EPI == EPI_SWIGLU) {
     uint16_t *out = static_cast<uint16_t *>(p.out);
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
@@ -400,7 +429,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
         }
       }
     }
-  } else if (p.epi == EPI_LOGITS) {
+  } else if constexpr (EPI == EPI_LOGITS) {
     float *out = static_cast<float *>(p.out);
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
@@ -424,9 +453,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
       s += __shfl_xor(s, 16);
       s += __shfl_xor(s, 32);
       if (gq == 0 && t < p.T) {
-        float *st = p.stats + ((size_t)grp * p.T + t) * 2;
-        st[0] = m;
-        st[1] = s;
+        *reinterpret_cast<float2 *>(p.stats + ((size_t)t * p.nblk + grp) * 2) = make_float2(m, s);
       }
     }
   } else {  // EPI_QKV: tile 0 holds pair firsts i, tile 1 the partners i + hd/2
@@ -436,9 +463,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
       const int t = t0 + tt * 16 + l16;
-      int seq = 0, pos = 0;
-      token_pos(p, min(t, p.T - 1), lane, seq, pos);
       if (t >= p.T) continue;
+      const int seq = p.tok_seq[t], pos = p.tok_pos[t];
       const bool kv_ok = pos >= 0 && pos < p.kv_cap;
       if (head >= p.hq && !kv_ok) {
         set_err(p.err, SV_DEV_ERR_KV_OVERFLOW);
@@ -450,12 +476,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
         const int fi = 16 * c + 4 * gq + e;  // rotation pair (fi, fi + hd/2)
         const float a = acc[0][tt][e] * rs[tt], b = acc[1][tt][e] * rs[tt];
         if (head < p.hq + p.hkv) {
-          const double inv = pow(static_cast<double>(p.rope_theta), -2.0 * fi / p.hd);
-          double sn, cs;
-          sincos(static_cast<double>(pos) * inv, &sn, &cs);
-          const float cf = static_cast<float>(cs), sf = static_cast<float>(sn);
-          ra[e] = a * cf - b * sf;
-          rb[e] = b * cf + a * sf;
+          const float2 cs = *reinterpret_cast<const float2 *>(p.rope_cs + ((size_t)t * half + fi) * 2);
+          ra[e] = a * cs.x - b * cs.y;
+          rb[e] = b * cs.x + a * cs.y;
         } else {
           ra[e] = a;
           rb[e] = b;
@@ -488,38 +511,111 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
   }
 }
 
-template <int WT, int TT>
-hipError_t launch_tt(const GemmParams &p, hipStream_t s, int trace_class) {
+template <int WT, int TT, int EPI, int G>
+hipError_t launch_g(const GemmParams &p, hipStream_t s, int trace_class) {
   const int nunits = p.nblk * p.splits * p.ntblk;
   const int nwg = (nunits + kWaves - 1) / kWaves;
   trace_before(trace_class, s);
-  hipLaunchKernelGGL((gemm_kernel<WT, TT>), dim3(nwg), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL((gemm_kernel<WT, TT, EPI, G>), dim3(nwg), dim3(kThreads), 0, s, p);
   trace_after(trace_class, s);
   return hipGetLastError();
 }
 
+template <int WT, int TT, int EPI>
+hipError_t launch_epi(const GemmParams &p, int depth, hipStream_t s, int trace_class) {
+  if constexpr (WT != WT_F32) {
+    if (depth >= 8) return launch_g<WT, TT, EPI, 8>(p, s, trace_class);
+  }
+  if (depth >= 4) return launch_g<WT, TT, EPI, 4>(p, s, trace_class);
+  return launch_g<WT, TT, EPI, 2>(p, s, trace_class);
+}
+
+template <int WT, int TT>
+hipError_t launch_tt(const GemmParams &p, int depth, hipStream_t s, int trace_class) {
+  switch (p.epi) {
+    case EPI_QKV: return launch_epi<WT, TT, EPI_QKV>(p, depth, s, trace_class);
+    case EPI_RESID: return launch_epi<WT, TT, EPI_RESID>(p, depth, s, trace_class);
+    case EPI_SWIGLU: return launch_epi<WT, TT, EPI_SWIGLU>(p, depth, s, trace_class);
+    default: return launch_epi<WT, TT, EPI_LOGITS>(p, depth, s, trace_class);
+  }
+}
+
 template <int WT>
-hipError_t launch_wt(const GemmParams &p, int tt, hipStream_t s, int tc) {
+hipError_t launch_wt(const GemmParams &p, int tt, int depth, hipStream_t s, int tc) {
   switch (tt) {
-    case 1: return launch_tt<WT, 1>(p, s, tc);
-    case 2: return launch_tt<WT, 2>(p, s, tc);
-    case 3: return launch_tt<WT, 3>(p, s, tc);
-    default: return launch_tt<WT, 4>(p, s, tc);
+    case 1: return launch_tt<WT, 1>(p, depth, s, tc);
+    case 2: return launch_tt<WT, 2>(p, depth, s, tc);
+    case 3: return launch_tt<WT, 3>(p, depth, s, tc);
+    default: return launch_tt<WT, 4>(p, depth, s, tc);
   }
 }
 
 }  // namespace
 
-hipError_t launch_gemm(const GemmParams &p, int wtype, int tok_tiles, hipStream_t s,
+hipError_t launch_gemm(const GemmParams &p, int wtype, int tok_tiles, int depth, hipStream_t s,
                        int trace_class) {
-  if (wtype == WT_BF16) return launch_wt<WT_BF16>(p, tok_tiles, s, trace_class);
-  if (wtype == WT_INT4) return launch_wt<WT_INT4>(p, tok_tiles, s, trace_class);
-  return launch_wt<WT_F32>(p, tok_tiles, s, trace_class);
+  if (wtype == WT_BF16) return launch_wt<WT_BF16>(p, tok_tiles, depth, s, trace_class);
+  if (wtype == WT_INT4) return launch_wt<WT_INT4>(p, tok_tiles, depth, s, trace_class);
+  return launch_wt<WT_F32>(p, tok_tiles, depth, s, trace_class);
+}
+
+namespace {
+// One thread per 16-byte fragment of the packed layout (see sv_pack_matrix).
+__global__ __launch_bounds__(256) void pack_bf16_kernel(const uint16_t *src, uint4 *dst, int N, int K) {
+  const int ks = K / 64;
+  const size_t total = (size_t)((N + 15) / 16) * ks * 128;
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int lane = idx & 63, m = (idx >> 6) & 1;
+  const size_t ts = idx >> 7;
+  const int step = (int)(ts % ks);
+  const size_t tile = ts / ks;
+  const size_t row = tile * 16 + (lane & 15);
+  const int k = step * 64 + 32 * m + 8 * (lane >> 4);
+  dst[idx] = row < (size_t)N ? *reinterpret_cast<const uint4 *>(src + row * K + k) : uint4{0u, 0u, 0u, 0u};
+}
+
+__global__ __launch_bounds__(256) void pack_int4_kernel(const uint32_t *src, const uint16_t *ssrc, uint4 *dst,
+                                                        uint16_t *sdst, int N, int K) {
+  const int ks = K / 128;
+  const size_t total = (size_t)((N + 15) / 16) * ks * 64;
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int lane = idx & 63;
+  const size_t ts = idx >> 6;
+  const int step = (int)(ts % ks);
+  const size_t tile = ts / ks;
+  const size_t row = tile * 16 + (lane & 15);
+  const int gq = lane >> 4;
+  if (row < (size_t)N) {
+    dst[idx] = *reinterpret_cast<const uint4 *>(src + row * (K / 8) + step * 16 + 4 * gq);
+    sdst[idx] = ssrc[row * (K / 32) + step * 4 + gq];
+  } else {
+    dst[idx] = uint4{0u, 0u, 0u, 0u};
+    sdst[idx] = 0;
+  }
+}
+}  // namespace
+
+hipError_t launch_pack(int wtype, int N, int K, const void *w, const void *scale, void *wp, void *sp,
+                       hipStream_t s) {
+  const size_t tiles = (size_t)(N + 15) / 16;
+  if (wtype == WT_BF16) {
+    const size_t total = tiles * (K / 64) * 128;
+    hipLaunchKernelGGL(pack_bf16_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+                       static_cast<const uint16_t *>(w), static_cast<uint4 *>(wp), N, K);
+  } else {
+    const size_t total = tiles * (K / 128) * 64;
+    hipLaunchKernelGGL(pack_int4_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+                       static_cast<const uint32_t *>(w), static_cast<const uint16_t *>(scale),
+                       static_cast<uint4 *>(wp), static_cast<uint16_t *>(sp), N, K);
+  }
+  return hipGetLastError();
 }
 
 size_t gemm_partial_floats(int ngroups, int splits, int ntblk, int tok_tiles) {
   if (splits <= 1) return 0;
-  return (size_t)splits * ngroups * ntblk * (2 * tok_tiles * 4 * 64 + tok_tiles * 64);
+  return (size_t)splits * ngroups * ntblk * (2 * tok_tiles * 4 * 64);
 }
 
 }  // namespace sv

@@ -7,41 +7,68 @@ namespace {
 constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 
-// p = exp(l - M) / S per row, where M and S combine the per-block statistics
-// (block max m_b, block sum of exp(l - m_b)) that the LM-head GEMM wrote.
-// The statistics are reduced in a fixed order, so every column block of a row
-// computes the same M and S.
-__global__ __launch_bounds__(kThreads) void head_softmax_kernel(HeadSoftmaxParams p) {
-  __shared__ float red[kThreads];
-  const int t = blockIdx.y, tid = threadIdx.x;
-  const float *st = p.stats;
-  float m = -INFINITY;
-  for (int b = tid; b < p.nblk; b += kThreads) m = fmaxf(m, st[((size_t)b * p.T + t) * 2]);
-  red[tid] = m;
+// p = exp(l - M) / S per row, where M and S combine the per-group statistics
+// (group max m_b, group sum of exp(l - m_b)) that the LM-head GEMM wrote,
+// token-major so that a row's statistics are one contiguous run.  They are
+// reduced in a fixed order, so every column block of a row computes the same
+// M and S.
+__device__ inline float block_max(float v, float *red) {
+  const int tid = threadIdx.x;
+  red[tid] = v;
   __syncthreads();
   for (int o = kThreads / 2; o > 0; o >>= 1) {
     if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
     __syncthreads();
   }
-  const float M = red[0];
+  const float r = red[0];
   __syncthreads();
-  float s = 0.f;
-  for (int b = tid; b < p.nblk; b += kThreads) {
-    const float *e = st + ((size_t)b * p.T + t) * 2;
-    s += e[1] * __builtin_amdgcn_exp2f((e[0] - M) * kLog2e);
-  }
-  red[tid] = s;
+  return r;
+}
+
+__device__ inline float block_sum(float v, float *red) {
+  const int tid = threadIdx.x;
+  red[tid] = v;
   __syncthreads();
   for (int o = kThreads / 2; o > 0; o >>= 1) {
     if (tid < o) red[tid] += red[tid + o];
     __syncthreads();
   }
-  const float S = red[0];
+  const float r = red[0];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(kThreads) void head_softmax_kernel(HeadSoftmaxParams p) {
+  __shared__ float red[kThreads];
+  const int t = blockIdx.y, tid = threadIdx.x;
+  const float2 *st = reinterpret_cast<const float2 *>(p.stats) + (size_t)t * p.nblk;
+  float m = -INFINITY;
+  for (int b = tid; b < p.nblk; b += kThreads) m = fmaxf(m, st[b].x);
+  const float M = block_max(m, red);
+  float s = 0.f;
+  for (int b = tid; b < p.nblk; b += kThreads) {
+    const float2 e = st[b];
+    s += e.y * __builtin_amdgcn_exp2f((e.x - M) * kLog2e);
+  }
+  const float S = block_sum(s, red);
   float *row = p.logits + (size_t)t * p.V;
   const int c0 = blockIdx.x * p.cols_per_block;
   const int c1 = min(p.V, c0 + p.cols_per_block);
-  for (int c = c0 + tid; c < c1; c += kThreads)
-    row[c] = __builtin_amdgcn_exp2f((row[c] - M) * kLog2e) / S;
+  const float Mk = M * kLog2e;
+  if ((p.V & 3) == 0) {  // rows are 16-byte aligned: four columns per load
+    float4 *r4 = reinterpret_cast<float4 *>(row);
+    for (int c = c0 / 4 + tid; c < c1 / 4; c += kThreads) {
+      float4 v = r4[c];
+      v.x = __builtin_amdgcn_exp2f(fmaf(v.x, kLog2e, -Mk)) / S;
+      v.y = __builtin_amdgcn_exp2f(fmaf(v.y, kLog2e, -Mk)) / S;
+      v.z = __builtin_amdgcn_exp2f(fmaf(v.z, kLog2e, -Mk)) / S;
+      v.w = __builtin_amdgcn_exp2f(fmaf(v.w, kLog2e, -Mk)) / S;
+      r4[c] = v;
+    }
+  } else {
+    for (int c = c0 + tid; c < c1; c += kThreads)
+      row[c] = __builtin_amdgcn_exp2f(fmaf(row[c], kLog2e, -Mk)) / S;
+  }
 }
 
 __global__ __launch_bounds__(kThreads) void embed_kernel(EmbedParams p) {

@@ -1,0 +1,94 @@
+// Per-call preparation pass: RMSNorm scales of the input rows and the token map.
+//
+// One workgroup per stacked token t:
+//   r[t] = 1 / sqrt(mean(x[t]^2) + eps), summed in a fixed order;
+//   (decoder calls) the token's sequence and position: sequence i owns rows
+//   q_start[i] .. q_start[i] + gamma_i (q_start = exclusive prefix sum of
+//   gamma_i + 1) and row j of it sits at position kv_len[i] + j.
+// Workgroup 0 also stores q_start[0..B] and the prefix sum of per-sequence
+// attention chunk counts ceil((kv_len[i] + gamma_i + 1) / chunk).
+// With a rotary table requested, each workgroup also stores cos and sin of
+// pos(t) * theta^(-2i/hd) for i < hd/2 (angles evaluated in fp64).
+#include "sv_common.h"
+
+namespace sv {
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ float red[kThreads];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  // sum of squares of row t: each thread a fixed set of 8-element chunks
+  const uint16_t *row = p.x + (size_t)t * p.d;
+  float s = 0.f;
+  for (int c = tid * 8; c < p.d; c += kThreads * 8) {
+    const uint4 v = *reinterpret_cast<const uint4 *>(row + c);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float a = __uint_as_float(w[i] << 16), b = __uint_as_float(w[i] & 0xFFFF0000u);
+      s += a * a;
+      s += b * b;
+    }
+  }
+  red[tid] = s;
+  __syncthreads();
+  for (int o = kThreads / 2; o > 0; o >>= 1) {
+    if (tid < o) red[tid] += red[tid + o];
+    __syncthreads();
+  }
+  if (tid == 0) p.rnorm[t] = 1.f / sqrtf(red[0] / static_cast<float>(p.d) + p.eps);
+  if (!p.gamma) return;
+
+  int *qs = reinterpret_cast<int *>(smem);
+  int *cs = qs + p.B + 1;
+  int *tmp = cs + p.B + 1;
+  for (int i = tid; i < p.B; i += kThreads) {
+    const int g = p.gamma[i];
+    qs[i] = g + 1;
+    cs[i] = (p.kv_len[i] + g + 1 + p.chunk - 1) / p.chunk;
+  }
+  __syncthreads();
+  const int total_t = block_exscan(qs, p.B, tmp);
+  const int total_c = block_exscan(cs, p.B, tmp);
+  const int seq = upper_index(qs, p.B, t);
+  const int pos = p.kv_len[seq] + (t - qs[seq]);
+  if (tid == 0) {
+    p.tok_seq[t] = seq;
+    p.tok_pos[t] = pos;
+  }
+  if (p.rope_cs) {
+    const int half = p.hd / 2;
+    for (int i = tid; i < half; i += kThreads) {
+      const double inv = pow(static_cast<double>(p.rope_theta), -2.0 * i / p.hd);
+      double sn, cs;
+      sincos(static_cast<double>(pos) * inv, &sn, &cs);
+      p.rope_cs[((size_t)t * half + i) * 2] = static_cast<float>(cs);
+      p.rope_cs[((size_t)t * half + i) * 2 + 1] = static_cast<float>(sn);
+    }
+  }
+  if (t == 0) {
+    for (int i = tid; i < p.B; i += kThreads) {
+      p.q_start[i] = qs[i];
+      p.chunk_start[i] = cs[i];
+    }
+    if (tid == 0) {
+      p.q_start[p.B] = total_t;
+      p.chunk_start[p.B] = total_c;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prep(const PrepParams &p, hipStream_t s) {
+  const size_t lds = p.gamma ? (size_t)(2 * (p.B + 1) + 260) * sizeof(int) : 0;
+  trace_before(SV_K_PREP, s);
+  hipLaunchKernelGGL(prep_kernel, dim3(p.T), dim3(kThreads), lds, s, p);
+  trace_after(SV_K_PREP, s);
+  return hipGetLastError();
+}
+
+}  // namespace sv

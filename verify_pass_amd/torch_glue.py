@@ -10,8 +10,9 @@ import ctypes as C
 import numpy as np
 import torch
 
-from . import (SV_LAYER_DECODER, SV_LAYER_EMBED, SV_LAYER_HEAD, WTYPES, sv_batch, sv_layer,
-               sv_matrix)
+from . import (SV_LAYER_DECODER, SV_LAYER_EMBED, SV_LAYER_HEAD, SV_LAYOUT_PACKED,
+               SV_LAYOUT_ROWMAJOR, SV_OK, WTYPES, SvError, sv_batch, sv_layer, sv_matrix,
+               sv_pack_matrix, sv_packed_matrix_bytes)
 
 __all__ = ["to_dev", "stream_handle", "workspace", "DeviceMatrix", "upload_matrix",
            "decoder_struct", "head_struct", "embed_struct", "DeviceBatch"]
@@ -51,14 +52,28 @@ class DeviceMatrix:
             0 if self.scale is None else self.scale.numel() * self.scale.element_size())
 
 
-def upload_matrix(m, device="cuda") -> DeviceMatrix:
-    """workloads.Weights -> DeviceMatrix."""
-    return DeviceMatrix(to_dev(m.data, device), None if m.scale is None else to_dev(m.scale, device))
+def upload_matrix(m, device="cuda", packed=False) -> DeviceMatrix:
+    """workloads.Weights -> DeviceMatrix, optionally re-laid out by the
+    library's packing kernel (sv_pack_matrix)."""
+    w = to_dev(m.data, device)
+    s = None if m.scale is None else to_dev(m.scale, device)
+    if not packed:
+        return DeviceMatrix(w, s)
+    wt = WTYPES[m.wtype]
+    wb, sb = sv_packed_matrix_bytes(wt, m.n, m.k)
+    wp = torch.empty(wb, dtype=torch.uint8, device=device)
+    sp = torch.empty(max(sb, 1), dtype=torch.uint8, device=device) if sb else None
+    st = sv_pack_matrix(wt, m.n, m.k, w, s, wp, sp, stream_handle())
+    if st != SV_OK:
+        raise SvError(st, "sv_pack_matrix")
+    torch.cuda.synchronize()
+    return DeviceMatrix(wp, sp)
 
 
-def decoder_struct(shape, wtype: str, mats: dict, eps=1e-6, theta=10000.0) -> sv_layer:
+def decoder_struct(shape, wtype: str, mats: dict, eps=1e-6, theta=10000.0, packed=False) -> sv_layer:
     L = sv_layer()
     L.kind, L.wtype = SV_LAYER_DECODER, WTYPES[wtype]
+    L.layout = SV_LAYOUT_PACKED if packed else SV_LAYOUT_ROWMAJOR
     L.d, L.n_q_heads, L.n_kv_heads = shape.d, shape.n_q, shape.n_kv
     L.head_dim, L.ffn, L.vocab = shape.hd, shape.ffn, shape.vocab
     L.eps, L.rope_theta = eps, theta
@@ -67,9 +82,10 @@ def decoder_struct(shape, wtype: str, mats: dict, eps=1e-6, theta=10000.0) -> sv
     return L
 
 
-def head_struct(shape, wtype: str, lm: DeviceMatrix, eps=1e-6) -> sv_layer:
+def head_struct(shape, wtype: str, lm: DeviceMatrix, eps=1e-6, packed=False) -> sv_layer:
     L = sv_layer()
     L.kind, L.wtype = SV_LAYER_HEAD, WTYPES[wtype]
+    L.layout = SV_LAYOUT_PACKED if packed else SV_LAYOUT_ROWMAJOR
     L.d, L.vocab, L.eps = shape.d, shape.vocab, eps
     L.lm_head = lm.struct()
     return L
