@@ -283,6 +283,20 @@ sv_status sv_plan_gamma(const sv_plan_params *params, int32_t B_live, int32_t *g
 sv_status sv_trace_begin(int32_t kernel_class, int32_t capacity);
 sv_status sv_trace_end(float *ms_out, int32_t capacity, int32_t *count);
 
+/* Launch-policy override for the GEMMs of later sv_verify_layer calls (and
+ * their workspace sizes), for tuning sweeps and tests; results stay within
+ * the same error bounds, though the summation order changes.  spec is a
+ * comma-separated list of kind:splits:depth[:waves] entries, kind one of
+ * qkv, o, gu, down, head; splits = K splits across workgroups, depth = K steps
+ * in flight per wave (2, 4 or 8), waves = waves of one workgroup sharing a
+ * unit's K range (1, 4, 8 or 16).  Zero or an absent kind keeps the default
+ * policy; settings beyond a kernel's register budget fall back to the nearest
+ * smaller one.  NULL restores the defaults (also read from the environment
+ * variable SV_GEMM_TUNE when the library loads).  Process-wide; set it
+ * between calls, not while another thread is inside the library.
+ * SV_ERR_INVALID_ARG for a malformed spec (the setting is unchanged). */
+sv_status sv_set_gemm_tuning(const char *spec);
+
 /* Message for a status code (static string). */
 const char *sv_status_string(sv_status status);
 

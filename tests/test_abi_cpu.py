@@ -213,3 +213,26 @@ def test_packed_sizes_and_validation():
     L = _layer()
     L.layout = 5
     assert _ws(L, _batch([1]))[0] == sv.SV_ERR_INVALID_ARG
+
+
+def test_gemm_tuning_setter():
+    """The launch-policy override parses, changes the plan (workspace size with
+    K splits across workgroups) and restores the defaults."""
+    L, b = _layer(d=1024, hq=8, hk=2, hd=128, ffn=4096), _batch([2, 0, 3])
+    try:
+        assert sv.sv_set_gemm_tuning(None) == sv.SV_OK
+        st, base = _ws(L, b)
+        assert st == sv.SV_OK
+        assert sv.sv_set_gemm_tuning("qkv:1:4:1,o:1:4:1,gu:1:4:1,down:1:4:1") == sv.SV_OK
+        st, single = _ws(L, b)
+        assert st == sv.SV_OK
+        assert sv.sv_set_gemm_tuning("down:8:4:1,gu:4:8") == sv.SV_OK
+        st, split = _ws(L, b)
+        assert st == sv.SV_OK and split > single
+        for bad in ("gu:x", "down:-1:4", "qkv:2"):
+            assert sv.sv_set_gemm_tuning(bad) == sv.SV_ERR_INVALID_ARG
+        assert _ws(L, b)[1] == split          # a rejected spec leaves the setting alone
+        assert sv.sv_set_gemm_tuning(None) == sv.SV_OK
+        assert _ws(L, b)[1] == base
+    finally:
+        sv.sv_set_gemm_tuning(None)

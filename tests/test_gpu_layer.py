@@ -235,3 +235,64 @@ def test_tiny_model_end_to_end():
     say(f"tiny model: accepted gpu={ga.tolist()} oracle-p={oa.tolist()} next {gy.tolist()}/{oy.tolist()}")
     for ly in layers:
         assert ly.batch.err.item() == 0
+
+
+# Launch settings (splits:depth:waves per unit) covering every GEMM variant:
+# waves per unit 1/4/8/16, depth 2/4/8, K splits across units alone and on
+# top of in-workgroup splits, uneven split sizes; settings beyond a kernel's
+# register budget fall back to smaller ones, which the same comparison covers.
+LAUNCH_SETTINGS = [
+    None,
+    "qkv:1:8:4,o:1:8:4,gu:1:8:4,down:1:8:4",
+    "qkv:1:4:8,o:1:8:8,gu:1:8:8,down:2:8:8",
+    "qkv:2:4:16,o:1:4:16,gu:1:4:16,down:4:4:16",
+    "qkv:4:2:1,o:2:4:1,gu:3:8:1,down:5:2:1",
+]
+
+
+@pytest.mark.parametrize("wtype", ["bf16", "int4", "f32"])
+@pytest.mark.parametrize("gamma", [[2, 0, 5, 1, 3, 1, 0, 4], [7, 7, 7, 7, 7, 7, 3, 2]],
+                         ids=["T24", "T55"])
+def test_decoder_launch_settings(wtype, gamma):
+    shape = Shape(2048, 16, 4, 128, 8192, 1000)
+    ctx = [300, 0, 777, 64, 1500, 5, 256, 900]
+    wl = custom_workload(shape, wtype, gamma, ctx, seed=5)
+    dec = GpuDecoder(wl, packed=wtype != "f32")
+    xh = hidden_states(wl.T, shape.d, wl.seed)
+    x = tg.to_dev(xh)
+    ref = dec.oracle(xh)
+    try:
+        for spec in LAUNCH_SETTINGS:
+            assert sv.sv_set_gemm_tuning(spec) == 0
+            dec.ws_bytes = sv.sv_verify_layer_workspace_bytes(dec.L, dec.bs)
+            dec.ws = tg.workspace(dec.ws_bytes)
+            y = dec.run(x)
+            torch.cuda.synchronize()
+            err = rel_rows(dev_bf16_to_f64(y), ref.y)
+            say(f"decoder {wtype} T={wl.T} [{spec}]: y rel err {err:.2e}")
+            assert err < TOL[wtype], spec
+            assert dec.batch.err.item() == 0
+    finally:
+        sv.sv_set_gemm_tuning(None)
+
+
+@pytest.mark.parametrize("wtype", ["bf16", "int4"])
+def test_head_launch_settings(wtype):
+    shape = Shape(1024, 8, 2, 128, 1024, 20011)
+    wl = custom_workload(shape, wtype, [2, 0, 4, 3, 9], [1, 1, 1, 1, 1], seed=13)
+    head = GpuHead(wl, packed=True)
+    yh = hidden_states(wl.T, shape.d, 78)
+    yd = tg.to_dev(yh)
+    ref = OV.head_logits(head.Wlm, yh)
+    try:
+        for spec in (None, "head:1:4:1", "head:1:8:1", "head:1:8:4", "head:2:4:8", "head:3:8:1"):
+            assert sv.sv_set_gemm_tuning(spec) == 0
+            n = sv.sv_verify_layer_workspace_bytes(head.L, head.bs, sv.SV_HEAD_LOGITS)
+            head.ws = tg.workspace(n)
+            head.ws_bytes[sv.SV_HEAD_LOGITS] = n
+            lg = head.run(yd, logits=True).cpu().numpy()
+            err = rel_rows(lg, ref)
+            say(f"head {wtype} [{spec}]: logits rel err {err:.2e}")
+            assert err < TOL[wtype], spec
+    finally:
+        sv.sv_set_gemm_tuning(None)

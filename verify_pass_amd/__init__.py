@@ -87,6 +87,7 @@ _SIGNATURES = [
      [C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]),
     ("sv_plan_gamma", C.c_int32,
      [C.POINTER(sv_plan_params), C.c_int32, C.POINTER(C.c_int32), C.POINTER(C.c_double)]),
+    ("sv_set_gemm_tuning", C.c_int32, [C.c_char_p]),
     ("sv_trace_begin", C.c_int32, [C.c_int32, C.c_int32]),
     ("sv_trace_end", C.c_int32, [C.POINTER(C.c_float), C.c_int32, C.POINTER(C.c_int32)]),
     ("sv_status_string", C.c_char_p, [C.c_int32]),
@@ -188,6 +189,10 @@ def sv_plan_gamma(params: sv_plan_params, B_live: int):
     bstar = C.c_double(0.0)
     st = _lib.sv_plan_gamma(C.byref(params), B_live, out, C.byref(bstar))
     return st, [int(out[i]) for i in range(B_live)], bstar.value
+
+
+def sv_set_gemm_tuning(spec: str | None) -> int:
+    return _lib.sv_set_gemm_tuning(None if spec is None else spec.encode())
 
 
 def sv_trace_begin(kernel_class: int, capacity: int) -> int:

@@ -16,7 +16,8 @@ CSRC = os.path.dirname(os.path.abspath(__file__))
 PKG = os.path.dirname(CSRC)
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsv.so")
-SOURCES = ["sv_prep.hip", "sv_gemm.hip", "sv_attn.hip", "sv_head.hip", "sv_accept.hip", "sv_abi.cpp",
+SOURCES = ["sv_prep.hip", "sv_gemm.hip", "sv_gemm_bf16.hip", "sv_gemm_int4.hip", "sv_gemm_f32.hip",
+           "sv_attn.hip", "sv_head.hip", "sv_accept.hip", "sv_abi.cpp",
            "sv_plan.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Wall", "-Wno-unused-function",
@@ -39,7 +40,7 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False, jobs: int = 6) -> str:
+def build(verbose: bool = False, jobs: int = 8) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))

@@ -106,45 +106,61 @@ constexpr size_t kMaxCounters = kCounterBytes / sizeof(int);
 // GEMM kinds of one pass (for the launch policy and its tuning override).
 enum GemmKind { GK_QKV = 0, GK_O, GK_GU, GK_DOWN, GK_HEAD, GK_COUNT };
 
-// Optional override of the (splits, depth) policy for tuning sweeps:
-// SV_GEMM_TUNE="qkv:8:8,o:8:8,gu:2:8,down:16:8,head:1:2" (kind:splits:depth).
+// Optional override of the launch policy (tuning sweeps, tests):
+// "qkv:1:4:16,o:1:4:16,gu:1:8:4,down:1:8:16,head:1:2:1"
+// (kind:splits:depth[:waves per unit]), from SV_GEMM_TUNE at load time or
+// sv_set_gemm_tuning.
 struct Tune {
   int splits[GK_COUNT];
   int depth[GK_COUNT];
+  int kw[GK_COUNT];
 };
-const Tune &tune() {
-  static Tune t = [] {
-    Tune r;
-    for (int i = 0; i < GK_COUNT; ++i) r.splits[i] = r.depth[i] = 0;
-    const char *e = std::getenv("SV_GEMM_TUNE");
-    if (!e) return r;
-    const char *names[GK_COUNT] = {"qkv", "o", "gu", "down", "head"};
-    for (int i = 0; i < GK_COUNT; ++i) {
-      const char *f = std::strstr(e, names[i]);
-      while (f && f != e && f[-1] != ',') f = std::strstr(f + 1, names[i]);
-      if (!f) continue;
-      int s = 0, d = 0;
-      if (std::sscanf(f + std::strlen(names[i]), ":%d:%d", &s, &d) == 2) {
-        r.splits[i] = s;
-        r.depth[i] = d;
-      }
-    }
-    return r;
-  }();
-  return t;
+
+bool parse_tune(const char *e, Tune &r) {
+  for (int i = 0; i < GK_COUNT; ++i) r.splits[i] = r.depth[i] = r.kw[i] = 0;
+  if (!e) return true;
+  const char *names[GK_COUNT] = {"qkv", "o", "gu", "down", "head"};
+  for (int i = 0; i < GK_COUNT; ++i) {
+    const char *f = std::strstr(e, names[i]);
+    while (f && !((f == e || f[-1] == ',') && f[std::strlen(names[i])] == ':'))
+      f = std::strstr(f + 1, names[i]);
+    if (!f) continue;
+    int s = 0, d = 0, k = 0;
+    const int n = std::sscanf(f + std::strlen(names[i]), ":%d:%d:%d", &s, &d, &k);
+    if (n < 2 || s < 0 || d < 0 || k < 0) return false;
+    r.splits[i] = s;
+    r.depth[i] = d;
+    if (n == 3) r.kw[i] = k;
+  }
+  return true;
+}
+
+std::mutex g_tune_mu;
+Tune g_tune = [] {
+  Tune r;
+  if (!parse_tune(std::getenv("SV_GEMM_TUNE"), r)) parse_tune(nullptr, r);
+  return r;
+}();
+
+Tune tune() {
+  std::lock_guard<std::mutex> lk(g_tune_mu);
+  return g_tune;
 }
 
 struct GemmCfg {
-  int nblk = 0, ntblk = 0, splits = 1, tt = 1, ksteps = 0, K = 0, N = 0, depth = 2;
+  int nblk = 0, ntblk = 0, splits = 1, tt = 1, ksteps = 0, K = 0, N = 0, depth = 2, kw = 1;
   size_t partial_floats() const { return gemm_partial_floats(nblk, splits, ntblk, tt); }
   size_t counters() const { return splits > 1 ? (size_t)nblk * ntblk : 0; }
 };
 
 // nblk: 32-row groups (16 gate/up feature pairs for SwiGLU).
-// Enough row groups to fill the chip: no K split, a shallow prefetch and many
-// resident waves.  Too few: a deep prefetch (8 steps in flight per wave) and
-// K split into units of about 16 steps, at most one round of units.
+// Enough row groups to fill the chip (2048 waves): one wave per unit, no K
+// split, a shallow prefetch and many resident waves.  Too few: several waves
+// of one workgroup per unit (4, 8 or 16, each at least 4 K steps), the fewest
+// that reach 2048 waves; K split across units only if that is still short.
+// The prefetch depth then covers a wave's steps in one or two rounds.
 GemmCfg gemm_cfg(int kind, int nblk, int N, int T, int K, int wtype) {
+  constexpr int kFill = 2048;
   GemmCfg c;
   c.nblk = nblk;
   c.N = N;
@@ -153,17 +169,36 @@ GemmCfg gemm_cfg(int kind, int nblk, int N, int T, int K, int wtype) {
   c.ntblk = (T + 16 * c.tt - 1) / (16 * c.tt);
   c.ksteps = K / kstep_of(wtype);
   const int base = std::max(1, nblk * c.ntblk);
-  if (base >= 2048) {
+  if (base >= kFill) {
     c.splits = 1;
+    c.kw = 1;
     c.depth = 2;
   } else {
-    // about 16 steps per unit, at most 2048 units (resident at depth 8)
-    c.splits = std::max(1, std::min(std::min(c.ksteps / 16, 32), 2048 / base));
-    c.depth = 8;
+    const int wt = wtype == SV_W_BF16 ? WT_BF16 : wtype == SV_W_INT4_G32 ? WT_INT4 : WT_F32;
+    for (int k : {4, 8, 16}) {
+      if (c.ksteps / k < 4 || !gemm_kw_ok(wt, c.tt, k)) break;
+      c.kw = k;
+      if ((long long)base * k >= kFill) break;
+    }
+    const int waves = base * c.kw;
+    if (waves < kFill) {
+      const int room = std::max(1, c.ksteps / (4 * c.kw));
+      c.splits = std::max(1, std::min(room, (kFill + waves - 1) / waves));
+    }
+    // 8 steps in flight take about 240 registers (2 waves per SIMD, 2048
+    // resident): only when every wave is resident and has 8 steps to fetch
+    const bool deep = gemm_deep_ok(wt, c.tt, c.kw);
+    const long long nw = (long long)base * c.kw * c.splits;
+    c.depth = deep && nw <= kFill && c.ksteps / (c.splits * c.kw) >= 8 ? 8 : 4;
+    // at most two rounds of loads per wave while 4096 waves stay resident
+    while (c.depth == 4 && c.ksteps / (c.splits * c.kw) > 8 &&
+           (long long)base * c.kw * (c.splits + 1) <= 2 * kFill && c.ksteps / ((c.splits + 1) * c.kw) >= 4)
+      ++c.splits;
   }
-  const Tune &tn = tune();
+  const Tune tn = tune();
   if (tn.splits[kind] > 0) c.splits = std::max(1, std::min(tn.splits[kind], c.ksteps));
   if (tn.depth[kind] > 0) c.depth = tn.depth[kind];
+  if (tn.kw[kind] > 0) c.kw = tn.kw[kind] >= 16 ? 16 : tn.kw[kind] >= 8 ? 8 : tn.kw[kind] >= 4 ? 4 : 1;
   if (c.splits > 1 && (size_t)base > kMaxCounters) c.splits = 1;
   return c;
 }
@@ -382,7 +417,7 @@ extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const
     p.out = y_out;
     p.ldo = L->vocab;
     p.stats = reinterpret_cast<float *>(ws + pl.off_stats);
-    e = launch_gemm(p, wt, pl.head.tt, pl.head.depth, s, SV_K_GEMM_LM_HEAD);
+    e = launch_gemm(p, wt, pl.head.tt, pl.head.depth, pl.head.kw, s, SV_K_GEMM_LM_HEAD);
     if (e == hipSuccess && !(flags & SV_HEAD_LOGITS)) {
       HeadSoftmaxParams h;
       h.logits = static_cast<float *>(y_out);
@@ -427,7 +462,8 @@ extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const
     pp.chunk_start = cstart;
     pp.rope_cs = reinterpret_cast<float *>(ws + pl.off_rope);
     pp.hd = hd;
-    pp.rope_theta = L->rope_theta;
+    for (int i = 0; i < hd / 2; ++i)
+      pp.inv_freq[i] = std::pow(static_cast<double>(L->rope_theta), -2.0 * i / hd);
     e = launch_prep(pp, s);
     if (e != hipSuccess) return SV_ERR_HIP;
   }
@@ -446,7 +482,6 @@ extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const
     p.qbuf = qbuf;
     p.hq = hq;
     p.hkv = hk;
-    p.rope_theta = L->rope_theta;
     p.tok_seq = tseq;
     p.tok_pos = tpos;
     p.rope_cs = reinterpret_cast<const float *>(ws + pl.off_rope);
@@ -455,7 +490,7 @@ extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const
     p.kc = b->k_cache;
     p.vc = b->v_cache;
     p.err = b->err_flag;
-    e = launch_gemm(p, wt, pl.qkv.tt, pl.qkv.depth, s, SV_K_GEMM_QKV);
+    e = launch_gemm(p, wt, pl.qkv.tt, pl.qkv.depth, pl.qkv.kw, s, SV_K_GEMM_QKV);
     if (e != hipSuccess) return SV_ERR_HIP;
   }
   {  // ragged attention + merge
@@ -498,7 +533,7 @@ extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const
     p.ldo = d;
     p.resid = static_cast<const uint16_t *>(x_in);
     p.sq_out = rparts;  // sums of squares of x1 for the next RMSNorm
-    e = launch_gemm(p, wt, pl.o.tt, pl.o.depth, s, SV_K_GEMM_O);
+    e = launch_gemm(p, wt, pl.o.tt, pl.o.depth, pl.o.kw, s, SV_K_GEMM_O);
     if (e != hipSuccess) return SV_ERR_HIP;
   }
   {  // gate || up + SwiGLU
@@ -514,7 +549,7 @@ extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const
     p.epi = EPI_SWIGLU;
     p.out = act;
     p.ldo = F;
-    e = launch_gemm(p, wt, pl.gu.tt, pl.gu.depth, s, SV_K_GEMM_GATE_UP);
+    e = launch_gemm(p, wt, pl.gu.tt, pl.gu.depth, pl.gu.kw, s, SV_K_GEMM_GATE_UP);
     if (e != hipSuccess) return SV_ERR_HIP;
   }
   {  // down projection + residual
@@ -527,7 +562,7 @@ extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const
     p.out = y_out;
     p.ldo = d;
     p.resid = x1;
-    e = launch_gemm(p, wt, pl.down.tt, pl.down.depth, s, SV_K_GEMM_DOWN);
+    e = launch_gemm(p, wt, pl.down.tt, pl.down.depth, pl.down.kw, s, SV_K_GEMM_DOWN);
     if (e != hipSuccess) return SV_ERR_HIP;
   }
   return SV_OK;
@@ -655,4 +690,12 @@ extern "C" sv_status sv_accept_commit(int32_t B, int32_t V, int32_t mode, const 
   (void)hipGetLastError();
   const hipError_t e = launch_accept(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+extern "C" sv_status sv_set_gemm_tuning(const char *spec) {
+  Tune r;
+  if (!parse_tune(spec, r)) return SV_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lk(g_tune_mu);
+  g_tune = r;
+  return SV_OK;
 }

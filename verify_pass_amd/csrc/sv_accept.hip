@@ -7,20 +7,22 @@
 // the order in which lanes and workgroups add them, so the token drawn for a
 // given uniform is the same on any grid shape.
 //
-// One kernel, grid = vocabulary chunks x sequences (x target rows in greedy
-// mode).  Every workgroup runs the sequence's acceptance tests (one draft per
-// lane, first rejection by LDS atomic min) and sums the integer weights of its
-// chunk of the resampling row, of the fallback target row, and the chunk's
-// argmax.  It publishes them with device-scope stores and bumps the
-// sequence's arrival counter; the last workgroup to arrive turns the uniform
-// into an integer target, finds the chunk holding it from the chunk sums,
-// scans that chunk exactly (staged through LDS) and commits.
+// One kernel, grid = vocabulary chunks x sequences.  Every workgroup of a
+// sequence reduces its chunk (stochastic: the acceptance tests, then integer
+// weight sums of the resampling row and of the fallback target row and the
+// chunk argmax; greedy: the chunk argmax of each of the sequence's target
+// rows), publishes the result with device-scope stores and counts its
+// arrival.  The last workgroup to arrive combines the chunk results with
+// block-wide reductions and scans, and commits.
 #include "sv_common.h"
 
 namespace sv {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kWavesA = kThreads / 64;
+constexpr int kSegMax = 32;  // chunk / kThreads: elements per thread in the exact scan
+constexpr int kVecA = kSegMax / 4;  // float4 loads per thread and row over a chunk
 constexpr float kTwo32 = 4294967296.0f;
 
 typedef unsigned long long u64;
@@ -30,7 +32,7 @@ __device__ __forceinline__ u64 weight_of(float r) {
   return static_cast<u64>(r * kTwo32);
 }
 
-// argmax combine: larger value wins, lower index on ties
+// argmax combine: larger value wins, lower index on ties (order-independent)
 __device__ __forceinline__ void amax(float &v, int &i, float v2, int i2) {
   if (v2 > v || (v2 == v && i2 < i)) {
     v = v2;
@@ -38,39 +40,73 @@ __device__ __forceinline__ void amax(float &v, int &i, float v2, int i2) {
   }
 }
 
-__device__ inline void block_reduce(u64 &a, u64 &b, float &v, int &ix, u64 *sa, u64 *sb, float *sv,
-                                    int *si) {
-  const int tid = threadIdx.x;
-  sa[tid] = a;
-  sb[tid] = b;
-  sv[tid] = v;
-  si[tid] = ix;
-  __syncthreads();
-  for (int o = kThreads / 2; o > 0; o >>= 1) {
-    if (tid < o) {
-      sa[tid] += sa[tid + o];
-      sb[tid] += sb[tid + o];
-      float vv = sv[tid];
-      int ii = si[tid];
-      amax(vv, ii, sv[tid + o], si[tid + o]);
-      sv[tid] = vv;
-      si[tid] = ii;
-    }
-    __syncthreads();
+struct Shared {
+  u64 a[kWavesA], b[kWavesA];
+  float v[kWavesA];
+  int i[kWavesA];
+  int first_fail, bad, flag, found, chunk_hit, result;
+  u64 target;
+};
+
+// Block-wide sums of two u64 values and an argmax; every thread gets the result.
+__device__ inline void block_reduce(u64 &a, u64 &b, float &v, int &ix, Shared &sh) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    a += __shfl_xor(a, o);
+    b += __shfl_xor(b, o);
+    const float v2 = __shfl_xor(v, o);
+    const int i2 = __shfl_xor(ix, o);
+    amax(v, ix, v2, i2);
   }
-  a = sa[0];
-  b = sb[0];
-  v = sv[0];
-  ix = si[0];
+  if (lane == 0) {
+    sh.a[w] = a;
+    sh.b[w] = b;
+    sh.v[w] = v;
+    sh.i[w] = ix;
+  }
+  __syncthreads();
+  a = 0;
+  b = 0;
+  v = -INFINITY;
+  ix = 0x7fffffff;
+#pragma unroll
+  for (int k = 0; k < kWavesA; ++k) {
+    a += sh.a[k];
+    b += sh.b[k];
+    amax(v, ix, sh.v[k], sh.i[k]);
+  }
   __syncthreads();
 }
 
+// Exclusive prefix sum over the block in thread order; *total gets the sum.
+__device__ inline u64 block_exscan(u64 v, u64 *total, Shared &sh) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  u64 inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const u64 y = __shfl_up(inc, o);
+    if (lane >= o) inc += y;
+  }
+  if (lane == 63) sh.a[w] = inc;
+  __syncthreads();
+  u64 before = 0, tot = 0;
+#pragma unroll
+  for (int k = 0; k < kWavesA; ++k) {
+    if (k < w) before += sh.a[k];
+    tot += sh.a[k];
+  }
+  __syncthreads();
+  *total = tot;
+  return before + inc - v;
+}
+
 // Device-scope (cross-XCD coherent) stores and loads of the chunk results.
-__device__ __forceinline__ void put_part(AcceptPart *p, const AcceptPart &v) {
+__device__ __forceinline__ void put_part(AcceptPart *p, u64 sres, u64 sp, float mv, int mi) {
   u64 *w = reinterpret_cast<u64 *>(p);
-  __hip_atomic_store(w, v.sum_res, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(w + 1, v.sum_p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const u64 mx = (static_cast<u64>(static_cast<uint32_t>(v.arg_p)) << 32) | __float_as_uint(v.max_p);
+  __hip_atomic_store(w, sres, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(w + 1, sp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const u64 mx = (static_cast<u64>(static_cast<uint32_t>(mi)) << 32) | __float_as_uint(mv);
   __hip_atomic_store(w + 2, mx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ AcceptPart get_part(const AcceptPart *p) {
@@ -85,226 +121,259 @@ __device__ __forceinline__ AcceptPart get_part(const AcceptPart *p) {
 }
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// Publish, count the arrival, and tell whether this workgroup arrived last
-// (then the counter is reset for the next call).
-__device__ inline bool arrive_last(int *ctr, int expected, int *flag) {
+// Count this workgroup's arrival after its results are stored; true for the
+// last of `expected` (which resets the counter for the next call).
+__device__ inline bool arrive_last(int *ctr, int expected, Shared &sh) {
   wait_vmem();
   __syncthreads();
   if (threadIdx.x == 0) {
     const int old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *flag = old == expected - 1;
-    if (*flag) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sh.flag = old == expected - 1;
+    if (sh.flag) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
-  return *flag != 0;
+  return sh.flag != 0;
 }
 
-// q_start of sequence i (exclusive prefix sum of gamma + 1), by a block reduction.
-__device__ inline int seq_start(const int *gamma, int i, int *red) {
-  int s = 0;
+// q_start of sequence i: sum of gamma_k + 1 over k < i.
+__device__ inline int seq_start(const int *gamma, int i, Shared &sh) {
+  u64 s = 0, z = 0;
   for (int k = threadIdx.x; k < i; k += kThreads) s += gamma[k] + 1;
-  red[threadIdx.x] = s;
-  __syncthreads();
-  for (int o = kThreads / 2; o > 0; o >>= 1) {
-    if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
-    __syncthreads();
+  float v = 0.f;
+  int ix = 0;
+  block_reduce(s, z, v, ix, sh);
+  return static_cast<int>(s);
+}
+
+// This thread's share of the argmax of row[x0, x1).
+__device__ inline void chunk_argmax(const float *row, int x0, int x1, bool vec, float &bv, int &bi) {
+  bv = -INFINITY;
+  bi = 0x7fffffff;
+  if (vec) {
+    const float4 *r4 = reinterpret_cast<const float4 *>(row);
+    float4 v[kVecA];
+#pragma unroll
+    for (int k = 0; k < kVecA; ++k) {
+      const int x = x0 / 4 + threadIdx.x + k * kThreads;
+      v[k] = x < x1 / 4 ? r4[x] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    }
+#pragma unroll
+    for (int k = 0; k < kVecA; ++k) {
+      const int x = x0 / 4 + threadIdx.x + k * kThreads;
+      if (x >= x1 / 4) continue;
+      amax(bv, bi, v[k].x, 4 * x);
+      amax(bv, bi, v[k].y, 4 * x + 1);
+      amax(bv, bi, v[k].z, 4 * x + 2);
+      amax(bv, bi, v[k].w, 4 * x + 3);
+    }
+  } else {
+    for (int x = x0 + threadIdx.x; x < x1; x += kThreads) amax(bv, bi, row[x], x);
   }
-  const int r = red[0];
-  __syncthreads();
-  return r;
+}
+
+__device__ inline void commit_bad(const AcceptParams &p, int i) {
+  p.accepted[i] = -1;
+  p.next_token[i] = -1;
+  set_err(p.err, SV_DEV_ERR_BAD_TOKEN);
 }
 
 __global__ __launch_bounds__(kThreads) void accept_kernel(AcceptParams p) {
-  __shared__ u64 sa[kThreads], sb[kThreads];
-  __shared__ float sv[kThreads];
-  __shared__ int si[kThreads];
-  __shared__ int red[kThreads];
-  __shared__ int first_fail, bad, flag, chosen_chunk, use_res, result;
-  __shared__ u64 target, seg[kThreads];
-  __shared__ int row_arg[64];
-  __shared__ float stage_p[8192];
-  __shared__ float stage_q[8192];
-  const int tid = threadIdx.x, c = blockIdx.x;
+  __shared__ Shared sh;
+  const int tid = threadIdx.x, c = blockIdx.x, i = blockIdx.y;
   const int x0 = c * p.chunk, x1 = min(p.V, x0 + p.chunk);
+  const bool vec = (p.V & 3) == 0;
+  const int g = p.gamma[i];
+  const int qst = seq_start(p.gamma, i, sh), dst = qst - i;
 
-  if (p.mode == SV_ACCEPT_GREEDY) {
-    // blockIdx.y = target row: chunk argmax; the last of the sequence's
-    // (gamma_i + 1) * nchunk workgroups decides
-    const int row = blockIdx.y;
-    const float *pr = p.p + (size_t)row * p.V;
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-    for (int x = x0 + tid; x < x1; x += kThreads) amax(bv, bi, pr[x], x);
-    u64 z0 = 0, z1 = 0;
-    block_reduce(z0, z1, bv, bi, sa, sb, sv, si);
-    if (tid == 0) put_part(p.parts + (size_t)row * p.nchunk + c, AcceptPart{0ull, 0ull, bv, bi});
-    // owner sequence of this row
-    if (tid == 0) {
-      int s = 0, i = 0;
-      while (i < p.B && s + p.gamma[i] + 1 <= row) s += p.gamma[i++] + 1;
-      red[0] = i;
-      red[1] = s;
+  if (tid == 0) {
+    sh.first_fail = g;
+    sh.bad = 0;
+  }
+  __syncthreads();
+  const bool greedy = p.mode == SV_ACCEPT_GREEDY;
+  for (int j = tid; j < g; j += kThreads) {
+    const int d = p.draft[dst + j];
+    if (d < 0 || d >= p.V) {
+      atomicOr(&sh.bad, 1);
+    } else if (!greedy) {
+      const float lhs = p.u_acc[dst + j] * p.q[(size_t)(dst + j) * p.V + d];
+      if (!(lhs < p.p[(size_t)(qst + j) * p.V + d])) atomicMin(&sh.first_fail, j);
     }
-    __syncthreads();
-    const int i = red[0], qst = red[1];
-    __syncthreads();
-    const int g = p.gamma[i];
-    if (!arrive_last(p.counters + i, (g + 1) * p.nchunk, &flag)) return;
-    for (int j = tid; j <= g; j += kThreads) {
+  }
+  __syncthreads();
+  const bool bad = sh.bad != 0;
+
+  if (greedy) {
+    // chunk argmax of each target row of the sequence
+    if (!bad) {
+      for (int j = 0; j <= g; ++j) {
+        float bv;
+        int bi;
+        chunk_argmax(p.p + (size_t)(qst + j) * p.V, x0, x1, vec, bv, bi);
+        u64 z0 = 0, z1 = 0;
+        block_reduce(z0, z1, bv, bi, sh);
+        if (tid == 0) put_part(p.parts + (size_t)(qst + j) * p.nchunk + c, 0ull, 0ull, bv, bi);
+      }
+    }
+    if (!arrive_last(p.counters + i, p.nchunk, sh)) return;
+    if (bad) {
+      if (tid == 0) commit_bad(p, i);
+      return;
+    }
+    // leading drafts equal to their row's argmax, then that row's argmax
+    int a = g, y = -1;
+    for (int j = 0; j <= g; ++j) {
       float v = -INFINITY;
-      int b = 0x7fffffff;
-      for (int cc = 0; cc < p.nchunk; ++cc) {
+      int ix = 0x7fffffff;
+      for (int cc = tid; cc < p.nchunk; cc += kThreads) {
         const AcceptPart q = get_part(p.parts + (size_t)(qst + j) * p.nchunk + cc);
-        amax(v, b, q.max_p, q.arg_p);
+        amax(v, ix, q.max_p, q.arg_p);
       }
-      if (j < 64) row_arg[j] = b;
-      else p.acc_ws[p.B + qst + j] = b;  // rare long drafts spill to workspace
+      u64 z0 = 0, z1 = 0;
+      block_reduce(z0, z1, v, ix, sh);
+      if (j < g && p.draft[dst + j] == ix) continue;
+      a = j;
+      y = ix;
+      break;
     }
-    wait_vmem();
-    __syncthreads();
     if (tid == 0) {
-      const int dst = qst - i;
-      auto arg = [&](int j) {
-        return j < 64 ? row_arg[j]
-                      : __hip_atomic_load(p.acc_ws + p.B + qst + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      };
-      int badtok = 0;
-      for (int j = 0; j < g; ++j) {
-        const int d = p.draft[dst + j];
-        if (d < 0 || d >= p.V) badtok = 1;
-      }
-      if (badtok) {
-        p.accepted[i] = -1;
-        p.next_token[i] = -1;
-        set_err(p.err, SV_DEV_ERR_BAD_TOKEN);
-        return;
-      }
-      int a = 0;
-      while (a < g && p.draft[dst + a] == arg(a)) ++a;
       p.accepted[i] = a;
-      p.next_token[i] = arg(a);
+      p.next_token[i] = y;
       p.kv_len[i] += a + 1;
     }
     return;
   }
 
   // ---- stochastic -----------------------------------------------------------
-  const int i = blockIdx.y;
-  const int g = p.gamma[i];
-  const int qst = seq_start(p.gamma, i, red), dst = qst - i;
-  if (tid == 0) {
-    first_fail = g;
-    bad = 0;
-  }
-  __syncthreads();
-  for (int j = tid; j < g; j += kThreads) {
-    const int d = p.draft[dst + j];
-    if (d < 0 || d >= p.V) {
-      atomicOr(&bad, 1);
-    } else {
-      const float lhs = p.u_acc[dst + j] * p.q[(size_t)(dst + j) * p.V + d];
-      if (!(lhs < p.p[(size_t)(qst + j) * p.V + d])) atomicMin(&first_fail, j);
-    }
-  }
-  __syncthreads();
-  const int a = bad ? -1 : first_fail;
-  const float *prow = p.p + (size_t)(qst + max(a, 0)) * p.V;
-  const float *qrow = (a >= 0 && a < g) ? p.q + (size_t)(dst + a) * p.V : nullptr;
+  const int a = sh.first_fail;
+  const float *prow = p.p + (size_t)(qst + a) * p.V;
+  const float *qrow = a < g ? p.q + (size_t)(dst + a) * p.V : nullptr;
   u64 sres = 0, sp = 0;
   float bv = -INFINITY;
   int bi = 0x7fffffff;
-  if (a >= 0) {
-    for (int x = x0 + tid; x < x1; x += kThreads) {
-      const float pv = prow[x];
-      const u64 w = weight_of(pv);
-      sres += qrow ? weight_of(pv - qrow[x]) : w;
-      sp += w;
-      amax(bv, bi, pv, x);
+  if (!bad) {
+    if (vec) {
+      // all of this thread's loads first (kVecA float4 of each row), then the sums
+      const float4 *p4 = reinterpret_cast<const float4 *>(prow);
+      const float4 *q4 = reinterpret_cast<const float4 *>(qrow);
+      float4 pv[kVecA], qv[kVecA];
+#pragma unroll
+      for (int k = 0; k < kVecA; ++k) {
+        const int x = x0 / 4 + tid + k * kThreads;
+        pv[k] = x < x1 / 4 ? p4[x] : make_float4(0.f, 0.f, 0.f, 0.f);
+        qv[k] = (qrow && x < x1 / 4) ? q4[x] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int k = 0; k < kVecA; ++k) {
+        const int x = x0 / 4 + tid + k * kThreads;
+        if (x >= x1 / 4) continue;
+        const float pe[4] = {pv[k].x, pv[k].y, pv[k].z, pv[k].w};
+        const float qe[4] = {qv[k].x, qv[k].y, qv[k].z, qv[k].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const u64 w = weight_of(pe[e]);
+          sres += qrow ? weight_of(pe[e] - qe[e]) : w;
+          sp += w;
+          amax(bv, bi, pe[e], 4 * x + e);
+        }
+      }
+    } else {
+      for (int x = x0 + tid; x < x1; x += kThreads) {
+        const float pv = prow[x];
+        const u64 w = weight_of(pv);
+        sres += qrow ? weight_of(pv - qrow[x]) : w;
+        sp += w;
+        amax(bv, bi, pv, x);
+      }
     }
   }
-  block_reduce(sres, sp, bv, bi, sa, sb, sv, si);
-  if (tid == 0) put_part(p.parts + (size_t)i * p.nchunk + c, AcceptPart{sres, sp, bv, bi});
-  if (!arrive_last(p.counters + i, p.nchunk, &flag)) return;
-
-  if (a < 0) {
-    if (tid == 0) {
-      p.accepted[i] = -1;
-      p.next_token[i] = -1;
-      set_err(p.err, SV_DEV_ERR_BAD_TOKEN);
-    }
+  block_reduce(sres, sp, bv, bi, sh);
+  if (tid == 0) put_part(p.parts + (size_t)i * p.nchunk + c, sres, sp, bv, bi);
+  if (!arrive_last(p.counters + i, p.nchunk, sh)) return;
+  if (bad) {
+    if (tid == 0) commit_bad(p, i);
     return;
   }
+
+  // totals over the chunks
   const AcceptPart *pp = p.parts + (size_t)i * p.nchunk;
-  if (tid == 0) {
-    u64 s_res = 0, s_p = 0;
-    float mv = -INFINITY;
-    int mi = 0x7fffffff;
-    for (int cc = 0; cc < p.nchunk; ++cc) {
-      const AcceptPart q = get_part(pp + cc);
-      s_res += q.sum_res;
-      s_p += q.sum_p;
-      amax(mv, mi, q.max_p, q.arg_p);
-    }
-    int ur;
-    u64 S;
-    if (s_res > 0) { ur = 1; S = s_res; }
-    else if (s_p > 0) { ur = 0; S = s_p; }
-    else { ur = -1; S = 0; }
-    use_res = ur;
-    result = -1;
-    if (ur < 0) {
-      result = mi;
-    } else {
-      u64 t = static_cast<u64>(floor(static_cast<double>(p.u_samp[i]) * static_cast<double>(S)));
-      if (t >= S) t = S - 1;
-      u64 run = 0;
-      int cc_hit = p.nchunk - 1;
-      for (int cc = 0; cc < p.nchunk; ++cc) {
-        const AcceptPart q = get_part(pp + cc);
-        const u64 v = ur ? q.sum_res : q.sum_p;
-        if (run + v > t) { cc_hit = cc; break; }
-        run += v;
-      }
-      chosen_chunk = cc_hit;
-      target = t - run;
-    }
+  u64 s_res = 0, s_p = 0;
+  float mv = -INFINITY;
+  int mi = 0x7fffffff;
+  for (int cc = tid; cc < p.nchunk; cc += kThreads) {
+    const AcceptPart q = get_part(pp + cc);
+    s_res += q.sum_res;
+    s_p += q.sum_p;
+    amax(mv, mi, q.max_p, q.arg_p);
   }
-  __syncthreads();
-  if (use_res >= 0) {
-    // exact scan of the chosen chunk: stage it in LDS with coalesced loads,
-    // then each thread sums a contiguous segment
-    const int cx0 = chosen_chunk * p.chunk, cx1 = min(p.V, cx0 + p.chunk);
-    const int n = cx1 - cx0;
-    const bool resid = use_res && a < g;
-    for (int x = tid; x < n; x += kThreads) {
-      stage_p[x] = prow[cx0 + x];
-      if (resid) stage_q[x] = qrow[cx0 + x];
-    }
-    __syncthreads();
-    const int per = (n + kThreads - 1) / kThreads;
-    const int lo = min(n, tid * per), hi = min(n, lo + per);
-    u64 s = 0;
-    for (int x = lo; x < hi; ++x) s += weight_of(resid ? stage_p[x] - stage_q[x] : stage_p[x]);
-    seg[tid] = s;
-    __syncthreads();
+  block_reduce(s_res, s_p, mv, mi, sh);
+  // weights: the resampling row, else the target row, else the argmax
+  const int ur = s_res > 0 ? 1 : (s_p > 0 ? 0 : -1);
+  int result = mi;
+  if (ur >= 0) {
+    const u64 S = ur ? s_res : s_p;
+    u64 t = static_cast<u64>(floor(static_cast<double>(p.u_samp[i]) * static_cast<double>(S)));
+    if (t >= S) t = S - 1;
+    // the chunk holding t: scan the chunk sums in thread order, 256 at a time
     if (tid == 0) {
-      u64 run = 0;
-      for (int k = 0; k < kThreads; ++k) {
-        const u64 v = seg[k];
-        seg[k] = run;
-        run += v;
+      sh.found = 0;
+      sh.chunk_hit = p.nchunk - 1;
+      sh.target = 0;
+    }
+    __syncthreads();
+    u64 run = 0;
+    for (int base = 0; base < p.nchunk; base += kThreads) {
+      const int cc = base + tid;
+      u64 v = 0;
+      if (cc < p.nchunk) {
+        const AcceptPart q = get_part(pp + cc);
+        v = ur ? q.sum_res : q.sum_p;
+      }
+      u64 tot;
+      const u64 before = run + block_exscan(v, &tot, sh);
+      if (v > 0 && before <= t && t < before + v) {
+        sh.found = 1;
+        sh.chunk_hit = cc;
+        sh.target = t - before;
+      }
+      run += tot;
+      __syncthreads();
+      if (sh.found) break;
+    }
+    // exact scan of that chunk: each thread a contiguous segment
+    const int cx0 = sh.chunk_hit * p.chunk, cx1 = min(p.V, cx0 + p.chunk);
+    const int n = cx1 - cx0;
+    const bool resid = ur == 1 && a < g;
+    const int per = (n + kThreads - 1) / kThreads;  // <= kSegMax
+    const int lo = min(n, tid * per), hi = min(n, lo + per);
+    float wv[kSegMax];
+    u64 s = 0;
+#pragma unroll
+    for (int k = 0; k < kSegMax; ++k) {
+      const int x = lo + k;
+      float r = 0.f;
+      if (x < hi) r = resid ? prow[cx0 + x] - qrow[cx0 + x] : prow[cx0 + x];
+      wv[k] = r;
+      s += weight_of(r);
+    }
+    u64 tot;
+    const u64 before = block_exscan(s, &tot, sh);
+    const u64 tt = sh.target;
+    if (tid == 0) sh.result = -1;
+    __syncthreads();
+    if (s > 0 && before <= tt && tt < before + s) {
+      u64 acc = before;
+#pragma unroll
+      for (int k = 0; k < kSegMax; ++k) {
+        acc += weight_of(wv[k]);
+        if (acc > tt) {
+          sh.result = cx0 + lo + k;
+          break;
+        }
       }
     }
     __syncthreads();
-    const u64 t = target, before = seg[tid];
-    if (before <= t && t < before + s) {
-      u64 run = before;
-      for (int x = lo; x < hi; ++x) {
-        run += weight_of(resid ? stage_p[x] - stage_q[x] : stage_p[x]);
-        if (run > t) { result = cx0 + x; break; }
-      }
-    }
-    __syncthreads();
+    result = sh.result;
   }
   if (tid == 0) {
     p.accepted[i] = a;
@@ -316,9 +385,9 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(AcceptParams p) {
 }  // namespace
 
 hipError_t launch_accept(const AcceptParams &p, hipStream_t s) {
-  const int rows = p.mode == SV_ACCEPT_GREEDY ? p.T : p.B;
+  if (p.chunk > kThreads * kSegMax) return hipErrorInvalidValue;
   trace_before(SV_K_ACCEPT, s);
-  hipLaunchKernelGGL(accept_kernel, dim3(p.nchunk, rows), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL(accept_kernel, dim3(p.nchunk, p.B), dim3(kThreads), 0, s, p);
   trace_after(SV_K_ACCEPT, s);
   return hipGetLastError();
 }

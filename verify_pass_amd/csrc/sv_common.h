@@ -123,7 +123,6 @@ struct GemmParams {
   // EPI_QKV
   uint16_t *qbuf;  // [T][hq][hd]
   int hq, hkv;
-  float rope_theta;
   const int *tok_seq;  // [T] sequence of each stacked token
   const int *tok_pos;  // [T] its position
   const float *rope_cs;  // [T][hd/2][2] rotation cos, sin
@@ -148,7 +147,7 @@ struct PrepParams {
   int *chunk_start;    // [B + 1] attention work items of each sequence
   float *rope_cs;      // [T][hd/2][2] cos, sin (nullptr: none)
   int hd;
-  float rope_theta;
+  double inv_freq[64]; // theta^(-2i/hd), i < hd/2 (evaluated on the host in fp64)
 };
 
 struct AttnParams {
@@ -212,7 +211,8 @@ struct AcceptParams {
 
 // ---------------------------------------------------------------------------
 // Host launchers (one per kernel family).  Return hipSuccess or the launch error.
-hipError_t launch_gemm(const GemmParams &p, int wtype, int tok_tiles, int depth, hipStream_t s,
+// depth = K steps in flight per wave (2, 4, 8); kw = waves per unit (1, 4, 8, 16).
+hipError_t launch_gemm(const GemmParams &p, int wtype, int tok_tiles, int depth, int kw, hipStream_t s,
                        int trace_class);
 hipError_t launch_pack(int wtype, int N, int K, const void *w, const void *scale, void *wp,
                        void *sp, hipStream_t s);
@@ -228,6 +228,18 @@ hipError_t launch_accept(const AcceptParams &p, hipStream_t s);
 // Kernel-timing trace hooks (host).
 void trace_before(int kernel_class, hipStream_t s);
 void trace_after(int kernel_class, hipStream_t s);
+
+// Register budget of the GEMM instantiations: which (weight type, token
+// tiles, waves per unit) combinations compile without spilling at 8 steps in
+// flight (deep) and at 4.  Larger workgroups leave fewer registers per wave.
+constexpr bool gemm_deep_ok(int wt, int tt, int kw) {
+  return wt == WT_BF16 ? (kw <= 4 || (kw == 8 && tt <= 2)) : wt == WT_INT4 ? (tt <= 2 && kw <= 4) : false;
+}
+constexpr bool gemm_kw_ok(int wt, int tt, int kw) {
+  return wt == WT_BF16   ? (kw <= 8 || tt <= 2)
+         : wt == WT_INT4 ? (kw <= 4 || (kw == 8 && tt <= 2) || (kw == 16 && tt == 1))
+                         : kw <= 8;
+}
 
 // Step sizes along K per weight type.
 inline int kstep_of(int wtype) { return wtype == WT_INT4 ? 128 : 64; }

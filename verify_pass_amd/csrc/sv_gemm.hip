@@ -4,11 +4,12 @@
 // N side.  One read of the weights serves every stacked token of every
 // sequence -- the single weight stream a verification pass is built around.
 //
-// Work unit = one wave: 32 weight rows (two 16-row MFMA tiles) x up to 64
-// tokens x one split of K.  The unit streams its weight rows straight from HBM
-// into registers with a rolling prefetch and reads the (small, L2-resident)
-// token rows directly as MFMA B operands: no LDS staging, no barriers, so the
-// four waves of a workgroup run independently and keep memory busy.
+// Work unit: 32 weight rows (two 16-row MFMA tiles) x up to 64 tokens x one
+// split of K, run by KW waves of one workgroup that each take a consecutive
+// piece of the split.  A wave streams its weight rows straight from HBM into
+// registers with a grouped prefetch and reads the (small, L2-resident) token
+// rows directly as MFMA B operands: no LDS staging in the main loop.  With
+// KW > 1 the pieces are added through LDS in wave order at the end.
 //
 // The two tiles of a unit are chosen so that every epilogue is lane-local:
 //   QKV     tile 0 = rotation-pair firsts, tile 1 = their partners (i + hd/2):
@@ -20,8 +21,8 @@
 // (r_t x) W = r_t (x W), so it is applied in the epilogue from sums of squares
 // of the token operand the unit already loads.
 //
-// K splits: when there are too few row groups to occupy the chip, units also
-// split K.  Each split stores its fp32 partial tile with device-scope (sc1)
+// K splits across units: for the remaining cases with too few row groups to
+// occupy the chip, units also split K.  Each split stores its fp32 partial tile with device-scope (sc1)
 // stores, waits for them to complete and bumps a per-tile counter; the split
 // that arrives last reads the partials back with device-scope loads, adds
 // them in split order (bitwise repeatable) and runs the epilogue.  No
@@ -30,533 +31,18 @@
 
 namespace sv {
 
-namespace {
+hipError_t launch_gemm_bf16(const GemmParams &p, int tok_tiles, int depth, int kw, hipStream_t s,
+                          int trace_class);
+hipError_t launch_gemm_int4(const GemmParams &p, int tok_tiles, int depth, int kw, hipStream_t s,
+                          int trace_class);
+hipError_t launch_gemm_f32(const GemmParams &p, int tok_tiles, int depth, int kw, hipStream_t s,
+                         int trace_class);
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
-constexpr float kLog2e = 1.4426950408889634f;
-
-// Raw per-lane payload of one K step for one 16-row tile.
-template <int WT> struct WStep;
-template <> struct WStep<WT_BF16> { uint4 v[2]; };
-template <> struct WStep<WT_F32> { uint4 v[4]; };
-template <> struct WStep<WT_INT4> { uint4 v; uint32_t s; };
-
-template <int WT> constexpr int kstep() { return WT == WT_INT4 ? 128 : 64; }
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-// Streaming (non-temporal) 16-byte load: weights are read once per pass and
-// should not evict the token operand from L2.
-__device__ __forceinline__ uint4 ld_nt(const void *p) {
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-  return __builtin_bit_cast(uint4, v);
-}
-
-// Per-lane weight stream of one 16-row tile.
-// Lane (row, gq) of step ks holds, for MFMA m, reduction indices
-//   bf16 : ks*64  + 32m + 8gq + [0, 8)
-//   int4 : ks*128 + 32gq + 8m + [0, 8)      (one 16-byte word group per lane)
-//   fp32 : ks*64  + 16gq + 8m + [0, 8)
-// and the token operand holds the same indices for its token.
-// Row-major [N][K] storage: each load instruction reads 16 rows x 64 bytes.
-// Packed storage (see sv_pack_matrix): the 16-row tile's fragments for one
-// step are contiguous in lane order, so each load instruction reads 1 KiB of
-// contiguous memory and a tile's whole K range is one sequential stream.
-template <int WT>
-struct WSrc {
-  const unsigned char *p;   // lane's base address for step 0
-  const uint16_t *s;        // int4 scales, lane's base for step 0
-  int step_bytes;           // byte advance per K step
-  int s_step;               // scale advance (elements) per K step
-  int m_off;                // byte offset of the second fragment (bf16)
-};
-
-template <int WT>
-__device__ __forceinline__ WSrc<WT> make_src(const GemmMat &mat, int row, int tile_row0, int K,
-                                             int ksteps, int packed, int lane, int gq) {
-  WSrc<WT> w;
-  if (packed) {
-    const size_t tile = (size_t)(tile_row0 / 16);
-    if constexpr (WT == WT_INT4) {
-      w.p = static_cast<const unsigned char *>(mat.w) + (tile * ksteps * 64 + lane) * 16;
-      w.s = mat.s + tile * ksteps * 64 + lane;
-      w.step_bytes = 64 * 16;
-      w.s_step = 64;
-      w.m_off = 0;
-    } else {
-      w.p = static_cast<const unsigned char *>(mat.w) + (tile * ksteps * 128 + lane) * 16;
-      w.s = nullptr;
-      w.step_bytes = 128 * 16;
-      w.s_step = 0;
-      w.m_off = 64 * 16;
-    }
-  } else {
-    if constexpr (WT == WT_BF16) {
-      w.p = static_cast<const unsigned char *>(mat.w) + ((size_t)row * K + 8 * gq) * 2;
-      w.step_bytes = 128;
-      w.m_off = 64;
-      w.s = nullptr;
-      w.s_step = 0;
-    } else if constexpr (WT == WT_INT4) {
-      w.p = static_cast<const unsigned char *>(mat.w) + ((size_t)row * (K / 8) + 4 * gq) * 4;
-      w.step_bytes = 64;
-      w.m_off = 0;
-      w.s = mat.s + (size_t)row * (K / 32) + gq;
-      w.s_step = 4;
-    } else {
-      w.p = static_cast<const unsigned char *>(mat.w) + ((size_t)row * K + 16 * gq) * 4;
-      w.step_bytes = 256;
-      w.m_off = 0;
-      w.s = nullptr;
-      w.s_step = 0;
-    }
-  }
-  return w;
-}
-
-template <int WT>
-__device__ __forceinline__ WStep<WT> load_w(const WSrc<WT> &w, int ks) {
-  WStep<WT> r;
-  const unsigned char *b = w.p + (size_t)ks * w.step_bytes;
-  if constexpr (WT == WT_BF16) {
-    r.v[0] = ld_nt(b);
-    r.v[1] = ld_nt(b + w.m_off);
-  } else if constexpr (WT == WT_F32) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r.v[i] = ld_nt(b + 16 * i);
-  } else {
-    r.v = ld_nt(b);
-    r.s = w.s[(size_t)ks * w.s_step];
-  }
-  return r;
-}
-
-// Token operand of one step: lane (token, gq) holds the step's reduction
-// indices in the same order as the weight operand (KS/4 bf16 values).
-template <int WT> struct XStep;
-template <> struct XStep<WT_BF16> { uint4 v[2]; };
-template <> struct XStep<WT_F32> { uint4 v[2]; };
-template <> struct XStep<WT_INT4> { uint4 v[4]; };
-
-template <int WT>
-__device__ __forceinline__ XStep<WT> load_x(const uint16_t *xrow, int ks, int gq) {
-  XStep<WT> r;
-  if constexpr (WT == WT_BF16) {
-    const uint16_t *b = xrow + ks * 64 + 8 * gq;
-    r.v[0] = *reinterpret_cast<const uint4 *>(b);
-    r.v[1] = *reinterpret_cast<const uint4 *>(b + 32);
-  } else {
-    constexpr int KS = kstep<WT>();
-    const uint16_t *b = xrow + ks * KS + (KS / 4) * gq;
-#pragma unroll
-    for (int i = 0; i < (KS / 32); ++i) r.v[i] = *reinterpret_cast<const uint4 *>(b + 8 * i);
-  }
-  return r;
-}
-
-// int4 word (8 codes, offset by 8) times the group scale, to bf16.
-__device__ __forceinline__ bf16x8 dequant8(uint32_t word, float s) {
-  uint32_t h[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float v = static_cast<float>(static_cast<int>((word >> (4 * e)) & 15u) - 8) * s;
-    h[e] = f2bf(v);
-  }
-  return as_bf16x8(uint4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                         h[6] | (h[7] << 16)});
-}
-
-// fp32 x8 -> (hi, lo) bf16 pairs with hi + lo == v to about 2^-17 relative.
-__device__ __forceinline__ void split8(const uint4 &a, const uint4 &b, bf16x8 &hi, bf16x8 &lo) {
-  const float f[8] = {__uint_as_float(a.x), __uint_as_float(a.y), __uint_as_float(a.z),
-                      __uint_as_float(a.w), __uint_as_float(b.x), __uint_as_float(b.y),
-                      __uint_as_float(b.z), __uint_as_float(b.w)};
-  uint32_t h[8], l[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    h[e] = f2bf(f[e]);
-    l[e] = f2bf(f[e] - bf2f(static_cast<uint16_t>(h[e])));
-  }
-  hi = as_bf16x8(uint4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)});
-  lo = as_bf16x8(uint4{l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16)});
-}
-
-// Physical (matrix, row) of row r of tile `tile` in 32-row group g.
-// Returns false past the end of the matrix (the lane then streams row 0 and
-// its results are dropped).
-__device__ __forceinline__ bool map_row(const GemmParams &p, int g, int tile, int r, int &m, int &pr) {
-  int n;
-  if (p.rowmap == RM_SWIGLU) {
-    const int f = g * 16 + r;
-    if (f >= p.mat[0].rows) return false;
-    m = tile;
-    pr = f;
-    return true;
-  }
-  if (p.rowmap == RM_ROPE_PAIRS) {
-    const int gph = p.hd / 32;  // groups per head
-    const int head = g / gph, c = g - head * gph;
-    n = head * p.hd + tile * (p.hd / 2) + 16 * c + r;
-  } else {
-    n = g * 32 + tile * 16 + r;
-  }
-  if (n >= p.N) return false;
-  int k = 0;
-  while (k < p.nmat - 1 && n >= p.mat[k].rows) {
-    n -= p.mat[k].rows;
-    ++k;
-  }
-  m = k;
-  pr = n;
-  return true;
-}
-
-__device__ __forceinline__ int rotate_step(int s, int rot, int n) {
-  const int r = s + rot;
-  return r >= n ? r - n : r;
-}
-
-// Bijective remap of the dispatch index so that consecutive logical
-// workgroups run on the same XCD (dispatch is round-robin over the 8 XCDs).
-__device__ __forceinline__ int xcd_remap(int wg, int nwg) {
-  const int q = nwg / 8, r = nwg % 8;
-  const int x = wg % 8, k = wg / 8;
-  return x * q + min(x, r) + k;
-}
-
-__device__ __forceinline__ void store_dev(float *p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_dev(const float *p) {
-  return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// wait until this wave's outstanding vector memory operations have completed
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-// Resident workgroups per CU to aim for: the skinny bf16 shapes are latency
-// bound, so more resident waves (fewer registers each) keep more loads in flight.
-template <int WT, int TT, int G> constexpr int min_wg_per_cu() {
-  return (WT == WT_BF16 && TT <= 2 && G <= 2) ? 8 : 1;
-}
-
-// G = K steps of weights and tokens in flight per wave: 2 for long streams
-// (many resident waves share the work), 8 for short K splits (one round of
-// loads per unit).
-template <int WT, int TT, int EPI, int G>
-__global__ __launch_bounds__(kThreads, (min_wg_per_cu<WT, TT, G>())) void gemm_kernel(GemmParams p) {
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int gq = lane >> 4, l16 = lane & 15;
-  const int wg = xcd_remap(blockIdx.x, gridDim.x);
-  const int unit = wg * kWaves + wave;
-  const int ngrp = p.nblk;
-  const int nunits = ngrp * p.splits * p.ntblk;
-  if (unit >= nunits) return;
-  const int grp = unit % ngrp;
-  const int rest = unit / ngrp;
-  const int split = rest % p.splits;
-  const int tb = rest / p.splits;
-  const int t0 = tb * TT * 16;
-  const int s0 = (int)((long long)split * p.ksteps / p.splits);
-  const int s1 = (int)((long long)(split + 1) * p.ksteps / p.splits);
-  const int nsteps = s1 - s0;
-
-  // weight stream of each of the unit's two tiles (rows past the end of a
-  // matrix stream its first tile; their results are dropped)
-  WSrc<WT> src[2];
-#pragma unroll
-  for (int tile = 0; tile < 2; ++tile) {
-    int mi = 0, pr0 = 0;
-    if (!map_row(p, grp, tile, 0, mi, pr0)) { mi = 0; pr0 = 0; }
-    int pr = pr0 + l16;
-    if (pr >= p.mat[mi].rows) pr = pr0;
-    src[tile] = make_src<WT>(p.mat[mi], pr, pr0, p.K, p.ksteps, p.packed, lane, gq);
-  }
-  // token rows this lane reads (clamped; results of padding tokens are dropped)
-  const uint16_t *xr[TT];
-#pragma unroll
-  for (int tt = 0; tt < TT; ++tt) xr[tt] = p.x + (size_t)min(t0 + tt * 16 + l16, p.T - 1) * p.K;
-
-  floatx4 acc[2][TT];
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) acc[a][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  const int rot = (grp * 7 + tb * 3) % max(nsteps, 1);
-  // Grouped prefetch: G steps of weights and tokens in flight per wave, then
-  // compute.  A shallow group keeps the register count low, so many waves are
-  // resident and together keep the memory system busy.
-  for (int base = 0; base < nsteps; base += G) {
-    WStep<WT> wbuf[G][2];
-    XStep<WT> xbuf[G][TT];
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      // units start at staggered steps (the order is fixed per unit) so that
-      // waves do not all read the same token-operand lines at the same time
-      const int st = s0 + rotate_step(min(base + j, nsteps - 1), rot, nsteps);
-#pragma unroll
-      for (int tile = 0; tile < 2; ++tile) wbuf[j][tile] = load_w<WT>(src[tile], st);
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt) xbuf[j][tt] = load_x<WT>(xr[tt], st, gq);
-    }
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      if (base + j < nsteps) {
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt) {
-#pragma unroll
-          for (int tile = 0; tile < 2; ++tile) {
-            if constexpr (WT == WT_BF16) {
-#pragma unroll
-              for (int m = 0; m < 2; ++m)
-                acc[tile][tt] = mfma16x16x32(as_bf16x8(wbuf[j][tile].v[m]), as_bf16x8(xbuf[j][tt].v[m]), acc[tile][tt]);
-            } else if constexpr (WT == WT_INT4) {
-              const float s = bf2f(static_cast<uint16_t>(wbuf[j][tile].s));
-              const uint32_t wv[4] = {wbuf[j][tile].v.x, wbuf[j][tile].v.y, wbuf[j][tile].v.z, wbuf[j][tile].v.w};
-#pragma unroll
-              for (int m = 0; m < 4; ++m)
-                acc[tile][tt] = mfma16x16x32(dequant8(wv[m], s), as_bf16x8(xbuf[j][tt].v[m]), acc[tile][tt]);
-            } else {
-#pragma unroll
-              for (int m = 0; m < 2; ++m) {
-                bf16x8 hi, lo;
-                split8(wbuf[j][tile].v[2 * m], wbuf[j][tile].v[2 * m + 1], hi, lo);
-                acc[tile][tt] = mfma16x16x32(hi, as_bf16x8(xbuf[j][tt].v[m]), acc[tile][tt]);
-                acc[tile][tt] = mfma16x16x32(lo, as_bf16x8(xbuf[j][tt].v[m]), acc[tile][tt]);
-              }
-            }
-          }
-        }
-      }
-    }
-  }
-
-  // ---- K-split reduction ----------------------------------------------------
-  if (p.splits > 1) {
-    constexpr int TILE = 2 * TT * 4 * 64;  // one partial value per (tile, token tile, row, lane)
-    const size_t tile_id = (size_t)tb * ngrp + grp;
-    float *mine = p.partial + ((size_t)split * ngrp * p.ntblk + tile_id) * TILE;
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) store_dev(mine + ((a * TT + tt) * 4 + i) * 64 + lane, acc[a][tt][i]);
-    wait_vmem();
-    int old = 0;
-    if (lane == 0)
-      old = __hip_atomic_fetch_add(p.counters + tile_id, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    old = __shfl(old, 0);
-    if (old != p.splits - 1) return;
-    if (lane == 0) __hip_atomic_store(p.counters + tile_id, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt) acc[a][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    for (int sp = 0; sp < p.splits; ++sp) {
-      const float *src = p.partial + ((size_t)sp * ngrp * p.ntblk + tile_id) * TILE;
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[a][tt][i] += load_dev(src + ((a * TT + tt) * 4 + i) * 64 + lane);
-    }
-  }
-
-  // per-token RMSNorm scale of the operand rows (lane's token is t0 + tt*16 + l16):
-  // precomputed scales, or sums of squares left in partials by the producer
-  float rs[TT];
-#pragma unroll
-  for (int tt = 0; tt < TT; ++tt) {
-    const int t = min(t0 + tt * 16 + l16, p.T - 1);
-    if (p.rnorm) {
-      rs[tt] = p.rnorm[t];
-    } else if (p.rparts) {
-      // lane group gq adds partials gq, gq+4, ... of its token; then the groups
-      float s = 0.f;
-      const float *pr = p.rparts + (size_t)t * p.nparts;
-#pragma unroll 8
-      for (int g = gq; g < p.nparts; g += 4) s += pr[g];
-      s += __shfl_xor(s, 16);
-      s += __shfl_xor(s, 32);
-      rs[tt] = 1.f / sqrtf(s / static_cast<float>(p.K) + p.eps);
-    } else {
-      rs[tt] = 1.f;
-    }
-  }
-
-  // ---- fused epilogues (lane-local) -----------------------------------------
-  if constexpr (EPI == EPI_RESID) {
-    uint16_t *out = static_cast<uint16_t *>(p.out);
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-      const int t = t0 + tt * 16 + l16;
-      float sq = 0.f;  // this lane's share of the output row's sum of squares
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int n = grp * 32 + a * 16 + 4 * gq + i;
-          if (n < p.N && t < p.T) {
-            const size_t o = (size_t)t * p.ldo + n;
-            const uint16_t h = f2bf(acc[a][tt][i] * rs[tt] + bf2f(p.resid[o]));
-            out[o] = h;
-            const float f = bf2f(h);
-            sq += f * f;
-          }
-        }
-      if (p.sq_out) {
-        sq += __shfl_xor(sq, 16);
-        sq += __shfl_xor(sq, 32);
-        if (gq == 0 && t < p.T) p.sq_out[(size_t)t * p.nblk + grp] = sq;
-      }
-    }
-  } else if constexpr (EPI == EPI_SWIGLU) {
-    uint16_t *out = static_cast<uint16_t *>(p.out);
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-      const int t = t0 + tt * 16 + l16;
-      if (t >= p.T) continue;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int f = grp * 16 + 4 * gq + i;
-        if (f < p.mat[0].rows) {
-          const float g = acc[0][tt][i] * rs[tt], u = acc[1][tt][i] * rs[tt];
-          const float sig = 1.f / (1.f + __builtin_amdgcn_exp2f(-g * kLog2e));
-          out[(size_t)t * p.ldo + f] = f2bf(g * sig * u);
-        }
-      }
-    }
-  } else if constexpr (EPI == EPI_LOGITS) {
-    float *out = static_cast<float *>(p.out);
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-      const int t = t0 + tt * 16 + l16;
-      float v[8];
-      float m = -INFINITY;
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int n = grp * 32 + a * 16 + 4 * gq + i;
-          v[a * 4 + i] = n < p.N ? acc[a][tt][i] * rs[tt] : -INFINITY;
-          m = fmaxf(m, v[a * 4 + i]);
-          if (t < p.T && n < p.N) out[(size_t)t * p.ldo + n] = v[a * 4 + i];
-        }
-      m = fmaxf(m, __shfl_xor(m, 16));
-      m = fmaxf(m, __shfl_xor(m, 32));
-      float s = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s += __builtin_amdgcn_exp2f((v[e] - m) * kLog2e);
-      s += __shfl_xor(s, 16);
-      s += __shfl_xor(s, 32);
-      if (gq == 0 && t < p.T) {
-        *reinterpret_cast<float2 *>(p.stats + ((size_t)t * p.nblk + grp) * 2) = make_float2(m, s);
-      }
-    }
-  } else {  // EPI_QKV: tile 0 holds pair firsts i, tile 1 the partners i + hd/2
-    const int gph = p.hd / 32;
-    const int head = grp / gph, c = grp - head * gph;
-    const int half = p.hd / 2;
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-      const int t = t0 + tt * 16 + l16;
-      if (t >= p.T) continue;
-      const int seq = p.tok_seq[t], pos = p.tok_pos[t];
-      const bool kv_ok = pos >= 0 && pos < p.kv_cap;
-      if (head >= p.hq && !kv_ok) {
-        set_err(p.err, SV_DEV_ERR_KV_OVERFLOW);
-        continue;
-      }
-      float ra[4], rb[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int fi = 16 * c + 4 * gq + e;  // rotation pair (fi, fi + hd/2)
-        const float a = acc[0][tt][e] * rs[tt], b = acc[1][tt][e] * rs[tt];
-        if (head < p.hq + p.hkv) {
-          const float2 cs = *reinterpret_cast<const float2 *>(p.rope_cs + ((size_t)t * half + fi) * 2);
-          ra[e] = a * cs.x - b * cs.y;
-          rb[e] = b * cs.x + a * cs.y;
-        } else {
-          ra[e] = a;
-          rb[e] = b;
-        }
-      }
-      const int fi0 = 16 * c + 4 * gq;
-      if (head < p.hq) {
-        uint16_t *q = p.qbuf + ((size_t)t * p.hq + head) * p.hd;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          q[fi0 + e] = f2bf(ra[e]);
-          q[fi0 + half + e] = f2bf(rb[e]);
-        }
-      } else if (head < p.hq + p.hkv) {
-        uint16_t *k = static_cast<uint16_t *>(p.kc[seq]) + ((size_t)(head - p.hq) * p.kv_cap + pos) * p.hd;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          k[fi0 + e] = f2bf(ra[e]);
-          k[fi0 + half + e] = f2bf(rb[e]);
-        }
-      } else {
-        uint16_t *v = static_cast<uint16_t *>(p.vc[seq]) + (size_t)(head - p.hq - p.hkv) * p.hd * p.kv_cap;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v[(size_t)(fi0 + e) * p.kv_cap + pos] = f2bf(ra[e]);
-          v[(size_t)(fi0 + half + e) * p.kv_cap + pos] = f2bf(rb[e]);
-        }
-      }
-    }
-  }
-}
-
-template <int WT, int TT, int EPI, int G>
-hipError_t launch_g(const GemmParams &p, hipStream_t s, int trace_class) {
-  const int nunits = p.nblk * p.splits * p.ntblk;
-  const int nwg = (nunits + kWaves - 1) / kWaves;
-  trace_before(trace_class, s);
-  hipLaunchKernelGGL((gemm_kernel<WT, TT, EPI, G>), dim3(nwg), dim3(kThreads), 0, s, p);
-  trace_after(trace_class, s);
-  return hipGetLastError();
-}
-
-template <int WT, int TT, int EPI>
-hipError_t launch_epi(const GemmParams &p, int depth, hipStream_t s, int trace_class) {
-  if constexpr (WT != WT_F32) {
-    if (depth >= 8) return launch_g<WT, TT, EPI, 8>(p, s, trace_class);
-  }
-  if (depth >= 4) return launch_g<WT, TT, EPI, 4>(p, s, trace_class);
-  return launch_g<WT, TT, EPI, 2>(p, s, trace_class);
-}
-
-template <int WT, int TT>
-hipError_t launch_tt(const GemmParams &p, int depth, hipStream_t s, int trace_class) {
-  switch (p.epi) {
-    case EPI_QKV: return launch_epi<WT, TT, EPI_QKV>(p, depth, s, trace_class);
-    case EPI_RESID: return launch_epi<WT, TT, EPI_RESID>(p, depth, s, trace_class);
-    case EPI_SWIGLU: return launch_epi<WT, TT, EPI_SWIGLU>(p, depth, s, trace_class);
-    default: return launch_epi<WT, TT, EPI_LOGITS>(p, depth, s, trace_class);
-  }
-}
-
-template <int WT>
-hipError_t launch_wt(const GemmParams &p, int tt, int depth, hipStream_t s, int tc) {
-  switch (tt) {
-    case 1: return launch_tt<WT, 1>(p, depth, s, tc);
-    case 2: return launch_tt<WT, 2>(p, depth, s, tc);
-    case 3: return launch_tt<WT, 3>(p, depth, s, tc);
-    default: return launch_tt<WT, 4>(p, depth, s, tc);
-  }
-}
-
-}  // namespace
-
-hipError_t launch_gemm(const GemmParams &p, int wtype, int tok_tiles, int depth, hipStream_t s,
+hipError_t launch_gemm(const GemmParams &p, int wtype, int tok_tiles, int depth, int kw, hipStream_t s,
                        int trace_class) {
-  if (wtype == WT_BF16) return launch_wt<WT_BF16>(p, tok_tiles, depth, s, trace_class);
-  if (wtype == WT_INT4) return launch_wt<WT_INT4>(p, tok_tiles, depth, s, trace_class);
-  return launch_wt<WT_F32>(p, tok_tiles, depth, s, trace_class);
+  if (wtype == WT_BF16) return launch_gemm_bf16(p, tok_tiles, depth, kw, s, trace_class);
+  if (wtype == WT_INT4) return launch_gemm_int4(p, tok_tiles, depth, kw, s, trace_class);
+  return launch_gemm_f32(p, tok_tiles, depth, kw, s, trace_class);
 }
 
 namespace {

@@ -7,63 +7,78 @@ namespace {
 constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 
+constexpr int kVec = 8;  // float4 loads per thread in flight: 8192 columns per workgroup
+
+// (m, s) pairs stand for s * exp(x - m); combining two keeps the larger m.
+__device__ __forceinline__ void combine(float &m, float &s, float m2, float s2) {
+  if (m2 == -INFINITY) return;
+  if (m2 > m) {
+    s = s * __builtin_amdgcn_exp2f((m - m2) * kLog2e) + s2;
+    m = m2;
+  } else {
+    s += s2 * __builtin_amdgcn_exp2f((m2 - m) * kLog2e);
+  }
+}
+
 // p = exp(l - M) / S per row, where M and S combine the per-group statistics
 // (group max m_b, group sum of exp(l - m_b)) that the LM-head GEMM wrote,
-// token-major so that a row's statistics are one contiguous run.  They are
-// reduced in a fixed order, so every column block of a row computes the same
-// M and S.
-__device__ inline float block_max(float v, float *red) {
-  const int tid = threadIdx.x;
-  red[tid] = v;
-  __syncthreads();
-  for (int o = kThreads / 2; o > 0; o >>= 1) {
-    if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
-    __syncthreads();
-  }
-  const float r = red[0];
-  __syncthreads();
-  return r;
-}
-
-__device__ inline float block_sum(float v, float *red) {
-  const int tid = threadIdx.x;
-  red[tid] = v;
-  __syncthreads();
-  for (int o = kThreads / 2; o > 0; o >>= 1) {
-    if (tid < o) red[tid] += red[tid + o];
-    __syncthreads();
-  }
-  const float r = red[0];
-  __syncthreads();
-  return r;
-}
-
+// token-major so that a row's statistics are one contiguous run.  The
+// combination order is fixed, so every column block of a row computes the
+// same M and S.
 __global__ __launch_bounds__(kThreads) void head_softmax_kernel(HeadSoftmaxParams p) {
-  __shared__ float red[kThreads];
-  const int t = blockIdx.y, tid = threadIdx.x;
+  __shared__ float red_m[kThreads / 64], red_s[kThreads / 64];
+  const int t = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const float2 *st = reinterpret_cast<const float2 *>(p.stats) + (size_t)t * p.nblk;
-  float m = -INFINITY;
-  for (int b = tid; b < p.nblk; b += kThreads) m = fmaxf(m, st[b].x);
-  const float M = block_max(m, red);
-  float s = 0.f;
-  for (int b = tid; b < p.nblk; b += kThreads) {
-    const float2 e = st[b];
-    s += e.y * __builtin_amdgcn_exp2f((e.x - M) * kLog2e);
+  float m = -INFINITY, s = 0.f;
+  // kVec statistics in flight per thread, combined in index order
+  for (int b0 = tid; b0 < p.nblk; b0 += kVec * kThreads) {
+    float2 e[kVec];
+#pragma unroll
+    for (int k = 0; k < kVec; ++k) {
+      const int b = b0 + k * kThreads;
+      e[k] = b < p.nblk ? st[b] : make_float2(-INFINITY, 0.f);
+    }
+#pragma unroll
+    for (int k = 0; k < kVec; ++k) combine(m, s, e[k].x, e[k].y);
   }
-  const float S = block_sum(s, red);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o);
+    combine(m, s, m2, s2);
+  }
+  if (lane == 0) {
+    red_m[w] = m;
+    red_s[w] = s;
+  }
+  __syncthreads();
+  float M = red_m[0], S = red_s[0];
+#pragma unroll
+  for (int k = 1; k < kThreads / 64; ++k) combine(M, S, red_m[k], red_s[k]);
+
   float *row = p.logits + (size_t)t * p.V;
   const int c0 = blockIdx.x * p.cols_per_block;
   const int c1 = min(p.V, c0 + p.cols_per_block);
   const float Mk = M * kLog2e;
-  if ((p.V & 3) == 0) {  // rows are 16-byte aligned: four columns per load
+  if ((p.V & 3) == 0) {  // rows are 16-byte aligned: four columns per load, all loads first
     float4 *r4 = reinterpret_cast<float4 *>(row);
-    for (int c = c0 / 4 + tid; c < c1 / 4; c += kThreads) {
-      float4 v = r4[c];
-      v.x = __builtin_amdgcn_exp2f(fmaf(v.x, kLog2e, -Mk)) / S;
-      v.y = __builtin_amdgcn_exp2f(fmaf(v.y, kLog2e, -Mk)) / S;
-      v.z = __builtin_amdgcn_exp2f(fmaf(v.z, kLog2e, -Mk)) / S;
-      v.w = __builtin_amdgcn_exp2f(fmaf(v.w, kLog2e, -Mk)) / S;
-      r4[c] = v;
+    const int e4 = c1 / 4;
+    float4 v[kVec];
+#pragma unroll
+    for (int k = 0; k < kVec; ++k) {
+      const int c = c0 / 4 + tid + k * kThreads;
+      if (c < e4) v[k] = r4[c];
+    }
+#pragma unroll
+    for (int k = 0; k < kVec; ++k) {
+      const int c = c0 / 4 + tid + k * kThreads;
+      if (c < e4) {
+        float4 o;
+        o.x = __builtin_amdgcn_exp2f(fmaf(v[k].x, kLog2e, -Mk)) / S;
+        o.y = __builtin_amdgcn_exp2f(fmaf(v[k].y, kLog2e, -Mk)) / S;
+        o.z = __builtin_amdgcn_exp2f(fmaf(v[k].z, kLog2e, -Mk)) / S;
+        o.w = __builtin_amdgcn_exp2f(fmaf(v[k].w, kLog2e, -Mk)) / S;
+        r4[c] = o;
+      }
     }
   } else {
     for (int c = c0 + tid; c < c1; c += kThreads)
@@ -92,6 +107,7 @@ __global__ __launch_bounds__(kThreads) void embed_kernel(EmbedParams p) {
 }  // namespace
 
 hipError_t launch_head_softmax(const HeadSoftmaxParams &p, hipStream_t s) {
+  if (p.cols_per_block != 4 * kThreads * kVec) return hipErrorInvalidValue;
   const dim3 grid((p.V + p.cols_per_block - 1) / p.cols_per_block, p.T);
   trace_before(SV_K_SOFTMAX, s);
   hipLaunchKernelGGL(head_softmax_kernel, grid, dim3(kThreads), 0, s, p);

@@ -8,7 +8,7 @@
 // Workgroup 0 also stores q_start[0..B] and the prefix sum of per-sequence
 // attention chunk counts ceil((kv_len[i] + gamma_i + 1) / chunk).
 // With a rotary table requested, each workgroup also stores cos and sin of
-// pos(t) * theta^(-2i/hd) for i < hd/2 (angles evaluated in fp64).
+// pos(t) * theta^(-2i/hd) for i < hd/2 (angle and its reduction in fp64).
 #include "sv_common.h"
 
 namespace sv {
@@ -60,13 +60,18 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams p) {
     p.tok_pos[t] = pos;
   }
   if (p.rope_cs) {
+    // angle pos * theta^(-2i/hd) and its reduction to [-pi, pi] in fp64 (two-part
+    // 2 pi), then fp32 sine and cosine of the reduced angle
+    constexpr double kTwoPiHi = 6.283185307179586232, kTwoPiLo = 2.449293598294706e-16;
     const int half = p.hd / 2;
     for (int i = tid; i < half; i += kThreads) {
-      const double inv = pow(static_cast<double>(p.rope_theta), -2.0 * i / p.hd);
-      double sn, cs;
-      sincos(static_cast<double>(pos) * inv, &sn, &cs);
-      p.rope_cs[((size_t)t * half + i) * 2] = static_cast<float>(cs);
-      p.rope_cs[((size_t)t * half + i) * 2 + 1] = static_cast<float>(sn);
+      const double ang = static_cast<double>(pos) * p.inv_freq[i];
+      const double k = rint(ang * (1.0 / kTwoPiHi));
+      const double r = fma(-k, kTwoPiLo, fma(-k, kTwoPiHi, ang));
+      float sn, cs;
+      sincosf(static_cast<float>(r), &sn, &cs);
+      p.rope_cs[((size_t)t * half + i) * 2] = cs;
+      p.rope_cs[((size_t)t * half + i) * 2 + 1] = sn;
     }
   }
   if (t == 0) {
