@@ -44,7 +44,8 @@
  *    can serve later calls of any kind on the same stream.  Calls that overlap
  *    in time must use different workspaces.
  *  - Thread safety: calls may come from several host threads; the only
- *    global state is the optional kernel-timing trace (sv_trace_*).
+ *    global state is the optional kernel-timing trace (sv_trace_*) and the
+ *    launch-policy override (sv_set_gemm_tuning).
  */
 #ifndef SV_H
 #define SV_H
@@ -261,12 +262,16 @@ typedef struct sv_plan_params {
 sv_status sv_plan_gamma(const sv_plan_params *params, int32_t B_live, int32_t *gamma_out,
                         double *bstar_out);
 
-/* Kernel-timing trace (profiling aid).  While a trace is active, every launch
- * of the named kernel class is bracketed by a pair of HIP events on the
- * launch stream, up to `capacity` launches.  sv_trace_end waits for the last
- * recorded event, writes the elapsed milliseconds of each bracketed launch to
- * ms_out (host, capacity entries), stores their number in *count and releases
- * the events. */
+/* Kernel-timing trace (profiling aid).  While a trace is active, every
+ * stride-th launch of the named kernel class (the 1st, the (stride+1)-th, ...)
+ * is bracketed by a pair of HIP events on the launch stream, up to `capacity`
+ * bracketed launches (timing-only events, recorded without a system-scope
+ * fence; each record still costs a few microseconds of stream time, which a
+ * stride above 1 spreads thinner).  sv_trace_end synchronises the device,
+ * writes the elapsed milliseconds of each bracketed launch to ms_out (host,
+ * capacity entries), stores their number in *count and releases the events.
+ * One trace at a time; SV_ERR_INVALID_ARG for a bad class, capacity or
+ * stride, or while another trace is active. */
 #define SV_K_GEMM_QKV 0
 #define SV_K_ATTENTION 1
 #define SV_K_ATTN_MERGE 2
@@ -280,7 +285,7 @@ sv_status sv_plan_gamma(const sv_plan_params *params, int32_t B_live, int32_t *g
 #define SV_K_EMBED 10
 #define SV_K_COUNT 11
 
-sv_status sv_trace_begin(int32_t kernel_class, int32_t capacity);
+sv_status sv_trace_begin(int32_t kernel_class, int32_t capacity, int32_t stride);
 sv_status sv_trace_end(float *ms_out, int32_t capacity, int32_t *count);
 
 /* Launch-policy override for the GEMMs of later sv_verify_layer calls (and

@@ -236,3 +236,13 @@ def test_gemm_tuning_setter():
         assert _ws(L, b)[1] == base
     finally:
         sv.sv_set_gemm_tuning(None)
+
+
+def test_trace_arguments():
+    """The timing trace rejects a bad class, capacity or stride, and an end
+    with no active trace."""
+    assert sv.sv_trace_begin(-1, 4) == sv.SV_ERR_INVALID_ARG
+    assert sv.sv_trace_begin(sv.SV_K_COUNT, 4) == sv.SV_ERR_INVALID_ARG
+    assert sv.sv_trace_begin(sv.SV_K_SOFTMAX, 0) == sv.SV_ERR_INVALID_ARG
+    assert sv.sv_trace_begin(sv.SV_K_SOFTMAX, 4, 0) == sv.SV_ERR_INVALID_ARG
+    assert sv.sv_trace_end(4)[0] == sv.SV_ERR_INVALID_ARG        # none active

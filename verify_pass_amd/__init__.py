@@ -88,7 +88,7 @@ _SIGNATURES = [
     ("sv_plan_gamma", C.c_int32,
      [C.POINTER(sv_plan_params), C.c_int32, C.POINTER(C.c_int32), C.POINTER(C.c_double)]),
     ("sv_set_gemm_tuning", C.c_int32, [C.c_char_p]),
-    ("sv_trace_begin", C.c_int32, [C.c_int32, C.c_int32]),
+    ("sv_trace_begin", C.c_int32, [C.c_int32, C.c_int32, C.c_int32]),
     ("sv_trace_end", C.c_int32, [C.POINTER(C.c_float), C.c_int32, C.POINTER(C.c_int32)]),
     ("sv_status_string", C.c_char_p, [C.c_int32]),
     ("sv_version", C.c_int32, []),
@@ -195,8 +195,8 @@ def sv_set_gemm_tuning(spec: str | None) -> int:
     return _lib.sv_set_gemm_tuning(None if spec is None else spec.encode())
 
 
-def sv_trace_begin(kernel_class: int, capacity: int) -> int:
-    return _lib.sv_trace_begin(kernel_class, capacity)
+def sv_trace_begin(kernel_class: int, capacity: int, stride: int = 1) -> int:
+    return _lib.sv_trace_begin(kernel_class, capacity, stride)
 
 
 def sv_trace_end(capacity: int):

@@ -20,6 +20,8 @@ struct TraceState {
   std::atomic<int> cls{-1};
   int cap = 0;
   int n = 0;
+  int stride = 1;
+  long long seen = 0;  // launches of the class since the trace began
   bool open = false;
   std::vector<hipEvent_t> ev;
 };
@@ -29,7 +31,8 @@ TraceState g_trace;
 void sv::trace_before(int kernel_class, hipStream_t s) {
   if (g_trace.cls.load(std::memory_order_relaxed) != kernel_class) return;
   std::lock_guard<std::mutex> lk(g_trace.mu);
-  if (g_trace.n < g_trace.cap && !g_trace.open) {
+  const bool take = g_trace.seen++ % g_trace.stride == 0;
+  if (take && g_trace.n < g_trace.cap && !g_trace.open) {
     if (hipEventRecord(g_trace.ev[2 * g_trace.n], s) == hipSuccess) g_trace.open = true;
   }
 }
@@ -44,14 +47,18 @@ void sv::trace_after(int kernel_class, hipStream_t s) {
   }
 }
 
-extern "C" sv_status sv_trace_begin(int32_t kernel_class, int32_t capacity) {
-  if (kernel_class < 0 || kernel_class >= SV_K_COUNT || capacity <= 0) return SV_ERR_INVALID_ARG;
+extern "C" sv_status sv_trace_begin(int32_t kernel_class, int32_t capacity, int32_t stride) {
+  if (kernel_class < 0 || kernel_class >= SV_K_COUNT || capacity <= 0 || stride <= 0) return SV_ERR_INVALID_ARG;
   std::lock_guard<std::mutex> lk(g_trace.mu);
   if (g_trace.cls.load() >= 0) return SV_ERR_INVALID_ARG;  // one trace at a time
   g_trace.ev.assign(2 * (size_t)capacity, nullptr);
+  // timing-only events: no system-scope fence (cache write-back) at each record,
+  // which would otherwise add a gap around every bracketed launch
   for (auto &e : g_trace.ev)
-    if (hipEventCreate(&e) != hipSuccess) return SV_ERR_HIP;
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return SV_ERR_HIP;
   g_trace.cap = capacity;
+  g_trace.stride = stride;
+  g_trace.seen = 0;
   g_trace.n = 0;
   g_trace.open = false;
   g_trace.cls.store(kernel_class);
@@ -64,7 +71,8 @@ extern "C" sv_status sv_trace_end(float *ms_out, int32_t capacity, int32_t *coun
   g_trace.cls.store(-1);
   sv_status st = SV_OK;
   const int n = g_trace.n;
-  if (n > 0 && hipEventSynchronize(g_trace.ev[2 * n - 1]) != hipSuccess) st = SV_ERR_HIP;
+  if (n > 0 && (hipEventSynchronize(g_trace.ev[2 * n - 1]) != hipSuccess || hipDeviceSynchronize() != hipSuccess))
+    st = SV_ERR_HIP;
   for (int i = 0; i < n && st == SV_OK; ++i) {
     float ms = 0.f;
     if (hipEventElapsedTime(&ms, g_trace.ev[2 * i], g_trace.ev[2 * i + 1]) != hipSuccess) st = SV_ERR_HIP;
