@@ -296,3 +296,28 @@ def test_head_launch_settings(wtype):
             assert err < TOL[wtype], spec
     finally:
         sv.sv_set_gemm_tuning(None)
+
+
+def test_kv_overflow_flagged_and_contained():
+    """A sequence whose chunk would run past its cache capacity is flagged on
+    the device (SV_DEV_ERR_KV_OVERFLOW): no row at or past the capacity is
+    written and the other sequences' results and caches are unaffected."""
+    shape = Shape(512, 8, 2, 128, 1024, 3000)
+    gamma, ctx, cap = [2, 3, 1], [100, 206, 50], 208   # sequence 1 needs rows 206..209
+    wl = custom_workload(shape, "bf16", gamma, ctx, seed=21, cap=cap)
+    dec = GpuDecoder(wl)
+    sentinel_before = [dec.batch.k_logical(i).copy() for i in range(wl.B)]
+    xh = hidden_states(wl.T, shape.d, wl.seed)
+    y = dec.run(tg.to_dev(xh))
+    torch.cuda.synchronize()
+    assert dec.batch.err.item() & sv.SV_DEV_ERR_KV_OVERFLOW
+    ref = dec.oracle(xh, seqs=[0, 2])
+    yh = dev_bf16_to_f64(y)
+    assert rel_rows(yh[ref.rows], ref.y) < TOL["bf16"]
+    for i in (0, 2):
+        c = int(ctx[i])
+        np.testing.assert_array_equal(dec.batch.k_logical(i)[:, :c], sentinel_before[i][:, :c])
+        np.testing.assert_array_equal(dec.batch.k_logical(i)[:, c + gamma[i] + 1:],
+                                      sentinel_before[i][:, c + gamma[i] + 1:])
+    # the overflowing sequence keeps its cached prefix
+    np.testing.assert_array_equal(dec.batch.k_logical(1)[:, :206], sentinel_before[1][:, :206])

@@ -12,7 +12,9 @@ and the oracle see bit-identical inputs.  Encodings:
 """
 from __future__ import annotations
 
+import concurrent.futures as _cf
 import dataclasses
+import os
 import zlib
 
 import numpy as np
@@ -25,6 +27,27 @@ __all__ = [
 ]
 
 _CHUNK = 1 << 24
+_GEN_CHUNK = 1 << 22  # elements per independent child stream of a large draw
+_POOL = None
+
+
+def _pool():
+    global _POOL
+    if _POOL is None:
+        n = min(16, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else 8)
+        _POOL = _cf.ThreadPoolExecutor(max_workers=max(1, n))
+    return _POOL
+
+
+def _parallel_chunks(rng: np.random.Generator, total: int, step: int, fn):
+    """fn(child_rng, start, count) for consecutive chunks of `step` elements,
+    each with its own child stream spawned from rng (deterministic for a given
+    rng state and size), run on a thread pool."""
+    n = (total + step - 1) // step
+    kids = rng.spawn(n) if n else []
+    futs = [_pool().submit(fn, kids[c], c * step, min(step, total - c * step)) for c in range(n)]
+    for f in futs:
+        f.result()
 
 
 @dataclasses.dataclass(frozen=True)
@@ -82,11 +105,13 @@ def bf16_bits_to_f32(u) -> np.ndarray:
 
 
 def normal_f32(rng: np.random.Generator, shape, std: float) -> np.ndarray:
+    """N(0, std^2) in fp32; chunks of the draw come from child streams of rng."""
     out = np.empty(shape, dtype=np.float32)
     flat = out.reshape(-1)
-    for s in range(0, flat.size, _CHUNK):
-        n = min(_CHUNK, flat.size - s)
-        flat[s:s + n] = rng.standard_normal(n, dtype=np.float32) * np.float32(std)
+
+    def fill(r, s, n):
+        flat[s:s + n] = r.standard_normal(n, dtype=np.float32) * np.float32(std)
+    _parallel_chunks(rng, flat.size, _GEN_CHUNK, fill)
     return out
 
 
@@ -94,10 +119,10 @@ def normal_bf16(rng: np.random.Generator, shape, std: float) -> np.ndarray:
     """N(0, std^2) drawn in fp32, stored as bf16 bit patterns."""
     out = np.empty(shape, dtype=np.uint16)
     flat = out.reshape(-1)
-    for s in range(0, flat.size, _CHUNK):
-        n = min(_CHUNK, flat.size - s)
-        flat[s:s + n] = f32_to_bf16_bits(
-            rng.standard_normal(n, dtype=np.float32) * np.float32(std))
+
+    def fill(r, s, n):
+        flat[s:s + n] = f32_to_bf16_bits(r.standard_normal(n, dtype=np.float32) * np.float32(std))
+    _parallel_chunks(rng, flat.size, _GEN_CHUNK, fill)
     return out
 
 
@@ -180,10 +205,11 @@ def _matrix(rng, n, k, std, wtype) -> Weights:
         packed = np.empty((n, k // 8), dtype=np.uint32)
         scales = np.empty((n, k // 32), dtype=np.uint16)
         rows = max(1, (1 << 22) // k)
-        for r0 in range(0, n, rows):
-            r1 = min(n, r0 + rows)
-            p, s = quantize_int4_g32(normal_f32(rng, (r1 - r0, k), std))
-            packed[r0:r1], scales[r0:r1] = p, s
+
+        def block(r, r0, m):
+            w = r.standard_normal((m, k), dtype=np.float32) * np.float32(std)
+            packed[r0:r0 + m], scales[r0:r0 + m] = quantize_int4_g32(w)
+        _parallel_chunks(rng, n, rows, block)
         return Weights("int4", n, k, packed, scales)
     raise ValueError(wtype)
 
@@ -216,12 +242,18 @@ def kv_cache(shape: Shape, ctx: np.ndarray, cap: int, seed: int, tag: str = "lay
     b = len(ctx)
     k = np.full((b, shape.n_kv, cap, shape.hd), 0x7F61, dtype=np.uint16)
     v = np.full((b, shape.n_kv, cap, shape.hd), 0x7F61, dtype=np.uint16)
+    ctx = [int(c) for c in np.asarray(ctx)]
     rk, rv = rng_for(seed, f"{tag}/kcache"), rng_for(seed, f"{tag}/vcache")
-    for i, c in enumerate(np.asarray(ctx)):
-        c = int(c)
+    kk, vk = (rk.spawn(b), rv.spawn(b)) if b else ([], [])
+
+    def seq(i):  # sequence i from its own child streams (no nested pool use)
+        c = ctx[i]
         if c:
-            k[i, :, :c] = normal_bf16(rk, (shape.n_kv, c, shape.hd), 1.0)
-            v[i, :, :c] = normal_bf16(rv, (shape.n_kv, c, shape.hd), 1.0)
+            shp = (shape.n_kv, c, shape.hd)
+            k[i, :, :c] = f32_to_bf16_bits(kk[i].standard_normal(shp, dtype=np.float32))
+            v[i, :, :c] = f32_to_bf16_bits(vk[i].standard_normal(shp, dtype=np.float32))
+    for f in [_pool().submit(seq, i) for i in range(b)]:
+        f.result()
     return k, v
 
 
