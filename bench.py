@@ -296,7 +296,7 @@ def main():
     kernels = {}
     if not args.no_kernel_table:
         names = {sv.SV_K_GEMM_QKV: "gemm_qkv", sv.SV_K_ATTENTION: "attention",
-                 sv.SV_K_ATTN_MERGE: "attn_merge", sv.SV_K_GEMM_O: "gemm_o",
+                 sv.SV_K_GEMM_O: "gemm_o",
                  sv.SV_K_GEMM_GATE_UP: "gemm_gate_up", sv.SV_K_GEMM_DOWN: "gemm_down",
                  sv.SV_K_GEMM_LM_HEAD: "gemm_lm_head", sv.SV_K_SOFTMAX: "softmax",
                  sv.SV_K_ACCEPT: "accept", sv.SV_K_PREP: "prep"}

@@ -139,16 +139,18 @@ typedef struct sv_layer {
  * committed token, j >= 1 the drafts).  T must equal sum(gamma_i + 1).
  *
  * KV caches: k_cache[i] points to sequence i's keys, bf16 [n_kv][kv_cap][hd]
- * (position-major); v_cache[i] to its values, bf16 [n_kv][hd][kv_cap]
- * (position-minor, so one head's values for consecutive positions are
- * contiguous).  Entries at positions < kv_len[i] are read; the pass writes
- * positions kv_len[i] .. kv_len[i] + gamma_i.  kv_cap is a multiple of 16. */
+ * (position-major); v_cache[i] to its values, bf16 in blocks of 32
+ * positions, [n_kv][kv_cap/32][hd][32] (value (head h, position p, column c)
+ * at ((h * kv_cap/32 + p/32) * hd + c) * 32 + p % 32: one head's values for
+ * 32 consecutive positions form one contiguous [hd][32] block).  Entries at
+ * positions < kv_len[i] are read; the pass writes positions kv_len[i] ..
+ * kv_len[i] + gamma_i.  kv_cap is a multiple of 32. */
 typedef struct sv_batch {
   int32_t B;                 /* sequences, >= 0 */
   int32_t T;                 /* stacked tokens = sum(gamma_i + 1) */
   int32_t max_ctx;           /* upper bound on every kv_len[i] (sizes the attention grid;
                                 a larger kv_len sets SV_DEV_ERR_CTX_BOUND) */
-  int32_t kv_cap;            /* cache capacity per sequence, multiple of 16 */
+  int32_t kv_cap;            /* cache capacity per sequence, multiple of 32 */
   const int32_t *gamma_host; /* (host) [B] draft counts, >= 0 */
   const int32_t *gamma;      /* [B] the same counts on the device */
   const int32_t *kv_len;     /* [B] cached tokens before the pass */
@@ -274,7 +276,7 @@ sv_status sv_plan_gamma(const sv_plan_params *params, int32_t B_live, int32_t *g
  * stride, or while another trace is active. */
 #define SV_K_GEMM_QKV 0
 #define SV_K_ATTENTION 1
-#define SV_K_ATTN_MERGE 2
+/* 2: unused (the attention kernel merges its chunks itself) */
 #define SV_K_GEMM_O 3
 #define SV_K_GEMM_GATE_UP 4
 #define SV_K_GEMM_DOWN 5

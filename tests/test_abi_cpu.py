@@ -81,7 +81,7 @@ def test_workspace_query_valid():
     (lambda L, b: setattr(L, "head_dim", 96), sv.SV_ERR_UNSUPPORTED),
     (lambda L, b: setattr(L, "n_kv_heads", 3), sv.SV_ERR_UNSUPPORTED),     # 4 % 3
     (lambda L, b: setattr(L, "d", 200), sv.SV_ERR_UNSUPPORTED),            # not a multiple of 64
-    (lambda L, b: setattr(b, "kv_cap", 120), sv.SV_ERR_INVALID_ARG),       # not a multiple of 16
+    (lambda L, b: setattr(b, "kv_cap", 112), sv.SV_ERR_INVALID_ARG),       # not a multiple of 32
     (lambda L, b: setattr(b, "max_ctx", -1), sv.SV_ERR_INVALID_ARG),
     (lambda L, b: setattr(L, "wq", sv.sv_matrix(None, None)), sv.SV_ERR_INVALID_ARG),
     (lambda L, b: setattr(b, "gamma", None), sv.SV_ERR_INVALID_ARG),

@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import (TOL, GpuDecoder, GpuHead, OV, accept_inputs, dev_bf16_to_f64,
+from gpu_helpers import (TOL, GpuDecoder, GpuHead, OF, OV, accept_inputs, dev_bf16_to_f64,
                          hidden_states, oracle_accept, rel_rows, run_accept, say, sv, tg)
 from workloads import workload
 
@@ -37,8 +37,8 @@ def _decoder_parity(wl, dec, xh):
     hd = wl.shape.hd
     for i in seqs:
         c, n = int(wl.ctx[i]), int(wl.gamma[i]) + 1
-        kg = dev_bf16_to_f64(dec.batch.k[i].view(torch.bfloat16)[:, c:c + n].contiguous())
-        vg = dev_bf16_to_f64(dec.batch.v[i].view(torch.bfloat16)[:, :, c:c + n].transpose(1, 2).contiguous())
+        kg = OF.bf16_to_f64(dec.batch.k_logical(i)[:, c:c + n])
+        vg = OF.bf16_to_f64(dec.batch.v_logical(i)[:, c:c + n])
         assert rel_rows(kg.reshape(-1, hd), ref.k_new[i].reshape(-1, hd)) < TOL[wl.wtype]
         assert rel_rows(vg.reshape(-1, hd), ref.v_new[i].reshape(-1, hd)) < TOL[wl.wtype]
     return y, yh

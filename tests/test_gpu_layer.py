@@ -303,7 +303,7 @@ def test_kv_overflow_flagged_and_contained():
     the device (SV_DEV_ERR_KV_OVERFLOW): no row at or past the capacity is
     written and the other sequences' results and caches are unaffected."""
     shape = Shape(512, 8, 2, 128, 1024, 3000)
-    gamma, ctx, cap = [2, 3, 1], [100, 206, 50], 208   # sequence 1 needs rows 206..209
+    gamma, ctx, cap = [2, 3, 1], [100, 222, 50], 224   # sequence 1 needs rows 222..225
     wl = custom_workload(shape, "bf16", gamma, ctx, seed=21, cap=cap)
     dec = GpuDecoder(wl)
     sentinel_before = [dec.batch.k_logical(i).copy() for i in range(wl.B)]
@@ -320,4 +320,4 @@ def test_kv_overflow_flagged_and_contained():
         np.testing.assert_array_equal(dec.batch.k_logical(i)[:, c + gamma[i] + 1:],
                                       sentinel_before[i][:, c + gamma[i] + 1:])
     # the overflowing sequence keeps its cached prefix
-    np.testing.assert_array_equal(dec.batch.k_logical(1)[:, :206], sentinel_before[1][:, :206])
+    np.testing.assert_array_equal(dec.batch.k_logical(1)[:, :222], sentinel_before[1][:, :222])

@@ -32,9 +32,9 @@ SV_LAYOUT_ROWMAJOR, SV_LAYOUT_PACKED = 0, 1
 SV_ACCEPT_STOCHASTIC, SV_ACCEPT_GREEDY = 0, 1
 SV_PLAN_BUDGET, SV_PLAN_SPEEDUP = 0, 1
 
-(SV_K_GEMM_QKV, SV_K_ATTENTION, SV_K_ATTN_MERGE, SV_K_GEMM_O, SV_K_GEMM_GATE_UP,
- SV_K_GEMM_DOWN, SV_K_GEMM_LM_HEAD, SV_K_SOFTMAX, SV_K_ACCEPT, SV_K_PREP,
- SV_K_EMBED, SV_K_COUNT) = range(12)
+SV_K_GEMM_QKV, SV_K_ATTENTION = 0, 1
+(SV_K_GEMM_O, SV_K_GEMM_GATE_UP, SV_K_GEMM_DOWN, SV_K_GEMM_LM_HEAD, SV_K_SOFTMAX, SV_K_ACCEPT,
+ SV_K_PREP, SV_K_EMBED, SV_K_COUNT) = range(3, 12)
 
 WTYPES = {"f32": SV_W_F32, "bf16": SV_W_BF16, "int4": SV_W_INT4_G32}
 

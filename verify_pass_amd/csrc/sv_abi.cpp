@@ -109,6 +109,7 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // workspace zero-filled once stays valid when it is shared between calls of
 // different kinds and shapes (each launch leaves the counters it used at 0).
 constexpr size_t kCounterBytes = 256 * 1024;
+constexpr int kSoftmaxCols = 8192;  // columns per softmax-finish workgroup (256 threads x 8 float4)
 constexpr size_t kMaxCounters = kCounterBytes / sizeof(int);
 
 // GEMM kinds of one pass (for the launch policy and its tuning override).
@@ -298,7 +299,8 @@ sv_status plan_layer(const sv_layer *L, const sv_batch *b, int32_t flags, LayerP
   if ((long long)pl.G * (gmax + 1) > 64) return SV_ERR_UNSUPPORTED;
   // per-sequence capacity (kv_len[i] + gamma_i + 1 <= kv_cap) is checked on the
   // device, where kv_len lives; max_ctx only sizes the attention grid
-  if (b->max_ctx < 0 || b->kv_cap <= 0 || b->kv_cap % 16) return SV_ERR_INVALID_ARG;
+  if (b->max_ctx < 0 || b->kv_cap <= 0 || b->kv_cap % 32) return SV_ERR_INVALID_ARG;
+  if ((long long)pl.B * hk > (long long)kMaxCounters) return SV_ERR_UNSUPPORTED;
   if (pl.B > 0 && (!b->gamma || !b->kv_len || !b->k_cache || !b->v_cache)) return SV_ERR_INVALID_ARG;
 
   const int nqkv = (hq + 2 * hk) * hd;
@@ -307,6 +309,9 @@ sv_status plan_layer(const sv_layer *L, const sv_batch *b, int32_t flags, LayerP
   pl.gu = gemm_cfg(GK_GU, (F + 15) / 16, 2 * F, pl.T, d, w);
   pl.down = gemm_cfg(GK_DOWN, (d + 31) / 32, d, pl.T, F, w);
   pl.attn_rpad = 16 * ((pl.G * (gmax + 1) + 15) / 16);
+  // keys per work item: 256, or more so that a sequence has at most 32 chunks
+  const long long max_len = (long long)b->max_ctx + gmax + 1;
+  pl.attn_chunk = 256 * (int)std::max<long long>(1, (max_len + 32 * 256 - 1) / (32 * 256));
   long long items = 0;
   for (int i = 0; i < pl.B; ++i)
     items += ((long long)b->max_ctx + b->gamma_host[i] + 1 + pl.attn_chunk - 1) / pl.attn_chunk;
@@ -433,7 +438,7 @@ extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const
       h.T = pl.T;
       h.V = L->vocab;
       h.nblk = pl.head.nblk;
-      h.cols_per_block = 8192;
+      h.cols_per_block = kSoftmaxCols;
       e = launch_head_softmax(h, s);
     }
     return e == hipSuccess ? SV_OK : SV_ERR_HIP;
@@ -501,7 +506,7 @@ extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const
     e = launch_gemm(p, wt, pl.qkv.tt, pl.qkv.depth, pl.qkv.kw, s, SV_K_GEMM_QKV);
     if (e != hipSuccess) return SV_ERR_HIP;
   }
-  {  // ragged attention + merge
+  {  // ragged attention (chunks merged by the last to arrive)
     AttnParams a;
     std::memset(&a, 0, sizeof(a));
     a.qbuf = qbuf;
@@ -525,9 +530,9 @@ extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const
     a.part_o = reinterpret_cast<float *>(ws + pl.off_po);
     a.part_ml = reinterpret_cast<float *>(ws + pl.off_pml);
     a.out = attn;
+    a.counters = reinterpret_cast<int *>(ws + pl.off_counters);
     a.err = b->err_flag;
     e = launch_attention(a, s);
-    if (e == hipSuccess) e = launch_attn_merge(a, s);
     if (e != hipSuccess) return SV_ERR_HIP;
   }
   {  // O projection + residual

@@ -13,9 +13,12 @@
 //   O^T[d][row] += V^T P^T (MFMA: head dim M, query rows N, keys K)
 // The key order inside an MFMA is permuted so that the S^T output a lane holds
 // (8 consecutive keys of one query row) is exactly the P^T operand it feeds to
-// the PV MFMA; values are stored position-minor (V^T per head) so that operand
-// is one contiguous 16-byte load.  Waves of a workgroup split the chunk and are
-// combined in LDS; chunks are combined by a log-sum-exp merge.
+// the PV MFMA.  Values are stored in 32-position blocks ([hd][32] per block),
+// so that operand is one 16-byte load and a step's values are one contiguous
+// 8 KiB run (hd 128).  Waves of a workgroup split the chunk and are combined
+// in LDS; each chunk's (o, max, sum) is published with device-scope stores,
+// and the last chunk of a (sequence, KV head) to arrive merges all of them by
+// log-sum-exp and writes the output rows.
 #include "sv_common.h"
 
 namespace sv {
@@ -41,15 +44,50 @@ __device__ __forceinline__ int dslice(int dg, int gq) {
   return 64 * (dg >> 1) + 16 * gq + 8 * (dg & 1);
 }
 
+__device__ __forceinline__ void store_dev(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_dev(const float *p) {
+  return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// One step's raw operands: keys (MFMA row m of key tile kt is key
+// k0 + 8*(m/4) + 4*kt + m%4) and values (lane (d = 16*dt + l16, gq) holds
+// keys k0 + 8*gq .. +7 of head-dim column d).
+template <int HD> struct Step {
+  uint4 k[2][HD / 32];
+  uint4 v[HD / 16];
+};
+
+template <int HD>
+__device__ __forceinline__ void load_step(Step<HD> &s, const uint16_t *kbase, const uint16_t *vbase, int k0,
+                                          int L, int l16, int gq) {
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const int key = min(k0 + 8 * (l16 >> 2) + 4 * kt + (l16 & 3), L - 1);
+    const uint16_t *kr = kbase + (size_t)key * HD;
+#pragma unroll
+    for (int dg = 0; dg < HD / 32; ++dg) s.k[kt][dg] = *reinterpret_cast<const uint4 *>(kr + dslice(dg, gq));
+  }
+  // k0 is a multiple of 32 and the block lies inside the cache (cap % 32 == 0)
+  const uint16_t *vb = vbase + (size_t)(k0 >> 5) * HD * 32 + 8 * gq;
+#pragma unroll
+  for (int dt = 0; dt < HD / 16; ++dt) s.v[dt] = *reinterpret_cast<const uint4 *>(vb + (dt * 16 + l16) * 32);
+}
+
 template <int RT, int HD>
-__global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
+__global__ __launch_bounds__(kThreads, (RT == 1 ? 3 : 1)) void attn_kernel(AttnParams p) {
   constexpr int NDG = HD / 32;  // MFMA k-groups over the head dim
   constexpr int NDT = HD / 16;  // 16-wide head-dim tiles of the output
   extern __shared__ __align__(16) unsigned char smem[];
   int *qs = reinterpret_cast<int *>(smem);
   int *cs = qs + p.B + 1;
-  float *red_o = reinterpret_cast<float *>(cs + p.B + 1 + 2);  // [4][HD][16]
-  float *red_ml = red_o + 4 * HD * 16;                   // [4][16][2]
+  int *flag = cs + p.B + 1;                                      // [2]
+  float *red_o = reinterpret_cast<float *>(flag + 2);            // [4][HD][16]
+  float *red_ml = red_o + 4 * HD * 16;                           // [4][16][2]
+  float *row_m = red_o;                                          // merge: [64] max, [64] 1/sum
+  float *row_il = red_o + 64;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int gq = lane >> 4, l16 = lane & 15;
@@ -65,6 +103,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   const int ctx = p.kv_len[seq];
   const int L = ctx + gam + 1;
   if (L > p.kv_cap) {
+    // every item of this sequence returns here: no arrivals are counted
     if (tid == 0) set_err(p.err, SV_DEV_ERR_KV_OVERFLOW);
     return;
   }
@@ -77,6 +116,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
 
   const uint16_t *kbase = static_cast<const uint16_t *>(p.kc[seq]) + (size_t)g * p.kv_cap * HD;
   const uint16_t *vbase = static_cast<const uint16_t *>(p.vc[seq]) + (size_t)g * HD * p.kv_cap;
+
 
   // query fragments and per-row causal limits
   bf16x8 qf[RT][NDG];
@@ -109,24 +149,15 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   }
 
   for (int k0 = kw0; k0 < kw1; k0 += kKeysPerStep) {
-    // K operand: MFMA row m of key tile kt is key k0 + 8*(m/4) + 4*kt + m%4
-    bf16x8 kf[2][NDG];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      int key = k0 + 8 * (l16 >> 2) + 4 * kt + (l16 & 3);
-      key = min(key, L - 1);
-      const uint16_t *kr = kbase + (size_t)key * HD;
-#pragma unroll
-      for (int dg = 0; dg < NDG; ++dg) kf[kt][dg] = as_bf16x8(*reinterpret_cast<const uint4 *>(kr + dslice(dg, gq)));
-    }
-    // V^T operand: lane (d = 16*dt + l16, gq) holds keys k0 + 8*gq .. +7
+    Step<HD> cur;
+    load_step<HD>(cur, kbase, vbase, k0, L, l16, gq);
+
+    // values of keys at or past L are zeroed (the cache holds anything there)
     bf16x8 vf[NDT];
-    const int vk = k0 + 8 * gq;
-    const int vstart = min(vk, (L - 1) & ~7);
-    const int nvalid = L - vk;  // keys at or past L are zeroed
+    const int nvalid = L - (k0 + 8 * gq);
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      uint4 v = *reinterpret_cast<const uint4 *>(vbase + (size_t)(dt * 16 + l16) * p.kv_cap + vstart);
+      uint4 v = cur.v[dt];
       if (nvalid < 8) {
         uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -144,7 +175,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
       for (int kt = 0; kt < 2; ++kt) {
         s[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int dg = 0; dg < NDG; ++dg) s[kt] = mfma16x16x32(kf[kt][dg], qf[rt][dg], s[kt]);
+        for (int dg = 0; dg < NDG; ++dg) s[kt] = mfma16x16x32(as_bf16x8(cur.k[kt][dg]), qf[rt][dg], s[kt]);
       }
       float sv[8];
       float mx = kNegBig;
@@ -179,8 +210,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     }
   }
 
-  // ---- combine the four waves, one row tile at a time ----------------------
-  const int G_items = p.hkv;
+  // ---- combine the four waves, one row tile at a time; publish the chunk ---
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     float l = l_run[rt];
@@ -195,9 +225,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) red_o[(wave * HD + dt * 16 + 4 * gq + i) * 16 + l16] = o[rt][dt][i];
     __syncthreads();
-    const size_t prow = ((size_t)item * G_items + g) * p.rpad + rt * 16;
+    const size_t prow = ((size_t)item * p.hkv + g) * p.rpad + rt * 16;
     for (int idx = tid; idx < HD * 16; idx += kThreads) {
       const int row = idx / HD, d = idx - row * HD;
+      if (rt * 16 + row >= R) continue;
       float M = kNegBig;
 #pragma unroll
       for (int w = 0; w < 4; ++w) M = fmaxf(M, red_ml[(w * 16 + row) * 2]);
@@ -208,49 +239,60 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
         acc += red_o[(w * HD + d) * 16 + row] * f;
         lt += red_ml[(w * 16 + row) * 2 + 1] * f;
       }
-      p.part_o[(prow + row) * HD + d] = acc;
+      store_dev(p.part_o + (prow + row) * HD + d, acc);
       if (d == 0) {
-        p.part_ml[(prow + row) * 2] = M;
-        p.part_ml[(prow + row) * 2 + 1] = lt;
+        store_dev(p.part_ml + (prow + row) * 2, M);
+        store_dev(p.part_ml + (prow + row) * 2 + 1, lt);
       }
     }
     __syncthreads();
   }
-}
 
-// One workgroup per (token, query head): log-sum-exp merge over the chunks.
-template <int HD>
-__global__ __launch_bounds__(HD) void merge_kernel(AttnParams p) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  int *qs = reinterpret_cast<int *>(smem);
-  int *cs = qs + p.B + 1;
-  load_maps(p, qs, cs);
-  const int t = blockIdx.x, qh = blockIdx.y, d = threadIdx.x;
-  const int seq = upper_index(qs, p.B, t);
-  const int j = t - qs[seq];
-  const int gam = p.gamma[seq];
-  const int G = p.hq / p.hkv;
-  const int g = qh / G, hg = qh - g * G;
-  const int row = hg * (gam + 1) + j;
-  const int L = p.kv_len[seq] + gam + 1;
-  const int nch = (L + p.chunk - 1) / p.chunk;
-  float M = kNegBig;
-  for (int c = 0; c < nch; ++c) {
-    const int item = cs[seq] + c;
-    if (item >= p.max_items) break;
-    M = fmaxf(M, p.part_ml[(((size_t)item * p.hkv + g) * p.rpad + row) * 2]);
+  // ---- the last chunk of (sequence, KV head) to arrive merges ---------------
+  // chunks of this sequence that were launched (all of them unless the grid
+  // was sized for a smaller context, which is flagged above)
+  const int first = cs[seq];
+  const int nch = min(cs[seq + 1], p.max_items) - first;
+  wait_vmem();
+  __syncthreads();
+  if (tid == 0) {
+    int *ctr = p.counters + (size_t)seq * p.hkv + g;
+    const int old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    flag[0] = old == nch - 1;
+    if (flag[0]) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  float acc = 0.f, lt = 0.f;
-  for (int c = 0; c < nch; ++c) {
-    const int item = cs[seq] + c;
-    if (item >= p.max_items) break;
-    const size_t pr = ((size_t)item * p.hkv + g) * p.rpad + row;
-    const float f = __builtin_amdgcn_exp2f(p.part_ml[pr * 2] - M);
-    acc += p.part_o[pr * HD + d] * f;
-    lt += p.part_ml[pr * 2 + 1] * f;
+  __syncthreads();
+  if (!flag[0]) return;
+
+  // per row: overall max and 1 / sum over the chunks
+  for (int r = tid; r < R; r += kThreads) {
+    float M = kNegBig;
+#pragma unroll 8
+    for (int cc = 0; cc < nch; ++cc)
+      M = fmaxf(M, load_dev(p.part_ml + ((((size_t)first + cc) * p.hkv + g) * p.rpad + r) * 2));
+    float lt = 0.f;
+#pragma unroll 8
+    for (int cc = 0; cc < nch; ++cc) {
+      const float *ml = p.part_ml + ((((size_t)first + cc) * p.hkv + g) * p.rpad + r) * 2;
+      lt += load_dev(ml + 1) * __builtin_amdgcn_exp2f(load_dev(ml) - M);
+    }
+    row_m[r] = M;
+    row_il[r] = lt > 0.f ? 1.f / lt : 0.f;
   }
-  const float v = lt > 0.f ? acc / lt : 0.f;
-  p.out[(size_t)t * p.hq * HD + qh * HD + d] = f2bf(v);
+  __syncthreads();
+  for (int idx = tid; idx < R * HD; idx += kThreads) {
+    const int r = idx / HD, d = idx - r * HD;
+    const float M = row_m[r];
+    float acc = 0.f;
+#pragma unroll 8
+    for (int cc = 0; cc < nch; ++cc) {
+      const size_t pr = (((size_t)first + cc) * p.hkv + g) * p.rpad + r;
+      acc += load_dev(p.part_o + pr * HD + d) * __builtin_amdgcn_exp2f(load_dev(p.part_ml + pr * 2) - M);
+    }
+    const int hg = r / n1, j = r - hg * n1;
+    const int t = qs[seq] + j;
+    p.out[((size_t)t * p.hq + g * G + hg) * HD + d] = f2bf(acc * row_il[r]);
+  }
 }
 
 template <int RT, int HD>
@@ -279,18 +321,8 @@ hipError_t launch_hd(const AttnParams &p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_attention(const AttnParams &p, hipStream_t s) {
+  if (p.kv_cap % 32 || p.chunk % (4 * kKeysPerStep) || p.rpad > 64) return hipErrorInvalidValue;
   return p.hd == 64 ? launch_hd<64>(p, s) : launch_hd<128>(p, s);
-}
-
-hipError_t launch_attn_merge(const AttnParams &p, hipStream_t s) {
-  const size_t lds = (size_t)(2 * (p.B + 1) + 2) * sizeof(int);
-  trace_before(SV_K_ATTN_MERGE, s);
-  if (p.hd == 64)
-    hipLaunchKernelGGL((merge_kernel<64>), dim3(p.T, p.hq), dim3(64), lds, s, p);
-  else
-    hipLaunchKernelGGL((merge_kernel<128>), dim3(p.T, p.hq), dim3(128), lds, s, p);
-  trace_after(SV_K_ATTN_MERGE, s);
-  return hipGetLastError();
 }
 
 }  // namespace sv

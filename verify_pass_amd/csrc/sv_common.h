@@ -166,6 +166,7 @@ struct AttnParams {
   float *part_o;    // [max_items][hkv][rpad][hd]
   float *part_ml;   // [max_items][hkv][rpad][2]
   uint16_t *out;    // [T][hq*hd]
+  int *counters;    // [B][hkv] arrival counters, zero between launches
   int *err;
 };
 
@@ -220,7 +221,6 @@ hipError_t launch_pack(int wtype, int N, int K, const void *w, const void *scale
 size_t gemm_partial_floats(int ngroups, int splits, int ntblk, int tok_tiles);
 hipError_t launch_prep(const PrepParams &p, hipStream_t s);
 hipError_t launch_attention(const AttnParams &p, hipStream_t s);
-hipError_t launch_attn_merge(const AttnParams &p, hipStream_t s);
 hipError_t launch_head_softmax(const HeadSoftmaxParams &p, hipStream_t s);
 hipError_t launch_embed(const EmbedParams &p, hipStream_t s);
 hipError_t launch_accept(const AcceptParams &p, hipStream_t s);

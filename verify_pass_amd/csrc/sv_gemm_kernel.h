@@ -507,11 +507,13 @@ __global__ __launch_bounds__(64 * waves_per_wg<KW>(), (min_wg_per_cu<WT, TT, G, 
           k[fi0 + half + e] = f2bf(rb[e]);
         }
       } else {
-        uint16_t *v = static_cast<uint16_t *>(p.vc[seq]) + (size_t)(head - p.hq - p.hkv) * p.hd * p.kv_cap;
+        // values in 32-position blocks: [n_kv][cap/32][hd][32]
+        uint16_t *v = static_cast<uint16_t *>(p.vc[seq]) + (size_t)(head - p.hq - p.hkv) * p.hd * p.kv_cap +
+                      (size_t)(pos >> 5) * p.hd * 32 + (pos & 31);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          v[(size_t)(fi0 + e) * p.kv_cap + pos] = f2bf(ra[e]);
-          v[(size_t)(fi0 + half + e) * p.kv_cap + pos] = f2bf(rb[e]);
+          v[(size_t)(fi0 + e) * 32] = f2bf(ra[e]);
+          v[(size_t)(fi0 + half + e) * 32] = f2bf(rb[e]);
         }
       }
     }

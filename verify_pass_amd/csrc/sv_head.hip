@@ -5,6 +5,7 @@ namespace sv {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kEmbedThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 
 constexpr int kVec = 8;  // float4 loads per thread in flight: 8192 columns per workgroup
@@ -86,21 +87,21 @@ __global__ __launch_bounds__(kThreads) void head_softmax_kernel(HeadSoftmaxParam
   }
 }
 
-__global__ __launch_bounds__(kThreads) void embed_kernel(EmbedParams p) {
+__global__ __launch_bounds__(kEmbedThreads) void embed_kernel(EmbedParams p) {
   const int t = blockIdx.x;
   const int tok = p.tokens[t];
   uint16_t *out = p.out + (size_t)t * p.d;
   if (tok < 0 || tok >= p.V) {
     if (threadIdx.x == 0) set_err(p.err, SV_DEV_ERR_BAD_TOKEN);
-    for (int k = threadIdx.x; k < p.d; k += kThreads) out[k] = 0;
+    for (int k = threadIdx.x; k < p.d; k += kEmbedThreads) out[k] = 0;
     return;
   }
   if (p.table_bf16) {
     const uint16_t *row = static_cast<const uint16_t *>(p.table) + (size_t)tok * p.d;
-    for (int k = threadIdx.x; k < p.d; k += kThreads) out[k] = row[k];
+    for (int k = threadIdx.x; k < p.d; k += kEmbedThreads) out[k] = row[k];
   } else {
     const float *row = static_cast<const float *>(p.table) + (size_t)tok * p.d;
-    for (int k = threadIdx.x; k < p.d; k += kThreads) out[k] = f2bf(row[k]);
+    for (int k = threadIdx.x; k < p.d; k += kEmbedThreads) out[k] = f2bf(row[k]);
   }
 }
 
@@ -117,7 +118,7 @@ hipError_t launch_head_softmax(const HeadSoftmaxParams &p, hipStream_t s) {
 
 hipError_t launch_embed(const EmbedParams &p, hipStream_t s) {
   trace_before(SV_K_EMBED, s);
-  hipLaunchKernelGGL(embed_kernel, dim3(p.T), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL(embed_kernel, dim3(p.T), dim3(kEmbedThreads), 0, s, p);
   trace_after(SV_K_EMBED, s);
   return hipGetLastError();
 }

@@ -15,7 +15,7 @@ from . import (SV_LAYER_DECODER, SV_LAYER_EMBED, SV_LAYER_HEAD, SV_LAYOUT_PACKED
                sv_pack_matrix, sv_packed_matrix_bytes)
 
 __all__ = ["to_dev", "stream_handle", "workspace", "DeviceMatrix", "upload_matrix",
-           "decoder_struct", "head_struct", "embed_struct", "DeviceBatch"]
+           "decoder_struct", "head_struct", "embed_struct", "DeviceBatch", "v_blocked", "v_logical"]
 
 
 def to_dev(a: np.ndarray, device="cuda") -> torch.Tensor:
@@ -103,8 +103,8 @@ def embed_struct(shape, table: torch.Tensor) -> sv_layer:
 class DeviceBatch:
     """Per-sequence KV caches and the batch arrays on the device.
 
-    K caches are [n_kv][cap][hd] per sequence; V caches are stored
-    position-minor, [n_kv][hd][cap]."""
+    K caches are [n_kv][cap][hd] per sequence; V caches are stored in blocks
+    of 32 positions, [n_kv][cap/32][hd][32]."""
 
     def __init__(self, gamma, kv_len, cap: int, max_ctx: int | None = None, kcache=None,
                  vcache=None, shape=None, device="cuda"):
@@ -121,11 +121,12 @@ class DeviceBatch:
         if kcache is not None:
             for i in range(self.B):
                 self.k.append(to_dev(kcache[i], device))
-                self.v.append(to_dev(np.ascontiguousarray(np.swapaxes(vcache[i], 1, 2)), device))
+                self.v.append(to_dev(v_blocked(vcache[i]), device))
         elif shape is not None:
             for _ in range(self.B):
                 self.k.append(torch.zeros(shape.n_kv, cap, shape.hd, dtype=torch.bfloat16, device=device))
-                self.v.append(torch.zeros(shape.n_kv, shape.hd, cap, dtype=torch.bfloat16, device=device))
+                self.v.append(torch.zeros(shape.n_kv, cap // 32, shape.hd, 32, dtype=torch.bfloat16,
+                                          device=device))
         self.kptr = torch.tensor([t.data_ptr() for t in self.k] or [0], dtype=torch.int64, device=device)
         self.vptr = torch.tensor([t.data_ptr() for t in self.v] or [0], dtype=torch.int64, device=device)
 
@@ -146,4 +147,16 @@ class DeviceBatch:
 
     def v_logical(self, i: int) -> np.ndarray:
         """Sequence i's V cache as bf16 bits in position-major order [n_kv][cap][hd]."""
-        return np.swapaxes(self.v[i].view(torch.int16).cpu().numpy().view(np.uint16), 1, 2)
+        return v_logical(self.v[i].view(torch.int16).cpu().numpy().view(np.uint16))
+
+
+def v_blocked(v: np.ndarray) -> np.ndarray:
+    """[n_kv][cap][hd] values -> the library's [n_kv][cap/32][hd][32] blocks."""
+    n, cap, hd = v.shape
+    return np.ascontiguousarray(v.reshape(n, cap // 32, 32, hd).transpose(0, 1, 3, 2))
+
+
+def v_logical(vb: np.ndarray) -> np.ndarray:
+    """Inverse of v_blocked."""
+    n, nb, hd, _ = vb.shape
+    return np.ascontiguousarray(vb.transpose(0, 1, 3, 2).reshape(n, nb * 32, hd))

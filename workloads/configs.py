@@ -49,7 +49,7 @@ class Workload:
     n_layers: int
     gamma: np.ndarray    # int32 [B]
     ctx: np.ndarray      # int32 [B] cached tokens before the pass
-    cap: int             # KV capacity per sequence (multiple of 16)
+    cap: int             # KV capacity per sequence (multiple of 32)
     head: bool           # an LM head is part of the pass
     embed: bool          # token embedding is part of the pass
     draft: str           # 'temp' | 'alpha' | 'noise'
@@ -76,8 +76,8 @@ class Workload:
 
 
 def _cap_for(ctx, gamma) -> int:
-    need = int(np.max(np.asarray(ctx) + np.asarray(gamma) + 1)) if len(ctx) else 16
-    return max(16, (need + 15) // 16 * 16)
+    need = int(np.max(np.asarray(ctx) + np.asarray(gamma) + 1)) if len(ctx) else 32
+    return max(32, (need + 31) // 32 * 32)
 
 
 def workload(cid: int) -> Workload:
