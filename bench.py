@@ -138,6 +138,148 @@ def cpu_baseline(wl, W, Wlm, kc, vc, xh, acc_in):
                       f"{dt:.1f} s on {blas} BLAS threads ({cores} cores visible)"}
 
 
+def expected_tokens(alpha: float, gamma: int) -> float:
+    """Tokens per verify pass at independent per-draft acceptance alpha
+    (accepted drafts plus the bonus token)."""
+    return float(gamma + 1) if alpha >= 1.0 else (1.0 - alpha ** (gamma + 1)) / (1.0 - alpha)
+
+
+def fit_step_model(bs, ts, n):
+    """Least-squares fit of t(B) = max(t_w + k B, c B n) (n = gamma + 1 tokens
+    per sequence) to measured step times; returns (t_w, k, c)."""
+    import numpy as np
+    from scipy.optimize import least_squares
+    b = np.asarray(bs, float)
+    t = np.asarray(ts, float)
+
+    def resid(v):
+        tw, k, c = v
+        return (np.maximum(tw + k * b, c * b * n) - t) / t
+    x0 = [t[0], max(1e-6, (t[min(2, len(t) - 1)] - t[0]) / max(1.0, b[min(2, len(b) - 1)] - b[0])),
+          t[-1] / (b[-1] * n)]
+    r = least_squares(resid, x0, bounds=([0, 0, 0], [np.inf, np.inf, np.inf]))
+    return tuple(float(v) for v in r.x)
+
+
+def sweep(args):
+    """Step time over a (B, gamma) grid: one layer of the chosen shape, the
+    151936-entry head and acceptance, all on device-generated synthetic data
+    (N(0,1) hidden states and KV entries, one-hot drafts); weights as in the
+    workloads (N(0, 1/d), packed)."""
+    import numpy as np
+    import torch
+
+    import verify_pass_amd as sv
+    from verify_pass_amd import torch_glue as tg
+    from workloads import SHAPES, head_weights, layer_weights
+
+    torch.cuda.set_device(0)
+    sh = SHAPES[args.sweep_shape]
+    wt, ctx = args.sweep_wtype, args.sweep_ctx
+    blist = [int(v) for v in args.sweep_b.split(",")]
+    glist = [int(v) for v in args.sweep_gamma.split(",")]
+    seed = 20260
+    log(f"sweep: {args.sweep_shape} {wt} ctx {ctx}, B {blist}, gamma {glist}")
+    mats = {k: tg.upload_matrix(v, packed=True) for k, v in layer_weights(sh, wt, seed).items()}
+    lm = tg.upload_matrix(head_weights(sh, wt, seed), packed=True)
+    Ld = tg.decoder_struct(sh, wt, mats, packed=True)
+    Lh = tg.head_struct(sh, wt, lm, packed=True)
+    V = sh.vocab
+    stream = tg.stream_handle()
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    rows = []
+    for B in blist:
+        cap = (ctx + max(glist) + 1 + 31) // 32 * 32
+        kcs = [torch.randn(sh.n_kv, cap, sh.hd, device="cuda", generator=gen).to(torch.bfloat16)
+               for _ in range(B)]
+        vcs = [torch.randn(sh.n_kv, cap // 32, sh.hd, 32, device="cuda", generator=gen).to(torch.bfloat16)
+               for _ in range(B)]
+        for g in glist:
+            T = B * (g + 1)
+            batch = tg.DeviceBatch([g] * B, [ctx] * B, cap)
+            batch.k, batch.v = kcs, vcs
+            batch.kptr = torch.tensor([t.data_ptr() for t in kcs], dtype=torch.int64, device="cuda")
+            batch.vptr = torch.tensor([t.data_ptr() for t in vcs], dtype=torch.int64, device="cuda")
+            bs = batch.struct()
+            nd = sv.sv_verify_layer_workspace_bytes(Ld, bs)
+            nh = sv.sv_verify_layer_workspace_bytes(Lh, bs)
+            na = sv.sv_accept_commit_workspace_bytes(B, V, 0, [g] * B)
+            ws = tg.workspace(max(nd, nh, na))
+            nws = ws.numel()
+            x = torch.randn(T, sh.d, device="cuda", generator=gen).to(torch.bfloat16)
+            y = torch.empty_like(x)
+            probs = torch.empty(T, V, dtype=torch.float32, device="cuda")
+            nd_ = max(1, B * g)
+            draft = torch.randint(0, V, (nd_,), device="cuda", generator=gen, dtype=torch.int32)
+            q = torch.zeros(nd_, V, device="cuda")
+            q[torch.arange(nd_, device="cuda"), draft.long()] = 1.0
+            ua = torch.rand(nd_, device="cuda", generator=gen)
+            us = torch.rand(B, device="cuda", generator=gen)
+            acc = torch.zeros(B, dtype=torch.int32, device="cuda")
+            nxt = torch.zeros(B, dtype=torch.int32, device="cuda")
+            kv0 = batch.kv_len.clone()
+            gl = [g] * B
+
+            def step():
+                batch.kv_len.copy_(kv0)
+                assert sv.sv_verify_layer(Ld, bs, x, y, 0, ws, nws, stream) == 0
+                assert sv.sv_verify_layer(Lh, bs, y, probs, 0, ws, nws, stream) == 0
+                assert sv.sv_accept_commit(B, V, 0, gl, batch.gamma, draft, probs, q, ua, us,
+                                           batch.kv_len, acc, nxt, batch.err, ws, nws, stream) == 0
+            for _ in range(3):
+                step()
+            torch.cuda.synchronize()
+            n_it = 10 if T <= 512 else 4
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(n_it):
+                step()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / n_it
+            assert batch.err.item() == 0
+            row = {"B": B, "gamma": g, "T": T, "ms": round(ms, 5),
+                   "verify_tok_s": round(T / ms * 1e3, 1),
+                   "accepted_tok_s_alpha0.8": round(B * expected_tokens(0.8, g) / ms * 1e3, 1)}
+            rows.append(row)
+            log(json.dumps(row))
+            del probs, q, ws, x, y
+        del kcs, vcs
+        torch.cuda.empty_cache()
+
+    fits = {}
+    for g in glist:
+        pts = sorted((r["B"], r["ms"]) for r in rows if r["gamma"] == g)
+        if len(pts) < 3:
+            continue
+        tw, k, c = fit_step_model([p[0] for p in pts], [p[1] for p in pts], g + 1)
+        den = (g + 1) * c - k
+        fits[g] = {"t_w_ms": tw, "k_ms": k, "c_ms": c, "bstar_fit": (tw / den) if den > 0 else None}
+    base = {r["B"]: r["ms"] for r in rows if r["gamma"] == 0}
+    for g in glist:
+        first = next((r["B"] for r in sorted(rows, key=lambda r: r["B"])
+                      if r["gamma"] == g and r["B"] in base and r["ms"] > 1.1 * base[r["B"]]), None)
+        if g in fits:
+            fits[g]["first_B_over_1.1x_gamma0"] = first
+    # draft lengths the library's planner picks with the fitted model (gamma = 1 fit)
+    plan = None
+    if 1 in fits:
+        f = fits[1]
+        pp = sv.make_plan_params(sv.SV_PLAN_SPEEDUP, 8, t_w_ms=f["t_w_ms"], k_ms=f["k_ms"],
+                                 c_ms=f["c_ms"], alpha=(0.8,))
+        plan = {}
+        for B in blist:
+            st, gam, bstar = sv.sv_plan_gamma(pp, B)
+            plan[B] = {"gamma": gam[0] if gam else None, "bstar": bstar}
+    out = {"shape": args.sweep_shape, "wtype": wt, "ctx": ctx, "rows": rows,
+           "fits": {str(g): v for g, v in fits.items()}, "planner_gamma_alpha0.8": plan}
+    if args.sweep_out:
+        with open(args.sweep_out, "w") as fh:
+            json.dump(out, fh, indent=1)
+    log(json.dumps(out["fits"]))
+    print(json.dumps({"sweep": True, "points": len(rows), "fits": out["fits"]}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -146,6 +288,15 @@ def main():
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-table", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time the step over a (B, gamma) grid on one layer shape instead, fit the "
+                         "step model per gamma and report the crossover batch")
+    ap.add_argument("--sweep-shape", default="9b", choices=("9b", "27b"))
+    ap.add_argument("--sweep-wtype", default="bf16", choices=("bf16", "int4"))
+    ap.add_argument("--sweep-ctx", type=int, default=2048)
+    ap.add_argument("--sweep-b", default="1,2,4,8,16,32,64,128,256")
+    ap.add_argument("--sweep-gamma", default="0,1,2,3,4,5,7")
+    ap.add_argument("--sweep-out", default="")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before the steps, copy a buffer of this many MiB device to device three "
                          "times (the known-size reference for HBM traffic counters)")
@@ -154,6 +305,9 @@ def main():
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the "
               "sharded design is described in DESIGN.md", file=sys.stderr)
         sys.exit(2)
+    if args.sweep:
+        sweep(args)
+        return
 
     import numpy as np
     import torch

@@ -236,10 +236,13 @@ __global__ __launch_bounds__(64 * waves_per_wg<KW>(), (min_wg_per_cu<WT, TT, G, 
   const bool active = wg * UPW + slot < nunits;
   if (KW == 1 && !active) return;
   const int unit = min(wg * UPW + slot, nunits - 1);
-  const int grp = unit % ngrp;
-  const int rest = unit / ngrp;
-  const int split = rest % p.splits;
-  const int tb = rest / p.splits;
+  // token block fastest: the units that share a row group's weights sit in
+  // the same and in neighbouring workgroups on one XCD, so only the first of
+  // them streams those weights from HBM and the others find them in L2
+  const int tb = unit % p.ntblk;
+  const int rest = unit / p.ntblk;
+  const int grp = rest % ngrp;
+  const int split = rest / ngrp;
   const int t0 = tb * TT * 16;
   const int u0 = (int)((long long)split * p.ksteps / p.splits);
   const int u1 = (int)((long long)(split + 1) * p.ksteps / p.splits);
