@@ -247,6 +247,7 @@ LAUNCH_SETTINGS = [
     "qkv:1:4:8,o:1:8:8,gu:1:8:8,down:2:8:8",
     "qkv:2:4:16,o:1:4:16,gu:1:4:16,down:4:4:16",
     "qkv:4:2:1,o:2:4:1,gu:3:8:1,down:5:2:1",
+    "qkv:1:2:0,o:1:2:0,gu:1:2:0,down:1:2:0",   # LDS-tiled kernel (bf16 packed)
 ]
 
 
@@ -285,7 +286,8 @@ def test_head_launch_settings(wtype):
     yd = tg.to_dev(yh)
     ref = OV.head_logits(head.Wlm, yh)
     try:
-        for spec in (None, "head:1:4:1", "head:1:8:1", "head:1:8:4", "head:2:4:8", "head:3:8:1"):
+        for spec in (None, "head:1:4:1", "head:1:8:1", "head:1:8:4", "head:2:4:8", "head:3:8:1",
+                     "head:1:2:0"):
             assert sv.sv_set_gemm_tuning(spec) == 0
             n = sv.sv_verify_layer_workspace_bytes(head.L, head.bs, sv.SV_HEAD_LOGITS)
             head.ws = tg.workspace(n)
@@ -321,3 +323,36 @@ def test_kv_overflow_flagged_and_contained():
                                       sentinel_before[i][:, c + gamma[i] + 1:])
     # the overflowing sequence keeps its cached prefix
     np.testing.assert_array_equal(dec.batch.k_logical(1)[:, :222], sentinel_before[1][:, :222])
+
+
+@pytest.mark.parametrize("tiling", [None, "qkv:1:2:0,o:1:2:0,gu:1:2:0,down:1:2:0,head:1:2:0"])
+def test_many_tokens_layer_and_head(tiling):
+    """300 stacked tokens (three 128-token blocks of the tiled kernel with a
+    ragged tail): decoder layer and head against the oracle, with the default
+    policy (tiled where it has enough workgroups) and with every GEMM tiled."""
+    shape = Shape(2048, 16, 4, 128, 8192, 20011)
+    gamma = [14] * 18 + [11, 12, 4]                  # 18*15 + 12 + 13 + 5 = 300 tokens
+    ctx = [int(c) for c in np.linspace(0, 300, len(gamma)).astype(int)]
+    wl = custom_workload(shape, "bf16", gamma, ctx, seed=17)
+    assert wl.T == 300
+    try:
+        assert sv.sv_set_gemm_tuning(tiling) == 0
+        dec = GpuDecoder(wl, packed=True)
+        xh = hidden_states(wl.T, shape.d, wl.seed)
+        y = dec.run(tg.to_dev(xh))
+        torch.cuda.synchronize()
+        assert dec.batch.err.item() == 0
+        seqs = [0, 7, len(gamma) - 2, len(gamma) - 1]
+        ref = dec.oracle(xh, seqs=seqs)
+        yh = dev_bf16_to_f64(y)
+        err = rel_rows(yh[ref.rows], ref.y)
+        say(f"many tokens [{tiling}]: y rel err {err:.2e}")
+        assert err < TOL["bf16"]
+        head = GpuHead(wl, packed=True)
+        lg = head.run(y, logits=True).cpu().numpy()
+        rows = [0, 127, 128, 255, 256, 299]
+        errh = rel_rows(lg[rows], OV.head_logits(head.Wlm, yh[rows]))
+        say(f"  head logits rel err {errh:.2e}")
+        assert errh < TOL["bf16"]
+    finally:
+        sv.sv_set_gemm_tuning(None)

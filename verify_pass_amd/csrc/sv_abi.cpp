@@ -117,8 +117,8 @@ enum GemmKind { GK_QKV = 0, GK_O, GK_GU, GK_DOWN, GK_HEAD, GK_COUNT };
 
 // Optional override of the launch policy (tuning sweeps, tests):
 // "qkv:1:4:16,o:1:4:16,gu:1:8:4,down:1:8:16,head:1:2:1"
-// (kind:splits:depth[:waves per unit]), from SV_GEMM_TUNE at load time or
-// sv_set_gemm_tuning.
+// (kind:splits:depth[:waves per unit, 0 = the LDS-tiled kernel]), from
+// SV_GEMM_TUNE at load time or sv_set_gemm_tuning.
 struct Tune {
   int splits[GK_COUNT];
   int depth[GK_COUNT];
@@ -126,7 +126,10 @@ struct Tune {
 };
 
 bool parse_tune(const char *e, Tune &r) {
-  for (int i = 0; i < GK_COUNT; ++i) r.splits[i] = r.depth[i] = r.kw[i] = 0;
+  for (int i = 0; i < GK_COUNT; ++i) {
+    r.splits[i] = r.depth[i] = 0;
+    r.kw[i] = -1;  // not set
+  }
   if (!e) return true;
   const char *names[GK_COUNT] = {"qkv", "o", "gu", "down", "head"};
   for (int i = 0; i < GK_COUNT; ++i) {
@@ -168,7 +171,7 @@ struct GemmCfg {
 // of one workgroup per unit (4, 8 or 16, each at least 4 K steps), the fewest
 // that reach 2048 waves; K split across units only if that is still short.
 // The prefetch depth then covers a wave's steps in one or two rounds.
-GemmCfg gemm_cfg(int kind, int nblk, int N, int T, int K, int wtype) {
+GemmCfg gemm_cfg(int kind, int nblk, int N, int T, int K, int wtype, bool packed) {
   constexpr int kFill = 2048;
   GemmCfg c;
   c.nblk = nblk;
@@ -204,10 +207,24 @@ GemmCfg gemm_cfg(int kind, int nblk, int N, int T, int K, int wtype) {
            (long long)base * c.kw * (c.splits + 1) <= 2 * kFill && c.ksteps / ((c.splits + 1) * c.kw) >= 4)
       ++c.splits;
   }
+  // many tokens (bf16, packed): the LDS-tiled kernel, when its grid of
+  // (256 rows x 128 tokens) tiles has enough workgroups
+  const bool tiled_ok = wtype == SV_W_BF16 && packed;
+  const long long tiled_wgs = (long long)((nblk + 7) / 8) * ((T + 127) / 128);
+  if (tiled_ok && T >= 128 && tiled_wgs >= 128) {
+    c.kw = kGemmTiled;
+    c.splits = 1;
+  }
   const Tune tn = tune();
   if (tn.splits[kind] > 0) c.splits = std::max(1, std::min(tn.splits[kind], c.ksteps));
   if (tn.depth[kind] > 0) c.depth = tn.depth[kind];
-  if (tn.kw[kind] > 0) c.kw = tn.kw[kind] >= 16 ? 16 : tn.kw[kind] >= 8 ? 8 : tn.kw[kind] >= 4 ? 4 : 1;
+  if (tn.kw[kind] == 0 && tiled_ok) {
+    c.kw = kGemmTiled;
+    c.splits = 1;
+  } else if (tn.kw[kind] > 0) {
+    c.kw = tn.kw[kind] >= 16 ? 16 : tn.kw[kind] >= 8 ? 8 : tn.kw[kind] >= 4 ? 4 : 1;
+  }
+  if (c.kw == kGemmTiled) c.splits = 1;
   if (c.splits > 1 && (size_t)base > kMaxCounters) c.splits = 1;
   return c;
 }
@@ -255,6 +272,7 @@ sv_status plan_layer(const sv_layer *L, const sv_batch *b, int32_t flags, LayerP
     return SV_OK;
   }
   const int w = L->wtype;
+  const bool packed = L->layout == SV_LAYOUT_PACKED;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -277,7 +295,7 @@ sv_status plan_layer(const sv_layer *L, const sv_batch *b, int32_t flags, LayerP
   if (L->kind == SV_LAYER_HEAD) {
     if (L->vocab <= 0) return SV_ERR_INVALID_ARG;
     if (check_matrix(L->lm_head, w) != SV_OK) return SV_ERR_INVALID_ARG;
-    pl.head = gemm_cfg(GK_HEAD, (L->vocab + 31) / 32, L->vocab, pl.T, L->d, w);
+    pl.head = gemm_cfg(GK_HEAD, (L->vocab + 31) / 32, L->vocab, pl.T, L->d, w, packed);
     pl.off_counters = take(kCounterBytes);
     pl.off_partial = take(pl.head.partial_floats() * sizeof(float));
     pl.off_stats = take((size_t)pl.head.nblk * pl.T * 2 * sizeof(float));
@@ -304,10 +322,10 @@ sv_status plan_layer(const sv_layer *L, const sv_batch *b, int32_t flags, LayerP
   if (pl.B > 0 && (!b->gamma || !b->kv_len || !b->k_cache || !b->v_cache)) return SV_ERR_INVALID_ARG;
 
   const int nqkv = (hq + 2 * hk) * hd;
-  pl.qkv = gemm_cfg(GK_QKV, nqkv / 32, nqkv, pl.T, d, w);
-  pl.o = gemm_cfg(GK_O, (d + 31) / 32, d, pl.T, hq * hd, w);
-  pl.gu = gemm_cfg(GK_GU, (F + 15) / 16, 2 * F, pl.T, d, w);
-  pl.down = gemm_cfg(GK_DOWN, (d + 31) / 32, d, pl.T, F, w);
+  pl.qkv = gemm_cfg(GK_QKV, nqkv / 32, nqkv, pl.T, d, w, packed);
+  pl.o = gemm_cfg(GK_O, (d + 31) / 32, d, pl.T, hq * hd, w, packed);
+  pl.gu = gemm_cfg(GK_GU, (F + 15) / 16, 2 * F, pl.T, d, w, packed);
+  pl.down = gemm_cfg(GK_DOWN, (d + 31) / 32, d, pl.T, F, w, packed);
   pl.attn_rpad = 16 * ((pl.G * (gmax + 1) + 15) / 16);
   // keys per work item: 256, or more so that a sequence has at most 32 chunks
   const long long max_len = (long long)b->max_ctx + gmax + 1;

@@ -6,4 +6,7 @@ hipError_t launch_gemm_bf16(const GemmParams &p, int tok_tiles, int depth, int k
                           int trace_class) {
   return launch_wt<WT_BF16>(p, tok_tiles, depth, kw, s, trace_class);
 }
+hipError_t launch_gemm_tiled_bf16(const GemmParams &p, hipStream_t s, int trace_class) {
+  return launch_tiled(p, s, trace_class);
+}
 }  // namespace sv

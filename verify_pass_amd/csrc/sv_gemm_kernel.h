@@ -25,6 +25,10 @@ __device__ __forceinline__ uint4 ld_nt(const void *p) {
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
   return __builtin_bit_cast(uint4, v);
 }
+// Plain 16-byte load through the vector type (keeps staging arrays in registers).
+__device__ __forceinline__ uint4 ld_v4(const void *p) {
+  return __builtin_bit_cast(uint4, *reinterpret_cast<const u32x4 *>(p));
+}
 
 // Per-lane weight stream of one 16-row tile.
 // Lane (row, gq) of step ks holds, for MFMA m, reduction indices
@@ -202,6 +206,160 @@ __device__ __forceinline__ float load_dev(const float *p) {
 // wait until this wave's outstanding vector memory operations have completed
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// RMSNorm scale of the unit's tokens and the fused epilogue of one 32-row
+// group: acc[a][tt] holds rows (group grp, tile a, 4*gq + i) x token
+// t0 + 16*tt + l16 of this lane.
+template <int TT, int EPI>
+__device__ __forceinline__ void epilogue(const GemmParams &p, floatx4 (&acc)[2][TT], int grp, int t0, int gq,
+                                         int l16) {
+  // per-token RMSNorm scale of the operand rows (lane's token is t0 + tt*16 + l16):
+  // precomputed scales, or sums of squares left in partials by the producer
+  float rs[TT];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) {
+    const int t = min(t0 + tt * 16 + l16, p.T - 1);
+    if (p.rnorm) {
+      rs[tt] = p.rnorm[t];
+    } else if (p.rparts) {
+      // lane group gq adds partials gq, gq+4, ... of its token; then the groups
+      float s = 0.f;
+      const float *pr = p.rparts + (size_t)t * p.nparts;
+#pragma unroll 8
+      for (int g = gq; g < p.nparts; g += 4) s += pr[g];
+      s += __shfl_xor(s, 16);
+      s += __shfl_xor(s, 32);
+      rs[tt] = 1.f / sqrtf(s / static_cast<float>(p.K) + p.eps);
+    } else {
+      rs[tt] = 1.f;
+    }
+  }
+
+  // ---- fused epilogues (lane-local) -----------------------------------------
+  if constexpr (EPI == EPI_RESID) {
+    uint16_t *out = static_cast<uint16_t *>(p.out);
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      const int t = t0 + tt * 16 + l16;
+      float sq = 0.f;  // this lane's share of the output row's sum of squares
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int n = grp * 32 + a * 16 + 4 * gq + i;
+          if (n < p.N && t < p.T) {
+            const size_t o = (size_t)t * p.ldo + n;
+            const uint16_t h = f2bf(acc[a][tt][i] * rs[tt] + bf2f(p.resid[o]));
+            out[o] = h;
+            const float f = bf2f(h);
+            sq += f * f;
+          }
+        }
+      if (p.sq_out) {
+        sq += __shfl_xor(sq, 16);
+        sq += __shfl_xor(sq, 32);
+        if (gq == 0 && t < p.T) p.sq_out[(size_t)t * p.nblk + grp] = sq;
+      }
+    }
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    uint16_t *out = static_cast<uint16_t *>(p.out);
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      const int t = t0 + tt * 16 + l16;
+      if (t >= p.T) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int f = grp * 16 + 4 * gq + i;
+        if (f < p.mat[0].rows) {
+          const float g = acc[0][tt][i] * rs[tt], u = acc[1][tt][i] * rs[tt];
+          const float sig = 1.f / (1.f + __builtin_amdgcn_exp2f(-g * kLog2e));
+          out[(size_t)t * p.ldo + f] = f2bf(g * sig * u);
+        }
+      }
+    }
+  } else if constexpr (EPI == EPI_LOGITS) {
+    float *out = static_cast<float *>(p.out);
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      const int t = t0 + tt * 16 + l16;
+      float v[8];
+      float m = -INFINITY;
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int n = grp * 32 + a * 16 + 4 * gq + i;
+          v[a * 4 + i] = n < p.N ? acc[a][tt][i] * rs[tt] : -INFINITY;
+          m = fmaxf(m, v[a * 4 + i]);
+          if (t < p.T && n < p.N) out[(size_t)t * p.ldo + n] = v[a * 4 + i];
+        }
+      m = fmaxf(m, __shfl_xor(m, 16));
+      m = fmaxf(m, __shfl_xor(m, 32));
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += __builtin_amdgcn_exp2f((v[e] - m) * kLog2e);
+      s += __shfl_xor(s, 16);
+      s += __shfl_xor(s, 32);
+      if (gq == 0 && t < p.T) {
+        *reinterpret_cast<float2 *>(p.stats + ((size_t)t * p.nblk + grp) * 2) = make_float2(m, s);
+      }
+    }
+  } else {  // EPI_QKV: tile 0 holds pair firsts i, tile 1 the partners i + hd/2
+    const int gph = p.hd / 32;
+    const int head = grp / gph, c = grp - head * gph;
+    const int half = p.hd / 2;
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      const int t = t0 + tt * 16 + l16;
+      if (t >= p.T) continue;
+      const int seq = p.tok_seq[t], pos = p.tok_pos[t];
+      const bool kv_ok = pos >= 0 && pos < p.kv_cap;
+      if (head >= p.hq && !kv_ok) {
+        set_err(p.err, SV_DEV_ERR_KV_OVERFLOW);
+        continue;
+      }
+      float ra[4], rb[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int fi = 16 * c + 4 * gq + e;  // rotation pair (fi, fi + hd/2)
+        const float a = acc[0][tt][e] * rs[tt], b = acc[1][tt][e] * rs[tt];
+        if (head < p.hq + p.hkv) {
+          const float2 cs = *reinterpret_cast<const float2 *>(p.rope_cs + ((size_t)t * half + fi) * 2);
+          ra[e] = a * cs.x - b * cs.y;
+          rb[e] = b * cs.x + a * cs.y;
+        } else {
+          ra[e] = a;
+          rb[e] = b;
+        }
+      }
+      const int fi0 = 16 * c + 4 * gq;
+      if (head < p.hq) {
+        uint16_t *q = p.qbuf + ((size_t)t * p.hq + head) * p.hd;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          q[fi0 + e] = f2bf(ra[e]);
+          q[fi0 + half + e] = f2bf(rb[e]);
+        }
+      } else if (head < p.hq + p.hkv) {
+        uint16_t *k = static_cast<uint16_t *>(p.kc[seq]) + ((size_t)(head - p.hq) * p.kv_cap + pos) * p.hd;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          k[fi0 + e] = f2bf(ra[e]);
+          k[fi0 + half + e] = f2bf(rb[e]);
+        }
+      } else {
+        // values in 32-position blocks: [n_kv][cap/32][hd][32]
+        uint16_t *v = static_cast<uint16_t *>(p.vc[seq]) + (size_t)(head - p.hq - p.hkv) * p.hd * p.kv_cap +
+                      (size_t)(pos >> 5) * p.hd * 32 + (pos & 31);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[(size_t)(fi0 + e) * 32] = f2bf(ra[e]);
+          v[(size_t)(fi0 + half + e) * 32] = f2bf(rb[e]);
+        }
+      }
+    }
+  }
+}
+
 // Waves per workgroup for KW waves per unit.
 template <int KW> constexpr int waves_per_wg() { return KW > 4 ? KW : 4; }
 
@@ -375,151 +533,154 @@ __global__ __launch_bounds__(64 * waves_per_wg<KW>(), (min_wg_per_cu<WT, TT, G, 
     }
   }
 
-  // per-token RMSNorm scale of the operand rows (lane's token is t0 + tt*16 + l16):
-  // precomputed scales, or sums of squares left in partials by the producer
-  float rs[TT];
+  epilogue<TT, EPI>(p, acc, grp, t0, gq, l16);
+}
+
+// ---------------------------------------------------------------------------
+// LDS-tiled GEMM for many stacked tokens (bf16, packed weights).
+//
+// With hundreds of tokens the per-wave streaming kernel above is bound by
+// each wave fetching its own copy of the token operand.  Here a workgroup of
+// 8 waves computes 8 row groups (256 weight rows) x 128 tokens: each K step
+// (64) of the weight fragments (copied in their packed, lane-ordered form) and
+// of the token rows (144-byte padded rows) is staged once in LDS and read by
+// every wave; each wave computes 2 row groups x 64 tokens (32 MFMAs per
+// step).  LDS is double-buffered and the next step's global loads are in
+// flight during the current step's MFMAs.  Workgroups run token block fastest
+// (XCD-aware), so the token blocks of one row block share its weights in L2.
+constexpr int kTThreads = 512;
+constexpr int kTGroups = 8;                                  // 32-row groups per workgroup
+constexpr int kTTok = 128;                                   // tokens per workgroup
+constexpr int kTXStride = 144;                               // bytes per staged token row
+constexpr int kTWBytes = kTGroups * 2 * 2 * 64 * 16;         // 16 tiles x 2 halves x 64 lanes x 16 B
+constexpr int kTXBytes = kTTok * kTXStride;
+constexpr int kTBuf = kTWBytes + kTXBytes;
+constexpr int kTLds = 2 * kTBuf;
+constexpr int kTWPer = kTWBytes / 16 / kTThreads;            // weight fragments staged per thread (4)
+constexpr int kTXPer = kTTok * 8 / kTThreads;                // token chunks staged per thread (2)
+
+template <int EPI>
+__global__ __launch_bounds__(kTThreads, 1) void gemm_tiled_kernel(GemmParams p) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int gq = lane >> 4, l16 = lane & 15;
+  const int ntb = (p.T + kTTok - 1) / kTTok;
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int tb = wg % ntb, rb = wg / ntb;
+  const int gp = wave & 3, th = wave >> 2;  // groups 2gp, 2gp+1 of the block; tokens th*64 ..
+
+  // staging sources: weight fragments f = tid + 512 j (tile f/128, half (f/64)%2,
+  // lane f%64) and token chunks f (row f/8, 16-byte chunk f%8)
+  const unsigned char *wsrc[kTWPer];
+  uint32_t xoff[kTXPer];  // element offsets of this thread's token chunks (step 0)
 #pragma unroll
-  for (int tt = 0; tt < TT; ++tt) {
-    const int t = min(t0 + tt * 16 + l16, p.T - 1);
-    if (p.rnorm) {
-      rs[tt] = p.rnorm[t];
-    } else if (p.rparts) {
-      // lane group gq adds partials gq, gq+4, ... of its token; then the groups
-      float s = 0.f;
-      const float *pr = p.rparts + (size_t)t * p.nparts;
-#pragma unroll 8
-      for (int g = gq; g < p.nparts; g += 4) s += pr[g];
-      s += __shfl_xor(s, 16);
-      s += __shfl_xor(s, 32);
-      rs[tt] = 1.f / sqrtf(s / static_cast<float>(p.K) + p.eps);
-    } else {
-      rs[tt] = 1.f;
+  for (int j = 0; j < kTWPer; ++j) {
+    const int f = tid + kTThreads * j;
+    const int q = f >> 7, m = (f >> 6) & 1, fl = f & 63;
+    int mi = 0, pr0 = 0;
+    if (!map_row(p, rb * kTGroups + (q >> 1), q & 1, 0, mi, pr0)) {
+      mi = 0;
+      pr0 = 0;
     }
+    const size_t tile = (size_t)(pr0 / 16);
+    wsrc[j] = static_cast<const unsigned char *>(p.mat[mi].w) + ((tile * p.ksteps * 2 + m) * 64 + fl) * 16;
+  }
+#pragma unroll
+  for (int j = 0; j < kTXPer; ++j) {
+    const int f = tid + kTThreads * j;
+    xoff[j] = (uint32_t)min(tb * kTTok + (f >> 3), p.T - 1) * (uint32_t)p.K + (f & 7) * 8;
+  }
+  uint4 sw[kTWPer], sx[kTXPer];
+#define SV_TILED_FETCH(st)                                                                          \
+  do {                                                                                             \
+    _Pragma("unroll") for (int j = 0; j < kTWPer; ++j) sw[j] = ld_nt(wsrc[j] + (size_t)(st) * 2048); \
+    _Pragma("unroll") for (int j = 0; j < kTXPer; ++j) sx[j] = ld_v4(p.x + xoff[j] + (st) * 64);   \
+  } while (0)
+#define SV_TILED_STASH(buf)                                                                         \
+  do {                                                                                             \
+    unsigned char *b_ = lds + (buf) * kTBuf;                                                       \
+    _Pragma("unroll") for (int j = 0; j < kTWPer; ++j)                                             \
+        *reinterpret_cast<uint4 *>(b_ + (tid + kTThreads * j) * 16) = sw[j];                       \
+    _Pragma("unroll") for (int j = 0; j < kTXPer; ++j) {                                           \
+      const int f_ = tid + kTThreads * j;                                                          \
+      *reinterpret_cast<uint4 *>(b_ + kTWBytes + (f_ >> 3) * kTXStride + (f_ & 7) * 16) = sx[j];   \
+    }                                                                                              \
+  } while (0)
+
+  floatx4 acc[2][2][4];
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) acc[gi][a][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  SV_TILED_FETCH(0);
+  SV_TILED_STASH(0);
+  __syncthreads();
+  for (int st = 0; st < p.ksteps; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < p.ksteps) SV_TILED_FETCH(st + 1);
+    const unsigned char *bw = lds + buf * kTBuf;
+    const unsigned char *bx = bw + kTWBytes;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      bf16x8 wv[2][2];
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+          const int q = (2 * gp + gi) * 2 + a;
+          wv[gi][a] = as_bf16x8(*reinterpret_cast<const uint4 *>(bw + ((q * 2 + m) * 64 + lane) * 16));
+        }
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const bf16x8 xv = as_bf16x8(*reinterpret_cast<const uint4 *>(
+            bx + (th * 64 + tt * 16 + l16) * kTXStride + (32 * m + 8 * gq) * 2));
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+          for (int a = 0; a < 2; ++a) acc[gi][a][tt] = mfma16x16x32(wv[gi][a], xv, acc[gi][a][tt]);
+      }
+    }
+    if (st + 1 < p.ksteps) SV_TILED_STASH(buf ^ 1);
+    __syncthreads();
   }
 
-  // ---- fused epilogues (lane-local) -----------------------------------------
-  if constexpr (EPI == EPI_RESID) {
-    uint16_t *out = static_cast<uint16_t *>(p.out);
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-      const int t = t0 + tt * 16 + l16;
-      float sq = 0.f;  // this lane's share of the output row's sum of squares
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int n = grp * 32 + a * 16 + 4 * gq + i;
-          if (n < p.N && t < p.T) {
-            const size_t o = (size_t)t * p.ldo + n;
-            const uint16_t h = f2bf(acc[a][tt][i] * rs[tt] + bf2f(p.resid[o]));
-            out[o] = h;
-            const float f = bf2f(h);
-            sq += f * f;
-          }
-        }
-      if (p.sq_out) {
-        sq += __shfl_xor(sq, 16);
-        sq += __shfl_xor(sq, 32);
-        if (gq == 0 && t < p.T) p.sq_out[(size_t)t * p.nblk + grp] = sq;
-      }
-    }
-  } else if constexpr (EPI == EPI_SWIGLU) {
-    uint16_t *out = static_cast<uint16_t *>(p.out);
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-      const int t = t0 + tt * 16 + l16;
-      if (t >= p.T) continue;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int f = grp * 16 + 4 * gq + i;
-        if (f < p.mat[0].rows) {
-          const float g = acc[0][tt][i] * rs[tt], u = acc[1][tt][i] * rs[tt];
-          const float sig = 1.f / (1.f + __builtin_amdgcn_exp2f(-g * kLog2e));
-          out[(size_t)t * p.ldo + f] = f2bf(g * sig * u);
-        }
-      }
-    }
-  } else if constexpr (EPI == EPI_LOGITS) {
-    float *out = static_cast<float *>(p.out);
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-      const int t = t0 + tt * 16 + l16;
-      float v[8];
-      float m = -INFINITY;
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int n = grp * 32 + a * 16 + 4 * gq + i;
-          v[a * 4 + i] = n < p.N ? acc[a][tt][i] * rs[tt] : -INFINITY;
-          m = fmaxf(m, v[a * 4 + i]);
-          if (t < p.T && n < p.N) out[(size_t)t * p.ldo + n] = v[a * 4 + i];
-        }
-      m = fmaxf(m, __shfl_xor(m, 16));
-      m = fmaxf(m, __shfl_xor(m, 32));
-      float s = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s += __builtin_amdgcn_exp2f((v[e] - m) * kLog2e);
-      s += __shfl_xor(s, 16);
-      s += __shfl_xor(s, 32);
-      if (gq == 0 && t < p.T) {
-        *reinterpret_cast<float2 *>(p.stats + ((size_t)t * p.nblk + grp) * 2) = make_float2(m, s);
-      }
-    }
-  } else {  // EPI_QKV: tile 0 holds pair firsts i, tile 1 the partners i + hd/2
-    const int gph = p.hd / 32;
-    const int head = grp / gph, c = grp - head * gph;
-    const int half = p.hd / 2;
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-      const int t = t0 + tt * 16 + l16;
-      if (t >= p.T) continue;
-      const int seq = p.tok_seq[t], pos = p.tok_pos[t];
-      const bool kv_ok = pos >= 0 && pos < p.kv_cap;
-      if (head >= p.hq && !kv_ok) {
-        set_err(p.err, SV_DEV_ERR_KV_OVERFLOW);
-        continue;
-      }
-      float ra[4], rb[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int fi = 16 * c + 4 * gq + e;  // rotation pair (fi, fi + hd/2)
-        const float a = acc[0][tt][e] * rs[tt], b = acc[1][tt][e] * rs[tt];
-        if (head < p.hq + p.hkv) {
-          const float2 cs = *reinterpret_cast<const float2 *>(p.rope_cs + ((size_t)t * half + fi) * 2);
-          ra[e] = a * cs.x - b * cs.y;
-          rb[e] = b * cs.x + a * cs.y;
-        } else {
-          ra[e] = a;
-          rb[e] = b;
-        }
-      }
-      const int fi0 = 16 * c + 4 * gq;
-      if (head < p.hq) {
-        uint16_t *q = p.qbuf + ((size_t)t * p.hq + head) * p.hd;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          q[fi0 + e] = f2bf(ra[e]);
-          q[fi0 + half + e] = f2bf(rb[e]);
-        }
-      } else if (head < p.hq + p.hkv) {
-        uint16_t *k = static_cast<uint16_t *>(p.kc[seq]) + ((size_t)(head - p.hq) * p.kv_cap + pos) * p.hd;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          k[fi0 + e] = f2bf(ra[e]);
-          k[fi0 + half + e] = f2bf(rb[e]);
-        }
-      } else {
-        // values in 32-position blocks: [n_kv][cap/32][hd][32]
-        uint16_t *v = static_cast<uint16_t *>(p.vc[seq]) + (size_t)(head - p.hq - p.hkv) * p.hd * p.kv_cap +
-                      (size_t)(pos >> 5) * p.hd * 32 + (pos & 31);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v[(size_t)(fi0 + e) * 32] = f2bf(ra[e]);
-          v[(size_t)(fi0 + half + e) * 32] = f2bf(rb[e]);
-        }
-      }
-    }
+  for (int gi = 0; gi < 2; ++gi) {
+    const int grp = rb * kTGroups + 2 * gp + gi;
+    if (grp < p.nblk) epilogue<4, EPI>(p, acc[gi], grp, tb * kTTok + th * 64, gq, l16);
+  }
+}
+#undef SV_TILED_FETCH
+#undef SV_TILED_STASH
+
+// Grid of the tiled kernel: row blocks x token blocks.
+inline int tiled_grid(const GemmParams &p) {
+  return ((p.nblk + kTGroups - 1) / kTGroups) * ((p.T + kTTok - 1) / kTTok);
+}
+
+template <int EPI>
+hipError_t launch_tiled_epi(const GemmParams &p, hipStream_t s, int trace_class) {
+  static bool attr = false;
+  if (!attr) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_tiled_kernel<EPI>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kTLds);
+    attr = true;
+  }
+  trace_before(trace_class, s);
+  hipLaunchKernelGGL((gemm_tiled_kernel<EPI>), dim3(tiled_grid(p)), dim3(kTThreads), kTLds, s, p);
+  trace_after(trace_class, s);
+  return hipGetLastError();
+}
+
+inline hipError_t launch_tiled(const GemmParams &p, hipStream_t s, int trace_class) {
+  switch (p.epi) {
+    case EPI_QKV: return launch_tiled_epi<EPI_QKV>(p, s, trace_class);
+    case EPI_RESID: return launch_tiled_epi<EPI_RESID>(p, s, trace_class);
+    case EPI_SWIGLU: return launch_tiled_epi<EPI_SWIGLU>(p, s, trace_class);
+    default: return launch_tiled_epi<EPI_LOGITS>(p, s, trace_class);
   }
 }
 
