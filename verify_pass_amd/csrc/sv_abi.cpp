@@ -208,10 +208,12 @@ GemmCfg gemm_cfg(int kind, int nblk, int N, int T, int K, int wtype, bool packed
       ++c.splits;
   }
   // many tokens (bf16, packed): the LDS-tiled kernel, when its grid of
-  // (256 rows x 128 tokens) tiles has enough workgroups
+  // (256 rows x 128 tokens) tiles has enough workgroups; from 49 tokens on it
+  // beats streaming the head (measured), where the streaming kernel's
+  // four-tile token blocks become bound by the token-operand traffic
   const bool tiled_ok = wtype == SV_W_BF16 && packed;
   const long long tiled_wgs = (long long)((nblk + 7) / 8) * ((T + 127) / 128);
-  if (tiled_ok && T >= 128 && tiled_wgs >= 128) {
+  if (tiled_ok && T > 48 && tiled_wgs >= 128) {
     c.kw = kGemmTiled;
     c.splits = 1;
   }

@@ -7,7 +7,8 @@
 // to the longest sequence.  Work items are (sequence, key chunk) pairs
 // enumerated by a prefix sum over per-sequence chunk counts, times KV heads.
 //
-// Per wave, 32 keys at a time:
+// Per wave, 32 keys at a time (values loaded once the keys are used, so the
+// two are never live together):
 //   S^T[key][row] = K Q^T  (MFMA: keys are M, query rows N, head dim K)
 //   online softmax in fp32 (exp2 domain), row max across lanes by shuffles
 //   O^T[d][row] += V^T P^T (MFMA: head dim M, query rows N, keys K)
@@ -52,32 +53,32 @@ __device__ __forceinline__ float load_dev(const float *p) {
 }
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// One step's raw operands: keys (MFMA row m of key tile kt is key
-// k0 + 8*(m/4) + 4*kt + m%4) and values (lane (d = 16*dt + l16, gq) holds
+// One step's operands, loaded in two parts so that keys and values are not
+// live at the same time: keys (MFMA row m of key tile kt is key
+// k0 + 8*(m/4) + 4*kt + m%4), then values (lane (d = 16*dt + l16, gq) holds
 // keys k0 + 8*gq .. +7 of head-dim column d).
-template <int HD> struct Step {
-  uint4 k[2][HD / 32];
-  uint4 v[HD / 16];
-};
-
 template <int HD>
-__device__ __forceinline__ void load_step(Step<HD> &s, const uint16_t *kbase, const uint16_t *vbase, int k0,
-                                          int L, int l16, int gq) {
+__device__ __forceinline__ void load_keys(uint4 (&k)[2][HD / 32], const uint16_t *kbase, int k0, int L, int l16,
+                                          int gq) {
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
     const int key = min(k0 + 8 * (l16 >> 2) + 4 * kt + (l16 & 3), L - 1);
     const uint16_t *kr = kbase + (size_t)key * HD;
 #pragma unroll
-    for (int dg = 0; dg < HD / 32; ++dg) s.k[kt][dg] = *reinterpret_cast<const uint4 *>(kr + dslice(dg, gq));
+    for (int dg = 0; dg < HD / 32; ++dg) k[kt][dg] = *reinterpret_cast<const uint4 *>(kr + dslice(dg, gq));
   }
+}
+
+template <int HD>
+__device__ __forceinline__ void load_values(uint4 (&v)[HD / 16], const uint16_t *vbase, int k0, int l16, int gq) {
   // k0 is a multiple of 32 and the block lies inside the cache (cap % 32 == 0)
   const uint16_t *vb = vbase + (size_t)(k0 >> 5) * HD * 32 + 8 * gq;
 #pragma unroll
-  for (int dt = 0; dt < HD / 16; ++dt) s.v[dt] = *reinterpret_cast<const uint4 *>(vb + (dt * 16 + l16) * 32);
+  for (int dt = 0; dt < HD / 16; ++dt) v[dt] = *reinterpret_cast<const uint4 *>(vb + (dt * 16 + l16) * 32);
 }
 
 template <int RT, int HD>
-__global__ __launch_bounds__(kThreads, (RT == 1 ? 3 : 1)) void attn_kernel(AttnParams p) {
+__global__ __launch_bounds__(kThreads, (RT == 1 ? 4 : RT <= 3 ? 2 : 1)) void attn_kernel(AttnParams p) {
   constexpr int NDG = HD / 32;  // MFMA k-groups over the head dim
   constexpr int NDT = HD / 16;  // 16-wide head-dim tiles of the output
   extern __shared__ __align__(16) unsigned char smem[];
@@ -149,47 +150,39 @@ __global__ __launch_bounds__(kThreads, (RT == 1 ? 3 : 1)) void attn_kernel(AttnP
   }
 
   for (int k0 = kw0; k0 < kw1; k0 += kKeysPerStep) {
-    Step<HD> cur;
-    load_step<HD>(cur, kbase, vbase, k0, L, l16, gq);
-
-    // values of keys at or past L are zeroed (the cache holds anything there)
-    bf16x8 vf[NDT];
-    const int nvalid = L - (k0 + 8 * gq);
+    uint4 kr[2][NDG];
+    load_keys<HD>(kr, kbase, k0, L, l16, gq);
+    // scores of every row tile first; the keys are dead afterwards
+    floatx4 s[RT][2];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      uint4 v = cur.v[dt];
-      if (nvalid < 8) {
-        uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (e >= nvalid) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-        v = uint4{w[0], w[1], w[2], w[3]};
-      }
-      vf[dt] = as_bf16x8(v);
-    }
-
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      floatx4 s[2];
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        s[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        s[rt][kt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int dg = 0; dg < NDG; ++dg) s[kt] = mfma16x16x32(as_bf16x8(cur.k[kt][dg]), qf[rt][dg], s[kt]);
+        for (int dg = 0; dg < NDG; ++dg) s[rt][kt] = mfma16x16x32(as_bf16x8(kr[kt][dg]), qf[rt][dg], s[rt][kt]);
       }
+    // values in flight during the softmax arithmetic
+    uint4 vr[NDT];
+    load_values<HD>(vr, vbase, k0, l16, gq);
+
+    bf16x8 pf[RT];
+    float alpha[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
       float sv[8];
       float mx = kNegBig;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int key = k0 + 8 * gq + e;
         const bool ok = key < kw1 && key <= lim[rt];
-        sv[e] = ok ? s[e >> 2][e & 3] * p.scale_log2 : -INFINITY;
+        sv[e] = ok ? s[rt][e >> 2][e & 3] * p.scale_log2 : -INFINITY;
         mx = fmaxf(mx, sv[e]);
       }
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float m_new = fmaxf(m_run[rt], mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run[rt] - m_new);
+      alpha[rt] = __builtin_amdgcn_exp2f(m_run[rt] - m_new);
       float lsum = 0.f;
       uint32_t pb[8];
 #pragma unroll
@@ -198,14 +191,29 @@ __global__ __launch_bounds__(kThreads, (RT == 1 ? 3 : 1)) void attn_kernel(AttnP
         lsum += pe;
         pb[e] = f2bf(pe);
       }
-      l_run[rt] = l_run[rt] * alpha + lsum;
+      l_run[rt] = l_run[rt] * alpha[rt] + lsum;
       m_run[rt] = m_new;
-      const bf16x8 pf = as_bf16x8(uint4{pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16),
-                                        pb[4] | (pb[5] << 16), pb[6] | (pb[7] << 16)});
+      pf[rt] = as_bf16x8(uint4{pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16), pb[4] | (pb[5] << 16),
+                               pb[6] | (pb[7] << 16)});
+    }
+
+    // values of keys at or past L are zeroed (the cache holds anything there)
+    const int nvalid = L - (k0 + 8 * gq);
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        o[rt][dt] *= alpha;
-        o[rt][dt] = mfma16x16x32(vf[dt], pf, o[rt][dt]);
+    for (int dt = 0; dt < NDT; ++dt) {
+      uint4 v = vr[dt];
+      if (nvalid < 8) {
+        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (e >= nvalid) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+        v = uint4{w[0], w[1], w[2], w[3]};
+      }
+      const bf16x8 vf = as_bf16x8(v);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        o[rt][dt] *= alpha[rt];
+        o[rt][dt] = mfma16x16x32(vf, pf[rt], o[rt][dt]);
       }
     }
   }

@@ -224,7 +224,7 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, floatx4 (&acc)[2][
       // lane group gq adds partials gq, gq+4, ... of its token; then the groups
       float s = 0.f;
       const float *pr = p.rparts + (size_t)t * p.nparts;
-#pragma unroll 8
+#pragma unroll 32
       for (int g = gq; g < p.nparts; g += 4) s += pr[g];
       s += __shfl_xor(s, 16);
       s += __shfl_xor(s, 32);
@@ -542,22 +542,37 @@ __global__ __launch_bounds__(64 * waves_per_wg<KW>(), (min_wg_per_cu<WT, TT, G, 
 // With hundreds of tokens the per-wave streaming kernel above is bound by
 // each wave fetching its own copy of the token operand.  Here a workgroup of
 // 8 waves computes 8 row groups (256 weight rows) x 128 tokens: each K step
-// (64) of the weight fragments (copied in their packed, lane-ordered form) and
-// of the token rows (144-byte padded rows) is staged once in LDS and read by
-// every wave; each wave computes 2 row groups x 64 tokens (32 MFMAs per
-// step).  LDS is double-buffered and the next step's global loads are in
-// flight during the current step's MFMAs.  Workgroups run token block fastest
-// (XCD-aware), so the token blocks of one row block share its weights in L2.
+// (64) of the weight fragments (in their packed, lane-ordered form) and of the
+// token rows is loaded straight into LDS (global_load_lds, 16 bytes per lane)
+// and read by every wave; each wave computes 2 row groups x 64 tokens (32
+// MFMAs per step).  Three LDS buffers keep the loads of the next two steps in
+// flight during the current step's MFMAs.  A token row's eight 16-byte chunks
+// are stored XOR-swizzled by the row index, which spreads the MFMA operand
+// reads over the LDS banks.  Workgroups run token block fastest (XCD-aware),
+// so the token blocks of one row block share its weights in L2.
 constexpr int kTThreads = 512;
 constexpr int kTGroups = 8;                                  // 32-row groups per workgroup
 constexpr int kTTok = 128;                                   // tokens per workgroup
-constexpr int kTXStride = 144;                               // bytes per staged token row
 constexpr int kTWBytes = kTGroups * 2 * 2 * 64 * 16;         // 16 tiles x 2 halves x 64 lanes x 16 B
-constexpr int kTXBytes = kTTok * kTXStride;
+constexpr int kTXBytes = kTTok * 128;                        // 128 rows x 64 bf16
 constexpr int kTBuf = kTWBytes + kTXBytes;
-constexpr int kTLds = 2 * kTBuf;
-constexpr int kTWPer = kTWBytes / 16 / kTThreads;            // weight fragments staged per thread (4)
-constexpr int kTXPer = kTTok * 8 / kTThreads;                // token chunks staged per thread (2)
+constexpr int kTStages = 3;
+constexpr int kTLds = kTStages * kTBuf;
+constexpr int kTWPer = kTWBytes / 16 / kTThreads;            // weight fragments loaded per thread (4)
+constexpr int kTXPer = kTXBytes / 16 / kTThreads;            // token chunks loaded per thread (2)
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Workgroup barrier for the LDS ring: __syncthreads() would also wait for all
+// of this wave's outstanding global loads (its release fence covers the
+// direct-to-LDS loads), draining the prefetch.  The waits it needs are issued
+// explicitly (vmcnt for this wave's loads of the step); the empty asm keeps the
+// compiler from moving LDS accesses across the barrier.
+__device__ __forceinline__ void ring_barrier() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
 
 template <int EPI>
 __global__ __launch_bounds__(kTThreads, 1) void gemm_tiled_kernel(GemmParams p) {
@@ -569,8 +584,10 @@ __global__ __launch_bounds__(kTThreads, 1) void gemm_tiled_kernel(GemmParams p) 
   const int tb = wg % ntb, rb = wg / ntb;
   const int gp = wave & 3, th = wave >> 2;  // groups 2gp, 2gp+1 of the block; tokens th*64 ..
 
-  // staging sources: weight fragments f = tid + 512 j (tile f/128, half (f/64)%2,
-  // lane f%64) and token chunks f (row f/8, 16-byte chunk f%8)
+  // Load j of this thread fills LDS bytes [16 f, 16 f + 16) of its region,
+  // f = tid + 512 j (a wave's 64 lanes fill one contiguous KiB).
+  //  weights: fragment f = (tile f/128, half (f/64)%2, lane f%64) of the packed layout
+  //  tokens:  row f/8, slot f%8 holding chunk (f%8) ^ (row%8) of the row's 64 values
   const unsigned char *wsrc[kTWPer];
   uint32_t xoff[kTXPer];  // element offsets of this thread's token chunks (step 0)
 #pragma unroll
@@ -588,24 +605,11 @@ __global__ __launch_bounds__(kTThreads, 1) void gemm_tiled_kernel(GemmParams p) 
 #pragma unroll
   for (int j = 0; j < kTXPer; ++j) {
     const int f = tid + kTThreads * j;
-    xoff[j] = (uint32_t)min(tb * kTTok + (f >> 3), p.T - 1) * (uint32_t)p.K + (f & 7) * 8;
+    const int r = f >> 3, c = (f & 7) ^ (r & 7);
+    xoff[j] = (uint32_t)min(tb * kTTok + r, p.T - 1) * (uint32_t)p.K + c * 8;
   }
-  uint4 sw[kTWPer], sx[kTXPer];
-#define SV_TILED_FETCH(st)                                                                          \
-  do {                                                                                             \
-    _Pragma("unroll") for (int j = 0; j < kTWPer; ++j) sw[j] = ld_nt(wsrc[j] + (size_t)(st) * 2048); \
-    _Pragma("unroll") for (int j = 0; j < kTXPer; ++j) sx[j] = ld_v4(p.x + xoff[j] + (st) * 64);   \
-  } while (0)
-#define SV_TILED_STASH(buf)                                                                         \
-  do {                                                                                             \
-    unsigned char *b_ = lds + (buf) * kTBuf;                                                       \
-    _Pragma("unroll") for (int j = 0; j < kTWPer; ++j)                                             \
-        *reinterpret_cast<uint4 *>(b_ + (tid + kTThreads * j) * 16) = sw[j];                       \
-    _Pragma("unroll") for (int j = 0; j < kTXPer; ++j) {                                           \
-      const int f_ = tid + kTThreads * j;                                                          \
-      *reinterpret_cast<uint4 *>(b_ + kTWBytes + (f_ >> 3) * kTXStride + (f_ & 7) * 16) = sx[j];   \
-    }                                                                                              \
-  } while (0)
+  // wave-uniform LDS destination of load j (lane offsets are implicit)
+  const int wbase = wave * 64 * 16;
 
   floatx4 acc[2][2][4];
 #pragma unroll
@@ -615,13 +619,30 @@ __global__ __launch_bounds__(kTThreads, 1) void gemm_tiled_kernel(GemmParams p) 
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) acc[gi][a][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  SV_TILED_FETCH(0);
-  SV_TILED_STASH(0);
-  __syncthreads();
-  for (int st = 0; st < p.ksteps; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < p.ksteps) SV_TILED_FETCH(st + 1);
-    const unsigned char *bw = lds + buf * kTBuf;
+  auto issue = [&](int st, int buf) {
+    unsigned char *b = lds + buf * kTBuf;
+#pragma unroll
+    for (int j = 0; j < kTWPer; ++j)
+      __builtin_amdgcn_global_load_lds(wsrc[j] + (size_t)st * 2048,
+                                       (lds_void *)(b + wbase + j * kTThreads * 16), 16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < kTXPer; ++j)
+      __builtin_amdgcn_global_load_lds(p.x + xoff[j] + st * 64,
+                                       (lds_void *)(b + kTWBytes + wbase + j * kTThreads * 16), 16, 0, 0);
+  };
+
+  const int ns = p.ksteps;
+  issue(0, 0);
+  if (ns > 1) issue(1, 1);
+  for (int st = 0; st < ns; ++st) {
+    // this wave's loads of step st are done once at most the next step's remain
+    if (st + 1 < ns)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (kTWPer + kTXPer));  // vmcnt(6)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);                      // vmcnt(0)
+    ring_barrier();  // everyone's step st is in LDS; everyone is done with step st - 1
+    if (st + 2 < ns) issue(st + 2, (st + 2) % kTStages);
+    const unsigned char *bw = lds + (st % kTStages) * kTBuf;
     const unsigned char *bx = bw + kTWBytes;
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
@@ -629,22 +650,20 @@ __global__ __launch_bounds__(kTThreads, 1) void gemm_tiled_kernel(GemmParams p) 
 #pragma unroll
       for (int gi = 0; gi < 2; ++gi)
 #pragma unroll
-        for (int a = 0; a < 2; ++a) {
-          const int q = (2 * gp + gi) * 2 + a;
-          wv[gi][a] = as_bf16x8(*reinterpret_cast<const uint4 *>(bw + ((q * 2 + m) * 64 + lane) * 16));
-        }
+        for (int a = 0; a < 2; ++a)
+          wv[gi][a] = as_bf16x8(*reinterpret_cast<const uint4 *>(
+              bw + ((((2 * gp + gi) * 2 + a) * 2 + m) * 64 + lane) * 16));
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
+        const int r = th * 64 + tt * 16 + l16;
         const bf16x8 xv = as_bf16x8(*reinterpret_cast<const uint4 *>(
-            bx + (th * 64 + tt * 16 + l16) * kTXStride + (32 * m + 8 * gq) * 2));
+            bx + r * 128 + (((4 * m + gq) ^ (r & 7)) * 16)));
 #pragma unroll
         for (int gi = 0; gi < 2; ++gi)
 #pragma unroll
           for (int a = 0; a < 2; ++a) acc[gi][a][tt] = mfma16x16x32(wv[gi][a], xv, acc[gi][a][tt]);
       }
     }
-    if (st + 1 < p.ksteps) SV_TILED_STASH(buf ^ 1);
-    __syncthreads();
   }
 
 #pragma unroll
@@ -653,8 +672,6 @@ __global__ __launch_bounds__(kTThreads, 1) void gemm_tiled_kernel(GemmParams p) 
     if (grp < p.nblk) epilogue<4, EPI>(p, acc[gi], grp, tb * kTTok + th * 64, gq, l16);
   }
 }
-#undef SV_TILED_FETCH
-#undef SV_TILED_STASH
 
 // Grid of the tiled kernel: row blocks x token blocks.
 inline int tiled_grid(const GemmParams &p) {
