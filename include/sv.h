@@ -159,17 +159,20 @@ typedef struct sv_batch {
   int32_t *err_flag;         /* [1] nullable */
 } sv_batch;
 
-/* Packed weight layout.  The weight GEMMs read each 16-row block of a matrix
- * as one sequential stream when it is stored fragment by fragment:
- *   bf16: for tile t (rows 16t..16t+15), step s (k = 64s..64s+63), half m,
- *         lane l (row 16t + l%16), the 8 values k = 64s + 32m + 8(l/16) + 0..7
- *         are stored at element ((t * K/64 + s) * 2 + m) * 512 + l * 8;
- *   int4: for tile t, step s (k = 128s..128s+127), lane l, the 32 codes
- *         k = 128s + 32(l/16) + 0..31 of row 16t + l%16 (four packed words)
- *         are stored at word ((t * K/128 + s) * 64 + l) * 4, and their group
- *         scale at element (t * K/128 + s) * 64 + l of the scale array.
- * Rows past N in the last tile are zero.  Packing is a one-time layout change
- * (done when weights are loaded), not part of a verification pass. */
+/* Packed weight layout.  The weight GEMMs read each 32-row group of a matrix
+ * as one sequential stream when it is stored fragment by fragment, the group's
+ * two 16-row tiles a = 0, 1 back to back for each K step:
+ *   bf16: for group g (rows 32g..32g+31), step s (k = 64s..64s+63), tile a,
+ *         half m, lane l (row 32g + 16a + l%16), the 8 values
+ *         k = 64s + 32m + 8(l/16) + 0..7 are stored at element
+ *         (((g * K/64 + s) * 2 + a) * 2 + m) * 512 + l * 8;
+ *   int4: for group g, step s (k = 128s..128s+127), tile a, lane l, the 32
+ *         codes k = 128s + 32(l/16) + 0..31 of row 32g + 16a + l%16 (four
+ *         packed words) are stored at word (((g * K/128 + s) * 2 + a) * 64 + l) * 4,
+ *         and their group scale at element ((g * K/128 + s) * 2 + a) * 64 + l
+ *         of the scale array.
+ * Rows past N in the last group are zero.  Packing is a one-time layout
+ * change (done when weights are loaded), not part of a verification pass. */
 sv_status sv_packed_matrix_bytes(int32_t wtype, int32_t N, int32_t K, size_t *w_bytes,
                                  size_t *scale_bytes);
 

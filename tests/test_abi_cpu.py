@@ -197,8 +197,8 @@ def test_plan_rejects_bad_params():
 
 
 def test_packed_sizes_and_validation():
-    assert sv.sv_packed_matrix_bytes(sv.SV_W_BF16, 100, 256) == (112 * 256 * 2, 0)
-    assert sv.sv_packed_matrix_bytes(sv.SV_W_INT4_G32, 77, 384) == (80 * 384 // 2, 80 * 12 * 2)
+    assert sv.sv_packed_matrix_bytes(sv.SV_W_BF16, 100, 256) == (128 * 256 * 2, 0)
+    assert sv.sv_packed_matrix_bytes(sv.SV_W_INT4_G32, 77, 384) == (96 * 384 // 2, 96 * 12 * 2)
     with pytest.raises(sv.SvError):
         sv.sv_packed_matrix_bytes(sv.SV_W_F32, 16, 64)
     with pytest.raises(sv.SvError):

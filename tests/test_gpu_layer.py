@@ -142,20 +142,20 @@ def test_decoder_then_head_shared_workspace():
 def _pack_reference(m):
     """Expected packed bytes, by an independent numpy re-layout of [N][K]."""
     n, k = m.n, m.k
-    nt = (n + 15) // 16
+    ng = (n + 31) // 32
     if m.wtype == "bf16":
-        w = np.zeros((nt * 16, k), np.uint16)
+        w = np.zeros((ng * 32, k), np.uint16)
         w[:n] = m.data
-        ks = k // 64   # row 16t+l, k = 64s + 32m + 8g + e  ->  [t][s][m][g*16+l][e]
-        a = w.reshape(nt, 16, ks, 2, 4, 8).transpose(0, 2, 3, 4, 1, 5)
+        ks = k // 64   # row 32g+16a+l, k = 64s + 32m + 8q + e  ->  [g][s][a][m][q*16+l][e]
+        a = w.reshape(ng, 2, 16, ks, 2, 4, 8).transpose(0, 3, 1, 4, 5, 2, 6)
         return a.reshape(-1).view(np.uint8), None
-    w = np.zeros((nt * 16, k // 8), np.uint32)
+    w = np.zeros((ng * 32, k // 8), np.uint32)
     w[:n] = m.data
-    s = np.zeros((nt * 16, k // 32), np.uint16)
+    s = np.zeros((ng * 32, k // 32), np.uint16)
     s[:n] = m.scale
-    ks = k // 128  # word 16s + 4g + j of row 16t+l -> [t][s][g*16+l][j]
-    a = w.reshape(nt, 16, ks, 4, 4).transpose(0, 2, 3, 1, 4)
-    b = s.reshape(nt, 16, ks, 4).transpose(0, 2, 3, 1)
+    ks = k // 128  # word 16s + 4q + j of row 32g+16a+l -> [g][s][a][q*16+l][j]
+    a = w.reshape(ng, 2, 16, ks, 4, 4).transpose(0, 3, 1, 4, 2, 5)
+    b = s.reshape(ng, 2, 16, ks, 4).transpose(0, 3, 1, 4, 2)
     return a.reshape(-1).view(np.uint8), b.reshape(-1).view(np.uint8)
 
 

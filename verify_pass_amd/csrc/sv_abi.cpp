@@ -606,7 +606,7 @@ extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const
 extern "C" sv_status sv_packed_matrix_bytes(int32_t wtype, int32_t N, int32_t K, size_t *w_bytes,
                                             size_t *scale_bytes) {
   if (N <= 0 || K <= 0) return SV_ERR_INVALID_ARG;
-  const size_t rows = (size_t)(N + 15) / 16 * 16;
+  const size_t rows = (size_t)(N + 31) / 32 * 32;
   if (wtype == SV_W_BF16) {
     if (K % 64) return SV_ERR_UNSUPPORTED;
     if (w_bytes) *w_bytes = rows * K * 2;

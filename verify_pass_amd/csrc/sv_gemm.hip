@@ -53,16 +53,20 @@ hipError_t launch_gemm(const GemmParams &p, int wtype, int tok_tiles, int depth,
 
 namespace {
 // One thread per 16-byte fragment of the packed layout (see sv_pack_matrix).
+// Packed layout: rows in 32-row groups g, each K step of a group holding its
+// two 16-row tiles a back to back, each tile as lane-ordered 16-byte MFMA
+// fragments.  One thread per 16-byte fragment.
 __global__ __launch_bounds__(256) void pack_bf16_kernel(const uint16_t *src, uint4 *dst, int N, int K) {
   const int ks = K / 64;
-  const size_t total = (size_t)((N + 15) / 16) * ks * 128;
+  const size_t total = (size_t)((N + 31) / 32) * ks * 256;
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= total) return;
-  const int lane = idx & 63, m = (idx >> 6) & 1;
-  const size_t ts = idx >> 7;
-  const int step = (int)(ts % ks);
-  const size_t tile = ts / ks;
-  const size_t row = tile * 16 + (lane & 15);
+  // idx = (((g * ks + step) * 2 + a) * 2 + m) * 64 + lane
+  const int lane = idx & 63, m = (idx >> 6) & 1, a = (idx >> 7) & 1;
+  const size_t gs = idx >> 8;
+  const int step = (int)(gs % ks);
+  const size_t g = gs / ks;
+  const size_t row = g * 32 + a * 16 + (lane & 15);
   const int k = step * 64 + 32 * m + 8 * (lane >> 4);
   dst[idx] = row < (size_t)N ? *reinterpret_cast<const uint4 *>(src + row * K + k) : uint4{0u, 0u, 0u, 0u};
 }
@@ -70,14 +74,15 @@ __global__ __launch_bounds__(256) void pack_bf16_kernel(const uint16_t *src, uin
 __global__ __launch_bounds__(256) void pack_int4_kernel(const uint32_t *src, const uint16_t *ssrc, uint4 *dst,
                                                         uint16_t *sdst, int N, int K) {
   const int ks = K / 128;
-  const size_t total = (size_t)((N + 15) / 16) * ks * 64;
+  const size_t total = (size_t)((N + 31) / 32) * ks * 128;
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= total) return;
-  const int lane = idx & 63;
-  const size_t ts = idx >> 6;
-  const int step = (int)(ts % ks);
-  const size_t tile = ts / ks;
-  const size_t row = tile * 16 + (lane & 15);
+  // idx = ((g * ks + step) * 2 + a) * 64 + lane
+  const int lane = idx & 63, a = (idx >> 6) & 1;
+  const size_t gs = idx >> 7;
+  const int step = (int)(gs % ks);
+  const size_t g = gs / ks;
+  const size_t row = g * 32 + a * 16 + (lane & 15);
   const int gq = lane >> 4;
   if (row < (size_t)N) {
     dst[idx] = *reinterpret_cast<const uint4 *>(src + row * (K / 8) + step * 16 + 4 * gq);
@@ -91,13 +96,13 @@ __global__ __launch_bounds__(256) void pack_int4_kernel(const uint32_t *src, con
 
 hipError_t launch_pack(int wtype, int N, int K, const void *w, const void *scale, void *wp, void *sp,
                        hipStream_t s) {
-  const size_t tiles = (size_t)(N + 15) / 16;
+  const size_t groups = (size_t)(N + 31) / 32;
   if (wtype == WT_BF16) {
-    const size_t total = tiles * (K / 64) * 128;
+    const size_t total = groups * (K / 64) * 256;
     hipLaunchKernelGGL(pack_bf16_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
                        static_cast<const uint16_t *>(w), static_cast<uint4 *>(wp), N, K);
   } else {
-    const size_t total = tiles * (K / 128) * 64;
+    const size_t total = groups * (K / 128) * 128;
     hipLaunchKernelGGL(pack_int4_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
                        static_cast<const uint32_t *>(w), static_cast<const uint16_t *>(scale),
                        static_cast<uint4 *>(wp), static_cast<uint16_t *>(sp), N, K);

@@ -54,17 +54,19 @@ __device__ __forceinline__ WSrc<WT> make_src(const GemmMat &mat, int row, int ti
                                              int ksteps, int packed, int lane, int gq) {
   WSrc<WT> w;
   if (packed) {
-    const size_t tile = (size_t)(tile_row0 / 16);
+    // 32-row group g, tile a within it; a group's K step holds both tiles
+    const size_t g = (size_t)(tile_row0 / 32);
+    const int a = (tile_row0 / 16) & 1;
     if constexpr (WT == WT_INT4) {
-      w.p = static_cast<const unsigned char *>(mat.w) + (tile * ksteps * 64 + lane) * 16;
-      w.s = mat.s + tile * ksteps * 64 + lane;
-      w.step_bytes = 64 * 16;
-      w.s_step = 64;
+      w.p = static_cast<const unsigned char *>(mat.w) + ((g * ksteps * 2 + a) * 64 + lane) * 16;
+      w.s = mat.s + (g * ksteps * 2 + a) * 64 + lane;
+      w.step_bytes = 2 * 64 * 16;
+      w.s_step = 2 * 64;
       w.m_off = 0;
     } else {
-      w.p = static_cast<const unsigned char *>(mat.w) + (tile * ksteps * 128 + lane) * 16;
+      w.p = static_cast<const unsigned char *>(mat.w) + ((g * ksteps * 2 + a) * 128 + lane) * 16;
       w.s = nullptr;
-      w.step_bytes = 128 * 16;
+      w.step_bytes = 2 * 128 * 16;
       w.s_step = 0;
       w.m_off = 64 * 16;
     }
@@ -599,8 +601,9 @@ __global__ __launch_bounds__(kTThreads, 1) void gemm_tiled_kernel(GemmParams p) 
       mi = 0;
       pr0 = 0;
     }
-    const size_t tile = (size_t)(pr0 / 16);
-    wsrc[j] = static_cast<const unsigned char *>(p.mat[mi].w) + ((tile * p.ksteps * 2 + m) * 64 + fl) * 16;
+    const size_t g = (size_t)(pr0 / 32);
+    const int a = (pr0 / 16) & 1;
+    wsrc[j] = static_cast<const unsigned char *>(p.mat[mi].w) + (((g * p.ksteps * 2 + a) * 2 + m) * 64 + fl) * 16;
   }
 #pragma unroll
   for (int j = 0; j < kTXPer; ++j) {
@@ -623,7 +626,7 @@ __global__ __launch_bounds__(kTThreads, 1) void gemm_tiled_kernel(GemmParams p) 
     unsigned char *b = lds + buf * kTBuf;
 #pragma unroll
     for (int j = 0; j < kTWPer; ++j)
-      __builtin_amdgcn_global_load_lds(wsrc[j] + (size_t)st * 2048,
+      __builtin_amdgcn_global_load_lds(wsrc[j] + (size_t)st * 4096,
                                        (lds_void *)(b + wbase + j * kTThreads * 16), 16, 0, 0);
 #pragma unroll
     for (int j = 0; j < kTXPer; ++j)
