@@ -159,18 +159,19 @@ typedef struct sv_batch {
   int32_t *err_flag;         /* [1] nullable */
 } sv_batch;
 
-/* Packed weight layout.  The weight GEMMs read each 32-row group of a matrix
- * as one sequential stream when it is stored fragment by fragment, the group's
- * two 16-row tiles a = 0, 1 back to back for each K step:
- *   bf16: for group g (rows 32g..32g+31), step s (k = 64s..64s+63), tile a,
- *         half m, lane l (row 32g + 16a + l%16), the 8 values
- *         k = 64s + 32m + 8(l/16) + 0..7 are stored at element
- *         (((g * K/64 + s) * 2 + a) * 2 + m) * 512 + l * 8;
- *   int4: for group g, step s (k = 128s..128s+127), tile a, lane l, the 32
+/* Packed weight layout.  Rows are taken in 32-row groups g (G = ceil(N/32)
+ * groups), each made of two 16-row tiles a = 0, 1, stored step-major: for K
+ * step s, group 0's fragments, then group 1's, ..., then step s + 1.  A GEMM
+ * unit of 32 rows reads one contiguous run per K step, and units working on
+ * the same step read neighbouring memory:
+ *   bf16: for step s (k = 64s..64s+63), group g, tile a, half m, lane l
+ *         (row 32g + 16a + l%16), the 8 values k = 64s + 32m + 8(l/16) + 0..7
+ *         are stored at element (((s * G + g) * 2 + a) * 2 + m) * 512 + l * 8;
+ *   int4: for step s (k = 128s..128s+127), group g, tile a, lane l, the 32
  *         codes k = 128s + 32(l/16) + 0..31 of row 32g + 16a + l%16 (four
- *         packed words) are stored at word (((g * K/128 + s) * 2 + a) * 64 + l) * 4,
- *         and their group scale at element ((g * K/128 + s) * 2 + a) * 64 + l
- *         of the scale array.
+ *         packed words) are stored at word (((s * G + g) * 2 + a) * 64 + l) * 4,
+ *         and their group scale at element ((s * G + g) * 2 + a) * 64 + l of
+ *         the scale array.
  * Rows past N in the last group are zero.  Packing is a one-time layout
  * change (done when weights are loaded), not part of a verification pass. */
 sv_status sv_packed_matrix_bytes(int32_t wtype, int32_t N, int32_t K, size_t *w_bytes,

@@ -146,16 +146,16 @@ def _pack_reference(m):
     if m.wtype == "bf16":
         w = np.zeros((ng * 32, k), np.uint16)
         w[:n] = m.data
-        ks = k // 64   # row 32g+16a+l, k = 64s + 32m + 8q + e  ->  [g][s][a][m][q*16+l][e]
-        a = w.reshape(ng, 2, 16, ks, 2, 4, 8).transpose(0, 3, 1, 4, 5, 2, 6)
+        ks = k // 64   # row 32g+16a+l, k = 64s + 32m + 8q + e  ->  [s][g][a][m][q*16+l][e]
+        a = w.reshape(ng, 2, 16, ks, 2, 4, 8).transpose(3, 0, 1, 4, 5, 2, 6)
         return a.reshape(-1).view(np.uint8), None
     w = np.zeros((ng * 32, k // 8), np.uint32)
     w[:n] = m.data
     s = np.zeros((ng * 32, k // 32), np.uint16)
     s[:n] = m.scale
-    ks = k // 128  # word 16s + 4q + j of row 32g+16a+l -> [g][s][a][q*16+l][j]
-    a = w.reshape(ng, 2, 16, ks, 4, 4).transpose(0, 3, 1, 4, 2, 5)
-    b = s.reshape(ng, 2, 16, ks, 4).transpose(0, 3, 1, 4, 2)
+    ks = k // 128  # word 16s + 4q + j of row 32g+16a+l -> [s][g][a][q*16+l][j]
+    a = w.reshape(ng, 2, 16, ks, 4, 4).transpose(3, 0, 1, 4, 2, 5)
+    b = s.reshape(ng, 2, 16, ks, 4).transpose(3, 0, 1, 4, 2)
     return a.reshape(-1).view(np.uint8), b.reshape(-1).view(np.uint8)
 
 

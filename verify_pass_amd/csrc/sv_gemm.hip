@@ -53,19 +53,20 @@ hipError_t launch_gemm(const GemmParams &p, int wtype, int tok_tiles, int depth,
 
 namespace {
 // One thread per 16-byte fragment of the packed layout (see sv_pack_matrix).
-// Packed layout: rows in 32-row groups g, each K step of a group holding its
-// two 16-row tiles a back to back, each tile as lane-ordered 16-byte MFMA
-// fragments.  One thread per 16-byte fragment.
+// Packed layout: step-major -- K step s of every 32-row group g in turn,
+// each holding the group's two 16-row tiles a back to back, each tile as
+// lane-ordered 16-byte MFMA fragments.  One thread per 16-byte fragment.
 __global__ __launch_bounds__(256) void pack_bf16_kernel(const uint16_t *src, uint4 *dst, int N, int K) {
   const int ks = K / 64;
-  const size_t total = (size_t)((N + 31) / 32) * ks * 256;
+  const size_t ng = (size_t)(N + 31) / 32;
+  const size_t total = ng * ks * 256;
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= total) return;
-  // idx = (((g * ks + step) * 2 + a) * 2 + m) * 64 + lane
+  // idx = (((step * ng + g) * 2 + a) * 2 + m) * 64 + lane
   const int lane = idx & 63, m = (idx >> 6) & 1, a = (idx >> 7) & 1;
-  const size_t gs = idx >> 8;
-  const int step = (int)(gs % ks);
-  const size_t g = gs / ks;
+  const size_t sg = idx >> 8;
+  const size_t g = sg % ng;
+  const int step = (int)(sg / ng);
   const size_t row = g * 32 + a * 16 + (lane & 15);
   const int k = step * 64 + 32 * m + 8 * (lane >> 4);
   dst[idx] = row < (size_t)N ? *reinterpret_cast<const uint4 *>(src + row * K + k) : uint4{0u, 0u, 0u, 0u};
@@ -74,14 +75,15 @@ __global__ __launch_bounds__(256) void pack_bf16_kernel(const uint16_t *src, uin
 __global__ __launch_bounds__(256) void pack_int4_kernel(const uint32_t *src, const uint16_t *ssrc, uint4 *dst,
                                                         uint16_t *sdst, int N, int K) {
   const int ks = K / 128;
-  const size_t total = (size_t)((N + 31) / 32) * ks * 128;
+  const size_t ng = (size_t)(N + 31) / 32;
+  const size_t total = ng * ks * 128;
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= total) return;
-  // idx = ((g * ks + step) * 2 + a) * 64 + lane
+  // idx = ((step * ng + g) * 2 + a) * 64 + lane
   const int lane = idx & 63, a = (idx >> 6) & 1;
-  const size_t gs = idx >> 7;
-  const int step = (int)(gs % ks);
-  const size_t g = gs / ks;
+  const size_t sg = idx >> 7;
+  const size_t g = sg % ng;
+  const int step = (int)(sg / ng);
   const size_t row = g * 32 + a * 16 + (lane & 15);
   const int gq = lane >> 4;
   if (row < (size_t)N) {

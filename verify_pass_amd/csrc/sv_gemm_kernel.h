@@ -54,19 +54,20 @@ __device__ __forceinline__ WSrc<WT> make_src(const GemmMat &mat, int row, int ti
                                              int ksteps, int packed, int lane, int gq) {
   WSrc<WT> w;
   if (packed) {
-    // 32-row group g, tile a within it; a group's K step holds both tiles
+    // step-major: K step s of 32-row group g at (s * ng + g); tile a within it
     const size_t g = (size_t)(tile_row0 / 32);
+    const int ng = (mat.rows + 31) / 32;
     const int a = (tile_row0 / 16) & 1;
     if constexpr (WT == WT_INT4) {
-      w.p = static_cast<const unsigned char *>(mat.w) + ((g * ksteps * 2 + a) * 64 + lane) * 16;
-      w.s = mat.s + (g * ksteps * 2 + a) * 64 + lane;
-      w.step_bytes = 2 * 64 * 16;
-      w.s_step = 2 * 64;
+      w.p = static_cast<const unsigned char *>(mat.w) + ((g * 2 + a) * 64 + lane) * 16;
+      w.s = mat.s + (g * 2 + a) * 64 + lane;
+      w.step_bytes = ng * 2 * 64 * 16;
+      w.s_step = ng * 2 * 64;
       w.m_off = 0;
     } else {
-      w.p = static_cast<const unsigned char *>(mat.w) + ((g * ksteps * 2 + a) * 128 + lane) * 16;
+      w.p = static_cast<const unsigned char *>(mat.w) + ((g * 2 + a) * 128 + lane) * 16;
       w.s = nullptr;
-      w.step_bytes = 2 * 128 * 16;
+      w.step_bytes = ng * 2 * 128 * 16;
       w.s_step = 0;
       w.m_off = 64 * 16;
     }
@@ -591,6 +592,7 @@ __global__ __launch_bounds__(kTThreads, 1) void gemm_tiled_kernel(GemmParams p) 
   //  weights: fragment f = (tile f/128, half (f/64)%2, lane f%64) of the packed layout
   //  tokens:  row f/8, slot f%8 holding chunk (f%8) ^ (row%8) of the row's 64 values
   const unsigned char *wsrc[kTWPer];
+  size_t wstep[kTWPer];   // bytes between K steps of the fragment's matrix (step-major)
   uint32_t xoff[kTXPer];  // element offsets of this thread's token chunks (step 0)
 #pragma unroll
   for (int j = 0; j < kTWPer; ++j) {
@@ -603,7 +605,8 @@ __global__ __launch_bounds__(kTThreads, 1) void gemm_tiled_kernel(GemmParams p) 
     }
     const size_t g = (size_t)(pr0 / 32);
     const int a = (pr0 / 16) & 1;
-    wsrc[j] = static_cast<const unsigned char *>(p.mat[mi].w) + (((g * p.ksteps * 2 + a) * 2 + m) * 64 + fl) * 16;
+    wsrc[j] = static_cast<const unsigned char *>(p.mat[mi].w) + (((g * 2 + a) * 2 + m) * 64 + fl) * 16;
+    wstep[j] = (size_t)((p.mat[mi].rows + 31) / 32) * 4096;
   }
 #pragma unroll
   for (int j = 0; j < kTXPer; ++j) {
@@ -626,7 +629,7 @@ __global__ __launch_bounds__(kTThreads, 1) void gemm_tiled_kernel(GemmParams p) 
     unsigned char *b = lds + buf * kTBuf;
 #pragma unroll
     for (int j = 0; j < kTWPer; ++j)
-      __builtin_amdgcn_global_load_lds(wsrc[j] + (size_t)st * 4096,
+      __builtin_amdgcn_global_load_lds(wsrc[j] + (size_t)st * wstep[j],
                                        (lds_void *)(b + wbase + j * kTThreads * 16), 16, 0, 0);
 #pragma unroll
     for (int j = 0; j < kTXPer; ++j)
