@@ -639,7 +639,7 @@ extern "C" sv_status sv_pack_matrix(int32_t wtype, int32_t N, int32_t K, const v
 // ---------------------------------------------------------------------------
 // Acceptance.
 namespace {
-constexpr int kAcceptChunk = 8192;
+constexpr int kAcceptChunk = 4096;
 
 struct AcceptPlan {
   long long T = 0, nd = 0;
@@ -720,6 +720,15 @@ extern "C" sv_status sv_accept_commit(int32_t B, int32_t V, int32_t mode, const 
   a.parts = reinterpret_cast<AcceptPart *>(ws + ap.off_parts);
   a.acc_ws = reinterpret_cast<int *>(ws + ap.off_acc);
   a.counters = reinterpret_cast<int *>(ws);
+  if (B <= kAcceptHostMax) {
+    a.host_map = 1;
+    int qs = 0;
+    for (int i = 0; i < B; ++i) {
+      a.hq_start[i] = qs;
+      a.hgamma[i] = gamma_host[i];
+      qs += gamma_host[i] + 1;
+    }
+  }
   (void)hipGetLastError();
   const hipError_t e = launch_accept(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SV_OK : SV_ERR_HIP;

@@ -182,8 +182,8 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(AcceptParams p) {
   const int tid = threadIdx.x, c = blockIdx.x, i = blockIdx.y;
   const int x0 = c * p.chunk, x1 = min(p.V, x0 + p.chunk);
   const bool vec = (p.V & 3) == 0;
-  const int g = p.gamma[i];
-  const int qst = seq_start(p.gamma, i, sh), dst = qst - i;
+  const int g = p.host_map ? p.hgamma[i] : p.gamma[i];
+  const int qst = p.host_map ? p.hq_start[i] : seq_start(p.gamma, i, sh), dst = qst - i;
 
   if (tid == 0) {
     sh.first_fail = g;
@@ -295,13 +295,19 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(AcceptParams p) {
     return;
   }
 
-  // totals over the chunks
+  // totals over the chunks (chunk results staged in LDS once when they fit)
   const AcceptPart *pp = p.parts + (size_t)i * p.nchunk;
+  __shared__ AcceptPart cpart[kThreads];
+  const bool staged = p.nchunk <= kThreads;
+  if (staged) {
+    if (tid < p.nchunk) cpart[tid] = get_part(pp + tid);
+    __syncthreads();
+  }
   u64 s_res = 0, s_p = 0;
   float mv = -INFINITY;
   int mi = 0x7fffffff;
   for (int cc = tid; cc < p.nchunk; cc += kThreads) {
-    const AcceptPart q = get_part(pp + cc);
+    const AcceptPart q = staged ? cpart[cc] : get_part(pp + cc);
     s_res += q.sum_res;
     s_p += q.sum_p;
     amax(mv, mi, q.max_p, q.arg_p);
@@ -326,7 +332,7 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(AcceptParams p) {
       const int cc = base + tid;
       u64 v = 0;
       if (cc < p.nchunk) {
-        const AcceptPart q = get_part(pp + cc);
+        const AcceptPart q = staged ? cpart[cc] : get_part(pp + cc);
         v = ur ? q.sum_res : q.sum_p;
       }
       u64 tot;
@@ -340,21 +346,44 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(AcceptParams p) {
       __syncthreads();
       if (sh.found) break;
     }
-    // exact scan of that chunk: each thread a contiguous segment
+    // exact scan of that chunk: each thread a contiguous segment of `per`
+    // elements (16-byte loads when rows are 16-byte aligned)
     const int cx0 = sh.chunk_hit * p.chunk, cx1 = min(p.V, cx0 + p.chunk);
     const int n = cx1 - cx0;
     const bool resid = ur == 1 && a < g;
-    const int per = (n + kThreads - 1) / kThreads;  // <= kSegMax
+    int per = (n + kThreads - 1) / kThreads;  // <= kSegMax
+    if (vec) per = (per + 3) & ~3;             // whole float4s (n is a multiple of 4)
     const int lo = min(n, tid * per), hi = min(n, lo + per);
     float wv[kSegMax];
     u64 s = 0;
+    if (vec) {
+      const float4 *p4 = reinterpret_cast<const float4 *>(prow + cx0 + lo);
+      const float4 *q4 = reinterpret_cast<const float4 *>(resid ? qrow + cx0 + lo : prow);
+      const int n4 = (hi - lo) / 4;  // hi - lo is a multiple of 4 (n % 4 == 0 here)
+      float4 pv[kSegMax / 4], qv[kSegMax / 4];
 #pragma unroll
-    for (int k = 0; k < kSegMax; ++k) {
-      const int x = lo + k;
-      float r = 0.f;
-      if (x < hi) r = resid ? prow[cx0 + x] - qrow[cx0 + x] : prow[cx0 + x];
-      wv[k] = r;
-      s += weight_of(r);
+      for (int k = 0; k < kSegMax / 4; ++k) {
+        pv[k] = k < n4 ? p4[k] : make_float4(0.f, 0.f, 0.f, 0.f);
+        qv[k] = (resid && k < n4) ? q4[k] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int k = 0; k < kSegMax / 4; ++k) {
+        wv[4 * k] = pv[k].x - qv[k].x;
+        wv[4 * k + 1] = pv[k].y - qv[k].y;
+        wv[4 * k + 2] = pv[k].z - qv[k].z;
+        wv[4 * k + 3] = pv[k].w - qv[k].w;
+      }
+#pragma unroll
+      for (int k = 0; k < kSegMax; ++k) s += weight_of(wv[k]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < kSegMax; ++k) {
+        const int x = lo + k;
+        float r = 0.f;
+        if (x < hi) r = resid ? prow[cx0 + x] - qrow[cx0 + x] : prow[cx0 + x];
+        wv[k] = r;
+        s += weight_of(r);
+      }
     }
     u64 tot;
     const u64 before = block_exscan(s, &tot, sh);

@@ -40,33 +40,38 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4 &v) {
 // Block-level helpers (blockDim.x == 256).
 
 // In-place exclusive prefix sum of n (<= 65536) ints in LDS; returns the total.
-// tmp: 257 ints of LDS.  Deterministic (fixed association order).
+// tmp: 257 ints of LDS (the first 4 are used).  Each thread sums a contiguous
+// segment; the segment sums are scanned with wave shuffles and the four wave
+// totals added in wave order.  Deterministic (integer sums).
 __device__ inline int block_exscan(int *vals, int n, int *tmp) {
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int per = (n + 255) / 256;
   const int lo = min(n, tid * per), hi = min(n, lo + per);
   int s = 0;
   for (int i = lo; i < hi; ++i) s += vals[i];
-  tmp[tid] = s;
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int i = 0; i < 256; ++i) {
-      const int v = tmp[i];
-      tmp[i] = run;
-      run += v;
-    }
-    tmp[256] = run;
+  int inc = s;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(inc, o);
+    if (lane >= o) inc += y;
   }
+  if (lane == 63) tmp[w] = inc;
   __syncthreads();
-  int run = tmp[tid];
+  int before = 0, total = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int v = tmp[k];
+    if (k < w) before += v;
+    total += v;
+  }
+  int run = before + inc - s;
   for (int i = lo; i < hi; ++i) {
     const int v = vals[i];
     vals[i] = run;
     run += v;
   }
   __syncthreads();
-  return tmp[256];
+  return total;
 }
 
 // Largest i in [0, n) with starts[i] <= x (starts ascending, starts[0] <= x).
@@ -192,6 +197,8 @@ struct AcceptPart {
   int arg_p;
 };
 
+constexpr int kAcceptHostMax = 256;  // batches up to this size get the token map with the launch
+
 struct AcceptParams {
   int B, V, T, nd, mode;
   int chunk, nchunk;
@@ -208,6 +215,11 @@ struct AcceptParams {
   AcceptPart *parts;   // stochastic: [B][nchunk]; greedy: [T][nchunk]
   int *acc_ws;         // [B + T] ints of spill space (greedy rows past the LDS table)
   int *counters;       // [B] arrival counters, zero between calls
+  // small batches: the token map from the host's draft counts, passed with the
+  // launch (no device pass over gamma before the first load)
+  int host_map;                        // 1 when the two arrays below are filled
+  int hq_start[kAcceptHostMax];        // q_start[i]
+  int hgamma[kAcceptHostMax];          // gamma_i
 };
 
 // ---------------------------------------------------------------------------
