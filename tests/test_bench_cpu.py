@@ -1,0 +1,29 @@
+"""Host-side pieces of bench.py: the oracle baseline on a bounded sample and
+the step-model fit (no GPU)."""
+import numpy as np
+
+import bench
+from workloads import accept_inputs, head_weights, hidden_states, kv_cache, layer_weights, workload
+
+
+def test_cpu_baseline_runs_whole_steps():
+    wl = workload(1)
+    sh = wl.shape
+    W = layer_weights(sh, wl.wtype, wl.seed)
+    Wlm = head_weights(sh, wl.wtype, wl.seed)
+    kc, vc = kv_cache(sh, wl.ctx, wl.cap, wl.seed)
+    xh = hidden_states(wl.T, sh.d, wl.seed)
+    acc_in = accept_inputs(wl, sh.vocab)
+    r = bench.cpu_baseline(wl, W, Wlm, kc, vc, xh, acc_in, min_seconds=0.0, max_reps=2)
+    assert r["kind"] == "oracle" and r["unit"] == "verify tokens/s"
+    assert r["value"] > 0 and r["cores"] >= 1
+    assert r["sample"].startswith(f"1 whole verify step(s) of the workload ({wl.T} verify tokens)")
+
+
+def test_step_model_fit_recovers_constants():
+    tw, k, c, n = 100e-6, 0.5e-6, 4e-6, 3
+    bs = np.array([1, 2, 4, 8, 16, 32, 64, 128, 256])
+    ts = np.maximum(tw + k * bs, c * bs * n)
+    ftw, fk, fc = bench.fit_step_model(bs, ts, n)
+    assert abs(ftw - tw) / tw < 1e-3 and abs(fc - c) / c < 1e-3
+    assert abs(fk - k) / k < 5e-2
