@@ -144,7 +144,9 @@ typedef struct sv_layer {
  * at ((h * kv_cap/32 + p/32) * hd + c) * 32 + p % 32: one head's values for
  * 32 consecutive positions form one contiguous [hd][32] block).  Entries at
  * positions < kv_len[i] are read; the pass writes positions kv_len[i] ..
- * kv_len[i] + gamma_i.  kv_cap is a multiple of 32. */
+ * kv_len[i] + gamma_i.  kv_cap is a multiple of 32; every cache base is
+ * 16-byte aligned (the kernels read and write them with 8- and 16-byte
+ * accesses). */
 typedef struct sv_batch {
   int32_t B;                 /* sequences, >= 0 */
   int32_t T;                 /* stacked tokens = sum(gamma_i + 1) */

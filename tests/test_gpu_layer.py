@@ -325,11 +325,14 @@ def test_kv_overflow_flagged_and_contained():
     np.testing.assert_array_equal(dec.batch.k_logical(1)[:, :222], sentinel_before[1][:, :222])
 
 
-@pytest.mark.parametrize("tiling", [None, "qkv:1:2:0,o:1:2:0,gu:1:2:0,down:1:2:0,head:1:2:0"])
+@pytest.mark.parametrize("tiling", [None, "qkv:1:2:0,o:1:2:0,gu:1:2:0,down:1:2:0,head:1:2:0",
+                                    "qkv:2:2:1,o:1:4:1,gu:1:2:1,down:3:4:1,head:2:2:1"])
 def test_many_tokens_layer_and_head(tiling):
     """300 stacked tokens (three 128-token blocks of the tiled kernel with a
     ragged tail): decoder layer and head against the oracle, with the default
-    policy (tiled where it has enough workgroups) and with every GEMM tiled."""
+    policy (tiled where it has enough workgroups), with every GEMM tiled, and
+    with every GEMM streamed one wave per unit (five token blocks, K splits,
+    workgroups sharing the token operand)."""
     shape = Shape(2048, 16, 4, 128, 8192, 20011)
     gamma = [14] * 18 + [11, 12, 4]                  # 18*15 + 12 + 13 + 5 = 300 tokens
     ctx = [int(c) for c in np.linspace(0, 300, len(gamma)).astype(int)]

@@ -18,6 +18,23 @@ template <> struct WStep<WT_INT4> { uint4 v; uint32_t s; };
 
 template <int WT> constexpr int kstep() { return WT == WT_INT4 ? 128 : 64; }
 
+// One-wave-per-unit launches share the token operand of a K step among the
+// workgroup's units through LDS: xfrags 16-byte fragments per lane and token
+// tile (the XStep payload), in a ring of two groups of G steps.
+template <int WT> constexpr int xfrags() { return WT == WT_INT4 ? 4 : 2; }
+template <int WT, int TT, int G> constexpr int xl_bytes() { return 2 * G * TT * xfrags<WT>() * 1024; }
+constexpr int kXlMax = 64 * 1024;
+// Element offset of fragment m of lane group gq inside a token row's K step.
+template <int WT> __device__ __forceinline__ int xoff(int m, int gq) {
+  return WT == WT_BF16 ? 32 * m + 8 * gq : WT == WT_INT4 ? 32 * gq + 8 * m : 16 * gq + 8 * m;
+}
+typedef __attribute__((address_space(3))) void lds_void;
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
+// at lds + 16 l (lds wave-uniform).
+__device__ __forceinline__ void load_lds16(const void *g, void *lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void *)lds, 16, 0, 0);
+}
+
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // Streaming (non-temporal) 16-byte load: weights are read once per pass and
 // should not evict the token operand from L2.
@@ -162,6 +179,28 @@ __device__ __forceinline__ void split8(const uint4 &a, const uint4 &b, bf16x8 &h
   lo = as_bf16x8(uint4{l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16)});
 }
 
+// One K step of one 16-row tile times one token fragment.
+template <int WT>
+__device__ __forceinline__ void mma_tile(const WStep<WT> &w, const XStep<WT> &x, floatx4 &acc) {
+  if constexpr (WT == WT_BF16) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) acc = mfma16x16x32(as_bf16x8(w.v[m]), as_bf16x8(x.v[m]), acc);
+  } else if constexpr (WT == WT_INT4) {
+    const float s = bf2f(static_cast<uint16_t>(w.s));
+    const uint32_t wv[4] = {w.v.x, w.v.y, w.v.z, w.v.w};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc = mfma16x16x32(dequant8(wv[m], s), as_bf16x8(x.v[m]), acc);
+  } else {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      bf16x8 hi, lo;
+      split8(w.v[2 * m], w.v[2 * m + 1], hi, lo);
+      acc = mfma16x16x32(hi, as_bf16x8(x.v[m]), acc);
+      acc = mfma16x16x32(lo, as_bf16x8(x.v[m]), acc);
+    }
+  }
+}
+
 // Physical (matrix, row) of row r of tile `tile` in 32-row group g.
 // Returns false past the end of the matrix (the lane then streams row 0 and
 // its results are dropped).
@@ -209,6 +248,13 @@ __device__ __forceinline__ float load_dev(const float *p) {
 // wait until this wave's outstanding vector memory operations have completed
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Four consecutive bf16 as one 8-byte access (the lane's four rows 4gq..4gq+3
+// of a tile are consecutive output columns).
+__device__ __forceinline__ void st_bf16x4(uint16_t *o, const float (&v)[4]) {
+  *reinterpret_cast<uint2 *>(o) = make_uint2(f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16),
+                                             f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16));
+}
+
 // RMSNorm scale of the unit's tokens and the fused epilogue of one 32-row
 // group: acc[a][tt] holds rows (group grp, tile a, 4*gq + i) x token
 // t0 + 16*tt + l16 of this lane.
@@ -238,25 +284,44 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, floatx4 (&acc)[2][
   }
 
   // ---- fused epilogues (lane-local) -----------------------------------------
+  // Each lane holds, per tile, four consecutive output columns (rows 4gq..4gq+3
+  // of the tile): written as one 8- or 16-byte access when the row stride keeps
+  // them aligned and all four exist.
+  const bool vec = (p.ldo & 3) == 0;
   if constexpr (EPI == EPI_RESID) {
     uint16_t *out = static_cast<uint16_t *>(p.out);
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
       const int t = t0 + tt * 16 + l16;
       float sq = 0.f;  // this lane's share of the output row's sum of squares
+      if (t < p.T) {
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
+        for (int a = 0; a < 2; ++a) {
+          const int n0 = grp * 32 + a * 16 + 4 * gq;
+          const size_t o = (size_t)t * p.ldo + n0;
+          if (vec && n0 + 3 < p.N) {
+            const uint2 r = *reinterpret_cast<const uint2 *>(p.resid + o);
+            const float rv[4] = {bf2f(r.x & 0xFFFFu), bf2f(r.x >> 16), bf2f(r.y & 0xFFFFu), bf2f(r.y >> 16)};
+            float hv[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int n = grp * 32 + a * 16 + 4 * gq + i;
-          if (n < p.N && t < p.T) {
-            const size_t o = (size_t)t * p.ldo + n;
-            const uint16_t h = f2bf(acc[a][tt][i] * rs[tt] + bf2f(p.resid[o]));
-            out[o] = h;
-            const float f = bf2f(h);
-            sq += f * f;
+            for (int i = 0; i < 4; ++i) {
+              hv[i] = bf2f(f2bf(acc[a][tt][i] * rs[tt] + rv[i]));
+              sq += hv[i] * hv[i];
+            }
+            st_bf16x4(out + o, hv);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              if (n0 + i < p.N) {
+                const uint16_t h = f2bf(acc[a][tt][i] * rs[tt] + bf2f(p.resid[o + i]));
+                out[o + i] = h;
+                const float f = bf2f(h);
+                sq += f * f;
+              }
+            }
           }
         }
+      }
       if (p.sq_out) {
         sq += __shfl_xor(sq, 16);
         sq += __shfl_xor(sq, 32);
@@ -269,14 +334,21 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, floatx4 (&acc)[2][
     for (int tt = 0; tt < TT; ++tt) {
       const int t = t0 + tt * 16 + l16;
       if (t >= p.T) continue;
+      const int f0 = grp * 16 + 4 * gq;
+      float hv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int f = grp * 16 + 4 * gq + i;
-        if (f < p.mat[0].rows) {
-          const float g = acc[0][tt][i] * rs[tt], u = acc[1][tt][i] * rs[tt];
-          const float sig = 1.f / (1.f + __builtin_amdgcn_exp2f(-g * kLog2e));
-          out[(size_t)t * p.ldo + f] = f2bf(g * sig * u);
-        }
+        const float g = acc[0][tt][i] * rs[tt], u = acc[1][tt][i] * rs[tt];
+        const float sig = 1.f / (1.f + __builtin_amdgcn_exp2f(-g * kLog2e));
+        hv[i] = g * sig * u;
+      }
+      uint16_t *o = out + (size_t)t * p.ldo + f0;
+      if (vec && f0 + 3 < p.mat[0].rows) {
+        st_bf16x4(o, hv);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (f0 + i < p.mat[0].rows) o[i] = f2bf(hv[i]);
       }
     }
   } else if constexpr (EPI == EPI_LOGITS) {
@@ -287,14 +359,24 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, floatx4 (&acc)[2][
       float v[8];
       float m = -INFINITY;
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
+      for (int a = 0; a < 2; ++a) {
+        const int n0 = grp * 32 + a * 16 + 4 * gq;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int n = grp * 32 + a * 16 + 4 * gq + i;
-          v[a * 4 + i] = n < p.N ? acc[a][tt][i] * rs[tt] : -INFINITY;
+          v[a * 4 + i] = n0 + i < p.N ? acc[a][tt][i] * rs[tt] : -INFINITY;
           m = fmaxf(m, v[a * 4 + i]);
-          if (t < p.T && n < p.N) out[(size_t)t * p.ldo + n] = v[a * 4 + i];
         }
+        if (t < p.T) {
+          float *o = out + (size_t)t * p.ldo + n0;
+          if (vec && n0 + 3 < p.N) {
+            *reinterpret_cast<float4 *>(o) = make_float4(v[a * 4], v[a * 4 + 1], v[a * 4 + 2], v[a * 4 + 3]);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (n0 + i < p.N) o[i] = v[a * 4 + i];
+          }
+        }
+      }
       m = fmaxf(m, __shfl_xor(m, 16));
       m = fmaxf(m, __shfl_xor(m, 32));
       float s = 0.f;
@@ -337,18 +419,12 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, floatx4 (&acc)[2][
       const int fi0 = 16 * c + 4 * gq;
       if (head < p.hq) {
         uint16_t *q = p.qbuf + ((size_t)t * p.hq + head) * p.hd;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          q[fi0 + e] = f2bf(ra[e]);
-          q[fi0 + half + e] = f2bf(rb[e]);
-        }
+        st_bf16x4(q + fi0, ra);
+        st_bf16x4(q + fi0 + half, rb);
       } else if (head < p.hq + p.hkv) {
         uint16_t *k = static_cast<uint16_t *>(p.kc[seq]) + ((size_t)(head - p.hq) * p.kv_cap + pos) * p.hd;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          k[fi0 + e] = f2bf(ra[e]);
-          k[fi0 + half + e] = f2bf(rb[e]);
-        }
+        st_bf16x4(k + fi0, ra);
+        st_bf16x4(k + fi0 + half, rb);
       } else {
         // values in 32-position blocks: [n_kv][cap/32][hd][32]
         uint16_t *v = static_cast<uint16_t *>(p.vc[seq]) + (size_t)(head - p.hq - p.hkv) * p.hd * p.kv_cap +
@@ -366,50 +442,59 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, floatx4 (&acc)[2][
 // Waves per workgroup for KW waves per unit.
 template <int KW> constexpr int waves_per_wg() { return KW > 4 ? KW : 4; }
 
-// Resident workgroups per CU to aim for: the skinny bf16 shapes are latency
-// bound, so more resident waves (fewer registers each) keep more loads in flight.
-template <int WT, int TT, int G, int KW> constexpr int min_wg_per_cu() {
-  return (KW == 1 && WT == WT_BF16 && TT <= 2 && G <= 2) ? 8 : 1;
-}
-
 // G = K steps of weights and tokens in flight per wave: 2 for long streams
 // (many resident waves share the work), 4 or 8 for short ones (one or two
-// rounds of loads per wave).
+// rounds of loads per wave).  No occupancy hint: forcing 8 workgroups per CU
+// (64 registers) on the one-wave-per-unit streams spills and measured slower
+// than the 6 the register count gives.
 // KW = waves per unit: the unit's K range is cut into KW consecutive pieces,
 // one per wave of the same workgroup, and the pieces are added through LDS in
 // wave order (bitwise repeatable) before the epilogue, which the unit's first
 // wave runs.  This fills the chip for short row counts without sending
 // partial sums through memory.
 template <int WT, int TT, int EPI, int G, int KW>
-__global__ __launch_bounds__(64 * waves_per_wg<KW>(), (min_wg_per_cu<WT, TT, G, KW>())) void gemm_kernel(
-    GemmParams p) {
+__global__ __launch_bounds__(64 * waves_per_wg<KW>()) void gemm_kernel(GemmParams p) {
   constexpr int WV = waves_per_wg<KW>();
   constexpr int UPW = WV / KW;  // units per workgroup
   constexpr int NACC = 2 * TT * 4;
   __shared__ float kred[KW > 1 ? WV * NACC * 64 : 1];
+  __shared__ __align__(16) unsigned char xl[KW == 1 ? xl_bytes<WT, TT, G>() : 16];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = wave % KW, slot = wave / KW;
   const int gq = lane >> 4, l16 = lane & 15;
-  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  // KW == 1 keeps the dispatch order (measured faster for the long streams);
+  // split launches run a unit's neighbours on one XCD
+  const int wg = KW == 1 ? (int)blockIdx.x : xcd_remap(blockIdx.x, gridDim.x);
   const int ngrp = p.nblk;
-  const int nunits = ngrp * p.splits * p.ntblk;
-  const bool active = wg * UPW + slot < nunits;
-  if (KW == 1 && !active) return;
-  const int unit = min(wg * UPW + slot, nunits - 1);
-  // token block fastest: the units that share a row group's weights sit in
-  // the same and in neighbouring workgroups on one XCD, so only the first of
-  // them streams those weights from HBM and the others find them in L2
-  const int tb = unit % p.ntblk;
-  const int rest = unit / p.ntblk;
-  const int grp = rest % ngrp;
-  const int split = rest / ngrp;
+  int tb, grp, split;
+  bool active;
+  if constexpr (KW == 1) {
+    // the workgroup's units are UPW consecutive row groups of one token block
+    // and K split, so they share the token operand; token block fastest, so
+    // the workgroups that need the same weights run at the same time
+    const int nq = (ngrp + UPW - 1) / UPW;
+    tb = wg % p.ntblk;
+    const int rest = wg / p.ntblk;
+    split = rest / nq;
+    grp = (rest % nq) * UPW + slot;
+    active = grp < ngrp;
+    grp = min(grp, ngrp - 1);  // idle waves still load their share of the tokens
+  } else {
+    const int nunits = ngrp * p.splits * p.ntblk;
+    active = wg < nunits;
+    const int unit = min(wg, nunits - 1);
+    tb = unit % p.ntblk;
+    const int rest = unit / p.ntblk;
+    grp = rest % ngrp;
+    split = rest / ngrp;
+  }
   const int t0 = tb * TT * 16;
   const int u0 = (int)((long long)split * p.ksteps / p.splits);
   const int u1 = (int)((long long)(split + 1) * p.ksteps / p.splits);
-  // this wave's piece of the unit's K range
+  // this wave's piece of the unit's K range (all of it when KW == 1)
   const int s0 = u0 + (u1 - u0) * sub / KW;
-  const int nsteps = active ? u0 + (u1 - u0) * (sub + 1) / KW - s0 : 0;
+  const int nsteps = (active || KW == 1) ? u0 + (u1 - u0) * (sub + 1) / KW - s0 : 0;
 
   // weight stream of each of the unit's two tiles (rows past the end of a
   // matrix stream its first tile; their results are dropped)
@@ -436,43 +521,79 @@ __global__ __launch_bounds__(64 * waves_per_wg<KW>(), (min_wg_per_cu<WT, TT, G, 
   // Grouped prefetch: G steps of weights and tokens in flight per wave, then
   // compute.  A shallow group keeps the register count low, so many waves are
   // resident and together keep the memory system busy.
-  for (int base = 0; base < nsteps; base += G) {
-    WStep<WT> wbuf[G][2];
-    XStep<WT> xbuf[G][TT];
+  if constexpr (KW == 1) {
+    // token operand through LDS: each step's fragments are loaded once per
+    // workgroup (fragment f by wave f % WV, straight into LDS in lane order)
+    // and read by every unit; a ring of two groups lets the loads of group
+    // i + 1 start while slower waves still read group i
+    constexpr int NXF = xfrags<WT>();
+    constexpr int XF = TT * NXF;
+    constexpr int NL = (XF + WV - 1) / WV;  // fragments loaded per wave and step
+    constexpr int SLOT = G * XF * 1024;
+    constexpr int KS = kstep<WT>();
+    const int wv = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform, in a scalar register
+    const uint16_t *xa[NL];
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const int st = s0 + min(base + j, nsteps - 1);
-#pragma unroll
-      for (int tile = 0; tile < 2; ++tile) wbuf[j][tile] = load_w<WT>(src[tile], st);
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt) xbuf[j][tt] = load_x<WT>(xr[tt], st, gq);
+    for (int i = 0; i < NL; ++i) {
+      const int f = min(wv + WV * i, XF - 1);
+      const int tt = f / NXF, m = f - tt * NXF;
+      xa[i] = p.x + (size_t)min(t0 + tt * 16 + l16, p.T - 1) * p.K + xoff<WT>(m, gq);
     }
+    for (int base = 0, gi = 0; base < nsteps; base += G, ++gi) {
+      unsigned char *xs = xl + (gi & 1) * SLOT;
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-      if (base + j < nsteps) {
+      for (int j = 0; j < G; ++j) {
+        const int st = s0 + min(base + j, nsteps - 1);
 #pragma unroll
-        for (int tt = 0; tt < TT; ++tt) {
+        for (int i = 0; i < NL; ++i) {
+          const int f = wv + WV * i;
+          if (f < XF)
+            load_lds16(xa[i] + st * KS, xs + (j * XF + f) * 1024);
+        }
+      }
+      WStep<WT> wbuf[G][2];
 #pragma unroll
-          for (int tile = 0; tile < 2; ++tile) {
-            if constexpr (WT == WT_BF16) {
+      for (int j = 0; j < G; ++j) {
+        const int st = s0 + min(base + j, nsteps - 1);
 #pragma unroll
-              for (int m = 0; m < 2; ++m)
-                acc[tile][tt] = mfma16x16x32(as_bf16x8(wbuf[j][tile].v[m]), as_bf16x8(xbuf[j][tt].v[m]), acc[tile][tt]);
-            } else if constexpr (WT == WT_INT4) {
-              const float s = bf2f(static_cast<uint16_t>(wbuf[j][tile].s));
-              const uint32_t wv[4] = {wbuf[j][tile].v.x, wbuf[j][tile].v.y, wbuf[j][tile].v.z, wbuf[j][tile].v.w};
+        for (int tile = 0; tile < 2; ++tile) wbuf[j][tile] = load_w<WT>(src[tile], st);
+      }
+      wait_vmem();
+      __syncthreads();
 #pragma unroll
-              for (int m = 0; m < 4; ++m)
-                acc[tile][tt] = mfma16x16x32(dequant8(wv[m], s), as_bf16x8(xbuf[j][tt].v[m]), acc[tile][tt]);
-            } else {
+      for (int j = 0; j < G; ++j) {
+        if (base + j < nsteps) {
 #pragma unroll
-              for (int m = 0; m < 2; ++m) {
-                bf16x8 hi, lo;
-                split8(wbuf[j][tile].v[2 * m], wbuf[j][tile].v[2 * m + 1], hi, lo);
-                acc[tile][tt] = mfma16x16x32(hi, as_bf16x8(xbuf[j][tt].v[m]), acc[tile][tt]);
-                acc[tile][tt] = mfma16x16x32(lo, as_bf16x8(xbuf[j][tt].v[m]), acc[tile][tt]);
-              }
-            }
+          for (int tt = 0; tt < TT; ++tt) {
+            XStep<WT> xv;
+#pragma unroll
+            for (int m = 0; m < NXF; ++m) xv.v[m] = ld_v4(xs + ((j * XF + tt * NXF + m) * 64 + lane) * 16);
+            mma_tile<WT>(wbuf[j][0], xv, acc[0][tt]);
+            mma_tile<WT>(wbuf[j][1], xv, acc[1][tt]);
+          }
+        }
+      }
+    }
+    if (!active) return;
+  } else {
+    for (int base = 0; base < nsteps; base += G) {
+      WStep<WT> wbuf[G][2];
+      XStep<WT> xbuf[G][TT];
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        const int st = s0 + min(base + j, nsteps - 1);
+#pragma unroll
+        for (int tile = 0; tile < 2; ++tile) wbuf[j][tile] = load_w<WT>(src[tile], st);
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) xbuf[j][tt] = load_x<WT>(xr[tt], st, gq);
+      }
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        if (base + j < nsteps) {
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt) {
+            mma_tile<WT>(wbuf[j][0], xbuf[j][tt], acc[0][tt]);
+            mma_tile<WT>(wbuf[j][1], xbuf[j][tt], acc[1][tt]);
           }
         }
       }
@@ -564,8 +685,6 @@ constexpr int kTLds = kTStages * kTBuf;
 constexpr int kTWPer = kTWBytes / 16 / kTThreads;            // weight fragments loaded per thread (4)
 constexpr int kTXPer = kTXBytes / 16 / kTThreads;            // token chunks loaded per thread (2)
 
-typedef __attribute__((address_space(3))) void lds_void;
-
 // Workgroup barrier for the LDS ring: __syncthreads() would also wait for all
 // of this wave's outstanding global loads (its release fence covers the
 // direct-to-LDS loads), draining the prefetch.  The waits it needs are issued
@@ -629,12 +748,10 @@ __global__ __launch_bounds__(kTThreads, 1) void gemm_tiled_kernel(GemmParams p) 
     unsigned char *b = lds + buf * kTBuf;
 #pragma unroll
     for (int j = 0; j < kTWPer; ++j)
-      __builtin_amdgcn_global_load_lds(wsrc[j] + (size_t)st * wstep[j],
-                                       (lds_void *)(b + wbase + j * kTThreads * 16), 16, 0, 0);
+      load_lds16(wsrc[j] + (size_t)st * wstep[j], b + wbase + j * kTThreads * 16);
 #pragma unroll
     for (int j = 0; j < kTXPer; ++j)
-      __builtin_amdgcn_global_load_lds(p.x + xoff[j] + st * 64,
-                                       (lds_void *)(b + kTWBytes + wbase + j * kTThreads * 16), 16, 0, 0);
+      load_lds16(p.x + xoff[j] + st * 64, b + kTWBytes + wbase + j * kTThreads * 16);
   };
 
   const int ns = p.ksteps;
@@ -710,8 +827,9 @@ inline hipError_t launch_tiled(const GemmParams &p, hipStream_t s, int trace_cla
 template <int WT, int TT, int EPI, int G, int KW>
 hipError_t launch_g(const GemmParams &p, hipStream_t s, int trace_class) {
   constexpr int WV = waves_per_wg<KW>();
-  const int nunits = p.nblk * p.splits * p.ntblk;
-  const int nwg = (nunits + WV / KW - 1) / (WV / KW);
+  constexpr int UPW = WV / KW;
+  // KW == 1: UPW consecutive row groups per workgroup; else one unit each
+  const int nwg = ((p.nblk + UPW - 1) / UPW) * p.splits * p.ntblk;
   trace_before(trace_class, s);
   hipLaunchKernelGGL((gemm_kernel<WT, TT, EPI, G, KW>), dim3(nwg), dim3(64 * WV), 0, s, p);
   trace_after(trace_class, s);
@@ -723,13 +841,18 @@ hipError_t launch_g(const GemmParams &p, hipStream_t s, int trace_class) {
 // outside it takes the nearest smaller setting.
 template <int WT, int TT, int EPI, int KW>
 hipError_t launch_kw(const GemmParams &p, int depth, hipStream_t s, int trace_class) {
-  if constexpr (gemm_deep_ok(WT, TT, KW)) {
+  // KW == 1 also keeps its token ring within kXlMax bytes of LDS
+  if constexpr (gemm_deep_ok(WT, TT, KW) && (KW > 1 || xl_bytes<WT, TT, 8>() <= kXlMax)) {
     if (depth >= 8) return launch_g<WT, TT, EPI, 8, KW>(p, s, trace_class);
   }
   if constexpr (KW == 1) {
-    if (depth < 4) return launch_g<WT, TT, EPI, 2, KW>(p, s, trace_class);
+    if constexpr (xl_bytes<WT, TT, 4>() <= kXlMax) {
+      if (depth >= 4) return launch_g<WT, TT, EPI, 4, KW>(p, s, trace_class);
+    }
+    return launch_g<WT, TT, EPI, 2, KW>(p, s, trace_class);
+  } else {
+    return launch_g<WT, TT, EPI, 4, KW>(p, s, trace_class);
   }
-  return launch_g<WT, TT, EPI, 4, KW>(p, s, trace_class);
 }
 
 template <int WT, int TT, int EPI>
