@@ -20,6 +20,8 @@ CASES = [
     ("hd128-gqa5-bf16-rows48", Shape(640, 10, 2, 128, 1280, 2000), "bf16", [7, 1], [400, 2]),
     ("hd64-gqa2-bf16-tok>64", Shape(256, 4, 2, 64, 512, 1000), "bf16",
      [6, 0, 3, 9, 2, 4, 1, 8, 5, 7, 3, 0, 6, 2], list(range(10, 150, 10))),
+    # 8 query heads per KV head x 8 tokens: 64 query rows (four row tiles)
+    ("hd64-gqa8-bf16-rows64", Shape(256, 16, 2, 64, 512, 1000), "bf16", [7, 3, 0], [100, 31, 250]),
 ]
 
 

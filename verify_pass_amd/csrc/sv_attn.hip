@@ -77,6 +77,61 @@ __device__ __forceinline__ void load_values(uint4 (&v)[HD / 16], const uint16_t 
   for (int dt = 0; dt < HD / 16; ++dt) v[dt] = *reinterpret_cast<const uint4 *>(vb + (dt * 16 + l16) * 32);
 }
 
+// Count this chunk's arrival for (seq, KV head g); the last chunk to arrive
+// merges every chunk's (o, max, sum) by log-sum-exp and writes the output
+// rows.  Called by all threads once their partial stores are issued.
+// row_m, row_il: 64 floats of LDS each; flag: one int of LDS.
+template <int HD>
+__device__ void publish_merge(const AttnParams &p, const int *qs, int seq, int g, int R, int n1, int G,
+                              int *flag, float *row_m, float *row_il) {
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int *cs = qs + p.B + 1;
+  // chunks of this sequence that were launched (all of them unless the grid
+  // was sized for a smaller context, which is flagged by the caller)
+  const int first = cs[seq];
+  const int nch = min(cs[seq + 1], p.max_items) - first;
+  wait_vmem();
+  __syncthreads();
+  if (tid == 0) {
+    int *ctr = p.counters + (size_t)seq * p.hkv + g;
+    const int old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    flag[0] = old == nch - 1;
+    if (flag[0]) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!flag[0]) return;
+
+  // per row: overall max and 1 / sum over the chunks
+  for (int r = tid; r < R; r += nthr) {
+    float M = kNegBig;
+#pragma unroll 8
+    for (int cc = 0; cc < nch; ++cc)
+      M = fmaxf(M, load_dev(p.part_ml + ((((size_t)first + cc) * p.hkv + g) * p.rpad + r) * 2));
+    float lt = 0.f;
+#pragma unroll 8
+    for (int cc = 0; cc < nch; ++cc) {
+      const float *ml = p.part_ml + ((((size_t)first + cc) * p.hkv + g) * p.rpad + r) * 2;
+      lt += load_dev(ml + 1) * __builtin_amdgcn_exp2f(load_dev(ml) - M);
+    }
+    row_m[r] = M;
+    row_il[r] = lt > 0.f ? 1.f / lt : 0.f;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < R * HD; idx += nthr) {
+    const int r = idx / HD, d = idx - r * HD;
+    const float M = row_m[r];
+    float acc = 0.f;
+#pragma unroll 8
+    for (int cc = 0; cc < nch; ++cc) {
+      const size_t pr = (((size_t)first + cc) * p.hkv + g) * p.rpad + r;
+      acc += load_dev(p.part_o + pr * HD + d) * __builtin_amdgcn_exp2f(load_dev(p.part_ml + pr * 2) - M);
+    }
+    const int hg = r / n1, j = r - hg * n1;
+    const int t = qs[seq] + j;
+    p.out[((size_t)t * p.hq + g * G + hg) * HD + d] = f2bf(acc * row_il[r]);
+  }
+}
+
 template <int RT, int HD>
 __global__ __launch_bounds__(kThreads, (RT == 1 ? 4 : RT <= 3 ? 2 : 1)) void attn_kernel(AttnParams p) {
   constexpr int NDG = HD / 32;  // MFMA k-groups over the head dim
@@ -256,51 +311,217 @@ __global__ __launch_bounds__(kThreads, (RT == 1 ? 4 : RT <= 3 ? 2 : 1)) void att
     __syncthreads();
   }
 
-  // ---- the last chunk of (sequence, KV head) to arrive merges ---------------
-  // chunks of this sequence that were launched (all of them unless the grid
-  // was sized for a smaller context, which is flagged above)
-  const int first = cs[seq];
-  const int nch = min(cs[seq + 1], p.max_items) - first;
-  wait_vmem();
-  __syncthreads();
-  if (tid == 0) {
-    int *ctr = p.counters + (size_t)seq * p.hkv + g;
-    const int old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    flag[0] = old == nch - 1;
-    if (flag[0]) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __syncthreads();
-  if (!flag[0]) return;
+  publish_merge<HD>(p, qs, seq, g, R, n1, G, flag, row_m, row_il);
+}
 
-  // per row: overall max and 1 / sum over the chunks
-  for (int r = tid; r < R; r += kThreads) {
-    float M = kNegBig;
-#pragma unroll 8
-    for (int cc = 0; cc < nch; ++cc)
-      M = fmaxf(M, load_dev(p.part_ml + ((((size_t)first + cc) * p.hkv + g) * p.rpad + r) * 2));
-    float lt = 0.f;
-#pragma unroll 8
-    for (int cc = 0; cc < nch; ++cc) {
-      const float *ml = p.part_ml + ((((size_t)first + cc) * p.hkv + g) * p.rpad + r) * 2;
-      lt += load_dev(ml + 1) * __builtin_amdgcn_exp2f(load_dev(ml) - M);
-    }
-    row_m[r] = M;
-    row_il[r] = lt > 0.f ? 1.f / lt : 0.f;
+// ---------------------------------------------------------------------------
+// Query-tiled variant for more than 16 query rows per KV head (long drafts,
+// wide GQA groups).  Wave w owns query rows 16w .. 16w + 15 over every key of
+// the chunk, so no wave holds more than one row tile and no cross-wave
+// combine is needed.  Each 32-key step's keys and values are loaded once per
+// workgroup straight into LDS in MFMA fragment order (lane l's 16 bytes of
+// fragment f at f * 1 KiB + 16 l, read back conflict-free), through a ring of
+// three steps so that two are in flight while one is computed.
+constexpr int kQtStages = 3;
+
+__device__ __forceinline__ void load_lds16(const void *g, void *lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
+// Workgroup barrier that does not wait for this wave's outstanding loads (the
+// waits the ring needs are explicit); the empty asm keeps LDS accesses on
+// their side of it.
+__device__ __forceinline__ void ring_barrier() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+template <int HD>
+__global__ __launch_bounds__(kThreads, 2) void attn_qt_kernel(AttnParams p) {
+  constexpr int NDG = HD / 32, NDT = HD / 16;
+  constexpr int F = 2 * NDG + NDT;   // 1 KiB fragments per step: keys (2 x NDG), values (NDT)
+  constexpr int FW = F / 4;          // fragments each wave loads per step
+  constexpr int SLOT = F * 1024;
+  static_assert(F % 4 == 0, "fragments must split evenly over the four waves");
+  extern __shared__ __align__(16) unsigned char smem[];
+  unsigned char *ring = smem;
+  int *qs = reinterpret_cast<int *>(smem + kQtStages * SLOT);
+  int *cs = qs + p.B + 1;
+  int *flag = cs + p.B + 1;
+  float *row_m = reinterpret_cast<float *>(flag + 2);  // [64]
+  float *row_il = row_m + 64;                           // [64]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int gq = lane >> 4, l16 = lane & 15;
+  const int g = blockIdx.y;
+
+  const int total = load_maps(p, qs, cs);
+  if (blockIdx.x == 0 && g == 0 && tid == 0 && total > p.max_items) set_err(p.err, SV_DEV_ERR_CTX_BOUND);
+  const int item = blockIdx.x;
+  if (item >= total) return;
+  const int seq = upper_index(cs, p.B, item);
+  const int c = item - cs[seq];
+  const int gam = p.gamma[seq];
+  const int ctx = p.kv_len[seq];
+  const int L = ctx + gam + 1;
+  if (L > p.kv_cap) {
+    if (tid == 0) set_err(p.err, SV_DEV_ERR_KV_OVERFLOW);
+    return;
   }
-  __syncthreads();
-  for (int idx = tid; idx < R * HD; idx += kThreads) {
-    const int r = idx / HD, d = idx - r * HD;
-    const float M = row_m[r];
-    float acc = 0.f;
-#pragma unroll 8
-    for (int cc = 0; cc < nch; ++cc) {
-      const size_t pr = (((size_t)first + cc) * p.hkv + g) * p.rpad + r;
-      acc += load_dev(p.part_o + pr * HD + d) * __builtin_amdgcn_exp2f(load_dev(p.part_ml + pr * 2) - M);
+  const int G = p.hq / p.hkv;
+  const int n1 = gam + 1;
+  const int R = G * n1;
+  const int kb = c * p.chunk, ke = min(L, kb + p.chunk);
+  const int ns = (ke - kb + kKeysPerStep - 1) / kKeysPerStep;
+  const bool active = wave * 16 < R;
+
+  const uint16_t *kbase = static_cast<const uint16_t *>(p.kc[seq]) + (size_t)g * p.kv_cap * HD;
+  const uint16_t *vbase = static_cast<const uint16_t *>(p.vc[seq]) + (size_t)g * HD * p.kv_cap;
+
+  // this lane's query fragments and causal limit (row 16 * wave + l16)
+  bf16x8 qf[NDG];
+  int lim = -1;
+  {
+    const int rr = wave * 16 + l16;
+    if (rr < R) {
+      const int hg = rr / n1, j = rr - hg * n1;
+      const uint16_t *q = p.qbuf + ((size_t)(qs[seq] + j) * p.hq + g * G + hg) * HD;
+#pragma unroll
+      for (int dg = 0; dg < NDG; ++dg) qf[dg] = as_bf16x8(*reinterpret_cast<const uint4 *>(q + dslice(dg, gq)));
+      lim = ctx + j;
+    } else {
+#pragma unroll
+      for (int dg = 0; dg < NDG; ++dg) qf[dg] = as_bf16x8(uint4{0u, 0u, 0u, 0u});
     }
-    const int hg = r / n1, j = r - hg * n1;
-    const int t = qs[seq] + j;
-    p.out[((size_t)t * p.hq + g * G + hg) * HD + d] = f2bf(acc * row_il[r]);
   }
+
+  // fragment f = wave + 4 i of a step: keys (kt = f / NDG, dg = f % NDG), whose
+  // lane rows are keys k0 + 8 (l16 / 4) + 4 kt + l16 % 4 (clamped to the
+  // sequence), or values dt = f - 2 NDG (head-dim column 16 dt + l16, keys
+  // k0 + 8 gq ..; the 32-key block lies inside the cache)
+  auto issue = [&](int st) {
+    const int k0 = kb + st * kKeysPerStep;
+    unsigned char *slot = ring + (st % kQtStages) * SLOT;
+#pragma unroll
+    for (int i = 0; i < FW; ++i) {
+      const int f = wave + 4 * i;
+      const uint16_t *src;
+      if (f < 2 * NDG) {
+        const int kt = f / NDG, dg = f - kt * NDG;
+        const int key = min(k0 + 8 * (l16 >> 2) + 4 * kt + (l16 & 3), L - 1);
+        src = kbase + (size_t)key * HD + dslice(dg, gq);
+      } else {
+        const int dt = f - 2 * NDG;
+        src = vbase + (size_t)(k0 >> 5) * HD * 32 + (dt * 16 + l16) * 32 + 8 * gq;
+      }
+      load_lds16(src, slot + f * 1024);
+    }
+  };
+
+  floatx4 o[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m_run = kNegBig, l_run = 0.f;
+
+  if (ns > 0) issue(0);
+  if (ns > 1) issue(1);
+  for (int st = 0; st < ns; ++st) {
+    // this wave's loads of step st are done once at most those of st + 1 remain
+    if (st + 1 < ns)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | FW);
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+    ring_barrier();  // every wave's step st is in LDS; every wave is done with step st - 1
+    if (st + 2 < ns) issue(st + 2);
+    if (!active) continue;
+    const unsigned char *sl = ring + (st % kQtStages) * SLOT;
+    const int k0 = kb + st * kKeysPerStep;
+    floatx4 sc[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      sc[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int dg = 0; dg < NDG; ++dg) {
+        const uint4 kf = *reinterpret_cast<const uint4 *>(sl + ((kt * NDG + dg) * 64 + lane) * 16);
+        sc[kt] = mfma16x16x32(as_bf16x8(kf), qf[dg], sc[kt]);
+      }
+    }
+    float sv[8];
+    float mx = kNegBig;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int key = k0 + 8 * gq + e;
+      const bool ok = key < ke && key <= lim;
+      sv[e] = ok ? sc[e >> 2][e & 3] * p.scale_log2 : -INFINITY;
+      mx = fmaxf(mx, sv[e]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    float lsum = 0.f;
+    uint32_t pb[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float pe = __builtin_amdgcn_exp2f(sv[e] - m_new);
+      lsum += pe;
+      pb[e] = f2bf(pe);
+    }
+    l_run = l_run * alpha + lsum;
+    m_run = m_new;
+    const bf16x8 pf = as_bf16x8(uint4{pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16), pb[4] | (pb[5] << 16),
+                                      pb[6] | (pb[7] << 16)});
+    // values of keys at or past L are zeroed (the cache holds anything there)
+    const int nvalid = L - (k0 + 8 * gq);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      uint4 v = *reinterpret_cast<const uint4 *>(sl + ((2 * NDG + dt) * 64 + lane) * 16);
+      if (nvalid < 8) {
+        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (e >= nvalid) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+        v = uint4{w[0], w[1], w[2], w[3]};
+      }
+      o[dt] *= alpha;
+      o[dt] = mfma16x16x32(as_bf16x8(v), pf, o[dt]);
+    }
+  }
+
+  // publish this chunk's rows: o^T[d][row] (d = 16 dt + 4 gq + i, row = l16)
+  if (active) {
+    float l = l_run;
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const int row = wave * 16 + l16;
+    if (row < R) {
+      const size_t pr = ((size_t)item * p.hkv + g) * p.rpad + row;
+      if (gq == 0) {
+        store_dev(p.part_ml + pr * 2, m_run);
+        store_dev(p.part_ml + pr * 2 + 1, l);
+      }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) store_dev(p.part_o + pr * HD + dt * 16 + 4 * gq + i, o[dt][i]);
+    }
+  }
+  publish_merge<HD>(p, qs, seq, g, R, n1, G, flag, row_m, row_il);
+}
+
+template <int HD>
+hipError_t launch_qt(const AttnParams &p, hipStream_t s) {
+  constexpr int F = 2 * (HD / 32) + HD / 16;
+  const size_t lds = (size_t)kQtStages * F * 1024 + (size_t)(2 * (p.B + 1) + 2) * sizeof(int) +
+                     128 * sizeof(float);
+  if (lds > 65536)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_qt_kernel<HD>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  trace_before(SV_K_ATTENTION, s);
+  hipLaunchKernelGGL((attn_qt_kernel<HD>), dim3(p.max_items, p.hkv), dim3(kThreads), lds, s, p);
+  trace_after(SV_K_ATTENTION, s);
+  return hipGetLastError();
 }
 
 template <int RT, int HD>
@@ -316,14 +537,12 @@ hipError_t launch_rt(const AttnParams &p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Up to 16 query rows per KV head: waves split the keys (one row tile each);
+// more: the query-tiled kernel (one wave per row tile, keys shared in LDS).
 template <int HD>
 hipError_t launch_hd(const AttnParams &p, hipStream_t s) {
-  switch (p.rpad / 16) {
-    case 1: return launch_rt<1, HD>(p, s);
-    case 2: return launch_rt<2, HD>(p, s);
-    case 3: return launch_rt<3, HD>(p, s);
-    default: return launch_rt<4, HD>(p, s);
-  }
+  if (p.rpad <= 16) return launch_rt<1, HD>(p, s);
+  return launch_qt<HD>(p, s);
 }
 
 }  // namespace
