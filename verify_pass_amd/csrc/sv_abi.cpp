@@ -236,7 +236,7 @@ struct LayerPlan {
   GemmCfg qkv, o, gu, down, head;
   int attn_chunk = 256, attn_items = 0, attn_rpad = 16;
   size_t off_counters = 0, off_partial = 0, off_qbuf = 0, off_po = 0, off_pml = 0;
-  size_t off_attn = 0, off_x1 = 0, off_act = 0, off_stats = 0;
+  size_t off_attn = 0, off_x1 = 0, off_act = 0, off_stats = 0, off_items = 0;
   size_t off_rnorm = 0, off_rparts = 0, off_tseq = 0, off_tpos = 0, off_qs = 0, off_cs = 0, off_rope = 0;
   size_t bytes = 0;
 };
@@ -329,9 +329,16 @@ sv_status plan_layer(const sv_layer *L, const sv_batch *b, int32_t flags, LayerP
   pl.gu = gemm_cfg(GK_GU, (F + 15) / 16, 2 * F, pl.T, d, w, packed);
   pl.down = gemm_cfg(GK_DOWN, (d + 31) / 32, d, pl.T, F, w, packed);
   pl.attn_rpad = 16 * ((pl.G * (gmax + 1) + 15) / 16);
-  // keys per work item: 256, or more so that a sequence has at most 32 chunks
+  // keys per work item (a multiple of 128): enough items for one round of the
+  // resident workgroups -- 4 per CU for the key-split kernel (<= 16 query
+  // rows per KV head), 3 for the query-tiled one (48 KiB of LDS at hd 128) --
+  // and at least 256 keys and ceil(length / 32) (a sequence has at most 32)
   const long long max_len = (long long)b->max_ctx + gmax + 1;
-  pl.attn_chunk = 256 * (int)std::max<long long>(1, (max_len + 32 * 256 - 1) / (32 * 256));
+  const long long slots = 256LL * (pl.attn_rpad <= 16 || hd == 64 ? 4 : 3);
+  const long long per_seq = std::max<long long>(1, slots / std::max<long long>(1, (long long)pl.B * hk));
+  long long chunk = (max_len + per_seq - 1) / per_seq;
+  chunk = std::max({chunk, 256LL, (max_len + 31) / 32});
+  pl.attn_chunk = (int)((chunk + 127) / 128 * 128);
   long long items = 0;
   for (int i = 0; i < pl.B; ++i)
     items += ((long long)b->max_ctx + b->gamma_host[i] + 1 + pl.attn_chunk - 1) / pl.attn_chunk;
@@ -354,6 +361,7 @@ sv_status plan_layer(const sv_layer *L, const sv_batch *b, int32_t flags, LayerP
   pl.off_tpos = take((size_t)pl.T * sizeof(int));
   pl.off_qs = take((size_t)(pl.B + 1) * sizeof(int));
   pl.off_cs = take((size_t)(pl.B + 1) * sizeof(int));
+  pl.off_items = take((size_t)pl.attn_items * 2 * sizeof(int4));
   pl.off_rope = take((size_t)pl.T * hd * sizeof(float));
   pl.bytes = off;
   return SV_OK;
@@ -495,6 +503,9 @@ extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const
     pp.chunk_start = cstart;
     pp.rope_cs = reinterpret_cast<float *>(ws + pl.off_rope);
     pp.hd = hd;
+    pp.items = reinterpret_cast<int4 *>(ws + pl.off_items);
+    pp.max_items = pl.attn_items;
+    pp.err = b->err_flag;
     for (int i = 0; i < hd / 2; ++i)
       pp.inv_freq[i] = std::pow(static_cast<double>(L->rope_theta), -2.0 * i / hd);
     e = launch_prep(pp, s);
@@ -530,10 +541,7 @@ extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const
     AttnParams a;
     std::memset(&a, 0, sizeof(a));
     a.qbuf = qbuf;
-    a.gamma = b->gamma;
-    a.kv_len = b->kv_len;
-    a.q_start = qstart;
-    a.chunk_start = cstart;
+    a.items = reinterpret_cast<const int4 *>(ws + pl.off_items);
     a.kc = b->k_cache;
     a.vc = b->v_cache;
     a.B = pl.B;

@@ -29,17 +29,6 @@ constexpr int kThreads = 256;
 constexpr int kKeysPerStep = 32;
 constexpr float kNegBig = -1.0e30f;
 
-// Copy the token map (q_start) and chunk map (chunk_start) of all sequences
-// into LDS; returns the total number of work items.
-__device__ inline int load_maps(const AttnParams &p, int *qs, int *cs) {
-  for (int i = threadIdx.x; i <= p.B; i += blockDim.x) {
-    qs[i] = p.q_start[i];
-    cs[i] = p.chunk_start[i];
-  }
-  __syncthreads();
-  return cs[p.B];
-}
-
 __device__ __forceinline__ int dslice(int dg, int gq) {
   // lane group gq covers head-dim columns [64*(dg/2) + 16*gq + 8*(dg%2), +8)
   return 64 * (dg >> 1) + 16 * gq + 8 * (dg & 1);
@@ -77,19 +66,33 @@ __device__ __forceinline__ void load_values(uint4 (&v)[HD / 16], const uint16_t 
   for (int dt = 0; dt < HD / 16; ++dt) v[dt] = *reinterpret_cast<const uint4 *>(vb + (dt * 16 + l16) * 32);
 }
 
+__device__ __forceinline__ void store_dev2(float *p, float a, float b) {
+  __hip_atomic_store(reinterpret_cast<uint64_t *>(p), (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 load_dev2(const float *p) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t *>(const_cast<float *>(p)), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+}
+
+constexpr int kMergeChunks = 16;  // chunk partials in flight per output pair
+constexpr int kMergeOuts = 2;     // output pairs per thread and round
+
 // Count this chunk's arrival for (seq, KV head g); the last chunk to arrive
 // merges every chunk's (o, max, sum) by log-sum-exp and writes the output
 // rows.  Called by all threads once their partial stores are issued.
-// row_m, row_il: 64 floats of LDS each; flag: one int of LDS.
+// mw: LDS for 2 * nch * R floats (nch <= 32 chunks, R <= 64 rows); flag: one int.
+// The merge is written for memory-level parallelism: all (max, sum) pairs in
+// one round, per-(chunk, row) weights in LDS, then each thread keeps
+// kMergeOuts x kMergeChunks coherent 8-byte loads of partial rows in flight.
+// qst: the sequence's first stacked row; first, nch: its work items (those
+// that were launched: all of them unless the grid was sized for a smaller
+// context, which the prep pass flags).
 template <int HD>
-__device__ void publish_merge(const AttnParams &p, const int *qs, int seq, int g, int R, int n1, int G,
-                              int *flag, float *row_m, float *row_il) {
+__device__ void publish_merge(const AttnParams &p, int qst, int first, int nch, int seq, int g, int R, int n1,
+                              int G, int *flag, float *mw) {
   const int tid = threadIdx.x, nthr = blockDim.x;
-  const int *cs = qs + p.B + 1;
-  // chunks of this sequence that were launched (all of them unless the grid
-  // was sized for a smaller context, which is flagged by the caller)
-  const int first = cs[seq];
-  const int nch = min(cs[seq + 1], p.max_items) - first;
   wait_vmem();
   __syncthreads();
   if (tid == 0) {
@@ -101,34 +104,67 @@ __device__ void publish_merge(const AttnParams &p, const int *qs, int seq, int g
   __syncthreads();
   if (!flag[0]) return;
 
-  // per row: overall max and 1 / sum over the chunks
-  for (int r = tid; r < R; r += nthr) {
-    float M = kNegBig;
-#pragma unroll 8
-    for (int cc = 0; cc < nch; ++cc)
-      M = fmaxf(M, load_dev(p.part_ml + ((((size_t)first + cc) * p.hkv + g) * p.rpad + r) * 2));
-    float lt = 0.f;
-#pragma unroll 8
-    for (int cc = 0; cc < nch; ++cc) {
-      const float *ml = p.part_ml + ((((size_t)first + cc) * p.hkv + g) * p.rpad + r) * 2;
-      lt += load_dev(ml + 1) * __builtin_amdgcn_exp2f(load_dev(ml) - M);
-    }
-    row_m[r] = M;
-    row_il[r] = lt > 0.f ? 1.f / lt : 0.f;
+  // partial row (chunk cc, row r) of this (sequence, KV head)
+  auto prow = [&](int cc, int r) { return (((size_t)first + cc) * p.hkv + g) * p.rpad + r; };
+  float *wm = mw, *wl = mw + nch * R;  // [nch][R] each
+  for (int q = tid; q < nch * R; q += nthr) {
+    const int cc = q / R, r = q - cc * R;
+    const float2 ml = load_dev2(p.part_ml + prow(cc, r) * 2);
+    wm[q] = ml.x;
+    wl[q] = ml.y;
   }
   __syncthreads();
-  for (int idx = tid; idx < R * HD; idx += nthr) {
-    const int r = idx / HD, d = idx - r * HD;
-    const float M = row_m[r];
-    float acc = 0.f;
-#pragma unroll 8
-    for (int cc = 0; cc < nch; ++cc) {
-      const size_t pr = (((size_t)first + cc) * p.hkv + g) * p.rpad + r;
-      acc += load_dev(p.part_o + pr * HD + d) * __builtin_amdgcn_exp2f(load_dev(p.part_ml + pr * 2) - M);
+  // per row: overall max and sum; then each chunk's weight exp2(m_c - M) / sum
+  for (int r = tid; r < R; r += nthr) {
+    float M = kNegBig;
+    for (int cc = 0; cc < nch; ++cc) M = fmaxf(M, wm[cc * R + r]);
+    float lt = 0.f;
+    for (int cc = 0; cc < nch; ++cc) lt += wl[cc * R + r] * __builtin_amdgcn_exp2f(wm[cc * R + r] - M);
+    const float il = lt > 0.f ? 1.f / lt : 0.f;
+    for (int cc = 0; cc < nch; ++cc) wm[cc * R + r] = __builtin_amdgcn_exp2f(wm[cc * R + r] - M) * il;
+  }
+  __syncthreads();
+  // outputs in column pairs: (row r, columns 2 d2, 2 d2 + 1)
+  constexpr int NP = HD / 2;
+  const int nq = R * NP;
+  for (int q0 = tid; q0 < nq; q0 += nthr * kMergeOuts) {
+    float2 acc[kMergeOuts];
+#pragma unroll
+    for (int u = 0; u < kMergeOuts; ++u) acc[u] = make_float2(0.f, 0.f);
+    for (int c0 = 0; c0 < nch; c0 += kMergeChunks) {
+      float2 v[kMergeOuts][kMergeChunks];
+#pragma unroll
+      for (int u = 0; u < kMergeOuts; ++u) {
+        const int q = min(q0 + u * nthr, nq - 1);
+        const int r = q / NP, d2 = q - r * NP;
+#pragma unroll
+        for (int k = 0; k < kMergeChunks; ++k) {
+          const int cc = min(c0 + k, nch - 1);
+          v[u][k] = load_dev2(p.part_o + prow(cc, r) * HD + 2 * d2);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kMergeOuts; ++u) {
+        const int q = min(q0 + u * nthr, nq - 1);
+        const int r = q / NP;
+#pragma unroll
+        for (int k = 0; k < kMergeChunks; ++k) {
+          const float w = c0 + k < nch ? wm[(c0 + k) * R + r] : 0.f;
+          acc[u].x += v[u][k].x * w;
+          acc[u].y += v[u][k].y * w;
+        }
+      }
     }
-    const int hg = r / n1, j = r - hg * n1;
-    const int t = qs[seq] + j;
-    p.out[((size_t)t * p.hq + g * G + hg) * HD + d] = f2bf(acc * row_il[r]);
+#pragma unroll
+    for (int u = 0; u < kMergeOuts; ++u) {
+      const int q = q0 + u * nthr;
+      if (q >= nq) continue;
+      const int r = q / NP, d2 = q - r * NP;
+      const int hg = r / n1, j = r - hg * n1;
+      const int t = qst + j;
+      *reinterpret_cast<uint32_t *>(p.out + ((size_t)t * p.hq + g * G + hg) * HD + 2 * d2) =
+          f2bf(acc[u].x) | ((uint32_t)f2bf(acc[u].y) << 16);
+    }
   }
 }
 
@@ -137,26 +173,19 @@ __global__ __launch_bounds__(kThreads, (RT == 1 ? 4 : RT <= 3 ? 2 : 1)) void att
   constexpr int NDG = HD / 32;  // MFMA k-groups over the head dim
   constexpr int NDT = HD / 16;  // 16-wide head-dim tiles of the output
   extern __shared__ __align__(16) unsigned char smem[];
-  int *qs = reinterpret_cast<int *>(smem);
-  int *cs = qs + p.B + 1;
-  int *flag = cs + p.B + 1;                                      // [2]
-  float *red_o = reinterpret_cast<float *>(flag + 2);            // [4][HD][16]
+  int *flag = reinterpret_cast<int *>(smem);                     // [4]
+  float *red_o = reinterpret_cast<float *>(smem + 16);           // [4][HD][16]
   float *red_ml = red_o + 4 * HD * 16;                           // [4][16][2]
-  float *row_m = red_o;                                          // merge: [64] max, [64] 1/sum
-  float *row_il = red_o + 64;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int gq = lane >> 4, l16 = lane & 15;
   const int g = blockIdx.y;
 
-  const int total = load_maps(p, qs, cs);
-  if (blockIdx.x == 0 && g == 0 && tid == 0 && total > p.max_items) set_err(p.err, SV_DEV_ERR_CTX_BOUND);
   const int item = blockIdx.x;
-  if (item >= total) return;
-  const int seq = upper_index(cs, p.B, item);
-  const int c = item - cs[seq];
-  const int gam = p.gamma[seq];
-  const int ctx = p.kv_len[seq];
+  const int4 ia = p.items[2 * item], ib = p.items[2 * item + 1];
+  const int seq = ia.x;
+  if (seq < 0) return;
+  const int kb = ia.y, ke = ia.z, gam = ia.w, ctx = ib.x, qst = ib.y;
   const int L = ctx + gam + 1;
   if (L > p.kv_cap) {
     // every item of this sequence returns here: no arrivals are counted
@@ -166,7 +195,6 @@ __global__ __launch_bounds__(kThreads, (RT == 1 ? 4 : RT <= 3 ? 2 : 1)) void att
   const int G = p.hq / p.hkv;
   const int n1 = gam + 1;
   const int R = G * n1;
-  const int kb = c * p.chunk, ke = min(L, kb + p.chunk);
   const int per_wave = p.chunk / 4;
   const int kw0 = kb + wave * per_wave, kw1 = min(ke, kw0 + per_wave);
 
@@ -182,7 +210,7 @@ __global__ __launch_bounds__(kThreads, (RT == 1 ? 4 : RT <= 3 ? 2 : 1)) void att
     const int rr = rt * 16 + l16;
     if (rr < R) {
       const int hg = rr / n1, j = rr - hg * n1;
-      const int t = qs[seq] + j;
+      const int t = qst + j;
       const uint16_t *q = p.qbuf + ((size_t)t * p.hq + g * G + hg) * HD;
 #pragma unroll
       for (int dg = 0; dg < NDG; ++dg) qf[rt][dg] = as_bf16x8(*reinterpret_cast<const uint4 *>(q + dslice(dg, gq)));
@@ -303,15 +331,12 @@ __global__ __launch_bounds__(kThreads, (RT == 1 ? 4 : RT <= 3 ? 2 : 1)) void att
         lt += red_ml[(w * 16 + row) * 2 + 1] * f;
       }
       store_dev(p.part_o + (prow + row) * HD + d, acc);
-      if (d == 0) {
-        store_dev(p.part_ml + (prow + row) * 2, M);
-        store_dev(p.part_ml + (prow + row) * 2 + 1, lt);
-      }
+      if (d == 0) store_dev2(p.part_ml + (prow + row) * 2, M, lt);
     }
     __syncthreads();
   }
 
-  publish_merge<HD>(p, qs, seq, g, R, n1, G, flag, row_m, row_il);
+  publish_merge<HD>(p, qst, ib.z, ib.w, seq, g, R, n1, G, flag, red_o);  // red_o is free again
 }
 
 // ---------------------------------------------------------------------------
@@ -345,25 +370,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_qt_kernel(AttnParams p) {
   static_assert(F % 4 == 0, "fragments must split evenly over the four waves");
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char *ring = smem;
-  int *qs = reinterpret_cast<int *>(smem + kQtStages * SLOT);
-  int *cs = qs + p.B + 1;
-  int *flag = cs + p.B + 1;
-  float *row_m = reinterpret_cast<float *>(flag + 2);  // [64]
-  float *row_il = row_m + 64;                           // [64]
+  int *flag = reinterpret_cast<int *>(smem + kQtStages * SLOT);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int gq = lane >> 4, l16 = lane & 15;
   const int g = blockIdx.y;
 
-  const int total = load_maps(p, qs, cs);
-  if (blockIdx.x == 0 && g == 0 && tid == 0 && total > p.max_items) set_err(p.err, SV_DEV_ERR_CTX_BOUND);
   const int item = blockIdx.x;
-  if (item >= total) return;
-  const int seq = upper_index(cs, p.B, item);
-  const int c = item - cs[seq];
-  const int gam = p.gamma[seq];
-  const int ctx = p.kv_len[seq];
+  const int4 ia = p.items[2 * item], ib = p.items[2 * item + 1];
+  const int seq = ia.x;
+  if (seq < 0) return;
+  const int kb = ia.y, ke = ia.z, gam = ia.w, ctx = ib.x, qst = ib.y;
   const int L = ctx + gam + 1;
   if (L > p.kv_cap) {
     if (tid == 0) set_err(p.err, SV_DEV_ERR_KV_OVERFLOW);
@@ -372,7 +390,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_qt_kernel(AttnParams p) {
   const int G = p.hq / p.hkv;
   const int n1 = gam + 1;
   const int R = G * n1;
-  const int kb = c * p.chunk, ke = min(L, kb + p.chunk);
   const int ns = (ke - kb + kKeysPerStep - 1) / kKeysPerStep;
   const bool active = wave * 16 < R;
 
@@ -386,7 +403,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_qt_kernel(AttnParams p) {
     const int rr = wave * 16 + l16;
     if (rr < R) {
       const int hg = rr / n1, j = rr - hg * n1;
-      const uint16_t *q = p.qbuf + ((size_t)(qs[seq] + j) * p.hq + g * G + hg) * HD;
+      const uint16_t *q = p.qbuf + ((size_t)(qst + j) * p.hq + g * G + hg) * HD;
 #pragma unroll
       for (int dg = 0; dg < NDG; ++dg) qf[dg] = as_bf16x8(*reinterpret_cast<const uint4 *>(q + dslice(dg, gq)));
       lim = ctx + j;
@@ -497,24 +514,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_qt_kernel(AttnParams p) {
     const int row = wave * 16 + l16;
     if (row < R) {
       const size_t pr = ((size_t)item * p.hkv + g) * p.rpad + row;
-      if (gq == 0) {
-        store_dev(p.part_ml + pr * 2, m_run);
-        store_dev(p.part_ml + pr * 2 + 1, l);
+      if (gq == 0) store_dev2(p.part_ml + pr * 2, m_run, l);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        store_dev2(p.part_o + pr * HD + dt * 16 + 4 * gq, o[dt][0], o[dt][1]);
+        store_dev2(p.part_o + pr * HD + dt * 16 + 4 * gq + 2, o[dt][2], o[dt][3]);
       }
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) store_dev(p.part_o + pr * HD + dt * 16 + 4 * gq + i, o[dt][i]);
     }
   }
-  publish_merge<HD>(p, qs, seq, g, R, n1, G, flag, row_m, row_il);
+  publish_merge<HD>(p, qst, ib.z, ib.w, seq, g, R, n1, G, flag, reinterpret_cast<float *>(ring));  // the ring is idle now
 }
 
 template <int HD>
 hipError_t launch_qt(const AttnParams &p, hipStream_t s) {
   constexpr int F = 2 * (HD / 32) + HD / 16;
-  const size_t lds = (size_t)kQtStages * F * 1024 + (size_t)(2 * (p.B + 1) + 2) * sizeof(int) +
-                     128 * sizeof(float);
+  const size_t lds = (size_t)kQtStages * F * 1024 + 16;
   if (lds > 65536)
     (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_qt_kernel<HD>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -526,8 +540,7 @@ hipError_t launch_qt(const AttnParams &p, hipStream_t s) {
 
 template <int RT, int HD>
 hipError_t launch_rt(const AttnParams &p, hipStream_t s) {
-  const size_t lds = (size_t)(2 * (p.B + 1) + 2) * sizeof(int) + (size_t)4 * HD * 16 * sizeof(float) +
-                     4 * 16 * 2 * sizeof(float);
+  const size_t lds = 16 + (size_t)4 * HD * 16 * sizeof(float) + 4 * 16 * 2 * sizeof(float);
   if (lds > 65536)
     (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_kernel<RT, HD>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

@@ -152,15 +152,19 @@ struct PrepParams {
   int *chunk_start;    // [B + 1] attention work items of each sequence
   float *rope_cs;      // [T][hd/2][2] cos, sin (nullptr: none)
   int hd;
+  int4 *items;         // [max_items][2] attention work items (see AttnParams)
+  int max_items;
+  int *err;
   double inv_freq[64]; // theta^(-2i/hd), i < hd/2 (evaluated on the host in fp64)
 };
 
+// Attention work item (written by the prep pass, two int4 per item):
+//   [0] = {sequence (-1: no work), first key, end key, gamma}
+//   [1] = {kv_len, first stacked row of the sequence, the sequence's first item,
+//          its number of items}
 struct AttnParams {
   const uint16_t *qbuf;  // [T][hq][hd] (rotated)
-  const int *gamma;
-  const int *kv_len;
-  const int *q_start;      // [B + 1]
-  const int *chunk_start;  // [B + 1]
+  const int4 *items;     // [max_items][2]
   void *const *kc;
   void *const *vc;
   int B, T, hq, hkv, hd, kv_cap, max_ctx;

@@ -6,7 +6,10 @@
 //   q_start[i] .. q_start[i] + gamma_i (q_start = exclusive prefix sum of
 //   gamma_i + 1) and row j of it sits at position kv_len[i] + j.
 // Workgroup 0 also stores q_start[0..B] and the prefix sum of per-sequence
-// attention chunk counts ceil((kv_len[i] + gamma_i + 1) / chunk).
+// attention chunk counts ceil((kv_len[i] + gamma_i + 1) / chunk), and all
+// workgroups together write the attention work items (sequence, key range,
+// lengths, the sequence's item range), so that an attention workgroup starts
+// from one 32-byte load.
 // With a rotary table requested, each workgroup also stores cos and sin of
 // pos(t) * theta^(-2i/hd) for i < hd/2 (angle and its reduction in fp64).
 #include "sv_common.h"
@@ -82,6 +85,26 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams p) {
     if (tid == 0) {
       p.q_start[p.B] = total_t;
       p.chunk_start[p.B] = total_c;
+      // the attention grid is sized from the host's context bound
+      if (total_c > p.max_items) set_err(p.err, SV_DEV_ERR_CTX_BOUND);
+    }
+  }
+  // attention work items, spread over all workgroups: item it is chunk
+  // it - cs[seq] of the sequence whose chunk range holds it
+  if (p.items) {
+    for (int it = t * kThreads + tid; it < p.max_items; it += p.T * kThreads) {
+      int4 a = make_int4(-1, 0, 0, 0), b = make_int4(0, 0, 0, 0);
+      if (it < total_c) {
+        const int sq = upper_index(cs, p.B, it);
+        const int g = p.gamma[sq], ctx = p.kv_len[sq];
+        const int L = ctx + g + 1;
+        const int kb = (it - cs[sq]) * p.chunk;
+        a = make_int4(sq, kb, min(L, kb + p.chunk), g);
+        const int next = sq + 1 < p.B ? cs[sq + 1] : total_c;
+        b = make_int4(ctx, qs[sq], cs[sq], min(next, p.max_items) - cs[sq]);
+      }
+      p.items[2 * it] = a;
+      p.items[2 * it + 1] = b;
     }
   }
 }
