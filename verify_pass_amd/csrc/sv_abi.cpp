@@ -117,7 +117,8 @@ enum GemmKind { GK_QKV = 0, GK_O, GK_GU, GK_DOWN, GK_HEAD, GK_COUNT };
 
 // Optional override of the launch policy (tuning sweeps, tests):
 // "qkv:1:4:16,o:1:4:16,gu:1:8:4,down:1:8:16,head:1:2:1"
-// (kind:splits:depth[:waves per unit, 0 = the LDS-tiled kernel]), from
+// (kind:splits:depth[:waves per unit, 0 = the LDS-tiled kernel, 2 = the wide
+// streaming kernel]), from
 // SV_GEMM_TUNE at load time or sv_set_gemm_tuning.
 struct Tune {
   int splits[GK_COUNT];
@@ -165,6 +166,14 @@ struct GemmCfg {
   size_t counters() const { return splits > 1 ? (size_t)nblk * ntblk : 0; }
 };
 
+// The wide streaming kernel: token blocks of 64 (T <= 64) or 128 tokens.
+void set_wide(GemmCfg &c, int T, int splits) {
+  c.kw = kGemmWide;
+  c.tt = T <= 64 ? 4 : 8;
+  c.ntblk = (T + 16 * c.tt - 1) / (16 * c.tt);
+  c.splits = std::max(1, std::min(splits, c.ksteps));
+}
+
 // nblk: 32-row groups (16 gate/up feature pairs for SwiGLU).
 // Enough row groups to fill the chip (2048 waves): one wave per unit, no K
 // split, a shallow prefetch and many resident waves.  Too few: several waves
@@ -179,6 +188,7 @@ GemmCfg gemm_cfg(int kind, int nblk, int N, int T, int K, int wtype, bool packed
   c.K = K;
   c.tt = T <= 16 ? 1 : T <= 32 ? 2 : T <= 48 ? 3 : 4;
   c.ntblk = (T + 16 * c.tt - 1) / (16 * c.tt);
+  const int stream_tt = c.tt, stream_ntblk = c.ntblk;
   c.ksteps = K / kstep_of(wtype);
   const int base = std::max(1, nblk * c.ntblk);
   if (base >= kFill) {
@@ -213,9 +223,18 @@ GemmCfg gemm_cfg(int kind, int nblk, int N, int T, int K, int wtype, bool packed
   // four-tile token blocks become bound by the token-operand traffic
   const bool tiled_ok = wtype == SV_W_BF16 && packed;
   const long long tiled_wgs = (long long)((nblk + 7) / 8) * ((T + 127) / 128);
-  if (tiled_ok && T > 48 && tiled_wgs >= 128) {
+  if (tiled_ok && T > 48 && tiled_wgs >= 256) {
     c.kw = kGemmTiled;
     c.splits = 1;
+  } else if (tiled_ok && T > 48) {
+    // too few tiles for the tiled kernel to fill the CUs: the wide streaming
+    // kernel, with K splits filling one round of resident workgroups (one per
+    // CU for 128-token blocks, two for 64), each split at least 8 K steps
+    set_wide(c, T, 1);
+    const long long per = (long long)((nblk + 7) / 8) * c.ntblk;
+    const long long slots = c.tt == 8 ? 256 : 512;
+    c.splits = (int)std::max<long long>(1, std::min<long long>(slots / per, c.ksteps / 8));
+    c.depth = 4;
   }
   const Tune tn = tune();
   if (tn.splits[kind] > 0) c.splits = std::max(1, std::min(tn.splits[kind], c.ksteps));
@@ -223,11 +242,17 @@ GemmCfg gemm_cfg(int kind, int nblk, int N, int T, int K, int wtype, bool packed
   if (tn.kw[kind] == 0 && tiled_ok) {
     c.kw = kGemmTiled;
     c.splits = 1;
+  } else if (tn.kw[kind] == 2 && tiled_ok && T > 16) {
+    set_wide(c, T, tn.splits[kind] > 0 ? tn.splits[kind] : 1);
   } else if (tn.kw[kind] > 0) {
     c.kw = tn.kw[kind] >= 16 ? 16 : tn.kw[kind] >= 8 ? 8 : tn.kw[kind] >= 4 ? 4 : 1;
   }
+  if (c.kw != kGemmWide) {  // the token blocking of the streaming kernels
+    c.tt = stream_tt;
+    c.ntblk = stream_ntblk;
+  }
   if (c.kw == kGemmTiled) c.splits = 1;
-  if (c.splits > 1 && (size_t)base > kMaxCounters) c.splits = 1;
+  if (c.splits > 1 && (size_t)c.nblk * c.ntblk > kMaxCounters) c.splits = 1;
   return c;
 }
 

@@ -229,8 +229,11 @@ struct AcceptParams {
 // ---------------------------------------------------------------------------
 // Host launchers (one per kernel family).  Return hipSuccess or the launch error.
 // depth = K steps in flight per wave (2, 4, 8); kw = waves per unit (1, 4, 8, 16),
-// or kGemmTiled for the LDS-tiled kernel (bf16, packed weights, no K split).
+// kGemmTiled for the LDS-tiled kernel (bf16, packed weights, no K split), or
+// kGemmWide for the wide streaming kernel (bf16, packed weights, tok_tiles 4
+// or 8 per token block).
 constexpr int kGemmTiled = -1;
+constexpr int kGemmWide = -2;
 hipError_t launch_gemm(const GemmParams &p, int wtype, int tok_tiles, int depth, int kw, hipStream_t s,
                        int trace_class);
 hipError_t launch_pack(int wtype, int N, int K, const void *w, const void *scale, void *wp,

@@ -2,6 +2,9 @@
 // (sv_gemm_bf16.hip, sv_gemm_int4.hip, sv_gemm_f32.hip) so that the three
 // translation units compile in parallel.
 #pragma once
+#include <type_traits>
+#include <utility>
+
 #include "sv_common.h"
 
 namespace sv {
@@ -442,6 +445,45 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, floatx4 (&acc)[2][
 // Waves per workgroup for KW waves per unit.
 template <int KW> constexpr int waves_per_wg() { return KW > 4 ? KW : 4; }
 
+// K split across workgroups: store this unit's partial tile with device-scope
+// stores, count its arrival, and if it is the last of the splits, add all
+// partials in split order into acc (bitwise repeatable).  Returns whether this
+// unit is the last (and must run the epilogue).
+template <int TT>
+__device__ __forceinline__ bool split_reduce(const GemmParams &p, floatx4 (&acc)[2][TT], int grp, int tb, int split,
+                                             int lane) {
+  constexpr int TILE = 2 * TT * 4 * 64;  // one partial value per (tile, token tile, row, lane)
+  const size_t tile_id = (size_t)tb * p.nblk + grp;
+  float *mine = p.partial + ((size_t)split * p.nblk * p.ntblk + tile_id) * TILE;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) store_dev(mine + ((a * TT + tt) * 4 + i) * 64 + lane, acc[a][tt][i]);
+  wait_vmem();
+  int old = 0;
+  if (lane == 0)
+    old = __hip_atomic_fetch_add(p.counters + tile_id, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  old = __shfl(old, 0);
+  if (old != p.splits - 1) return false;
+  if (lane == 0) __hip_atomic_store(p.counters + tile_id, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) acc[a][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < p.splits; ++sp) {
+    const float *src = p.partial + ((size_t)sp * p.nblk * p.ntblk + tile_id) * TILE;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[a][tt][i] += load_dev(src + ((a * TT + tt) * 4 + i) * 64 + lane);
+  }
+  return true;
+}
+
 // G = K steps of weights and tokens in flight per wave: 2 for long streams
 // (many resident waves share the work), 4 or 8 for short ones (one or two
 // rounds of loads per wave).  No occupancy hint: forcing 8 workgroups per CU
@@ -625,37 +667,7 @@ __global__ __launch_bounds__(64 * waves_per_wg<KW>()) void gemm_kernel(GemmParam
   }
 
   // ---- K-split reduction across units ---------------------------------------
-  if (p.splits > 1) {
-    constexpr int TILE = 2 * TT * 4 * 64;  // one partial value per (tile, token tile, row, lane)
-    const size_t tile_id = (size_t)tb * ngrp + grp;
-    float *mine = p.partial + ((size_t)split * ngrp * p.ntblk + tile_id) * TILE;
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) store_dev(mine + ((a * TT + tt) * 4 + i) * 64 + lane, acc[a][tt][i]);
-    wait_vmem();
-    int old = 0;
-    if (lane == 0)
-      old = __hip_atomic_fetch_add(p.counters + tile_id, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    old = __shfl(old, 0);
-    if (old != p.splits - 1) return;
-    if (lane == 0) __hip_atomic_store(p.counters + tile_id, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt) acc[a][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    for (int sp = 0; sp < p.splits; ++sp) {
-      const float *src = p.partial + ((size_t)sp * ngrp * p.ntblk + tile_id) * TILE;
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[a][tt][i] += load_dev(src + ((a * TT + tt) * 4 + i) * 64 + lane);
-    }
-  }
+  if (p.splits > 1 && !split_reduce<TT>(p, acc, grp, tb, split, lane)) return;
 
   epilogue<TT, EPI>(p, acc, grp, t0, gq, l16);
 }
@@ -821,6 +833,191 @@ inline hipError_t launch_tiled(const GemmParams &p, hipStream_t s, int trace_cla
     case EPI_RESID: return launch_tiled_epi<EPI_RESID>(p, s, trace_class);
     case EPI_SWIGLU: return launch_tiled_epi<EPI_SWIGLU>(p, s, trace_class);
     default: return launch_tiled_epi<EPI_LOGITS>(p, s, trace_class);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Wide streaming GEMM for many stacked tokens (bf16, packed weights).
+//
+// A workgroup of 4 waves computes 8 row groups (256 weight rows) x 16 TT
+// tokens over a K range.  Each wave owns two row groups (64 rows) and streams
+// their weight fragments straight from HBM into registers; the token operand
+// of a step is loaded once per workgroup straight into LDS (fragment order)
+// and read by all four waves.  Both run D steps ahead of the MFMAs (a ring of
+// D + 1 register buffers and D + 1 LDS slots): a step's MFMAs take well under
+// an HBM round trip, so one step of lookahead leaves every step waiting for
+// its weights.  Per step a wave issues 16 TT MFMAs for 2 TT 16-byte LDS reads
+// (256 B of LDS per MFMA), half of what staging the weights through LDS as
+// well would read.  K splits across workgroups go through the same
+// deterministic last-arriver reduction as the streaming kernel, and the
+// epilogues are the same.
+constexpr int kWGroups = 8;  // 32-row groups per workgroup (two per wave)
+
+// f(std::integral_constant<int, k>()) for k = 0 .. N-1 (compile-time indices
+// keep register ring slots static)
+template <class F, int... K>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, K...>) {
+  (f(std::integral_constant<int, K>()), ...);
+}
+template <int N, class F> __device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>());
+}
+
+
+template <int EPI, int TT, int D>
+__global__ __launch_bounds__(256, (D <= 2 ? 2 : 1)) void gemm_wide_kernel(GemmParams p) {
+  constexpr int NB = D + 1;   // ring slots (registers and LDS)
+  constexpr int XF = TT * 2;  // token fragments (1 KiB) per step
+  constexpr int XW = XF / 4;  // loaded by each wave
+  constexpr int PER = 8 + XW; // loads a wave issues per step (weights, tokens)
+  constexpr int SLOT = XF * 1024;
+  static_assert(XF % 4 == 0, "token fragments must split over the four waves");
+  static_assert((D - 1) * PER <= 63, "outstanding loads beyond the vmcnt range");
+  static_assert(NB <= 5, "ring slots");
+  // one LDS object per ring slot: reads of one slot then provably do not
+  // alias the direct-to-LDS loads in flight into the others, and the compiler
+  // does not wait for those loads before every LDS read
+  __shared__ __align__(16) unsigned char xr0[SLOT], xr1[SLOT], xr2[SLOT];
+  __shared__ __align__(16) unsigned char xr3[NB > 3 ? SLOT : 16], xr4[NB > 4 ? SLOT : 16];
+  auto slot_of = [&](auto kc) -> unsigned char * {
+    constexpr int k = decltype(kc)::value;
+    if constexpr (k == 0) return xr0;
+    else if constexpr (k == 1) return xr1;
+    else if constexpr (k == 2) return xr2;
+    else if constexpr (k == 3) return xr3;
+    else return xr4;
+  };
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int gq = lane >> 4, l16 = lane & 15;
+  const int nrb = (p.nblk + kWGroups - 1) / kWGroups;
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  // token block fastest: the workgroups that read a row block's weights run
+  // side by side on one XCD and find them in its L2
+  const int tb = wg % p.ntblk;
+  const int rest = wg / p.ntblk;
+  const int rb = rest % nrb, split = rest / nrb;
+  const int t0 = tb * TT * 16;
+  const int u0 = (int)((long long)split * p.ksteps / p.splits);
+  const int u1 = (int)((long long)(split + 1) * p.ksteps / p.splits);
+  const int ns = u1 - u0;
+
+  int grp[2];
+  bool gact[2];
+  WSrc<WT_BF16> src[2][2];
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi) {
+    const int gr = rb * kWGroups + 2 * wave + gi;
+    gact[gi] = gr < p.nblk;
+    grp[gi] = min(gr, p.nblk - 1);  // idle groups stream a valid group; results dropped
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      int mi = 0, pr0 = 0;
+      if (!map_row(p, grp[gi], a, 0, mi, pr0)) { mi = 0; pr0 = 0; }
+      src[gi][a] = make_src<WT_BF16>(p.mat[mi], pr0, pr0, p.K, p.ksteps, 1, lane, gq);
+    }
+  }
+  // token fragments this wave loads: f = wave + 4 i -> (tt = f / 2, half m = f % 2)
+  const uint16_t *xa[XW];
+#pragma unroll
+  for (int i = 0; i < XW; ++i) {
+    const int f = wave + 4 * i, tt = f >> 1, m = f & 1;
+    xa[i] = p.x + (size_t)min(t0 + tt * 16 + l16, p.T - 1) * p.K + (size_t)u0 * 64 + 32 * m + 8 * gq;
+  }
+
+  floatx4 acc[2][2][TT];
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) acc[gi][a][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  WStep<WT_BF16> wb[NB][2][2];  // [slot][group][tile]
+  // Step st's tokens go to LDS slot st % NB and its weights to wb[st % NB].
+  // The loop is branch-free so the compiler can count which loads feed which
+  // registers (behind conditional loads it drains every load at each step):
+  // steps past the end reload the last step (clamped addresses) and compute
+  // with a zero token operand.
+  auto issue = [&](int st, auto kc) {
+    constexpr int k = decltype(kc)::value;
+    const int sc = min(st, ns - 1);
+    unsigned char *slot = slot_of(kc);
+#pragma unroll
+    for (int i = 0; i < XW; ++i) load_lds16(xa[i] + sc * 64, slot + (wave + 4 * i) * 1024);
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+      for (int a = 0; a < 2; ++a) wb[k][gi][a] = load_w<WT_BF16>(src[gi][a], u0 + sc);
+  };
+  if (ns > 0) {
+    static_for<D>([&](auto kc) { issue(decltype(kc)::value, kc); });
+    // step st (slot b = st % NB): wait for its loads (the D - 1 later steps'
+    // stay in flight), barrier, issue step st + D into the slot step st - 1
+    // used, compute
+    auto step = [&](int st, auto bc) {
+      constexpr int b = decltype(bc)::value;
+      constexpr int later = (D - 1) * PER;
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (later & 15) | ((later >> 4) << 14));
+      ring_barrier();  // step st's tokens in LDS for everyone; everyone is done with step st - 1
+      issue(st + D, std::integral_constant<int, (b + D) % NB>());
+      const bool live = st < ns;
+      const unsigned char *xs = slot_of(bc);
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+          uint4 xr = ld_v4(xs + ((tt * 2 + m) * 64 + lane) * 16);
+          if (!live) xr = uint4{0u, 0u, 0u, 0u};
+          const bf16x8 xv = as_bf16x8(xr);
+#pragma unroll
+          for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+              acc[gi][a][tt] = mfma16x16x32(as_bf16x8(wb[b][gi][a].v[m]), xv, acc[gi][a][tt]);
+        }
+    };
+    for (int st0 = 0; st0 < ns; st0 += NB) static_for<NB>([&](auto kc) { step(st0 + decltype(kc)::value, kc); });
+    wait_vmem();  // the clamped tail loads
+  }
+
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi) {
+    if (!gact[gi]) continue;
+    if (p.splits > 1 && !split_reduce<TT>(p, acc[gi], grp[gi], tb, split, lane)) continue;
+    epilogue<TT, EPI>(p, acc[gi], grp[gi], t0, gq, l16);
+  }
+}
+
+// Grid of the wide kernel: row blocks x token blocks x K splits.
+inline int wide_grid(const GemmParams &p) {
+  return ((p.nblk + kWGroups - 1) / kWGroups) * p.ntblk * p.splits;
+}
+
+template <int EPI, int TT, int D>
+hipError_t launch_wide_d(const GemmParams &p, hipStream_t s, int trace_class) {
+  trace_before(trace_class, s);
+  hipLaunchKernelGGL((gemm_wide_kernel<EPI, TT, D>), dim3(wide_grid(p)), dim3(256), 0, s, p);
+  trace_after(trace_class, s);
+  return hipGetLastError();
+}
+
+// tok_tiles: 4 (up to 64 tokens per block; depth = steps of lookahead, 2 or 4)
+// or 8 (128 tokens; 4 steps of lookahead -- at 2 the two resident waves per
+// SIMD leave too few registers and it spills)
+template <int EPI>
+hipError_t launch_wide_epi(const GemmParams &p, int tok_tiles, int depth, hipStream_t s, int trace_class) {
+  if (tok_tiles <= 4)
+    return depth >= 4 ? launch_wide_d<EPI, 4, 4>(p, s, trace_class) : launch_wide_d<EPI, 4, 2>(p, s, trace_class);
+  return launch_wide_d<EPI, 8, 4>(p, s, trace_class);
+}
+
+inline hipError_t launch_wide(const GemmParams &p, int tok_tiles, int depth, hipStream_t s, int trace_class) {
+  switch (p.epi) {
+    case EPI_QKV: return launch_wide_epi<EPI_QKV>(p, tok_tiles, depth, s, trace_class);
+    case EPI_RESID: return launch_wide_epi<EPI_RESID>(p, tok_tiles, depth, s, trace_class);
+    case EPI_SWIGLU: return launch_wide_epi<EPI_SWIGLU>(p, tok_tiles, depth, s, trace_class);
+    default: return launch_wide_epi<EPI_LOGITS>(p, tok_tiles, depth, s, trace_class);
   }
 }
 
