@@ -302,9 +302,10 @@ sv_status sv_trace_end(float *ms_out, int32_t capacity, int32_t *count);
  * comma-separated list of kind:splits:depth[:waves] entries, kind one of
  * qkv, o, gu, down, head; splits = K splits across workgroups, depth = K steps
  * in flight per wave (2, 4 or 8), waves = waves of one workgroup sharing a
- * unit's K range (1, 4, 8 or 16), 0 for the LDS-tiled kernel or 2 for the
- * wide streaming kernel, both for many stacked tokens (bf16 packed weights
- * and more than 16 tokens only; otherwise the policy's choice stays).  Zero splits or depth, or an absent kind, keep the default
+ * unit's K range (1, 4, 8 or 16), or for many stacked tokens 0 (the
+ * LDS-tiled kernel), 2 (the wide streaming kernel) or 3 (the square-tiled
+ * kernel), bf16 packed weights only (the wide kernel also needs more than 16
+ * tokens; otherwise the policy's choice stays).  Zero splits or depth, or an absent kind, keep the default
  * policy; settings beyond a kernel's register budget fall back to the nearest
  * smaller one.  NULL restores the defaults (also read from the environment
  * variable SV_GEMM_TUNE when the library loads).  Process-wide; set it

@@ -234,6 +234,7 @@ struct AcceptParams {
 // or 8 per token block).
 constexpr int kGemmTiled = -1;
 constexpr int kGemmWide = -2;
+constexpr int kGemmSquare = -3;  // 256 x 256 square-tiled kernel (bf16 packed, no K split)
 hipError_t launch_gemm(const GemmParams &p, int wtype, int tok_tiles, int depth, int kw, hipStream_t s,
                        int trace_class);
 hipError_t launch_pack(int wtype, int N, int K, const void *w, const void *scale, void *wp,

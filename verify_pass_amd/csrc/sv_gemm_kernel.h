@@ -1021,6 +1021,146 @@ inline hipError_t launch_wide(const GemmParams &p, int tok_tiles, int depth, hip
   }
 }
 
+// ---------------------------------------------------------------------------
+// Square-tiled GEMM for the MFMA-bound range (hundreds of stacked tokens;
+// bf16, packed weights).
+//
+// A workgroup of 8 waves computes 256 weight rows x 256 tokens; wave w owns
+// row groups 2 (w % 4), +1 (64 rows) x tokens 128 (w / 4) .. +127, 128
+// accumulators.  K advances in half steps of 32: each half step's 16 weight
+// fragments and 16 token fragments (1 KiB each, in MFMA lane order) are loaded
+// straight into LDS, four per wave, and each wave reads 4 weight and 8 token
+// fragments for its 32 MFMAs (384 B of LDS per MFMA; the 256 x 128 tiled
+// kernel reads 512).  A ring of four half-step slots, each its own LDS object,
+// keeps three half steps in flight; the loop is branch-free (clamped tail
+// loads, zero token operand past the end), so the compiler's waits stay
+// exact.  No K split; the epilogues are the streaming kernel's.
+constexpr int kSThreads = 512;
+constexpr int kSGroups = 8;     // 32-row groups per workgroup
+constexpr int kSTok = 256;      // tokens per workgroup
+constexpr int kSStages = 4;
+constexpr int kSSlot = 32 * 1024;  // 16 weight + 16 token fragments
+
+template <int EPI>
+__global__ __launch_bounds__(kSThreads, 1) void gemm_sq_kernel(GemmParams p) {
+  constexpr int D = kSStages - 1;  // half steps in flight
+  constexpr int PER = 4;           // loads per wave and half step
+  __shared__ __align__(16) unsigned char sl0[kSSlot], sl1[kSSlot], sl2[kSSlot], sl3[kSSlot];
+  auto slot_of = [&](auto kc) -> unsigned char * {
+    constexpr int k = decltype(kc)::value;
+    if constexpr (k == 0) return sl0;
+    else if constexpr (k == 1) return sl1;
+    else if constexpr (k == 2) return sl2;
+    else return sl3;
+  };
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int gq = lane >> 4, l16 = lane & 15;
+  const int ntb = (p.T + kSTok - 1) / kSTok;
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int tb = wg % ntb, rb = wg / ntb;  // token block fastest (shared weights in L2)
+  const int gp = wave & 3, th = wave >> 2;
+  const int nh = 2 * p.ksteps;            // half steps
+
+  // the four fragments this wave loads each half step: f = wave + 8 i;
+  // f < 16: weight fragment (group f / 2, tile f % 2), else token tile f - 16
+  const unsigned char *src[PER];
+  size_t sstep[PER];  // bytes per full K step (weights: the matrix's step stride; tokens: 128)
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int f = wave + 8 * i;
+    if (f < 16) {
+      int mi = 0, pr0 = 0;
+      if (!map_row(p, rb * kSGroups + (f >> 1), f & 1, 0, mi, pr0)) { mi = 0; pr0 = 0; }
+      const size_t g = (size_t)(pr0 / 32);
+      const int a = (pr0 / 16) & 1;
+      src[i] = static_cast<const unsigned char *>(p.mat[mi].w) + (((g * 2 + a) * 2) * 64 + lane) * 16;
+      sstep[i] = (size_t)((p.mat[mi].rows + 31) / 32) * 4096;
+    } else {
+      const int tt = f - 16;
+      src[i] = reinterpret_cast<const unsigned char *>(
+          p.x + (size_t)min(tb * kSTok + tt * 16 + l16, p.T - 1) * p.K + 8 * gq);
+      sstep[i] = 128;
+    }
+  }
+  // half step h = 2 s + m: weights at s * stride + m * 1 KiB, tokens at s * 128 + m * 64 bytes
+  auto issue = [&](int h, auto kc) {
+    const int hc = min(h, nh - 1);
+    const int s = hc >> 1, m = hc & 1;
+    unsigned char *slot = slot_of(kc);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int f = wave + 8 * i;
+      const size_t off = (size_t)s * sstep[i] + (f < 16 ? m * 1024 : m * 64);
+      load_lds16(src[i] + off, slot + f * 1024);
+    }
+  };
+
+  floatx4 acc[2][2][8];
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[gi][a][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  static_for<D>([&](auto kc) { issue(decltype(kc)::value, kc); });
+  auto step = [&](int h, auto bc) {
+    constexpr int later = (D - 1) * PER;
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (later & 15) | ((later >> 4) << 14));
+    ring_barrier();  // half step h in LDS for everyone; everyone is done with h - 1
+    issue(h + D, std::integral_constant<int, (decltype(bc)::value + D) % kSStages>());
+    const unsigned char *sl = slot_of(bc);
+    bf16x8 wv[2][2];
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+        wv[gi][a] = as_bf16x8(ld_v4(sl + (((2 * gp + gi) * 2 + a) * 64 + lane) * 16));
+    const bool live = h < nh;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint4 xr = ld_v4(sl + ((16 + th * 8 + j) * 64 + lane) * 16);
+      if (!live) xr = uint4{0u, 0u, 0u, 0u};
+      const bf16x8 xv = as_bf16x8(xr);
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+        for (int a = 0; a < 2; ++a) acc[gi][a][j] = mfma16x16x32(wv[gi][a], xv, acc[gi][a][j]);
+    }
+  };
+  for (int h0 = 0; h0 < nh; h0 += kSStages)
+    static_for<kSStages>([&](auto kc) { step(h0 + decltype(kc)::value, kc); });
+  wait_vmem();  // the clamped tail loads
+
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi) {
+    const int grp = rb * kSGroups + 2 * gp + gi;
+    if (grp < p.nblk) epilogue<8, EPI>(p, acc[gi], grp, tb * kSTok + th * 128, gq, l16);
+  }
+}
+
+inline int sq_grid(const GemmParams &p) {
+  return ((p.nblk + kSGroups - 1) / kSGroups) * ((p.T + kSTok - 1) / kSTok);
+}
+
+template <int EPI>
+hipError_t launch_sq_epi(const GemmParams &p, hipStream_t s, int trace_class) {
+  trace_before(trace_class, s);
+  hipLaunchKernelGGL((gemm_sq_kernel<EPI>), dim3(sq_grid(p)), dim3(kSThreads), 0, s, p);
+  trace_after(trace_class, s);
+  return hipGetLastError();
+}
+
+inline hipError_t launch_sq(const GemmParams &p, hipStream_t s, int trace_class) {
+  switch (p.epi) {
+    case EPI_QKV: return launch_sq_epi<EPI_QKV>(p, s, trace_class);
+    case EPI_RESID: return launch_sq_epi<EPI_RESID>(p, s, trace_class);
+    case EPI_SWIGLU: return launch_sq_epi<EPI_SWIGLU>(p, s, trace_class);
+    default: return launch_sq_epi<EPI_LOGITS>(p, s, trace_class);
+  }
+}
+
 template <int WT, int TT, int EPI, int G, int KW>
 hipError_t launch_g(const GemmParams &p, hipStream_t s, int trace_class) {
   constexpr int WV = waves_per_wg<KW>();
