@@ -220,23 +220,28 @@ def sweep(args):
             us = torch.rand(B, device="cuda", generator=gen)
             acc = torch.zeros(B, dtype=torch.int32, device="cuda")
             nxt = torch.zeros(B, dtype=torch.int32, device="cuda")
-            kv0 = batch.kv_len.clone()
             gl = [g] * B
-
-            def step():
-                batch.kv_len.copy_(kv0)
-                assert sv.sv_verify_layer(Ld, bs, x, y, 0, ws, nws, stream) == 0
-                assert sv.sv_verify_layer(Lh, bs, y, probs, 0, ws, nws, stream) == 0
-                assert sv.sv_accept_commit(B, V, 0, gl, batch.gamma, draft, probs, q, ua, us,
-                                           batch.kv_len, acc, nxt, batch.err, ws, nws, stream) == 0
-            for _ in range(3):
-                step()
-            torch.cuda.synchronize()
             n_it = 10 if T <= 512 else 4
+            # each step reads and commits its own copy of the starting lengths
+            kv_all = batch.kv_len.clone().repeat(3 + n_it, 1).contiguous()
+            bss = []
+            for k in range(3 + n_it):
+                b_ = batch.struct()
+                b_.kv_len = kv_all[k].data_ptr()
+                bss.append(b_)
+
+            def step(k):
+                assert sv.sv_verify_layer(Ld, bss[k], x, y, 0, ws, nws, stream) == 0
+                assert sv.sv_verify_layer(Lh, bss[k], y, probs, 0, ws, nws, stream) == 0
+                assert sv.sv_accept_commit(B, V, 0, gl, batch.gamma, draft, probs, q, ua, us,
+                                           kv_all[k], acc, nxt, batch.err, ws, nws, stream) == 0
+            for k in range(3):
+                step(k)
+            torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            for _ in range(n_it):
-                step()
+            for k in range(n_it):
+                step(3 + k)
             e1.record()
             torch.cuda.synchronize()
             ms = e0.elapsed_time(e1) / n_it
@@ -377,6 +382,14 @@ def main():
     acc_all = torch.zeros(nsteps, wl.B, dtype=torch.int32, device="cuda")
     nxt_all = torch.zeros(nsteps, wl.B, dtype=torch.int32, device="cuda")
     kv0 = batch.kv_len.clone()
+    # every step verifies the same state: step k reads and commits its own
+    # copy of the starting KV lengths (no restore inside the timed region)
+    kv_all = kv0.repeat(nsteps, 1).contiguous()
+    bss = []
+    for k in range(nsteps):
+        b_ = batch.struct()
+        b_.kv_len = kv_all[k].data_ptr()
+        bss.append(b_)
     na = sv.sv_accept_commit_workspace_bytes(wl.B, V, 0, list(wl.gamma))
     ws_a = tg.workspace(na)
     glist = list(int(g) for g in wl.gamma)
@@ -385,13 +398,12 @@ def main():
     def step(k):
         st, _, _ = sv.sv_plan_gamma(plan, wl.B)          # host: draft lengths for the live batch
         assert st == 0
-        batch.kv_len.copy_(kv0)                            # every step verifies the same state
-        assert sv.sv_verify_layer(Ld, bs, x, y, 0, ws_d, nd, stream) == 0
+        assert sv.sv_verify_layer(Ld, bss[k], x, y, 0, ws_d, nd, stream) == 0
         if lm is not None:
-            assert sv.sv_verify_layer(Lh, bs, y, probs, 0, ws_h, nh, stream) == 0
+            assert sv.sv_verify_layer(Lh, bss[k], y, probs, 0, ws_h, nh, stream) == 0
         p_acc = p_alpha if p_alpha is not None else probs
         assert sv.sv_accept_commit(wl.B, V, 0, glist, batch.gamma, draft, p_acc, q, ua[k], us[k],
-                                   batch.kv_len, acc_all[k], nxt_all[k], batch.err, ws_a, na,
+                                   kv_all[k], acc_all[k], nxt_all[k], batch.err, ws_a, na,
                                    stream) == 0
 
     if args.copy_probe_mib > 0:
@@ -459,6 +471,7 @@ def main():
                  sv.SV_K_ACCEPT: "accept", sv.SV_K_PREP: "prep"}
         for cls, nm in names.items():
             n = 10
+            kv_all.copy_(kv0.expand_as(kv_all))   # the starting lengths again
             assert sv.sv_trace_begin(cls, n) == 0
             for k in range(n):
                 step(k % nsteps)

@@ -330,7 +330,7 @@ def test_kv_overflow_flagged_and_contained():
 
 
 @pytest.mark.parametrize("tiling", [None, "qkv:1:2:0,o:1:2:0,gu:1:2:0,down:1:2:0,head:1:2:0",
-                                    "qkv:2:2:1,o:1:4:1,gu:1:2:1,down:3:4:1,head:2:2:1",
+                                    "qkv:2:2:1,o:1:4:1,gu:1:2:1,down:3:4:1,head:1:2:1",
                                     "qkv:1:2:2,o:3:2:2,gu:1:2:2,down:2:2:2,head:2:2:2",
                                     "qkv:1:2:3,o:1:2:3,gu:1:2:3,down:1:2:3,head:1:2:3"])
 def test_many_tokens_layer_and_head(tiling):

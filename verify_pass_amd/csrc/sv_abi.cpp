@@ -472,17 +472,23 @@ extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const
   }
 
   if (L->kind == SV_LAYER_HEAD) {
-    PrepParams pp;
-    std::memset(&pp, 0, sizeof(pp));
-    pp.x = static_cast<const uint16_t *>(x_in);
-    pp.T = pl.T;
-    pp.d = L->d;
-    pp.eps = L->eps;
-    pp.rnorm = reinterpret_cast<float *>(ws + pl.off_rnorm);
-    e = launch_prep(pp, s);
-    if (e != hipSuccess) return SV_ERR_HIP;
     GemmParams p = base_params(pl.head, x_in, pl.T, wt, ws, pl);
-    p.rnorm = pp.rnorm;
+    if (pl.head.kw == 1 && pl.head.splits == 1) {
+      // one wave per unit, whole K range: the kernel takes the RMSNorm scale
+      // from the token rows it loads (no separate pass)
+      p.rms_inline = 1;
+    } else {
+      PrepParams pp;
+      std::memset(&pp, 0, sizeof(pp));
+      pp.x = static_cast<const uint16_t *>(x_in);
+      pp.T = pl.T;
+      pp.d = L->d;
+      pp.eps = L->eps;
+      pp.rnorm = reinterpret_cast<float *>(ws + pl.off_rnorm);
+      e = launch_prep(pp, s);
+      if (e != hipSuccess) return SV_ERR_HIP;
+      p.rnorm = pp.rnorm;
+    }
     p.packed = L->layout == SV_LAYOUT_PACKED;
     p.nmat = 1;
     p.mat[0] = mat_of(L->lm_head, L->vocab);

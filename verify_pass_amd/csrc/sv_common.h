@@ -116,6 +116,8 @@ struct GemmParams {
   const float *rnorm;      // per-token RMSNorm scale [T] (nullptr: see rparts / none)
   const float *rparts;     // per-token sums of squares in nparts partials [T][nparts]
   int nparts;
+  int rms_inline;          // one-wave-per-unit launches without K split: the RMSNorm
+                           // scale from the token operand the workgroup loads
   float eps;
   float *sq_out;           // EPI_RESID: sums of squares of the output, [T][row groups]
   float *partial;      // K-split partial tiles (device-scope stores)

@@ -258,15 +258,11 @@ __device__ __forceinline__ void st_bf16x4(uint16_t *o, const float (&v)[4]) {
                                              f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16));
 }
 
-// RMSNorm scale of the unit's tokens and the fused epilogue of one 32-row
-// group: acc[a][tt] holds rows (group grp, tile a, 4*gq + i) x token
-// t0 + 16*tt + l16 of this lane.
-template <int TT, int EPI>
-__device__ __forceinline__ void epilogue(const GemmParams &p, floatx4 (&acc)[2][TT], int grp, int t0, int gq,
-                                         int l16) {
-  // per-token RMSNorm scale of the operand rows (lane's token is t0 + tt*16 + l16):
-  // precomputed scales, or sums of squares left in partials by the producer
-  float rs[TT];
+// RMSNorm scale of the operand rows for this lane's tokens (t0 + 16 tt + l16):
+// precomputed scales, or sums of squares left in partials by the producer,
+// or 1.
+template <int TT>
+__device__ __forceinline__ void token_scales(const GemmParams &p, int t0, int gq, int l16, float (&rs)[TT]) {
 #pragma unroll
   for (int tt = 0; tt < TT; ++tt) {
     const int t = min(t0 + tt * 16 + l16, p.T - 1);
@@ -285,7 +281,25 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, floatx4 (&acc)[2][
       rs[tt] = 1.f;
     }
   }
+}
 
+template <int TT, int EPI>
+__device__ __forceinline__ void epilogue_rs(const GemmParams &p, floatx4 (&acc)[2][TT], int grp, int t0, int gq,
+                                            int l16, const float (&rs)[TT]);
+
+// The fused epilogue of one 32-row group: acc[a][tt] holds rows (group grp,
+// tile a, 4*gq + i) x token t0 + 16*tt + l16 of this lane.
+template <int TT, int EPI>
+__device__ __forceinline__ void epilogue(const GemmParams &p, floatx4 (&acc)[2][TT], int grp, int t0, int gq,
+                                         int l16) {
+  float rs[TT];
+  token_scales<TT>(p, t0, gq, l16, rs);
+  epilogue_rs<TT, EPI>(p, acc, grp, t0, gq, l16, rs);
+}
+
+template <int TT, int EPI>
+__device__ __forceinline__ void epilogue_rs(const GemmParams &p, floatx4 (&acc)[2][TT], int grp, int t0, int gq,
+                                            int l16, const float (&rs)[TT]) {
   // ---- fused epilogues (lane-local) -----------------------------------------
   // Each lane holds, per tile, four consecutive output columns (rows 4gq..4gq+3
   // of the tile): written as one 8- or 16-byte access when the row stride keeps
@@ -486,16 +500,22 @@ __device__ __forceinline__ bool split_reduce(const GemmParams &p, floatx4 (&acc)
 
 // G = K steps of weights and tokens in flight per wave: 2 for long streams
 // (many resident waves share the work), 4 or 8 for short ones (one or two
-// rounds of loads per wave).  No occupancy hint: forcing 8 workgroups per CU
-// (64 registers) on the one-wave-per-unit streams spills and measured slower
-// than the 6 the register count gives.
+// rounds of loads per wave).  The one-wave-per-unit bf16 stream (the LM head
+// at up to 32 tokens) is held to 6 resident workgroups per CU (80 registers):
+// a few registers more drop it to 5 and cost 2% of its time; forcing 8 (64
+// registers) spills and measured slower.
 // KW = waves per unit: the unit's K range is cut into KW consecutive pieces,
 // one per wave of the same workgroup, and the pieces are added through LDS in
 // wave order (bitwise repeatable) before the epilogue, which the unit's first
 // wave runs.  This fills the chip for short row counts without sending
 // partial sums through memory.
+template <int WT, int TT, int G, int KW> constexpr int min_wg_per_cu() {
+  return (KW == 1 && WT == WT_BF16 && TT <= 2 && G <= 2) ? 6 : 1;
+}
+
 template <int WT, int TT, int EPI, int G, int KW>
-__global__ __launch_bounds__(64 * waves_per_wg<KW>()) void gemm_kernel(GemmParams p) {
+__global__ __launch_bounds__(64 * waves_per_wg<KW>(), (min_wg_per_cu<WT, TT, G, KW>())) void gemm_kernel(
+    GemmParams p) {
   constexpr int WV = waves_per_wg<KW>();
   constexpr int UPW = WV / KW;  // units per workgroup
   constexpr int NACC = 2 * TT * 4;
@@ -559,6 +579,9 @@ __global__ __launch_bounds__(64 * waves_per_wg<KW>()) void gemm_kernel(GemmParam
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) acc[a][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float ssq[TT];  // rms_inline: this lane's share of its tokens' sums of squares
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) ssq[tt] = 0.f;
 
   // Grouped prefetch: G steps of weights and tokens in flight per wave, then
   // compute.  A shallow group keeps the register count low, so many waves are
@@ -610,6 +633,17 @@ __global__ __launch_bounds__(64 * waves_per_wg<KW>()) void gemm_kernel(GemmParam
             XStep<WT> xv;
 #pragma unroll
             for (int m = 0; m < NXF; ++m) xv.v[m] = ld_v4(xs + ((j * XF + tt * NXF + m) * 64 + lane) * 16);
+            if (p.rms_inline) {
+#pragma unroll
+              for (int m = 0; m < NXF; ++m) {
+                const uint32_t w4[4] = {xv.v[m].x, xv.v[m].y, xv.v[m].z, xv.v[m].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const float lo = __uint_as_float(w4[e] << 16), hi = __uint_as_float(w4[e] & 0xFFFF0000u);
+                  ssq[tt] += lo * lo + hi * hi;
+                }
+              }
+            }
             mma_tile<WT>(wbuf[j][0], xv, acc[0][tt]);
             mma_tile<WT>(wbuf[j][1], xv, acc[1][tt]);
           }
@@ -669,7 +703,20 @@ __global__ __launch_bounds__(64 * waves_per_wg<KW>()) void gemm_kernel(GemmParam
   // ---- K-split reduction across units ---------------------------------------
   if (p.splits > 1 && !split_reduce<TT>(p, acc, grp, tb, split, lane)) return;
 
-  epilogue<TT, EPI>(p, acc, grp, t0, gq, l16);
+  if (KW == 1 && p.rms_inline) {
+    // every lane group gq read a quarter of each token's K values
+    float rs[TT];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      float sq = ssq[tt];
+      sq += __shfl_xor(sq, 16);
+      sq += __shfl_xor(sq, 32);
+      rs[tt] = 1.f / sqrtf(sq / static_cast<float>(p.K) + p.eps);
+    }
+    epilogue_rs<TT, EPI>(p, acc, grp, t0, gq, l16, rs);
+  } else {
+    epilogue<TT, EPI>(p, acc, grp, t0, gq, l16);
+  }
 }
 
 // ---------------------------------------------------------------------------
