@@ -8,7 +8,8 @@ constexpr int kThreads = 256;
 constexpr int kEmbedThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 
-constexpr int kVec = 8;  // float4 loads per thread in flight: 8192 columns per workgroup
+constexpr int kVec = 8;   // float4 loads per thread in flight: 8192 columns per workgroup
+constexpr int kStat = 20; // statistics per thread in flight (one round up to 5120 groups)
 
 // (m, s) pairs stand for s * exp(x - m); combining two keeps the larger m.
 __device__ __forceinline__ void combine(float &m, float &s, float m2, float s2) {
@@ -29,18 +30,34 @@ __device__ __forceinline__ void combine(float &m, float &s, float m2, float s2) 
 __global__ __launch_bounds__(kThreads) void head_softmax_kernel(HeadSoftmaxParams p) {
   __shared__ float red_m[kThreads / 64], red_s[kThreads / 64];
   const int t = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const float2 *st = reinterpret_cast<const float2 *>(p.stats) + (size_t)t * p.nblk;
-  float m = -INFINITY, s = 0.f;
-  // kVec statistics in flight per thread, combined in index order
-  for (int b0 = tid; b0 < p.nblk; b0 += kVec * kThreads) {
-    float2 e[kVec];
+  float *row = p.logits + (size_t)t * p.V;
+  const int c0 = blockIdx.x * p.cols_per_block;
+  const int c1 = min(p.V, c0 + p.cols_per_block);
+  const bool vec = (p.V & 3) == 0;  // rows are 16-byte aligned: four columns per access
+  // this block's logits first: their loads do not depend on the row's M and S
+  // and stay in flight while the statistics are combined
+  float4 *r4 = reinterpret_cast<float4 *>(row);
+  const int e4 = c1 / 4;
+  float4 v[kVec];
+  if (vec) {
 #pragma unroll
     for (int k = 0; k < kVec; ++k) {
+      const int c = c0 / 4 + tid + k * kThreads;
+      if (c < e4) v[k] = r4[c];
+    }
+  }
+  // the row's statistics, kStat per thread in flight, combined in index order
+  const float2 *st = reinterpret_cast<const float2 *>(p.stats) + (size_t)t * p.nblk;
+  float m = -INFINITY, s = 0.f;
+  for (int b0 = tid; b0 < p.nblk; b0 += kStat * kThreads) {
+    float2 e[kStat];
+#pragma unroll
+    for (int k = 0; k < kStat; ++k) {
       const int b = b0 + k * kThreads;
       e[k] = b < p.nblk ? st[b] : make_float2(-INFINITY, 0.f);
     }
 #pragma unroll
-    for (int k = 0; k < kVec; ++k) combine(m, s, e[k].x, e[k].y);
+    for (int k = 0; k < kStat; ++k) combine(m, s, e[k].x, e[k].y);
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -56,19 +73,8 @@ __global__ __launch_bounds__(kThreads) void head_softmax_kernel(HeadSoftmaxParam
 #pragma unroll
   for (int k = 1; k < kThreads / 64; ++k) combine(M, S, red_m[k], red_s[k]);
 
-  float *row = p.logits + (size_t)t * p.V;
-  const int c0 = blockIdx.x * p.cols_per_block;
-  const int c1 = min(p.V, c0 + p.cols_per_block);
   const float Mk = M * kLog2e;
-  if ((p.V & 3) == 0) {  // rows are 16-byte aligned: four columns per load, all loads first
-    float4 *r4 = reinterpret_cast<float4 *>(row);
-    const int e4 = c1 / 4;
-    float4 v[kVec];
-#pragma unroll
-    for (int k = 0; k < kVec; ++k) {
-      const int c = c0 / 4 + tid + k * kThreads;
-      if (c < e4) v[k] = r4[c];
-    }
+  if (vec) {
 #pragma unroll
     for (int k = 0; k < kVec; ++k) {
       const int c = c0 / 4 + tid + k * kThreads;
