@@ -76,19 +76,21 @@ __device__ __forceinline__ float2 load_dev2(const float *p) {
   return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
 }
 
-constexpr int kMergeChunks = 16;  // chunk partials in flight per output pair
+constexpr int kMergeChunks = 12;  // chunk partials in flight per output pair
 constexpr int kMergeOuts = 2;     // output pairs per thread and round
 
 // Count this chunk's arrival for (seq, KV head g); the last chunk to arrive
 // merges every chunk's (o, max, sum) by log-sum-exp and writes the output
 // rows.  Called by all threads once their partial stores are issued.
-// mw: LDS for 2 * nch * R floats (nch <= 32 chunks, R <= 64 rows); flag: one int.
-// The merge is written for memory-level parallelism: all (max, sum) pairs in
-// one round, per-(chunk, row) weights in LDS, then each thread keeps
-// kMergeOuts x kMergeChunks coherent 8-byte loads of partial rows in flight.
 // qst: the sequence's first stacked row; first, nch: its work items (those
 // that were launched: all of them unless the grid was sized for a smaller
 // context, which the prep pass flags).
+// mw: LDS for 2 * nch * R floats (nch <= 32 chunks, R <= 64 rows); flag: one int.
+// The merge is written for memory-level parallelism: the first round of
+// partial-row loads (kMergeOuts output pairs x kMergeChunks chunks per
+// thread, coherent 8-byte loads) is issued together with the loads of every
+// chunk's (max, sum); the per-(chunk, row) weights are formed in LDS while
+// they are in flight.
 template <int HD>
 __device__ void publish_merge(const AttnParams &p, int qst, int first, int nch, int seq, int g, int R, int n1,
                               int G, int *flag, float *mw) {
@@ -106,6 +108,22 @@ __device__ void publish_merge(const AttnParams &p, int qst, int first, int nch, 
 
   // partial row (chunk cc, row r) of this (sequence, KV head)
   auto prow = [&](int cc, int r) { return (((size_t)first + cc) * p.hkv + g) * p.rpad + r; };
+  constexpr int NP = HD / 2;  // outputs in column pairs: (row r, columns 2 d2, 2 d2 + 1)
+  const int nq = R * NP;
+  float2 v[kMergeOuts][kMergeChunks];
+  auto load_round = [&](int q0, int c0) {
+#pragma unroll
+    for (int u = 0; u < kMergeOuts; ++u) {
+      const int q = min(q0 + u * nthr, nq - 1);
+      const int r = q / NP, d2 = q - r * NP;
+#pragma unroll
+      for (int k = 0; k < kMergeChunks; ++k) {
+        const int cc = min(c0 + k, nch - 1);
+        v[u][k] = load_dev2(p.part_o + prow(cc, r) * HD + 2 * d2);
+      }
+    }
+  };
+  load_round(tid, 0);  // in flight with the (max, sum) loads below
   float *wm = mw, *wl = mw + nch * R;  // [nch][R] each
   for (int q = tid; q < nch * R; q += nthr) {
     const int cc = q / R, r = q - cc * R;
@@ -124,29 +142,15 @@ __device__ void publish_merge(const AttnParams &p, int qst, int first, int nch, 
     for (int cc = 0; cc < nch; ++cc) wm[cc * R + r] = __builtin_amdgcn_exp2f(wm[cc * R + r] - M) * il;
   }
   __syncthreads();
-  // outputs in column pairs: (row r, columns 2 d2, 2 d2 + 1)
-  constexpr int NP = HD / 2;
-  const int nq = R * NP;
   for (int q0 = tid; q0 < nq; q0 += nthr * kMergeOuts) {
     float2 acc[kMergeOuts];
 #pragma unroll
     for (int u = 0; u < kMergeOuts; ++u) acc[u] = make_float2(0.f, 0.f);
     for (int c0 = 0; c0 < nch; c0 += kMergeChunks) {
-      float2 v[kMergeOuts][kMergeChunks];
+      if (q0 != tid || c0 != 0) load_round(q0, c0);  // the first round is already loaded
 #pragma unroll
       for (int u = 0; u < kMergeOuts; ++u) {
-        const int q = min(q0 + u * nthr, nq - 1);
-        const int r = q / NP, d2 = q - r * NP;
-#pragma unroll
-        for (int k = 0; k < kMergeChunks; ++k) {
-          const int cc = min(c0 + k, nch - 1);
-          v[u][k] = load_dev2(p.part_o + prow(cc, r) * HD + 2 * d2);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kMergeOuts; ++u) {
-        const int q = min(q0 + u * nthr, nq - 1);
-        const int r = q / NP;
+        const int r = min(q0 + u * nthr, nq - 1) / NP;
 #pragma unroll
         for (int k = 0; k < kMergeChunks; ++k) {
           const float w = c0 + k < nch ? wm[(c0 + k) * R + r] : 0.f;
