@@ -164,6 +164,16 @@ def fit_step_model(bs, ts, n):
     return tuple(float(v) for v in r.x)
 
 
+def head_modes(args, sv):
+    """Head flags and acceptance mode of a step: by default the head writes
+    logits plus each row's (max, sum of exp) and acceptance forms the
+    probabilities it reads from them (bit-identical to reading materialized
+    probabilities); --head-probs materializes the probabilities."""
+    if args.head_probs:
+        return 0, sv.SV_ACCEPT_STOCHASTIC
+    return sv.SV_HEAD_LOGITS_STATS, sv.SV_ACCEPT_STOCHASTIC | sv.SV_ACCEPT_FROM_LOGITS
+
+
 def sweep(args):
     """Step time over a (B, gamma) grid: one layer of the chosen shape, the
     151936-entry head and acceptance, all on device-generated synthetic data
@@ -173,6 +183,7 @@ def sweep(args):
     import torch
 
     import verify_pass_amd as sv
+    hflags, amode = head_modes(args, sv)
     from verify_pass_amd import torch_glue as tg
     from workloads import SHAPES, head_weights, layer_weights
 
@@ -205,13 +216,13 @@ def sweep(args):
             batch.vptr = torch.tensor([t.data_ptr() for t in vcs], dtype=torch.int64, device="cuda")
             bs = batch.struct()
             nd = sv.sv_verify_layer_workspace_bytes(Ld, bs)
-            nh = sv.sv_verify_layer_workspace_bytes(Lh, bs)
-            na = sv.sv_accept_commit_workspace_bytes(B, V, 0, [g] * B)
+            nh = sv.sv_verify_layer_workspace_bytes(Lh, bs, hflags)
+            na = sv.sv_accept_commit_workspace_bytes(B, V, amode, [g] * B)
             ws = tg.workspace(max(nd, nh, na))
             nws = ws.numel()
             x = torch.randn(T, sh.d, device="cuda", generator=gen).to(torch.bfloat16)
             y = torch.empty_like(x)
-            probs = torch.empty(T, V, dtype=torch.float32, device="cuda")
+            probs = torch.empty(T * (V + 2), dtype=torch.float32, device="cuda")
             nd_ = max(1, B * g)
             draft = torch.randint(0, V, (nd_,), device="cuda", generator=gen, dtype=torch.int32)
             q = torch.zeros(nd_, V, device="cuda")
@@ -232,8 +243,8 @@ def sweep(args):
 
             def step(k):
                 assert sv.sv_verify_layer(Ld, bss[k], x, y, 0, ws, nws, stream) == 0
-                assert sv.sv_verify_layer(Lh, bss[k], y, probs, 0, ws, nws, stream) == 0
-                assert sv.sv_accept_commit(B, V, 0, gl, batch.gamma, draft, probs, q, ua, us,
+                assert sv.sv_verify_layer(Lh, bss[k], y, probs, hflags, ws, nws, stream) == 0
+                assert sv.sv_accept_commit(B, V, amode, gl, batch.gamma, draft, probs, q, ua, us,
                                            kv_all[k], acc, nxt, batch.err, ws, nws, stream) == 0
             for k in range(3):
                 step(k)
@@ -296,6 +307,9 @@ def main():
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-table", action="store_true")
+    ap.add_argument("--head-probs", action="store_true",
+                    help="head writes probabilities and acceptance reads them (default: logits "
+                         "plus row (max, sum), acceptance forms the probabilities it reads)")
     ap.add_argument("--sweep", action="store_true",
                     help="time the step over a (B, gamma) grid on one layer shape instead, fit the "
                          "step model per gamma and report the crossover batch")
@@ -326,6 +340,7 @@ def main():
                            rng_for, uniforms_2m24, workload)
 
     torch.cuda.set_device(0)
+    hflags, amode = head_modes(args, sv)
     wl = workload(args.workload)
     sh = wl.shape
     K, Wm = args.steps, args.warmup
@@ -352,10 +367,10 @@ def main():
     stream = tg.stream_handle()
     if lm is not None:
         Lh = tg.head_struct(sh, wl.wtype, lm, packed=packed)
-        nh = sv.sv_verify_layer_workspace_bytes(Lh, bs)
+        nh = sv.sv_verify_layer_workspace_bytes(Lh, bs, hflags)
         nhl = sv.sv_verify_layer_workspace_bytes(Lh, bs, sv.SV_HEAD_LOGITS)
         ws_h = tg.workspace(max(nh, nhl))
-        probs = torch.empty(wl.T, V, dtype=torch.float32, device="cuda")
+        probs = torch.empty(wl.T * (V + 2), dtype=torch.float32, device="cuda")
 
     # draft rows / target rows for acceptance, built once from the model's own outputs
     if lm is not None:
@@ -390,7 +405,8 @@ def main():
         b_ = batch.struct()
         b_.kv_len = kv_all[k].data_ptr()
         bss.append(b_)
-    na = sv.sv_accept_commit_workspace_bytes(wl.B, V, 0, list(wl.gamma))
+    p_mode = sv.SV_ACCEPT_STOCHASTIC if p_alpha is not None else amode
+    na = sv.sv_accept_commit_workspace_bytes(wl.B, V, p_mode, list(wl.gamma))
     ws_a = tg.workspace(na)
     glist = list(int(g) for g in wl.gamma)
     plan = sv.make_plan_params(sv.SV_PLAN_BUDGET, 64, budget_tokens=24)
@@ -400,9 +416,9 @@ def main():
         assert st == 0
         assert sv.sv_verify_layer(Ld, bss[k], x, y, 0, ws_d, nd, stream) == 0
         if lm is not None:
-            assert sv.sv_verify_layer(Lh, bss[k], y, probs, 0, ws_h, nh, stream) == 0
+            assert sv.sv_verify_layer(Lh, bss[k], y, probs, hflags, ws_h, nh, stream) == 0
         p_acc = p_alpha if p_alpha is not None else probs
-        assert sv.sv_accept_commit(wl.B, V, 0, glist, batch.gamma, draft, p_acc, q, ua[k], us[k],
+        assert sv.sv_accept_commit(wl.B, V, p_mode, glist, batch.gamma, draft, p_acc, q, ua[k], us[k],
                                    kv_all[k], acc_all[k], nxt_all[k], batch.err, ws_a, na,
                                    stream) == 0
 
@@ -467,7 +483,8 @@ def main():
         names = {sv.SV_K_GEMM_QKV: "gemm_qkv", sv.SV_K_ATTENTION: "attention",
                  sv.SV_K_GEMM_O: "gemm_o",
                  sv.SV_K_GEMM_GATE_UP: "gemm_gate_up", sv.SV_K_GEMM_DOWN: "gemm_down",
-                 sv.SV_K_GEMM_LM_HEAD: "gemm_lm_head", sv.SV_K_SOFTMAX: "softmax",
+                 sv.SV_K_GEMM_LM_HEAD: "gemm_lm_head",
+                 sv.SV_K_SOFTMAX: "softmax" if args.head_probs else "row_stats",
                  sv.SV_K_ACCEPT: "accept", sv.SV_K_PREP: "prep"}
         for cls, nm in names.items():
             n = 10
@@ -505,7 +522,8 @@ def main():
                    "T": wl.T, "ctx": int(wl.ctx[0]) if len(set(wl.ctx.tolist())) == 1 else "ragged",
                    "weights": wl.wtype + (" packed" if packed else ""), "d": sh.d, "heads": f"{sh.n_q}q/{sh.n_kv}kv x {sh.hd}",
                    "ffn": sh.ffn, "vocab": V if lm is not None else None,
-                   "acceptance": (wl.alphas[0] if wl.alphas else wl.draft)},
+                   "acceptance": (wl.alphas[0] if wl.alphas else wl.draft),
+                   "head_output": "probabilities" if args.head_probs else "logits+row stats"},
         "accepted_tok_s": round(accepted_tok_s, 2),
         "tokens_per_step": round(tokens_per_step, 3),
         "roofline": roof,

@@ -88,7 +88,10 @@ typedef int32_t sv_status;
 #define SV_LAYOUT_PACKED 1   /* produced by sv_pack_matrix (bf16 and int4 only) */
 
 /* sv_verify_layer flags. */
-#define SV_HEAD_LOGITS 1 /* HEAD: write fp32 logits instead of probabilities */
+#define SV_HEAD_LOGITS 1       /* HEAD: write fp32 logits instead of probabilities */
+#define SV_HEAD_LOGITS_STATS 2 /* HEAD: write fp32 logits [T][vocab] followed by each
+                                  row's (max, sum of exp(logit - max)) [T][2]; feeds
+                                  sv_accept_commit with SV_ACCEPT_FROM_LOGITS */
 
 /* One weight matrix in [N][K] = [output features][reduction] layout.
  * scale is used only for SV_W_INT4_G32. */
@@ -191,7 +194,9 @@ sv_status sv_verify_layer_workspace_bytes(const sv_layer *layer, const sv_batch 
 /* One verify pass through one layer.
  *   DECODER: x_in bf16 [T][d] -> y_out bf16 [T][d]; appends K/V rows.
  *   HEAD:    x_in bf16 [T][d] -> y_out fp32 [T][vocab] probabilities
- *            (or logits with SV_HEAD_LOGITS).
+ *            (or logits with SV_HEAD_LOGITS; or logits followed by the rows'
+ *            softmax statistics, T * (vocab + 2) floats, with
+ *            SV_HEAD_LOGITS_STATS).
  *   EMBED:   x_in int32 token ids [T] -> y_out bf16 [T][d].
  * x_in and y_out must not overlap.  Only B, T, gamma_host and err_flag of the
  * batch are used by EMBED and HEAD. */
@@ -199,9 +204,15 @@ sv_status sv_verify_layer(const sv_layer *layer, const sv_batch *batch, const vo
                           void *y_out, int32_t flags, void *workspace, size_t workspace_bytes,
                           void *stream);
 
-/* Acceptance modes. */
+/* Acceptance modes, optionally or'ed with SV_ACCEPT_FROM_LOGITS: p is then
+ * the output of an SV_HEAD_LOGITS_STATS head call (logits [T][V] followed by
+ * each row's (max M, sum S of exp(logit - M)) [T][2]) and every probability
+ * the rule reads is formed from it exactly as the head's softmax finish
+ * forms it (exp2(logit * log2 e - M log2 e) / S in fp32), so the results are
+ * bit-identical to passing the head's probabilities. */
 #define SV_ACCEPT_STOCHASTIC 0
 #define SV_ACCEPT_GREEDY 1
+#define SV_ACCEPT_FROM_LOGITS 0x100
 
 /* Workspace needed by sv_accept_commit. */
 sv_status sv_accept_commit_workspace_bytes(int32_t B, int32_t V, int32_t mode,

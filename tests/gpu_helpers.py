@@ -74,12 +74,18 @@ class GpuHead:
         self.batch = tg.DeviceBatch(wl.gamma, wl.ctx, wl.cap)
         self.bs = self.batch.struct()
         self.ws_bytes = {f: sv.sv_verify_layer_workspace_bytes(self.L, self.bs, f)
-                         for f in (0, sv.SV_HEAD_LOGITS)}
+                         for f in (0, sv.SV_HEAD_LOGITS, sv.SV_HEAD_LOGITS_STATS)}
         self.ws = tg.workspace(max(self.ws_bytes.values()))
 
-    def run(self, y: torch.Tensor, logits=False) -> torch.Tensor:
-        f = sv.SV_HEAD_LOGITS if logits else 0
-        out = torch.empty(y.shape[0], self.wl.shape.vocab, dtype=torch.float32, device=y.device)
+    def run(self, y: torch.Tensor, logits=False, flags=None) -> torch.Tensor:
+        """Probabilities [T][V], logits [T][V] (logits=True), or with
+        flags=SV_HEAD_LOGITS_STATS the flat T*V logits followed by T (max, sum)."""
+        f = flags if flags is not None else (sv.SV_HEAD_LOGITS if logits else 0)
+        T, V = y.shape[0], self.wl.shape.vocab
+        if f == sv.SV_HEAD_LOGITS_STATS:
+            out = torch.empty(T * (V + 2), dtype=torch.float32, device=y.device)
+        else:
+            out = torch.empty(T, V, dtype=torch.float32, device=y.device)
         check(sv.sv_verify_layer(self.L, self.bs, y, out, f, self.ws, self.ws_bytes[f],
                                  tg.stream_handle()), "head")
         return out

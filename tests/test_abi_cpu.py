@@ -100,6 +100,12 @@ def test_negative_gamma_and_flags_rejected():
     assert st == sv.SV_ERR_INVALID_ARG
     st = sv._lib.sv_verify_layer(C.byref(L), C.byref(_batch([1])), 0x10, 0x20, 8, 0x30, 1 << 30, None)
     assert st == sv.SV_ERR_INVALID_ARG
+    # the two head output flags exclude each other; each alone is a valid query
+    H = _layer(kind=sv.SV_LAYER_HEAD)
+    for f in (sv.SV_HEAD_LOGITS, sv.SV_HEAD_LOGITS_STATS):
+        assert _ws(H, _batch([2, 0, 3]), f)[0] == sv.SV_OK
+    assert _ws(H, _batch([2, 0, 3]), sv.SV_HEAD_LOGITS | sv.SV_HEAD_LOGITS_STATS)[0] == \
+        sv.SV_ERR_INVALID_ARG
 
 
 def test_int4_needs_scales_and_128_multiples():
@@ -153,6 +159,12 @@ def test_accept_validation():
     # greedy needs no q / uniforms
     ng = sv.sv_accept_commit_workspace_bytes(2, 100, sv.SV_ACCEPT_GREEDY, g)
     assert ng > 0
+    # the logits flag combines with either mode and changes no workspace size;
+    # other high bits are rejected
+    for m, size in ((sv.SV_ACCEPT_STOCHASTIC, n), (sv.SV_ACCEPT_GREEDY, ng)):
+        assert sv.sv_accept_commit_workspace_bytes(2, 100, m | sv.SV_ACCEPT_FROM_LOGITS, g) == size
+    assert f(2, 100, 0x200, ga, *ok_ptrs, 0x20, n, None) == sv.SV_ERR_INVALID_ARG
+    assert f(2, 100, sv.SV_ACCEPT_FROM_LOGITS | 2, ga, *ok_ptrs, 0x20, n, None) == sv.SV_ERR_INVALID_ARG
 
 
 # ---- planner: host logic, against the oracle -------------------------------

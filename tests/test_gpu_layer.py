@@ -116,6 +116,53 @@ def test_head_parity(packed):
         np.testing.assert_allclose(pr, OV.softmax(lg), rtol=2e-5, atol=1e-9)
 
 
+@pytest.mark.parametrize("vocab", [5003, 12288])
+def test_head_logits_stats_feed_accept(vocab):
+    """The head's logits plus per-row (max, sum of exp) fed to acceptance give
+    the same accepted counts, next tokens and KV lengths, bit for bit, as the
+    head's probabilities; the statistics are the rows' max and sum of exp.
+    Vocabularies: odd (scalar loads, two chunks) and a multiple of 4 (vector
+    loads, three chunks)."""
+    shape = Shape(512, 8, 2, 128, 1024, vocab)
+    gamma = [3, 0, 5, 1, 2, 4]
+    wl = custom_workload(shape, "bf16", gamma, [1] * len(gamma), seed=21)
+    head = GpuHead(wl)
+    yh = hidden_states(wl.T, shape.d, 5)
+    yd = tg.to_dev(yh)
+    T, V = wl.T, vocab
+    pr = head.run(yd).cpu().numpy()
+    lg = head.run(yd, logits=True).cpu().numpy()
+    fused = head.run(yd, flags=sv.SV_HEAD_LOGITS_STATS).cpu().numpy()
+    np.testing.assert_array_equal(fused[:T * V].reshape(T, V), lg)
+    ms = fused[T * V:].reshape(T, 2)
+    np.testing.assert_array_equal(ms[:, 0], lg.max(1))
+    ref_s = np.exp(lg.astype(np.float64) - lg.max(1, keepdims=True).astype(np.float64)).sum(1)
+    np.testing.assert_allclose(ms[:, 1], ref_s, rtol=1e-5)
+    kv = np.full(wl.B, 40, np.int32)
+    drows = np.concatenate([np.arange(wl.q_start[i], wl.q_start[i] + gamma[i]) for i in range(wl.B)])
+    lens = set()
+    for seed in (1, 2, 3):
+        for greedy in (False, True):
+            inp = accept_inputs(wl, V, target_logits=lg, target_probs=pr, seed=seed)
+            if greedy:  # agree with the target's argmax on a seed-dependent prefix
+                d = inp["draft"].copy()
+                for n, r in enumerate(drows):
+                    if (n + seed) % 3:
+                        d[n] = int(np.argmax(pr[r]))
+                inp["draft"] = d
+            mode = sv.SV_ACCEPT_GREEDY if greedy else sv.SV_ACCEPT_STOCHASTIC
+            a1, y1, k1, e1 = run_accept(gamma, V, inp, kv, mode)
+            a2, y2, k2, e2 = run_accept(gamma, V, dict(inp, p=fused), kv,
+                                        mode | sv.SV_ACCEPT_FROM_LOGITS)
+            ra, ry, rk, _ = oracle_accept(gamma, inp, kv, greedy=greedy)
+            say(f"V={V} seed={seed} greedy={greedy}: accepted {a1.tolist()}")
+            for u, w in ((a1, a2), (y1, y2), (k1, k2), (a1, ra), (y1, ry), (k1, rk)):
+                np.testing.assert_array_equal(u, w)
+            assert e1 == e2 == 0
+            lens.update(a1.tolist())
+    assert len(lens) >= 3  # the cases reach several accepted lengths
+
+
 def test_decoder_then_head_shared_workspace():
     """The chain a verify step runs: decoder layer then LM head on one stream,
     sharing one workspace, against the oracle chain."""

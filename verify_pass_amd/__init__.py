@@ -27,9 +27,10 @@ SV_DEV_ERR_CTX_BOUND = 4
 
 SV_LAYER_EMBED, SV_LAYER_DECODER, SV_LAYER_HEAD = 0, 1, 2
 SV_W_F32, SV_W_BF16, SV_W_INT4_G32 = 0, 1, 2
-SV_HEAD_LOGITS = 1
+SV_HEAD_LOGITS, SV_HEAD_LOGITS_STATS = 1, 2
 SV_LAYOUT_ROWMAJOR, SV_LAYOUT_PACKED = 0, 1
 SV_ACCEPT_STOCHASTIC, SV_ACCEPT_GREEDY = 0, 1
+SV_ACCEPT_FROM_LOGITS = 0x100
 SV_PLAN_BUDGET, SV_PLAN_SPEEDUP = 0, 1
 
 SV_K_GEMM_QKV, SV_K_ATTENTION = 0, 1

@@ -295,7 +295,8 @@ sv_status check_matrix(const sv_matrix &m, int wtype) {
 sv_status plan_layer(const sv_layer *L, const sv_batch *b, int32_t flags, LayerPlan &pl) {
   if (!L || !b) return SV_ERR_INVALID_ARG;
   if (L->kind < SV_LAYER_EMBED || L->kind > SV_LAYER_HEAD) return SV_ERR_INVALID_ARG;
-  if (flags & ~SV_HEAD_LOGITS) return SV_ERR_INVALID_ARG;
+  if (flags & ~(SV_HEAD_LOGITS | SV_HEAD_LOGITS_STATS)) return SV_ERR_INVALID_ARG;
+  if ((flags & SV_HEAD_LOGITS) && (flags & SV_HEAD_LOGITS_STATS)) return SV_ERR_INVALID_ARG;
   if (b->B < 0 || b->T < 0) return SV_ERR_INVALID_ARG;
   if (b->B > 0 && !b->gamma_host) return SV_ERR_INVALID_ARG;
   long long T = 0;
@@ -516,7 +517,8 @@ extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const
       h.V = L->vocab;
       h.nblk = pl.head.nblk;
       h.cols_per_block = kSoftmaxCols;
-      e = launch_head_softmax(h, s);
+      h.row_ms = static_cast<float *>(y_out) + (size_t)pl.T * L->vocab;
+      e = (flags & SV_HEAD_LOGITS_STATS) ? launch_head_rowstats(h, s) : launch_head_softmax(h, s);
     }
     return e == hipSuccess ? SV_OK : SV_ERR_HIP;
   }
@@ -706,6 +708,8 @@ struct AcceptPlan {
 
 sv_status plan_accept(int32_t B, int32_t V, int32_t mode, const int32_t *gamma_host, AcceptPlan &ap) {
   if (B < 0 || V <= 0) return SV_ERR_INVALID_ARG;
+  if (mode & ~(0xFF | SV_ACCEPT_FROM_LOGITS)) return SV_ERR_INVALID_ARG;
+  mode &= 0xFF;
   if (mode != SV_ACCEPT_STOCHASTIC && mode != SV_ACCEPT_GREEDY) return SV_ERR_INVALID_ARG;
   if (B > 0 && !gamma_host) return SV_ERR_INVALID_ARG;
   if (B > kScanMaxB) return SV_ERR_UNSUPPORTED;
@@ -749,6 +753,8 @@ extern "C" sv_status sv_accept_commit(int32_t B, int32_t V, int32_t mode, const 
   if (B == 0) return SV_OK;
   if (!gamma || !p || !kv_len || !accepted || !next_token) return SV_ERR_INVALID_ARG;
   if (ap.nd > 0 && !draft) return SV_ERR_INVALID_ARG;
+  const bool from_logits = (mode & SV_ACCEPT_FROM_LOGITS) != 0;
+  mode &= 0xFF;
   if (mode == SV_ACCEPT_STOCHASTIC) {
     if (!u_samp) return SV_ERR_INVALID_ARG;
     if (ap.nd > 0 && (!q || !u_acc)) return SV_ERR_INVALID_ARG;
@@ -767,6 +773,7 @@ extern "C" sv_status sv_accept_commit(int32_t B, int32_t V, int32_t mode, const 
   a.gamma = gamma;
   a.draft = draft;
   a.p = p;
+  a.row_ms = from_logits ? p + ap.T * (size_t)V : nullptr;
   a.q = q;
   a.u_acc = u_acc;
   a.u_samp = u_samp;

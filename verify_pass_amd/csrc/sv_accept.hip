@@ -40,6 +40,24 @@ __device__ __forceinline__ void amax(float &v, int &i, float v2, int i2) {
   }
 }
 
+// Probabilities of one row as the rule reads them: the entries themselves, or
+// (logits mode) formed from the row's logits and (max, sum) exactly as the
+// head's softmax finish forms them.
+struct PXf {
+  bool on;
+  float Mk, S;
+  __device__ __forceinline__ float operator()(float v) const { return on ? prob_of_logit(v, Mk, S) : v; }
+  __device__ __forceinline__ float4 operator()(float4 v) const {
+    return on ? make_float4(prob_of_logit(v.x, Mk, S), prob_of_logit(v.y, Mk, S), prob_of_logit(v.z, Mk, S),
+                            prob_of_logit(v.w, Mk, S))
+              : v;
+  }
+};
+__device__ __forceinline__ PXf pxf_of(const AcceptParams &p, int row) {
+  if (!p.row_ms) return PXf{false, 0.f, 1.f};
+  return PXf{true, p.row_ms[2 * row] * kLog2eF, p.row_ms[2 * row + 1]};
+}
+
 struct Shared {
   u64 a[kWavesA], b[kWavesA];
   float v[kWavesA];
@@ -146,7 +164,7 @@ __device__ inline int seq_start(const int *gamma, int i, Shared &sh) {
 }
 
 // This thread's share of the argmax of row[x0, x1).
-__device__ inline void chunk_argmax(const float *row, int x0, int x1, bool vec, float &bv, int &bi) {
+__device__ inline void chunk_argmax(const float *row, PXf xf, int x0, int x1, bool vec, float &bv, int &bi) {
   bv = -INFINITY;
   bi = 0x7fffffff;
   if (vec) {
@@ -155,7 +173,7 @@ __device__ inline void chunk_argmax(const float *row, int x0, int x1, bool vec, 
 #pragma unroll
     for (int k = 0; k < kVecA; ++k) {
       const int x = x0 / 4 + threadIdx.x + k * kThreads;
-      v[k] = x < x1 / 4 ? r4[x] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      v[k] = x < x1 / 4 ? xf(r4[x]) : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
     }
 #pragma unroll
     for (int k = 0; k < kVecA; ++k) {
@@ -167,7 +185,7 @@ __device__ inline void chunk_argmax(const float *row, int x0, int x1, bool vec, 
       amax(bv, bi, v[k].w, 4 * x + 3);
     }
   } else {
-    for (int x = x0 + threadIdx.x; x < x1; x += kThreads) amax(bv, bi, row[x], x);
+    for (int x = x0 + threadIdx.x; x < x1; x += kThreads) amax(bv, bi, xf(row[x]), x);
   }
 }
 
@@ -197,7 +215,8 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(AcceptParams p) {
       atomicOr(&sh.bad, 1);
     } else if (!greedy) {
       const float lhs = p.u_acc[dst + j] * p.q[(size_t)(dst + j) * p.V + d];
-      if (!(lhs < p.p[(size_t)(qst + j) * p.V + d])) atomicMin(&sh.first_fail, j);
+      const float pd = pxf_of(p, qst + j)(p.p[(size_t)(qst + j) * p.V + d]);
+      if (!(lhs < pd)) atomicMin(&sh.first_fail, j);
     }
   }
   __syncthreads();
@@ -209,7 +228,7 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(AcceptParams p) {
       for (int j = 0; j <= g; ++j) {
         float bv;
         int bi;
-        chunk_argmax(p.p + (size_t)(qst + j) * p.V, x0, x1, vec, bv, bi);
+        chunk_argmax(p.p + (size_t)(qst + j) * p.V, pxf_of(p, qst + j), x0, x1, vec, bv, bi);
         u64 z0 = 0, z1 = 0;
         block_reduce(z0, z1, bv, bi, sh);
         if (tid == 0) put_part(p.parts + (size_t)(qst + j) * p.nchunk + c, 0ull, 0ull, bv, bi);
@@ -247,6 +266,7 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(AcceptParams p) {
   // ---- stochastic -----------------------------------------------------------
   const int a = sh.first_fail;
   const float *prow = p.p + (size_t)(qst + a) * p.V;
+  const PXf xf = pxf_of(p, qst + a);
   const float *qrow = a < g ? p.q + (size_t)(dst + a) * p.V : nullptr;
   u64 sres = 0, sp = 0;
   float bv = -INFINITY;
@@ -260,7 +280,7 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(AcceptParams p) {
 #pragma unroll
       for (int k = 0; k < kVecA; ++k) {
         const int x = x0 / 4 + tid + k * kThreads;
-        pv[k] = x < x1 / 4 ? p4[x] : make_float4(0.f, 0.f, 0.f, 0.f);
+        pv[k] = x < x1 / 4 ? xf(p4[x]) : make_float4(0.f, 0.f, 0.f, 0.f);
         qv[k] = (qrow && x < x1 / 4) ? q4[x] : make_float4(0.f, 0.f, 0.f, 0.f);
       }
 #pragma unroll
@@ -279,7 +299,7 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(AcceptParams p) {
       }
     } else {
       for (int x = x0 + tid; x < x1; x += kThreads) {
-        const float pv = prow[x];
+        const float pv = xf(prow[x]);
         const u64 w = weight_of(pv);
         sres += qrow ? weight_of(pv - qrow[x]) : w;
         sp += w;
@@ -363,7 +383,7 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(AcceptParams p) {
       float4 pv[kSegMax / 4], qv[kSegMax / 4];
 #pragma unroll
       for (int k = 0; k < kSegMax / 4; ++k) {
-        pv[k] = k < n4 ? p4[k] : make_float4(0.f, 0.f, 0.f, 0.f);
+        pv[k] = k < n4 ? xf(p4[k]) : make_float4(0.f, 0.f, 0.f, 0.f);
         qv[k] = (resid && k < n4) ? q4[k] : make_float4(0.f, 0.f, 0.f, 0.f);
       }
 #pragma unroll
@@ -380,7 +400,7 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(AcceptParams p) {
       for (int k = 0; k < kSegMax; ++k) {
         const int x = lo + k;
         float r = 0.f;
-        if (x < hi) r = resid ? prow[cx0 + x] - qrow[cx0 + x] : prow[cx0 + x];
+        if (x < hi) r = resid ? xf(prow[cx0 + x]) - qrow[cx0 + x] : xf(prow[cx0 + x]);
         wv[k] = r;
         s += weight_of(r);
       }

@@ -185,6 +185,7 @@ struct HeadSoftmaxParams {
   float *logits;        // [T][V] in: logits, out: probabilities
   const float *stats;   // [T][nblk][2]
   int T, V, nblk, cols_per_block;
+  float *row_ms;        // row statistics kernel: [T][2] (max, sum of exp)
 };
 
 struct EmbedParams {
@@ -211,6 +212,7 @@ struct AcceptParams {
   const int *gamma;
   const int *draft;
   const float *p;
+  const float *row_ms;  // non-null: p holds logits, row_ms[row] = (max, sum of exp)
   const float *q;
   const float *u_acc;
   const float *u_samp;
@@ -246,6 +248,14 @@ size_t gemm_partial_floats(int ngroups, int splits, int ntblk, int tok_tiles);
 hipError_t launch_prep(const PrepParams &p, hipStream_t s);
 hipError_t launch_attention(const AttnParams &p, hipStream_t s);
 hipError_t launch_head_softmax(const HeadSoftmaxParams &p, hipStream_t s);
+hipError_t launch_head_rowstats(const HeadSoftmaxParams &p, hipStream_t s);
+
+// Probability of a logit from its row's (max M, sum S), exactly as the head's
+// softmax finish computes it.
+constexpr float kLog2eF = 1.4426950408889634f;
+__device__ __forceinline__ float prob_of_logit(float l, float Mk, float S) {
+  return __builtin_amdgcn_exp2f(fmaf(l, kLog2eF, -Mk)) / S;
+}
 hipError_t launch_embed(const EmbedParams &p, hipStream_t s);
 hipError_t launch_accept(const AcceptParams &p, hipStream_t s);
 

@@ -22,33 +22,17 @@ __device__ __forceinline__ void combine(float &m, float &s, float m2, float s2) 
   }
 }
 
-// p = exp(l - M) / S per row, where M and S combine the per-group statistics
-// (group max m_b, group sum of exp(l - m_b)) that the LM-head GEMM wrote,
-// token-major so that a row's statistics are one contiguous run.  The
-// combination order is fixed, so every column block of a row computes the
-// same M and S.
-__global__ __launch_bounds__(kThreads) void head_softmax_kernel(HeadSoftmaxParams p) {
+// M and S of row t: the per-group statistics (group max m_b, group sum of
+// exp(l - m_b)) that the LM-head GEMM wrote, token-major so that a row's
+// statistics are one contiguous run, combined in a fixed order (every column
+// block of the row, and the row statistics kernel, get the same M and S).
+// Called by all threads of the workgroup.
+__device__ inline void row_stats(const HeadSoftmaxParams &p, int t, float &M, float &S) {
   __shared__ float red_m[kThreads / 64], red_s[kThreads / 64];
-  const int t = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  float *row = p.logits + (size_t)t * p.V;
-  const int c0 = blockIdx.x * p.cols_per_block;
-  const int c1 = min(p.V, c0 + p.cols_per_block);
-  const bool vec = (p.V & 3) == 0;  // rows are 16-byte aligned: four columns per access
-  // this block's logits first: their loads do not depend on the row's M and S
-  // and stay in flight while the statistics are combined
-  float4 *r4 = reinterpret_cast<float4 *>(row);
-  const int e4 = c1 / 4;
-  float4 v[kVec];
-  if (vec) {
-#pragma unroll
-    for (int k = 0; k < kVec; ++k) {
-      const int c = c0 / 4 + tid + k * kThreads;
-      if (c < e4) v[k] = r4[c];
-    }
-  }
-  // the row's statistics, kStat per thread in flight, combined in index order
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const float2 *st = reinterpret_cast<const float2 *>(p.stats) + (size_t)t * p.nblk;
   float m = -INFINITY, s = 0.f;
+  // kStat statistics per thread in flight, combined in index order
   for (int b0 = tid; b0 < p.nblk; b0 += kStat * kThreads) {
     float2 e[kStat];
 #pragma unroll
@@ -69,9 +53,43 @@ __global__ __launch_bounds__(kThreads) void head_softmax_kernel(HeadSoftmaxParam
     red_s[w] = s;
   }
   __syncthreads();
-  float M = red_m[0], S = red_s[0];
+  M = red_m[0];
+  S = red_s[0];
 #pragma unroll
   for (int k = 1; k < kThreads / 64; ++k) combine(M, S, red_m[k], red_s[k]);
+}
+
+// Row statistics only (logits stay as they are): one workgroup per row.
+__global__ __launch_bounds__(kThreads) void head_rowstats_kernel(HeadSoftmaxParams p) {
+  float M, S;
+  row_stats(p, blockIdx.x, M, S);
+  if (threadIdx.x == 0) {
+    p.row_ms[2 * blockIdx.x] = M;
+    p.row_ms[2 * blockIdx.x + 1] = S;
+  }
+}
+
+// p = exp(l - M) / S per row (row_stats), in place.
+__global__ __launch_bounds__(kThreads) void head_softmax_kernel(HeadSoftmaxParams p) {
+  const int t = blockIdx.y, tid = threadIdx.x;
+  float *row = p.logits + (size_t)t * p.V;
+  const int c0 = blockIdx.x * p.cols_per_block;
+  const int c1 = min(p.V, c0 + p.cols_per_block);
+  const bool vec = (p.V & 3) == 0;  // rows are 16-byte aligned: four columns per access
+  // this block's logits first: their loads do not depend on the row's M and S
+  // and stay in flight while the statistics are combined
+  float4 *r4 = reinterpret_cast<float4 *>(row);
+  const int e4 = c1 / 4;
+  float4 v[kVec];
+  if (vec) {
+#pragma unroll
+    for (int k = 0; k < kVec; ++k) {
+      const int c = c0 / 4 + tid + k * kThreads;
+      if (c < e4) v[k] = r4[c];
+    }
+  }
+  float M, S;
+  row_stats(p, t, M, S);
 
   const float Mk = M * kLog2e;
   if (vec) {
@@ -80,16 +98,16 @@ __global__ __launch_bounds__(kThreads) void head_softmax_kernel(HeadSoftmaxParam
       const int c = c0 / 4 + tid + k * kThreads;
       if (c < e4) {
         float4 o;
-        o.x = __builtin_amdgcn_exp2f(fmaf(v[k].x, kLog2e, -Mk)) / S;
-        o.y = __builtin_amdgcn_exp2f(fmaf(v[k].y, kLog2e, -Mk)) / S;
-        o.z = __builtin_amdgcn_exp2f(fmaf(v[k].z, kLog2e, -Mk)) / S;
-        o.w = __builtin_amdgcn_exp2f(fmaf(v[k].w, kLog2e, -Mk)) / S;
+        o.x = prob_of_logit(v[k].x, Mk, S);
+        o.y = prob_of_logit(v[k].y, Mk, S);
+        o.z = prob_of_logit(v[k].z, Mk, S);
+        o.w = prob_of_logit(v[k].w, Mk, S);
         r4[c] = o;
       }
     }
   } else {
     for (int c = c0 + tid; c < c1; c += kThreads)
-      row[c] = __builtin_amdgcn_exp2f(fmaf(row[c], kLog2e, -Mk)) / S;
+      row[c] = prob_of_logit(row[c], Mk, S);
   }
 }
 
@@ -118,6 +136,13 @@ hipError_t launch_head_softmax(const HeadSoftmaxParams &p, hipStream_t s) {
   const dim3 grid((p.V + p.cols_per_block - 1) / p.cols_per_block, p.T);
   trace_before(SV_K_SOFTMAX, s);
   hipLaunchKernelGGL(head_softmax_kernel, grid, dim3(kThreads), 0, s, p);
+  trace_after(SV_K_SOFTMAX, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_head_rowstats(const HeadSoftmaxParams &p, hipStream_t s) {
+  trace_before(SV_K_SOFTMAX, s);
+  hipLaunchKernelGGL(head_rowstats_kernel, dim3(p.T), dim3(kThreads), 0, s, p);
   trace_after(SV_K_SOFTMAX, s);
   return hipGetLastError();
 }
