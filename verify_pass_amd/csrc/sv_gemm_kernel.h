@@ -513,14 +513,25 @@ template <int WT, int TT, int G, int KW> constexpr int min_wg_per_cu() {
   return (KW == 1 && WT == WT_BF16 && TT <= 2 && G <= 2) ? 6 : 1;
 }
 
+// Largest number of partial sums of squares per token (the previous
+// projection's row groups) that the gate||up launch stages in LDS.
+constexpr int kRsPartsMax = 160;
+
 template <int WT, int TT, int EPI, int G, int KW>
 __global__ __launch_bounds__(64 * waves_per_wg<KW>(), (min_wg_per_cu<WT, TT, G, KW>())) void gemm_kernel(
     GemmParams p) {
   constexpr int WV = waves_per_wg<KW>();
   constexpr int UPW = WV / KW;  // units per workgroup
   constexpr int NACC = 2 * TT * 4;
+  // gate||up with several waves per unit: the token block's rows of partial
+  // sums of squares ([T][nparts], from the previous projection) are copied
+  // straight into LDS when the workgroup starts, so the epilogue forms the
+  // RMSNorm scales from LDS instead of a scattered global round trip at the end
+  constexpr bool kRsl = EPI == EPI_SWIGLU && KW > 1 && TT <= 2;
+  constexpr int kRslI = kRsl ? (TT * 16 * kRsPartsMax / 4 + 64 * WV - 1) / (64 * WV) : 1;
   __shared__ float kred[KW > 1 ? WV * NACC * 64 : 1];
   __shared__ __align__(16) unsigned char xl[KW == 1 ? xl_bytes<WT, TT, G>() : 16];
+  __shared__ __align__(16) float rsl[kRsl ? kRslI * WV * 64 * 4 : 4];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = wave % KW, slot = wave / KW;
@@ -582,6 +593,26 @@ __global__ __launch_bounds__(64 * waves_per_wg<KW>(), (min_wg_per_cu<WT, TT, G, 
   float ssq[TT];  // rms_inline: this lane's share of its tokens' sums of squares
 #pragma unroll
   for (int tt = 0; tt < TT; ++tt) ssq[tt] = 0.f;
+
+  bool rs_lds = false;
+  if constexpr (kRsl) {
+    // row tok of the block (token min(t0 + tok, T - 1)) at rsl[tok * nparts];
+    // 16-byte pieces in lane order, every lane loading (past the rows' end it
+    // repeats the last piece into space nobody reads); without partial sums
+    // the loads read the token operand and the result is unused
+    rs_lds = p.rparts && !p.rnorm && (p.nparts & 3) == 0 && p.nparts > 0 && p.nparts <= kRsPartsMax;
+    const int q4 = rs_lds ? p.nparts >> 2 : 1;
+    const int nch = TT * 16 * q4;
+#pragma unroll
+    for (int i = 0; i < kRslI; ++i) {
+      const int cb = (i * WV + wave) * 64;
+      const int c = min(cb + lane, nch - 1);
+      const int tok = c / q4, q = c - tok * q4;
+      const void *src = rs_lds ? static_cast<const void *>(p.rparts + (size_t)min(t0 + tok, p.T - 1) * p.nparts + 4 * q)
+                               : static_cast<const void *>(p.x);
+      load_lds16(src, rsl + cb * 4);
+    }
+  }
 
   // Grouped prefetch: G steps of weights and tokens in flight per wave, then
   // compute.  A shallow group keeps the register count low, so many waves are
@@ -678,6 +709,7 @@ __global__ __launch_bounds__(64 * waves_per_wg<KW>(), (min_wg_per_cu<WT, TT, G, 
 
   // ---- in-workgroup reduction of the unit's K pieces ------------------------
   if constexpr (KW > 1) {
+    if constexpr (kRsl) wait_vmem();  // this wave's copies into rsl (the barrier publishes them)
     if (sub != 0) {
 #pragma unroll
       for (int a = 0; a < 2; ++a)
@@ -712,6 +744,21 @@ __global__ __launch_bounds__(64 * waves_per_wg<KW>(), (min_wg_per_cu<WT, TT, G, 
       sq += __shfl_xor(sq, 16);
       sq += __shfl_xor(sq, 32);
       rs[tt] = 1.f / sqrtf(sq / static_cast<float>(p.K) + p.eps);
+    }
+    epilogue_rs<TT, EPI>(p, acc, grp, t0, gq, l16, rs);
+  } else if (kRsl && rs_lds) {
+    // the same partial sums in the same order as token_scales, from LDS
+    float rs[TT];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      const int tok = min(t0 + tt * 16 + l16, p.T - 1) - t0;
+      const float *pr = rsl + tok * p.nparts;
+      float s = 0.f;
+#pragma unroll 8
+      for (int g = gq; g < p.nparts; g += 4) s += pr[g];
+      s += __shfl_xor(s, 16);
+      s += __shfl_xor(s, 32);
+      rs[tt] = 1.f / sqrtf(s / static_cast<float>(p.K) + p.eps);
     }
     epilogue_rs<TT, EPI>(p, acc, grp, t0, gq, l16, rs);
   } else {
