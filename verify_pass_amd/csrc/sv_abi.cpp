@@ -274,9 +274,19 @@ GemmCfg gemm_cfg(int kind, int nblk, int N, int T, int K, int wtype, bool packed
   return c;
 }
 
+// Token operands in fragment layout: the bf16 streaming launches with several
+// waves per unit read them as contiguous KiB fragments (tiles = ntblk * tt).
+bool frag_input(const GemmCfg &c, int wtype) {
+  return wtype == SV_W_BF16 && (c.kw == 4 || c.kw == 8 || c.kw == 16);
+}
+int frag_tiles(const GemmCfg &c) { return c.ntblk * c.tt; }
+size_t frag_bytes(const GemmCfg &c) { return (size_t)(c.K / 64) * frag_tiles(c) * 2048; }
+
 struct LayerPlan {
   int T = 0, B = 0, G = 1, gmax = 0;
   GemmCfg qkv, o, gu, down, head;
+  bool pk_qkv = false, pk_o = false, pk_gu = false, pk_down = false;
+  size_t off_xp = 0, off_x1p = 0;
   int attn_chunk = 256, attn_items = 0, attn_rpad = 16;
   size_t off_counters = 0, off_partial = 0, off_qbuf = 0, off_po = 0, off_pml = 0;
   size_t off_attn = 0, off_x1 = 0, off_act = 0, off_stats = 0, off_items = 0;
@@ -389,6 +399,10 @@ sv_status plan_layer(const sv_layer *L, const sv_batch *b, int32_t flags, LayerP
   if (items > (1 << 30)) return SV_ERR_UNSUPPORTED;
   pl.attn_items = (int)items;
 
+  pl.pk_qkv = frag_input(pl.qkv, w);
+  pl.pk_o = frag_input(pl.o, w);
+  pl.pk_gu = frag_input(pl.gu, w);
+  pl.pk_down = frag_input(pl.down, w);
   size_t partial = 0;
   for (const GemmCfg *g : {&pl.qkv, &pl.o, &pl.gu, &pl.down}) partial = std::max(partial, g->partial_floats());
   pl.off_counters = take(kCounterBytes);
@@ -396,9 +410,11 @@ sv_status plan_layer(const sv_layer *L, const sv_batch *b, int32_t flags, LayerP
   pl.off_qbuf = take((size_t)pl.T * hq * hd * 2);
   pl.off_po = take((size_t)pl.attn_items * hk * pl.attn_rpad * hd * sizeof(float));
   pl.off_pml = take((size_t)pl.attn_items * hk * pl.attn_rpad * 2 * sizeof(float));
-  pl.off_attn = take((size_t)pl.T * hq * hd * 2);
+  pl.off_attn = take(std::max((size_t)pl.T * hq * hd * 2, pl.pk_o ? frag_bytes(pl.o) : 0));
   pl.off_x1 = take((size_t)pl.T * d * 2);
-  pl.off_act = take((size_t)pl.T * F * 2);
+  pl.off_act = take(std::max((size_t)pl.T * F * 2, pl.pk_down ? frag_bytes(pl.down) : 0));
+  pl.off_xp = take(pl.pk_qkv ? frag_bytes(pl.qkv) : 0);
+  pl.off_x1p = take(pl.pk_gu ? frag_bytes(pl.gu) : 0);
   pl.off_rnorm = take((size_t)pl.T * sizeof(float));
   pl.off_rparts = take((size_t)pl.o.nblk * pl.T * sizeof(float));
   pl.off_tseq = take((size_t)pl.T * sizeof(int));
@@ -556,6 +572,8 @@ extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const
     pp.hd = hd;
     pp.items = reinterpret_cast<int4 *>(ws + pl.off_items);
     pp.max_items = pl.attn_items;
+    pp.xp = pl.pk_qkv ? reinterpret_cast<uint16_t *>(ws + pl.off_xp) : nullptr;
+    pp.xp_ntt = frag_tiles(pl.qkv);
     pp.err = b->err_flag;
     for (int i = 0; i < hd / 2; ++i)
       pp.inv_freq[i] = std::pow(static_cast<double>(L->rope_theta), -2.0 * i / hd);
@@ -564,6 +582,10 @@ extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const
   }
   {  // QKV + RoPE + KV append
     GemmParams p = base_params(pl.qkv, x_in, pl.T, wt, ws, pl);
+    if (pl.pk_qkv) {
+      p.xp = reinterpret_cast<const uint16_t *>(ws + pl.off_xp);
+      p.xp_ntt = frag_tiles(pl.qkv);
+    }
     p.rnorm = rnorm;
     p.packed = L->layout == SV_LAYOUT_PACKED;
     p.nmat = 3;
@@ -609,6 +631,7 @@ extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const
     a.part_o = reinterpret_cast<float *>(ws + pl.off_po);
     a.part_ml = reinterpret_cast<float *>(ws + pl.off_pml);
     a.out = attn;
+    a.out_ntt = pl.pk_o ? frag_tiles(pl.o) : 0;
     a.counters = reinterpret_cast<int *>(ws + pl.off_counters);
     a.err = b->err_flag;
     e = launch_attention(a, s);
@@ -616,6 +639,14 @@ extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const
   }
   {  // O projection + residual
     GemmParams p = base_params(pl.o, attn, pl.T, wt, ws, pl);
+    if (pl.pk_o) {
+      p.xp = attn;
+      p.xp_ntt = frag_tiles(pl.o);
+    }
+    if (pl.pk_gu) {  // the gate||up token operand, besides x1 itself
+      p.out_pk = reinterpret_cast<uint16_t *>(ws + pl.off_x1p);
+      p.out_pk_ntt = frag_tiles(pl.gu);
+    }
     p.packed = L->layout == SV_LAYOUT_PACKED;
     p.nmat = 1;
     p.mat[0] = mat_of(L->wo, d);
@@ -630,6 +661,14 @@ extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const
   }
   {  // gate || up + SwiGLU
     GemmParams p = base_params(pl.gu, x1, pl.T, wt, ws, pl);
+    if (pl.pk_gu) {
+      p.xp = reinterpret_cast<const uint16_t *>(ws + pl.off_x1p);
+      p.xp_ntt = frag_tiles(pl.gu);
+    }
+    if (pl.pk_down) {  // act only feeds the down projection
+      p.out_pk = act;
+      p.out_pk_ntt = frag_tiles(pl.down);
+    }
     p.packed = L->layout == SV_LAYOUT_PACKED;
     p.nmat = 2;
     p.mat[0] = mat_of(L->w_gate, F);
@@ -646,6 +685,10 @@ extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const
   }
   {  // down projection + residual
     GemmParams p = base_params(pl.down, act, pl.T, wt, ws, pl);
+    if (pl.pk_down) {
+      p.xp = act;
+      p.xp_ntt = frag_tiles(pl.down);
+    }
     p.packed = L->layout == SV_LAYOUT_PACKED;
     p.nmat = 1;
     p.mat[0] = mat_of(L->w_down, d);

@@ -166,8 +166,9 @@ __device__ void publish_merge(const AttnParams &p, int qst, int first, int nch, 
       const int r = q / NP, d2 = q - r * NP;
       const int hg = r / n1, j = r - hg * n1;
       const int t = qst + j;
-      *reinterpret_cast<uint32_t *>(p.out + ((size_t)t * p.hq + g * G + hg) * HD + 2 * d2) =
-          f2bf(acc[u].x) | ((uint32_t)f2bf(acc[u].y) << 16);
+      const int k = (g * G + hg) * HD + 2 * d2;
+      const size_t o = p.out_ntt > 0 ? frag_index(t, k, p.out_ntt) : (size_t)t * p.hq * HD + k;
+      *reinterpret_cast<uint32_t *>(p.out + o) = f2bf(acc[u].x) | ((uint32_t)f2bf(acc[u].y) << 16);
     }
   }
 }

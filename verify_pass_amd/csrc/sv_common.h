@@ -37,6 +37,18 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4 &v) {
 }
 
 // ---------------------------------------------------------------------------
+// Fragment layout of a bf16 activation matrix [T][K] (the token operand of the
+// short-projection GEMMs): for each K step s of 64 and 16-token tile, two
+// 1 KiB fragments m = 0, 1 in MFMA lane order, lane (gq, l16) holding the
+// eight values x[16 tile + l16][64 s + 32 m + 8 gq ..]; ntt tiles per step.
+// A wave then loads each fragment as one contiguous 1 KiB access instead of
+// sixteen 64-byte row pieces.
+__host__ __device__ inline size_t frag_index(int t, int k, int ntt) {
+  const int s = k >> 6, m = (k >> 5) & 1, gq = (k >> 3) & 3, e = k & 7;
+  return ((((size_t)s * ntt + (t >> 4)) * 2 + m) * 64 + gq * 16 + (t & 15)) * 8 + e;
+}
+
+// ---------------------------------------------------------------------------
 // Block-level helpers (blockDim.x == 256).
 
 // In-place exclusive prefix sum of n (<= 65536) ints in LDS; returns the total.
@@ -106,6 +118,10 @@ struct GemmMat {
 
 struct GemmParams {
   const uint16_t *x;  // activations bf16 [T][K]
+  const uint16_t *xp; // the same in fragment layout (ntt = xp_ntt), or nullptr
+  int xp_ntt;
+  uint16_t *out_pk;   // EPI_RESID: also write the output in fragment layout;
+  int out_pk_ntt;     // EPI_SWIGLU: write it only in fragment layout (nullptr: row-major)
   int T, K, N;        // N = logical rows
   int nmat;
   GemmMat mat[3];
@@ -156,6 +172,8 @@ struct PrepParams {
   int hd;
   int4 *items;         // [max_items][2] attention work items (see AttnParams)
   int max_items;
+  uint16_t *xp;        // x in fragment layout for the QKV GEMM (nullptr: none)
+  int xp_ntt;
   int *err;
   double inv_freq[64]; // theta^(-2i/hd), i < hd/2 (evaluated on the host in fp64)
 };
@@ -176,7 +194,8 @@ struct AttnParams {
   float scale_log2; // log2(e) / sqrt(hd)
   float *part_o;    // [max_items][hkv][rpad][hd]
   float *part_ml;   // [max_items][hkv][rpad][2]
-  uint16_t *out;    // [T][hq*hd]
+  uint16_t *out;    // [T][hq*hd], or in fragment layout when out_ntt > 0
+  int out_ntt;
   int *counters;    // [B][hkv] arrival counters, zero between launches
   int *err;
 };

@@ -326,12 +326,14 @@ __device__ __forceinline__ void epilogue_rs(const GemmParams &p, floatx4 (&acc)[
               sq += hv[i] * hv[i];
             }
             st_bf16x4(out + o, hv);
+            if (p.out_pk) st_bf16x4(p.out_pk + frag_index(t, n0, p.out_pk_ntt), hv);
           } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               if (n0 + i < p.N) {
                 const uint16_t h = f2bf(acc[a][tt][i] * rs[tt] + bf2f(p.resid[o + i]));
                 out[o + i] = h;
+                if (p.out_pk) p.out_pk[frag_index(t, n0 + i, p.out_pk_ntt)] = h;
                 const float f = bf2f(h);
                 sq += f * f;
               }
@@ -358,6 +360,16 @@ __device__ __forceinline__ void epilogue_rs(const GemmParams &p, floatx4 (&acc)[
         const float g = acc[0][tt][i] * rs[tt], u = acc[1][tt][i] * rs[tt];
         const float sig = 1.f / (1.f + __builtin_amdgcn_exp2f(-g * kLog2e));
         hv[i] = g * sig * u;
+      }
+      if (p.out_pk) {  // fragment layout only (the down projection's token operand)
+        if (f0 + 3 < p.mat[0].rows) {
+          st_bf16x4(p.out_pk + frag_index(t, f0, p.out_pk_ntt), hv);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (f0 + i < p.mat[0].rows) p.out_pk[frag_index(t, f0 + i, p.out_pk_ntt)] = f2bf(hv[i]);
+        }
+        continue;
       }
       uint16_t *o = out + (size_t)t * p.ldo + f0;
       if (vec && f0 + 3 < p.mat[0].rows) {
@@ -683,6 +695,21 @@ __global__ __launch_bounds__(64 * waves_per_wg<KW>(), (min_wg_per_cu<WT, TT, G, 
     }
     if (!active) return;
   } else {
+    // bf16 token fragments: row-major rows (sixteen 64-byte pieces per load) or
+    // the fragment layout (one contiguous KiB); both affine in the step
+    const uint16_t *xb[TT];
+    int xstride = 64, xoff1 = 32;
+    if constexpr (WT == WT_BF16) {
+      if (p.xp) {
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) xb[tt] = p.xp + (size_t)(tb * TT + tt) * 1024 + lane * 8;
+        xstride = p.xp_ntt * 1024;
+        xoff1 = 512;
+      } else {
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) xb[tt] = xr[tt] + 8 * gq;
+      }
+    }
     for (int base = 0; base < nsteps; base += G) {
       WStep<WT> wbuf[G][2];
       XStep<WT> xbuf[G][TT];
@@ -692,7 +719,15 @@ __global__ __launch_bounds__(64 * waves_per_wg<KW>(), (min_wg_per_cu<WT, TT, G, 
 #pragma unroll
         for (int tile = 0; tile < 2; ++tile) wbuf[j][tile] = load_w<WT>(src[tile], st);
 #pragma unroll
-        for (int tt = 0; tt < TT; ++tt) xbuf[j][tt] = load_x<WT>(xr[tt], st, gq);
+        for (int tt = 0; tt < TT; ++tt) {
+          if constexpr (WT == WT_BF16) {
+            const uint16_t *b = xb[tt] + (size_t)st * xstride;
+            xbuf[j][tt].v[0] = *reinterpret_cast<const uint4 *>(b);
+            xbuf[j][tt].v[1] = *reinterpret_cast<const uint4 *>(b + xoff1);
+          } else {
+            xbuf[j][tt] = load_x<WT>(xr[tt], st, gq);
+          }
+        }
       }
 #pragma unroll
       for (int j = 0; j < G; ++j) {

@@ -1,4 +1,5 @@
-// Per-call preparation pass: RMSNorm scales of the input rows and the token map.
+// Per-call preparation pass: RMSNorm scales of the input rows and the token map
+// (and, when asked, a copy of the input rows in fragment layout).
 //
 // One workgroup per stacked token t:
 //   r[t] = 1 / sqrt(mean(x[t]^2) + eps), summed in a fixed order;
@@ -28,6 +29,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams p) {
   float s = 0.f;
   for (int c = tid * 8; c < p.d; c += kThreads * 8) {
     const uint4 v = *reinterpret_cast<const uint4 *>(row + c);
+    if (p.xp) *reinterpret_cast<uint4 *>(p.xp + frag_index(t, c, p.xp_ntt)) = v;
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
