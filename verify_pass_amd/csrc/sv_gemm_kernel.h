@@ -521,8 +521,8 @@ __device__ __forceinline__ bool split_reduce(const GemmParams &p, floatx4 (&acc)
 // wave order (bitwise repeatable) before the epilogue, which the unit's first
 // wave runs.  This fills the chip for short row counts without sending
 // partial sums through memory.
-template <int WT, int TT, int G, int KW> constexpr int min_wg_per_cu() {
-  return (KW == 1 && WT == WT_BF16 && TT <= 2 && G <= 2) ? 6 : 1;
+template <int WT, int TT, int EPI, int G, int KW> constexpr int min_wg_per_cu() {
+  return (KW == 1 && WT == WT_BF16 && EPI == EPI_LOGITS && TT <= 2 && G <= 2) ? 6 : 1;
 }
 
 // Largest number of partial sums of squares per token (the previous
@@ -530,7 +530,7 @@ template <int WT, int TT, int G, int KW> constexpr int min_wg_per_cu() {
 constexpr int kRsPartsMax = 160;
 
 template <int WT, int TT, int EPI, int G, int KW>
-__global__ __launch_bounds__(64 * waves_per_wg<KW>(), (min_wg_per_cu<WT, TT, G, KW>())) void gemm_kernel(
+__global__ __launch_bounds__(64 * waves_per_wg<KW>(), (min_wg_per_cu<WT, TT, EPI, G, KW>())) void gemm_kernel(
     GemmParams p) {
   constexpr int WV = waves_per_wg<KW>();
   constexpr int UPW = WV / KW;  // units per workgroup
