@@ -233,9 +233,14 @@ GemmCfg gemm_cfg(int kind, int nblk, int N, int T, int K, int wtype, bool packed
   const bool tiled_ok = wtype == SV_W_BF16 && packed;
   const long long tiled_wgs = (long long)((nblk + 7) / 8) * ((T + 127) / 128);
   const long long square_wgs = (long long)((nblk + 7) / 8) * ((T + 255) / 256);
-  if (tiled_ok && T > 256 && square_wgs >= 1024) {
-    // hundreds of tokens and at least four rounds of 256 x 256 tiles (the LM
-    // head from 512 tokens): the square-tiled kernel (measured 10-14% faster)
+  // both kernels run one workgroup per CU; a 256 x 256 tile measured about
+  // 1.75x the time of a 256 x 128 one (LM head, 1024 tokens: 129 vs 74 us per
+  // round of 256 workgroups), so the square kernel wins when its rounds of
+  // tiles take less time than the tiled kernel's
+  const long long r_sq = (square_wgs + 255) / 256, r_t = (tiled_wgs + 255) / 256;
+  if (tiled_ok && T > 256 && 7 * r_sq < 4 * r_t) {
+    // hundreds of tokens: the square-tiled kernel (the LM head from 512
+    // tokens, gate||up and QKV at 2048)
     c.kw = kGemmSquare;
     c.splits = 1;
   } else if (tiled_ok && T > 48 && tiled_wgs >= 256) {
@@ -674,8 +679,16 @@ extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const
     p.mat[0] = mat_of(L->w_gate, F);
     p.mat[1] = mat_of(L->w_up, F);
     p.rowmap = RM_SWIGLU;
-    p.rparts = rparts;
-    p.nparts = pl.o.nblk;
+    if (rs_parts_in_gemm(pl.gu.kw, pl.gu.tt, pl.o.nblk)) {
+      p.rparts = rparts;  // staged in LDS by the GEMM itself
+      p.nparts = pl.o.nblk;
+    } else {
+      // one scale per token first (the tiled kernels would otherwise gather the
+      // partials once per lane and token tile)
+      e = launch_rnorm_parts(rparts, pl.o.nblk, pl.T, d, L->eps, rnorm, s);
+      if (e != hipSuccess) return SV_ERR_HIP;
+      p.rnorm = rnorm;
+    }
     p.eps = L->eps;
     p.epi = EPI_SWIGLU;
     p.out = act;

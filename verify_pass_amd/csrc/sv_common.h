@@ -265,6 +265,9 @@ hipError_t launch_pack(int wtype, int N, int K, const void *w, const void *scale
 // Workspace floats for the K-split partial tiles of one GEMM launch.
 size_t gemm_partial_floats(int ngroups, int splits, int ntblk, int tok_tiles);
 hipError_t launch_prep(const PrepParams &p, hipStream_t s);
+// rnorm[t] = 1 / sqrt(sum of parts[t][0 .. nparts) / K + eps)
+hipError_t launch_rnorm_parts(const float *parts, int nparts, int T, int K, float eps, float *rnorm,
+                              hipStream_t s);
 hipError_t launch_attention(const AttnParams &p, hipStream_t s);
 hipError_t launch_head_softmax(const HeadSoftmaxParams &p, hipStream_t s);
 hipError_t launch_head_rowstats(const HeadSoftmaxParams &p, hipStream_t s);
@@ -292,6 +295,15 @@ constexpr bool gemm_kw_ok(int wt, int tt, int kw) {
   return wt == WT_BF16   ? (kw <= 8 || tt <= 2)
          : wt == WT_INT4 ? (kw <= 4 || (kw == 8 && tt <= 2) || (kw == 16 && tt == 1))
                          : kw <= 8;
+}
+
+// Largest number of partial sums of squares per token (the previous
+// projection's row groups) that a gate||up launch with several waves per unit
+// stages in LDS (four-aligned counts, up to two token tiles); other gate||up
+// launches take the scales from a separate reduction pass.
+constexpr int kRsPartsMax = 160;
+inline bool rs_parts_in_gemm(int kw, int tt, int nparts) {
+  return kw > 1 && tt <= 2 && nparts > 0 && nparts % 4 == 0 && nparts <= kRsPartsMax;
 }
 
 // Step sizes along K per weight type.

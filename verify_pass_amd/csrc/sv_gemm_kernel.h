@@ -525,9 +525,6 @@ template <int WT, int TT, int EPI, int G, int KW> constexpr int min_wg_per_cu() 
   return (KW == 1 && WT == WT_BF16 && EPI == EPI_LOGITS && TT <= 2 && G <= 2) ? 6 : 1;
 }
 
-// Largest number of partial sums of squares per token (the previous
-// projection's row groups) that the gate||up launch stages in LDS.
-constexpr int kRsPartsMax = 160;
 
 template <int WT, int TT, int EPI, int G, int KW>
 __global__ __launch_bounds__(64 * waves_per_wg<KW>(), (min_wg_per_cu<WT, TT, EPI, G, KW>())) void gemm_kernel(

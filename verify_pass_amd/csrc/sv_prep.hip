@@ -111,7 +111,32 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams p) {
   }
 }
 
+// RMSNorm scales from per-row-group partial sums of squares ([T][nparts], as
+// the residual epilogue writes them): one wave per token, the partials added
+// in the same order as the GEMM epilogue adds them when it reads them itself
+// (lane group gq takes partials gq, gq + 4, ..., then the four groups).
+__global__ __launch_bounds__(kThreads) void rnorm_parts_kernel(const float *parts, int nparts, int T, int K,
+                                                               float eps, float *rnorm) {
+  const int t = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int gq = (threadIdx.x & 63) >> 4;
+  const float *pr = parts + (size_t)t * nparts;
+  float s = 0.f;
+  for (int g = gq; g < nparts; g += 4) s += pr[g];
+  s += __shfl_xor(s, 16);
+  s += __shfl_xor(s, 32);
+  if ((threadIdx.x & 63) == 0) rnorm[t] = 1.f / sqrtf(s / static_cast<float>(K) + eps);
+}
+
 }  // namespace
+
+hipError_t launch_rnorm_parts(const float *parts, int nparts, int T, int K, float eps, float *rnorm,
+                              hipStream_t s) {
+  trace_before(SV_K_PREP, s);
+  hipLaunchKernelGGL(rnorm_parts_kernel, dim3((T + 3) / 4), dim3(kThreads), 0, s, parts, nparts, T, K, eps, rnorm);
+  trace_after(SV_K_PREP, s);
+  return hipGetLastError();
+}
 
 hipError_t launch_prep(const PrepParams &p, hipStream_t s) {
   const size_t lds = p.gamma ? (size_t)(2 * (p.B + 1) + 260) * sizeof(int) : 0;
