@@ -20,6 +20,9 @@
 // in LDS; each chunk's (o, max, sum) is published with device-scope stores,
 // and the last chunk of a (sequence, KV head) to arrive merges all of them by
 // log-sum-exp and writes the output rows.
+#include <type_traits>
+#include <utility>
+
 #include "sv_common.h"
 
 namespace sv {
@@ -41,6 +44,11 @@ __device__ __forceinline__ float load_dev(const float *p) {
   return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Element (stacked row t, column k of [T][hq * hd]) of the attention output.
+__device__ __forceinline__ size_t out_offset(const AttnParams &p, int t, int k) {
+  return p.out_ntt > 0 ? frag_index(t, k, p.out_ntt) : (size_t)t * p.hq * p.hd + k;
+}
 
 // One step's operands, loaded in two parts so that keys and values are not
 // live at the same time: keys (MFMA row m of key tile kt is key
@@ -166,9 +174,8 @@ __device__ void publish_merge(const AttnParams &p, int qst, int first, int nch, 
       const int r = q / NP, d2 = q - r * NP;
       const int hg = r / n1, j = r - hg * n1;
       const int t = qst + j;
-      const int k = (g * G + hg) * HD + 2 * d2;
-      const size_t o = p.out_ntt > 0 ? frag_index(t, k, p.out_ntt) : (size_t)t * p.hq * HD + k;
-      *reinterpret_cast<uint32_t *>(p.out + o) = f2bf(acc[u].x) | ((uint32_t)f2bf(acc[u].y) << 16);
+      *reinterpret_cast<uint32_t *>(p.out + out_offset(p, t, (g * G + hg) * HD + 2 * d2)) =
+          f2bf(acc[u].x) | ((uint32_t)f2bf(acc[u].y) << 16);
     }
   }
 }
@@ -335,12 +342,21 @@ __global__ __launch_bounds__(kThreads, (RT == 1 ? 4 : RT <= 3 ? 2 : 1)) void att
         acc += red_o[(w * HD + d) * 16 + row] * f;
         lt += red_ml[(w * 16 + row) * 2 + 1] * f;
       }
+      if (ib.w == 1) {
+        // the sequence's keys are this one item: its rows are the output (as
+        // the merge of one chunk computes them: o * (1 / l))
+        const int rr = rt * 16 + row, hg = rr / n1, j = rr - hg * n1;
+        const float il = lt > 0.f ? 1.f / lt : 0.f;
+        p.out[out_offset(p, qst + j, (g * G + hg) * HD + d)] = f2bf(acc * il);
+        continue;
+      }
       store_dev(p.part_o + (prow + row) * HD + d, acc);
       if (d == 0) store_dev2(p.part_ml + (prow + row) * 2, M, lt);
     }
     __syncthreads();
   }
 
+  if (ib.w == 1) return;
   publish_merge<HD>(p, qst, ib.z, ib.w, seq, g, R, n1, G, flag, red_o);  // red_o is free again
 }
 
@@ -351,8 +367,21 @@ __global__ __launch_bounds__(kThreads, (RT == 1 ? 4 : RT <= 3 ? 2 : 1)) void att
 // combine is needed.  Each 32-key step's keys and values are loaded once per
 // workgroup straight into LDS in MFMA fragment order (lane l's 16 bytes of
 // fragment f at f * 1 KiB + 16 l, read back conflict-free), through a ring of
-// three steps so that two are in flight while one is computed.
+// three steps so that two are in flight while one is computed.  Each ring slot
+// is an LDS object of its own and the step loop is unrolled over the slots
+// with no conditional loads: the compiler can then tell that the LDS reads of
+// one slot do not alias the direct-to-LDS loads still landing in the others,
+// and does not wait for every outstanding load before each step.
 constexpr int kQtStages = 3;
+
+// f(std::integral_constant<int, k>()) for k = 0 .. N-1
+template <class Fn, int... K>
+__device__ __forceinline__ void static_for_impl(Fn &&f, std::integer_sequence<int, K...>) {
+  (f(std::integral_constant<int, K>()), ...);
+}
+template <int N, class Fn> __device__ __forceinline__ void static_for(Fn &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>());
+}
 
 __device__ __forceinline__ void load_lds16(const void *g, void *lds) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
@@ -373,9 +402,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_qt_kernel(AttnParams p) {
   constexpr int FW = F / 4;          // fragments each wave loads per step
   constexpr int SLOT = F * 1024;
   static_assert(F % 4 == 0, "fragments must split evenly over the four waves");
-  extern __shared__ __align__(16) unsigned char smem[];
-  unsigned char *ring = smem;
-  int *flag = reinterpret_cast<int *>(smem + kQtStages * SLOT);
+  static_assert(kQtStages == 3, "three ring slots");
+  __shared__ __align__(16) unsigned char ring0[SLOT], ring1[SLOT], ring2[SLOT];
+  // the merge's per-(chunk, row) weights: up to 32 chunks x 64 rows x 2 floats
+  // (in the first ring slot when it is large enough)
+  constexpr int kMw = 32 * 64 * 2;
+  __shared__ float mw_own[kMw * 4 > SLOT ? kMw : 1];
+  __shared__ int flag[4];
+  auto slot_of = [&](auto kc) -> unsigned char * {
+    constexpr int k = decltype(kc)::value;
+    if constexpr (k == 0) return ring0;
+    else if constexpr (k == 1) return ring1;
+    else return ring2;
+  };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -422,9 +461,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_qt_kernel(AttnParams p) {
   // lane rows are keys k0 + 8 (l16 / 4) + 4 kt + l16 % 4 (clamped to the
   // sequence), or values dt = f - 2 NDG (head-dim column 16 dt + l16, keys
   // k0 + 8 gq ..; the 32-key block lies inside the cache)
-  auto issue = [&](int st) {
-    const int k0 = kb + st * kKeysPerStep;
-    unsigned char *slot = ring + (st % kQtStages) * SLOT;
+  // steps past the last reload it (clamped): every step issues the same loads
+  auto issue = [&](int st, auto kc) {
+    const int k0 = kb + min(st, ns - 1) * kKeysPerStep;
+    unsigned char *slot = slot_of(kc);
 #pragma unroll
     for (int i = 0; i < FW; ++i) {
       const int f = wave + 4 * i;
@@ -446,18 +486,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_qt_kernel(AttnParams p) {
   for (int dt = 0; dt < NDT; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m_run = kNegBig, l_run = 0.f;
 
-  if (ns > 0) issue(0);
-  if (ns > 1) issue(1);
-  for (int st = 0; st < ns; ++st) {
-    // this wave's loads of step st are done once at most those of st + 1 remain
-    if (st + 1 < ns)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | FW);
-    else
-      __builtin_amdgcn_s_waitcnt(0x0F70);
+  // step st (slot b = st % 3): wait for this wave's loads of st (those of
+  // st + 1 stay in flight), barrier, issue st + 2 into the slot st - 1 used,
+  // compute
+  auto step = [&](int st, auto bc) {
+    constexpr int b = decltype(bc)::value;
+    __builtin_amdgcn_s_waitcnt(0x0F70 | FW);
     ring_barrier();  // every wave's step st is in LDS; every wave is done with step st - 1
-    if (st + 2 < ns) issue(st + 2);
-    if (!active) continue;
-    const unsigned char *sl = ring + (st % kQtStages) * SLOT;
+    issue(st + 2, std::integral_constant<int, (b + 2) % kQtStages>());
+    if (!active || st >= ns) return;
+    const unsigned char *sl = slot_of(bc);
     const int k0 = kb + st * kKeysPerStep;
     floatx4 sc[2];
 #pragma unroll
@@ -509,6 +547,37 @@ __global__ __launch_bounds__(kThreads, 2) void attn_qt_kernel(AttnParams p) {
       o[dt] *= alpha;
       o[dt] = mfma16x16x32(as_bf16x8(v), pf, o[dt]);
     }
+  };
+  if (ns > 0) {
+    issue(0, std::integral_constant<int, 0>());
+    issue(1, std::integral_constant<int, 1>());
+    for (int st0 = 0; st0 < ns; st0 += kQtStages)
+      static_for<kQtStages>([&](auto kc) { step(st0 + decltype(kc)::value, kc); });
+    wait_vmem();  // the clamped loads past the last step
+  }
+  __syncthreads();  // the ring is free for the merge
+
+  if (ib.w == 1) {
+    // the sequence's keys are this one item: normalise and write the output
+    // rows (as the merge of one chunk computes them: o * (1 / l))
+    if (active) {
+      float l = l_run;
+      l += __shfl_xor(l, 16);
+      l += __shfl_xor(l, 32);
+      const int row = wave * 16 + l16;
+      if (row < R) {
+        const float il = l > 0.f ? 1.f / l : 0.f;
+        const int hg = row / n1, j = row - hg * n1;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const uint32_t lo = f2bf(o[dt][0] * il) | ((uint32_t)f2bf(o[dt][1] * il) << 16);
+          const uint32_t hi = f2bf(o[dt][2] * il) | ((uint32_t)f2bf(o[dt][3] * il) << 16);
+          *reinterpret_cast<uint2 *>(p.out + out_offset(p, qst + j, (g * G + hg) * HD + dt * 16 + 4 * gq)) =
+              make_uint2(lo, hi);
+        }
+      }
+    }
+    return;
   }
 
   // publish this chunk's rows: o^T[d][row] (d = 16 dt + 4 gq + i, row = l16)
@@ -527,18 +596,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_qt_kernel(AttnParams p) {
       }
     }
   }
-  publish_merge<HD>(p, qst, ib.z, ib.w, seq, g, R, n1, G, flag, reinterpret_cast<float *>(ring));  // the ring is idle now
+  float *mw = kMw * 4 > SLOT ? mw_own : reinterpret_cast<float *>(ring0);  // the ring is idle now
+  publish_merge<HD>(p, qst, ib.z, ib.w, seq, g, R, n1, G, flag, mw);
 }
 
 template <int HD>
 hipError_t launch_qt(const AttnParams &p, hipStream_t s) {
-  constexpr int F = 2 * (HD / 32) + HD / 16;
-  const size_t lds = (size_t)kQtStages * F * 1024 + 16;
-  if (lds > 65536)
-    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_qt_kernel<HD>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   trace_before(SV_K_ATTENTION, s);
-  hipLaunchKernelGGL((attn_qt_kernel<HD>), dim3(p.max_items, p.hkv), dim3(kThreads), lds, s, p);
+  hipLaunchKernelGGL((attn_qt_kernel<HD>), dim3(p.max_items, p.hkv), dim3(kThreads), 0, s, p);
   trace_after(SV_K_ATTENTION, s);
   return hipGetLastError();
 }
