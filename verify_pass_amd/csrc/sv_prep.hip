@@ -22,8 +22,15 @@ constexpr int kThreads = 256;
 
 __global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ float red[kThreads];
+  __shared__ float red[kThreads / 64];
   const int t = blockIdx.x, tid = threadIdx.x;
+  // the draft counts and lengths of the first sequences, loaded now so that
+  // their latency overlaps the row's
+  int g_pre = 0, kv_pre = 0;
+  if (p.gamma && tid < p.B) {
+    g_pre = p.gamma[tid];
+    kv_pre = p.kv_len[tid];
+  }
   // sum of squares of row t: each thread a fixed set of 8-element chunks
   const uint16_t *row = p.x + (size_t)t * p.d;
   float s = 0.f;
@@ -38,28 +45,37 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams p) {
       s += b * b;
     }
   }
-  red[tid] = s;
+  // fixed-order reduction: within each wave by shuffles, then the four waves
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  if ((tid & 63) == 0) red[tid >> 6] = s;
   __syncthreads();
-  for (int o = kThreads / 2; o > 0; o >>= 1) {
-    if (tid < o) red[tid] += red[tid + o];
-    __syncthreads();
+  if (tid == 0) {
+    float r = 0.f;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) r += red[w];
+    p.rnorm[t] = 1.f / sqrtf(r / static_cast<float>(p.d) + p.eps);
   }
-  if (tid == 0) p.rnorm[t] = 1.f / sqrtf(red[0] / static_cast<float>(p.d) + p.eps);
   if (!p.gamma) return;
 
   int *qs = reinterpret_cast<int *>(smem);
   int *cs = qs + p.B + 1;
-  int *tmp = cs + p.B + 1;
+  int *gs = cs + p.B + 1;   // gamma_i
+  int *ks = gs + p.B + 1;   // kv_len[i]
+  int *tmp = ks + p.B + 1;
   for (int i = tid; i < p.B; i += kThreads) {
-    const int g = p.gamma[i];
+    const int g = i < kThreads ? g_pre : p.gamma[i];
+    const int kv = i < kThreads ? kv_pre : p.kv_len[i];
+    gs[i] = g;
+    ks[i] = kv;
     qs[i] = g + 1;
-    cs[i] = (p.kv_len[i] + g + 1 + p.chunk - 1) / p.chunk;
+    cs[i] = (kv + g + 1 + p.chunk - 1) / p.chunk;
   }
   __syncthreads();
   const int total_t = block_exscan(qs, p.B, tmp);
   const int total_c = block_exscan(cs, p.B, tmp);
   const int seq = upper_index(qs, p.B, t);
-  const int pos = p.kv_len[seq] + (t - qs[seq]);
+  const int pos = ks[seq] + (t - qs[seq]);
   if (tid == 0) {
     p.tok_seq[t] = seq;
     p.tok_pos[t] = pos;
@@ -98,7 +114,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams p) {
       int4 a = make_int4(-1, 0, 0, 0), b = make_int4(0, 0, 0, 0);
       if (it < total_c) {
         const int sq = upper_index(cs, p.B, it);
-        const int g = p.gamma[sq], ctx = p.kv_len[sq];
+        const int g = gs[sq], ctx = ks[sq];
         const int L = ctx + g + 1;
         const int kb = (it - cs[sq]) * p.chunk;
         a = make_int4(sq, kb, min(L, kb + p.chunk), g);
@@ -139,7 +155,7 @@ hipError_t launch_rnorm_parts(const float *parts, int nparts, int T, int K, floa
 }
 
 hipError_t launch_prep(const PrepParams &p, hipStream_t s) {
-  const size_t lds = p.gamma ? (size_t)(2 * (p.B + 1) + 260) * sizeof(int) : 0;
+  const size_t lds = p.gamma ? (size_t)(4 * (p.B + 1) + 260) * sizeof(int) : 0;
   trace_before(SV_K_PREP, s);
   hipLaunchKernelGGL(prep_kernel, dim3(p.T), dim3(kThreads), lds, s, p);
   trace_after(SV_K_PREP, s);
