@@ -181,7 +181,7 @@ __device__ void publish_merge(const AttnParams &p, int qst, int first, int nch, 
 }
 
 template <int RT, int HD>
-__global__ __launch_bounds__(kThreads, (RT == 1 ? 4 : RT <= 3 ? 2 : 1)) void attn_kernel(AttnParams p) {
+__global__ __launch_bounds__(kThreads, (RT == 1 ? 3 : RT <= 3 ? 2 : 1)) void attn_kernel(AttnParams p) {
   constexpr int NDG = HD / 32;  // MFMA k-groups over the head dim
   constexpr int NDT = HD / 16;  // 16-wide head-dim tiles of the output
   extern __shared__ __align__(16) unsigned char smem[];
@@ -247,6 +247,8 @@ __global__ __launch_bounds__(kThreads, (RT == 1 ? 4 : RT <= 3 ? 2 : 1)) void att
   for (int k0 = kw0; k0 < kw1; k0 += kKeysPerStep) {
     uint4 kr[2][NDG];
     load_keys<HD>(kr, kbase, k0, L, l16, gq);
+    uint4 vr[NDT];  // the values in flight with the keys
+    load_values<HD>(vr, vbase, k0, l16, gq);
     // scores of every row tile first; the keys are dead afterwards
     floatx4 s[RT][2];
 #pragma unroll
@@ -257,9 +259,6 @@ __global__ __launch_bounds__(kThreads, (RT == 1 ? 4 : RT <= 3 ? 2 : 1)) void att
 #pragma unroll
         for (int dg = 0; dg < NDG; ++dg) s[rt][kt] = mfma16x16x32(as_bf16x8(kr[kt][dg]), qf[rt][dg], s[rt][kt]);
       }
-    // values in flight during the softmax arithmetic
-    uint4 vr[NDT];
-    load_values<HD>(vr, vbase, k0, l16, gq);
 
     bf16x8 pf[RT];
     float alpha[RT];
