@@ -84,8 +84,6 @@ __device__ __forceinline__ float2 load_dev2(const float *p) {
   return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
 }
 
-constexpr int kMergeChunks = 12;  // chunk partials in flight per output pair
-constexpr int kMergeOuts = 2;     // output pairs per thread and round
 
 // Count this chunk's arrival for (seq, KV head g); the last chunk to arrive
 // merges every chunk's (o, max, sum) by log-sum-exp and writes the output
@@ -95,11 +93,13 @@ constexpr int kMergeOuts = 2;     // output pairs per thread and round
 // context, which the prep pass flags).
 // mw: LDS for 2 * nch * R floats (nch <= 32 chunks, R <= 64 rows); flag: one int.
 // The merge is written for memory-level parallelism: the first round of
-// partial-row loads (kMergeOuts output pairs x kMergeChunks chunks per
-// thread, coherent 8-byte loads) is issued together with the loads of every
-// chunk's (max, sum); the per-(chunk, row) weights are formed in LDS while
-// they are in flight.
-template <int HD>
+// partial-row loads (OUTS output pairs x CHUNKS chunks per thread, coherent
+// 8-byte loads) is issued together with the loads of every chunk's (max,
+// sum); the per-(chunk, row) weights are formed in LDS while they are in
+// flight.  The key-split kernel takes 3 x 9 (its 12 query rows x 9 chunks at
+// 24 stacked tokens in one round of loads); the query-tiled kernel, whose
+// main loop holds more registers, 2 x 12.
+template <int HD, int OUTS, int CHUNKS>
 __device__ void publish_merge(const AttnParams &p, int qst, int first, int nch, int seq, int g, int R, int n1,
                               int G, int *flag, float *mw) {
   const int tid = threadIdx.x, nthr = blockDim.x;
@@ -118,14 +118,14 @@ __device__ void publish_merge(const AttnParams &p, int qst, int first, int nch, 
   auto prow = [&](int cc, int r) { return (((size_t)first + cc) * p.hkv + g) * p.rpad + r; };
   constexpr int NP = HD / 2;  // outputs in column pairs: (row r, columns 2 d2, 2 d2 + 1)
   const int nq = R * NP;
-  float2 v[kMergeOuts][kMergeChunks];
+  float2 v[OUTS][CHUNKS];
   auto load_round = [&](int q0, int c0) {
 #pragma unroll
-    for (int u = 0; u < kMergeOuts; ++u) {
+    for (int u = 0; u < OUTS; ++u) {
       const int q = min(q0 + u * nthr, nq - 1);
       const int r = q / NP, d2 = q - r * NP;
 #pragma unroll
-      for (int k = 0; k < kMergeChunks; ++k) {
+      for (int k = 0; k < CHUNKS; ++k) {
         const int cc = min(c0 + k, nch - 1);
         v[u][k] = load_dev2(p.part_o + prow(cc, r) * HD + 2 * d2);
       }
@@ -150,17 +150,17 @@ __device__ void publish_merge(const AttnParams &p, int qst, int first, int nch, 
     for (int cc = 0; cc < nch; ++cc) wm[cc * R + r] = __builtin_amdgcn_exp2f(wm[cc * R + r] - M) * il;
   }
   __syncthreads();
-  for (int q0 = tid; q0 < nq; q0 += nthr * kMergeOuts) {
-    float2 acc[kMergeOuts];
+  for (int q0 = tid; q0 < nq; q0 += nthr * OUTS) {
+    float2 acc[OUTS];
 #pragma unroll
-    for (int u = 0; u < kMergeOuts; ++u) acc[u] = make_float2(0.f, 0.f);
-    for (int c0 = 0; c0 < nch; c0 += kMergeChunks) {
+    for (int u = 0; u < OUTS; ++u) acc[u] = make_float2(0.f, 0.f);
+    for (int c0 = 0; c0 < nch; c0 += CHUNKS) {
       if (q0 != tid || c0 != 0) load_round(q0, c0);  // the first round is already loaded
 #pragma unroll
-      for (int u = 0; u < kMergeOuts; ++u) {
+      for (int u = 0; u < OUTS; ++u) {
         const int r = min(q0 + u * nthr, nq - 1) / NP;
 #pragma unroll
-        for (int k = 0; k < kMergeChunks; ++k) {
+        for (int k = 0; k < CHUNKS; ++k) {
           const float w = c0 + k < nch ? wm[(c0 + k) * R + r] : 0.f;
           acc[u].x += v[u][k].x * w;
           acc[u].y += v[u][k].y * w;
@@ -168,7 +168,7 @@ __device__ void publish_merge(const AttnParams &p, int qst, int first, int nch, 
       }
     }
 #pragma unroll
-    for (int u = 0; u < kMergeOuts; ++u) {
+    for (int u = 0; u < OUTS; ++u) {
       const int q = q0 + u * nthr;
       if (q >= nq) continue;
       const int r = q / NP, d2 = q - r * NP;
@@ -356,7 +356,7 @@ __global__ __launch_bounds__(kThreads, (RT == 1 ? 3 : RT <= 3 ? 2 : 1)) void att
   }
 
   if (ib.w == 1) return;
-  publish_merge<HD>(p, qst, ib.z, ib.w, seq, g, R, n1, G, flag, red_o);  // red_o is free again
+  publish_merge<HD, 3, 9>(p, qst, ib.z, ib.w, seq, g, R, n1, G, flag, red_o);  // red_o is free again
 }
 
 // ---------------------------------------------------------------------------
@@ -596,7 +596,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_qt_kernel(AttnParams p) {
     }
   }
   float *mw = kMw * 4 > SLOT ? mw_own : reinterpret_cast<float *>(ring0);  // the ring is idle now
-  publish_merge<HD>(p, qst, ib.z, ib.w, seq, g, R, n1, G, flag, mw);
+  publish_merge<HD, 2, 12>(p, qst, ib.z, ib.w, seq, g, R, n1, G, flag, mw);
 }
 
 template <int HD>
