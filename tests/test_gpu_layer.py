@@ -380,18 +380,22 @@ def test_kv_overflow_flagged_and_contained():
                                     "qkv:2:2:1,o:1:4:1,gu:1:2:1,down:3:4:1,head:1:2:1",
                                     "qkv:1:2:2,o:3:2:2,gu:1:2:2,down:2:2:2,head:2:2:2",
                                     "qkv:1:2:3,o:1:2:3,gu:1:2:3,down:1:2:3,head:1:2:3"])
-def test_many_tokens_layer_and_head(tiling):
+@pytest.mark.parametrize("wtype", ["bf16", "int4"])
+def test_many_tokens_layer_and_head(tiling, wtype):
     """300 stacked tokens (three 128-token blocks of the tiled kernel with a
     ragged tail): decoder layer and head against the oracle, with the default
     policy (tiled where it has enough workgroups), with every GEMM tiled,
     with every GEMM streamed one wave per unit (five token blocks, K splits,
     workgroups sharing the token operand), with every GEMM on the wide
     streaming kernel (three 128-token blocks, K splits), and with every GEMM
-    on the square-tiled kernel (two 256-token blocks, the second ragged)."""
+    on the square-tiled kernel (two 256-token blocks, the second ragged).
+    With int4 weights (from 256 tokens) the tiled, wide and square launches
+    run on packed bf16 dequantised into the workspace; the one-wave setting
+    keeps the int4 streaming kernel."""
     shape = Shape(2048, 16, 4, 128, 8192, 20011)
     gamma = [14] * 18 + [11, 12, 4]                  # 18*15 + 12 + 13 + 5 = 300 tokens
     ctx = [int(c) for c in np.linspace(0, 300, len(gamma)).astype(int)]
-    wl = custom_workload(shape, "bf16", gamma, ctx, seed=17)
+    wl = custom_workload(shape, wtype, gamma, ctx, seed=17)
     assert wl.T == 300
     try:
         assert sv.sv_set_gemm_tuning(tiling) == 0
@@ -404,13 +408,13 @@ def test_many_tokens_layer_and_head(tiling):
         ref = dec.oracle(xh, seqs=seqs)
         yh = dev_bf16_to_f64(y)
         err = rel_rows(yh[ref.rows], ref.y)
-        say(f"many tokens [{tiling}]: y rel err {err:.2e}")
-        assert err < TOL["bf16"]
+        say(f"many tokens {wtype} [{tiling}]: y rel err {err:.2e}")
+        assert err < TOL[wtype]
         head = GpuHead(wl, packed=True)
         lg = head.run(y, logits=True).cpu().numpy()
         rows = [0, 127, 128, 255, 256, 299]
         errh = rel_rows(lg[rows], OV.head_logits(head.Wlm, yh[rows]))
         say(f"  head logits rel err {errh:.2e}")
-        assert errh < TOL["bf16"]
+        assert errh < TOL[wtype]
     finally:
         sv.sv_set_gemm_tuning(None)
