@@ -817,11 +817,16 @@ extern "C" sv_status sv_pack_matrix(int32_t wtype, int32_t N, int32_t K, const v
 // ---------------------------------------------------------------------------
 // Acceptance.
 namespace {
+// Vocabulary chunk per workgroup: 4096 entries, or 8192 once the batch has
+// more than about 1024 workgroups' worth of chunks, where each workgroup's
+// latency chain is better spent on twice the loads (measured: 77 -> 67 us at
+// B = 128, 16.7 -> 18.8 us at B = 8).
 constexpr int kAcceptChunk = 4096;
+constexpr int kAcceptChunkWide = 8192;
 
 struct AcceptPlan {
   long long T = 0, nd = 0;
-  int nchunk = 0;
+  int nchunk = 0, chunk = kAcceptChunk;
   size_t off_parts = 0, off_acc = 0, bytes = 0;
 };
 
@@ -838,7 +843,8 @@ sv_status plan_accept(int32_t B, int32_t V, int32_t mode, const int32_t *gamma_h
     ap.nd += gamma_host[i];
   }
   if (ap.T > (1 << 24)) return SV_ERR_UNSUPPORTED;
-  ap.nchunk = (V + kAcceptChunk - 1) / kAcceptChunk;
+  ap.chunk = (long long)B * ((V + kAcceptChunk - 1) / kAcceptChunk) > 1024 ? kAcceptChunkWide : kAcceptChunk;
+  ap.nchunk = (V + ap.chunk - 1) / ap.chunk;
   const long long rows = mode == SV_ACCEPT_GREEDY ? ap.T : B;
   size_t off = kCounterBytes;  // shared-workspace layout: counters first
   ap.off_parts = off;
@@ -887,7 +893,7 @@ extern "C" sv_status sv_accept_commit(int32_t B, int32_t V, int32_t mode, const 
   a.T = (int)ap.T;
   a.nd = (int)ap.nd;
   a.mode = mode;
-  a.chunk = kAcceptChunk;
+  a.chunk = ap.chunk;
   a.nchunk = ap.nchunk;
   a.gamma = gamma;
   a.draft = draft;
