@@ -291,7 +291,9 @@ constexpr int kDqMinT = 256;
 GemmCfg gemm_cfg_w(int kind, int nblk, int N, int T, int K, int wtype, bool packed) {
   if (wtype == SV_W_INT4_G32 && packed && T >= kDqMinT) {
     GemmCfg c = gemm_cfg(kind, nblk, N, T, K, SV_W_BF16, true);
-    if (c.kw == kGemmTiled || c.kw == kGemmSquare || c.kw == kGemmWide) {
+    // the square-tiled kernel has an int4 form (converts in LDS, no copy)
+    if (c.kw == kGemmSquare) return c;
+    if (c.kw == kGemmTiled || c.kw == kGemmWide) {
       c.dq = true;
       return c;
     }

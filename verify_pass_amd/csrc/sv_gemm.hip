@@ -40,6 +40,7 @@ hipError_t launch_gemm_f32(const GemmParams &p, int tok_tiles, int depth, int kw
 
 hipError_t launch_gemm_tiled_bf16(const GemmParams &p, hipStream_t s, int trace_class);
 hipError_t launch_gemm_square_bf16(const GemmParams &p, hipStream_t s, int trace_class);
+hipError_t launch_gemm_square_int4(const GemmParams &p, hipStream_t s, int trace_class);
 hipError_t launch_gemm_wide_bf16(const GemmParams &p, int tok_tiles, int depth, hipStream_t s, int trace_class);
 
 hipError_t launch_gemm(const GemmParams &p, int wtype, int tok_tiles, int depth, int kw, hipStream_t s,
@@ -49,8 +50,8 @@ hipError_t launch_gemm(const GemmParams &p, int wtype, int tok_tiles, int depth,
     return launch_gemm_tiled_bf16(p, s, trace_class);
   }
   if (kw == kGemmSquare) {
-    if (wtype != WT_BF16 || !p.packed || p.splits != 1) return hipErrorInvalidValue;
-    return launch_gemm_square_bf16(p, s, trace_class);
+    if ((wtype != WT_BF16 && wtype != WT_INT4) || !p.packed || p.splits != 1) return hipErrorInvalidValue;
+    return wtype == WT_INT4 ? launch_gemm_square_int4(p, s, trace_class) : launch_gemm_square_bf16(p, s, trace_class);
   }
   if (kw == kGemmWide) {
     if (wtype != WT_BF16 || !p.packed || (tok_tiles != 4 && tok_tiles != 8)) return hipErrorInvalidValue;

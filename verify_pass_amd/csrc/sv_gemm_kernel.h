@@ -1266,6 +1266,197 @@ __global__ __launch_bounds__(kSThreads, 1) void gemm_sq_kernel(GemmParams p) {
   }
 }
 
+// The same tiling for packed int4 weights, every load direct-to-LDS (so the
+// explicit waits stay exact).  Each ring slot also stages a half step's int4
+// codes (16 fragments x 16 rows x 16 bytes: one row's k range of the half
+// step) and their group scales.  Each wave issues three loads per half step:
+// two token fragments and one 16-byte-per-lane load of: codes of four
+// fragments (waves 0-3), the scales of all sixteen (wave 4), a dummy (5-7).  At half step s every
+// thread converts half of one (fragment, row) pair of the staged codes of
+// s + 1 to bf16 (code - 8 times the scale, as the int4 streaming kernel does)
+// after its MFMAs, and writes them in MFMA lane order into that slot's weight
+// area (word i of row r goes to lane i * 16 + r); right after the barrier it
+// issues the codes of s + 4 and the tokens of s + 3.  The MFMA loop is the bf16 kernel's; the weights cross HBM
+// once, as int4.  Weight fragments, token fragments and staging of each slot
+// are separate LDS objects: no LDS access then touches an object a
+// direct-to-LDS load in flight is writing, and the compiler adds no waits.
+constexpr int kS4Stage = 4096 + 512 + 2048;  // codes, scales, dummy
+
+template <int EPI>
+__global__ __launch_bounds__(kSThreads, 1) void gemm_sq4_kernel(GemmParams p) {
+  constexpr int D = kSStages - 1;  // token half steps in flight
+  constexpr int kCodes = 0, kScales = 4096, kJunk = 4096 + 512;
+  __shared__ __align__(16) unsigned char w0[16384], w1[16384], w2[16384], w3[16384];
+  __shared__ __align__(16) unsigned char t0[16384], t1[16384], t2[16384], t3[16384];
+  __shared__ __align__(16) unsigned char g0[kS4Stage], g1[kS4Stage], g2[kS4Stage], g3[kS4Stage];
+  auto wslot = [&](auto kc) -> unsigned char * {
+    constexpr int k = decltype(kc)::value % kSStages;
+    if constexpr (k == 0) return w0;
+    else if constexpr (k == 1) return w1;
+    else if constexpr (k == 2) return w2;
+    else return w3;
+  };
+  auto tslot = [&](auto kc) -> unsigned char * {
+    constexpr int k = decltype(kc)::value % kSStages;
+    if constexpr (k == 0) return t0;
+    else if constexpr (k == 1) return t1;
+    else if constexpr (k == 2) return t2;
+    else return t3;
+  };
+  auto gslot = [&](auto kc) -> unsigned char * {
+    constexpr int k = decltype(kc)::value % kSStages;
+    if constexpr (k == 0) return g0;
+    else if constexpr (k == 1) return g1;
+    else if constexpr (k == 2) return g2;
+    else return g3;
+  };
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int gq = lane >> 4, l16 = lane & 15;
+  const int ntb = (p.T + kSTok - 1) / kSTok;
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int tb = wg % ntb, rb = wg / ntb;
+  const int gp = wave & 3, th = wave >> 2;
+  const int nh = 2 * p.ksteps;  // half steps of 32 (ksteps counts steps of 64)
+
+  // base of fragment f's int4 data (uint4 units) and scales, and the matrix's
+  // step stride (fragments per int4 step of 128)
+  auto frag_src = [&](int f, const uint4 *&w, const uint16_t *&sc, size_t &stride) {
+    int mi = 0, pr0 = 0;
+    if (!map_row(p, rb * kSGroups + (f >> 1), f & 1, 0, mi, pr0)) { mi = 0; pr0 = 0; }
+    const size_t base = ((size_t)(pr0 / 32) * 2 + ((pr0 / 16) & 1)) * 64;
+    w = static_cast<const uint4 *>(p.mat[mi].w) + base;
+    sc = p.mat[mi].s + base;
+    stride = (size_t)((p.mat[mi].rows + 31) / 32) * 128;
+  };
+  // this lane's extra load: bytes at xs + int4 step * xstep + (half step % 4) * xhs
+  const unsigned char *xs;
+  size_t xstep;
+  int xhs, xdst;
+  {
+    const uint4 *w;
+    const uint16_t *sc;
+    size_t stride;
+    if (wave < 4) {  // codes: fragment 4 wave + lane / 16, row lane % 16
+      frag_src(4 * wave + (lane >> 4), w, sc, stride);
+      xs = reinterpret_cast<const unsigned char *>(w + l16);
+      xstep = stride * 16;
+      xhs = 256;
+      xdst = kCodes + wave * 1024;
+    } else if (wave == 4) {  // scales: fragment (lane % 32) / 2, rows 8 (lane % 2) .. +7
+      frag_src((lane & 31) >> 1, w, sc, stride);
+      xs = reinterpret_cast<const unsigned char *>(sc + 8 * (lane & 1));
+      xstep = stride * 2;
+      xhs = 32;
+      xdst = kScales + lane * 16;  // lanes 32..63 repeat 0..31 into the dummy area
+    } else {  // dummy: any valid bytes
+      frag_src(0, w, sc, stride);
+      xs = reinterpret_cast<const unsigned char *>(w + l16);
+      xstep = 0;
+      xhs = 0;
+      xdst = kJunk + ((wave - 5) & 1) * 1024;
+    }
+  }
+  auto xissue = [&](int hh, auto kc) {
+    const int hc = min(hh, nh - 1);
+    load_lds16(xs + (size_t)(hc >> 2) * xstep + (hc & 3) * xhs, gslot(kc) + xdst);
+  };
+  // token tiles wave + 8 i
+  const unsigned char *tsrc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    tsrc[i] = reinterpret_cast<const unsigned char *>(
+        p.x + (size_t)min(tb * kSTok + (wave + 8 * i) * 16 + l16, p.T - 1) * p.K + 8 * gq);
+  auto tissue = [&](int hh, auto kc) {
+    const int hc = min(hh, nh - 1);
+    const int st = hc >> 1, m = hc & 1;
+    unsigned char *slot = tslot(kc);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) load_lds16(tsrc[i] + (size_t)st * 128 + m * 64, slot + (wave + 8 * i) * 1024);
+  };
+  // conversion: pair (fragment cf, row cr), words 2 ch, 2 ch + 1
+  const int pair = threadIdx.x >> 1, ch = threadIdx.x & 1;
+  const int cf = pair >> 4, cr = pair & 15;
+  auto convert = [&](auto kc) {
+    const unsigned char *stg = gslot(kc);
+    unsigned char *slot = wslot(kc);
+    const uint2 cw = *reinterpret_cast<const uint2 *>(stg + kCodes + (cf * 16 + cr) * 16 + ch * 8);
+    const float sc = bf2f(*reinterpret_cast<const uint16_t *>(stg + kScales + (cf * 16 + cr) * 2));
+    auto put = [&](uint32_t word, int i) {
+      uint32_t hv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = static_cast<float>(static_cast<int>((word >> (8 * e)) & 15u) - 8) * sc;
+        const float hi = static_cast<float>(static_cast<int>((word >> (8 * e + 4)) & 15u) - 8) * sc;
+        hv[e] = f2bf(lo) | (f2bf(hi) << 16);
+      }
+      *reinterpret_cast<uint4 *>(slot + cf * 1024 + ((2 * ch + i) * 16 + cr) * 16) = uint4{hv[0], hv[1], hv[2], hv[3]};
+    };
+    put(cw.x, 0);
+    put(cw.y, 1);
+  };
+
+  floatx4 acc[2][2][8];
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[gi][a][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // prologue: half step 0's weights converted; extra(1), tokens(0), extra(2),
+  // tokens(1), extra(3), tokens(2) in flight
+  xissue(0, std::integral_constant<int, 0>());
+  wait_vmem();
+  __syncthreads();
+  convert(std::integral_constant<int, 0>());
+  static_for<D>([&](auto kc) {
+    constexpr int k = decltype(kc)::value;
+    xissue(k + 1, std::integral_constant<int, k + 1>());
+    tissue(k, kc);
+  });
+  // half step s (slot b = s % 4): this wave's tokens of s are in (so are the
+  // codes of s + 1, issued before them; 6 loads issued later may remain) and
+  // its LDS writes are done; barrier; issue the codes of s + 4 and the tokens
+  // of s + 3; compute s; convert s + 1
+  auto step = [&](int sh, auto bc) {
+    constexpr int b = decltype(bc)::value;
+    __builtin_amdgcn_s_waitcnt(0x0070 | 6);
+    ring_barrier();
+    xissue(sh + 4, std::integral_constant<int, b + 4>());
+    tissue(sh + D, std::integral_constant<int, b + D>());
+    const unsigned char *wl = wslot(bc), *tl = tslot(bc);
+    bf16x8 wv[2][2];
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+        wv[gi][a] = as_bf16x8(ld_v4(wl + (((2 * gp + gi) * 2 + a) * 64 + lane) * 16));
+    const bool live = sh < nh;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j == 4) __builtin_amdgcn_sched_barrier(0);  // two groups of token reads (register pressure)
+      uint4 xr = ld_v4(tl + ((th * 8 + j) * 64 + lane) * 16);
+      if (!live) xr = uint4{0u, 0u, 0u, 0u};
+      const bf16x8 xv = as_bf16x8(xr);
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+        for (int a = 0; a < 2; ++a) acc[gi][a][j] = mfma16x16x32(wv[gi][a], xv, acc[gi][a][j]);
+    }
+    convert(std::integral_constant<int, b + 1>());  // read at s + 1, after its barrier
+  };
+  for (int h0 = 0; h0 < nh; h0 += kSStages)
+    static_for<kSStages>([&](auto kc) { step(h0 + decltype(kc)::value, kc); });
+  wait_vmem();  // the clamped tail loads
+
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi) {
+    const int grp = rb * kSGroups + 2 * gp + gi;
+    if (grp < p.nblk) epilogue<8, EPI>(p, acc[gi], grp, tb * kSTok + th * 128, gq, l16);
+  }
+}
+
 inline int sq_grid(const GemmParams &p) {
   return ((p.nblk + kSGroups - 1) / kSGroups) * ((p.T + kSTok - 1) / kSTok);
 }
@@ -1276,6 +1467,23 @@ hipError_t launch_sq_epi(const GemmParams &p, hipStream_t s, int trace_class) {
   hipLaunchKernelGGL((gemm_sq_kernel<EPI>), dim3(sq_grid(p)), dim3(kSThreads), 0, s, p);
   trace_after(trace_class, s);
   return hipGetLastError();
+}
+
+template <int EPI>
+hipError_t launch_sq4_epi(const GemmParams &p, hipStream_t s, int trace_class) {
+  trace_before(trace_class, s);
+  hipLaunchKernelGGL((gemm_sq4_kernel<EPI>), dim3(sq_grid(p)), dim3(kSThreads), 0, s, p);
+  trace_after(trace_class, s);
+  return hipGetLastError();
+}
+
+inline hipError_t launch_sq4(const GemmParams &p, hipStream_t s, int trace_class) {
+  switch (p.epi) {
+    case EPI_QKV: return launch_sq4_epi<EPI_QKV>(p, s, trace_class);
+    case EPI_RESID: return launch_sq4_epi<EPI_RESID>(p, s, trace_class);
+    case EPI_SWIGLU: return launch_sq4_epi<EPI_SWIGLU>(p, s, trace_class);
+    default: return launch_sq4_epi<EPI_LOGITS>(p, s, trace_class);
+  }
 }
 
 inline hipError_t launch_sq(const GemmParams &p, hipStream_t s, int trace_class) {
