@@ -379,19 +379,22 @@ def test_kv_overflow_flagged_and_contained():
 @pytest.mark.parametrize("tiling", [None, "qkv:1:2:0,o:1:2:0,gu:1:2:0,down:1:2:0,head:1:2:0",
                                     "qkv:2:2:1,o:1:4:1,gu:1:2:1,down:3:4:1,head:1:2:1",
                                     "qkv:1:2:2,o:3:2:2,gu:1:2:2,down:2:2:2,head:2:2:2",
-                                    "qkv:1:2:3,o:1:2:3,gu:1:2:3,down:1:2:3,head:1:2:3"])
+                                    "qkv:1:2:3,o:1:2:3,gu:1:2:3,down:1:2:3,head:1:2:3",
+                                    "qkv:3:2:3,o:2:2:3,gu:5:2:3,down:7:2:3,head:2:2:3"])
 @pytest.mark.parametrize("wtype", ["bf16", "int4"])
 def test_many_tokens_layer_and_head(tiling, wtype):
     """300 stacked tokens (three 128-token blocks of the tiled kernel with a
     ragged tail): decoder layer and head against the oracle, with the default
-    policy (tiled where it has enough workgroups), with every GEMM tiled,
+    policy, with every GEMM tiled,
     with every GEMM streamed one wave per unit (five token blocks, K splits,
     workgroups sharing the token operand), with every GEMM on the wide
     streaming kernel (three 128-token blocks, K splits), and with every GEMM
-    on the square-tiled kernel (two 256-token blocks, the second ragged).
-    With int4 weights (from 256 tokens) the tiled, wide and square launches
-    run on packed bf16 dequantised into the workspace; the one-wave setting
-    keeps the int4 streaming kernel."""
+    on the square-tiled kernel (two 256-token blocks, the second ragged),
+    without and with uneven K splits (partial tiles per 128-token block, the
+    third block ragged and the fourth empty).  With int4 weights (from 256 tokens) the
+    tiled and wide launches run on packed bf16 dequantised into the
+    workspace, the square launches convert the int4 codes in LDS, and the
+    one-wave setting keeps the int4 streaming kernel."""
     shape = Shape(2048, 16, 4, 128, 8192, 20011)
     gamma = [14] * 18 + [11, 12, 4]                  # 18*15 + 12 + 13 + 5 = 300 tokens
     ctx = [int(c) for c in np.linspace(0, 300, len(gamma)).astype(int)]

@@ -251,7 +251,10 @@ GemmCfg gemm_cfg(int kind, int nblk, int N, int T, int K, int wtype, bool packed
   } else if (tiled_ok && T > 48) {
     // too few tiles for the tiled kernel to fill the CUs: the wide streaming
     // kernel, with K splits filling one round of resident workgroups (one per
-    // CU for 128-token blocks, two for 64), each split at least 8 K steps
+    // CU for 128-token blocks, two for 64), each split at least 8 K steps.
+    // (The square kernel with K splits filling one round measured slower on
+    // the 9B- and 27B-class QKV and O at 256 and 512 tokens: 65 -> 88 us for
+    // O at 512; the partial tiles are 4 bytes per output per split.)
     set_wide(c, T, 1);
     const long long per = (long long)((nblk + 7) / 8) * c.ntblk;
     const long long slots = c.tt == 8 ? 256 : 512;
@@ -268,15 +271,18 @@ GemmCfg gemm_cfg(int kind, int nblk, int N, int T, int K, int wtype, bool packed
     set_wide(c, T, tn.splits[kind] > 0 ? tn.splits[kind] : 1);
   } else if (tn.kw[kind] == 3 && tiled_ok) {
     c.kw = kGemmSquare;
-    c.splits = 1;
+    c.splits = tn.splits[kind] > 0 ? std::max(1, std::min(tn.splits[kind], c.ksteps / 2)) : 1;
   } else if (tn.kw[kind] > 0) {
     c.kw = tn.kw[kind] >= 16 ? 16 : tn.kw[kind] >= 8 ? 8 : tn.kw[kind] >= 4 ? 4 : 1;
   }
-  if (c.kw != kGemmWide) {  // the token blocking of the streaming kernels
+  if (c.kw == kGemmSquare && c.splits > 1) {  // partial tiles of 32 rows x 128 tokens
+    c.tt = 8;
+    c.ntblk = (T + 127) / 128;
+  } else if (c.kw != kGemmWide) {  // the token blocking of the streaming kernels
     c.tt = stream_tt;
     c.ntblk = stream_ntblk;
   }
-  if (c.kw == kGemmTiled || c.kw == kGemmSquare) c.splits = 1;
+  if (c.kw == kGemmTiled) c.splits = 1;
   if (c.splits > 1 && (size_t)c.nblk * c.ntblk > kMaxCounters) c.splits = 1;
   return c;
 }

@@ -50,7 +50,10 @@ hipError_t launch_gemm(const GemmParams &p, int wtype, int tok_tiles, int depth,
     return launch_gemm_tiled_bf16(p, s, trace_class);
   }
   if (kw == kGemmSquare) {
-    if ((wtype != WT_BF16 && wtype != WT_INT4) || !p.packed || p.splits != 1) return hipErrorInvalidValue;
+    if ((wtype != WT_BF16 && wtype != WT_INT4) || !p.packed) return hipErrorInvalidValue;
+    // K splits: at least one half step (of 32) each; partial tiles per 128 tokens
+    if (p.splits < 1 || p.splits > 2 * p.ksteps || (p.splits > 1 && p.ntblk != (p.T + 127) / 128))
+      return hipErrorInvalidValue;
     return wtype == WT_INT4 ? launch_gemm_square_int4(p, s, trace_class) : launch_gemm_square_bf16(p, s, trace_class);
   }
   if (kw == kGemmWide) {

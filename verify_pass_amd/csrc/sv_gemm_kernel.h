@@ -500,12 +500,20 @@ __device__ __forceinline__ bool split_reduce(const GemmParams &p, floatx4 (&acc)
     for (int tt = 0; tt < TT; ++tt) acc[a][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
   for (int sp = 0; sp < p.splits; ++sp) {
     const float *src = p.partial + ((size_t)sp * p.nblk * p.ntblk + tile_id) * TILE;
+    // half a tile is loaded before any of it is added, so that its loads are
+    // in flight together
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < 2; ++a) {
+      float v[TT][4];
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[a][tt][i] += load_dev(src + ((a * TT + tt) * 4 + i) * 64 + lane);
+        for (int i = 0; i < 4; ++i) v[tt][i] = load_dev(src + ((a * TT + tt) * 4 + i) * 64 + lane);
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[a][tt][i] += v[tt][i];
+    }
   }
   return true;
 }
@@ -1160,7 +1168,9 @@ inline hipError_t launch_wide(const GemmParams &p, int tok_tiles, int depth, hip
 // kernel reads 512).  A ring of four half-step slots, each its own LDS object,
 // keeps three half steps in flight; the loop is branch-free (clamped tail
 // loads, zero token operand past the end), so the compiler's waits stay
-// exact.  No K split; the epilogues are the streaming kernel's.
+// exact.  The epilogues are the streaming kernel's, and so is the K split
+// reduction, which only a tuning override selects (partial tiles through
+// memory measured slower than the default choices).
 constexpr int kSThreads = 512;
 constexpr int kSGroups = 8;     // 32-row groups per workgroup
 constexpr int kSTok = 256;      // tokens per workgroup
@@ -1184,9 +1194,13 @@ __global__ __launch_bounds__(kSThreads, 1) void gemm_sq_kernel(GemmParams p) {
   const int gq = lane >> 4, l16 = lane & 15;
   const int ntb = (p.T + kSTok - 1) / kSTok;
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
-  const int tb = wg % ntb, rb = wg / ntb;  // token block fastest (shared weights in L2)
+  // token block fastest (shared weights in L2), then row block, then K split
+  const int nrb = (p.nblk + kSGroups - 1) / kSGroups;
+  const int tb = wg % ntb, rb = (wg / ntb) % nrb, split = wg / ntb / nrb;
   const int gp = wave & 3, th = wave >> 2;
-  const int nh = 2 * p.ksteps;            // half steps
+  // this split's half steps h0 .. h0 + nh - 1
+  const int h0 = (int)((long long)split * 2 * p.ksteps / p.splits);
+  const int nh = (int)((long long)(split + 1) * 2 * p.ksteps / p.splits) - h0;
 
   // the four fragments this wave loads each half step: f = wave + 8 i;
   // f < 16: weight fragment (group f / 2, tile f % 2), else token tile f - 16
@@ -1211,7 +1225,7 @@ __global__ __launch_bounds__(kSThreads, 1) void gemm_sq_kernel(GemmParams p) {
   }
   // half step h = 2 s + m: weights at s * stride + m * 1 KiB, tokens at s * 128 + m * 64 bytes
   auto issue = [&](int h, auto kc) {
-    const int hc = min(h, nh - 1);
+    const int hc = h0 + min(h, nh - 1);
     const int s = hc >> 1, m = hc & 1;
     unsigned char *slot = slot_of(kc);
 #pragma unroll
@@ -1255,14 +1269,17 @@ __global__ __launch_bounds__(kSThreads, 1) void gemm_sq_kernel(GemmParams p) {
         for (int a = 0; a < 2; ++a) acc[gi][a][j] = mfma16x16x32(wv[gi][a], xv, acc[gi][a][j]);
     }
   };
-  for (int h0 = 0; h0 < nh; h0 += kSStages)
-    static_for<kSStages>([&](auto kc) { step(h0 + decltype(kc)::value, kc); });
+  for (int hb = 0; hb < nh; hb += kSStages)
+    static_for<kSStages>([&](auto kc) { step(hb + decltype(kc)::value, kc); });
   wait_vmem();  // the clamped tail loads
 
 #pragma unroll
   for (int gi = 0; gi < 2; ++gi) {
     const int grp = rb * kSGroups + 2 * gp + gi;
-    if (grp < p.nblk) epilogue<8, EPI>(p, acc[gi], grp, tb * kSTok + th * 128, gq, l16);
+    if (grp >= p.nblk || tb * kSTok + th * 128 >= p.T) continue;
+    // K splits: the last split to arrive at (group, 128-token block) adds all
+    if (p.splits > 1 && !split_reduce<8>(p, acc[gi], grp, tb * 2 + th, split, lane)) continue;
+    epilogue<8, EPI>(p, acc[gi], grp, tb * kSTok + th * 128, gq, l16);
   }
 }
 
@@ -1315,9 +1332,12 @@ __global__ __launch_bounds__(kSThreads, 1) void gemm_sq4_kernel(GemmParams p) {
   const int gq = lane >> 4, l16 = lane & 15;
   const int ntb = (p.T + kSTok - 1) / kSTok;
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
-  const int tb = wg % ntb, rb = wg / ntb;
+  const int nrb = (p.nblk + kSGroups - 1) / kSGroups;
+  const int tb = wg % ntb, rb = (wg / ntb) % nrb, split = wg / ntb / nrb;
   const int gp = wave & 3, th = wave >> 2;
-  const int nh = 2 * p.ksteps;  // half steps of 32 (ksteps counts steps of 64)
+  // this split's half steps (of 32; ksteps counts steps of 64) h0 .. h0 + nh - 1
+  const int h0 = (int)((long long)split * 2 * p.ksteps / p.splits);
+  const int nh = (int)((long long)(split + 1) * 2 * p.ksteps / p.splits) - h0;
 
   // base of fragment f's int4 data (uint4 units) and scales, and the matrix's
   // step stride (fragments per int4 step of 128)
@@ -1358,7 +1378,7 @@ __global__ __launch_bounds__(kSThreads, 1) void gemm_sq4_kernel(GemmParams p) {
     }
   }
   auto xissue = [&](int hh, auto kc) {
-    const int hc = min(hh, nh - 1);
+    const int hc = h0 + min(hh, nh - 1);
     load_lds16(xs + (size_t)(hc >> 2) * xstep + (hc & 3) * xhs, gslot(kc) + xdst);
   };
   // token tiles wave + 8 i
@@ -1368,7 +1388,7 @@ __global__ __launch_bounds__(kSThreads, 1) void gemm_sq4_kernel(GemmParams p) {
     tsrc[i] = reinterpret_cast<const unsigned char *>(
         p.x + (size_t)min(tb * kSTok + (wave + 8 * i) * 16 + l16, p.T - 1) * p.K + 8 * gq);
   auto tissue = [&](int hh, auto kc) {
-    const int hc = min(hh, nh - 1);
+    const int hc = h0 + min(hh, nh - 1);
     const int st = hc >> 1, m = hc & 1;
     unsigned char *slot = tslot(kc);
 #pragma unroll
@@ -1446,19 +1466,23 @@ __global__ __launch_bounds__(kSThreads, 1) void gemm_sq4_kernel(GemmParams p) {
     }
     convert(std::integral_constant<int, b + 1>());  // read at s + 1, after its barrier
   };
-  for (int h0 = 0; h0 < nh; h0 += kSStages)
-    static_for<kSStages>([&](auto kc) { step(h0 + decltype(kc)::value, kc); });
+  for (int hb = 0; hb < nh; hb += kSStages)
+    static_for<kSStages>([&](auto kc) { step(hb + decltype(kc)::value, kc); });
   wait_vmem();  // the clamped tail loads
 
 #pragma unroll
   for (int gi = 0; gi < 2; ++gi) {
     const int grp = rb * kSGroups + 2 * gp + gi;
-    if (grp < p.nblk) epilogue<8, EPI>(p, acc[gi], grp, tb * kSTok + th * 128, gq, l16);
+    if (grp >= p.nblk || tb * kSTok + th * 128 >= p.T) continue;
+    if (p.splits > 1 && !split_reduce<8>(p, acc[gi], grp, tb * 2 + th, split, lane)) continue;
+    epilogue<8, EPI>(p, acc[gi], grp, tb * kSTok + th * 128, gq, l16);
   }
 }
 
+// Grid of the square-tiled kernels: row blocks x 256-token blocks x K splits.
+// With K splits the partial tiles are indexed by 128-token blocks (p.ntblk).
 inline int sq_grid(const GemmParams &p) {
-  return ((p.nblk + kSGroups - 1) / kSGroups) * ((p.T + kSTok - 1) / kSTok);
+  return ((p.nblk + kSGroups - 1) / kSGroups) * ((p.T + kSTok - 1) / kSTok) * p.splits;
 }
 
 template <int EPI>
