@@ -107,7 +107,7 @@ class DeviceBatch:
     of 32 positions, [n_kv][cap/32][hd][32]."""
 
     def __init__(self, gamma, kv_len, cap: int, max_ctx: int | None = None, kcache=None,
-                 vcache=None, shape=None, device="cuda"):
+                 vcache=None, shape=None, device="cuda", caches=None):
         self.gamma_list = [int(g) for g in gamma]
         self.B = len(self.gamma_list)
         self.T = int(sum(g + 1 for g in self.gamma_list))
@@ -118,7 +118,10 @@ class DeviceBatch:
         self.err = torch.zeros(1, dtype=torch.int32, device=device)
         self._gh = (C.c_int32 * max(1, self.B))(*self.gamma_list)
         self.k, self.v = [], []
-        if kcache is not None:
+        if caches is not None:  # device caches of an earlier batch, shared (not copied)
+            self.k, self.v = list(caches[0]), list(caches[1])
+            assert len(self.k) == self.B and len(self.v) == self.B
+        elif kcache is not None:
             for i in range(self.B):
                 self.k.append(to_dev(kcache[i], device))
                 self.v.append(to_dev(v_blocked(vcache[i]), device))
