@@ -324,8 +324,8 @@ def main():
                          "times (the known-size reference for HBM traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the "
-              "sharded design is described in DESIGN.md", file=sys.stderr)
+        print(f"bench.py: the verify path runs on one GPU only (asked for --gpus {args.gpus}); "
+              "sharding across GPUs is not implemented", file=sys.stderr)
         sys.exit(2)
     if args.sweep:
         sweep(args)

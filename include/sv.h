@@ -61,7 +61,7 @@ typedef int32_t sv_status;
 
 #define SV_OK 0
 #define SV_ERR_INVALID_ARG (-1) /* null pointer, negative size, inconsistent counts */
-#define SV_ERR_UNSUPPORTED (-2) /* a shape or dtype this build does not handle */
+#define SV_ERR_UNSUPPORTED (-2) /* a shape or dtype the library does not handle */
 #define SV_ERR_WORKSPACE (-3)   /* workspace missing or smaller than required */
 #define SV_ERR_HIP (-4)         /* a kernel launch failed */
 
