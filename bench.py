@@ -3,19 +3,23 @@
 
 A step is the whole hot path over one batch: plan the draft lengths (host),
 the decoder layer over the stacked verify tokens (QKV + RoPE + KV append,
-ragged attention, O, SwiGLU FFN), the LM head with softmax, and acceptance /
-resampling / KV-length commit.  Default workload: one 9B-class bf16 layer,
-B=8 sequences with gamma=2 drafts each, 2048 cached tokens, a 151936-entry
-head, acceptance rate 0.8.  Inputs are seeded synthetic data resident in HBM
-before timing starts.
+ragged attention, O, SwiGLU FFN), the LM head (logits + row statistics), and
+acceptance / resampling / KV-length commit reading the head's logits.  The
+headline workload is the largest single-GPU one: a 27B-class bf16 layer,
+B=32 sequences with gamma=7 drafts each (256 verify tokens), 2048 cached
+tokens, a 151936-entry head, drafts from noisy target logits.  The 9B-class
+bf16 layer (B=8, gamma=2) and the 9B-class int4 layer (B=128, gamma=3, 1024
+cached tokens) are reported beside it under "workloads".  Inputs are seeded
+synthetic data resident in HBM before timing starts.
 
 Prints one JSON line (stdout); progress goes to stderr.
 
-    python bench.py [--steps K] [--warmup W] [--workload N] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload N] [--extra 2,5] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -108,37 +112,54 @@ def measured_traffic(wl, dom_name):
         return None
 
 
-def cpu_baseline(wl, W, Wlm, kc, vc, xh, acc_in, min_seconds=10.0, max_reps=8):
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, W, Wlm, kc, vc, xh, acc_in, seqs_per_rep, min_seconds=10.0, max_reps=6):
     """The oracle, as it stands, on a bounded sample of the same workload:
-    whole verify steps (every sequence of the batch through the layer, the
-    head and acceptance), repeated until min_seconds have passed or max_reps
-    steps are done."""
+    whole verify steps of the first seqs_per_rep sequences (decoder layer,
+    LM head + softmax, acceptance), repeated until min_seconds have passed or
+    max_reps steps are done."""
     import numpy as np
     from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle import accept as OA
     from oracle import verify as OV
     cores = len(os.sched_getaffinity(0))
+    S = max(1, min(wl.B, int(seqs_per_rep)))
+    seqs = list(range(S))
+    qs = wl.q_start
+    g = wl.gamma[:S]
+    drows = int(np.sum(g))
     with threadpool_limits(limits=cores):
         blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
         t0 = time.perf_counter()
         reps = n_tok = 0
         while reps < max_reps and (reps == 0 or time.perf_counter() - t0 < min_seconds):
-            out = OV.decoder_layer(wl.shape, W, xh, wl.gamma, wl.ctx, kc, vc)
+            out = OV.decoder_layer(wl.shape, W, xh, wl.gamma, wl.ctx, kc, vc, seqs=seqs)
             if Wlm is not None:
                 p = OV.softmax(OV.head_logits(Wlm, out.y)).astype(np.float32)
             else:
-                p = acc_in["p"]
-            OA.accept_commit(wl.gamma, acc_in["draft"], p, acc_in["q"], acc_in["u_acc"],
-                             acc_in["u_samp"], wl.ctx)
+                p = acc_in["p"][:qs[S]]
+            OA.accept_commit(g, acc_in["draft"][:drows], p, acc_in["q"][:drows],
+                             acc_in["u_acc"][:drows], acc_in["u_samp"][:S], wl.ctx[:S])
             n_tok += len(out.rows)
             reps += 1
         dt = time.perf_counter() - t0
     return {"value": round(n_tok / dt, 4), "unit": "verify tokens/s", "cores": int(blas),
-            "kind": "oracle",
-            "sample": f"{reps} whole verify step(s) of the workload ({n_tok} verify tokens): decoder "
-                      f"layer, {'LM head + softmax, ' if Wlm is not None else ''}acceptance for all "
-                      f"{wl.B} sequences; {dt:.1f} s on {blas} BLAS threads ({cores} cores visible)"}
+            "kind": "oracle", "cpu": cpu_model(),
+            "sample": f"{reps} verify step(s) of the first {S} of the workload's {wl.B} sequences "
+                      f"({n_tok} verify tokens in all): decoder layer, "
+                      f"{'LM head + softmax, ' if Wlm is not None else ''}acceptance; {dt:.1f} s on "
+                      f"{blas} BLAS threads ({cores} cores visible)"}
 
 
 def expected_tokens(alpha: float, gamma: int) -> float:
@@ -299,38 +320,17 @@ def sweep(args):
     print(json.dumps({"sweep": True, "points": len(rows), "fits": out["fits"]}), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=2)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-kernel-table", action="store_true")
-    ap.add_argument("--head-probs", action="store_true",
-                    help="head writes probabilities and acceptance reads them (default: logits "
-                         "plus row (max, sum), acceptance forms the probabilities it reads)")
-    ap.add_argument("--sweep", action="store_true",
-                    help="time the step over a (B, gamma) grid on one layer shape instead, fit the "
-                         "step model per gamma and report the crossover batch")
-    ap.add_argument("--sweep-shape", default="9b", choices=("9b", "27b"))
-    ap.add_argument("--sweep-wtype", default="bf16", choices=("bf16", "int4"))
-    ap.add_argument("--sweep-ctx", type=int, default=2048)
-    ap.add_argument("--sweep-b", default="1,2,4,8,16,32,64,128,256")
-    ap.add_argument("--sweep-gamma", default="0,1,2,3,4,5,7")
-    ap.add_argument("--sweep-out", default="")
-    ap.add_argument("--copy-probe-mib", type=int, default=0,
-                    help="before the steps, copy a buffer of this many MiB device to device three "
-                         "times (the known-size reference for HBM traffic counters)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py: the verify path runs on one GPU only (asked for --gpus {args.gpus}); "
-              "sharding across GPUs is not implemented", file=sys.stderr)
-        sys.exit(2)
-    if args.sweep:
-        sweep(args)
-        return
+def kernel_names(sv, head_probs):
+    return {sv.SV_K_GEMM_QKV: "gemm_qkv", sv.SV_K_ATTENTION: "attention", sv.SV_K_GEMM_O: "gemm_o",
+            sv.SV_K_GEMM_GATE_UP: "gemm_gate_up", sv.SV_K_GEMM_DOWN: "gemm_down",
+            sv.SV_K_GEMM_LM_HEAD: "gemm_lm_head",
+            sv.SV_K_SOFTMAX: "softmax" if head_probs else "row_stats",
+            sv.SV_K_ACCEPT: "accept", sv.SV_K_PREP: "prep"}
 
+
+def run_workload(cid, args, K, Wm, headline):
+    """Times K steps of workload cid after Wm warm-ups; returns the result
+    dict (and, for the headline workload, the oracle baseline)."""
     import numpy as np
     import torch
 
@@ -339,11 +339,9 @@ def main():
     from workloads import (accept_inputs, head_weights, hidden_states, kv_cache, layer_weights,
                            rng_for, uniforms_2m24, workload)
 
-    torch.cuda.set_device(0)
     hflags, amode = head_modes(args, sv)
-    wl = workload(args.workload)
+    wl = workload(cid)
     sh = wl.shape
-    K, Wm = args.steps, args.warmup
     log(f"workload {wl.cid} {wl.name}: B={wl.B} T={wl.T} wtype={wl.wtype}")
 
     t0 = time.perf_counter()
@@ -386,6 +384,8 @@ def main():
         del logits
     else:
         acc_in = accept_inputs(wl, V, alpha=wl.alphas[0] if wl.alphas else None)
+    # the acceptance-rate construction fixes the target rows themselves (not
+    # the head's output), so those workloads accept from staged probabilities
     p_alpha = tg.to_dev(acc_in["p"]) if (wl.draft == "alpha" or lm is None) else None
     draft = tg.to_dev(acc_in["draft"]) if wl.n_draft else torch.zeros(1, dtype=torch.int32, device="cuda")
     q = tg.to_dev(acc_in["q"]) if wl.n_draft else torch.zeros(1, V, device="cuda")
@@ -400,29 +400,50 @@ def main():
     # every step verifies the same state: step k reads and commits its own
     # copy of the starting KV lengths (no restore inside the timed region)
     kv_all = kv0.repeat(nsteps, 1).contiguous()
+    p_mode = sv.SV_ACCEPT_STOCHASTIC if p_alpha is not None else amode
+    na = sv.sv_accept_commit_workspace_bytes(wl.B, V, p_mode, list(wl.gamma))
+    ws_a = tg.workspace(na)
+
+    # Draft lengths: the planner splits the step's verify-token budget (the
+    # workload's T) over the live batch; each step's lengths go to the device
+    # through their own pinned slot.  A workload whose lengths the split does
+    # not reproduce (the ragged batch) keeps its own.
+    plan = sv.make_plan_params(sv.SV_PLAN_BUDGET, 64, budget_tokens=wl.T)
+    st, gplan, _ = sv.sv_plan_gamma(plan, wl.B)
+    plan_drives = st == 0 and gplan == [int(g) for g in wl.gamma]
+    g_pin = torch.tensor([int(g) for g in wl.gamma] * nsteps, dtype=torch.int32).reshape(
+        nsteps, max(1, wl.B)).pin_memory()
+    g_dev = torch.empty_like(g_pin, device="cuda")
     bss = []
     for k in range(nsteps):
         b_ = batch.struct()
         b_.kv_len = kv_all[k].data_ptr()
+        if plan_drives:
+            b_.gamma = g_dev[k].data_ptr()
         bss.append(b_)
-    p_mode = sv.SV_ACCEPT_STOCHASTIC if p_alpha is not None else amode
-    na = sv.sv_accept_commit_workspace_bytes(wl.B, V, p_mode, list(wl.gamma))
-    ws_a = tg.workspace(na)
-    glist = list(int(g) for g in wl.gamma)
-    plan = sv.make_plan_params(sv.SV_PLAN_BUDGET, 64, budget_tokens=24)
+    glist = [int(g) for g in wl.gamma]
+    gh = [None] * nsteps  # host copies of each step's planned lengths (kept alive)
 
     def step(k):
-        st, _, _ = sv.sv_plan_gamma(plan, wl.B)          # host: draft lengths for the live batch
-        assert st == 0
+        if plan_drives:
+            st_, gam, _ = sv.sv_plan_gamma(plan, wl.B)     # host: lengths for the live batch
+            assert st_ == 0 and len(gam) == wl.B
+            g_pin[k] = torch.as_tensor(gam, dtype=torch.int32)
+            g_dev[k].copy_(g_pin[k], non_blocking=True)
+            gh[k] = (ctypes.c_int32 * wl.B)(*gam)
+            bss[k].gamma_host = ctypes.cast(gh[k], ctypes.POINTER(ctypes.c_int32))
+            gl = gam
+        else:
+            gl = glist
         assert sv.sv_verify_layer(Ld, bss[k], x, y, 0, ws_d, nd, stream) == 0
         if lm is not None:
             assert sv.sv_verify_layer(Lh, bss[k], y, probs, hflags, ws_h, nh, stream) == 0
         p_acc = p_alpha if p_alpha is not None else probs
-        assert sv.sv_accept_commit(wl.B, V, p_mode, glist, batch.gamma, draft, p_acc, q, ua[k], us[k],
-                                   kv_all[k], acc_all[k], nxt_all[k], batch.err, ws_a, na,
+        assert sv.sv_accept_commit(wl.B, V, p_mode, gl, bss[k].gamma, draft, p_acc, q, ua[k],
+                                   us[k], kv_all[k], acc_all[k], nxt_all[k], batch.err, ws_a, na,
                                    stream) == 0
 
-    if args.copy_probe_mib > 0:
+    if headline and args.copy_probe_mib > 0:
         n = args.copy_probe_mib << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -480,13 +501,7 @@ def main():
 
     kernels = {}
     if not args.no_kernel_table:
-        names = {sv.SV_K_GEMM_QKV: "gemm_qkv", sv.SV_K_ATTENTION: "attention",
-                 sv.SV_K_GEMM_O: "gemm_o",
-                 sv.SV_K_GEMM_GATE_UP: "gemm_gate_up", sv.SV_K_GEMM_DOWN: "gemm_down",
-                 sv.SV_K_GEMM_LM_HEAD: "gemm_lm_head",
-                 sv.SV_K_SOFTMAX: "softmax" if args.head_probs else "row_stats",
-                 sv.SV_K_ACCEPT: "accept", sv.SV_K_PREP: "prep"}
-        for cls, nm in names.items():
+        for cls, nm in kernel_names(sv, args.head_probs).items():
             n = 10
             kv_all.copy_(kv0.expand_as(kv_all))   # the starting lengths again
             assert sv.sv_trace_begin(cls, n) == 0
@@ -507,29 +522,99 @@ def main():
                 kernels[nm] = entry
         log("kernels: " + json.dumps(kernels))
 
+    has_head = lm is not None
     cpu = None
-    if not args.no_cpu_baseline:
+    if headline and not args.no_cpu_baseline:
         log("timing the oracle on the host (bounded sample)...")
-        cpu = cpu_baseline(wl, W, Wlm, kc, vc, xh, acc_in)
+        del mats, lm, ws_d, x, y
+        torch.cuda.empty_cache()
+        per_rep = max(1, args.cpu_tokens // max(1, int(wl.gamma[0]) + 1))
+        cpu = cpu_baseline(wl, W, Wlm, kc, vc, xh, acc_in, per_rep)
         log(f"oracle: {cpu}")
 
+    res = {
+        "ms_per_step": round(ms, 5), "verify_tok_s": round(verify_tok_s, 2),
+        "accepted_tok_s": round(accepted_tok_s, 2), "tokens_per_step": round(tokens_per_step, 3),
+        "config": {"workload": wl.name, "B": wl.B,
+                   "gamma": glist if wl.B <= 16 else int(wl.gamma[0]), "T": wl.T,
+                   "ctx": int(wl.ctx[0]) if len(set(wl.ctx.tolist())) == 1 else "ragged",
+                   "weights": wl.wtype + (" packed" if packed else ""), "d": sh.d,
+                   "heads": f"{sh.n_q}q/{sh.n_kv}kv x {sh.hd}", "ffn": sh.ffn,
+                   "vocab": V if has_head else None,
+                   "acceptance": (wl.alphas[0] if wl.alphas else wl.draft),
+                   "head_output": "probabilities" if args.head_probs else "logits+row stats",
+                   "accept_reads": ("staged target probabilities (acceptance-rate construction)"
+                                    if p_alpha is not None else
+                                    ("the head's probabilities" if args.head_probs else
+                                     "the head's logits + row stats")),
+                   "gamma_source": "sv_plan_gamma (budget = T tokens), copied to the device each step"
+                                   if plan_drives else "the workload's own draft lengths"},
+        "roofline": roof, "step_roofline": step_roof, "kernels": kernels,
+    }
+    return res, cpu, wl
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=3,
+                    help="headline workload (default 3: the 27B-class bf16 layer, B=32, gamma=7)")
+    ap.add_argument("--extra", default="2,5",
+                    help="further workloads reported under 'workloads' (empty: none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=64,
+                    help="verify tokens per oracle step in the CPU baseline sample")
+    ap.add_argument("--no-kernel-table", action="store_true")
+    ap.add_argument("--head-probs", action="store_true",
+                    help="head writes probabilities and acceptance reads them (default: logits "
+                         "plus row (max, sum), acceptance forms the probabilities it reads)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time the step over a (B, gamma) grid on one layer shape instead, fit the "
+                         "step model per gamma and report the crossover batch")
+    ap.add_argument("--sweep-shape", default="9b", choices=("9b", "27b"))
+    ap.add_argument("--sweep-wtype", default="bf16", choices=("bf16", "int4"))
+    ap.add_argument("--sweep-ctx", type=int, default=2048)
+    ap.add_argument("--sweep-b", default="1,2,4,8,16,32,64,128,256")
+    ap.add_argument("--sweep-gamma", default="0,1,2,3,4,5,7")
+    ap.add_argument("--sweep-out", default="")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="before the steps, copy a buffer of this many MiB device to device three "
+                         "times (the known-size reference for HBM traffic counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: the verify path runs on one GPU only (asked for --gpus {args.gpus}); "
+              "sharding across GPUs is not implemented", file=sys.stderr)
+        sys.exit(2)
+    if args.sweep:
+        sweep(args)
+        return
+
+    import torch
+    torch.cuda.set_device(0)
+    K, Wm = args.steps, args.warmup
+    res, cpu, wl = run_workload(args.workload, args, K, Wm, headline=True)
+    others = {}
+    for c in [int(v) for v in args.extra.split(",") if v.strip()]:
+        if c == args.workload:
+            continue
+        torch.cuda.empty_cache()
+        r, _, w = run_workload(c, args, K, Wm, headline=False)
+        others[w.name] = r
     out = {
-        "metric": METRIC, "value": round(verify_tok_s, 2), "unit": "verify tokens/s",
-        "n_gpus": 1, "steps": K, "warmup": Wm, "ms_per_step": round(ms, 5),
+        "metric": METRIC, "value": res["verify_tok_s"], "unit": "verify tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": Wm, "ms_per_step": res["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if wl.wtype != "f32" else "f32", "data": "synthetic",
-        "config": {"workload": wl.name, "B": wl.B, "gamma": glist if wl.B <= 16 else int(wl.gamma[0]),
-                   "T": wl.T, "ctx": int(wl.ctx[0]) if len(set(wl.ctx.tolist())) == 1 else "ragged",
-                   "weights": wl.wtype + (" packed" if packed else ""), "d": sh.d, "heads": f"{sh.n_q}q/{sh.n_kv}kv x {sh.hd}",
-                   "ffn": sh.ffn, "vocab": V if lm is not None else None,
-                   "acceptance": (wl.alphas[0] if wl.alphas else wl.draft),
-                   "head_output": "probabilities" if args.head_probs else "logits+row stats"},
-        "accepted_tok_s": round(accepted_tok_s, 2),
-        "tokens_per_step": round(tokens_per_step, 3),
-        "roofline": roof,
-        "step_roofline": step_roof,
-        "kernels": kernels,
+        "config": res["config"],
+        "accepted_tok_s": res["accepted_tok_s"],
+        "tokens_per_step": res["tokens_per_step"],
+        "roofline": res["roofline"],
+        "step_roofline": res["step_roofline"],
+        "kernels": res["kernels"],
         "cpu_baseline": cpu,
+        "workloads": others,
     }
     print(json.dumps(out), flush=True)
 

@@ -68,7 +68,9 @@ typedef int32_t sv_status;
 /* Device-side error bits, OR-ed into *err_flag. */
 #define SV_DEV_ERR_BAD_TOKEN 1   /* token id outside [0, vocab) */
 #define SV_DEV_ERR_KV_OVERFLOW 2 /* kv_len[i] + gamma_i + 1 > kv_cap */
-#define SV_DEV_ERR_CTX_BOUND 4   /* kv_len[i] > max_ctx (work beyond the bound skipped) */
+#define SV_DEV_ERR_CTX_BOUND 4   /* kv_len[i] > max_ctx: that sequence gets no attention
+                                    work and its output rows are unspecified; the other
+                                    sequences' results are unaffected */
 
 /* Layer kinds (sv_layer.kind). */
 #define SV_LAYER_EMBED 0   /* x[t] = E[token[t]] */
@@ -154,7 +156,8 @@ typedef struct sv_batch {
   int32_t B;                 /* sequences, >= 0 */
   int32_t T;                 /* stacked tokens = sum(gamma_i + 1) */
   int32_t max_ctx;           /* upper bound on every kv_len[i] (sizes the attention grid;
-                                a larger kv_len sets SV_DEV_ERR_CTX_BOUND) */
+                                a sequence with a larger kv_len is skipped by attention
+                                and sets SV_DEV_ERR_CTX_BOUND) */
   int32_t kv_cap;            /* cache capacity per sequence, multiple of 32 */
   const int32_t *gamma_host; /* (host) [B] draft counts, >= 0 */
   const int32_t *gamma;      /* [B] the same counts on the device */
@@ -192,6 +195,15 @@ sv_status sv_verify_layer_workspace_bytes(const sv_layer *layer, const sv_batch 
                                           int32_t flags, size_t *bytes);
 
 /* One verify pass through one layer.
+ *
+ * Defined by: "Speculative Decoding at High Batch Size: Where the 3x Speedup
+ * Turns Into a Tax", section "Why do the headline speedups all come from
+ * batch 1?" (one target pass checks every drafted token of every sequence
+ * with a single read of the weights), and "Speculative Decoding and Batching
+ * Compete for the Same Compute Slack on RDNA4", section "The batch also goes
+ * ragged" and its FAQ on the ragged tensor problem (each sequence keeps its
+ * own draft count, positions, causal mask and KV length; no padding).
+ *
  *   DECODER: x_in bf16 [T][d] -> y_out bf16 [T][d]; appends K/V rows.
  *   HEAD:    x_in bf16 [T][d] -> y_out fp32 [T][vocab] probabilities
  *            (or logits with SV_HEAD_LOGITS; or logits followed by the rows'
@@ -220,6 +232,16 @@ sv_status sv_accept_commit_workspace_bytes(int32_t B, int32_t V, int32_t mode,
 
 /* Acceptance, resampling and commit for every sequence (rejection sampling
  * in the sense of Leviathan, Kalman and Matias).
+ *
+ * Defined by: the speculative-decoding primer (splicedso.github.io/learn),
+ * section "The idea" (keep the drafts up to the first rejection, then one
+ * token of the target's own: 3 of 4 accepted gives 4 tokens, none gives 1);
+ * "Speculative Decoding at High Batch Size: Where the 3x Speedup Turns Into
+ * a Tax", section "Why do the headline speedups all come from batch 1?" (the
+ * rejection-sampling rule keeps the target's output distribution); and
+ * "Speculative Decoding and Batching Compete for the Same Compute Slack on
+ * RDNA4", section "The batch also goes ragged" (sequences accept different
+ * lengths; only each sequence's KV length is committed, nothing realigned).
  *
  * Rows: p row q_start[i] + j (j = 0..gamma_i) is the target distribution of
  * the (j+1)-th new token of sequence i; q row q_start[i] - i + j
@@ -266,7 +288,19 @@ typedef struct sv_plan_params {
   const double *alpha;     /* (host) [n_alpha] */
 } sv_plan_params;
 
-/* gamma_out (host) [B_live] receives the draft lengths.
+/* Draft lengths for the live batch.
+ *
+ * Defined by: BUDGET -- "Speculative Decoding and Batching Compete for the
+ * Same Compute Slack on RDNA4", sections "The budget is fixed, and the batch
+ * is inside it" and "What the budget says to build" (Table 1: the slack of
+ * one decode step, in tokens, less one committed token per live sequence,
+ * split over the sequences); SPEEDUP -- "Speculative Decoding at High Batch
+ * Size: Where the 3x Speedup Turns Into a Tax", sections "What does one
+ * speculative iteration actually cost?" (expected tokens and the speedup
+ * ratio) and "How does the roofline model work?" (step time and the
+ * crossover batch B*).
+ *
+ * gamma_out (host) [B_live] receives the draft lengths.
  * BUDGET: n = budget tokens; if B_live >= n every gamma is 0, otherwise the
  *   n - B_live free tokens are split evenly (floor), the first
  *   (n - B_live) mod B_live sequences getting one more if fill_remainder,

@@ -17,11 +17,12 @@ Sources:
 """
 from __future__ import annotations
 
+import dataclasses
 import math
 
 __all__ = [
     "expected_tokens_indep", "expected_tokens_cond", "decaying_alphas",
-    "step_time", "speedup", "crossover_batch", "budget_tokens_from_rates",
+    "StepModel", "speedup", "crossover_batch", "budget_tokens_from_rates",
     "plan_budget", "plan_speedup", "best_gamma",
 ]
 
@@ -54,29 +55,46 @@ def decaying_alphas(n: int, first: float = 0.94, step: float = 0.07) -> list:
     return [max(0.0, first - step * k) for k in range(n)]
 
 
-def step_time(b: float, tokens_per_seq: float, frac: float, t_w: float, k: float,
-              c: float) -> float:
-    """Roofline step time: max(frac*t_w + b*k, frac*b*tokens_per_seq*c).
+@dataclasses.dataclass(frozen=True)
+class StepModel:
+    """The roofline step model of [tax], "How does the roofline model work?".
 
-    t_w = weight bytes / bandwidth, k = per-sequence KV bytes / bandwidth,
-    c = 2 * params / peak flops per token.  The KV term is not scaled by frac,
-    as in the page's model (a drafter of 4 % of the target's size reads its
-    own KV for every sequence)."""
-    mem = frac * t_w + b * k
-    cmp_ = frac * b * tokens_per_seq * c
-    return max(mem, cmp_)
+    A pass over b sequences that each carry n tokens, through a model whose
+    size is `size` times the target's, takes the larger of two times: reading
+    its weights (size * t_w) plus every sequence's KV cache (b * k -- a
+    drafter reads its own KV per sequence, so this term is not scaled by
+    size), and its arithmetic (size * c per token, b * n tokens).
+
+    t_w: weight-read time of the target, k: KV-read time per sequence,
+    c: compute time per token (2 * params / peak flops)."""
+    t_w: float
+    k: float
+    c: float
+
+    def pass_time(self, b: float, n: float, size: float = 1.0) -> float:
+        reads = size * self.t_w + b * self.k
+        arithmetic = size * self.c * b * n
+        return reads if reads >= arithmetic else arithmetic
+
+    def iteration_time(self, b: float, gamma: int, draft_frac: float) -> float:
+        """One speculative iteration: the target verifies gamma + 1 tokens per
+        sequence, a drafter of draft_frac the target's size proposes gamma."""
+        return self.pass_time(b, gamma + 1) + self.pass_time(b, gamma, draft_frac)
+
+    def speedup(self, b: float, gamma: int, e_tokens: float, draft_frac: float = 0.04) -> float:
+        """[tax], "What does one speculative iteration actually cost?": tokens
+        per iteration times the plain decode step, over the iteration's time
+        (throughput relative to plain decoding at the same batch).  gamma = 0
+        is plain decoding itself, exactly 1."""
+        if gamma == 0:
+            return 1.0
+        return e_tokens * self.pass_time(b, 1) / self.iteration_time(b, gamma, draft_frac)
 
 
 def speedup(b: float, gamma: int, e_tokens: float, t_w: float, k: float, c: float,
             draft_frac: float = 0.04) -> float:
-    """Throughput relative to plain decoding at the same batch:
-    E * t(B, 1) / (t(B, gamma + 1) + t_draft(B, gamma)).  gamma = 0 means
-    speculation off, i.e. exactly 1."""
-    if gamma == 0:
-        return 1.0
-    base = step_time(b, 1, 1.0, t_w, k, c)
-    spec = step_time(b, gamma + 1, 1.0, t_w, k, c) + step_time(b, gamma, draft_frac, t_w, k, c)
-    return e_tokens * base / spec
+    """StepModel(t_w, k, c).speedup(...)."""
+    return StepModel(t_w, k, c).speedup(b, gamma, e_tokens, draft_frac)
 
 
 def crossover_batch(gamma: int, t_w: float, k: float, c: float) -> float:

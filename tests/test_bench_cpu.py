@@ -14,10 +14,26 @@ def test_cpu_baseline_runs_whole_steps():
     kc, vc = kv_cache(sh, wl.ctx, wl.cap, wl.seed)
     xh = hidden_states(wl.T, sh.d, wl.seed)
     acc_in = accept_inputs(wl, sh.vocab)
-    r = bench.cpu_baseline(wl, W, Wlm, kc, vc, xh, acc_in, min_seconds=0.0, max_reps=2)
+    r = bench.cpu_baseline(wl, W, Wlm, kc, vc, xh, acc_in, seqs_per_rep=1, min_seconds=0.0,
+                           max_reps=2)
     assert r["kind"] == "oracle" and r["unit"] == "verify tokens/s"
-    assert r["value"] > 0 and r["cores"] >= 1
-    assert r["sample"].startswith(f"1 whole verify step(s) of the workload ({wl.T} verify tokens)")
+    assert r["value"] > 0 and r["cores"] >= 1 and r["cpu"]
+    assert r["sample"].startswith(f"1 verify step(s) of the first 1 of the workload's {wl.B} "
+                                  f"sequences ({wl.T} verify tokens in all)")
+
+
+def test_cpu_baseline_sample_of_a_larger_batch():
+    from workloads import SHAPES, custom_workload
+    sh = SHAPES["tiny"]
+    wl = custom_workload(sh, "f32", [2, 1, 3], [10, 20, 30], draft="noise", seed=5)
+    W = layer_weights(sh, wl.wtype, wl.seed)
+    Wlm = head_weights(sh, wl.wtype, wl.seed)
+    kc, vc = kv_cache(sh, wl.ctx, wl.cap, wl.seed)
+    xh = hidden_states(wl.T, sh.d, wl.seed)
+    acc_in = accept_inputs(wl, sh.vocab)
+    r = bench.cpu_baseline(wl, W, Wlm, kc, vc, xh, acc_in, seqs_per_rep=2, min_seconds=0.0,
+                           max_reps=1)
+    assert "first 2 of the workload's 3 sequences (5 verify tokens in all)" in r["sample"]
 
 
 def test_step_model_fit_recovers_constants():

@@ -35,6 +35,21 @@ def test_accept_bit_exact_workload_shapes(cid):
 
 
 @pytest.mark.parametrize("greedy", [False, True])
+def test_accept_bit_exact_large_batch(greedy):
+    """Batches above the size whose token map travels with the launch: the
+    kernel builds each sequence's row offsets on the device."""
+    sh = SHAPES["tiny"]
+    rng = np.random.default_rng(77)
+    gam = rng.integers(0, 5, size=300)
+    ctx = rng.integers(0, 1000, size=300)
+    wl = custom_workload(sh, "f32", gam, ctx, draft="noise", seed=77)
+    V = 3001
+    inp = accept_inputs(wl, V, target_logits=rng.standard_normal((wl.T, V)).astype(np.float32) * 2)
+    a, _ = _exact(wl, inp, V, greedy=greedy)
+    say(f"accept B=300 greedy={greedy}: mean accepted {a.mean():.3f}")
+
+
+@pytest.mark.parametrize("greedy", [False, True])
 def test_accept_ragged_small_vocab(greedy):
     sh = SHAPES["tiny"]
     for seed in range(6):

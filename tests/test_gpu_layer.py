@@ -376,6 +376,37 @@ def test_kv_overflow_flagged_and_contained():
     np.testing.assert_array_equal(dec.batch.k_logical(1)[:, :222], sentinel_before[1][:, :222])
 
 
+def test_ctx_bound_flagged_and_contained():
+    """A sequence longer than the batch's max_ctx (here by enough that its keys
+    would span more than the attention merge's 32 chunks) gets no attention
+    work and sets SV_DEV_ERR_CTX_BOUND; every other sequence's rows, and its
+    appended K/V, still match the oracle."""
+    shape = Shape(512, 8, 2, 128, 1024, 3000)
+    B = 40
+    gamma = [1] * B
+    gamma[1] = 15                       # 64 query rows per KV head: the query-tiled kernel
+    gamma[7] = 15
+    ctx = [10 + 3 * i for i in range(B)]
+    ctx[1] = 13000                      # 51 chunks of 256 keys
+    cap = 13024
+    wl = custom_workload(shape, "bf16", gamma, ctx, seed=23, cap=cap)
+    dec = GpuDecoder(wl, max_ctx=1000)
+    xh = hidden_states(wl.T, shape.d, wl.seed)
+    y = dec.run(tg.to_dev(xh))
+    torch.cuda.synchronize()
+    assert dec.batch.err.item() == sv.SV_DEV_ERR_CTX_BOUND
+    others = [i for i in range(B) if i != 1]
+    ref = dec.oracle(xh, seqs=others)
+    yh = dev_bf16_to_f64(y)
+    err = rel_rows(yh[ref.rows], ref.y)
+    say(f"ctx bound: {len(others)} other sequences, y rel err {err:.2e}")
+    assert err < TOL["bf16"]
+    for i in (0, 7, B - 1):
+        c, n = int(ctx[i]), gamma[i] + 1
+        kg = OF.bf16_to_f64(dec.batch.k_logical(i)[:, c:c + n])
+        assert rel_rows(kg.reshape(-1, 128), ref.k_new[i].reshape(-1, 128)) < TOL["bf16"]
+
+
 @pytest.mark.parametrize("tiling", [None, "qkv:1:2:0,o:1:2:0,gu:1:2:0,down:1:2:0,head:1:2:0",
                                     "qkv:2:2:1,o:1:4:1,gu:1:2:1,down:3:4:1,head:1:2:1",
                                     "qkv:1:2:2,o:3:2:2,gu:1:2:2,down:2:2:2,head:2:2:2",

@@ -61,7 +61,7 @@ def test_crossover_is_where_step_turns_compute_bound(G):
     for g in (3, 7):
         bs = plan.crossover_batch(g, tw, k, c)
         lo, hi = math.floor(bs), math.ceil(bs)
-        t = lambda b: plan.step_time(b, g + 1, 1.0, tw, k, c)  # noqa: E731
+        t = lambda b: plan.StepModel(tw, k, c).pass_time(b, g + 1)  # noqa: E731
         assert t(lo) == pytest.approx(tw + lo * k)           # memory side
         assert t(hi) == pytest.approx(hi * (g + 1) * c)      # compute side
 

@@ -208,3 +208,15 @@ def test_bf16_rounding_matches_torch():
     ties = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 0.0])
     np.testing.assert_array_equal(OF.round_bf16(ties), [1.0, 1 + 2 ** -6, -1.0, 0.0])
     np.testing.assert_array_equal(OF.bf16_to_f64(f32_to_bf16_bits(a)), ref)
+
+
+def test_embed_selects_rows_by_token():
+    # a hand-written table: row r holds r + 0.25 c, so each gathered value names
+    # its row and column; bf16 storage decodes to the same values
+    table = np.array([[r + 0.25 * c for c in range(4)] for r in range(5)], np.float32)
+    got = OV.embed(table, [3, 0, 3, 4])
+    np.testing.assert_array_equal(got, [[3, 3.25, 3.5, 3.75], [0, 0.25, 0.5, 0.75],
+                                        [3, 3.25, 3.5, 3.75], [4, 4.25, 4.5, 4.75]])
+    got_bf = OV.embed(f32_to_bf16_bits(table), np.array([1, 2], np.int32))
+    np.testing.assert_array_equal(got_bf, [[1, 1.25, 1.5, 1.75], [2, 2.25, 2.5, 2.75]])
+    assert OV.embed(table, []).shape == (0, 4)

@@ -637,6 +637,7 @@ extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const
     pp.hd = hd;
     pp.items = reinterpret_cast<int4 *>(ws + pl.off_items);
     pp.max_items = pl.attn_items;
+    pp.max_ctx = b->max_ctx;
     pp.xp = pl.pk_qkv ? reinterpret_cast<uint16_t *>(ws + pl.off_xp) : nullptr;
     pp.xp_ntt = frag_tiles(pl.qkv);
     pp.err = b->err_flag;
@@ -834,13 +835,12 @@ namespace {
 constexpr int kAcceptChunk = 4096;
 constexpr int kAcceptChunkWide = 8192;
 
-struct AcceptPlan {
-  long long T = 0, nd = 0;
-  int nchunk = 0, chunk = kAcceptChunk;
-  size_t off_parts = 0, off_acc = 0, bytes = 0;
-};
+}  // namespace
 
-sv_status plan_accept(int32_t B, int32_t V, int32_t mode, const int32_t *gamma_host, AcceptPlan &ap) {
+// counter_bytes: room for the per-sequence arrival counters at the start of
+// the scratch memory (the shared workspace layout reserves kCounterBytes).
+sv_status sv::plan_accept(int32_t B, int32_t V, int32_t mode, const int32_t *gamma_host, AcceptPlan &ap,
+                      size_t counter_bytes) {
   if (B < 0 || V <= 0) return SV_ERR_INVALID_ARG;
   if (mode & ~(0xFF | SV_ACCEPT_FROM_LOGITS)) return SV_ERR_INVALID_ARG;
   mode &= 0xFF;
@@ -856,7 +856,7 @@ sv_status plan_accept(int32_t B, int32_t V, int32_t mode, const int32_t *gamma_h
   ap.chunk = (long long)B * ((V + kAcceptChunk - 1) / kAcceptChunk) > 1024 ? kAcceptChunkWide : kAcceptChunk;
   ap.nchunk = (V + ap.chunk - 1) / ap.chunk;
   const long long rows = mode == SV_ACCEPT_GREEDY ? ap.T : B;
-  size_t off = kCounterBytes;  // shared-workspace layout: counters first
+  size_t off = counter_bytes;  // counters first
   ap.off_parts = off;
   off = align_up(off + (size_t)rows * ap.nchunk * sizeof(AcceptPart));
   ap.off_acc = off;
@@ -864,45 +864,46 @@ sv_status plan_accept(int32_t B, int32_t V, int32_t mode, const int32_t *gamma_h
   ap.bytes = off;
   return SV_OK;
 }
-}  // namespace
 
 extern "C" sv_status sv_accept_commit_workspace_bytes(int32_t B, int32_t V, int32_t mode,
                                                       const int32_t *gamma_host, size_t *bytes) {
   if (!bytes) return SV_ERR_INVALID_ARG;
   AcceptPlan ap;
-  const sv_status st = plan_accept(B, V, mode, gamma_host, ap);
+  const sv_status st = plan_accept(B, V, mode, gamma_host, ap, kCounterBytes);
   if (st != SV_OK) return st;
   *bytes = ap.bytes;
   return SV_OK;
 }
 
-extern "C" sv_status sv_accept_commit(int32_t B, int32_t V, int32_t mode, const int32_t *gamma_host,
-                                      const int32_t *gamma, const int32_t *draft, const float *p,
-                                      const float *q, const float *u_acc, const float *u_samp,
-                                      int32_t *kv_len, int32_t *accepted, int32_t *next_token,
-                                      int32_t *err_flag, void *workspace, size_t workspace_bytes,
-                                      void *stream) {
-  AcceptPlan ap;
-  sv_status st = plan_accept(B, V, mode, gamma_host, ap);
-  if (st != SV_OK) return st;
+// Host checks of an acceptance call's pointers (after plan_accept).
+sv_status sv::check_accept_args(int32_t B, int32_t mode, const AcceptPlan &ap, const int32_t *gamma,
+                            const int32_t *draft, const float *p, const float *q, const float *u_acc,
+                            const float *u_samp, const int32_t *kv_len, const int32_t *accepted,
+                            const int32_t *next_token) {
   if (B == 0) return SV_OK;
   if (!gamma || !p || !kv_len || !accepted || !next_token) return SV_ERR_INVALID_ARG;
   if (ap.nd > 0 && !draft) return SV_ERR_INVALID_ARG;
-  const bool from_logits = (mode & SV_ACCEPT_FROM_LOGITS) != 0;
-  mode &= 0xFF;
-  if (mode == SV_ACCEPT_STOCHASTIC) {
+  if ((mode & 0xFF) == SV_ACCEPT_STOCHASTIC) {
     if (!u_samp) return SV_ERR_INVALID_ARG;
     if (ap.nd > 0 && (!q || !u_acc)) return SV_ERR_INVALID_ARG;
   }
-  if (!workspace || workspace_bytes < ap.bytes) return SV_ERR_WORKSPACE;
-  unsigned char *ws = static_cast<unsigned char *>(workspace);
+  return SV_OK;
+}
+
+// Enqueue the acceptance kernel with its scratch memory at ws (counters at
+// ws, zero on entry; the rest at the plan's offsets).
+sv_status sv::run_accept(int32_t B, int32_t V, int32_t mode, const int32_t *gamma_host, const AcceptPlan &ap,
+                     const int32_t *gamma, const int32_t *draft, const float *p, const float *q,
+                     const float *u_acc, const float *u_samp, int32_t *kv_len, int32_t *accepted,
+                     int32_t *next_token, int32_t *err_flag, unsigned char *ws, hipStream_t stream) {
+  const bool from_logits = (mode & SV_ACCEPT_FROM_LOGITS) != 0;
   AcceptParams a;
   std::memset(&a, 0, sizeof(a));
   a.B = B;
   a.V = V;
   a.T = (int)ap.T;
   a.nd = (int)ap.nd;
-  a.mode = mode;
+  a.mode = mode & 0xFF;
   a.chunk = ap.chunk;
   a.nchunk = ap.nchunk;
   a.gamma = gamma;
@@ -928,9 +929,26 @@ extern "C" sv_status sv_accept_commit(int32_t B, int32_t V, int32_t mode, const 
       qs += gamma_host[i] + 1;
     }
   }
-  (void)hipGetLastError();
-  const hipError_t e = launch_accept(a, static_cast<hipStream_t>(stream));
+  const hipError_t e = launch_accept(a, stream);
   return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+extern "C" sv_status sv_accept_commit(int32_t B, int32_t V, int32_t mode, const int32_t *gamma_host,
+                                      const int32_t *gamma, const int32_t *draft, const float *p,
+                                      const float *q, const float *u_acc, const float *u_samp,
+                                      int32_t *kv_len, int32_t *accepted, int32_t *next_token,
+                                      int32_t *err_flag, void *workspace, size_t workspace_bytes,
+                                      void *stream) {
+  AcceptPlan ap;
+  sv_status st = plan_accept(B, V, mode, gamma_host, ap, kCounterBytes);
+  if (st != SV_OK) return st;
+  st = check_accept_args(B, mode, ap, gamma, draft, p, q, u_acc, u_samp, kv_len, accepted, next_token);
+  if (st != SV_OK || B == 0) return st;
+  if (!workspace || workspace_bytes < ap.bytes) return SV_ERR_WORKSPACE;
+  (void)hipGetLastError();
+  return run_accept(B, V, mode, gamma_host, ap, gamma, draft, p, q, u_acc, u_samp, kv_len, accepted,
+                    next_token, err_flag, static_cast<unsigned char *>(workspace),
+                    static_cast<hipStream_t>(stream));
 }
 
 extern "C" sv_status sv_set_gemm_tuning(const char *spec) {

@@ -104,6 +104,7 @@ __device__ inline void set_err(int *err, int bits) {
 // Kernel parameter blocks.
 
 constexpr int kMaxB = 65536;        // sequences per call (LDS token-map limit)
+constexpr int kAttnMaxChunks = 32;  // attention work items (key chunks) per sequence
 constexpr int kScanMaxB = 4096;     // kernels that keep the full map in LDS
 
 enum RowMap { RM_LINEAR = 0, RM_ROPE_PAIRS = 1, RM_SWIGLU = 2 };
@@ -172,6 +173,7 @@ struct PrepParams {
   int hd;
   int4 *items;         // [max_items][2] attention work items (see AttnParams)
   int max_items;
+  int max_ctx;         // the host's bound on kv_len (a longer sequence is flagged, not attended)
   uint16_t *xp;        // x in fragment layout for the QKV GEMM (nullptr: none)
   int xp_ntt;
   int *err;
@@ -282,6 +284,24 @@ __device__ __forceinline__ float prob_of_logit(float l, float Mk, float S) {
 }
 hipError_t launch_embed(const EmbedParams &p, hipStream_t s);
 hipError_t launch_accept(const AcceptParams &p, hipStream_t s);
+
+// Acceptance call geometry and its scratch layout: arrival counters first
+// (counter_bytes of room), then the per-chunk results and the spill space.
+struct AcceptPlan {
+  long long T = 0, nd = 0;
+  int nchunk = 0, chunk = 0;
+  size_t off_parts = 0, off_acc = 0, bytes = 0;
+};
+sv_status plan_accept(int32_t B, int32_t V, int32_t mode, const int32_t *gamma_host, AcceptPlan &ap,
+                      size_t counter_bytes);
+sv_status check_accept_args(int32_t B, int32_t mode, const AcceptPlan &ap, const int32_t *gamma,
+                            const int32_t *draft, const float *p, const float *q, const float *u_acc,
+                            const float *u_samp, const int32_t *kv_len, const int32_t *accepted,
+                            const int32_t *next_token);
+sv_status run_accept(int32_t B, int32_t V, int32_t mode, const int32_t *gamma_host, const AcceptPlan &ap,
+                     const int32_t *gamma, const int32_t *draft, const float *p, const float *q,
+                     const float *u_acc, const float *u_samp, int32_t *kv_len, int32_t *accepted,
+                     int32_t *next_token, int32_t *err_flag, unsigned char *ws, hipStream_t stream);
 
 // Kernel-timing trace hooks (host).
 void trace_before(int kernel_class, hipStream_t s);

@@ -36,17 +36,24 @@ double expected_tokens(const sv_plan_params &p, int g) {
   return e;
 }
 
-double step_time(double b, double n, double frac, const sv_plan_params &p) {
-  const double mem = frac * p.t_w_ms + b * p.k_ms;
-  const double cmp = frac * b * n * p.c_ms;
-  return mem > cmp ? mem : cmp;
-}
+// The roofline step model: a pass over b sequences of n tokens each, through
+// a model `size` times the target's, costs the larger of its reads (weights
+// scaled by size, every sequence's KV not) and its arithmetic.
+struct StepModel {
+  double t_w, k, c;
+  double pass(double b, double n, double size) const {
+    const double reads = size * t_w + b * k, arithmetic = size * c * b * n;
+    return reads >= arithmetic ? reads : arithmetic;
+  }
+  // target verifies g + 1 tokens per sequence, drafter of size f proposes g
+  double iteration(double b, int g, double f) const { return pass(b, g + 1.0, 1.0) + pass(b, g, f); }
+};
 
+// Throughput relative to plain decoding at the same batch (g = 0: exactly 1).
 double speedup(double b, int g, const sv_plan_params &p) {
   if (g == 0) return 1.0;
-  const double base = step_time(b, 1, 1.0, p);
-  const double spec = step_time(b, g + 1, 1.0, p) + step_time(b, g, p.draft_frac, p);
-  return expected_tokens(p, g) * base / spec;
+  const StepModel m{p.t_w_ms, p.k_ms, p.c_ms};
+  return expected_tokens(p, g) * m.pass(b, 1.0, 1.0) / m.iteration(b, g, p.draft_frac);
 }
 
 double crossover(int g, const sv_plan_params &p) {

@@ -69,7 +69,13 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams p) {
     gs[i] = g;
     ks[i] = kv;
     qs[i] = g + 1;
-    cs[i] = (kv + g + 1 + p.chunk - 1) / p.chunk;
+    // a sequence past the host's context bound would need more chunks than
+    // the attention merge holds (and than the grid was sized for): it gets no
+    // attention work and is flagged; the other sequences are unaffected
+    const int nchunks = (kv + g + 1 + p.chunk - 1) / p.chunk;
+    const bool over = kv > p.max_ctx || nchunks > kAttnMaxChunks;
+    cs[i] = over ? 0 : nchunks;
+    if (over && t == 0) set_err(p.err, SV_DEV_ERR_CTX_BOUND);
   }
   __syncthreads();
   const int total_t = block_exscan(qs, p.B, tmp);
@@ -103,7 +109,8 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams p) {
     if (tid == 0) {
       p.q_start[p.B] = total_t;
       p.chunk_start[p.B] = total_c;
-      // the attention grid is sized from the host's context bound
+      // the attention grid is sized from the host's context bound and the
+      // host's draft counts (a device count above them can still overflow it)
       if (total_c > p.max_items) set_err(p.err, SV_DEV_ERR_CTX_BOUND);
     }
   }
