@@ -64,6 +64,8 @@ typedef int32_t sv_status;
 #define SV_ERR_UNSUPPORTED (-2) /* a shape or dtype the library does not handle */
 #define SV_ERR_WORKSPACE (-3)   /* workspace missing or smaller than required */
 #define SV_ERR_HIP (-4)         /* a kernel launch failed */
+#define SV_ERR_TOO_LARGE (-5)   /* the call needs more scratch than the fixed array of
+                                   sv_accept_commit_noalloc holds */
 
 /* Device-side error bits, OR-ed into *err_flag. */
 #define SV_DEV_ERR_BAD_TOKEN 1   /* token id outside [0, vocab) */
@@ -268,6 +270,25 @@ sv_status sv_accept_commit(int32_t B, int32_t V, int32_t mode, const int32_t *ga
                            int32_t *kv_len, int32_t *accepted, int32_t *next_token,
                            int32_t *err_flag, void *workspace, size_t workspace_bytes,
                            void *stream);
+
+/* sv_accept_commit without a workspace, for callers that cannot allocate
+ * device memory or hand the library a workspace: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Arguments
+ * and results are those of sv_accept_commit (bit-identical outputs).  The
+ * scratch memory comes from a fixed device array of
+ * SV_ACCEPT_NOALLOC_SCRATCH_BYTES that each GPU holds from the library's first
+ * call on it until the process ends; the call allocates and frees nothing.
+ * Every call on one GPU shares that array, so calls that overlap in time on
+ * one GPU (other streams, other threads) race: serialise them.  A call whose
+ * scratch would exceed the array (about B * 4 + rows * ceil(V / chunk) * 24 +
+ * (B + T) * 4 bytes, rows = B stochastic or T greedy, chunk 4096 or 8192)
+ * returns SV_ERR_TOO_LARGE before enqueueing anything. */
+#define SV_ACCEPT_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+sv_status sv_accept_commit_noalloc(int32_t B, int32_t V, int32_t mode, const int32_t *gamma_host,
+                                   const int32_t *gamma, const int32_t *draft, const float *p,
+                                   const float *q, const float *u_acc, const float *u_samp,
+                                   int32_t *kv_len, int32_t *accepted, int32_t *next_token,
+                                   int32_t *err_flag, void *stream);
 
 /* Draft-length planning (host only). */
 #define SV_PLAN_BUDGET 0  /* keep sum(gamma_i + 1) within the compute-slack budget */

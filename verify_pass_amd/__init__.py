@@ -20,6 +20,8 @@ SV_ERR_INVALID_ARG = -1
 SV_ERR_UNSUPPORTED = -2
 SV_ERR_WORKSPACE = -3
 SV_ERR_HIP = -4
+SV_ERR_TOO_LARGE = -5
+SV_ACCEPT_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 SV_DEV_ERR_BAD_TOKEN = 1
 SV_DEV_ERR_KV_OVERFLOW = 2
@@ -82,6 +84,10 @@ _SIGNATURES = [
      [C.c_int32, C.c_int32, C.c_int32, C.POINTER(C.c_int32), C.c_void_p, C.c_void_p, C.c_void_p,
       C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
       C.c_void_p, C.c_size_t, C.c_void_p]),
+    ("sv_accept_commit_noalloc", C.c_int32,
+     [C.c_int32, C.c_int32, C.c_int32, C.POINTER(C.c_int32), C.c_void_p, C.c_void_p, C.c_void_p,
+      C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+      C.c_void_p]),
     ("sv_packed_matrix_bytes", C.c_int32,
      [C.c_int32, C.c_int32, C.c_int32, C.POINTER(C.c_size_t), C.POINTER(C.c_size_t)]),
     ("sv_pack_matrix", C.c_int32,
@@ -168,6 +174,14 @@ def sv_accept_commit(B, V, mode, gamma_host, gamma, draft, p, q, u_acc, u_samp, 
                                  _ptr(u_acc), _ptr(u_samp), _ptr(kv_len), _ptr(accepted),
                                  _ptr(next_token), _ptr(err_flag), _ptr(workspace),
                                  workspace_bytes, _ptr(stream))
+
+
+def sv_accept_commit_noalloc(B, V, mode, gamma_host, gamma, draft, p, q, u_acc, u_samp, kv_len,
+                             accepted, next_token, err_flag, stream) -> int:
+    g = (C.c_int32 * max(1, len(gamma_host)))(*[int(x) for x in gamma_host])
+    return _lib.sv_accept_commit_noalloc(B, V, mode, g, _ptr(gamma), _ptr(draft), _ptr(p), _ptr(q),
+                                         _ptr(u_acc), _ptr(u_samp), _ptr(kv_len), _ptr(accepted),
+                                         _ptr(next_token), _ptr(err_flag), _ptr(stream))
 
 
 def sv_packed_matrix_bytes(wtype: int, N: int, K: int):

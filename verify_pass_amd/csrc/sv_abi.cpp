@@ -93,6 +93,7 @@ extern "C" const char *sv_status_string(sv_status s) {
     case SV_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case SV_ERR_WORKSPACE: return "workspace missing or too small";
     case SV_ERR_HIP: return "HIP launch failure";
+    case SV_ERR_TOO_LARGE: return "the call needs more scratch than the fixed no-allocation array holds";
     default: return "unknown status";
   }
 }
