@@ -281,6 +281,18 @@ def sweep(args):
             row = {"B": B, "gamma": g, "T": T, "ms": round(ms, 5),
                    "verify_tok_s": round(T / ms * 1e3, 1),
                    "accepted_tok_s_alpha0.8": round(B * expected_tokens(0.8, g) / ms * 1e3, 1)}
+            if args.sweep_kernels:
+                kt = {}
+                for cls, nm in kernel_names(sv, args.head_probs).items():
+                    kv_all.copy_(batch.kv_len.expand_as(kv_all))
+                    assert sv.sv_trace_begin(cls, n_it) == 0
+                    for k in range(n_it):
+                        step(3 + k)
+                    torch.cuda.synchronize()
+                    st_, t_ = sv.sv_trace_end(n_it)
+                    if t_:
+                        kt[nm] = round(float(sum(t_) / len(t_)), 5)
+                row["kernels_ms"] = kt
             rows.append(row)
             log(json.dumps(row))
             del probs, q, ws, x, y
@@ -579,6 +591,8 @@ def main():
     ap.add_argument("--sweep-b", default="1,2,4,8,16,32,64,128,256")
     ap.add_argument("--sweep-gamma", default="0,1,2,3,4,5,7")
     ap.add_argument("--sweep-out", default="")
+    ap.add_argument("--sweep-kernels", action="store_true",
+                    help="also time each kernel class at every sweep point")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before the steps, copy a buffer of this many MiB device to device three "
                          "times (the known-size reference for HBM traffic counters)")

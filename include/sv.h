@@ -290,6 +290,25 @@ sv_status sv_accept_commit_noalloc(int32_t B, int32_t V, int32_t mode, const int
                                    int32_t *kv_len, int32_t *accepted, int32_t *next_token,
                                    int32_t *err_flag, void *stream);
 
+/* Per-position acceptance counters, accumulated over calls.
+ *
+ * Defined by: "Speculative Decoding at High Batch Size: Where the 3x Speedup
+ * Turns Into a Tax", section "How do you measure this on your own server?"
+ * (log acceptance per position and turn it into a conditional rate: position
+ * k accepted given position k-1 was) -- the rates SV_PLAN_SPEEDUP takes as
+ * its per-position acceptance.
+ *
+ * For the gamma[B] and accepted[B] of an sv_accept_commit call (device
+ * arrays), adds to counts (device, int64 [2][n_pos], zero it before the first
+ * call):  counts[0][k-1] += sequences that tested draft k (gamma_i >= k and
+ * accepted_i >= k - 1),  counts[1][k-1] += sequences that accepted it
+ * (accepted_i >= k), for k = 1..n_pos (1 <= n_pos <= 256).  Sequences left
+ * uncommitted (accepted_i < 0) are skipped.  counts[1][k] / counts[0][k] is
+ * the conditional acceptance rate at position k + 1.  Integer adds: the
+ * totals do not depend on the order of the additions. */
+sv_status sv_accept_position_counts(int32_t B, int32_t n_pos, const int32_t *gamma,
+                                    const int32_t *accepted, int64_t *counts, void *stream);
+
 /* Draft-length planning (host only). */
 #define SV_PLAN_BUDGET 0  /* keep sum(gamma_i + 1) within the compute-slack budget */
 #define SV_PLAN_SPEEDUP 1 /* maximise the step-model speedup over plain decoding */

@@ -38,6 +38,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = ["accept_commit", "passes", "resample_weights", "integer_weights",
+           "position_counts", "conditional_rates",
            "draw_integer_cdf", "ERR_BAD_TOKEN"]
 
 ERR_BAD_TOKEN = 1
@@ -126,3 +127,35 @@ def accept_commit(gamma, draft, p, q, u_acc, u_samp, kv_len, *, greedy=False):
         new_len[i] = kv_len[i] + a + 1
         qs += g + 1
     return acc, nxt, new_len, err
+
+
+def position_counts(gamma, accepted, n_pos: int) -> np.ndarray:
+    """Per-position acceptance counters of one verify pass, for positions
+    k = 1..n_pos (draft k of a sequence):
+
+      reached[k-1]  = sequences that tested draft k: gamma_i >= k and the
+                      drafts before it were all accepted (a_i >= k - 1);
+      accepted[k-1] = sequences that accepted draft k (a_i >= k).
+
+    accepted / reached is the conditional acceptance rate at position k
+    (draft k accepted given drafts 1..k-1 were), the measure [tax] section
+    "How do you measure this on your own server?" asks for.  Uncommitted
+    sequences (a_i < 0) are not counted.  Returns int64 [2, n_pos]:
+    row 0 reached, row 1 accepted."""
+    out = np.zeros((2, n_pos), dtype=np.int64)
+    for g, a in zip(np.asarray(gamma, np.int64), np.asarray(accepted, np.int64)):
+        if a < 0:
+            continue
+        for k in range(1, n_pos + 1):
+            if g >= k and a >= k - 1:
+                out[0, k - 1] += 1
+            if a >= k:
+                out[1, k - 1] += 1
+    return out
+
+
+def conditional_rates(counts) -> list:
+    """accepted / reached per position (0 where nothing reached it)."""
+    counts = np.asarray(counts, np.int64)
+    return [float(counts[1, k]) / float(counts[0, k]) if counts[0, k] else 0.0
+            for k in range(counts.shape[1])]

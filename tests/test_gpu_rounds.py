@@ -15,8 +15,9 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import (TOL, OF, OV, dev_bf16_to_f64, oracle_accept, rel_rows, run_accept, say, sv,
-                         tg)
+from gpu_helpers import (TOL, OA, OF, OV, dev_bf16_to_f64, oracle_accept, rel_rows, run_accept, say,
+                         sv, tg)
+from oracle import plan as OP
 from workloads import (Shape, accept_inputs, custom_workload, embed_weights, f32_to_bf16_bits,
                        head_weights, kv_cache, layer_weights)
 
@@ -32,83 +33,84 @@ def _layer_out(L, bs, x, ws_cache):
     return y
 
 
-def test_rounds_plan_verify_accept_commit():
-    shape = Shape(d=512, n_q=8, n_kv=2, hd=128, ffn=1024, vocab=4099)
-    seed, cap, n_layers, budget = 2024, 128, 2, 14
-    ctx = [5, 40, 0, 17, 23]
-    stop_at = [11, 49, 4, 29, 30]               # a sequence leaves once its length reaches this
-    B0 = len(ctx)
-    ctx0 = list(ctx)
-    E = embed_weights(shape, seed)
-    table = tg.to_dev(E)
-    Ws = [layer_weights(shape, "bf16", seed, f"layer{k}") for k in range(n_layers)]
-    devs = [{k: tg.upload_matrix(v, packed=True) for k, v in W.items()} for W in Ws]
-    Ls = [tg.decoder_struct(shape, "bf16", d, packed=True) for d in devs]
-    Wlm = head_weights(shape, "bf16", seed)
-    lm = tg.upload_matrix(Wlm, packed=True)
-    Lh = tg.head_struct(shape, "bf16", lm, packed=True)
-    # per layer: host oracle caches (bf16 bits [B][n_kv][cap][hd]) and the device caches
-    kc_o, vc_o, kdev, vdev = [], [], [], []
-    for k in range(n_layers):
-        kc, vc = kv_cache(shape, np.asarray(ctx), cap, seed, f"layer{k}")
-        kc_o.append(kc.copy())
-        vc_o.append(vc.copy())
-        kdev.append([tg.to_dev(kc[i]) for i in range(B0)])
-        vdev.append([tg.to_dev(tg.v_blocked(vc[i])) for i in range(B0)])
-    last = list(np.random.default_rng(seed).integers(0, shape.vocab, B0).astype(np.int32))
-    live = list(range(B0))
-    ws_cache = {}
-    plan = sv.make_plan_params(sv.SV_PLAN_BUDGET, 4, budget_tokens=budget, fill_remainder=True)
-    total_acc, rounds = 0, 0
-    seen_gammas = set()
-    while live and rounds < 16:
-        st, gl, _ = sv.sv_plan_gamma(plan, len(live))
-        assert st == sv.SV_OK
-        gamma = [int(g) for g in gl]
-        seen_gammas.add(tuple(gamma))
-        lctx = [ctx[i] for i in live]
+class _Model:
+    """The small model, its device caches and the oracle's caches, with one
+    round of verify -> accept/commit on both sides."""
+
+    def __init__(self, ctx, seed=2024, cap=128, n_layers=2):
+        self.shape = shape = Shape(d=512, n_q=8, n_kv=2, hd=128, ffn=1024, vocab=4099)
+        self.seed, self.cap, self.n_layers = seed, cap, n_layers
+        self.ctx = list(ctx)
+        self.ctx0 = list(ctx)
+        B0 = len(ctx)
+        self.E = embed_weights(shape, seed)
+        self.table = tg.to_dev(self.E)
+        self.Ws = [layer_weights(shape, "bf16", seed, f"layer{k}") for k in range(n_layers)]
+        devs = [{k: tg.upload_matrix(v, packed=True) for k, v in W.items()} for W in self.Ws]
+        self.devs = devs
+        self.Ls = [tg.decoder_struct(shape, "bf16", d, packed=True) for d in devs]
+        self.Wlm = head_weights(shape, "bf16", seed)
+        self.lm = tg.upload_matrix(self.Wlm, packed=True)
+        self.Lh = tg.head_struct(shape, "bf16", self.lm, packed=True)
+        # per layer: host oracle caches (bf16 bits [B][n_kv][cap][hd]) and the device caches
+        self.kc_o, self.vc_o, self.kdev, self.vdev = [], [], [], []
+        for k in range(n_layers):
+            kc, vc = kv_cache(shape, np.asarray(ctx), cap, seed, f"layer{k}")
+            self.kc_o.append(kc.copy())
+            self.vc_o.append(vc.copy())
+            self.kdev.append([tg.to_dev(kc[i]) for i in range(B0)])
+            self.vdev.append([tg.to_dev(tg.v_blocked(vc[i])) for i in range(B0)])
+        self.last = list(np.random.default_rng(seed).integers(0, shape.vocab, B0).astype(np.int32))
+        self.ws_cache = {}
+
+    def round(self, live, gamma, r):
+        """One round for the live sequences with these draft lengths; returns
+        the GPU's (accepted, next, lengths) after checking them against the
+        oracle, and commits them to both sides' state."""
+        shape, cap, seed = self.shape, self.cap, self.seed
+        lctx = [self.ctx[i] for i in live]
         assert all(c + g + 1 <= cap for c, g in zip(lctx, gamma))
-        wl = custom_workload(shape, "bf16", gamma, lctx, draft="temp", temp=0.7, seed=seed + rounds,
-                             cap=cap)
-        acc_in = accept_inputs(wl, shape.vocab, seed=seed + 101 * rounds)
+        wl = custom_workload(shape, "bf16", gamma, lctx, draft="temp", temp=0.7, seed=seed + r, cap=cap)
+        acc_in = accept_inputs(wl, shape.vocab, seed=seed + 101 * r)
         # stacked tokens: each live sequence's last committed token, then its drafts
         tokens, o = [], 0
         for i, g in zip(live, gamma):
-            tokens += [last[i]] + list(acc_in["draft"][o:o + g])
+            tokens += [self.last[i]] + list(acc_in["draft"][o:o + g])
             o += g
         tokens = np.asarray(tokens, np.int32)
         T = len(tokens)
         # device: embedding, layers (caches shared across rounds), head
         b_emb = tg.DeviceBatch(gamma, lctx, cap)
         x = torch.empty(T, shape.d, dtype=torch.bfloat16, device="cuda")
-        assert sv.sv_verify_layer(tg.embed_struct(shape, table), b_emb.struct(),
+        assert sv.sv_verify_layer(tg.embed_struct(shape, self.table), b_emb.struct(),
                                   torch.tensor(tokens, device="cuda"), x, 0, None, 0,
                                   tg.stream_handle()) == 0
         h = x
-        xo = OV.embed(E, tokens)
-        for k in range(n_layers):
-            bk = tg.DeviceBatch(gamma, lctx, cap, caches=([kdev[k][i] for i in live],
-                                                          [vdev[k][i] for i in live]))
-            h = _layer_out(Ls[k], bk.struct(), h, ws_cache)
-            ref = OV.decoder_layer(shape, Ws[k], xo, gamma, lctx, kc_o[k][live], vc_o[k][live])
+        xo = OV.embed(self.E, tokens)
+        for k in range(self.n_layers):
+            bk = tg.DeviceBatch(gamma, lctx, cap, caches=([self.kdev[k][i] for i in live],
+                                                          [self.vdev[k][i] for i in live]))
+            h = _layer_out(self.Ls[k], bk.struct(), h, self.ws_cache)
+            ref = OV.decoder_layer(shape, self.Ws[k], xo, gamma, lctx, self.kc_o[k][live],
+                                   self.vc_o[k][live])
             err = rel_rows(dev_bf16_to_f64(h), ref.y)
-            assert err < TOL["bf16"], (rounds, k, err)
+            assert err < TOL["bf16"], (r, k, err)
             # the oracle appends its own rows (rounded to bf16) at ctx_i .. ctx_i + gamma_i
             for n_i, i in enumerate(live):
-                c, g = ctx[i], gamma[n_i]
-                kc_o[k][i, :, c:c + g + 1] = f32_to_bf16_bits(ref.k_new[n_i].astype(np.float32))
-                vc_o[k][i, :, c:c + g + 1] = f32_to_bf16_bits(ref.v_new[n_i].astype(np.float32))
+                c, g = self.ctx[i], gamma[n_i]
+                self.kc_o[k][i, :, c:c + g + 1] = f32_to_bf16_bits(ref.k_new[n_i].astype(np.float32))
+                self.vc_o[k][i, :, c:c + g + 1] = f32_to_bf16_bits(ref.v_new[n_i].astype(np.float32))
             xo = ref.y
         bh = tg.DeviceBatch(gamma, lctx, cap)
-        nh = {f: sv.sv_verify_layer_workspace_bytes(Lh, bh.struct(), f) for f in (0, sv.SV_HEAD_LOGITS)}
+        nh = {f: sv.sv_verify_layer_workspace_bytes(self.Lh, bh.struct(), f) for f in (0, sv.SV_HEAD_LOGITS)}
         wsh = tg.workspace(max(nh.values()))
         lg = torch.empty(T, shape.vocab, dtype=torch.float32, device="cuda")
         pr = torch.empty_like(lg)
-        assert sv.sv_verify_layer(Lh, bh.struct(), h, lg, sv.SV_HEAD_LOGITS, wsh, nh[sv.SV_HEAD_LOGITS],
-                                  tg.stream_handle()) == 0
-        assert sv.sv_verify_layer(Lh, bh.struct(), h, pr, 0, wsh, nh[0], tg.stream_handle()) == 0
-        errh = rel_rows(lg.cpu().numpy(), OV.head_logits(Wlm, xo))
-        assert errh < TOL["bf16"], (rounds, errh)
+        assert sv.sv_verify_layer(self.Lh, bh.struct(), h, lg, sv.SV_HEAD_LOGITS, wsh,
+                                  nh[sv.SV_HEAD_LOGITS], tg.stream_handle()) == 0
+        assert sv.sv_verify_layer(self.Lh, bh.struct(), h, pr, 0, wsh, nh[0], tg.stream_handle()) == 0
+        errh = rel_rows(lg.cpu().numpy(), OV.head_logits(self.Wlm, xo))
+        assert errh < TOL["bf16"], (r, errh)
         # accept + commit on the GPU's probabilities, against the oracle on the same rows
         inp = dict(acc_in, p=pr.cpu().numpy())
         ga, gy, gk, gerr = run_accept(gamma, shape.vocab, inp, lctx)
@@ -117,27 +119,115 @@ def test_rounds_plan_verify_accept_commit():
         np.testing.assert_array_equal(ga, ra)
         np.testing.assert_array_equal(gy, ry)
         np.testing.assert_array_equal(gk, rk)
-        say(f"round {rounds}: live {live} gamma {gamma} accepted {ga.tolist()} next {gy.tolist()} "
+        say(f"round {r}: live {live} gamma {gamma} accepted {ga.tolist()} next {gy.tolist()} "
             f"lengths {gk.tolist()} (layer err {err:.1e}, logits err {errh:.1e})")
-        total_acc += int(ga.sum())
         for n_i, i in enumerate(live):
-            ctx[i] = int(gk[n_i])
-            last[i] = int(gy[n_i])
-        live = [i for i in live if ctx[i] < stop_at[i]]
+            self.ctx[i] = int(gk[n_i])
+            self.last[i] = int(gy[n_i])
+        return ga, gy, gk
+
+    def check_caches(self):
+        """The device caches: the starting rows untouched, every row committed
+        since equal to the oracle's (bf16 rounding of the two computations apart)."""
+        hd = self.shape.hd
+        for k in range(self.n_layers):
+            for i in range(len(self.ctx)):
+                kd = tg.DeviceBatch([0], [self.ctx[i]], self.cap,
+                                    caches=([self.kdev[k][i]], [self.vdev[k][i]]))
+                c0, c = self.ctx0[i], self.ctx[i]
+                gk_bits, gv_bits = kd.k_logical(0), kd.v_logical(0)
+                np.testing.assert_array_equal(gk_bits[:, :c0], self.kc_o[k][i, :, :c0])
+                np.testing.assert_array_equal(gv_bits[:, :c0], self.vc_o[k][i, :, :c0])
+                for got, want in ((gk_bits, self.kc_o[k][i]), (gv_bits, self.vc_o[k][i])):
+                    e = rel_rows(OF.bf16_to_f64(got[:, c0:c]).reshape(-1, hd),
+                                 OF.bf16_to_f64(want[:, c0:c]).reshape(-1, hd))
+                    assert e < TOL["bf16"], (k, i, e)
+
+
+def test_rounds_plan_verify_accept_commit():
+    ctx = [5, 40, 0, 17, 23]
+    stop_at = [11, 49, 4, 29, 30]               # a sequence leaves once its length reaches this
+    m = _Model(ctx)
+    live = list(range(len(ctx)))
+    plan = sv.make_plan_params(sv.SV_PLAN_BUDGET, 4, budget_tokens=14, fill_remainder=True)
+    total_acc, rounds = 0, 0
+    seen_gammas = set()
+    while live and rounds < 16:
+        st, gl, _ = sv.sv_plan_gamma(plan, len(live))
+        assert st == sv.SV_OK
+        gamma = [int(g) for g in gl]
+        seen_gammas.add(tuple(gamma))
+        ga, _, _ = m.round(live, gamma, rounds)
+        total_acc += int(ga.sum())
+        live = [i for i in live if m.ctx[i] < stop_at[i]]
         rounds += 1
     assert not live, "every sequence reaches its stop length"
     assert len(seen_gammas) > 1                 # the plan changed as the batch shrank
     assert total_acc > 0
-    # the device caches: the starting rows untouched, every row committed since
-    # equal to the oracle's (bf16 rounding of the two computations apart)
-    for k in range(n_layers):
-        for i in range(B0):
-            kd = tg.DeviceBatch([0], [ctx[i]], cap, caches=([kdev[k][i]], [vdev[k][i]]))
-            c0, c = ctx0[i], ctx[i]
-            gk_bits, gv_bits = kd.k_logical(0), kd.v_logical(0)
-            np.testing.assert_array_equal(gk_bits[:, :c0], kc_o[k][i, :, :c0])
-            np.testing.assert_array_equal(gv_bits[:, :c0], vc_o[k][i, :, :c0])
-            for got, want in ((gk_bits, kc_o[k][i]), (gv_bits, vc_o[k][i])):
-                e = rel_rows(OF.bf16_to_f64(got[:, c0:c]).reshape(-1, shape.hd),
-                             OF.bf16_to_f64(want[:, c0:c]).reshape(-1, shape.hd))
-                assert e < TOL["bf16"], (k, i, e)
+    m.check_caches()
+
+
+# Step-model constants fitted on MI355X (9B-class bf16 layer, its 151936-entry
+# head and acceptance at 2048 cached tokens; the gamma = 1 fit of the (B, gamma)
+# sweep): weight-read time, KV time per sequence, compute time per token, ms.
+MI355X_FIT = {"t_w_ms": 0.3112, "k_ms": 0.0054, "c_ms": 0.0031}
+PRIOR = [0.94 - 0.07 * k for k in range(8)]   # decaying acceptance until measured
+
+
+def _alphas_from_counts(counts, min_reached=3):
+    rates = OA.conditional_rates(counts)
+    return [rates[k] if counts[0, k] >= min_reached else PRIOR[k] for k in range(counts.shape[1])]
+
+
+def test_rounds_speedup_replan_from_position_counters():
+    """Every round re-plans one draft length for the live batch in SPEEDUP
+    mode, with the MI355X-fitted step model and per-position acceptance
+    measured so far by the library's counters (accumulated on the device over
+    the rounds; positions not yet measured take a decaying prior).  The
+    oracle derives the same counters from its own acceptance results (bit
+    for bit) and the oracle planner picks the same draft length."""
+    ctx = [5, 40, 0, 17, 23, 9]
+    stop_at = [c + n for c, n in zip(ctx, [14, 9, 20, 12, 16, 11])]
+    m = _Model(ctx, seed=2025)
+    live = list(range(len(ctx)))
+    npos = 8
+    counts_dev = torch.zeros(2, npos, dtype=torch.int64, device="cuda")
+    counts_ref = np.zeros((2, npos), np.int64)
+    rounds, gammas = 0, []
+    while live and rounds < 40:
+        alphas = _alphas_from_counts(counts_ref)
+        pp = sv.make_plan_params(sv.SV_PLAN_SPEEDUP, npos, alpha=tuple(alphas), **MI355X_FIT)
+        st, gl, bstar = sv.sv_plan_gamma(pp, len(live))
+        assert st == sv.SV_OK
+        want, _, want_bstar = OP.plan_speedup(len(live), npos, alphas, MI355X_FIT["t_w_ms"],
+                                              MI355X_FIT["k_ms"], MI355X_FIT["c_ms"])
+        assert gl == want and bstar == pytest.approx(want_bstar)
+        # keep every draft within the cache
+        gamma = [min(g, m.cap - 1 - m.ctx[i]) for g, i in zip(gl, live)]
+        ga, _, _ = m.round(live, gamma, rounds)
+        g_dev = torch.tensor(gamma, dtype=torch.int32, device="cuda")
+        a_dev = torch.tensor(ga, dtype=torch.int32, device="cuda")
+        assert sv.sv_accept_position_counts(len(live), npos, g_dev, a_dev, counts_dev,
+                                            tg.stream_handle()) == sv.SV_OK
+        counts_ref += OA.position_counts(gamma, ga, npos)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(counts_dev.cpu().numpy(), counts_ref)
+        gammas.append(gl[0] if gl else 0)
+        live = [i for i in live if m.ctx[i] < stop_at[i]]
+        rounds += 1
+    assert not live, "every sequence reaches its stop length"
+    say(f"planned gammas per round {gammas}; conditional rates {OA.conditional_rates(counts_ref)}")
+    assert counts_ref[0, 0] > 0
+    # the same measured rates at larger live batches: the plan follows the batch
+    alphas = _alphas_from_counts(counts_ref)
+    pp = sv.make_plan_params(sv.SV_PLAN_SPEEDUP, npos, alpha=tuple(alphas), **MI355X_FIT)
+    picks = []
+    for b in (1, 8, 64, 256, 1024, 4096):
+        st, gl, _ = sv.sv_plan_gamma(pp, b)
+        want, _, _ = OP.plan_speedup(b, npos, alphas, MI355X_FIT["t_w_ms"], MI355X_FIT["k_ms"],
+                                     MI355X_FIT["c_ms"])
+        assert st == sv.SV_OK and gl == want
+        picks.append(gl[0])
+    say(f"planned gamma at B = 1, 8, 64, 256, 1024, 4096: {picks}")
+    assert picks[0] >= picks[-1] and len(set(picks)) > 1
+    m.check_caches()

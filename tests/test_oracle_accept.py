@@ -262,3 +262,45 @@ def test_integer_cdf_is_exact_quantised_inverse_cdf():
     # weights: exact scale by 2^32, truncation, negatives clipped
     w = A.integer_weights(np.array([1.0, 0.5, 2 ** -32, 2 ** -33, -0.25], np.float32))
     assert list(w) == [2 ** 32, 2 ** 31, 1, 0, 0]
+
+
+def test_position_counts_hand_example():
+    # gamma, accepted -> drafts tested / accepted at positions 1..4
+    gamma = [3, 2, 0, 4, 3]
+    acc = [1, 2, 0, 4, -1]            # the last sequence was left uncommitted
+    c = A.position_counts(gamma, acc, 4)
+    np.testing.assert_array_equal(c[0], [3, 3, 1, 1])   # reached
+    np.testing.assert_array_equal(c[1], [3, 2, 1, 1])   # accepted
+    assert c[1].sum() == sum(a for a in acc if a > 0)
+    assert A.conditional_rates(c) == [1.0, 2 / 3, 1.0, 1.0]
+    assert A.conditional_rates(A.position_counts([0, 0], [0, 0], 2)) == [0.0, 0.0]
+
+
+@pytest.mark.parametrize("alphas", [(0.8,) * 5, (0.94, 0.87, 0.80, 0.73, 0.66)])
+def test_position_counts_recover_conditional_acceptance(alphas):
+    """With acceptance alpha_k at position k given the earlier drafts passed
+    (independent: all equal; the decaying reading: 94 % falling 7 points per
+    position), the counters' conditional rates estimate alpha_k, not the
+    unconditional P(a >= k) = prod alpha_j."""
+    rng = np.random.default_rng(11)
+    B, V, gamma = 30000, 16, len(alphas)
+    draft, p, q, u_acc, u_s = _alpha_batch(rng, B, gamma, V, 0.5)
+    # re-weight each target row so draft j is accepted with probability alpha_j
+    base = p.copy()
+    for i in range(B):
+        for j in range(gamma):
+            r, dr = i * (gamma + 1) + j, i * gamma + j
+            row = base[r].astype(np.float64)
+            row = (1 - alphas[j]) * row / (1 - row[draft[dr]])
+            row[draft[dr]] = alphas[j]
+            p[r] = row
+    acc, _, _, _ = A.accept_commit(np.full(B, gamma), draft, p, q, u_acc, u_s, np.zeros(B, np.int64))
+    c = A.position_counts(np.full(B, gamma), acc, gamma)
+    rates = A.conditional_rates(c)
+    for k in range(gamma):
+        n = c[0, k]
+        assert n == (acc >= k).sum()
+        assert abs(rates[k] - alphas[k]) < 4 * np.sqrt(alphas[k] * (1 - alphas[k]) / n), (k, rates[k])
+    # the expected tokens of the estimated rates match the measured mean
+    e = plan.expected_tokens_cond(rates, gamma)
+    assert abs((acc + 1).mean() - e) < 0.02 * e

@@ -88,6 +88,8 @@ _SIGNATURES = [
      [C.c_int32, C.c_int32, C.c_int32, C.POINTER(C.c_int32), C.c_void_p, C.c_void_p, C.c_void_p,
       C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
       C.c_void_p]),
+    ("sv_accept_position_counts", C.c_int32,
+     [C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]),
     ("sv_packed_matrix_bytes", C.c_int32,
      [C.c_int32, C.c_int32, C.c_int32, C.POINTER(C.c_size_t), C.POINTER(C.c_size_t)]),
     ("sv_pack_matrix", C.c_int32,
@@ -182,6 +184,11 @@ def sv_accept_commit_noalloc(B, V, mode, gamma_host, gamma, draft, p, q, u_acc, 
     return _lib.sv_accept_commit_noalloc(B, V, mode, g, _ptr(gamma), _ptr(draft), _ptr(p), _ptr(q),
                                          _ptr(u_acc), _ptr(u_samp), _ptr(kv_len), _ptr(accepted),
                                          _ptr(next_token), _ptr(err_flag), _ptr(stream))
+
+
+def sv_accept_position_counts(B, n_pos, gamma, accepted, counts, stream) -> int:
+    return _lib.sv_accept_position_counts(B, n_pos, _ptr(gamma), _ptr(accepted), _ptr(counts),
+                                          _ptr(stream))
 
 
 def sv_packed_matrix_bytes(wtype: int, N: int, K: int):

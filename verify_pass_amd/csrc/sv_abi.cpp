@@ -952,6 +952,18 @@ extern "C" sv_status sv_accept_commit(int32_t B, int32_t V, int32_t mode, const 
                     static_cast<hipStream_t>(stream));
 }
 
+extern "C" sv_status sv_accept_position_counts(int32_t B, int32_t n_pos, const int32_t *gamma,
+                                               const int32_t *accepted, int64_t *counts, void *stream) {
+  if (B < 0 || n_pos < 1 || n_pos > kMaxCountPositions) return SV_ERR_INVALID_ARG;
+  if (!counts || (B > 0 && (!gamma || !accepted))) return SV_ERR_INVALID_ARG;
+  if (B == 0) return SV_OK;
+  (void)hipGetLastError();
+  const hipError_t e = launch_position_counts(B, n_pos, gamma, accepted,
+                                              reinterpret_cast<unsigned long long *>(counts),
+                                              static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
 extern "C" sv_status sv_set_gemm_tuning(const char *spec) {
   Tune r;
   if (!parse_tune(spec, r)) return SV_ERR_INVALID_ARG;

@@ -431,7 +431,39 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(AcceptParams p) {
   }
 }
 
+// Per-position acceptance counters: thread i takes sequence i; counts for
+// positions 1..n_pos gather in LDS and each workgroup adds its totals to the
+// caller's 64-bit counters (integer adds: the totals do not depend on order).
+__global__ __launch_bounds__(kThreads) void position_counts_kernel(int B, int n_pos, const int *gamma,
+                                                                   const int *accepted,
+                                                                   unsigned long long *counts) {
+  __shared__ unsigned int hist[2 * kMaxCountPositions];
+  for (int k = threadIdx.x; k < 2 * n_pos; k += kThreads) hist[k] = 0;
+  __syncthreads();
+  const int i = blockIdx.x * kThreads + threadIdx.x;
+  if (i < B) {
+    const int a = accepted[i], g = gamma[i];
+    if (a >= 0) {
+      // draft k was tested iff k <= gamma_i and drafts 1..k-1 passed (k <= a + 1)
+      const int reached = min(min(g, a + 1), n_pos), acc = min(a, n_pos);
+      for (int k = 0; k < reached; ++k) atomicAdd(&hist[k], 1u);
+      for (int k = 0; k < acc; ++k) atomicAdd(&hist[n_pos + k], 1u);
+    }
+  }
+  __syncthreads();
+  for (int k = threadIdx.x; k < 2 * n_pos; k += kThreads)
+    if (hist[k]) atomicAdd(&counts[k], (unsigned long long)hist[k]);
+}
+
 }  // namespace
+
+hipError_t launch_position_counts(int B, int n_pos, const int *gamma, const int *accepted,
+                                  unsigned long long *counts, hipStream_t s) {
+  if (n_pos < 1 || n_pos > kMaxCountPositions) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(position_counts_kernel, dim3((B + kThreads - 1) / kThreads), dim3(kThreads), 0, s, B, n_pos,
+                     gamma, accepted, counts);
+  return hipGetLastError();
+}
 
 hipError_t launch_accept(const AcceptParams &p, hipStream_t s) {
   if (p.chunk > kThreads * kSegMax) return hipErrorInvalidValue;

@@ -25,11 +25,18 @@ __device__ __forceinline__ float bf2f(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
-// fp32 -> bf16, round to nearest even (finite inputs).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> a packed bf16 pair (a in the low half), round to nearest even:
+// one v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
+// fp32 -> bf16, round to nearest even.
 __device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4 &v) {
@@ -284,6 +291,9 @@ __device__ __forceinline__ float prob_of_logit(float l, float Mk, float S) {
 }
 hipError_t launch_embed(const EmbedParams &p, hipStream_t s);
 hipError_t launch_accept(const AcceptParams &p, hipStream_t s);
+constexpr int kMaxCountPositions = 256;  // positions a counter call can record
+hipError_t launch_position_counts(int B, int n_pos, const int *gamma, const int *accepted,
+                                  unsigned long long *counts, hipStream_t s);
 
 // Acceptance call geometry and its scratch layout: arrival counters first
 // (counter_bytes of room), then the per-chunk results and the spill space.

@@ -155,16 +155,22 @@ __device__ __forceinline__ XStep<WT> load_x(const uint16_t *xrow, int ks, int gq
   return r;
 }
 
-// int4 word (8 codes, offset by 8) times the group scale, to bf16.
+// int4 word (8 codes, offset by 8) times the group scale, to bf16.  The
+// nibbles are unpacked bytewise (one mask for the even, a shift and mask for
+// the odd ones, each byte then converted to fp32 directly); (code - 8) * s is
+// one fma from the unsigned nibble, exact in fp32 (a 4-bit times an 8-bit
+// significand), and pairs are rounded to bf16 by one conversion each.
 __device__ __forceinline__ bf16x8 dequant8(uint32_t word, float s) {
-  uint32_t h[8];
+  const uint32_t ev = word & 0x0F0F0F0Fu, od = (word >> 4) & 0x0F0F0F0Fu;
+  const float m8 = -8.f * s;
+  uint32_t h[4];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float v = static_cast<float>(static_cast<int>((word >> (4 * e)) & 15u) - 8) * s;
-    h[e] = f2bf(v);
+  for (int b = 0; b < 4; ++b) {
+    const float fe = static_cast<float>((ev >> (8 * b)) & 0xFFu);  // nibble 2b
+    const float fo = static_cast<float>((od >> (8 * b)) & 0xFFu);  // nibble 2b + 1
+    h[b] = pack_bf16x2(fmaf(fe, s, m8), fmaf(fo, s, m8));
   }
-  return as_bf16x8(uint4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                         h[6] | (h[7] << 16)});
+  return as_bf16x8(uint4{h[0], h[1], h[2], h[3]});
 }
 
 // fp32 x8 -> (hi, lo) bf16 pairs with hi + lo == v to about 2^-17 relative.
@@ -1403,14 +1409,8 @@ __global__ __launch_bounds__(kSThreads, 1) void gemm_sq4_kernel(GemmParams p) {
     const uint2 cw = *reinterpret_cast<const uint2 *>(stg + kCodes + (cf * 16 + cr) * 16 + ch * 8);
     const float sc = bf2f(*reinterpret_cast<const uint16_t *>(stg + kScales + (cf * 16 + cr) * 2));
     auto put = [&](uint32_t word, int i) {
-      uint32_t hv[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float lo = static_cast<float>(static_cast<int>((word >> (8 * e)) & 15u) - 8) * sc;
-        const float hi = static_cast<float>(static_cast<int>((word >> (8 * e + 4)) & 15u) - 8) * sc;
-        hv[e] = f2bf(lo) | (f2bf(hi) << 16);
-      }
-      *reinterpret_cast<uint4 *>(slot + cf * 1024 + ((2 * ch + i) * 16 + cr) * 16) = uint4{hv[0], hv[1], hv[2], hv[3]};
+      *reinterpret_cast<uint4 *>(slot + cf * 1024 + ((2 * ch + i) * 16 + cr) * 16) =
+          __builtin_bit_cast(uint4, dequant8(word, sc));
     };
     put(cw.x, 0);
     put(cw.y, 1);
