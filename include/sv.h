@@ -70,6 +70,7 @@ typedef int32_t sv_status;
 /* Device-side error bits, OR-ed into *err_flag. */
 #define SV_DEV_ERR_BAD_TOKEN 1   /* token id outside [0, vocab) */
 #define SV_DEV_ERR_KV_OVERFLOW 2 /* kv_len[i] + gamma_i + 1 > kv_cap */
+#define SV_DEV_ERR_BAD_TREE 8    /* a tree node whose parent is not an earlier node */
 #define SV_DEV_ERR_CTX_BOUND 4   /* kv_len[i] > max_ctx: that sequence gets no attention
                                     work and its output rows are unspecified; the other
                                     sequences' results are unaffected */
@@ -167,6 +168,15 @@ typedef struct sv_batch {
   void *const *k_cache;      /* [B] device pointers */
   void *const *v_cache;      /* [B] device pointers */
   int32_t *err_flag;         /* [1] nullable */
+  /* Token trees (NULL for the linear pass): sequence i's stacked rows are
+   * then the nodes 0 .. gamma_i of a tree in topological order (node 0 the
+   * last committed token, gamma_i + 1 <= 64), and tree_parent[q_start[i] + j]
+   * is node j's parent (< j; ignored for node 0).  Node j is at position
+   * kv_len[i] + depth(j) (its rotary angle), its key and value are appended
+   * at cache row kv_len[i] + j, and it attends to keys 0 .. kv_len[i] - 1 and
+   * to the rows of its ancestors and itself.  A parent that is not an earlier
+   * node sets SV_DEV_ERR_BAD_TREE (that node's outputs are unspecified). */
+  const int32_t *tree_parent; /* [T] */
 } sv_batch;
 
 /* Packed weight layout.  Rows are taken in 32-row groups g (G = ceil(N/32)
@@ -289,6 +299,61 @@ sv_status sv_accept_commit_noalloc(int32_t B, int32_t V, int32_t mode, const int
                                    const float *q, const float *u_acc, const float *u_samp,
                                    int32_t *kv_len, int32_t *accepted, int32_t *next_token,
                                    int32_t *err_flag, void *stream);
+
+/* Token-tree acceptance and commit.
+ *
+ * Defined by: "Speculative Decoding and Batching Compete for the Same Compute
+ * Slack on RDNA4", section "What the budget says to build" (Table 1: a lone
+ * agent spends its slack on "a small tree, ~8 to 16 deep" of candidates) and
+ * the page's opening (the tree rides under the weight stream of one verify
+ * pass); the acceptance keeps the target's distribution as the rejection
+ * rule of sv_accept_commit does ("Speculative Decoding at High Batch Size:
+ * Where the 3x Speedup Turns Into a Tax", section "Why do the headline
+ * speedups all come from batch 1?").
+ *
+ * Sequence i's stacked rows q_start[i] .. q_start[i] + gamma_i are the nodes
+ * of a tree in topological order (node 0 = the last committed token);
+ * parent[t] is the node's parent within its tree (< its own index; ignored
+ * for node 0), tokens[t] its token.  p fp32 [T][V]: target row of each node
+ * (the distribution of the token after it, e.g. an SV_LAYER_HEAD output over
+ * a tree verify pass); q fp32 [T][V]: the draft distribution each node's
+ * children were drawn from (independently); u_acc [T]: one uniform per node
+ * for its own test (node 0's unused); u_samp [B].  Uniforms in [0, 1) on the
+ * 2^-24 grid.
+ * Stochastic mode walks down from the root; at node v the children are tested
+ * in index order: the first passes iff fl32(u * q_v(d)) < p_v(d); after a
+ * rejection the target is the integer residual R (first
+ * trunc(fl32(max(0, fl32(p_v - q_v)) * 2^32)), sum S) and a later child d
+ * passes iff U * Q(d) * S < R(d) * SQ * 2^24 (U = u * 2^24,
+ * Q = trunc(fl32(q_v * 2^32)), SQ = sum Q); each further rejection sets
+ * R = max(0, R * SQ - Q * S) shifted right until its sum fits 32 bits.  The
+ * first passing child becomes v; with none, or at a leaf, next_token is drawn
+ * from R (or from trunc(fl32(p_v * 2^32)), the bonus row) by the inverse-CDF
+ * rule of sv_accept_commit.  On a chain (one child per node) this is exactly
+ * sv_accept_commit.  Greedy mode follows the child whose token is argmax p_v
+ * (lowest index on ties); q, u_acc, u_samp may be NULL.
+ * Outputs: accepted[i] = depth of the last accepted node, next_token[i],
+ * kv_len[i] += accepted[i] + 1, path (device int32 [B][64]): the accepted node
+ * at each depth (path[i][0] = 0), -1 past the end.  A tree with a bad parent
+ * (SV_DEV_ERR_BAD_TREE) or token (SV_DEV_ERR_BAD_TOKEN) is left uncommitted
+ * (accepted = next_token = -1).  B <= 256, gamma_i + 1 <= 64 nodes. */
+sv_status sv_accept_tree_workspace_bytes(int32_t B, int32_t V, const int32_t *gamma_host,
+                                         size_t *bytes);
+sv_status sv_accept_tree(int32_t B, int32_t V, int32_t mode, const int32_t *gamma_host,
+                         const int32_t *parent, const int32_t *tokens, const float *p,
+                         const float *q, const float *u_acc, const float *u_samp,
+                         int32_t *kv_len, int32_t *accepted, int32_t *next_token, int32_t *path,
+                         int32_t *err_flag, void *workspace, size_t workspace_bytes, void *stream);
+
+/* The tree commit's cache-row moves for one layer's caches (call once per
+ * layer after sv_accept_tree): the accepted node at depth k moves from row
+ * ctx + path[i][k] to ctx + k, ctx = kv_len[i] - accepted[i] - 1 (kv_len and
+ * accepted as sv_accept_tree left them).  Caches as in sv_batch (K
+ * [n_kv][kv_cap][head_dim], V in 32-position blocks); sequences with
+ * accepted <= 0 are untouched. */
+sv_status sv_tree_commit_kv(int32_t B, int32_t n_kv_heads, int32_t head_dim, int32_t kv_cap,
+                            const int32_t *kv_len, const int32_t *accepted, const int32_t *path,
+                            void *const *k_cache, void *const *v_cache, void *stream);
 
 /* Per-position acceptance counters, accumulated over calls.
  *

@@ -119,11 +119,24 @@ def test_int4_needs_scales_and_128_multiples():
 
 
 def test_gqa_rows_limit():
-    # group 2 x (gamma + 1) query rows per KV head must fit 64
-    st, _ = _ws(_layer(), _batch([31], max_ctx=10, cap=64))
+    # group 2 x (gamma + 1) query rows per KV head must fit 128
+    st, _ = _ws(_layer(), _batch([63], max_ctx=10, cap=128))
     assert st == sv.SV_OK
-    st, _ = _ws(_layer(), _batch([32], max_ctx=10, cap=64))
+    st, _ = _ws(_layer(), _batch([64], max_ctx=10, cap=128))
     assert st == sv.SV_ERR_UNSUPPORTED
+
+
+def test_tree_fields_validated():
+    b = _batch([3, 5])
+    b.tree_parent = 0x4000
+    st, _ = _ws(_layer(), b)
+    assert st == sv.SV_OK
+    b = _batch([63], max_ctx=10, cap=128)    # 64 nodes: the largest tree a mask describes
+    b.tree_parent = 0x4000
+    assert _ws(_layer(), b)[0] == sv.SV_OK
+    b = _batch([64], max_ctx=10, cap=128)
+    b.tree_parent = 0x4000
+    assert _ws(_layer(hq=2, hk=2), b)[0] == sv.SV_ERR_UNSUPPORTED
 
 
 def test_workspace_too_small_and_empty_batch():

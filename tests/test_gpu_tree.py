@@ -1,0 +1,268 @@
+"""GPU parity of token-tree verification against the oracle: the decoder
+layer over stacked trees (ancestor masks derived on the device from the
+parent arrays, positions at ctx + depth, rows at ctx + node), more than 64
+query rows per KV head, tree acceptance bit for bit (both modes, full and
+small vocabularies), and the commit's cache-row moves; then one round end to
+end (tree verify -> head -> tree accept -> commit) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import TOL, GpuDecoder, GpuHead, OF, OV, dev_bf16_to_f64, rel_rows, say, sv, tg
+from oracle import tree as OT
+from workloads import Shape, custom_workload, hidden_states, kv_cache, layer_weights
+
+pytestmark = pytest.mark.gpu
+GRID = 1 << 24
+
+
+def random_tree(rng, n, width=3):
+    """Parent array of an n-node tree: each node hangs under one of the last
+    `width` nodes (deep and bushy enough)."""
+    par = [-1]
+    for j in range(1, n):
+        par.append(int(rng.integers(max(0, j - width), j)))
+    return par
+
+
+def _tree_layer(shape, wtype, parents, ctx, seed, packed=False):
+    gamma = [len(p) - 1 for p in parents]
+    wl = custom_workload(shape, wtype, gamma, ctx, seed=seed)
+    W = layer_weights(shape, wtype, wl.seed)
+    mats = {k: tg.upload_matrix(v, packed=packed) for k, v in W.items()}
+    L = tg.decoder_struct(shape, wtype, mats, packed=packed)
+    kc, vc = kv_cache(shape, wl.ctx, wl.cap, wl.seed)
+    batch = tg.DeviceBatch(gamma, ctx, wl.cap, kcache=kc, vcache=vc, tree_parents=parents)
+    bs = batch.struct()
+    n = sv.sv_verify_layer_workspace_bytes(L, bs)
+    ws = tg.workspace(n)
+    xh = hidden_states(wl.T, shape.d, wl.seed)
+    x = tg.to_dev(xh)
+    y = torch.empty_like(x)
+    assert sv.sv_verify_layer(L, bs, x, y, 0, ws, n, tg.stream_handle()) == sv.SV_OK
+    torch.cuda.synchronize()
+    assert batch.err.item() == 0
+    ref = OT.tree_decoder_layer(shape, W, xh, parents, ctx, kc, vc)
+    return wl, batch, y, ref
+
+
+CASES = [
+    # (name, shape, wtype, tree sizes, ctx)
+    ("gqa4-rows96-and-small", Shape(512, 8, 2, 128, 1024, 3000), "bf16", [24, 5, 1, 9], [700, 33, 0, 257]),
+    ("gqa5-rows120", Shape(640, 10, 2, 128, 1280, 2000), "bf16", [24, 2], [300, 1100]),
+    ("gqa4-keysplit-rows16", Shape(512, 8, 2, 128, 1024, 3000), "bf16", [4, 3, 2], [100, 513, 5]),
+    ("hd64-gqa2-int4", Shape(512, 8, 4, 64, 1024, 3000), "int4", [17, 6], [64, 2000]),
+]
+
+
+@pytest.mark.parametrize("name,shape,wtype,sizes,ctx", CASES, ids=[c[0] for c in CASES])
+def test_tree_verify_parity(name, shape, wtype, sizes, ctx):
+    rng = np.random.default_rng(len(name))
+    parents = [random_tree(rng, n) for n in sizes]
+    wl, batch, y, ref = _tree_layer(shape, wtype, parents, ctx, seed=31, packed=(wtype == "int4"))
+    err = rel_rows(dev_bf16_to_f64(y), ref.y)
+    say(f"{name}: depths {[int(OT.depths(p).max()) for p in parents]}, y rel err {err:.2e}")
+    assert err < TOL[wtype]
+    hd = shape.hd
+    for i, par in enumerate(parents):
+        c, n = ctx[i], len(par)
+        kg = OF.bf16_to_f64(batch.k_logical(i)[:, c:c + n])
+        vg = OF.bf16_to_f64(batch.v_logical(i)[:, c:c + n])
+        assert rel_rows(kg.reshape(-1, hd), ref.k_new[i].reshape(-1, hd)) < TOL[wtype]
+        assert rel_rows(vg.reshape(-1, hd), ref.v_new[i].reshape(-1, hd)) < TOL[wtype]
+
+
+def test_chain_beyond_64_rows_per_kv_head():
+    """Linear drafts with 96 query rows per KV head (the eight-wave kernel)."""
+    shape = Shape(512, 8, 2, 128, 1024, 3000)
+    wl = custom_workload(shape, "bf16", [23, 3, 0], [400, 17, 1000], seed=8)
+    dec = GpuDecoder(wl)
+    xh = hidden_states(wl.T, shape.d, wl.seed)
+    y = dec.run(tg.to_dev(xh))
+    torch.cuda.synchronize()
+    ref = dec.oracle(xh)
+    err = rel_rows(dev_bf16_to_f64(y), ref.y)
+    say(f"chain 96 rows: y rel err {err:.2e}")
+    assert err < TOL["bf16"] and dec.batch.err.item() == 0
+
+
+def test_bad_parent_is_flagged():
+    shape = Shape(512, 8, 2, 128, 1024, 3000)
+    parents = [[-1, 0, 5, 1]]           # node 2 names a later node
+    wl = custom_workload(shape, "bf16", [3], [50], seed=9)
+    W = layer_weights(shape, "bf16", wl.seed)
+    mats = {k: tg.upload_matrix(v) for k, v in W.items()}
+    L = tg.decoder_struct(shape, "bf16", mats)
+    kc, vc = kv_cache(shape, wl.ctx, wl.cap, wl.seed)
+    batch = tg.DeviceBatch([3], [50], wl.cap, kcache=kc, vcache=vc, tree_parents=parents)
+    bs = batch.struct()
+    n = sv.sv_verify_layer_workspace_bytes(L, bs)
+    ws = tg.workspace(n)
+    x = tg.to_dev(hidden_states(wl.T, shape.d, wl.seed))
+    assert sv.sv_verify_layer(L, bs, x, torch.empty_like(x), 0, ws, n, tg.stream_handle()) == 0
+    torch.cuda.synchronize()
+    assert batch.err.item() & sv.SV_DEV_ERR_BAD_TREE
+
+
+def _rows(rng, n, V, scale=3.0):
+    z = rng.standard_normal((n, V)).astype(np.float32) * scale
+    z -= z.max(1, keepdims=True)
+    e = np.exp(z)
+    return (e / e.sum(1, keepdims=True)).astype(np.float32)
+
+
+def _run_tree_accept(parents, tokens, p, q, ua, us, ctx, greedy):
+    B, V = len(parents), p.shape[1]
+    gam = [len(x) - 1 for x in parents]
+    dev = lambda a, dt: torch.as_tensor(np.ascontiguousarray(a), dtype=dt, device="cuda")  # noqa: E731
+    par = dev(np.concatenate([np.asarray(x) for x in parents]), torch.int32)
+    tok = dev(tokens, torch.int32)
+    kv = dev(np.asarray(ctx), torch.int32)
+    acc = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    nxt = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    path = torch.full((B, 64), -7, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    n = sv.sv_accept_tree_workspace_bytes(B, V, gam)
+    ws = tg.workspace(n)
+    mode = sv.SV_ACCEPT_GREEDY if greedy else sv.SV_ACCEPT_STOCHASTIC
+    st = sv.sv_accept_tree(B, V, mode, gam, par, tok, dev(p, torch.float32), dev(q, torch.float32),
+                           dev(ua, torch.float32), dev(us, torch.float32), kv, acc, nxt, path, err, ws,
+                           n, tg.stream_handle())
+    assert st == sv.SV_OK
+    torch.cuda.synchronize()
+    return (acc.cpu().numpy(), nxt.cpu().numpy(), kv.cpu().numpy(), path.cpu().numpy(),
+            int(err.item()))
+
+
+def _tree_accept_case(rng, sizes, V, greedy, draft_from_q=True, q_equals_p=False, mix=0.0):
+    parents = [random_tree(rng, n) for n in sizes]
+    T = sum(sizes)
+    p = _rows(rng, T, V)
+    q = p.copy() if q_equals_p else _rows(rng, T, V, 2.0)
+    if mix > 0:  # drafts close to the target: deep acceptance, several siblings tested
+        q = (mix * p + (1 - mix) * q).astype(np.float32)
+        q /= q.sum(1, keepdims=True)
+    tokens = np.zeros(T, np.int64)
+    r0 = 0
+    for par in parents:
+        for j in range(1, len(par)):
+            row = q[r0 + par[j]].astype(np.float64)
+            if greedy and rng.random() < 0.6:
+                tokens[r0 + j] = int(np.argmax(p[r0 + par[j]]))
+            elif draft_from_q:
+                tokens[r0 + j] = int(rng.choice(V, p=row / row.sum()))
+            else:
+                tokens[r0 + j] = int(rng.integers(0, V))
+        r0 += len(par)
+    ua = (rng.integers(0, GRID, size=T) / GRID).astype(np.float32)
+    us = (rng.integers(0, GRID, size=len(sizes)) / GRID).astype(np.float32)
+    ctx = rng.integers(0, 3000, size=len(sizes))
+    got = _run_tree_accept(parents, tokens, p, q, ua, us, ctx, greedy)
+    want = OT.tree_accept(parents, tokens, p, q, ua, us, ctx, greedy=greedy)
+    np.testing.assert_array_equal(got[0], want[0])
+    np.testing.assert_array_equal(got[1], want[1])
+    np.testing.assert_array_equal(got[2], want[2])
+    for i, path in enumerate(want[3]):
+        np.testing.assert_array_equal(got[3][i, :len(path)], path)
+        assert (got[3][i, len(path):] == -1).all()
+    assert got[4] == 0
+    return got
+
+
+@pytest.mark.parametrize("greedy", [False, True])
+def test_tree_accept_bit_exact_small_vocab(greedy):
+    rng = np.random.default_rng(40 + greedy)
+    depth_seen = []
+    for trial in range(6):
+        sizes = [int(v) for v in rng.integers(1, 25, size=int(rng.integers(1, 6)))]
+        got = _tree_accept_case(rng, sizes, int(rng.integers(3, 400)), greedy, q_equals_p=(trial == 5))
+        depth_seen += got[0].tolist()
+    say(f"tree accept small vocab greedy={greedy}: accepted depths {depth_seen}")
+    assert max(depth_seen) >= 2
+
+
+def test_tree_accept_bit_exact_close_drafts():
+    rng = np.random.default_rng(45)
+    depths = []
+    for trial in range(8):
+        sizes = [int(v) for v in rng.integers(8, 25, size=int(rng.integers(1, 4)))]
+        got = _tree_accept_case(rng, sizes, int(rng.integers(3, 60)), False, mix=0.85)
+        depths += got[0].tolist()
+    say(f"tree accept, drafts close to the target: accepted depths {depths}")
+    assert max(depths) >= 3
+
+
+@pytest.mark.parametrize("greedy", [False, True])
+def test_tree_accept_bit_exact_full_vocab(greedy):
+    rng = np.random.default_rng(50 + greedy)
+    got = _tree_accept_case(rng, [16, 9], 151936, greedy)
+    say(f"tree accept V=151936 greedy={greedy}: accepted {got[0].tolist()} next {got[1].tolist()}")
+
+
+def test_tree_commit_moves_accepted_rows():
+    shape = Shape(512, 8, 2, 128, 1024, 3000)
+    B, cap = 3, 96
+    ctx = np.array([10, 40, 3])
+    acc = np.array([3, 0, 2])
+    paths = [[0, 2, 5, 9], [0], [0, 1, 4]]
+    kc, vc = kv_cache(shape, ctx + 20, cap, 77)
+    batch = tg.DeviceBatch([0] * B, list(ctx), cap, kcache=kc, vcache=vc)
+    kv_after = torch.tensor(ctx + acc + 1, dtype=torch.int32, device="cuda")
+    a_dev = torch.tensor(acc, dtype=torch.int32, device="cuda")
+    pm = np.full((B, 64), -1, np.int32)
+    for i, pth in enumerate(paths):
+        pm[i, :len(pth)] = pth
+    assert sv.sv_tree_commit_kv(B, shape.n_kv, shape.hd, cap, kv_after, a_dev,
+                                torch.tensor(pm, device="cuda"), batch.kptr, batch.vptr,
+                                tg.stream_handle()) == sv.SV_OK
+    torch.cuda.synchronize()
+    for i in range(B):
+        np.testing.assert_array_equal(batch.k_logical(i), OT.compact_rows(kc[i], int(ctx[i]), paths[i]))
+        np.testing.assert_array_equal(batch.v_logical(i), OT.compact_rows(vc[i], int(ctx[i]), paths[i]))
+
+
+def test_tree_round_end_to_end():
+    """Tree verify of a lone sequence (a 20-node tree, 80 query rows per KV
+    head), the LM head over its nodes, tree acceptance on the GPU's
+    probabilities against the oracle, and the commit's row moves."""
+    shape = Shape(512, 8, 2, 128, 1024, 3000)
+    rng = np.random.default_rng(61)
+    parents = [random_tree(rng, 20, width=2)]
+    ctx = [333]
+    wl, batch, y, ref = _tree_layer(shape, "bf16", parents, ctx, seed=62, packed=True)
+    assert rel_rows(dev_bf16_to_f64(y), ref.y) < TOL["bf16"]
+    head = GpuHead(wl, packed=True)
+    pr = head.run(y)
+    torch.cuda.synchronize()
+    lg = OV.head_logits(head.Wlm, dev_bf16_to_f64(y))
+    p = pr.cpu().numpy()
+    np.testing.assert_allclose(p, OV.softmax(head.run(y, logits=True).cpu().numpy()), rtol=2e-5, atol=1e-9)
+    assert rel_rows(head.run(y, logits=True).cpu().numpy(), lg) < TOL["bf16"]
+    V = shape.vocab
+    # drafts: each node's children from a draft distribution close to the target
+    q = _rows(rng, len(parents[0]), V, 1.0)
+    q = (0.7 * p + 0.3 * q).astype(np.float32)
+    q /= q.sum(1, keepdims=True)
+    tokens = np.zeros(len(parents[0]), np.int64)
+    for j in range(1, len(parents[0])):
+        row = q[parents[0][j]].astype(np.float64)
+        tokens[j] = int(rng.choice(V, p=row / row.sum()))
+    ua = (rng.integers(0, GRID, size=len(tokens)) / GRID).astype(np.float32)
+    us = np.array([0.37], np.float32)
+    got = _run_tree_accept(parents, tokens, p, q, ua, us, ctx, False)
+    want = OT.tree_accept(parents, tokens, p, q, ua, us, ctx)
+    np.testing.assert_array_equal(got[0], want[0])
+    np.testing.assert_array_equal(got[1], want[1])
+    a = int(got[0][0])
+    say(f"tree round: accepted depth {a}, path {want[3][0]}, next {int(got[1][0])}")
+    # commit: the accepted path's rows move to ctx + depth
+    k_before = batch.k_logical(0).copy()
+    v_before = batch.v_logical(0).copy()
+    kv_after = torch.tensor(got[2], dtype=torch.int32, device="cuda")
+    assert sv.sv_tree_commit_kv(1, shape.n_kv, shape.hd, wl.cap, kv_after,
+                                torch.tensor(got[0], dtype=torch.int32, device="cuda"),
+                                torch.tensor(got[3], dtype=torch.int32, device="cuda"), batch.kptr,
+                                batch.vptr, tg.stream_handle()) == sv.SV_OK
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(batch.k_logical(0), OT.compact_rows(k_before, ctx[0], want[3][0]))
+    np.testing.assert_array_equal(batch.v_logical(0), OT.compact_rows(v_before, ctx[0], want[3][0]))

@@ -26,6 +26,7 @@ SV_ACCEPT_NOALLOC_SCRATCH_BYTES = 4 << 20
 SV_DEV_ERR_BAD_TOKEN = 1
 SV_DEV_ERR_KV_OVERFLOW = 2
 SV_DEV_ERR_CTX_BOUND = 4
+SV_DEV_ERR_BAD_TREE = 8
 
 SV_LAYER_EMBED, SV_LAYER_DECODER, SV_LAYER_HEAD = 0, 1, 2
 SV_W_F32, SV_W_BF16, SV_W_INT4_G32 = 0, 1, 2
@@ -60,7 +61,8 @@ class sv_batch(C.Structure):
     _fields_ = [("B", C.c_int32), ("T", C.c_int32), ("max_ctx", C.c_int32),
                 ("kv_cap", C.c_int32), ("gamma_host", C.POINTER(C.c_int32)),
                 ("gamma", C.c_void_p), ("kv_len", C.c_void_p), ("k_cache", C.c_void_p),
-                ("v_cache", C.c_void_p), ("err_flag", C.c_void_p)]
+                ("v_cache", C.c_void_p), ("err_flag", C.c_void_p),
+                ("tree_parent", C.c_void_p)]
 
 
 class sv_plan_params(C.Structure):
@@ -88,6 +90,12 @@ _SIGNATURES = [
      [C.c_int32, C.c_int32, C.c_int32, C.POINTER(C.c_int32), C.c_void_p, C.c_void_p, C.c_void_p,
       C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
       C.c_void_p]),
+    ("sv_accept_tree_workspace_bytes", C.c_int32,
+     [C.c_int32, C.c_int32, C.POINTER(C.c_int32), C.POINTER(C.c_size_t)]),
+    ("sv_accept_tree", C.c_int32,
+     [C.c_int32, C.c_int32, C.c_int32, C.POINTER(C.c_int32)] + [C.c_void_p] * 14),
+    ("sv_tree_commit_kv", C.c_int32,
+     [C.c_int32, C.c_int32, C.c_int32, C.c_int32] + [C.c_void_p] * 6),
     ("sv_accept_position_counts", C.c_int32,
      [C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]),
     ("sv_packed_matrix_bytes", C.c_int32,
@@ -184,6 +192,30 @@ def sv_accept_commit_noalloc(B, V, mode, gamma_host, gamma, draft, p, q, u_acc, 
     return _lib.sv_accept_commit_noalloc(B, V, mode, g, _ptr(gamma), _ptr(draft), _ptr(p), _ptr(q),
                                          _ptr(u_acc), _ptr(u_samp), _ptr(kv_len), _ptr(accepted),
                                          _ptr(next_token), _ptr(err_flag), _ptr(stream))
+
+
+def sv_accept_tree_workspace_bytes(B, V, gamma_host) -> int:
+    n = C.c_size_t(0)
+    g = (C.c_int32 * max(1, len(gamma_host)))(*[int(x) for x in gamma_host])
+    st = _lib.sv_accept_tree_workspace_bytes(B, V, g, C.byref(n))
+    if st != SV_OK:
+        raise SvError(st, "sv_accept_tree_workspace_bytes")
+    return n.value
+
+
+def sv_accept_tree(B, V, mode, gamma_host, parent, tokens, p, q, u_acc, u_samp, kv_len, accepted,
+                   next_token, path, err_flag, workspace, workspace_bytes, stream) -> int:
+    g = (C.c_int32 * max(1, len(gamma_host)))(*[int(x) for x in gamma_host])
+    return _lib.sv_accept_tree(B, V, mode, g, _ptr(parent), _ptr(tokens), _ptr(p), _ptr(q),
+                               _ptr(u_acc), _ptr(u_samp), _ptr(kv_len), _ptr(accepted),
+                               _ptr(next_token), _ptr(path), _ptr(err_flag), _ptr(workspace),
+                               workspace_bytes, _ptr(stream))
+
+
+def sv_tree_commit_kv(B, n_kv_heads, head_dim, kv_cap, kv_len, accepted, path, k_cache, v_cache,
+                      stream) -> int:
+    return _lib.sv_tree_commit_kv(B, n_kv_heads, head_dim, kv_cap, _ptr(kv_len), _ptr(accepted),
+                                  _ptr(path), _ptr(k_cache), _ptr(v_cache), _ptr(stream))
 
 
 def sv_accept_position_counts(B, n_pos, gamma, accepted, counts, stream) -> int:

@@ -327,6 +327,7 @@ struct LayerPlan {
   size_t off_counters = 0, off_partial = 0, off_qbuf = 0, off_po = 0, off_pml = 0;
   size_t off_attn = 0, off_x1 = 0, off_act = 0, off_stats = 0, off_items = 0;
   size_t off_rnorm = 0, off_rparts = 0, off_tseq = 0, off_tpos = 0, off_qs = 0, off_cs = 0, off_rope = 0;
+  size_t off_tmask = 0;
   size_t bytes = 0;
 };
 
@@ -407,7 +408,9 @@ sv_status plan_layer(const sv_layer *L, const sv_batch *b, int32_t flags, LayerP
     if (check_matrix(*m, w) != SV_OK) return SV_ERR_INVALID_ARG;
   pl.G = hq / hk;
   if (pl.B > kScanMaxB) return SV_ERR_UNSUPPORTED;
-  if ((long long)pl.G * (gmax + 1) > 64) return SV_ERR_UNSUPPORTED;
+  if ((long long)pl.G * (gmax + 1) > kAttnMaxRows) return SV_ERR_UNSUPPORTED;
+  // token trees: every tree within the 64-node ancestor masks
+  if (b->tree_parent && gmax + 1 > kMaxTreeNodes) return SV_ERR_UNSUPPORTED;
   // per-sequence capacity (kv_len[i] + gamma_i + 1 <= kv_cap) is checked on the
   // device, where kv_len lives; max_ctx only sizes the attention grid
   if (b->max_ctx < 0 || b->kv_cap <= 0 || b->kv_cap % 32) return SV_ERR_INVALID_ARG;
@@ -464,6 +467,7 @@ sv_status plan_layer(const sv_layer *L, const sv_batch *b, int32_t flags, LayerP
   pl.off_rparts = take((size_t)pl.o.nblk * pl.T * sizeof(float));
   pl.off_tseq = take((size_t)pl.T * sizeof(int));
   pl.off_tpos = take((size_t)pl.T * sizeof(int));
+  pl.off_tmask = take(b->tree_parent ? (size_t)pl.T * sizeof(unsigned long long) : 0);
   pl.off_qs = take((size_t)(pl.B + 1) * sizeof(int));
   pl.off_cs = take((size_t)(pl.B + 1) * sizeof(int));
   pl.off_items = take((size_t)pl.attn_items * 2 * sizeof(int4));
@@ -636,6 +640,8 @@ extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const
     pp.chunk_start = cstart;
     pp.rope_cs = reinterpret_cast<float *>(ws + pl.off_rope);
     pp.hd = hd;
+    pp.tree_parent = b->tree_parent;
+    pp.tree_mask = b->tree_parent ? reinterpret_cast<unsigned long long *>(ws + pl.off_tmask) : nullptr;
     pp.items = reinterpret_cast<int4 *>(ws + pl.off_items);
     pp.max_items = pl.attn_items;
     pp.max_ctx = b->max_ctx;
@@ -694,6 +700,7 @@ extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const
     a.hd = hd;
     a.kv_cap = b->kv_cap;
     a.max_ctx = b->max_ctx;
+    a.tree_mask = b->tree_parent ? reinterpret_cast<const unsigned long long *>(ws + pl.off_tmask) : nullptr;
     a.chunk = pl.attn_chunk;
     a.max_items = pl.attn_items;
     a.rpad = pl.attn_rpad;
@@ -950,6 +957,91 @@ extern "C" sv_status sv_accept_commit(int32_t B, int32_t V, int32_t mode, const 
   return run_accept(B, V, mode, gamma_host, ap, gamma, draft, p, q, u_acc, u_samp, kv_len, accepted,
                     next_token, err_flag, static_cast<unsigned char *>(workspace),
                     static_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------------------
+// Token trees.
+namespace {
+sv_status plan_tree(int32_t B, int32_t V, const int32_t *gamma_host, long long &T, size_t &bytes) {
+  if (B < 0 || V <= 0 || (B > 0 && !gamma_host)) return SV_ERR_INVALID_ARG;
+  if (B > kTreeMaxB) return SV_ERR_UNSUPPORTED;
+  T = 0;
+  for (int i = 0; i < B; ++i) {
+    if (gamma_host[i] < 0) return SV_ERR_INVALID_ARG;
+    if (gamma_host[i] + 1 > kMaxTreeNodes) return SV_ERR_UNSUPPORTED;
+    T += gamma_host[i] + 1;
+  }
+  bytes = align_up((size_t)B * V * sizeof(unsigned long long));
+  return SV_OK;
+}
+}  // namespace
+
+extern "C" sv_status sv_accept_tree_workspace_bytes(int32_t B, int32_t V, const int32_t *gamma_host,
+                                                    size_t *bytes) {
+  if (!bytes) return SV_ERR_INVALID_ARG;
+  long long T = 0;
+  return plan_tree(B, V, gamma_host, T, *bytes);
+}
+
+extern "C" sv_status sv_accept_tree(int32_t B, int32_t V, int32_t mode, const int32_t *gamma_host,
+                                    const int32_t *parent, const int32_t *tokens, const float *p,
+                                    const float *q, const float *u_acc, const float *u_samp,
+                                    int32_t *kv_len, int32_t *accepted, int32_t *next_token, int32_t *path,
+                                    int32_t *err_flag, void *workspace, size_t workspace_bytes,
+                                    void *stream) {
+  if (mode != SV_ACCEPT_STOCHASTIC && mode != SV_ACCEPT_GREEDY) return SV_ERR_INVALID_ARG;
+  long long T = 0;
+  size_t bytes = 0;
+  sv_status st = plan_tree(B, V, gamma_host, T, bytes);
+  if (st != SV_OK || B == 0) return st;
+  if (!parent || !tokens || !p || !kv_len || !accepted || !next_token || !path) return SV_ERR_INVALID_ARG;
+  if (mode == SV_ACCEPT_STOCHASTIC && (!q || !u_acc || !u_samp)) return SV_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < bytes) return SV_ERR_WORKSPACE;
+  TreeAcceptParams a;
+  std::memset(&a, 0, sizeof(a));
+  a.B = B;
+  a.V = V;
+  a.greedy = mode == SV_ACCEPT_GREEDY;
+  a.parent = parent;
+  a.tokens = tokens;
+  a.p = p;
+  a.q = q;
+  a.u_acc = u_acc;
+  a.u_samp = u_samp;
+  a.kv_len = kv_len;
+  a.accepted = accepted;
+  a.next_token = next_token;
+  a.path = path;
+  a.err = err_flag;
+  a.rbuf = static_cast<unsigned long long *>(workspace);
+  int qs = 0;
+  for (int i = 0; i < B; ++i) {
+    a.q_start[i] = qs;
+    qs += gamma_host[i] + 1;
+  }
+  a.q_start[B] = qs;
+  (void)hipGetLastError();
+  return launch_tree_accept(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+extern "C" sv_status sv_tree_commit_kv(int32_t B, int32_t n_kv_heads, int32_t head_dim, int32_t kv_cap,
+                                       const int32_t *kv_len, const int32_t *accepted, const int32_t *path,
+                                       void *const *k_cache, void *const *v_cache, void *stream) {
+  if (B < 0 || n_kv_heads <= 0 || head_dim <= 0 || kv_cap <= 0 || kv_cap % 32) return SV_ERR_INVALID_ARG;
+  if (B == 0) return SV_OK;
+  if (!kv_len || !accepted || !path || !k_cache || !v_cache) return SV_ERR_INVALID_ARG;
+  TreeCommitParams c;
+  c.B = B;
+  c.hkv = n_kv_heads;
+  c.hd = head_dim;
+  c.kv_cap = kv_cap;
+  c.kv_len = kv_len;
+  c.accepted = accepted;
+  c.path = path;
+  c.kc = k_cache;
+  c.vc = v_cache;
+  (void)hipGetLastError();
+  return launch_tree_commit(c, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
 extern "C" sv_status sv_accept_position_counts(int32_t B, int32_t n_pos, const int32_t *gamma,

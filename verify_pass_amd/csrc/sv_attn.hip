@@ -45,6 +45,15 @@ __device__ __forceinline__ float load_dev(const float *p) {
 }
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Whether a query row sees key `key` of its sequence (ctx cached keys, then
+// the new rows): up to and including its limit lim (-1: a padding row), and
+// for token trees (tree set) among the new rows only those its ancestor mask
+// names.
+__device__ __forceinline__ bool key_visible(int key, int lim, int ctx, bool tree, unsigned long long tm) {
+  const int rel = key - ctx;
+  return key <= lim && (!tree || rel < 0 || ((tm >> (rel & 63)) & 1ull));
+}
+
 // Element (stacked row t, column k of [T][hq * hd]) of the attention output.
 __device__ __forceinline__ size_t out_offset(const AttnParams &p, int t, int k) {
   return p.out_ntt > 0 ? frag_index(t, k, p.out_ntt) : (size_t)t * p.hq * p.hd + k;
@@ -214,19 +223,23 @@ __global__ __launch_bounds__(kThreads, (RT == 1 ? 3 : RT <= 3 ? 2 : 1)) void att
   const uint16_t *vbase = static_cast<const uint16_t *>(p.vc[seq]) + (size_t)g * HD * p.kv_cap;
 
 
-  // query fragments and per-row causal limits
+  // query fragments and per-row causal limits (token trees: ancestor masks)
+  const bool tree = p.tree_mask != nullptr;
   bf16x8 qf[RT][NDG];
   int lim[RT];  // last visible key of this lane's row (or -1 for padding rows)
+  unsigned long long tm[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int rr = rt * 16 + l16;
+    tm[rt] = 0ull;
     if (rr < R) {
       const int hg = rr / n1, j = rr - hg * n1;
       const int t = qst + j;
       const uint16_t *q = p.qbuf + ((size_t)t * p.hq + g * G + hg) * HD;
 #pragma unroll
       for (int dg = 0; dg < NDG; ++dg) qf[rt][dg] = as_bf16x8(*reinterpret_cast<const uint4 *>(q + dslice(dg, gq)));
-      lim[rt] = ctx + j;
+      lim[rt] = tree ? L - 1 : ctx + j;
+      if (tree) tm[rt] = p.tree_mask[t];
     } else {
 #pragma unroll
       for (int dg = 0; dg < NDG; ++dg) qf[rt][dg] = as_bf16x8(uint4{0u, 0u, 0u, 0u});
@@ -269,7 +282,7 @@ __global__ __launch_bounds__(kThreads, (RT == 1 ? 3 : RT <= 3 ? 2 : 1)) void att
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int key = k0 + 8 * gq + e;
-        const bool ok = key < kw1 && key <= lim[rt];
+        const bool ok = key < kw1 && key_visible(key, lim[rt], ctx, tree, tm[rt]);
         sv[e] = ok ? s[rt][e >> 2][e & 3] * p.scale_log2 : -INFINITY;
         mx = fmaxf(mx, sv[e]);
       }
@@ -394,18 +407,18 @@ __device__ __forceinline__ void ring_barrier() {
   __asm__ volatile("" ::: "memory");
 }
 
-template <int HD>
-__global__ __launch_bounds__(kThreads, 2) void attn_qt_kernel(AttnParams p) {
+template <int HD, int NW>
+__global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void attn_qt_kernel(AttnParams p) {
   constexpr int NDG = HD / 32, NDT = HD / 16;
   constexpr int F = 2 * NDG + NDT;   // 1 KiB fragments per step: keys (2 x NDG), values (NDT)
-  constexpr int FW = F / 4;          // fragments each wave loads per step
+  constexpr int FW = F / NW;         // fragments each wave loads per step
   constexpr int SLOT = F * 1024;
-  static_assert(F % 4 == 0, "fragments must split evenly over the four waves");
+  static_assert(F % NW == 0, "fragments must split evenly over the waves");
   static_assert(kQtStages == 3, "three ring slots");
   __shared__ __align__(16) unsigned char ring0[SLOT], ring1[SLOT], ring2[SLOT];
-  // the merge's per-(chunk, row) weights: up to 32 chunks x 64 rows x 2 floats
-  // (in the first ring slot when it is large enough)
-  constexpr int kMw = 32 * 64 * 2;
+  // the merge's per-(chunk, row) weights: up to 32 chunks x 16 NW rows x 2
+  // floats (in the first ring slot when it is large enough)
+  constexpr int kMw = kAttnMaxChunks * 16 * NW * 2;
   __shared__ float mw_own[kMw * 4 > SLOT ? kMw : 1];
   __shared__ int flag[4];
   auto slot_of = [&](auto kc) -> unsigned char * {
@@ -439,9 +452,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_qt_kernel(AttnParams p) {
   const uint16_t *kbase = static_cast<const uint16_t *>(p.kc[seq]) + (size_t)g * p.kv_cap * HD;
   const uint16_t *vbase = static_cast<const uint16_t *>(p.vc[seq]) + (size_t)g * HD * p.kv_cap;
 
-  // this lane's query fragments and causal limit (row 16 * wave + l16)
+  // this lane's query fragments and causal limit (row 16 * wave + l16;
+  // token trees: its ancestor mask)
+  const bool tree = p.tree_mask != nullptr;
   bf16x8 qf[NDG];
   int lim = -1;
+  unsigned long long tm = 0ull;
   {
     const int rr = wave * 16 + l16;
     if (rr < R) {
@@ -449,14 +465,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_qt_kernel(AttnParams p) {
       const uint16_t *q = p.qbuf + ((size_t)(qst + j) * p.hq + g * G + hg) * HD;
 #pragma unroll
       for (int dg = 0; dg < NDG; ++dg) qf[dg] = as_bf16x8(*reinterpret_cast<const uint4 *>(q + dslice(dg, gq)));
-      lim = ctx + j;
+      lim = tree ? L - 1 : ctx + j;
+      if (tree) tm = p.tree_mask[qst + j];
     } else {
 #pragma unroll
       for (int dg = 0; dg < NDG; ++dg) qf[dg] = as_bf16x8(uint4{0u, 0u, 0u, 0u});
     }
   }
 
-  // fragment f = wave + 4 i of a step: keys (kt = f / NDG, dg = f % NDG), whose
+  // fragment f = wave + NW i of a step: keys (kt = f / NDG, dg = f % NDG), whose
   // lane rows are keys k0 + 8 (l16 / 4) + 4 kt + l16 % 4 (clamped to the
   // sequence), or values dt = f - 2 NDG (head-dim column 16 dt + l16, keys
   // k0 + 8 gq ..; the 32-key block lies inside the cache)
@@ -466,7 +483,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_qt_kernel(AttnParams p) {
     unsigned char *slot = slot_of(kc);
 #pragma unroll
     for (int i = 0; i < FW; ++i) {
-      const int f = wave + 4 * i;
+      const int f = wave + NW * i;
       const uint16_t *src;
       if (f < 2 * NDG) {
         const int kt = f / NDG, dg = f - kt * NDG;
@@ -511,7 +528,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_qt_kernel(AttnParams p) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int key = k0 + 8 * gq + e;
-      const bool ok = key < ke && key <= lim;
+      const bool ok = key < ke && key_visible(key, lim, ctx, tree, tm);
       sv[e] = ok ? sc[e >> 2][e & 3] * p.scale_log2 : -INFINITY;
       mx = fmaxf(mx, sv[e]);
     }
@@ -599,10 +616,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_qt_kernel(AttnParams p) {
   publish_merge<HD, 2, 12>(p, qst, ib.z, ib.w, seq, g, R, n1, G, flag, mw);
 }
 
-template <int HD>
+template <int HD, int NW>
 hipError_t launch_qt(const AttnParams &p, hipStream_t s) {
   trace_before(SV_K_ATTENTION, s);
-  hipLaunchKernelGGL((attn_qt_kernel<HD>), dim3(p.max_items, p.hkv), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL((attn_qt_kernel<HD, NW>), dim3(p.max_items, p.hkv), dim3(64 * NW), 0, s, p);
   trace_after(SV_K_ATTENTION, s);
   return hipGetLastError();
 }
@@ -620,17 +637,19 @@ hipError_t launch_rt(const AttnParams &p, hipStream_t s) {
 }
 
 // Up to 16 query rows per KV head: waves split the keys (one row tile each);
-// more: the query-tiled kernel (one wave per row tile, keys shared in LDS).
+// more: the query-tiled kernel (one wave per row tile, keys shared in LDS),
+// four waves up to 64 rows, eight up to 128.
 template <int HD>
 hipError_t launch_hd(const AttnParams &p, hipStream_t s) {
   if (p.rpad <= 16) return launch_rt<1, HD>(p, s);
-  return launch_qt<HD>(p, s);
+  if (p.rpad <= 64) return launch_qt<HD, 4>(p, s);
+  return launch_qt<HD, 8>(p, s);
 }
 
 }  // namespace
 
 hipError_t launch_attention(const AttnParams &p, hipStream_t s) {
-  if (p.kv_cap % 32 || p.chunk % (4 * kKeysPerStep) || p.rpad > 64) return hipErrorInvalidValue;
+  if (p.kv_cap % 32 || p.chunk % (4 * kKeysPerStep) || p.rpad > kAttnMaxRows) return hipErrorInvalidValue;
   return p.hd == 64 ? launch_hd<64>(p, s) : launch_hd<128>(p, s);
 }
 

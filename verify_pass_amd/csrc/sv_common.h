@@ -112,6 +112,7 @@ __device__ inline void set_err(int *err, int bits) {
 
 constexpr int kMaxB = 65536;        // sequences per call (LDS token-map limit)
 constexpr int kAttnMaxChunks = 32;  // attention work items (key chunks) per sequence
+constexpr int kAttnMaxRows = 128;   // query rows per (sequence, KV head): GQA group x tokens
 constexpr int kScanMaxB = 4096;     // kernels that keep the full map in LDS
 
 enum RowMap { RM_LINEAR = 0, RM_ROPE_PAIRS = 1, RM_SWIGLU = 2 };
@@ -178,6 +179,8 @@ struct PrepParams {
   int *chunk_start;    // [B + 1] attention work items of each sequence
   float *rope_cs;      // [T][hd/2][2] cos, sin (nullptr: none)
   int hd;
+  const int *tree_parent;        // [T] token trees: parent of each node (nullptr: chains)
+  unsigned long long *tree_mask; // [T] out: ancestor-or-self mask of each node
   int4 *items;         // [max_items][2] attention work items (see AttnParams)
   int max_items;
   int max_ctx;         // the host's bound on kv_len (a longer sequence is flagged, not attended)
@@ -194,6 +197,7 @@ struct PrepParams {
 struct AttnParams {
   const uint16_t *qbuf;  // [T][hq][hd] (rotated)
   const int4 *items;     // [max_items][2]
+  const unsigned long long *tree_mask;  // [T] visible new keys per row (nullptr: causal chain)
   void *const *kc;
   void *const *vc;
   int B, T, hq, hkv, hd, kv_cap, max_ctx;
@@ -292,6 +296,36 @@ __device__ __forceinline__ float prob_of_logit(float l, float Mk, float S) {
 hipError_t launch_embed(const EmbedParams &p, hipStream_t s);
 hipError_t launch_accept(const AcceptParams &p, hipStream_t s);
 constexpr int kMaxCountPositions = 256;  // positions a counter call can record
+
+// Token trees: nodes per tree (ancestor masks are 64-bit) and sequences per
+// tree-acceptance call (their row offsets travel with the launch).
+constexpr int kMaxTreeNodes = 64;
+constexpr int kTreeMaxB = 256;
+
+struct TreeAcceptParams {
+  int B, V, greedy;
+  const int *parent;      // [T] parent node of each stacked node (roots: any)
+  const int *tokens;      // [T] token of each node (roots: ignored)
+  const float *p;         // [T][V] target rows
+  const float *q;         // [T][V] draft distribution of each node's children
+  const float *u_acc;     // [T] one uniform per node (its own test)
+  const float *u_samp;    // [B]
+  int *kv_len, *accepted, *next_token;
+  int *path;              // [B][kMaxTreeNodes] accepted node at each depth, -1 past the end
+  int *err;
+  unsigned long long *rbuf;  // [B][V] integer weights of the current residual
+  int q_start[kTreeMaxB + 1];
+};
+
+struct TreeCommitParams {
+  int B, hkv, hd, kv_cap;
+  const int *kv_len, *accepted, *path;
+  void *const *kc;
+  void *const *vc;
+};
+
+hipError_t launch_tree_accept(const TreeAcceptParams &p, hipStream_t s);
+hipError_t launch_tree_commit(const TreeCommitParams &p, hipStream_t s);
 hipError_t launch_position_counts(int B, int n_pos, const int *gamma, const int *accepted,
                                   unsigned long long *counts, hipStream_t s);
 

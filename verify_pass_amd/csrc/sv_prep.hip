@@ -81,7 +81,41 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams p) {
   const int total_t = block_exscan(qs, p.B, tmp);
   const int total_c = block_exscan(cs, p.B, tmp);
   const int seq = upper_index(qs, p.B, t);
-  const int pos = ks[seq] + (t - qs[seq]);
+  const int jn = t - qs[seq];               // index of the token in its sequence's chunk
+  const int pos = ks[seq] + jn;             // its cache row
+  // its position (rotary angle): the row's, or ctx + depth for a tree node,
+  // whose ancestor mask the attention reads (the walk up the parent array,
+  // staged in LDS: at most 64 nodes)
+  int rpos = pos;
+  if (p.tree_parent) {
+    int *par = tmp + 8;  // block_exscan uses the first four entries
+    const int n = gs[seq] + 1;
+    for (int j = tid; j < n && j < kMaxTreeNodes; j += kThreads) par[j] = p.tree_parent[qs[seq] + j];
+    __syncthreads();
+    if (tid == 0) {
+      unsigned long long m = 1ull << (jn & 63);
+      int depth = 0, v = jn;
+      bool bad = jn >= kMaxTreeNodes;
+      while (v > 0 && !bad) {
+        const int u = par[v];
+        if (u < 0 || u >= v) {
+          bad = true;
+          break;
+        }
+        m |= 1ull << u;
+        v = u;
+        ++depth;
+      }
+      if (bad) {
+        set_err(p.err, SV_DEV_ERR_BAD_TREE);
+        m = (1ull << (jn & 63)) | 1ull;
+      }
+      p.tree_mask[t] = m;
+      red[0] = __int_as_float(depth);
+    }
+    __syncthreads();
+    rpos = ks[seq] + __float_as_int(red[0]);
+  }
   if (tid == 0) {
     p.tok_seq[t] = seq;
     p.tok_pos[t] = pos;
@@ -92,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepParams p) {
     constexpr double kTwoPiHi = 6.283185307179586232, kTwoPiLo = 2.449293598294706e-16;
     const int half = p.hd / 2;
     for (int i = tid; i < half; i += kThreads) {
-      const double ang = static_cast<double>(pos) * p.inv_freq[i];
+      const double ang = static_cast<double>(rpos) * p.inv_freq[i];
       const double k = rint(ang * (1.0 / kTwoPiHi));
       const double r = fma(-k, kTwoPiLo, fma(-k, kTwoPiHi, ang));
       float sn, cs;

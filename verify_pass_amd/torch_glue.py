@@ -107,7 +107,7 @@ class DeviceBatch:
     of 32 positions, [n_kv][cap/32][hd][32]."""
 
     def __init__(self, gamma, kv_len, cap: int, max_ctx: int | None = None, kcache=None,
-                 vcache=None, shape=None, device="cuda", caches=None):
+                 vcache=None, shape=None, device="cuda", caches=None, tree_parents=None):
         self.gamma_list = [int(g) for g in gamma]
         self.B = len(self.gamma_list)
         self.T = int(sum(g + 1 for g in self.gamma_list))
@@ -130,6 +130,12 @@ class DeviceBatch:
                 self.k.append(torch.zeros(shape.n_kv, cap, shape.hd, dtype=torch.bfloat16, device=device))
                 self.v.append(torch.zeros(shape.n_kv, cap // 32, shape.hd, 32, dtype=torch.bfloat16,
                                           device=device))
+        # token trees: every sequence's parent array, stacked like the tokens
+        self.tree_parent = None
+        if tree_parents is not None:
+            flat = [int(v) for par in tree_parents for v in par]
+            assert len(tree_parents) == self.B and len(flat) == self.T
+            self.tree_parent = torch.tensor(flat or [0], dtype=torch.int32, device=device)
         self.kptr = torch.tensor([t.data_ptr() for t in self.k] or [0], dtype=torch.int64, device=device)
         self.vptr = torch.tensor([t.data_ptr() for t in self.v] or [0], dtype=torch.int64, device=device)
 
@@ -142,6 +148,7 @@ class DeviceBatch:
         b.k_cache = self.kptr.data_ptr()
         b.v_cache = self.vptr.data_ptr()
         b.err_flag = self.err.data_ptr()
+        b.tree_parent = self.tree_parent.data_ptr() if self.tree_parent is not None else None
         return b
 
     def k_logical(self, i: int) -> np.ndarray:
