@@ -566,6 +566,163 @@ def run_workload(cid, args, K, Wm, headline):
     return res, cpu, wl
 
 
+SWARM_LENGTHS = (40, 90, 150, 220, 300, 480, 650, 900)
+
+
+def swarm(args):
+    """The static-batching page's eight-agent swarm (output lengths 40..900
+    tokens, plain decoding: one token per live sequence per step) through the
+    real verify path -- the 9B-class bf16 layer, the 151936-entry head and
+    acceptance -- under each policy of the library's scheduler, with the
+    requests resubmitted `--swarm-waves` times so that continuous batching
+    has a queue to refill from.  Also measures the plain decode step t(B) at
+    B = 1..8 and fits t(B) = t0 + t1 B, from which the oracle's batching
+    model predicts each policy's throughput."""
+    import numpy as np
+    import torch
+
+    import verify_pass_amd as sv
+    from oracle import batching as OB
+    from verify_pass_amd import torch_glue as tg
+    from workloads import SHAPES, head_weights, layer_weights
+
+    torch.cuda.set_device(0)
+    sh = SHAPES["9b"]
+    slots, ctx0 = 8, args.swarm_ctx
+    lengths = list(SWARM_LENGTHS) * args.swarm_waves
+    cap = (ctx0 + max(SWARM_LENGTHS) + 1 + 31) // 32 * 32
+    seed = 20262
+    mats = {k: tg.upload_matrix(v, packed=True) for k, v in layer_weights(sh, "bf16", seed).items()}
+    lm = tg.upload_matrix(head_weights(sh, "bf16", seed), packed=True)
+    Ld = tg.decoder_struct(sh, "bf16", mats, packed=True)
+    Lh = tg.head_struct(sh, "bf16", lm, packed=True)
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    kcs = [torch.randn(sh.n_kv, cap, sh.hd, device="cuda", generator=gen).to(torch.bfloat16) for _ in range(slots)]
+    vcs = [torch.randn(sh.n_kv, cap // 32, sh.hd, 32, device="cuda", generator=gen).to(torch.bfloat16)
+           for _ in range(slots)]
+    kp = [t.data_ptr() for t in kcs]
+    vp = [t.data_ptr() for t in vcs]
+    V = sh.vocab
+    stream = tg.stream_handle()
+    x_all = torch.randn(slots, sh.d, device="cuda", generator=gen).to(torch.bfloat16)
+    y = torch.empty_like(x_all)
+    probs = torch.empty(slots * (V + 2), dtype=torch.float32, device="cuda")
+    us = torch.rand(slots, device="cuda", generator=gen)
+    acc = torch.zeros(slots, dtype=torch.int32, device="cuda")
+    nxt = torch.zeros(slots, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    zeros = torch.zeros(slots, dtype=torch.int32, device="cuda")
+    amode = sv.SV_ACCEPT_STOCHASTIC | sv.SV_ACCEPT_FROM_LOGITS
+    # per batch width: pointer tables and a workspace (built once)
+    nmax = 0
+    tables = {}
+    for w in range(1, slots + 1):
+        b = tg.DeviceBatch([0] * w, [ctx0] * w, cap, max_ctx=ctx0 + max(SWARM_LENGTHS))
+        nmax = max(nmax, sv.sv_verify_layer_workspace_bytes(Ld, b.struct()),
+                   sv.sv_verify_layer_workspace_bytes(Lh, b.struct(), sv.SV_HEAD_LOGITS_STATS),
+                   sv.sv_accept_commit_workspace_bytes(w, V, amode, [0] * w))
+        tables[w] = b
+    ws = tg.workspace(nmax)
+    # one pinned slot per step of the whole run (the host may run far ahead of
+    # the device; a slot is never rewritten before its copy has executed)
+    nring = 184 + 3 * len(lengths) * max(SWARM_LENGTHS) + 64
+    kv_pin = torch.zeros(nring, slots, dtype=torch.int32).pin_memory()
+    kv_dev = torch.zeros(nring, slots, dtype=torch.int32, device="cuda")
+    ptr_pin = torch.zeros(nring, 2, slots, dtype=torch.int64).pin_memory()
+    ptr_dev = torch.zeros(nring, 2, slots, dtype=torch.int64, device="cuda")
+
+    def step(ring, lanes, kv_host):
+        """One plain decode step over the given lanes (their caches and lengths)."""
+        w = len(lanes)
+        r = ring
+        assert r < nring
+        kv_pin[r, :w] = torch.as_tensor([kv_host[k] for k in lanes], dtype=torch.int32)
+        ptr_pin[r, 0, :w] = torch.as_tensor([kp[k] for k in lanes], dtype=torch.int64)
+        ptr_pin[r, 1, :w] = torch.as_tensor([vp[k] for k in lanes], dtype=torch.int64)
+        kv_dev[r].copy_(kv_pin[r], non_blocking=True)
+        ptr_dev[r].copy_(ptr_pin[r], non_blocking=True)
+        b = tables[w].struct()
+        b.kv_len = kv_dev[r].data_ptr()
+        b.k_cache = ptr_dev[r, 0].data_ptr()
+        b.v_cache = ptr_dev[r, 1].data_ptr()
+        b.err_flag = err.data_ptr()
+        x = x_all[:w]
+        assert sv.sv_verify_layer(Ld, b, x, y[:w], 0, ws, nmax, stream) == 0
+        assert sv.sv_verify_layer(Lh, b, y[:w], probs, sv.SV_HEAD_LOGITS_STATS, ws, nmax, stream) == 0
+        assert sv.sv_accept_commit(w, V, amode, [0] * w, zeros, zeros, probs, None, None, us, kv_dev[r],
+                                   acc, nxt, err, ws, nmax, stream) == 0
+
+    # t(B): plain decode steps at fixed widths
+    tb = {}
+    kv_host = [ctx0] * slots
+    ring = 0
+    for w in range(1, slots + 1):
+        for _ in range(3):
+            step(ring, list(range(w)), kv_host)
+            ring += 1
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            step(ring, list(range(w)), kv_host)
+            ring += 1
+        e1.record()
+        torch.cuda.synchronize()
+        tb[w] = e0.elapsed_time(e1) / 20
+        log(f"t({w}) = {tb[w]:.4f} ms")
+    ws_ = np.arange(1, slots + 1)
+    t1, t0 = np.polyfit(ws_, np.array([tb[w] for w in ws_]), 1)
+    log(f"fit t(B) = {t0:.4f} + {t1:.5f} B ms")
+
+    res = {}
+    for pname, pol in (("static", sv.SV_SCHED_STATIC), ("shrink", sv.SV_SCHED_SHRINK),
+                       ("continuous", sv.SV_SCHED_CONTINUOUS)):
+        sch = sv.Scheduler(slots, pol)
+        for n in lengths:
+            sch.submit(n)
+        kv_host = [ctx0] * slots
+        owner = [-1] * slots
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        t_host = time.perf_counter()
+        nsteps = useful = widths = 0
+        while True:
+            req, live, width = sch.next()
+            if width == 0:
+                break
+            lanes = [k for k in range(slots) if req[k] >= 0]
+            for k in lanes:
+                if owner[k] != req[k]:       # a new request took the lane: its own context
+                    owner[k] = req[k]
+                    kv_host[k] = ctx0
+            step(ring, lanes, kv_host)
+            ring += 1
+            for k in lanes:
+                kv_host[k] += 1               # plain decoding commits one token per step
+            useful += sch.commit([1] * slots)
+            nsteps += 1
+            widths += width
+        e1.record()
+        torch.cuda.synchronize()
+        sec = e0.elapsed_time(e1) / 1e3
+        host_s = time.perf_counter() - t_host
+        _, msec, model_tps, util = OB.throughput(pname, slots, lengths, t0, t1)
+        res[pname] = {"steps": nsteps, "useful_tokens": useful, "seconds": round(sec, 4),
+                      "tok_s": round(useful / sec, 1), "utilization": round(useful / widths, 4),
+                      "model_tok_s": round(model_tps, 1), "host_seconds": round(host_s, 4)}
+        log(f"{pname}: {json.dumps(res[pname])}")
+    ceiling = slots / (tb[slots] * 1e-3)
+    out = {"swarm": True, "lengths": list(SWARM_LENGTHS), "waves": args.swarm_waves, "ctx": ctx0,
+           "t_B_ms": {str(w): round(v, 5) for w, v in tb.items()},
+           "fit_ms": {"t0": round(float(t0), 5), "t1": round(float(t1), 6)},
+           "ceiling_tok_s": round(ceiling, 1), "policies": res,
+           "ratio_to_ceiling": {k: round(v["tok_s"] / ceiling, 4) for k, v in res.items()}}
+    if err.item() != 0:
+        raise RuntimeError(f"device error flags {err.item()}")
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -593,6 +750,11 @@ def main():
     ap.add_argument("--sweep-out", default="")
     ap.add_argument("--sweep-kernels", action="store_true",
                     help="also time each kernel class at every sweep point")
+    ap.add_argument("--swarm", action="store_true",
+                    help="run the eight-agent swarm through the verify path under the static, "
+                         "shrinking and continuous batching policies of the library's scheduler")
+    ap.add_argument("--swarm-waves", type=int, default=16)
+    ap.add_argument("--swarm-ctx", type=int, default=1024)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before the steps, copy a buffer of this many MiB device to device three "
                          "times (the known-size reference for HBM traffic counters)")
@@ -603,6 +765,9 @@ def main():
         sys.exit(2)
     if args.sweep:
         sweep(args)
+        return
+    if args.swarm:
+        swarm(args)
         return
 
     import torch

@@ -355,6 +355,35 @@ sv_status sv_tree_commit_kv(int32_t B, int32_t n_kv_heads, int32_t head_dim, int
                             const int32_t *kv_len, const int32_t *accepted, const int32_t *path,
                             void *const *k_cache, void *const *v_cache, void *stream);
 
+/* Iteration-level batching (host only).
+ *
+ * Defined by: "Why Static Batching Wastes an RX 9070 XT Agent Swarm and
+ * Continuous Batching Wins It Back", sections "What a draining batch actually
+ * costs" (a static batch keeps finished lanes as padding until its longest
+ * member stops; a shrinking one drops them) and "Continuous batching refills
+ * the slot instead of freezing it" (membership decided every step, a
+ * finished sequence's slot refilled from the queue on the next step).
+ *
+ * A scheduler of `slots` lanes serves submitted requests (each needing a
+ * number of tokens) in submission order; request ids are 0, 1, 2, ...
+ * Per step: sv_sched_next fills slot_request[slots] (request per lane, -1
+ * empty) and live[slots] (1 where that request still needs tokens; static
+ * batches keep finished lanes as padding, live 0) and *width (lanes the step
+ * carries, padding included; 0 once nothing is left); the caller runs the
+ * verify pass over the lanes and reports each lane's emitted tokens (for a
+ * verify pass accepted + 1) with sv_sched_commit, which returns the useful
+ * tokens of the step (emissions past a request's need are not counted).  A
+ * handle is used by one thread at a time. */
+#define SV_SCHED_STATIC 0
+#define SV_SCHED_SHRINK 1
+#define SV_SCHED_CONTINUOUS 2
+typedef struct sv_sched sv_sched;
+sv_status sv_sched_create(int32_t slots, int32_t policy, sv_sched **out);
+sv_status sv_sched_destroy(sv_sched *sched);
+sv_status sv_sched_submit(sv_sched *sched, int32_t tokens, int32_t *request_out);
+sv_status sv_sched_next(sv_sched *sched, int32_t *slot_request, int32_t *live, int32_t *width);
+sv_status sv_sched_commit(sv_sched *sched, const int32_t *emitted, int32_t *useful_out);
+
 /* Per-position acceptance counters, accumulated over calls.
  *
  * Defined by: "Speculative Decoding at High Batch Size: Where the 3x Speedup

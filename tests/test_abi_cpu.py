@@ -271,3 +271,47 @@ def test_trace_arguments():
     assert sv.sv_trace_begin(sv.SV_K_SOFTMAX, 0) == sv.SV_ERR_INVALID_ARG
     assert sv.sv_trace_begin(sv.SV_K_SOFTMAX, 4, 0) == sv.SV_ERR_INVALID_ARG
     assert sv.sv_trace_end(4)[0] == sv.SV_ERR_INVALID_ARG        # none active
+
+
+def _oracle_sched_run(policy_name, slots, lengths, emitted_fn):
+    from oracle import batching as OB
+    return OB.schedule(policy_name, slots, lengths, emitted_fn)
+
+
+@pytest.mark.parametrize("policy,name", [(sv.SV_SCHED_STATIC, "static"), (sv.SV_SCHED_SHRINK, "shrink"),
+                                         (sv.SV_SCHED_CONTINUOUS, "continuous")])
+def test_scheduler_matches_oracle(policy, name):
+    import numpy as np
+    rng = np.random.default_rng(policy + 3)
+    for trial in range(5):
+        slots = int(rng.integers(1, 9))
+        lengths = [int(v) for v in rng.integers(1, 60, size=int(rng.integers(1, 25)))]
+        em_table = rng.integers(1, 5, size=(5000, slots))   # tokens a lane emits per step
+        emit = (lambda st, s, r: 1) if trial % 2 == 0 else (lambda st, s, r: int(em_table[st, s]))
+        want_steps, want_useful = _oracle_sched_run(name, slots, lengths, emit)
+        sch = sv.Scheduler(slots, policy)
+        assert [sch.submit(n) for n in lengths] == list(range(len(lengths)))
+        k = 0
+        while True:
+            req, live, width = sch.next()
+            if width == 0:
+                break
+            w = want_steps[k]
+            assert req == w.slot_request and live == w.live and width == w.width, (trial, k)
+            useful = sch.commit([emit(k, s, req[s]) for s in range(slots)])
+            assert useful == want_useful[k]
+            k += 1
+        assert k == len(want_steps)
+
+
+def test_scheduler_validation():
+    with pytest.raises(sv.SvError):
+        sv.Scheduler(0, sv.SV_SCHED_STATIC)
+    with pytest.raises(sv.SvError):
+        sv.Scheduler(4, 7)
+    sch = sv.Scheduler(2, sv.SV_SCHED_CONTINUOUS)
+    with pytest.raises(sv.SvError):
+        sch.submit(0)
+    with pytest.raises(sv.SvError):
+        sch.commit([1, 1])                   # no step taken
+    assert sch.next() == ([-1, -1], [0, 0], 0)

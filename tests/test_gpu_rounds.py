@@ -231,3 +231,52 @@ def test_rounds_speedup_replan_from_position_counters():
     say(f"planned gamma at B = 1, 8, 64, 256, 1024, 4096: {picks}")
     assert picks[0] >= picks[-1] and len(set(picks)) > 1
     m.check_caches()
+
+
+def test_continuous_batching_refills_lanes():
+    """Iteration-level batching through the verify path: the library's
+    scheduler (continuous policy, 4 lanes) serves 7 requests of different
+    lengths; each step the budget planner splits 12 tokens over the lanes in
+    use, the lanes' sequences go through verify -> accept/commit (checked
+    against the oracle inside each round), a lane whose request is done is
+    refilled from the queue on the next step with a fresh context, and the
+    oracle's batching model, fed the same emitted counts, makes the same
+    membership decisions."""
+    from oracle import batching as OB
+    slots, ctx0 = 4, 10
+    need = [5, 12, 3, 9, 7, 4, 10]
+    m = _Model([ctx0] * slots, seed=2026)
+    sch = sv.Scheduler(slots, sv.SV_SCHED_CONTINUOUS)
+    for n in need:
+        sch.submit(n)
+    plan = sv.make_plan_params(sv.SV_PLAN_BUDGET, 6, budget_tokens=12, fill_remainder=True)
+    owner = [-1] * slots
+    history, emitted_log = [], {}
+    r = useful = 0
+    while True:
+        req, live, width = sch.next()
+        if width == 0:
+            break
+        history.append((req, live, width))
+        lanes = [k for k in range(slots) if req[k] >= 0]
+        for k in lanes:
+            if owner[k] != req[k]:           # refilled: the new request's own context
+                owner[k] = req[k]
+                m.ctx[k] = ctx0
+        st, gl, _ = sv.sv_plan_gamma(plan, len(lanes))
+        assert st == sv.SV_OK
+        ga, _, _ = m.round(lanes, [int(g) for g in gl], r)
+        emitted = [0] * slots
+        for n_i, k in enumerate(lanes):
+            emitted[k] = int(ga[n_i]) + 1
+        emitted_log[r] = emitted
+        useful += sch.commit(emitted)
+        r += 1
+        assert r < 60
+    assert useful == sum(need)
+    refills = sum(1 for (req, _, _), (req2, _, _) in zip(history, history[1:])
+                  for k in range(slots) if req2[k] >= 0 and req2[k] != req[k])
+    say(f"continuous batching: {r} steps, {refills} refills, widths {[h[2] for h in history]}")
+    assert refills >= len(need) - slots
+    want, _ = OB.schedule(OB.CONTINUOUS, slots, need, emitted_fn=lambda st, s, q: emitted_log[st][s])
+    assert [(w.slot_request, w.live, w.width) for w in want] == history

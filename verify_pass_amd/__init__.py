@@ -35,6 +35,7 @@ SV_LAYOUT_ROWMAJOR, SV_LAYOUT_PACKED = 0, 1
 SV_ACCEPT_STOCHASTIC, SV_ACCEPT_GREEDY = 0, 1
 SV_ACCEPT_FROM_LOGITS = 0x100
 SV_PLAN_BUDGET, SV_PLAN_SPEEDUP = 0, 1
+SV_SCHED_STATIC, SV_SCHED_SHRINK, SV_SCHED_CONTINUOUS = 0, 1, 2
 
 SV_K_GEMM_QKV, SV_K_ATTENTION = 0, 1
 (SV_K_GEMM_O, SV_K_GEMM_GATE_UP, SV_K_GEMM_DOWN, SV_K_GEMM_LM_HEAD, SV_K_SOFTMAX, SV_K_ACCEPT,
@@ -105,6 +106,12 @@ _SIGNATURES = [
     ("sv_plan_gamma", C.c_int32,
      [C.POINTER(sv_plan_params), C.c_int32, C.POINTER(C.c_int32), C.POINTER(C.c_double)]),
     ("sv_set_gemm_tuning", C.c_int32, [C.c_char_p]),
+    ("sv_sched_create", C.c_int32, [C.c_int32, C.c_int32, C.POINTER(C.c_void_p)]),
+    ("sv_sched_destroy", C.c_int32, [C.c_void_p]),
+    ("sv_sched_submit", C.c_int32, [C.c_void_p, C.c_int32, C.POINTER(C.c_int32)]),
+    ("sv_sched_next", C.c_int32, [C.c_void_p, C.POINTER(C.c_int32), C.POINTER(C.c_int32),
+                                  C.POINTER(C.c_int32)]),
+    ("sv_sched_commit", C.c_int32, [C.c_void_p, C.POINTER(C.c_int32), C.POINTER(C.c_int32)]),
     ("sv_trace_begin", C.c_int32, [C.c_int32, C.c_int32, C.c_int32]),
     ("sv_trace_end", C.c_int32, [C.POINTER(C.c_float), C.c_int32, C.POINTER(C.c_int32)]),
     ("sv_status_string", C.c_char_p, [C.c_int32]),
@@ -259,6 +266,49 @@ def sv_trace_end(capacity: int):
     n = C.c_int32(0)
     st = _lib.sv_trace_end(buf, capacity, C.byref(n))
     return st, [float(buf[i]) for i in range(min(n.value, capacity))]
+
+
+class Scheduler:
+    """sv_sched_* handle: submit(tokens) -> request id; next() -> (slot
+    requests, live flags, width); commit(emitted per lane) -> useful tokens."""
+
+    def __init__(self, slots: int, policy: int):
+        self.slots = slots
+        self._h = C.c_void_p()
+        st = _lib.sv_sched_create(slots, policy, C.byref(self._h))
+        if st != SV_OK:
+            raise SvError(st, "sv_sched_create")
+        self._req = (C.c_int32 * slots)()
+        self._live = (C.c_int32 * slots)()
+        self._em = (C.c_int32 * slots)()
+
+    def submit(self, tokens: int) -> int:
+        r = C.c_int32(-1)
+        st = _lib.sv_sched_submit(self._h, tokens, C.byref(r))
+        if st != SV_OK:
+            raise SvError(st, "sv_sched_submit")
+        return r.value
+
+    def next(self):
+        w = C.c_int32(0)
+        st = _lib.sv_sched_next(self._h, self._req, self._live, C.byref(w))
+        if st != SV_OK:
+            raise SvError(st, "sv_sched_next")
+        return list(self._req), list(self._live), w.value
+
+    def commit(self, emitted) -> int:
+        for k in range(self.slots):
+            self._em[k] = int(emitted[k])
+        u = C.c_int32(0)
+        st = _lib.sv_sched_commit(self._h, self._em, C.byref(u))
+        if st != SV_OK:
+            raise SvError(st, "sv_sched_commit")
+        return u.value
+
+    def __del__(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            _lib.sv_sched_destroy(self._h)
+            self._h = C.c_void_p()
 
 
 def make_plan_params(mode, gamma_max, *, budget_tokens=0, fill_remainder=True, t_floor_ms=0.0,

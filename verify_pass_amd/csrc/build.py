@@ -18,7 +18,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsv.so")
 SOURCES = ["sv_prep.hip", "sv_gemm.hip", "sv_gemm_bf16.hip", "sv_gemm_int4.hip", "sv_gemm_f32.hip",
            "sv_attn.hip", "sv_head.hip", "sv_accept.hip", "sv_accept_noalloc.hip", "sv_tree.hip", "sv_abi.cpp",
-           "sv_plan.cpp"]
+           "sv_plan.cpp", "sv_sched.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Wall", "-Wno-unused-function",
          # keep the compiler from emitting packed-fp32 VALU instructions
