@@ -21,6 +21,15 @@ standard pre-norm decoder layer:
   head: logits = RMSNorm(y) Wlm^T, p = softmax(logits)
   embedding: x = E[token]
 
+Quantized KV cache (optional): [static], section "The catch is prefill, and
+it points back at admission", has the swarm quantize its KV to keep the
+per-sequence read from sinking the ceiling as context grows ([tax], "What
+does this model leave out?", names longer context as the term the model
+misses).  The pages fix no format; the plainest reading is symmetric int8
+per cached vector (one position of one KV head): scale = fl32(absmax / 127),
+code = clamp(rne(fl32(x / scale)), -127, 127), value = code * scale, with
+the appended keys and values rounded to bf16 first and stored the same way.
+
 Token map: sequence i owns stacked rows q_start[i] .. q_start[i] + gamma_i,
 q_start = exclusive prefix sum of (gamma_i + 1); row j of sequence i is the
 token at position ctx_i + j (ctx_i = tokens already cached).
@@ -34,7 +43,7 @@ import numpy as np
 from .formats import bf16_to_f64, matrix_f64, round_bf16
 
 __all__ = ["token_map", "rms_norm", "rope", "attend", "LayerOut", "decoder_layer",
-           "head_logits", "softmax", "embed"]
+           "head_logits", "softmax", "embed", "quantize_int8_row", "dequantize_int8"]
 
 
 def token_map(gamma, ctx):
@@ -98,8 +107,28 @@ class LayerOut:
     v_new: dict            # seq -> [n_kv, gamma+1, hd]
 
 
+def quantize_int8_row(v):
+    """Symmetric int8 code of one cached key or value vector (one position,
+    one KV head): scale = fl32(absmax / 127), code = clamp(rne(fl32(x / scale)),
+    -127, 127) with fp32 division; an all-zero vector has scale 0 and codes 0.
+    v holds the vector's values (bf16-representable).  Returns (codes int8,
+    scale fp32)."""
+    x = np.asarray(v, dtype=np.float32)
+    amax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0)
+    if amax == 0:
+        return np.zeros(x.shape, np.int8), np.float32(0)
+    scale = np.float32(amax / np.float32(127.0))
+    codes = np.clip(np.rint(x / scale), -127, 127).astype(np.int8)
+    return codes, scale
+
+
+def dequantize_int8(codes, scale):
+    """code * scale, exact in fp64."""
+    return np.asarray(codes, np.float64) * np.float64(np.float32(scale))
+
+
 def decoder_layer(shape, w, x, gamma, ctx, kcache, vcache, *, eps=1e-6, theta=10000.0,
-                  seqs=None, store_bf16=True) -> LayerOut:
+                  seqs=None, store_bf16=True, kscale=None, vscale=None) -> LayerOut:
     """One decoder layer over the stacked verify tokens.
 
     shape: object with d, n_q, n_kv, hd, ffn.  w: dict of decoded fp64
@@ -109,7 +138,11 @@ def decoder_layer(shape, w, x, gamma, ctx, kcache, vcache, *, eps=1e-6, theta=10
     position-major).  seqs: subset of sequences to evaluate (default all).
     store_bf16: round appended keys/values to the cache's bf16 storage (the
     default; False keeps them exact, for comparisons with formulations that
-    have no bf16 cache)."""
+    have no bf16 cache).
+    kscale / vscale (fp32 [B, n_kv, cap]) given: an int8 cache -- kcache and
+    vcache hold int8 codes, a cached vector is code * scale, and every appended
+    key or value is rounded to bf16 and then stored as its int8 code and
+    scale (quantize_int8_row): attention reads the stored values."""
     W = {n: (m if isinstance(m, np.ndarray) else matrix_f64(m)) for n, m in w.items()}
     gamma = np.asarray(gamma, dtype=np.int64)
     ctx = np.asarray(ctx, dtype=np.int64)
@@ -120,7 +153,13 @@ def decoder_layer(shape, w, x, gamma, ctx, kcache, vcache, *, eps=1e-6, theta=10
     rows = np.concatenate([np.arange(q_start[i], q_start[i + 1]) for i in seqs]).astype(np.int64)
     hd, hq, hk = shape.hd, shape.n_q, shape.n_kv
     grp = hq // hk
-    store = round_bf16 if store_bf16 else (lambda a: a)
+    int8 = kscale is not None
+    if int8:
+        def store(a):
+            codes, sc = quantize_int8_row(round_bf16(a))
+            return dequantize_int8(codes, sc)
+    else:
+        store = round_bf16 if store_bf16 else (lambda a: a)
 
     xs = x[rows]
     h = rms_norm(xs, eps)
@@ -136,8 +175,14 @@ def decoder_layer(shape, w, x, gamma, ctx, kcache, vcache, *, eps=1e-6, theta=10
         c = int(ctx[i])
         kk = np.empty((hk, c + n, hd))
         vv = np.empty((hk, c + n, hd))
-        kk[:, :c] = bf16_to_f64(kcache[i, :, :c])
-        vv[:, :c] = bf16_to_f64(vcache[i, :, :c])
+        if int8:
+            kk[:, :c] = np.asarray(kcache[i, :, :c], np.float64) * \
+                np.asarray(kscale[i, :, :c], np.float32).astype(np.float64)[..., None]
+            vv[:, :c] = np.asarray(vcache[i, :, :c], np.float64) * \
+                np.asarray(vscale[i, :, :c], np.float32).astype(np.float64)[..., None]
+        else:
+            kk[:, :c] = bf16_to_f64(kcache[i, :, :c])
+            vv[:, :c] = bf16_to_f64(vcache[i, :, :c])
         for j in range(n):
             pos = c + j
             for g in range(hk):

@@ -27,8 +27,22 @@ from workloads import (Shape, custom_workload, f32_to_bf16_bits, hidden_states,
 SMALL = Shape(d=128, n_q=4, n_kv=2, hd=32, ffn=192, vocab=300)
 
 
-def _torch_layer(shape, W, x, gamma, ctx, kc, vc, eps=1e-6, theta=10000.0):
-    """Independent formulation from torch library routines (fp64)."""
+def _torch_int8_store(t):
+    """Per (position, head) symmetric int8 storage of appended keys/values,
+    written with torch routines: bf16 rounding, fp32 absmax / 127 scale,
+    round-half-even codes clipped to +-127, then code * scale."""
+    b = t.to(torch.bfloat16).to(torch.float32)
+    scale = (b.abs().amax(dim=-1, keepdim=True) / 127.0).to(torch.float32)
+    safe = torch.where(scale > 0, scale, torch.ones_like(scale))
+    codes = torch.clamp(torch.round(b / safe), -127, 127)
+    codes = torch.where(scale > 0, codes, torch.zeros_like(codes))
+    return codes.to(torch.float64) * scale.to(torch.float64)
+
+
+def _torch_layer(shape, W, x, gamma, ctx, kc, vc, eps=1e-6, theta=10000.0, ks=None, vs=None):
+    """Independent formulation from torch library routines (fp64).  With
+    ks / vs (fp32 scales) the caches hold int8 codes and the appended rows are
+    stored as int8 (_torch_int8_store)."""
     Wt = {k: torch.from_numpy(v) for k, v in W.items()}
     hd, hq, hk = shape.hd, shape.n_q, shape.n_kv
     half = hd // 2
@@ -48,8 +62,17 @@ def _torch_layer(shape, W, x, gamma, ctx, kc, vc, eps=1e-6, theta=10000.0):
             z = torch.complex(t[..., :half], t[..., half:]) * rot[:, None, :]
             return torch.cat([z.real, z.imag], dim=-1)
         q, k = rope(q), rope(k)
-        K = torch.cat([torch.from_numpy(OF.bf16_to_f64(kc[i, :, :c])), k.transpose(0, 1)], dim=1)
-        V = torch.cat([torch.from_numpy(OF.bf16_to_f64(vc[i, :, :c])), v.transpose(0, 1)], dim=1)
+        if ks is None:
+            Kc = torch.from_numpy(OF.bf16_to_f64(kc[i, :, :c]))
+            Vc = torch.from_numpy(OF.bf16_to_f64(vc[i, :, :c]))
+        else:
+            Kc = torch.from_numpy(kc[i, :, :c].astype(np.float64)) * \
+                torch.from_numpy(ks[i, :, :c].astype(np.float64))[..., None]
+            Vc = torch.from_numpy(vc[i, :, :c].astype(np.float64)) * \
+                torch.from_numpy(vs[i, :, :c].astype(np.float64))[..., None]
+            k, v = _torch_int8_store(k), _torch_int8_store(v)
+        K = torch.cat([Kc, k.transpose(0, 1)], dim=1)
+        V = torch.cat([Vc, v.transpose(0, 1)], dim=1)
         G = hq // hk
         K = K.repeat_interleave(G, dim=0)
         V = V.repeat_interleave(G, dim=0)
@@ -220,3 +243,47 @@ def test_embed_selects_rows_by_token():
     got_bf = OV.embed(f32_to_bf16_bits(table), np.array([1, 2], np.int32))
     np.testing.assert_array_equal(got_bf, [[1, 1.25, 1.5, 1.75], [2, 2.25, 2.5, 2.75]])
     assert OV.embed(table, []).shape == (0, 4)
+
+
+def test_int8_kv_quantizer_hand_example_and_bounds():
+    codes, sc = OV.quantize_int8_row([0.75, -1.0, 0.3, 0.0])
+    assert sc == np.float32(np.float32(1.0) / np.float32(127.0))
+    np.testing.assert_array_equal(codes, [95, -127, 38, 0])
+    codes, sc = OV.quantize_int8_row(np.zeros(8))
+    assert sc == 0 and not codes.any()
+    rng = np.random.default_rng(3)
+    for _ in range(50):
+        v = OF.round_bf16(rng.standard_normal(128) * np.exp(rng.uniform(-6, 6)))
+        codes, sc = OV.quantize_int8_row(v)
+        dq = OV.dequantize_int8(codes, sc)
+        assert np.abs(codes).max() == 127
+        # half a step, plus the fp32 rounding of the division (|x / s| <= 127)
+        assert np.all(np.abs(dq - v) <= (0.5 + 127 * 2.0 ** -23) * float(sc))
+
+
+def _int8_cache(kc, vc):
+    """Synthetic int8 caches from the bf16 ones: one code vector and scale per
+    (sequence, head, position)."""
+    B, H, cap, hd = kc.shape
+    out = []
+    for c in (kc, vc):
+        codes = np.zeros(c.shape, np.int8)
+        scales = np.zeros((B, H, cap), np.float32)
+        vals = OF.bf16_to_f64(c)
+        for b in range(B):
+            for h in range(H):
+                for pos in range(cap):
+                    codes[b, h, pos], scales[b, h, pos] = OV.quantize_int8_row(vals[b, h, pos])
+        out += [codes, scales]
+    return out
+
+
+def test_int8_kv_layer_matches_library_formulation():
+    wl, W, kc, vc, x = _case([2, 0, 3], [5, 0, 17], wtype="bf16")
+    k8, ks, v8, vs = _int8_cache(kc, vc)
+    out = OV.decoder_layer(SMALL, W, x, wl.gamma, wl.ctx, k8, v8, kscale=ks, vscale=vs)
+    ref = _torch_layer(SMALL, W, x, wl.gamma, wl.ctx, k8, v8, ks=ks, vs=vs)
+    np.testing.assert_allclose(out.y, ref, rtol=0, atol=1e-11 * np.abs(ref).max())
+    # and it is a different layer from the bf16 cache's
+    out16 = OV.decoder_layer(SMALL, W, x, wl.gamma, wl.ctx, kc, vc)
+    assert np.abs(out16.y - out.y).max() > 1e-4 * np.abs(out.y).max()
