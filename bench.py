@@ -57,10 +57,13 @@ def gemm_algorithmic(wl, which: str):
     return wbytes(n, k) + extra, 2.0 * T * n * k
 
 
-def attention_algorithmic(wl):
+def attention_algorithmic(wl, kv8=False):
+    """Bytes and flops of the attention: every key and value of every
+    sequence once (int8 caches: one byte per value plus an fp32 scale per
+    vector), the queries in and the outputs out."""
     sh = wl.shape
     keys = int(sum(int(c) + int(g) + 1 for c, g in zip(wl.ctx, wl.gamma)))
-    kv = keys * sh.n_kv * sh.hd * 2 * 2
+    kv = keys * sh.n_kv * (sh.hd + 4) * 2 if kv8 else keys * sh.n_kv * sh.hd * 2 * 2
     qo = wl.T * sh.n_q * sh.hd * 2 * 2
     pairs = sum((int(g) + 1) * int(c) + (int(g) + 1) * (int(g) + 2) // 2
                 for c, g in zip(wl.ctx, wl.gamma))
@@ -340,33 +343,43 @@ def kernel_names(sv, head_probs):
             sv.SV_K_ACCEPT: "accept", sv.SV_K_PREP: "prep"}
 
 
-def run_workload(cid, args, K, Wm, headline):
+def run_workload(cid, args, K, Wm, headline, kv8=False):
     """Times K steps of workload cid after Wm warm-ups; returns the result
-    dict (and, for the headline workload, the oracle baseline)."""
+    dict (and, for the headline workload, the oracle baseline).  kv8: the
+    same workload over int8 KV caches."""
     import numpy as np
     import torch
 
     import verify_pass_amd as sv
     from verify_pass_amd import torch_glue as tg
-    from workloads import (accept_inputs, head_weights, hidden_states, kv_cache, layer_weights,
-                           rng_for, uniforms_2m24, workload)
+    from workloads import (accept_inputs, head_weights, hidden_states, kv_cache, kv_cache_int8,
+                           layer_weights, rng_for, uniforms_2m24, workload)
 
     hflags, amode = head_modes(args, sv)
     wl = workload(cid)
+    if kv8:
+        wl.name = wl.name + "-kv8"
     sh = wl.shape
     log(f"workload {wl.cid} {wl.name}: B={wl.B} T={wl.T} wtype={wl.wtype}")
 
     t0 = time.perf_counter()
     W = layer_weights(sh, wl.wtype, wl.seed)
     Wlm = head_weights(sh, wl.wtype, wl.seed) if wl.head else None
-    kc, vc = kv_cache(sh, wl.ctx, wl.cap, wl.seed)
+    if kv8:
+        k8, ks8, v8, vs8 = kv_cache_int8(sh, wl.ctx, wl.cap, wl.seed)
+        kc, vc = k8, v8
+    else:
+        kc, vc = kv_cache(sh, wl.ctx, wl.cap, wl.seed)
     xh = hidden_states(wl.T, sh.d, wl.seed)
     log(f"generated inputs in {time.perf_counter() - t0:.1f} s")
 
     packed = wl.wtype != "f32"
     mats = {k: tg.upload_matrix(v, packed=packed) for k, v in W.items()}
     lm = tg.upload_matrix(Wlm, packed=packed) if Wlm is not None else None
-    batch = tg.DeviceBatch(wl.gamma, wl.ctx, wl.cap, kcache=kc, vcache=vc)
+    if kv8:
+        batch = tg.DeviceBatch(wl.gamma, wl.ctx, wl.cap, kcache=kc, vcache=vc, kscale=ks8, vscale=vs8)
+    else:
+        batch = tg.DeviceBatch(wl.gamma, wl.ctx, wl.cap, kcache=kc, vcache=vc)
     bs = batch.struct()
     Ld = tg.decoder_struct(sh, wl.wtype, mats, packed=packed)
     nd = sv.sv_verify_layer_workspace_bytes(Ld, bs)
@@ -505,7 +518,7 @@ def run_workload(cid, args, K, Wm, headline):
         b_, f_ = gemm_algorithmic(wl, w_)
         tot_b += b_
         tot_f += f_
-    ab, af = attention_algorithmic(wl)
+    ab, af = attention_algorithmic(wl, kv8)
     tot_b += ab
     tot_f += af
     step_roof = roofline_of(tot_b, tot_f, ms)
@@ -551,6 +564,7 @@ def run_workload(cid, args, K, Wm, headline):
                    "gamma": glist if wl.B <= 16 else int(wl.gamma[0]), "T": wl.T,
                    "ctx": int(wl.ctx[0]) if len(set(wl.ctx.tolist())) == 1 else "ragged",
                    "weights": wl.wtype + (" packed" if packed else ""), "d": sh.d,
+                   "kv_cache": "int8 + fp32 scale per vector" if kv8 else "bf16",
                    "heads": f"{sh.n_q}q/{sh.n_kv}kv x {sh.hd}", "ffn": sh.ffn,
                    "vocab": V if has_head else None,
                    "acceptance": (wl.alphas[0] if wl.alphas else wl.draft),
@@ -730,8 +744,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=3,
                     help="headline workload (default 3: the 27B-class bf16 layer, B=32, gamma=7)")
-    ap.add_argument("--extra", default="2,5",
-                    help="further workloads reported under 'workloads' (empty: none)")
+    ap.add_argument("--extra", default="2,5,5k",
+                    help="further workloads reported under 'workloads' (empty: none; a 'k' "
+                         "suffix runs the workload over int8 KV caches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=64,
                     help="verify tokens per oracle step in the CPU baseline sample")
@@ -775,11 +790,12 @@ def main():
     K, Wm = args.steps, args.warmup
     res, cpu, wl = run_workload(args.workload, args, K, Wm, headline=True)
     others = {}
-    for c in [int(v) for v in args.extra.split(",") if v.strip()]:
-        if c == args.workload:
+    for tok in [v.strip() for v in args.extra.split(",") if v.strip()]:
+        c, kv8 = int(tok.rstrip("k")), tok.endswith("k")
+        if c == args.workload and not kv8:
             continue
         torch.cuda.empty_cache()
-        r, _, w = run_workload(c, args, K, Wm, headline=False)
+        r, _, w = run_workload(c, args, K, Wm, headline=False, kv8=kv8)
         others[w.name] = r
     out = {
         "metric": METRIC, "value": res["verify_tok_s"], "unit": "verify tokens/s",

@@ -177,7 +177,21 @@ typedef struct sv_batch {
    * to the rows of its ancestors and itself.  A parent that is not an earlier
    * node sets SV_DEV_ERR_BAD_TREE (that node's outputs are unspecified). */
   const int32_t *tree_parent; /* [T] */
+  /* KV cache storage: SV_KV_BF16 (the layouts above) or SV_KV_INT8: the same
+   * layouts with one int8 code per value, and per sequence the fp32 scales of
+   * every cached vector, k_scale[i] / v_scale[i] -> [n_kv][kv_cap] (value =
+   * code * scale).  The pass stores its new keys and values the same way:
+   * rounded to bf16, then scale = absmax / 127 over the head's vector (fp32,
+   * correctly rounded), code = clamp(rne(x / scale), -127, 127) (0 for an
+   * all-zero vector).  int8 caches need at most 16 query rows per KV head
+   * (GQA group x (gamma_i + 1)). */
+  int32_t kv_dtype;
+  void *const *k_scale; /* [B] device pointers (SV_KV_INT8) */
+  void *const *v_scale; /* [B] */
 } sv_batch;
+
+#define SV_KV_BF16 0
+#define SV_KV_INT8 1
 
 /* Packed weight layout.  Rows are taken in 32-row groups g (G = ceil(N/32)
  * groups), each made of two 16-row tiles a = 0, 1, stored step-major: for K

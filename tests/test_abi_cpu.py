@@ -315,3 +315,16 @@ def test_scheduler_validation():
     with pytest.raises(sv.SvError):
         sch.commit([1, 1])                   # no step taken
     assert sch.next() == ([-1, -1], [0, 0], 0)
+
+
+def test_int8_kv_validation():
+    b = _batch([3, 1])                       # G = 2: 8 rows per KV head
+    b.kv_dtype = sv.SV_KV_INT8
+    assert _ws(_layer(), b)[0] == sv.SV_ERR_INVALID_ARG   # scales missing
+    b.k_scale = b.v_scale = 0x6000
+    assert _ws(_layer(), b)[0] == sv.SV_OK
+    b = _batch([8])                          # 18 rows per KV head: past the int8 kernel's 16
+    b.kv_dtype, b.k_scale, b.v_scale = sv.SV_KV_INT8, 0x6000, 0x6000
+    assert _ws(_layer(), b)[0] == sv.SV_ERR_UNSUPPORTED
+    b.kv_dtype = 5
+    assert _ws(_layer(), b)[0] == sv.SV_ERR_INVALID_ARG

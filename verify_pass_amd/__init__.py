@@ -36,6 +36,7 @@ SV_ACCEPT_STOCHASTIC, SV_ACCEPT_GREEDY = 0, 1
 SV_ACCEPT_FROM_LOGITS = 0x100
 SV_PLAN_BUDGET, SV_PLAN_SPEEDUP = 0, 1
 SV_SCHED_STATIC, SV_SCHED_SHRINK, SV_SCHED_CONTINUOUS = 0, 1, 2
+SV_KV_BF16, SV_KV_INT8 = 0, 1
 
 SV_K_GEMM_QKV, SV_K_ATTENTION = 0, 1
 (SV_K_GEMM_O, SV_K_GEMM_GATE_UP, SV_K_GEMM_DOWN, SV_K_GEMM_LM_HEAD, SV_K_SOFTMAX, SV_K_ACCEPT,
@@ -63,7 +64,8 @@ class sv_batch(C.Structure):
                 ("kv_cap", C.c_int32), ("gamma_host", C.POINTER(C.c_int32)),
                 ("gamma", C.c_void_p), ("kv_len", C.c_void_p), ("k_cache", C.c_void_p),
                 ("v_cache", C.c_void_p), ("err_flag", C.c_void_p),
-                ("tree_parent", C.c_void_p)]
+                ("tree_parent", C.c_void_p), ("kv_dtype", C.c_int32),
+                ("k_scale", C.c_void_p), ("v_scale", C.c_void_p)]
 
 
 class sv_plan_params(C.Structure):

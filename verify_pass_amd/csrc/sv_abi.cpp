@@ -327,7 +327,8 @@ struct LayerPlan {
   size_t off_counters = 0, off_partial = 0, off_qbuf = 0, off_po = 0, off_pml = 0;
   size_t off_attn = 0, off_x1 = 0, off_act = 0, off_stats = 0, off_items = 0;
   size_t off_rnorm = 0, off_rparts = 0, off_tseq = 0, off_tpos = 0, off_qs = 0, off_cs = 0, off_rope = 0;
-  size_t off_tmask = 0;
+  size_t off_tmask = 0, off_kvstage = 0;
+  bool kv8 = false;
   size_t bytes = 0;
 };
 
@@ -411,6 +412,11 @@ sv_status plan_layer(const sv_layer *L, const sv_batch *b, int32_t flags, LayerP
   if ((long long)pl.G * (gmax + 1) > kAttnMaxRows) return SV_ERR_UNSUPPORTED;
   // token trees: every tree within the 64-node ancestor masks
   if (b->tree_parent && gmax + 1 > kMaxTreeNodes) return SV_ERR_UNSUPPORTED;
+  // int8 caches: the key-split attention kernel (up to 16 query rows per KV head)
+  if (b->kv_dtype != SV_KV_BF16 && b->kv_dtype != SV_KV_INT8) return SV_ERR_INVALID_ARG;
+  pl.kv8 = b->kv_dtype == SV_KV_INT8;
+  if (pl.kv8 && (long long)pl.G * (gmax + 1) > 16) return SV_ERR_UNSUPPORTED;
+  if (pl.kv8 && pl.B > 0 && (!b->k_scale || !b->v_scale)) return SV_ERR_INVALID_ARG;
   // per-sequence capacity (kv_len[i] + gamma_i + 1 <= kv_cap) is checked on the
   // device, where kv_len lives; max_ctx only sizes the attention grid
   if (b->max_ctx < 0 || b->kv_cap <= 0 || b->kv_cap % 32) return SV_ERR_INVALID_ARG;
@@ -468,6 +474,7 @@ sv_status plan_layer(const sv_layer *L, const sv_batch *b, int32_t flags, LayerP
   pl.off_tseq = take((size_t)pl.T * sizeof(int));
   pl.off_tpos = take((size_t)pl.T * sizeof(int));
   pl.off_tmask = take(b->tree_parent ? (size_t)pl.T * sizeof(unsigned long long) : 0);
+  pl.off_kvstage = take(pl.kv8 ? (size_t)pl.T * 2 * hk * hd * 2 : 0);
   pl.off_qs = take((size_t)(pl.B + 1) * sizeof(int));
   pl.off_cs = take((size_t)(pl.B + 1) * sizeof(int));
   pl.off_items = take((size_t)pl.attn_items * 2 * sizeof(int4));
@@ -679,11 +686,28 @@ extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const
     p.kv_cap = b->kv_cap;
     p.kc = b->k_cache;
     p.vc = b->v_cache;
+    p.kvstage = pl.kv8 ? reinterpret_cast<uint16_t *>(ws + pl.off_kvstage) : nullptr;
     p.err = b->err_flag;
     int wl = wt;
     e = dequant_mats(pl.qkv, p, d, ws + pl.off_dq, wl, s);
     if (e != hipSuccess) return SV_ERR_HIP;
     e = launch_gemm(p, wl, pl.qkv.tt, pl.qkv.depth, pl.qkv.kw, s, SV_K_GEMM_QKV);
+    if (e != hipSuccess) return SV_ERR_HIP;
+  }
+  if (pl.kv8) {  // the new keys and values into the int8 caches
+    KvQuantParams q;
+    q.kvstage = reinterpret_cast<const uint16_t *>(ws + pl.off_kvstage);
+    q.tok_seq = tseq;
+    q.tok_pos = tpos;
+    q.T = pl.T;
+    q.hkv = hk;
+    q.hd = hd;
+    q.kv_cap = b->kv_cap;
+    q.kc = b->k_cache;
+    q.vc = b->v_cache;
+    q.ksc = b->k_scale;
+    q.vsc = b->v_scale;
+    e = launch_kv_quant(q, s);
     if (e != hipSuccess) return SV_ERR_HIP;
   }
   {  // ragged attention (chunks merged by the last to arrive)
@@ -701,6 +725,9 @@ extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const
     a.kv_cap = b->kv_cap;
     a.max_ctx = b->max_ctx;
     a.tree_mask = b->tree_parent ? reinterpret_cast<const unsigned long long *>(ws + pl.off_tmask) : nullptr;
+    a.kv8 = pl.kv8 ? 1 : 0;
+    a.ksc = b->k_scale;
+    a.vsc = b->v_scale;
     a.chunk = pl.attn_chunk;
     a.max_items = pl.attn_items;
     a.rpad = pl.attn_rpad;

@@ -75,6 +75,48 @@ __device__ __forceinline__ void load_keys(uint4 (&k)[2][HD / 32], const uint16_t
   }
 }
 
+// Eight int8 codes (in memory order) to eight bf16 values (codes are exact in bf16).
+__device__ __forceinline__ uint4 codes_to_bf16x8(uint2 c) {
+  const uint32_t w[2] = {c.x, c.y};
+  uint32_t h[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t word = w[i >> 1];
+    const int sh = (i & 1) * 16;
+    const float a = static_cast<float>(static_cast<int8_t>((word >> sh) & 0xFFu));
+    const float b = static_cast<float>(static_cast<int8_t>((word >> (sh + 8)) & 0xFFu));
+    h[i] = pack_bf16x2(a, b);
+  }
+  return uint4{h[0], h[1], h[2], h[3]};
+}
+
+// int8 caches: the same fragments as load_keys / load_values, one byte per
+// value, converted to bf16 codes (the per-position scales are applied to the
+// scores and to the probabilities instead).
+template <int HD>
+__device__ __forceinline__ void load_keys8(uint4 (&k)[2][HD / 32], const int8_t *kbase, int k0, int L, int l16,
+                                           int gq) {
+  uint2 raw[2][HD / 32];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const int key = min(k0 + 8 * (l16 >> 2) + 4 * kt + (l16 & 3), L - 1);
+    const int8_t *kr = kbase + (size_t)key * HD;
+#pragma unroll
+    for (int dg = 0; dg < HD / 32; ++dg) raw[kt][dg] = *reinterpret_cast<const uint2 *>(kr + dslice(dg, gq));
+  }
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int dg = 0; dg < HD / 32; ++dg) k[kt][dg] = codes_to_bf16x8(raw[kt][dg]);
+}
+
+template <int HD>
+__device__ __forceinline__ void load_values8(uint2 (&v)[HD / 16], const int8_t *vbase, int k0, int l16, int gq) {
+  const int8_t *vb = vbase + (size_t)(k0 >> 5) * HD * 32 + 8 * gq;
+#pragma unroll
+  for (int dt = 0; dt < HD / 16; ++dt) v[dt] = *reinterpret_cast<const uint2 *>(vb + (dt * 16 + l16) * 32);
+}
+
 template <int HD>
 __device__ __forceinline__ void load_values(uint4 (&v)[HD / 16], const uint16_t *vbase, int k0, int l16, int gq) {
   // k0 is a multiple of 32 and the block lies inside the cache (cap % 32 == 0)
@@ -189,7 +231,7 @@ __device__ void publish_merge(const AttnParams &p, int qst, int first, int nch, 
   }
 }
 
-template <int RT, int HD>
+template <int RT, int HD, bool KV8>
 __global__ __launch_bounds__(kThreads, (RT == 1 ? 3 : RT <= 3 ? 2 : 1)) void attn_kernel(AttnParams p) {
   constexpr int NDG = HD / 32;  // MFMA k-groups over the head dim
   constexpr int NDT = HD / 16;  // 16-wide head-dim tiles of the output
@@ -257,11 +299,32 @@ __global__ __launch_bounds__(kThreads, (RT == 1 ? 3 : RT <= 3 ? 2 : 1)) void att
     for (int dt = 0; dt < NDT; ++dt) o[rt][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
+  // int8 caches: codes and per-position scales
+  const int8_t *kbase8 = KV8 ? static_cast<const int8_t *>(p.kc[seq]) + (size_t)g * p.kv_cap * HD : nullptr;
+  const int8_t *vbase8 = KV8 ? static_cast<const int8_t *>(p.vc[seq]) + (size_t)g * HD * p.kv_cap : nullptr;
+  const float *ksc = KV8 ? static_cast<const float *>(p.ksc[seq]) + (size_t)g * p.kv_cap : nullptr;
+  const float *vsc = KV8 ? static_cast<const float *>(p.vsc[seq]) + (size_t)g * p.kv_cap : nullptr;
+
   for (int k0 = kw0; k0 < kw1; k0 += kKeysPerStep) {
     uint4 kr[2][NDG];
-    load_keys<HD>(kr, kbase, k0, L, l16, gq);
     uint4 vr[NDT];  // the values in flight with the keys
-    load_values<HD>(vr, vbase, k0, l16, gq);
+    float skey[8], sval[8];  // scales of this lane's keys k0 + 8 gq + e (int8 caches)
+    if constexpr (KV8) {
+      uint2 v8[NDT];
+      load_values8<HD>(v8, vbase8, k0, l16, gq);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int key = min(k0 + 8 * gq + e, L - 1);
+        skey[e] = ksc[key];
+        sval[e] = vsc[key];
+      }
+      load_keys8<HD>(kr, kbase8, k0, L, l16, gq);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) vr[dt] = codes_to_bf16x8(v8[dt]);
+    } else {
+      load_keys<HD>(kr, kbase, k0, L, l16, gq);
+      load_values<HD>(vr, vbase, k0, l16, gq);
+    }
     // scores of every row tile first; the keys are dead afterwards
     floatx4 s[RT][2];
 #pragma unroll
@@ -283,7 +346,8 @@ __global__ __launch_bounds__(kThreads, (RT == 1 ? 3 : RT <= 3 ? 2 : 1)) void att
       for (int e = 0; e < 8; ++e) {
         const int key = k0 + 8 * gq + e;
         const bool ok = key < kw1 && key_visible(key, lim[rt], ctx, tree, tm[rt]);
-        sv[e] = ok ? s[rt][e >> 2][e & 3] * p.scale_log2 : -INFINITY;
+        const float raw = KV8 ? s[rt][e >> 2][e & 3] * skey[e] : s[rt][e >> 2][e & 3];
+        sv[e] = ok ? raw * p.scale_log2 : -INFINITY;
         mx = fmaxf(mx, sv[e]);
       }
       mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -296,7 +360,7 @@ __global__ __launch_bounds__(kThreads, (RT == 1 ? 3 : RT <= 3 ? 2 : 1)) void att
       for (int e = 0; e < 8; ++e) {
         const float pe = __builtin_amdgcn_exp2f(sv[e] - m_new);
         lsum += pe;
-        pb[e] = f2bf(pe);
+        pb[e] = f2bf(KV8 ? pe * sval[e] : pe);  // int8 values: their scale rides on p
       }
       l_run[rt] = l_run[rt] * alpha[rt] + lsum;
       m_run[rt] = m_new;
@@ -624,14 +688,14 @@ hipError_t launch_qt(const AttnParams &p, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int RT, int HD>
+template <int RT, int HD, bool KV8>
 hipError_t launch_rt(const AttnParams &p, hipStream_t s) {
   const size_t lds = 16 + (size_t)4 * HD * 16 * sizeof(float) + 4 * 16 * 2 * sizeof(float);
   if (lds > 65536)
-    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_kernel<RT, HD>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_kernel<RT, HD, KV8>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   trace_before(SV_K_ATTENTION, s);
-  hipLaunchKernelGGL((attn_kernel<RT, HD>), dim3(p.max_items, p.hkv), dim3(kThreads), lds, s, p);
+  hipLaunchKernelGGL((attn_kernel<RT, HD, KV8>), dim3(p.max_items, p.hkv), dim3(kThreads), lds, s, p);
   trace_after(SV_K_ATTENTION, s);
   return hipGetLastError();
 }
@@ -641,12 +705,56 @@ hipError_t launch_rt(const AttnParams &p, hipStream_t s) {
 // four waves up to 64 rows, eight up to 128.
 template <int HD>
 hipError_t launch_hd(const AttnParams &p, hipStream_t s) {
-  if (p.rpad <= 16) return launch_rt<1, HD>(p, s);
+  if (p.kv8) return p.rpad <= 16 ? launch_rt<1, HD, true>(p, s) : hipErrorInvalidValue;
+  if (p.rpad <= 16) return launch_rt<1, HD, false>(p, s);
   if (p.rpad <= 64) return launch_qt<HD, 4>(p, s);
   return launch_qt<HD, 8>(p, s);
 }
 
+// The pass's new keys and values into int8 caches: one wave per (token, K or
+// V, KV head); scale = absmax / 127 (fp32, correctly rounded), code =
+// clamp(rne(x / scale), -127, 127), 0 for an all-zero vector.
+template <int HD>
+__global__ __launch_bounds__(64) void kv_quant_kernel(KvQuantParams p) {
+  const int t = blockIdx.x, which = blockIdx.y / p.hkv, h = blockIdx.y - which * p.hkv;
+  const int lane = threadIdx.x;
+  const int seq = p.tok_seq[t], pos = p.tok_pos[t];
+  if (pos < 0 || pos >= p.kv_cap) return;  // flagged by the QKV pass
+  constexpr int PER = HD / 64;
+  const uint16_t *src = p.kvstage + (((size_t)t * 2 + which) * p.hkv + h) * HD;
+  float x[PER];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    x[i] = bf2f(src[lane + 64 * i]);
+    amax = fmaxf(amax, fabsf(x[i]));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  const float scale = __fdiv_rn(amax, 127.f);
+  int8_t *codes = static_cast<int8_t *>(which == 0 ? p.kc[seq] : p.vc[seq]);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int d = lane + 64 * i;
+    const float c = amax > 0.f ? fminf(fmaxf(rintf(__fdiv_rn(x[i], scale)), -127.f), 127.f) : 0.f;
+    const size_t at = which == 0 ? ((size_t)h * p.kv_cap + pos) * HD + d
+                                 : (((size_t)h * (p.kv_cap >> 5) + (pos >> 5)) * HD + d) * 32 + (pos & 31);
+    codes[at] = static_cast<int8_t>(c);
+  }
+  if (lane == 0) static_cast<float *>(which == 0 ? p.ksc[seq] : p.vsc[seq])[(size_t)h * p.kv_cap + pos] = scale;
+}
+
 }  // namespace
+
+hipError_t launch_kv_quant(const KvQuantParams &p, hipStream_t s) {
+  if (p.hd != 64 && p.hd != 128) return hipErrorInvalidValue;
+  if (p.T == 0) return hipSuccess;
+  if (p.hd == 64)
+    hipLaunchKernelGGL(kv_quant_kernel<64>, dim3(p.T, 2 * p.hkv), dim3(64), 0, s, p);
+  else
+    hipLaunchKernelGGL(kv_quant_kernel<128>, dim3(p.T, 2 * p.hkv), dim3(64), 0, s, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_attention(const AttnParams &p, hipStream_t s) {
   if (p.kv_cap % 32 || p.chunk % (4 * kKeysPerStep) || p.rpad > kAttnMaxRows) return hipErrorInvalidValue;

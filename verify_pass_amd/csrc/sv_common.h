@@ -161,6 +161,7 @@ struct GemmParams {
   int B, kv_cap;
   void *const *kc;
   void *const *vc;
+  uint16_t *kvstage;  // int8 caches: the new keys / values go here instead, [T][2][hkv][hd] bf16
   int *err;
 };
 
@@ -211,7 +212,24 @@ struct AttnParams {
   int out_ntt;
   int *counters;    // [B][hkv] arrival counters, zero between launches
   int *err;
+  // int8 caches (kv8): codes in the bf16 layouts with one byte per value, and
+  // per (head, position) fp32 scales [hkv][kv_cap] behind ksc[seq], vsc[seq]
+  int kv8;
+  void *const *ksc;
+  void *const *vsc;
 };
+
+// Quantisation of the pass's new keys and values into int8 caches.
+struct KvQuantParams {
+  const uint16_t *kvstage;  // [T][2][hkv][hd] bf16
+  const int *tok_seq, *tok_pos;
+  int T, hkv, hd, kv_cap;
+  void *const *kc;
+  void *const *vc;
+  void *const *ksc;
+  void *const *vsc;
+};
+hipError_t launch_kv_quant(const KvQuantParams &p, hipStream_t s);
 
 struct HeadSoftmaxParams {
   float *logits;        // [T][V] in: logits, out: probabilities

@@ -452,7 +452,14 @@ __device__ __forceinline__ void epilogue_rs(const GemmParams &p, floatx4 (&acc)[
         }
       }
       const int fi0 = 16 * c + 4 * gq;
-      if (head < p.hq) {
+      if (head >= p.hq && p.kvstage) {
+        // int8 caches: stage the new key / value row; a later pass quantises it
+        const int which = head < p.hq + p.hkv ? 0 : 1;
+        const int kh = head - p.hq - which * p.hkv;
+        uint16_t *st = p.kvstage + (((size_t)t * 2 + which) * p.hkv + kh) * p.hd;
+        st_bf16x4(st + fi0, ra);
+        st_bf16x4(st + fi0 + half, rb);
+      } else if (head < p.hq) {
         uint16_t *q = p.qbuf + ((size_t)t * p.hq + head) * p.hd;
         st_bf16x4(q + fi0, ra);
         st_bf16x4(q + fi0 + half, rb);

@@ -107,7 +107,8 @@ class DeviceBatch:
     of 32 positions, [n_kv][cap/32][hd][32]."""
 
     def __init__(self, gamma, kv_len, cap: int, max_ctx: int | None = None, kcache=None,
-                 vcache=None, shape=None, device="cuda", caches=None, tree_parents=None):
+                 vcache=None, shape=None, device="cuda", caches=None, tree_parents=None,
+                 kscale=None, vscale=None):
         self.gamma_list = [int(g) for g in gamma]
         self.B = len(self.gamma_list)
         self.T = int(sum(g + 1 for g in self.gamma_list))
@@ -130,6 +131,15 @@ class DeviceBatch:
                 self.k.append(torch.zeros(shape.n_kv, cap, shape.hd, dtype=torch.bfloat16, device=device))
                 self.v.append(torch.zeros(shape.n_kv, cap // 32, shape.hd, 32, dtype=torch.bfloat16,
                                           device=device))
+        # int8 caches (codes in the bf16 layouts, one byte per value) and their
+        # per-vector fp32 scales [n_kv][cap]
+        self.kv8 = kscale is not None
+        self.ks, self.vs = [], []
+        if self.kv8:
+            self.ks = [to_dev(np.ascontiguousarray(kscale[i]), device) for i in range(self.B)]
+            self.vs = [to_dev(np.ascontiguousarray(vscale[i]), device) for i in range(self.B)]
+        self.ksptr = torch.tensor([t.data_ptr() for t in self.ks] or [0], dtype=torch.int64, device=device)
+        self.vsptr = torch.tensor([t.data_ptr() for t in self.vs] or [0], dtype=torch.int64, device=device)
         # token trees: every sequence's parent array, stacked like the tokens
         self.tree_parent = None
         if tree_parents is not None:
@@ -149,14 +159,22 @@ class DeviceBatch:
         b.v_cache = self.vptr.data_ptr()
         b.err_flag = self.err.data_ptr()
         b.tree_parent = self.tree_parent.data_ptr() if self.tree_parent is not None else None
+        b.kv_dtype = 1 if self.kv8 else 0
+        b.k_scale = self.ksptr.data_ptr() if self.kv8 else None
+        b.v_scale = self.vsptr.data_ptr() if self.kv8 else None
         return b
 
     def k_logical(self, i: int) -> np.ndarray:
-        """Sequence i's K cache as bf16 bits [n_kv][cap][hd]."""
+        """Sequence i's K cache as bf16 bits [n_kv][cap][hd] (int8 caches: the codes)."""
+        if self.kv8:
+            return self.k[i].cpu().numpy()
         return self.k[i].view(torch.int16).cpu().numpy().view(np.uint16)
 
     def v_logical(self, i: int) -> np.ndarray:
-        """Sequence i's V cache as bf16 bits in position-major order [n_kv][cap][hd]."""
+        """Sequence i's V cache as bf16 bits in position-major order [n_kv][cap][hd]
+        (int8 caches: the codes)."""
+        if self.kv8:
+            return v_logical(self.v[i].cpu().numpy())
         return v_logical(self.v[i].view(torch.int16).cpu().numpy().view(np.uint16))
 
 

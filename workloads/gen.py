@@ -23,7 +23,7 @@ __all__ = [
     "Shape", "SHAPES", "rng_for", "f32_to_bf16_bits", "bf16_bits_to_f32",
     "normal_f32", "normal_bf16", "quantize_int4_g32", "uniforms_2m24",
     "stable_softmax_f32", "sample_from_probs", "Weights", "layer_weights",
-    "head_weights", "embed_weights", "kv_cache", "hidden_states",
+    "head_weights", "embed_weights", "kv_cache", "kv_cache_int8", "hidden_states",
 ]
 
 _CHUNK = 1 << 24
@@ -255,6 +255,28 @@ def kv_cache(shape: Shape, ctx: np.ndarray, cap: int, seed: int, tag: str = "lay
     for f in [_pool().submit(seq, i) for i in range(b)]:
         f.result()
     return k, v
+
+
+def kv_cache_int8(shape: Shape, ctx: np.ndarray, cap: int, seed: int, tag: str = "layer0"):
+    """Synthetic int8 K and V caches: codes [B, n_kv, cap, hd] int8 and fp32
+    scales [B, n_kv, cap] per cached vector, shaped like quantised N(0,1)
+    vectors (codes from a rounded N(0, 40^2) clipped to +-127, scales around
+    3/127).  Rows >= ctx_i hold code 127 with scale 3e38 (never to be read)."""
+    b = len(ctx)
+    out = []
+    for which in ("k", "v"):
+        codes = np.full((b, shape.n_kv, cap, shape.hd), 127, dtype=np.int8)
+        scales = np.full((b, shape.n_kv, cap), 3.0e38, dtype=np.float32)
+        rng = rng_for(seed, f"{tag}/{which}cache_int8")
+        for i in range(b):
+            c = int(np.asarray(ctx)[i])
+            if c:
+                codes[i, :, :c] = np.clip(np.rint(rng.standard_normal((shape.n_kv, c, shape.hd)) * 40.0),
+                                          -127, 127).astype(np.int8)
+                scales[i, :, :c] = (3.0 / 127.0 * np.exp(0.1 * rng.standard_normal((shape.n_kv, c)))
+                                    ).astype(np.float32)
+        out += [codes, scales]
+    return tuple(out)  # kcodes, kscales, vcodes, vscales
 
 
 def hidden_states(t: int, d: int, seed: int, tag: str = "x") -> np.ndarray:
