@@ -297,7 +297,7 @@ LAUNCH_SETTINGS = [
     "qkv:2:4:16,o:1:4:16,gu:1:4:16,down:4:4:16",
     "qkv:4:2:1,o:2:4:1,gu:3:8:1,down:5:2:1",
     "qkv:1:2:0,o:1:2:0,gu:1:2:0,down:1:2:0",   # LDS-tiled kernel (bf16 packed)
-    "qkv:1:2:2,o:2:2:2,gu:1:2:2,down:3:2:2",   # wide streaming kernel (bf16 packed)
+    "qkv:1:2:2,o:2:2:2,gu:1:2:2,down:3:2:2",   # wide streaming kernel (bf16 / int4 packed)
     "qkv:1:2:3,o:1:2:3,gu:1:2:3,down:1:2:3",   # square-tiled kernel (bf16 packed)
 ]
 
@@ -338,7 +338,7 @@ def test_head_launch_settings(wtype):
     ref = OV.head_logits(head.Wlm, yh)
     try:
         for spec in (None, "head:1:4:1", "head:1:8:1", "head:1:8:4", "head:2:4:8", "head:3:8:1",
-                     "head:1:2:0"):
+                     "head:1:2:0", "head:3:2:2"):
             assert sv.sv_set_gemm_tuning(spec) == 0
             n = sv.sv_verify_layer_workspace_bytes(head.L, head.bs, sv.SV_HEAD_LOGITS)
             head.ws = tg.workspace(n)
@@ -347,6 +347,41 @@ def test_head_launch_settings(wtype):
             err = rel_rows(lg, ref)
             say(f"head {wtype} [{spec}]: logits rel err {err:.2e}")
             assert err < TOL[wtype], spec
+    finally:
+        sv.sv_set_gemm_tuning(None)
+
+
+@pytest.mark.parametrize("gamma", [[3, 3, 0, 1], [0, 2, 1], [7, 7, 7, 7, 7, 3, 2], [9, 0, 4, 7, 5, 3]],
+                         ids=["T13", "T6", "T45", "T34"])
+def test_int4_wide_token_blocks(gamma):
+    """The int4 wide kernel at every token-block size (16, 32 and 64 tokens,
+    ragged) and with K splits, forced on every GEMM of the decoder layer and
+    the head, against the oracle."""
+    shape = Shape(2048, 16, 4, 128, 8192, 20011)
+    ctx = [int(c) for c in np.linspace(3, 700, len(gamma)).astype(int)]
+    wl = custom_workload(shape, "int4", gamma, ctx, seed=23)
+    dec = GpuDecoder(wl, packed=True)
+    xh = hidden_states(wl.T, shape.d, wl.seed)
+    ref = dec.oracle(xh)
+    head = GpuHead(wl, packed=True)
+    try:
+        for spec in ("qkv:1:2:2,o:1:2:2,gu:1:2:2,down:1:2:2,head:1:2:2",
+                     "qkv:3:2:2,o:2:2:2,gu:5:2:2,down:7:2:2,head:2:2:2"):
+            assert sv.sv_set_gemm_tuning(spec) == 0
+            dec.ws_bytes = sv.sv_verify_layer_workspace_bytes(dec.L, dec.bs)
+            dec.ws = tg.workspace(dec.ws_bytes)
+            y = dec.run(tg.to_dev(xh))
+            torch.cuda.synchronize()
+            assert dec.batch.err.item() == 0
+            err = rel_rows(dev_bf16_to_f64(y), ref.y)
+            n = sv.sv_verify_layer_workspace_bytes(head.L, head.bs, sv.SV_HEAD_LOGITS)
+            head.ws = tg.workspace(n)
+            head.ws_bytes[sv.SV_HEAD_LOGITS] = n
+            yh = dev_bf16_to_f64(y)
+            lg = head.run(y, logits=True).cpu().numpy()
+            errh = rel_rows(lg, OV.head_logits(head.Wlm, yh))
+            say(f"int4 wide T={wl.T} [{spec}]: y rel err {err:.2e}, logits {errh:.2e}")
+            assert err < TOL["int4"] and errh < TOL["int4"], spec
     finally:
         sv.sv_set_gemm_tuning(None)
 
@@ -422,10 +457,11 @@ def test_many_tokens_layer_and_head(tiling, wtype):
     streaming kernel (three 128-token blocks, K splits), and with every GEMM
     on the square-tiled kernel (two 256-token blocks, the second ragged),
     without and with uneven K splits (partial tiles per 128-token block, the
-    third block ragged and the fourth empty).  With int4 weights (from 256 tokens) the
-    tiled and wide launches run on packed bf16 dequantised into the
-    workspace, the square launches convert the int4 codes in LDS, and the
-    one-wave setting keeps the int4 streaming kernel."""
+    third block ragged and the fourth empty).  With int4 weights the default
+    and wide settings (and the tiled one: the tiled kernel has no int4 form)
+    run the int4 wide kernel (codes converted in registers, three 128-token
+    blocks, even and uneven K splits), the square launches convert the int4
+    codes in LDS, and the one-wave setting keeps the int4 streaming kernel."""
     shape = Shape(2048, 16, 4, 128, 8192, 20011)
     gamma = [14] * 18 + [11, 12, 4]                  # 18*15 + 12 + 13 + 5 = 300 tokens
     ctx = [int(c) for c in np.linspace(0, 300, len(gamma)).astype(int)]

@@ -163,7 +163,6 @@ Tune tune() {
 
 struct GemmCfg {
   int nblk = 0, ntblk = 0, splits = 1, tt = 1, ksteps = 0, K = 0, N = 0, depth = 2, kw = 1;
-  bool dq = false;  // packed int4 weights dequantized to packed bf16 for this launch
   size_t partial_floats() const { return gemm_partial_floats(nblk, splits, ntblk, tt); }
   size_t counters() const { return splits > 1 ? (size_t)nblk * ntblk : 0; }
 };
@@ -288,27 +287,45 @@ GemmCfg gemm_cfg(int kind, int nblk, int N, int T, int K, int wtype, bool packed
   return c;
 }
 
-// Packed int4 weights at hundreds of stacked tokens: the streaming int4 kernel
-// re-reads and re-dequantises the weights once per token block of 64, so the
-// launch instead dequantises them once into packed bf16 in the workspace (a
-// pass at about 6 TB/s over 4.5 bytes per weight) and runs the bf16 tiled /
-// square / wide kernels.  Measured on the 9B-class shapes: a clear gain from
-// 256 tokens (LM head at 512: 2124 -> 733 + 256 us), about even at 128.
-constexpr int kDqMinT = 256;
+// Packed int4 weights.  The int4 form of the wide streaming kernel shares
+// each step's token fragments (through LDS) among the workgroup's 256 weight
+// rows and converts each weight once per token block of 16, 32, 64 or 128
+// tokens (in registers); K splits fill the resident workgroups (two per CU
+// for blocks of up to 64 tokens, one for 128) at 4 or more int4 K steps each.
+// From the size where the bf16 square-tiled kernel would win, its int4 form
+// (converted in LDS).  The int4 streaming kernel (several waves per row
+// group sharing K) stays where the wide grid is small: up to 64 tokens
+// unless the matrix has 64 or more row blocks of 256 (the 9B-class LM head at
+// 64 tokens: 390 -> 136 us, gate||up 69 -> 41 us; QKV and O slower), and up to
+// 16 tokens unless it has 256 (the LM head: 94 -> 86 us).  Tuning overrides:
+// waves per unit 1-16 keep the streaming int4 kernel, 2 (and 0: the tiled
+// kernel has no int4 form) the wide one, 3 the square one.
 GemmCfg gemm_cfg_w(int kind, int nblk, int N, int T, int K, int wtype, bool packed) {
-  if (wtype == SV_W_INT4_G32 && packed && T >= kDqMinT) {
-    GemmCfg c = gemm_cfg(kind, nblk, N, T, K, SV_W_BF16, true);
-    // the square-tiled kernel has an int4 form (converts in LDS, no copy)
-    if (c.kw == kGemmSquare) return c;
-    if (c.kw == kGemmTiled || c.kw == kGemmWide) {
-      c.dq = true;
-      return c;
-    }
+  if (wtype == SV_W_INT4_G32 && packed) {
+    const Tune tn = tune();
+    const int ov = tn.kw[kind];
+    if (ov == 1 || ov == 4 || ov == 8 || ov == 16) return gemm_cfg(kind, nblk, N, T, K, wtype, packed);
+    const GemmCfg b = gemm_cfg(kind, nblk, N, T, K, SV_W_BF16, true);
+    if (b.kw == kGemmSquare && ov != 2 && ov != 0) return b;
+    GemmCfg c;
+    c.nblk = nblk;
+    c.N = N;
+    c.K = K;
+    c.ksteps = K / kstep_of(wtype);
+    c.kw = kGemmWide;
+    c.tt = T <= 16 ? 1 : T <= 32 ? 2 : T <= 64 ? 4 : 8;
+    c.ntblk = (T + 16 * c.tt - 1) / (16 * c.tt);
+    const long long per = (long long)((nblk + 7) / 8) * c.ntblk;
+    const long long slots = c.tt == 8 ? 256 : 512;
+    c.splits = (int)std::max<long long>(1, std::min<long long>(slots / per, c.ksteps / 4));
+    if (tn.splits[kind] > 0) c.splits = std::max(1, std::min(tn.splits[kind], c.ksteps));
+    c.depth = 2;
+    if (c.splits > 1 && (size_t)c.nblk * c.ntblk > kMaxCounters) c.splits = 1;
+    const int nrb = (nblk + 7) / 8;
+    if (ov == 2 || ov == 0 || T > 64 || nrb >= (T > 16 ? 64 : 256)) return c;
   }
   return gemm_cfg(kind, nblk, N, T, K, wtype, packed);
 }
-// Bytes of packed bf16 for one matrix of `rows` rows (32-row groups) and K.
-size_t dq_bytes(int rows, int K) { return (size_t)((rows + 31) / 32) * 32 * K * 2; }
 
 // Token operands in fragment layout: the bf16 streaming launches with several
 // waves per unit read them as contiguous KiB fragments (tiles = ntblk * tt).
@@ -322,7 +339,7 @@ struct LayerPlan {
   int T = 0, B = 0, G = 1, gmax = 0;
   GemmCfg qkv, o, gu, down, head;
   bool pk_qkv = false, pk_o = false, pk_gu = false, pk_down = false;
-  size_t off_xp = 0, off_x1p = 0, off_dq = 0;
+  size_t off_xp = 0, off_x1p = 0;
   int attn_chunk = 256, attn_items = 0, attn_rpad = 16;
   size_t off_counters = 0, off_partial = 0, off_qbuf = 0, off_po = 0, off_pml = 0;
   size_t off_attn = 0, off_x1 = 0, off_act = 0, off_stats = 0, off_items = 0;
@@ -394,7 +411,6 @@ sv_status plan_layer(const sv_layer *L, const sv_batch *b, int32_t flags, LayerP
     pl.off_partial = take(pl.head.partial_floats() * sizeof(float));
     pl.off_stats = take((size_t)pl.head.nblk * pl.T * 2 * sizeof(float));
     pl.off_rnorm = take((size_t)pl.T * sizeof(float));
-    pl.off_dq = take(pl.head.dq ? dq_bytes(L->vocab, L->d) : 0);
     pl.bytes = off;
     return SV_OK;
   }
@@ -463,12 +479,6 @@ sv_status plan_layer(const sv_layer *L, const sv_batch *b, int32_t flags, LayerP
   pl.off_xp = take(pl.pk_qkv ? frag_bytes(pl.qkv) : 0);
   pl.off_x1p = take(pl.pk_gu ? frag_bytes(pl.gu) : 0);
   // one buffer for the dequantised weights of whichever projection runs
-  size_t dq = 0;
-  if (pl.qkv.dq) dq = std::max(dq, dq_bytes(hq * hd, d) + 2 * dq_bytes(hk * hd, d));
-  if (pl.o.dq) dq = std::max(dq, dq_bytes(d, hq * hd));
-  if (pl.gu.dq) dq = std::max(dq, 2 * dq_bytes(F, d));
-  if (pl.down.dq) dq = std::max(dq, dq_bytes(d, F));
-  pl.off_dq = take(dq);
   pl.off_rnorm = take((size_t)pl.T * sizeof(float));
   pl.off_rparts = take((size_t)pl.o.nblk * pl.T * sizeof(float));
   pl.off_tseq = take((size_t)pl.T * sizeof(int));
@@ -510,24 +520,6 @@ GemmMat mat_of(const sv_matrix &m, int rows) {
   g.s = static_cast<const uint16_t *>(m.scale);
   g.rows = rows;
   return g;
-}
-
-// For a launch with dequantised weights: rewrite p's matrices to packed bf16
-// copies in the workspace (one after another from `buf`); returns the weight
-// type the launch then uses.
-hipError_t dequant_mats(const GemmCfg &c, GemmParams &p, int K, unsigned char *buf, int &wt, hipStream_t s) {
-  if (!c.dq) return hipSuccess;
-  size_t off = 0;
-  for (int i = 0; i < p.nmat; ++i) {
-    const hipError_t e = launch_dequant_int4(p.mat[i].rows, K, p.mat[i].w, p.mat[i].s, buf + off, s);
-    if (e != hipSuccess) return e;
-    p.mat[i].w = buf + off;
-    p.mat[i].s = nullptr;
-    off += dq_bytes(p.mat[i].rows, K);
-  }
-  p.packed = 1;
-  wt = WT_BF16;
-  return hipSuccess;
 }
 
 }  // namespace
@@ -598,9 +590,7 @@ extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const
     p.out = y_out;
     p.ldo = L->vocab;
     p.stats = reinterpret_cast<float *>(ws + pl.off_stats);
-    int wl = wt;
-    e = dequant_mats(pl.head, p, L->d, ws + pl.off_dq, wl, s);
-    if (e != hipSuccess) return SV_ERR_HIP;
+    const int wl = wt;
     e = launch_gemm(p, wl, pl.head.tt, pl.head.depth, pl.head.kw, s, SV_K_GEMM_LM_HEAD);
     if (e == hipSuccess && !(flags & SV_HEAD_LOGITS)) {
       HeadSoftmaxParams h;
@@ -688,9 +678,7 @@ extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const
     p.vc = b->v_cache;
     p.kvstage = pl.kv8 ? reinterpret_cast<uint16_t *>(ws + pl.off_kvstage) : nullptr;
     p.err = b->err_flag;
-    int wl = wt;
-    e = dequant_mats(pl.qkv, p, d, ws + pl.off_dq, wl, s);
-    if (e != hipSuccess) return SV_ERR_HIP;
+    const int wl = wt;
     e = launch_gemm(p, wl, pl.qkv.tt, pl.qkv.depth, pl.qkv.kw, s, SV_K_GEMM_QKV);
     if (e != hipSuccess) return SV_ERR_HIP;
   }
@@ -760,9 +748,7 @@ extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const
     p.ldo = d;
     p.resid = static_cast<const uint16_t *>(x_in);
     p.sq_out = rparts;  // sums of squares of x1 for the next RMSNorm
-    int wl = wt;
-    e = dequant_mats(pl.o, p, hq * hd, ws + pl.off_dq, wl, s);
-    if (e != hipSuccess) return SV_ERR_HIP;
+    const int wl = wt;
     e = launch_gemm(p, wl, pl.o.tt, pl.o.depth, pl.o.kw, s, SV_K_GEMM_O);
     if (e != hipSuccess) return SV_ERR_HIP;
   }
@@ -795,9 +781,7 @@ extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const
     p.epi = EPI_SWIGLU;
     p.out = act;
     p.ldo = F;
-    int wl = wt;
-    e = dequant_mats(pl.gu, p, d, ws + pl.off_dq, wl, s);
-    if (e != hipSuccess) return SV_ERR_HIP;
+    const int wl = wt;
     e = launch_gemm(p, wl, pl.gu.tt, pl.gu.depth, pl.gu.kw, s, SV_K_GEMM_GATE_UP);
     if (e != hipSuccess) return SV_ERR_HIP;
   }
@@ -815,9 +799,7 @@ extern "C" sv_status sv_verify_layer(const sv_layer *L, const sv_batch *b, const
     p.out = y_out;
     p.ldo = d;
     p.resid = x1;
-    int wl = wt;
-    e = dequant_mats(pl.down, p, F, ws + pl.off_dq, wl, s);
-    if (e != hipSuccess) return SV_ERR_HIP;
+    const int wl = wt;
     e = launch_gemm(p, wl, pl.down.tt, pl.down.depth, pl.down.kw, s, SV_K_GEMM_DOWN);
     if (e != hipSuccess) return SV_ERR_HIP;
   }

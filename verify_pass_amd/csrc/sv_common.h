@@ -294,7 +294,6 @@ hipError_t launch_gemm(const GemmParams &p, int wtype, int tok_tiles, int depth,
 hipError_t launch_pack(int wtype, int N, int K, const void *w, const void *scale, void *wp,
                        void *sp, hipStream_t s);
 // Packed int4 [N][K] (+ scales) -> packed bf16, the values the int4 GEMM uses.
-hipError_t launch_dequant_int4(int N, int K, const void *wp, const void *sp, void *dst, hipStream_t s);
 // Workspace floats for the K-split partial tiles of one GEMM launch.
 size_t gemm_partial_floats(int ngroups, int splits, int ntblk, int tok_tiles);
 hipError_t launch_prep(const PrepParams &p, hipStream_t s);

@@ -42,6 +42,7 @@ hipError_t launch_gemm_tiled_bf16(const GemmParams &p, hipStream_t s, int trace_
 hipError_t launch_gemm_square_bf16(const GemmParams &p, hipStream_t s, int trace_class);
 hipError_t launch_gemm_square_int4(const GemmParams &p, hipStream_t s, int trace_class);
 hipError_t launch_gemm_wide_bf16(const GemmParams &p, int tok_tiles, int depth, hipStream_t s, int trace_class);
+hipError_t launch_gemm_wide_int4(const GemmParams &p, int tok_tiles, hipStream_t s, int trace_class);
 
 hipError_t launch_gemm(const GemmParams &p, int wtype, int tok_tiles, int depth, int kw, hipStream_t s,
                        int trace_class) {
@@ -57,7 +58,13 @@ hipError_t launch_gemm(const GemmParams &p, int wtype, int tok_tiles, int depth,
     return wtype == WT_INT4 ? launch_gemm_square_int4(p, s, trace_class) : launch_gemm_square_bf16(p, s, trace_class);
   }
   if (kw == kGemmWide) {
-    if (wtype != WT_BF16 || !p.packed || (tok_tiles != 4 && tok_tiles != 8)) return hipErrorInvalidValue;
+    if (!p.packed) return hipErrorInvalidValue;
+    if (wtype == WT_INT4) {
+      if (tok_tiles != 1 && tok_tiles != 2 && tok_tiles != 4 && tok_tiles != 8) return hipErrorInvalidValue;
+      return launch_gemm_wide_int4(p, tok_tiles, s, trace_class);
+    }
+    if (tok_tiles != 4 && tok_tiles != 8) return hipErrorInvalidValue;
+    if (wtype != WT_BF16) return hipErrorInvalidValue;
     return launch_gemm_wide_bf16(p, tok_tiles, depth, s, trace_class);
   }
   if (wtype == WT_BF16) return launch_gemm_bf16(p, tok_tiles, depth, kw, s, trace_class);
@@ -109,48 +116,7 @@ __global__ __launch_bounds__(256) void pack_int4_kernel(const uint32_t *src, con
   }
 }
 
-// Packed int4 (with its group scales) to packed bf16, formed exactly as the
-// int4 GEMM forms its MFMA operand (code - 8, times the scale in fp32, rounded
-// to bf16).  One thread per 16-byte int4 fragment (row 32 g + 16 a + l16,
-// k = 128 s + 32 gq' .. +31): its four words are the eight-value pieces
-// k = 128 s + 32 gq' + 8 w of the bf16 fragments of K step 2 s + (gq' >> 1),
-// half gq' & 1, lane (w, l16).
-__global__ __launch_bounds__(256) void dequant_int4_kernel(const uint4 *wp, const uint16_t *sp, uint4 *dst,
-                                                           int N, int K) {
-  const int ks = K / 128;
-  const size_t ng = (size_t)(N + 31) / 32;
-  const size_t total = ng * ks * 128;
-  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= total) return;
-  // idx = ((s * ng + g) * 2 + a) * 64 + lane'
-  const int lane = idx & 63, a = (idx >> 6) & 1;
-  const size_t sg = idx >> 7;
-  const size_t g = sg % ng;
-  const int s = (int)(sg / ng);
-  const int gq = lane >> 4, l16 = lane & 15;
-  const uint4 w4 = wp[idx];
-  const float sc = bf2f(sp[idx]);
-  const uint32_t words[4] = {w4.x, w4.y, w4.z, w4.w};
-  // bf16 fragment base of (step 2 s + (gq >> 1), group g, tile a, half gq & 1)
-  uint4 *o = dst + ((((size_t)(2 * s + (gq >> 1)) * ng + g) * 2 + a) * 2 + (gq & 1)) * 64 + l16;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    uint32_t h[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      h[e] = f2bf(static_cast<float>(static_cast<int>((words[w] >> (4 * e)) & 15u) - 8) * sc);
-    o[w * 16] = uint4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-  }
-}
 }  // namespace
-
-hipError_t launch_dequant_int4(int N, int K, const void *wp, const void *sp, void *dst, hipStream_t s) {
-  const size_t total = (size_t)((N + 31) / 32) * (K / 128) * 128;
-  hipLaunchKernelGGL(dequant_int4_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
-                     static_cast<const uint4 *>(wp), static_cast<const uint16_t *>(sp), static_cast<uint4 *>(dst),
-                     N, K);
-  return hipGetLastError();
-}
 
 hipError_t launch_pack(int wtype, int N, int K, const void *w, const void *scale, void *wp, void *sp,
                        hipStream_t s) {

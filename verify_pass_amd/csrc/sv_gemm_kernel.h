@@ -155,13 +155,23 @@ __device__ __forceinline__ XStep<WT> load_x(const uint16_t *xrow, int ks, int gq
   return r;
 }
 
+// a & m through one v_and_b32 the compiler cannot see into: it then
+// converts each masked byte with v_cvt_f32_ubyte{0..3} instead of first
+// re-extracting every 4-bit field from the original word
+__device__ __forceinline__ uint32_t and_opaque(uint32_t a, uint32_t m) {
+  uint32_t r;
+  asm("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(m), "v"(a));
+  return r;
+}
+
 // int4 word (8 codes, offset by 8) times the group scale, to bf16.  The
 // nibbles are unpacked bytewise (one mask for the even, a shift and mask for
 // the odd ones, each byte then converted to fp32 directly); (code - 8) * s is
 // one fma from the unsigned nibble, exact in fp32 (a 4-bit times an 8-bit
-// significand), and pairs are rounded to bf16 by one conversion each.
+// significand), and pairs are rounded to bf16 by one conversion each:
+// 23 VALU operations per 8 weights.
 __device__ __forceinline__ bf16x8 dequant8(uint32_t word, float s) {
-  const uint32_t ev = word & 0x0F0F0F0Fu, od = (word >> 4) & 0x0F0F0F0Fu;
+  const uint32_t ev = and_opaque(word, 0x0F0F0F0Fu), od = and_opaque(word >> 4, 0x0F0F0F0Fu);
   const float m8 = -8.f * s;
   uint32_t h[4];
 #pragma unroll
@@ -1147,6 +1157,200 @@ hipError_t launch_wide_d(const GemmParams &p, hipStream_t s, int trace_class) {
   hipLaunchKernelGGL((gemm_wide_kernel<EPI, TT, D>), dim3(wide_grid(p)), dim3(256), 0, s, p);
   trace_after(trace_class, s);
   return hipGetLastError();
+}
+
+// The wide streaming kernel for packed int4 weights: the same tiling (8 row
+// groups x 16 TT tokens per workgroup, each wave streaming two row groups'
+// codes and scales into registers, the token operand shared in LDS), with
+// int4 steps of 128 along K.  Each step's weights are converted to bf16 once
+// in registers (dequant8) and reused for every token tile, so a weight is
+// read and converted once per 16 TT tokens (the int4 streaming kernel does so
+// per 16 x up to 4 tokens).  The token fragments follow the int4 operand
+// order (lane group gq holds one group of 32 along K).  D = 2 steps of
+// lookahead (an LDS ring of three slots of TT x 4 KiB; a step is 128 of K).
+template <int EPI, int TT, int D>
+__global__ __launch_bounds__(256, (TT >= 8 ? 1 : 2)) void gemm_wide4_kernel(GemmParams p) {
+  constexpr int NB = D + 1;   // ring slots (registers and LDS)
+  constexpr int XF = TT * 4;  // token fragments (1 KiB) per step
+  constexpr int XW = XF / 4;  // loaded by each wave
+  constexpr int PER = 8 + XW; // loads a wave issues per step (4 x codes and scales, tokens)
+  constexpr int SLOT = XF * 1024;
+  static_assert(NB == 3, "three ring slots");
+  static_assert((D - 1) * PER <= 63, "outstanding loads beyond the vmcnt range");
+  __shared__ __align__(16) unsigned char xr0[SLOT], xr1[SLOT], xr2[SLOT];
+  auto slot_of = [&](auto kc) -> unsigned char * {
+    constexpr int k = decltype(kc)::value;
+    if constexpr (k == 0) return xr0;
+    else if constexpr (k == 1) return xr1;
+    else return xr2;
+  };
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int gq = lane >> 4, l16 = lane & 15;
+  const int nrb = (p.nblk + kWGroups - 1) / kWGroups;
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int tb = wg % p.ntblk;
+  const int rest = wg / p.ntblk;
+  const int rb = rest % nrb, split = rest / nrb;
+  const int t0 = tb * TT * 16;
+  const int u0 = (int)((long long)split * p.ksteps / p.splits);
+  const int u1 = (int)((long long)(split + 1) * p.ksteps / p.splits);
+  const int ns = u1 - u0;
+
+  int grp[2];
+  bool gact[2];
+  WSrc<WT_INT4> src[2][2];
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi) {
+    const int gr = rb * kWGroups + 2 * wave + gi;
+    gact[gi] = gr < p.nblk;
+    grp[gi] = min(gr, p.nblk - 1);
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      int mi = 0, pr0 = 0;
+      if (!map_row(p, grp[gi], a, 0, mi, pr0)) { mi = 0; pr0 = 0; }
+      src[gi][a] = make_src<WT_INT4>(p.mat[mi], pr0, pr0, p.K, p.ksteps, 1, lane, gq);
+    }
+  }
+  // token fragments this wave loads: f = wave + 4 i -> (tt = f / 4, m = f % 4),
+  // lane (gq, l16) holding x[token][128 s + 32 gq + 8 m .. + 7]
+  const uint16_t *xa[XW];
+#pragma unroll
+  for (int i = 0; i < XW; ++i) {
+    const int f = wave + 4 * i, tt = f >> 2, m = f & 3;
+    xa[i] = p.x + (size_t)min(t0 + tt * 16 + l16, p.T - 1) * p.K + (size_t)u0 * 128 + 32 * gq + 8 * m;
+  }
+
+  floatx4 acc[2][2][TT];
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) acc[gi][a][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  WStep<WT_INT4> wb[NB][2][2];  // [slot][group][tile]
+  // branch-free as the bf16 kernel: steps past the end reload the last one
+  // (and convert it with scale 0)
+  auto issue = [&](int st, auto kc) {
+    constexpr int k = decltype(kc)::value;
+    const int sc = min(st, ns - 1);
+    unsigned char *slot = slot_of(kc);
+#pragma unroll
+    for (int i = 0; i < XW; ++i) load_lds16(xa[i] + sc * 128, slot + (wave + 4 * i) * 1024);
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+      for (int a = 0; a < 2; ++a) wb[k][gi][a] = load_w<WT_INT4>(src[gi][a], u0 + sc);
+  };
+  // fragment m (K 32 gq + 8 m of the step) of the four tiles of ring slot k, in bf16
+  auto convert = [&](auto kc, auto mc, bool live, bf16x8 (&out)[2][2]) {
+    constexpr int k = decltype(kc)::value, m = decltype(mc)::value;
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        const uint4 &v = wb[k][gi][a].v;
+        const uint32_t word = m == 0 ? v.x : m == 1 ? v.y : m == 2 ? v.z : v.w;
+        out[gi][a] = dequant8(word, live ? bf2f(static_cast<uint16_t>(wb[k][gi][a].s)) : 0.f);
+      }
+  };
+  // Each step runs in four phases, one per fragment m: the MFMAs of phase m
+  // (4 tiles x TT token tiles) are interleaved with the conversion of
+  // fragment m + 1 and the LDS reads of its token fragments (phase 3 converts
+  // fragment 0 of the next step), so the VALU work of the conversion hides
+  // under the matrix pipe.
+  bf16x8 wv[2][2][2];  // [phase parity][group][tile]
+  bf16x8 xv[2][TT];    // [phase parity][token tile]
+  if (ns > 0) {
+    // steps in order: the waits count loads in issue order
+    static_for<D>([&](auto kc) {
+      issue(decltype(kc)::value, kc);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    convert(std::integral_constant<int, 0>(), std::integral_constant<int, 0>(), true, wv[0]);
+    auto step = [&](int st, auto bc) {
+      constexpr int b = decltype(bc)::value;
+      constexpr int later = (D - 1) * PER;
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (later & 15) | ((later >> 4) << 14));
+      ring_barrier();  // step st's tokens in LDS for everyone; everyone is done with step st - 1
+      // keep every instruction of this step below the wait: hoisting the
+      // conversion of a later step's weights above it makes the compiler
+      // drain all loads in flight
+      __builtin_amdgcn_sched_barrier(0);
+      issue(st + D, std::integral_constant<int, (b + D) % NB>());
+      const unsigned char *xs = slot_of(bc);
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) xv[0][tt] = as_bf16x8(ld_v4(xs + ((tt * 4) * 64 + lane) * 16));
+      __builtin_amdgcn_sched_barrier(0);
+      const bool live = st < ns, live_next = st + 1 < ns;
+      static_for<4>([&](auto mc) {
+        constexpr int m = decltype(mc)::value, P = m & 1;
+        if constexpr (m < 3) {
+          convert(bc, std::integral_constant<int, m + 1>(), live, wv[P ^ 1]);
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt)
+            xv[P ^ 1][tt] = as_bf16x8(ld_v4(xs + ((tt * 4 + m + 1) * 64 + lane) * 16));
+        } else {
+          // the next step's loads (all but this step's issue) have landed
+          __builtin_amdgcn_s_waitcnt(0x0F70 | (PER & 15) | ((PER >> 4) << 14));
+          __builtin_amdgcn_sched_barrier(0);
+          convert(std::integral_constant<int, (b + 1) % NB>(), std::integral_constant<int, 0>(), live_next, wv[0]);
+        }
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+          for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+            for (int a = 0; a < 2; ++a) acc[gi][a][tt] = mfma16x16x32(wv[P][gi][a], xv[P][tt], acc[gi][a][tt]);
+        // one MFMA, then the next phase's LDS reads and conversion in the gaps
+#pragma unroll
+        for (int i = 0; i < 4 * TT; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          if (i < TT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    };
+    for (int st0 = 0; st0 < ns; st0 += NB) static_for<NB>([&](auto kc) { step(st0 + decltype(kc)::value, kc); });
+    wait_vmem();  // the clamped tail loads
+  }
+
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi) {
+    if (!gact[gi]) continue;
+    if (p.splits > 1 && !split_reduce<TT>(p, acc[gi], grp[gi], tb, split, lane)) continue;
+    epilogue<TT, EPI>(p, acc[gi], grp[gi], t0, gq, l16);
+  }
+}
+
+template <int EPI, int TT>
+hipError_t launch_wide4_tt(const GemmParams &p, hipStream_t s, int trace_class) {
+  trace_before(trace_class, s);
+  hipLaunchKernelGGL((gemm_wide4_kernel<EPI, TT, 2>), dim3(wide_grid(p)), dim3(256), 0, s, p);
+  trace_after(trace_class, s);
+  return hipGetLastError();
+}
+
+// tok_tiles: 16-token tiles per block (1, 2, 4 or 8)
+template <int EPI>
+hipError_t launch_wide4_epi(const GemmParams &p, int tok_tiles, hipStream_t s, int trace_class) {
+  switch (tok_tiles) {
+    case 1: return launch_wide4_tt<EPI, 1>(p, s, trace_class);
+    case 2: return launch_wide4_tt<EPI, 2>(p, s, trace_class);
+    case 4: return launch_wide4_tt<EPI, 4>(p, s, trace_class);
+    default: return launch_wide4_tt<EPI, 8>(p, s, trace_class);
+  }
+}
+
+inline hipError_t launch_wide4(const GemmParams &p, int tok_tiles, hipStream_t s, int trace_class) {
+  switch (p.epi) {
+    case EPI_QKV: return launch_wide4_epi<EPI_QKV>(p, tok_tiles, s, trace_class);
+    case EPI_RESID: return launch_wide4_epi<EPI_RESID>(p, tok_tiles, s, trace_class);
+    case EPI_SWIGLU: return launch_wide4_epi<EPI_SWIGLU>(p, tok_tiles, s, trace_class);
+    default: return launch_wide4_epi<EPI_LOGITS>(p, tok_tiles, s, trace_class);
+  }
 }
 
 // tok_tiles: 4 (up to 64 tokens per block; depth = steps of lookahead, 2 or 4)
