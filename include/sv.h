@@ -183,8 +183,8 @@ typedef struct sv_batch {
    * code * scale).  The pass stores its new keys and values the same way:
    * rounded to bf16, then scale = absmax / 127 over the head's vector (fp32,
    * correctly rounded), code = clamp(rne(x / scale), -127, 127) (0 for an
-   * all-zero vector).  int8 caches need at most 16 query rows per KV head
-   * (GQA group x (gamma_i + 1)). */
+   * all-zero vector).  The query-row limit per KV head (GQA group x
+   * (gamma_i + 1) <= 128) is the same as for bf16 caches. */
   int32_t kv_dtype;
   void *const *k_scale; /* [B] device pointers (SV_KV_INT8) */
   void *const *v_scale; /* [B] */

@@ -323,8 +323,11 @@ def test_int8_kv_validation():
     assert _ws(_layer(), b)[0] == sv.SV_ERR_INVALID_ARG   # scales missing
     b.k_scale = b.v_scale = 0x6000
     assert _ws(_layer(), b)[0] == sv.SV_OK
-    b = _batch([8])                          # 18 rows per KV head: past the int8 kernel's 16
+    b = _batch([8], max_ctx=10)              # 18 rows per KV head: the query-tiled int8 kernel
     b.kv_dtype, b.k_scale, b.v_scale = sv.SV_KV_INT8, 0x6000, 0x6000
-    assert _ws(_layer(), b)[0] == sv.SV_ERR_UNSUPPORTED
+    assert _ws(_layer(), b)[0] == sv.SV_OK
     b.kv_dtype = 5
     assert _ws(_layer(), b)[0] == sv.SV_ERR_INVALID_ARG
+    b = _batch([64], max_ctx=10)             # 130 rows per KV head: past every attention kernel's 128
+    b.kv_dtype, b.k_scale, b.v_scale = sv.SV_KV_INT8, 0x6000, 0x6000
+    assert _ws(_layer(), b)[0] == sv.SV_ERR_UNSUPPORTED

@@ -1,7 +1,8 @@
 """GPU parity of verification over int8 KV caches (one fp32 scale per cached
 vector) against the oracle: layer outputs and the pass's own appended keys
-and values (dequantised) on ragged batches and at the int4 workload's full
-size, plus the host-side limits."""
+and values (dequantised) on ragged batches with up to 16 query rows per KV
+head (the key-split attention kernel) and beyond (the query-tiled kernel),
+and at the int4 and 27B-class workloads' full size."""
 import numpy as np
 import pytest
 import torch
@@ -53,6 +54,10 @@ CASES = [
     ("hd128-gqa4-bf16", Shape(512, 8, 2, 128, 1024, 3000), "bf16", [2, 0, 3, 1], [300, 0, 777, 64]),
     ("hd64-gqa2-bf16", Shape(256, 4, 2, 64, 512, 1000), "bf16", [7, 0, 3, 5, 1], [10, 513, 260, 1, 2000]),
     ("hd128-gqa4-int4", Shape(512, 8, 2, 128, 1024, 3000), "int4", [3, 3, 0], [1000, 17, 513]),
+    # more than 16 query rows per KV head: the query-tiled kernel (four waves,
+    # 40 rows; eight waves, 128 rows), ragged chunks and an empty context
+    ("hd128-gqa5-rows40-bf16", Shape(640, 10, 2, 128, 1280, 2000), "bf16", [7, 7, 3, 0], [300, 1000, 64, 0]),
+    ("hd64-gqa8-rows128-bf16", Shape(256, 16, 2, 64, 512, 1000), "bf16", [15, 3, 0, 9], [100, 31, 250, 777]),
 ]
 
 
@@ -75,3 +80,15 @@ def test_int8_kv_fullsize_int4_workload():
     say(f"int4 workload, int8 KV: all {wl.T} rows, y rel err {err:.2e}")
     assert err < TOL["int4"]
     _check_appended(wl, batch, ref, [0, 63, 127], "int4")
+
+
+def test_int8_kv_fullsize_27b_workload():
+    """The 27B-class workload (B=32, gamma=7, 2048 cached tokens: 40 query rows
+    per KV head, the query-tiled kernel) over int8 caches, every row against
+    the oracle."""
+    wl = workload(3)
+    batch, y, ref, _ = _run(wl, packed=True)
+    err = rel_rows(dev_bf16_to_f64(y), ref.y)
+    say(f"27B workload, int8 KV: all {wl.T} rows, y rel err {err:.2e}")
+    assert err < TOL["bf16"]
+    _check_appended(wl, batch, ref, [0, 15, 31], "bf16")

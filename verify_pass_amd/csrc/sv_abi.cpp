@@ -428,10 +428,9 @@ sv_status plan_layer(const sv_layer *L, const sv_batch *b, int32_t flags, LayerP
   if ((long long)pl.G * (gmax + 1) > kAttnMaxRows) return SV_ERR_UNSUPPORTED;
   // token trees: every tree within the 64-node ancestor masks
   if (b->tree_parent && gmax + 1 > kMaxTreeNodes) return SV_ERR_UNSUPPORTED;
-  // int8 caches: the key-split attention kernel (up to 16 query rows per KV head)
+  // int8 caches: codes plus per-vector scales (both attention kernels)
   if (b->kv_dtype != SV_KV_BF16 && b->kv_dtype != SV_KV_INT8) return SV_ERR_INVALID_ARG;
   pl.kv8 = b->kv_dtype == SV_KV_INT8;
-  if (pl.kv8 && (long long)pl.G * (gmax + 1) > 16) return SV_ERR_UNSUPPORTED;
   if (pl.kv8 && pl.B > 0 && (!b->k_scale || !b->v_scale)) return SV_ERR_INVALID_ARG;
   // per-sequence capacity (kv_len[i] + gamma_i + 1 <= kv_cap) is checked on the
   // device, where kv_len lives; max_ctx only sizes the attention grid

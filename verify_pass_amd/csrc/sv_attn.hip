@@ -471,7 +471,12 @@ __device__ __forceinline__ void ring_barrier() {
   __asm__ volatile("" ::: "memory");
 }
 
-template <int HD, int NW>
+// KV8: int8 caches.  Each wave then reads the codes and per-position scales
+// of a step straight into registers (the bytes are half those of bf16, and
+// the waves of a workgroup read the same lines close together in time, so
+// the repeats are served by the vector cache); the scales are applied to the
+// scores and to the probabilities as in the key-split kernel.
+template <int HD, int NW, bool KV8>
 __global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void attn_qt_kernel(AttnParams p) {
   constexpr int NDG = HD / 32, NDT = HD / 16;
   constexpr int F = 2 * NDG + NDT;   // 1 KiB fragments per step: keys (2 x NDG), values (NDT)
@@ -515,6 +520,10 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void attn_qt_kernel(Att
 
   const uint16_t *kbase = static_cast<const uint16_t *>(p.kc[seq]) + (size_t)g * p.kv_cap * HD;
   const uint16_t *vbase = static_cast<const uint16_t *>(p.vc[seq]) + (size_t)g * HD * p.kv_cap;
+  const int8_t *kbase8 = KV8 ? static_cast<const int8_t *>(p.kc[seq]) + (size_t)g * p.kv_cap * HD : nullptr;
+  const int8_t *vbase8 = KV8 ? static_cast<const int8_t *>(p.vc[seq]) + (size_t)g * HD * p.kv_cap : nullptr;
+  const float *ksc = KV8 ? static_cast<const float *>(p.ksc[seq]) + (size_t)g * p.kv_cap : nullptr;
+  const float *vsc = KV8 ? static_cast<const float *>(p.vsc[seq]) + (size_t)g * p.kv_cap : nullptr;
 
   // this lane's query fragments and causal limit (row 16 * wave + l16;
   // token trees: its ancestor mask)
@@ -628,7 +637,71 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void attn_qt_kernel(Att
       o[dt] = mfma16x16x32(as_bf16x8(v), pf, o[dt]);
     }
   };
-  if (ns > 0) {
+  // int8 caches: one step's codes and scales straight from memory
+  auto step8 = [&](int st) {
+    const int k0 = kb + st * kKeysPerStep;
+    uint2 v8[NDT];
+    load_values8<HD>(v8, vbase8, k0, l16, gq);
+    float skey[8], sval[8];  // scales of this lane's keys k0 + 8 gq + e
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int key = min(k0 + 8 * gq + e, L - 1);
+      skey[e] = ksc[key];
+      sval[e] = vsc[key];
+    }
+    uint4 kr[2][NDG];
+    load_keys8<HD>(kr, kbase8, k0, L, l16, gq);
+    floatx4 sc[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      sc[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int dg = 0; dg < NDG; ++dg) sc[kt] = mfma16x16x32(as_bf16x8(kr[kt][dg]), qf[dg], sc[kt]);
+    }
+    float sv[8];
+    float mx = kNegBig;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int key = k0 + 8 * gq + e;
+      const bool ok = key < ke && key_visible(key, lim, ctx, tree, tm);
+      sv[e] = ok ? sc[e >> 2][e & 3] * skey[e] * p.scale_log2 : -INFINITY;
+      mx = fmaxf(mx, sv[e]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    float lsum = 0.f;
+    uint32_t pb[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float pe = __builtin_amdgcn_exp2f(sv[e] - m_new);
+      lsum += pe;
+      pb[e] = f2bf(pe * sval[e]);  // the values' scale rides on p
+    }
+    l_run = l_run * alpha + lsum;
+    m_run = m_new;
+    const bf16x8 pf = as_bf16x8(uint4{pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16), pb[4] | (pb[5] << 16),
+                                      pb[6] | (pb[7] << 16)});
+    const int nvalid = L - (k0 + 8 * gq);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      uint4 v = codes_to_bf16x8(v8[dt]);
+      if (nvalid < 8) {
+        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (e >= nvalid) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+        v = uint4{w[0], w[1], w[2], w[3]};
+      }
+      o[dt] *= alpha;
+      o[dt] = mfma16x16x32(as_bf16x8(v), pf, o[dt]);
+    }
+  };
+  if constexpr (KV8) {
+    if (active)
+      for (int st = 0; st < ns; ++st) step8(st);
+  } else if (ns > 0) {
     issue(0, std::integral_constant<int, 0>());
     issue(1, std::integral_constant<int, 1>());
     for (int st0 = 0; st0 < ns; st0 += kQtStages)
@@ -680,10 +753,10 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void attn_qt_kernel(Att
   publish_merge<HD, 2, 12>(p, qst, ib.z, ib.w, seq, g, R, n1, G, flag, mw);
 }
 
-template <int HD, int NW>
+template <int HD, int NW, bool KV8 = false>
 hipError_t launch_qt(const AttnParams &p, hipStream_t s) {
   trace_before(SV_K_ATTENTION, s);
-  hipLaunchKernelGGL((attn_qt_kernel<HD, NW>), dim3(p.max_items, p.hkv), dim3(64 * NW), 0, s, p);
+  hipLaunchKernelGGL((attn_qt_kernel<HD, NW, KV8>), dim3(p.max_items, p.hkv), dim3(64 * NW), 0, s, p);
   trace_after(SV_K_ATTENTION, s);
   return hipGetLastError();
 }
@@ -705,7 +778,10 @@ hipError_t launch_rt(const AttnParams &p, hipStream_t s) {
 // four waves up to 64 rows, eight up to 128.
 template <int HD>
 hipError_t launch_hd(const AttnParams &p, hipStream_t s) {
-  if (p.kv8) return p.rpad <= 16 ? launch_rt<1, HD, true>(p, s) : hipErrorInvalidValue;
+  if (p.kv8) {
+    if (p.rpad <= 16) return launch_rt<1, HD, true>(p, s);
+    return p.rpad <= 64 ? launch_qt<HD, 4, true>(p, s) : launch_qt<HD, 8, true>(p, s);
+  }
   if (p.rpad <= 16) return launch_rt<1, HD, false>(p, s);
   if (p.rpad <= 64) return launch_qt<HD, 4>(p, s);
   return launch_qt<HD, 8>(p, s);
