@@ -386,6 +386,21 @@ def test_int4_wide_token_blocks(gamma):
         sv.sv_set_gemm_tuning(None)
 
 
+@pytest.mark.parametrize("gamma", [[9] * 10, [14] * 10, [15] * 16, [19] * 15], ids=["T100", "T150", "T256", "T300"])
+def test_int4_head_default_policy(gamma):
+    """The int4 LM head with the default launch policy across its kernel
+    changes: the wide kernel with one and with three 128-token blocks, and
+    the square-tiled one for 129 to 256 tokens (one 256-token block)."""
+    shape = Shape(2048, 16, 4, 128, 8192, 20011)
+    wl = custom_workload(shape, "int4", gamma, [5] * len(gamma), seed=29)
+    head = GpuHead(wl, packed=True)
+    yh = hidden_states(wl.T, shape.d, 81)
+    lg = head.run(tg.to_dev(yh), logits=True).cpu().numpy()
+    err = rel_rows(lg, OV.head_logits(head.Wlm, yh))
+    say(f"int4 head T={wl.T}: logits rel err {err:.2e}")
+    assert err < TOL["int4"]
+
+
 def test_kv_overflow_flagged_and_contained():
     """A sequence whose chunk would run past its cache capacity is flagged on
     the device (SV_DEV_ERR_KV_OVERFLOW): no row at or past the capacity is

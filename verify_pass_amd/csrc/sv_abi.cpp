@@ -305,8 +305,18 @@ GemmCfg gemm_cfg_w(int kind, int nblk, int N, int T, int K, int wtype, bool pack
     const Tune tn = tune();
     const int ov = tn.kw[kind];
     if (ov == 1 || ov == 4 || ov == 8 || ov == 16) return gemm_cfg(kind, nblk, N, T, K, wtype, packed);
-    const GemmCfg b = gemm_cfg(kind, nblk, N, T, K, SV_W_BF16, true);
+    GemmCfg b = gemm_cfg(kind, nblk, N, T, K, SV_W_BF16, true);
     if (b.kw == kGemmSquare && ov != 2 && ov != 0) return b;
+    // the LM head from 129 to 256 tokens: one 256-token block of the square
+    // kernel reads the weights once where the wide kernel's two 128-token
+    // blocks read them twice (9B-class, 151936 rows: 160 tokens 414 -> 387 us,
+    // 256 tokens 420 -> 411 us; from 257 the square kernel's half-empty second
+    // block loses: 320 tokens 572 -> 673 us)
+    if (kind == GK_HEAD && T > 128 && T <= 256 && ov < 0) {
+      b.kw = kGemmSquare;
+      b.splits = 1;
+      return b;
+    }
     GemmCfg c;
     c.nblk = nblk;
     c.N = N;
