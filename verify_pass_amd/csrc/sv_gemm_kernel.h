@@ -37,6 +37,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ void load_lds16(const void *g, void *lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_void *)lds, 16, 0, 0);
 }
+__device__ __forceinline__ void load_lds16(const void *g, lds_void *lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+}
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // Streaming (non-temporal) 16-byte load: weights are read once per pass and
@@ -865,6 +868,13 @@ __device__ __forceinline__ void ring_barrier() {
   __asm__ volatile("" ::: "memory");
 }
 
+// LDS byte pointers and 16-byte reads through them (address space 3).
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+__device__ __forceinline__ uint4 ld_lds_v4(const lds_u8 *p) {
+  return __builtin_bit_cast(uint4, *reinterpret_cast<lds_u32x4 *>(p));
+}
+
 template <int EPI>
 __global__ __launch_bounds__(kTThreads, 1) void gemm_tiled_kernel(GemmParams p) {
   extern __shared__ __align__(16) unsigned char lds[];
@@ -1022,7 +1032,7 @@ template <int N, class F> __device__ __forceinline__ void static_for(F &&f) {
 
 
 template <int EPI, int TT, int D>
-__global__ __launch_bounds__(256, (D <= 2 ? 2 : 1)) void gemm_wide_kernel(GemmParams p) {
+__global__ __launch_bounds__(256, (D <= 2 && TT <= 4 ? 2 : 1)) void gemm_wide_kernel(GemmParams p) {
   constexpr int NB = D + 1;   // ring slots (registers and LDS)
   constexpr int XF = TT * 2;  // token fragments (1 KiB) per step
   constexpr int XW = XF / 4;  // loaded by each wave
@@ -1030,19 +1040,19 @@ __global__ __launch_bounds__(256, (D <= 2 ? 2 : 1)) void gemm_wide_kernel(GemmPa
   constexpr int SLOT = XF * 1024;
   static_assert(XF % 4 == 0, "token fragments must split over the four waves");
   static_assert((D - 1) * PER <= 63, "outstanding loads beyond the vmcnt range");
-  static_assert(NB <= 5, "ring slots");
+  static_assert(NB <= 5 && NB * SLOT <= 160 * 1024, "ring slots");
   // one LDS object per ring slot: reads of one slot then provably do not
   // alias the direct-to-LDS loads in flight into the others, and the compiler
   // does not wait for those loads before every LDS read
   __shared__ __align__(16) unsigned char xr0[SLOT], xr1[SLOT], xr2[SLOT];
   __shared__ __align__(16) unsigned char xr3[NB > 3 ? SLOT : 16], xr4[NB > 4 ? SLOT : 16];
-  auto slot_of = [&](auto kc) -> unsigned char * {
+  auto slot_of = [&](auto kc) -> lds_u8 * {
     constexpr int k = decltype(kc)::value;
-    if constexpr (k == 0) return xr0;
-    else if constexpr (k == 1) return xr1;
-    else if constexpr (k == 2) return xr2;
-    else if constexpr (k == 3) return xr3;
-    else return xr4;
+    if constexpr (k == 0) return (lds_u8 *)xr0;
+    else if constexpr (k == 1) return (lds_u8 *)xr1;
+    else if constexpr (k == 2) return (lds_u8 *)xr2;
+    else if constexpr (k == 3) return (lds_u8 *)xr3;
+    else return (lds_u8 *)xr4;
   };
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1074,12 +1084,14 @@ __global__ __launch_bounds__(256, (D <= 2 ? 2 : 1)) void gemm_wide_kernel(GemmPa
       src[gi][a] = make_src<WT_BF16>(p.mat[mi], pr0, pr0, p.K, p.ksteps, 1, lane, gq);
     }
   }
-  // token fragments this wave loads: f = wave + 4 i -> (tt = f / 2, half m = f % 2)
-  const uint16_t *xa[XW];
+  // token fragments this wave loads: f = wave + 4 i -> (tt = f / 2, half m = f % 2),
+  // as element offsets from the split's first step
+  const uint16_t *xbase = p.x + (size_t)u0 * 64;
+  uint32_t xo[XW];
 #pragma unroll
   for (int i = 0; i < XW; ++i) {
     const int f = wave + 4 * i, tt = f >> 1, m = f & 1;
-    xa[i] = p.x + (size_t)min(t0 + tt * 16 + l16, p.T - 1) * p.K + (size_t)u0 * 64 + 32 * m + 8 * gq;
+    xo[i] = (uint32_t)min(t0 + tt * 16 + l16, p.T - 1) * (uint32_t)p.K + 32 * m + 8 * gq;
   }
 
   floatx4 acc[2][2][TT];
@@ -1094,45 +1106,64 @@ __global__ __launch_bounds__(256, (D <= 2 ? 2 : 1)) void gemm_wide_kernel(GemmPa
   // Step st's tokens go to LDS slot st % NB and its weights to wb[st % NB].
   // The loop is branch-free so the compiler can count which loads feed which
   // registers (behind conditional loads it drains every load at each step):
-  // steps past the end reload the last step (clamped addresses) and compute
-  // with a zero token operand.
-  auto issue = [&](int st, auto kc) {
+  // steps past the end reload the last step (clamped addresses) and skip
+  // their MFMAs (a wave-uniform branch around compute only).
+  auto issue = [&](int st, auto kc, lds_u8 *slot) {
     constexpr int k = decltype(kc)::value;
     const int sc = min(st, ns - 1);
-    unsigned char *slot = slot_of(kc);
 #pragma unroll
-    for (int i = 0; i < XW; ++i) load_lds16(xa[i] + sc * 64, slot + (wave + 4 * i) * 1024);
+    for (int i = 0; i < XW; ++i) load_lds16(xbase + xo[i] + sc * 64, (lds_void *)(slot + (wave + 4 * i) * 1024));
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi)
 #pragma unroll
       for (int a = 0; a < 2; ++a) wb[k][gi][a] = load_w<WT_BF16>(src[gi][a], u0 + sc);
   };
   if (ns > 0) {
-    static_for<D>([&](auto kc) { issue(decltype(kc)::value, kc); });
-    // step st (slot b = st % NB): wait for its loads (the D - 1 later steps'
-    // stay in flight), barrier, issue step st + D into the slot step st - 1
-    // used, compute
+    // steps in order: the waits count loads in issue order
+    static_for<D>([&](auto kc) {
+      issue(decltype(kc)::value, kc, slot_of(kc));
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    // step st (slot b = st % NB): wait for this wave's loads of step st (the
+    // D - 1 later steps' stay in flight) and its LDS reads of step st - 1,
+    // barrier, compute, then issue step st + D into the slot step st - 1
+    // used.  The barrier is the bare instruction (the compiler's scheduler
+    // keeps memory accesses on their side of it); a memory clobber there, as
+    // in the other kernels' ring_barrier, pins the schedule of the whole step
+    // to source order, and each LDS read then waits before its MFMAs.
     auto step = [&](int st, auto bc) {
       constexpr int b = decltype(bc)::value;
       constexpr int later = (D - 1) * PER;
-      __builtin_amdgcn_s_waitcnt(0x0F70 | (later & 15) | ((later >> 4) << 14));
-      ring_barrier();  // step st's tokens in LDS for everyone; everyone is done with step st - 1
-      issue(st + D, std::integral_constant<int, (b + D) % NB>());
-      const bool live = st < ns;
-      const unsigned char *xs = slot_of(bc);
+      __builtin_amdgcn_s_waitcnt(0x0070 | (later & 15) | ((later >> 4) << 14));  // vmcnt(later) lgkmcnt(0)
+      __builtin_amdgcn_s_barrier();  // step st's tokens in LDS for everyone; everyone is done with step st - 1
+      if (st < ns) {
+        const lds_u8 *xs = slot_of(bc);
 #pragma unroll
-      for (int m = 0; m < 2; ++m)
+        for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int tt = 0; tt < TT; ++tt) {
-          uint4 xr = ld_v4(xs + ((tt * 2 + m) * 64 + lane) * 16);
-          if (!live) xr = uint4{0u, 0u, 0u, 0u};
-          const bf16x8 xv = as_bf16x8(xr);
+          for (int tt = 0; tt < TT; ++tt) {
+            const bf16x8 xv = as_bf16x8(ld_lds_v4(xs + ((tt * 2 + m) * 64 + lane) * 16));
 #pragma unroll
-          for (int gi = 0; gi < 2; ++gi)
+            for (int gi = 0; gi < 2; ++gi)
 #pragma unroll
-            for (int a = 0; a < 2; ++a)
-              acc[gi][a][tt] = mfma16x16x32(as_bf16x8(wb[b][gi][a].v[m]), xv, acc[gi][a][tt]);
+              for (int a = 0; a < 2; ++a)
+                acc[gi][a][tt] = mfma16x16x32(as_bf16x8(wb[b][gi][a].v[m]), xv, acc[gi][a][tt]);
+          }
+        // batches of four fragments: a batch's four reads are issued after
+        // the first four of the previous batch's 16 MFMAs, so the wait before
+        // a batch (the compiler waits for every outstanding LDS read) comes
+        // 12 MFMAs after them
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS read
+#pragma unroll
+        for (int i = 0; i < 2 * TT / 4 - 1; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);   // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // DS read
+          __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);  // MFMA
         }
+        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+      }
+      constexpr int nb = (b + D) % NB;
+      issue(st + D, std::integral_constant<int, nb>(), slot_of(std::integral_constant<int, nb>()));
     };
     for (int st0 = 0; st0 < ns; st0 += NB) static_for<NB>([&](auto kc) { step(st0 + decltype(kc)::value, kc); });
     wait_vmem();  // the clamped tail loads
