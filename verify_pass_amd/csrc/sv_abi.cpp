@@ -454,13 +454,15 @@ sv_status plan_layer(const sv_layer *L, const sv_batch *b, int32_t flags, LayerP
   pl.gu = gemm_cfg_w(GK_GU, (F + 15) / 16, 2 * F, pl.T, d, w, packed);
   pl.down = gemm_cfg_w(GK_DOWN, (d + 31) / 32, d, pl.T, F, w, packed);
   pl.attn_rpad = 16 * ((pl.G * (gmax + 1) + 15) / 16);
-  // keys per work item (a multiple of 128): enough items for one round of the
-  // resident workgroups -- 3 per CU at hd 128 (the key-split kernel holds a
-  // step's keys and values in registers at once, the query-tiled one 48 KiB
-  // of LDS), 4 at hd 64 -- and at least 256 keys and ceil(length / 32) (a
-  // sequence has at most 32)
+  // keys per work item (a multiple of 128): enough items for two workgroups
+  // per CU at hd 128 (three fit -- the key-split kernel holds a step's keys
+  // and values in registers at once, the query-tiled one 48 KiB of LDS -- but
+  // the third's shorter chunks and extra merge inputs cost more than its
+  // loads in flight gain: 86 -> 82 us at 256 query tokens and 2048 cached,
+  // 25.0 -> 23.2 us at 24 tokens), 4 at hd 64, and at least 256 keys and
+  // ceil(length / 32) (a sequence has at most 32)
   const long long max_len = (long long)b->max_ctx + gmax + 1;
-  const long long slots = 256LL * (hd == 64 ? 4 : 3);
+  const long long slots = 256LL * (hd == 64 ? 4 : 2);
   const long long per_seq = std::max<long long>(1, slots / std::max<long long>(1, (long long)pl.B * hk));
   long long chunk = (max_len + per_seq - 1) / per_seq;
   chunk = std::max({chunk, 256LL, (max_len + 31) / 32});
