@@ -40,9 +40,6 @@ __device__ __forceinline__ int dslice(int dg, int gq) {
 __device__ __forceinline__ void store_dev(float *p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float load_dev(const float *p) {
-  return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Whether a query row sees key `key` of its sequence (ctx cached keys, then
