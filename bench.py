@@ -583,6 +583,172 @@ def run_workload(cid, args, K, Wm, headline, kv8=False):
 SWARM_LENGTHS = (40, 90, 150, 220, 300, 480, 650, 900)
 
 
+def tree_shape(depth: int) -> list:
+    """Parent array (topological order) of the measured token tree: a chain of
+    `depth` drafts with one alternative child at each of its first depth - 1
+    levels (2 * depth nodes with the root, e.g. 16 nodes 8 deep)."""
+    par = [-1]
+    for d in range(1, depth + 1):
+        up = 0 if d == 1 else 2 * d - 3   # the chain node one level up
+        par.append(up)                    # chain node at depth d: index 2d - 1
+        if d < depth:
+            par.append(up)                # its sibling: index 2d
+    return par
+
+
+def tree_bench(args):
+    """Token-tree verification ([slack], "What the budget says to build": a
+    small tree, about 8 to 16 deep) against linear drafts at the same depth
+    and at the same number of verified rows: step time (decoder layer with
+    ancestor masks, head probabilities, tree acceptance and the commit's row
+    moves, or linear acceptance and commit) and the tokens a step emits per
+    sequence, on synthetic data: device-generated N(0,1) hidden states and
+    KV entries, draft rows q = 0.7 p + 0.3 r (p the pass's own target row,
+    r a random softmax row), each draft drawn from its parent's q row, fresh
+    uniforms every step."""
+    import numpy as np
+    import torch
+
+    import verify_pass_amd as sv
+    from verify_pass_amd import torch_glue as tg
+    from workloads import SHAPES, head_weights, layer_weights
+
+    torch.cuda.set_device(0)
+    sh = SHAPES[args.tree_shape_name]
+    ctx, depth = args.tree_ctx, args.tree_depth
+    blist = [int(v) for v in args.tree_b.split(",")]
+    seed = 20261
+    rng = np.random.default_rng(seed)
+    mats = {k: tg.upload_matrix(v, packed=True) for k, v in layer_weights(sh, "bf16", seed).items()}
+    lm = tg.upload_matrix(head_weights(sh, "bf16", seed), packed=True)
+    Ld = tg.decoder_struct(sh, "bf16", mats, packed=True)
+    Lh = tg.head_struct(sh, "bf16", lm, packed=True)
+    V = sh.vocab
+    stream = tg.stream_handle()
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    tpar = tree_shape(depth)
+    variants = [("tree", len(tpar) - 1), ("chain-depth", depth), ("chain-rows", len(tpar) - 1)]
+    n_it, rows = 10, []
+    log(f"tree: {args.tree_shape_name} bf16 ctx {ctx}, tree of {len(tpar)} nodes {depth} deep, B {blist}")
+
+    def rand_rows(n):
+        z = rng.standard_normal((n, V)).astype(np.float32) * 3.0
+        z -= z.max(1, keepdims=True)
+        e = np.exp(z)
+        return e / e.sum(1, keepdims=True)
+
+    for B in blist:
+        cap = (ctx + len(tpar) + 31) // 32 * 32
+        kcs = [torch.randn(sh.n_kv, cap, sh.hd, device="cuda", generator=gen).to(torch.bfloat16)
+               for _ in range(B)]
+        vcs = [torch.randn(sh.n_kv, cap // 32, sh.hd, 32, device="cuda", generator=gen).to(torch.bfloat16)
+               for _ in range(B)]
+        for name, g in variants:
+            tree = name == "tree"
+            T = B * (g + 1)
+            batch = tg.DeviceBatch([g] * B, [ctx] * B, cap, tree_parents=[tpar] * B if tree else None)
+            batch.k, batch.v = kcs, vcs
+            batch.kptr = torch.tensor([t.data_ptr() for t in kcs], dtype=torch.int64, device="cuda")
+            batch.vptr = torch.tensor([t.data_ptr() for t in vcs], dtype=torch.int64, device="cuda")
+            gl = [g] * B
+            nd = sv.sv_verify_layer_workspace_bytes(Ld, batch.struct())
+            nh = sv.sv_verify_layer_workspace_bytes(Lh, batch.struct(), 0)
+            na = (sv.sv_accept_tree_workspace_bytes(B, V, gl) if tree
+                  else sv.sv_accept_commit_workspace_bytes(B, V, sv.SV_ACCEPT_STOCHASTIC, gl))
+            ws = tg.workspace(max(nd, nh, na))
+            nws = ws.numel()
+            x = torch.randn(T, sh.d, device="cuda", generator=gen).to(torch.bfloat16)
+            y = torch.empty_like(x)
+            probs = torch.empty(T, V, dtype=torch.float32, device="cuda")
+            kv_all = batch.kv_len.clone().repeat(3 + n_it, 1).contiguous()
+            bss = []
+            for k in range(3 + n_it):
+                b_ = batch.struct()
+                b_.kv_len = kv_all[k].data_ptr()
+                bss.append(b_)
+            # the pass's target rows, then drafts from q rows close to them
+            assert sv.sv_verify_layer(Ld, bss[0], x, y, 0, ws, nws, stream) == 0
+            assert sv.sv_verify_layer(Lh, bss[0], y, probs, 0, ws, nws, stream) == 0
+            torch.cuda.synchronize()
+            assert batch.err.item() == 0
+            p_h = probs.cpu().numpy()
+            if tree:
+                q_h = (0.7 * p_h + 0.3 * rand_rows(T)).astype(np.float32)
+                tok = np.zeros(T, np.int32)
+                for i in range(B):
+                    for j in range(1, g + 1):
+                        row = q_h[i * (g + 1) + tpar[j]].astype(np.float64)
+                        tok[i * (g + 1) + j] = rng.choice(V, p=row / row.sum())
+                q = torch.as_tensor(q_h, device="cuda")
+                tokens = torch.as_tensor(tok, device="cuda")
+                path = torch.zeros(B, 64, dtype=torch.int32, device="cuda")
+                ua = torch.rand(3 + n_it, T, device="cuda", generator=gen)
+            else:
+                rows_q = np.concatenate([np.arange(i * (g + 1), i * (g + 1) + g) for i in range(B)])
+                q_h = (0.7 * p_h[rows_q] + 0.3 * rand_rows(B * g)).astype(np.float32)
+                drafts = np.array([rng.choice(V, p=r / r.sum()) for r in q_h.astype(np.float64)], np.int32)
+                q = torch.as_tensor(q_h, device="cuda")
+                draft = torch.as_tensor(drafts, device="cuda")
+                ua = torch.rand(3 + n_it, max(1, B * g), device="cuda", generator=gen)
+            us = torch.rand(3 + n_it, B, device="cuda", generator=gen)
+            acc_all = torch.zeros(3 + n_it, B, dtype=torch.int32, device="cuda")
+            nxt = torch.zeros(B, dtype=torch.int32, device="cuda")
+
+            def accept(k):
+                if tree:
+                    assert sv.sv_accept_tree(B, V, sv.SV_ACCEPT_STOCHASTIC, gl, batch.tree_parent, tokens, probs,
+                                             q, ua[k], us[k], kv_all[k], acc_all[k], nxt, path, batch.err, ws,
+                                             nws, stream) == 0
+                    assert sv.sv_tree_commit_kv(B, sh.n_kv, sh.hd, cap, kv_all[k], acc_all[k], path,
+                                                batch.kptr, batch.vptr, stream) == 0
+                else:
+                    assert sv.sv_accept_commit(B, V, sv.SV_ACCEPT_STOCHASTIC, gl, batch.gamma, draft, probs, q,
+                                               ua[k], us[k], kv_all[k], acc_all[k], nxt, batch.err, ws, nws,
+                                               stream) == 0
+
+            def step(k):
+                assert sv.sv_verify_layer(Ld, bss[k], x, y, 0, ws, nws, stream) == 0
+                assert sv.sv_verify_layer(Lh, bss[k], y, probs, 0, ws, nws, stream) == 0
+                accept(k)
+
+            kv_all.copy_(batch.kv_len.expand_as(kv_all))
+            for k in range(3):
+                step(k)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for k in range(n_it):
+                step(3 + k)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / n_it
+            assert batch.err.item() == 0
+            emitted = float((acc_all[3:].float() + 1).mean().item())
+            # acceptance (and commit) alone, on the same inputs
+            kv_all.copy_(batch.kv_len.expand_as(kv_all))
+            torch.cuda.synchronize()
+            e0.record()
+            for k in range(n_it):
+                accept(3 + k)
+            e1.record()
+            torch.cuda.synchronize()
+            acc_ms = e0.elapsed_time(e1) / n_it
+            row = {"B": B, "variant": name, "rows_per_seq": g + 1, "T": T, "ms": round(ms, 5),
+                   "accept_ms": round(acc_ms, 5), "tokens_per_seq_step": round(emitted, 3),
+                   "verify_tok_s": round(T / ms * 1e3, 1), "emitted_tok_s": round(B * emitted / ms * 1e3, 1)}
+            rows.append(row)
+            log(json.dumps(row))
+            del probs, q, ws, x, y
+        del kcs, vcs
+        torch.cuda.empty_cache()
+    out = {"tree": True, "shape": args.tree_shape_name, "ctx": ctx, "depth": depth, "parents": tpar,
+           "rows": rows}
+    if args.tree_out:
+        with open(args.tree_out, "w") as fh:
+            json.dump(out, fh, indent=1)
+    print(json.dumps({"tree": True, "points": len(rows)}), flush=True)
+
+
 def swarm(args):
     """The static-batching page's eight-agent swarm (output lengths 40..900
     tokens, plain decoding: one token per live sequence per step) through the
@@ -770,6 +936,13 @@ def main():
                          "shrinking and continuous batching policies of the library's scheduler")
     ap.add_argument("--swarm-waves", type=int, default=16)
     ap.add_argument("--swarm-ctx", type=int, default=1024)
+    ap.add_argument("--tree", action="store_true",
+                    help="token-tree verification against linear drafts (step time, emitted tokens)")
+    ap.add_argument("--tree-shape-name", default="27b", choices=("9b", "27b"))
+    ap.add_argument("--tree-ctx", type=int, default=2048)
+    ap.add_argument("--tree-depth", type=int, default=8)
+    ap.add_argument("--tree-b", default="1,2,4,8,16,32")
+    ap.add_argument("--tree-out", default="")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before the steps, copy a buffer of this many MiB device to device three "
                          "times (the known-size reference for HBM traffic counters)")
@@ -783,6 +956,9 @@ def main():
         return
     if args.swarm:
         swarm(args)
+        return
+    if args.tree:
+        tree_bench(args)
         return
 
     import torch
