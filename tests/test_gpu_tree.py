@@ -25,6 +25,19 @@ def random_tree(rng, n, width=3):
     return par
 
 
+def spine_tree(depth, width=2):
+    """A chain of `depth` drafts with width - 1 extra candidates beside it at
+    each of the first depth - 1 levels (the chain goes on through the first)."""
+    par, chain = [-1], 0
+    for lvl in range(depth):
+        first = len(par)
+        par.append(chain)
+        if lvl < depth - 1:
+            par += [chain] * (width - 1)
+        chain = first
+    return par
+
+
 def _tree_layer(shape, wtype, parents, ctx, seed, packed=False):
     gamma = [len(p) - 1 for p in parents]
     wl = custom_workload(shape, wtype, gamma, ctx, seed=seed)
@@ -134,8 +147,10 @@ def _run_tree_accept(parents, tokens, p, q, ua, us, ctx, greedy):
             int(err.item()))
 
 
-def _tree_accept_case(rng, sizes, V, greedy, draft_from_q=True, q_equals_p=False, mix=0.0):
-    parents = [random_tree(rng, n) for n in sizes]
+def _tree_accept_case(rng, sizes, V, greedy, draft_from_q=True, q_equals_p=False, mix=0.0, parents=None):
+    if parents is None:
+        parents = [random_tree(rng, n) for n in sizes]
+    sizes = [len(par) for par in parents]
     T = sum(sizes)
     p = _rows(rng, T, V)
     q = p.copy() if q_equals_p else _rows(rng, T, V, 2.0)
@@ -197,6 +212,27 @@ def test_tree_accept_bit_exact_full_vocab(greedy):
     rng = np.random.default_rng(50 + greedy)
     got = _tree_accept_case(rng, [16, 9], 151936, greedy)
     say(f"tree accept V=151936 greedy={greedy}: accepted {got[0].tolist()} next {got[1].tolist()}")
+
+
+@pytest.mark.parametrize("V", [20003, 151936])
+def test_tree_accept_bit_exact_spines(V):
+    """Spines of two and of four candidates per level over several vocabulary
+    chunks (V = 20003: the scalar path, V = 151936: 16-byte loads).  Walks end
+    on the bonus row (a leaf), on the first residual (one child rejected), on
+    the second (both of two rejected) and at a node of four whose first two
+    are rejected, finished by one workgroup alone; all bit for bit."""
+    rng = np.random.default_rng(61 + V % 2)
+    assert spine_tree(8) == [-1, 0, 0, 1, 1, 3, 3, 5, 5, 7, 7, 9, 9, 11, 11, 13]
+    ends = {}
+    for mix in (0.0, 0.5, 0.9):
+        parents = [spine_tree(8), spine_tree(4, 4), spine_tree(3), [-1, 0], [-1]]
+        got = _tree_accept_case(rng, None, V, False, mix=mix, parents=parents)
+        for i, par in enumerate(parents):
+            last = int(got[3][i, got[0][i]])
+            kids = min(3, sum(1 for x in par[1:] if x == last))
+            ends[kids] = ends.get(kids, 0) + 1
+    say(f"tree accept spines V={V}: walks ending at nodes of 0/1/2/3+ children: {ends}")
+    assert ends.get(0, 0) > 0 and ends.get(2, 0) > 0
 
 
 def test_tree_commit_moves_accepted_rows():

@@ -991,7 +991,7 @@ sv_status plan_tree(int32_t B, int32_t V, const int32_t *gamma_host, long long &
     if (gamma_host[i] + 1 > kMaxTreeNodes) return SV_ERR_UNSUPPORTED;
     T += gamma_host[i] + 1;
   }
-  bytes = align_up((size_t)B * V * sizeof(unsigned long long));
+  bytes = tree_workspace_bytes(B, V, T);
   return SV_OK;
 }
 }  // namespace
@@ -1033,7 +1033,7 @@ extern "C" sv_status sv_accept_tree(int32_t B, int32_t V, int32_t mode, const in
   a.next_token = next_token;
   a.path = path;
   a.err = err_flag;
-  a.rbuf = static_cast<unsigned long long *>(workspace);
+  a.ws = static_cast<unsigned char *>(workspace);
   int qs = 0;
   for (int i = 0; i < B; ++i) {
     a.q_start[i] = qs;

@@ -330,9 +330,12 @@ struct TreeAcceptParams {
   int *kv_len, *accepted, *next_token;
   int *path;              // [B][kMaxTreeNodes] accepted node at each depth, -1 past the end
   int *err;
-  unsigned long long *rbuf;  // [B][V] integer weights of the current residual
+  unsigned char *ws;      // workspace, tree_workspace_bytes(B, V, T) bytes
   int q_start[kTreeMaxB + 1];
 };
+
+// Workspace of one tree acceptance call over B sequences, T stacked nodes.
+size_t tree_workspace_bytes(int B, int V, long long T);
 
 struct TreeCommitParams {
   int B, hkv, hd, kv_cap;
