@@ -16,16 +16,22 @@
 //
 // The walk itself touches a few entries per node; what costs is the
 // vocabulary-long sums behind a rejection and the draw.  Those run on grids
-// of vocabulary chunks (8192 entries, one workgroup each), five launches:
+// of vocabulary chunks (8192 entries, one workgroup each).  Stochastic mode,
+// six launches:
+//   walk 1 (sequences): one workgroup per tree gathers every node's own test
+//          inputs once and walks down in LDS.  It ends on a draw from p_v (a
+//          leaf) or from the first residual (the only child rejected), or
+//          stops where a rejected first child has a sibling: that test needs
+//          sum Q and the first residual's sum;
 //   sums   (chunks x nodes): per chunk, sum w(p), sum w(p - q), sum w(q) of
-//          every node with two or more children (greedy: the chunk argmax of
-//          every node);
-//   walk   (sequences): one workgroup per tree walks down with gathers and
-//          the chunk totals; it ends on a draw from p_v (leaf), from the first
-//          residual (the only or both first children rejected decide how far)
-//          or from the second, and records which.  A third sibling's test
-//          needs the second residual's sum: that node is finished by the
-//          workgroup alone, with the residual in its own [V] buffer;
+//          the nodes walk 1 flagged: the stopping node and those of two or
+//          more children below its second child;
+//   walk 2 (sequences): the stopped walks go on from the chunk totals and end
+//          on a draw from p_v, the first or the second residual (both of two
+//          children rejected).  A node that needs sums it does not have, or a
+//          third sibling's test (it needs the second residual's sum), is
+//          finished by the workgroup alone, with the residual in its own [V]
+//          buffer;
 //   resid2 (chunks x sequences): the 128-bit chunk sums of the unshifted
 //          second residual, whose total fixes the shift;
 //   draw   (chunks x sequences): per chunk, the sum of the draw's weights, of
@@ -33,6 +39,7 @@
 //          row fallback);
 //   pick   (sequences): the chunk holding the target from the chunk sums, then
 //          an exact scan of that chunk alone.
+// Greedy mode: the chunk argmaxes of every node, then one walk.
 // Every result passes between launches through the workspace; no counters,
 // nothing needs clearing.
 //
@@ -103,12 +110,12 @@ struct NodePart {
   int mi;
 };
 // How a sequence's walk ended.
-enum DrawMode : int { kDone = 0, kDrawP = 1, kDrawR1 = 2, kDrawR2 = 3 };
+enum DrawMode : int { kDone = 0, kDrawP = 1, kDrawR1 = 2, kDrawR2 = 3, kNeedSums = 4 };
 struct DrawDesc {
-  int row;   // stacked row of the node the token is drawn at
-  int mode;  // DrawMode
-  int p1;    // first residual replaced by w(p) (its sum was 0)
-  int pad;
+  int row;    // stacked row of the node the token is drawn at (kNeedSums: the walk's node)
+  int mode;   // DrawMode
+  int p1;     // first residual replaced by w(p) (its sum was 0)
+  int depth;  // the walk's depth at that node
   u64 s1, sq;  // first residual's sum (after that replacement) and sum Q
 };
 // Chunk results of a draw row: sum of the draw weights, of w(p), argmax of p.
@@ -122,6 +129,7 @@ struct DrawPart {
 struct TreeWs {
   u64 *rbuf;       // [B][V] residual of a node finished by its walk workgroup alone
   NodePart *np;    // [T][nchunk]
+  int *need;       // [T] node whose chunk sums the second walk pass may use
   DrawDesc *desc;  // [B]
   U128 *p2;        // [B][nchunk] unshifted second-residual chunk sums
   DrawPart *p3;    // [B][nchunk]
@@ -134,12 +142,14 @@ inline size_t ws_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign;
 inline int chunks_of(int V) { return (V + kChunk - 1) / kChunk; }
 
 // Region offsets of the workspace (each 256-byte aligned); returns the total.
-size_t carve_offsets(int B, int V, long long T, size_t off[5]) {
+constexpr int kRegions = 6;
+size_t carve_offsets(int B, int V, long long T, size_t off[kRegions]) {
   const size_t nc = static_cast<size_t>(chunks_of(V));
-  const size_t sz[5] = {(size_t)B * V * sizeof(u64), (size_t)T * nc * sizeof(NodePart), (size_t)B * sizeof(DrawDesc),
-                        (size_t)B * nc * sizeof(U128), (size_t)B * nc * sizeof(DrawPart)};
+  const size_t sz[kRegions] = {(size_t)B * V * sizeof(u64),      (size_t)T * nc * sizeof(NodePart),
+                               (size_t)T * sizeof(int),          (size_t)B * sizeof(DrawDesc),
+                               (size_t)B * nc * sizeof(U128),    (size_t)B * nc * sizeof(DrawPart)};
   size_t o = 0;
-  for (int k = 0; k < 5; ++k) {
+  for (int k = 0; k < kRegions; ++k) {
     off[k] = o;
     o = ws_up(o + sz[k]);
   }
@@ -147,14 +157,15 @@ size_t carve_offsets(int B, int V, long long T, size_t off[5]) {
 }
 
 TreeWs carve(unsigned char *base, int B, int V, long long T) {
-  size_t off[5];
+  size_t off[kRegions];
   carve_offsets(B, V, T, off);
   TreeWs w{};
   w.rbuf = reinterpret_cast<u64 *>(base + off[0]);
   w.np = reinterpret_cast<NodePart *>(base + off[1]);
-  w.desc = reinterpret_cast<DrawDesc *>(base + off[2]);
-  w.p2 = reinterpret_cast<U128 *>(base + off[3]);
-  w.p3 = reinterpret_cast<DrawPart *>(base + off[4]);
+  w.need = reinterpret_cast<int *>(base + off[2]);
+  w.desc = reinterpret_cast<DrawDesc *>(base + off[3]);
+  w.p2 = reinterpret_cast<U128 *>(base + off[4]);
+  w.p3 = reinterpret_cast<DrawPart *>(base + off[5]);
   w.nchunk = chunks_of(V);
   return w;
 }
@@ -284,7 +295,7 @@ __device__ __forceinline__ int seq_of(const TreeAcceptParams &p, int r) {
   return lo;
 }
 
-// ---- sums: chunk results of every node that may need them --------------------
+// ---- sums: chunk results of the nodes the walk needs them for -----------------
 
 __global__ __launch_bounds__(kThreads) void tree_sums_kernel(TreeAcceptParams p, TreeWs w) {
   __shared__ RedShared sh;
@@ -297,10 +308,7 @@ __global__ __launch_bounds__(kThreads) void tree_sums_kernel(TreeAcceptParams p,
   if (p.greedy) {
     chunk_for(pr, nullptr, x0, x1, w.vec != 0, [&](int x, float pe, float) { amax(mv, mi, pe, x); });
   } else {
-    // only a node with two or more children can need these sums in the walk
-    const int i = seq_of(p, r), qs = p.q_start[i], n = p.q_start[i + 1] - qs, j = r - qs;
-    const int kid = (tid > j && tid < n && p.parent[qs + tid] == j) ? 1 : 0;
-    if (__syncthreads_count(kid) < 2) return;
+    if (!w.need[r]) return;  // flagged by the first walk pass
     chunk_for(pr, p.q + (size_t)r * V, x0, x1, w.vec != 0, [&](int, float pe, float qe) {
       s0 += weight_of(pe);
       s1 += weight_of(pe - qe);
@@ -319,6 +327,10 @@ struct WalkShared {
   int path[kMaxTreeNodes];
   int first_kid[kMaxTreeNodes];
   int next_sib[kMaxTreeNodes];
+  int nkids[kMaxTreeNodes];
+  u64 anc[kMaxTreeNodes];  // bit m: node m is the node or one of its ancestors
+  // each node's own test inputs: its uniform, and p and q of its parent's row at its token
+  float ua[kMaxTreeNodes], pd[kMaxTreeNodes], qd[kMaxTreeNodes];
   int bad;
   int step, arg;
   int ok, result;
@@ -496,13 +508,27 @@ __device__ int walk_node_alone(const TreeAcceptParams &p, WalkShared &sh, int i,
   return -1;
 }
 
-enum Step : int { kMove = 0, kEnd = 1, kDraw = 2, kAlone = 3 };
+enum Step : int { kMove = 0, kEnd = 1, kDraw = 2, kAlone = 3, kNeed = 4 };
 
-__global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeAcceptParams p, TreeWs w) {
+// The walk of one tree, one workgroup.  pass 0: greedy (chunk argmaxes of
+// every node ready).  pass 1: stochastic, no chunk sums yet; a node whose
+// first child is rejected and which has a second stops the walk, flagging
+// that node and the nodes with two or more children below the second child
+// (the only ones the walk can go on to without a third test).  pass 2: the
+// walks that stopped go on with those nodes' sums; any other node that needs
+// sums is finished by the workgroup alone.
+__global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeAcceptParams p, TreeWs w, int pass) {
   __shared__ WalkShared sh;
   const int i = blockIdx.x, tid = threadIdx.x;
   const int qs = p.q_start[i], n = p.q_start[i + 1] - qs;
   const int V = p.V, nc = w.nchunk;
+  int v = 0, depth = 0;
+  if (pass == 2) {
+    const DrawDesc dd = w.desc[i];
+    if (dd.mode != kNeedSums) return;
+    v = dd.row - qs;
+    depth = dd.depth;
+  }
   if (tid == 0) sh.bad = 0;
   __syncthreads();
   for (int j = tid; j < n; j += kThreads) {
@@ -513,7 +539,7 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeAcceptParams p,
     if (j > 0 && (tj < 0 || tj >= V)) atomicOr(&sh.bad, SV_DEV_ERR_BAD_TOKEN);
   }
   __syncthreads();
-  if (sh.bad) {
+  if (sh.bad) {  // (a second pass never sees a bad tree: the first left it done)
     if (tid == 0) {
       set_err(p.err, sh.bad);
       p.accepted[i] = -1;
@@ -521,15 +547,18 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeAcceptParams p,
       w.desc[i] = DrawDesc{qs, kDone, 0, 0, 0ull, 0ull};
       for (int k = 0; k < kMaxTreeNodes; ++k) p.path[(size_t)i * kMaxTreeNodes + k] = -1;
     }
+    if (pass == 1)
+      for (int j = tid; j < n; j += kThreads) w.need[qs + j] = 0;
     return;
   }
-  // children in index order: first child and next sibling of every node
+  // children in index order, child counts, ancestor sets, and every node's
+  // own test inputs (gathered once: the walk then reads only LDS)
   for (int j = tid; j < n; j += kThreads) {
-    int fk = -1, ns = -1;
-    for (int c = j + 1; c < n; ++c)
+    int fk = -1, ns = -1, nk = 0;
+    for (int c = n - 1; c > j; --c)
       if (sh.par[c] == j) {
         fk = c;
-        break;
+        ++nk;
       }
     if (j > 0)
       for (int c = j + 1; c < n; ++c)
@@ -537,18 +566,31 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeAcceptParams p,
           ns = c;
           break;
         }
+    u64 m = 1ull;
+    for (int x = j; x > 0; x = sh.par[x]) m |= 1ull << x;
     sh.first_kid[j] = fk;
     sh.next_sib[j] = ns;
+    sh.nkids[j] = nk;
+    sh.anc[j] = m;
+    if (!p.greedy && j > 0) {
+      const size_t at = (size_t)(qs + sh.par[j]) * V + sh.tok[j];
+      sh.ua[j] = p.u_acc[qs + j];
+      sh.pd[j] = p.p[at];
+      sh.qd[j] = p.q[at];
+    }
   }
-  if (tid == 0) sh.path[0] = 0;
+  if (pass == 2) {
+    for (int k = tid; k <= depth; k += kThreads) sh.path[k] = p.path[(size_t)i * kMaxTreeNodes + k];
+  } else if (tid == 0) {
+    sh.path[0] = 0;
+  }
   __syncthreads();
 
-  int v = 0, depth = 0, y = -1;
+  int y = -1;
   bool drawn_here = false;
   for (;;) {
-    // one step of the walk, decided by thread 0 from gathers and chunk totals
+    // one step of the walk, decided by thread 0 from LDS and chunk totals
     if (tid == 0) {
-      const float *pv = p.p + (size_t)(qs + v) * V;
       const NodePart *np = w.np + (size_t)(qs + v) * nc;
       int step = kEnd, arg = 0;
       if (p.greedy) {
@@ -561,17 +603,22 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeAcceptParams p,
         step = c >= 0 ? kMove : kEnd;
         arg = c >= 0 ? c : mi;
       } else {
-        const float *qv = p.q + (size_t)(qs + v) * V;
-        DrawDesc dd{qs + v, kDrawP, 0, 0, 0ull, 0ull};
+        DrawDesc dd{qs + v, kDrawP, 0, depth, 0ull, 0ull};
         const int c1 = sh.first_kid[v];
         step = kDraw;  // a leaf: the bonus token from p_v
         if (c1 >= 0) {
-          const int d1 = sh.tok[c1];
-          if (p.u_acc[qs + c1] * qv[d1] < pv[d1]) {
+          const int c2 = sh.next_sib[c1];
+          if (sh.ua[c1] * sh.qd[c1] < sh.pd[c1]) {
             step = kMove;
             arg = c1;
-          } else if (sh.next_sib[c1] < 0) {
+          } else if (c2 < 0) {
             dd.mode = kDrawR1;  // the only child rejected
+          } else if (pass == 1) {
+            step = kNeed;
+            arg = c2;
+            dd.mode = kNeedSums;
+          } else if (!w.need[qs + v]) {
+            step = kAlone;
           } else {
             u64 S0 = 0, S1 = 0, SQ = 0;
             for (int cc = 0; cc < nc; ++cc) {
@@ -581,20 +628,19 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeAcceptParams p,
             }
             const int p1 = S1 == 0;  // empty first residual: w(p) instead
             if (p1) S1 = S0;
-            const int c2 = sh.next_sib[c1], d2 = sh.tok[c2];
-            const u64 U = static_cast<u64>(static_cast<double>(p.u_acc[qs + c2]) * 16777216.0);
-            const u64 R1 = p1 ? weight_of(pv[d2]) : weight_of(pv[d2] - qv[d2]);
-            if (less128(mul64(U * weight_of(qv[d2]), S1), shl128(mul64(R1, SQ), 24))) {
+            const u64 U = static_cast<u64>(static_cast<double>(sh.ua[c2]) * 16777216.0);
+            const u64 R1 = p1 ? weight_of(sh.pd[c2]) : weight_of(sh.pd[c2] - sh.qd[c2]);
+            if (less128(mul64(U * weight_of(sh.qd[c2]), S1), shl128(mul64(R1, SQ), 24))) {
               step = kMove;
               arg = c2;
             } else if (sh.next_sib[c2] < 0) {
-              dd = DrawDesc{qs + v, kDrawR2, p1, 0, S1, SQ};  // both children rejected
+              dd = DrawDesc{qs + v, kDrawR2, p1, depth, S1, SQ};  // both children rejected
             } else {
               step = kAlone;  // a third sibling's test needs the second residual's sum
             }
           }
         }
-        if (step == kDraw) w.desc[i] = dd;
+        if (step == kDraw || step == kNeed) w.desc[i] = dd;
       }
       sh.step = step;
       sh.arg = arg;
@@ -613,6 +659,14 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeAcceptParams p,
       drawn_here = true;
       break;
     }
+    if (step == kNeed) {
+      // sums for v and for the nodes of two or more children below its
+      // second child; the path so far, for the second pass
+      for (int j = tid; j < n; j += kThreads)
+        w.need[qs + j] = (j == v || (((sh.anc[j] >> arg) & 1ull) && sh.nkids[j] >= 2)) ? 1 : 0;
+      for (int k = tid; k <= depth; k += kThreads) p.path[(size_t)i * kMaxTreeNodes + k] = sh.path[k];
+      return;
+    }
     if (step == kDraw) break;
     const int c = walk_node_alone(p, sh, i, qs, n, v, w.rbuf + (size_t)i * V, &y);
     if (c >= 0) {
@@ -624,13 +678,15 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeAcceptParams p,
     drawn_here = true;
     break;
   }
+  if (pass == 1)
+    for (int j = tid; j < n; j += kThreads) w.need[qs + j] = 0;
   __syncthreads();
   if (tid == 0) {
     p.accepted[i] = depth;
     p.kv_len[i] += depth + 1;
     if (drawn_here) {
       p.next_token[i] = y;
-      w.desc[i] = DrawDesc{qs + v, kDone, 0, 0, 0ull, 0ull};
+      w.desc[i] = DrawDesc{qs + v, kDone, 0, depth, 0ull, 0ull};
     }
   }
   for (int k = tid; k < kMaxTreeNodes; k += kThreads)
@@ -829,7 +885,7 @@ __global__ __launch_bounds__(kThreads) void tree_commit_kernel(TreeCommitParams 
 }  // namespace
 
 size_t tree_workspace_bytes(int B, int V, long long T) {
-  size_t off[5];
+  size_t off[kRegions];
   return carve_offsets(B, V, T, off);
 }
 
@@ -840,9 +896,14 @@ hipError_t launch_tree_accept(const TreeAcceptParams &p, hipStream_t s) {
   w.vec = (p.V % 4) == 0 && (al % 16) == 0;
   const dim3 blk(kThreads);
   trace_before(SV_K_ACCEPT, s);
-  hipLaunchKernelGGL(tree_sums_kernel, dim3(w.nchunk, static_cast<unsigned>(T)), blk, 0, s, p, w);
-  hipLaunchKernelGGL(tree_walk_kernel, dim3(p.B), blk, 0, s, p, w);
-  if (!p.greedy) {
+  const dim3 all_rows(w.nchunk, static_cast<unsigned>(T));
+  if (p.greedy) {
+    hipLaunchKernelGGL(tree_sums_kernel, all_rows, blk, 0, s, p, w);
+    hipLaunchKernelGGL(tree_walk_kernel, dim3(p.B), blk, 0, s, p, w, 0);
+  } else {
+    hipLaunchKernelGGL(tree_walk_kernel, dim3(p.B), blk, 0, s, p, w, 1);
+    hipLaunchKernelGGL(tree_sums_kernel, all_rows, blk, 0, s, p, w);
+    hipLaunchKernelGGL(tree_walk_kernel, dim3(p.B), blk, 0, s, p, w, 2);
     hipLaunchKernelGGL(tree_resid2_kernel, dim3(w.nchunk, p.B), blk, 0, s, p, w);
     hipLaunchKernelGGL(tree_draw_sums_kernel, dim3(w.nchunk, p.B), blk, 0, s, p, w);
     hipLaunchKernelGGL(tree_pick_kernel, dim3(p.B), blk, 0, s, p, w);
