@@ -258,7 +258,7 @@ def sweep(args):
             gl = [g] * B
             n_it = 10 if T <= 512 else 4
             # each step reads and commits its own copy of the starting lengths
-            kv_all = batch.kv_len.clone().repeat(3 + n_it, 1).contiguous()
+            kv_all = batch.kv_len.clone().repeat(3 + n_it + n_stat, 1).contiguous()
             bss = []
             for k in range(3 + n_it):
                 b_ = batch.struct()
@@ -604,8 +604,9 @@ def tree_bench(args):
     moves, or linear acceptance and commit) and the tokens a step emits per
     sequence, on synthetic data: device-generated N(0,1) hidden states and
     KV entries, draft rows q = 0.7 p + 0.3 r (p the pass's own target row,
-    r a random softmax row), each draft drawn from its parent's q row, fresh
-    uniforms every step."""
+    r a random softmax row), each draft drawn from its parent's q row; every
+    acceptance call gets fresh drafts and uniforms, and tokens per step are
+    averaged over the timed calls and --tree-stat-calls untimed ones."""
     import numpy as np
     import torch
 
@@ -628,8 +629,20 @@ def tree_bench(args):
     gen = torch.Generator(device="cuda").manual_seed(seed)
     tpar = tree_shape(depth)
     variants = [("tree", len(tpar) - 1), ("chain-depth", depth), ("chain-rows", len(tpar) - 1)]
-    n_it, rows = 10, []
+    n_it, n_stat, rows = 10, args.tree_stat_calls, []
     log(f"tree: {args.tree_shape_name} bf16 ctx {ctx}, tree of {len(tpar)} nodes {depth} deep, B {blist}")
+
+    def draw_rows(qrows, src, out, skip=None):
+        """out[k, t] ~ qrows[src[t]] for every set k (independent draws by the
+        inverse CDF of each row), t with skip[t] left alone."""
+        for r in np.unique(src):
+            ts = [t for t in np.nonzero(src == r)[0] if skip is None or not skip[t]]
+            if not ts:
+                continue
+            c = np.cumsum(qrows[r].astype(np.float64))
+            c /= c[-1]
+            u = rng.random((out.shape[0], len(ts)))
+            out[:, ts] = np.minimum(np.searchsorted(c, u, side="right"), V - 1)
 
     def rand_rows(n):
         z = rng.standard_normal((n, V)).astype(np.float32) * 3.0
@@ -660,7 +673,7 @@ def tree_bench(args):
             x = torch.randn(T, sh.d, device="cuda", generator=gen).to(torch.bfloat16)
             y = torch.empty_like(x)
             probs = torch.empty(T, V, dtype=torch.float32, device="cuda")
-            kv_all = batch.kv_len.clone().repeat(3 + n_it, 1).contiguous()
+            kv_all = batch.kv_len.clone().repeat(3 + n_it + n_stat, 1).contiguous()
             bss = []
             for k in range(3 + n_it):
                 b_ = batch.struct()
@@ -672,37 +685,38 @@ def tree_bench(args):
             torch.cuda.synchronize()
             assert batch.err.item() == 0
             p_h = probs.cpu().numpy()
+            # a fresh set of drafts for every call: warm-up, timed, then statistics only
+            n_sets = 3 + n_it + n_stat
             if tree:
                 q_h = (0.7 * p_h + 0.3 * rand_rows(T)).astype(np.float32)
-                tok = np.zeros(T, np.int32)
-                for i in range(B):
-                    for j in range(1, g + 1):
-                        row = q_h[i * (g + 1) + tpar[j]].astype(np.float64)
-                        tok[i * (g + 1) + j] = rng.choice(V, p=row / row.sum())
+                src = np.array([i * (g + 1) + (tpar[j] if j else 0) for i in range(B) for j in range(g + 1)])
+                tok = np.zeros((n_sets, T), np.int32)
+                draw_rows(q_h, src, tok, skip=np.arange(T) % (g + 1) == 0)
                 q = torch.as_tensor(q_h, device="cuda")
                 tokens = torch.as_tensor(tok, device="cuda")
                 path = torch.zeros(B, 64, dtype=torch.int32, device="cuda")
-                ua = torch.rand(3 + n_it, T, device="cuda", generator=gen)
+                ua = torch.rand(n_sets, T, device="cuda", generator=gen)
             else:
                 rows_q = np.concatenate([np.arange(i * (g + 1), i * (g + 1) + g) for i in range(B)])
                 q_h = (0.7 * p_h[rows_q] + 0.3 * rand_rows(B * g)).astype(np.float32)
-                drafts = np.array([rng.choice(V, p=r / r.sum()) for r in q_h.astype(np.float64)], np.int32)
+                drafts = np.zeros((n_sets, B * g), np.int32)
+                draw_rows(q_h, np.arange(B * g), drafts)
                 q = torch.as_tensor(q_h, device="cuda")
                 draft = torch.as_tensor(drafts, device="cuda")
-                ua = torch.rand(3 + n_it, max(1, B * g), device="cuda", generator=gen)
-            us = torch.rand(3 + n_it, B, device="cuda", generator=gen)
-            acc_all = torch.zeros(3 + n_it, B, dtype=torch.int32, device="cuda")
+                ua = torch.rand(n_sets, max(1, B * g), device="cuda", generator=gen)
+            us = torch.rand(n_sets, B, device="cuda", generator=gen)
+            acc_all = torch.zeros(n_sets, B, dtype=torch.int32, device="cuda")
             nxt = torch.zeros(B, dtype=torch.int32, device="cuda")
 
             def accept(k):
                 if tree:
-                    assert sv.sv_accept_tree(B, V, sv.SV_ACCEPT_STOCHASTIC, gl, batch.tree_parent, tokens, probs,
+                    assert sv.sv_accept_tree(B, V, sv.SV_ACCEPT_STOCHASTIC, gl, batch.tree_parent, tokens[k], probs,
                                              q, ua[k], us[k], kv_all[k], acc_all[k], nxt, path, batch.err, ws,
                                              nws, stream) == 0
                     assert sv.sv_tree_commit_kv(B, sh.n_kv, sh.hd, cap, kv_all[k], acc_all[k], path,
                                                 batch.kptr, batch.vptr, stream) == 0
                 else:
-                    assert sv.sv_accept_commit(B, V, sv.SV_ACCEPT_STOCHASTIC, gl, batch.gamma, draft, probs, q,
+                    assert sv.sv_accept_commit(B, V, sv.SV_ACCEPT_STOCHASTIC, gl, batch.gamma, draft[k], probs, q,
                                                ua[k], us[k], kv_all[k], acc_all[k], nxt, batch.err, ws, nws,
                                                stream) == 0
 
@@ -722,6 +736,12 @@ def tree_bench(args):
             e1.record()
             torch.cuda.synchronize()
             ms = e0.elapsed_time(e1) / n_it
+            assert batch.err.item() == 0
+            # tokens per sequence-step over the timed calls and n_stat more, each
+            # with its own drafts and uniforms
+            for k in range(3 + n_it, n_sets):
+                accept(k)
+            torch.cuda.synchronize()
             assert batch.err.item() == 0
             emitted = float((acc_all[3:].float() + 1).mean().item())
             # acceptance (and commit) alone, on the same inputs
@@ -941,6 +961,8 @@ def main():
     ap.add_argument("--tree-shape-name", default="27b", choices=("9b", "27b"))
     ap.add_argument("--tree-ctx", type=int, default=2048)
     ap.add_argument("--tree-depth", type=int, default=8)
+    ap.add_argument("--tree-stat-calls", type=int, default=64,
+                    help="untimed acceptance calls (fresh drafts each) added to the tokens-per-step statistic")
     ap.add_argument("--tree-b", default="1,2,4,8,16,32")
     ap.add_argument("--tree-out", default="")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
