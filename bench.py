@@ -258,7 +258,7 @@ def sweep(args):
             gl = [g] * B
             n_it = 10 if T <= 512 else 4
             # each step reads and commits its own copy of the starting lengths
-            kv_all = batch.kv_len.clone().repeat(3 + n_it + n_stat, 1).contiguous()
+            kv_all = batch.kv_len.clone().repeat(3 + n_it, 1).contiguous()
             bss = []
             for k in range(3 + n_it):
                 b_ = batch.struct()
