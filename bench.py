@@ -600,8 +600,8 @@ def tree_bench(args):
     """Token-tree verification ([slack], "What the budget says to build": a
     small tree, about 8 to 16 deep) against linear drafts at the same depth
     and at the same number of verified rows: step time (decoder layer with
-    ancestor masks, head probabilities, tree acceptance and the commit's row
-    moves, or linear acceptance and commit) and the tokens a step emits per
+    ancestor masks, head logits and row statistics, tree acceptance from them
+    and the commit's row moves, or linear acceptance and commit) and the tokens a step emits per
     sequence, on synthetic data: device-generated N(0,1) hidden states and
     KV entries, draft rows q = 0.7 p + 0.3 r (p the pass's own target row,
     r a random softmax row), each draft drawn from its parent's q row; every
@@ -629,6 +629,7 @@ def tree_bench(args):
     gen = torch.Generator(device="cuda").manual_seed(seed)
     tpar = tree_shape(depth)
     variants = [("tree", len(tpar) - 1), ("chain-depth", depth), ("chain-rows", len(tpar) - 1)]
+    amode = sv.SV_ACCEPT_STOCHASTIC | sv.SV_ACCEPT_FROM_LOGITS
     n_it, n_stat, rows = 10, args.tree_stat_calls, []
     log(f"tree: {args.tree_shape_name} bf16 ctx {ctx}, tree of {len(tpar)} nodes {depth} deep, B {blist}")
 
@@ -665,14 +666,16 @@ def tree_bench(args):
             batch.vptr = torch.tensor([t.data_ptr() for t in vcs], dtype=torch.int64, device="cuda")
             gl = [g] * B
             nd = sv.sv_verify_layer_workspace_bytes(Ld, batch.struct())
-            nh = sv.sv_verify_layer_workspace_bytes(Lh, batch.struct(), 0)
+            nh = max(sv.sv_verify_layer_workspace_bytes(Lh, batch.struct(), f)
+                     for f in (0, sv.SV_HEAD_LOGITS_STATS))
             na = (sv.sv_accept_tree_workspace_bytes(B, V, gl) if tree
-                  else sv.sv_accept_commit_workspace_bytes(B, V, sv.SV_ACCEPT_STOCHASTIC, gl))
+                  else sv.sv_accept_commit_workspace_bytes(B, V, amode, gl))
             ws = tg.workspace(max(nd, nh, na))
             nws = ws.numel()
             x = torch.randn(T, sh.d, device="cuda", generator=gen).to(torch.bfloat16)
             y = torch.empty_like(x)
-            probs = torch.empty(T, V, dtype=torch.float32, device="cuda")
+            # the head's logits and row statistics (acceptance forms the probabilities)
+            logits = torch.empty(T * (V + 2), dtype=torch.float32, device="cuda")
             kv_all = batch.kv_len.clone().repeat(3 + n_it + n_stat, 1).contiguous()
             bss = []
             for k in range(3 + n_it):
@@ -680,11 +683,13 @@ def tree_bench(args):
                 b_.kv_len = kv_all[k].data_ptr()
                 bss.append(b_)
             # the pass's target rows, then drafts from q rows close to them
+            probs = torch.empty(T, V, dtype=torch.float32, device="cuda")
             assert sv.sv_verify_layer(Ld, bss[0], x, y, 0, ws, nws, stream) == 0
             assert sv.sv_verify_layer(Lh, bss[0], y, probs, 0, ws, nws, stream) == 0
             torch.cuda.synchronize()
             assert batch.err.item() == 0
             p_h = probs.cpu().numpy()
+            del probs
             # a fresh set of drafts for every call: warm-up, timed, then statistics only
             n_sets = 3 + n_it + n_stat
             if tree:
@@ -710,19 +715,19 @@ def tree_bench(args):
 
             def accept(k):
                 if tree:
-                    assert sv.sv_accept_tree(B, V, sv.SV_ACCEPT_STOCHASTIC, gl, batch.tree_parent, tokens[k], probs,
+                    assert sv.sv_accept_tree(B, V, amode, gl, batch.tree_parent, tokens[k], logits,
                                              q, ua[k], us[k], kv_all[k], acc_all[k], nxt, path, batch.err, ws,
                                              nws, stream) == 0
                     assert sv.sv_tree_commit_kv(B, sh.n_kv, sh.hd, cap, kv_all[k], acc_all[k], path,
                                                 batch.kptr, batch.vptr, stream) == 0
                 else:
-                    assert sv.sv_accept_commit(B, V, sv.SV_ACCEPT_STOCHASTIC, gl, batch.gamma, draft[k], probs, q,
+                    assert sv.sv_accept_commit(B, V, amode, gl, batch.gamma, draft[k], logits, q,
                                                ua[k], us[k], kv_all[k], acc_all[k], nxt, batch.err, ws, nws,
                                                stream) == 0
 
             def step(k):
                 assert sv.sv_verify_layer(Ld, bss[k], x, y, 0, ws, nws, stream) == 0
-                assert sv.sv_verify_layer(Lh, bss[k], y, probs, 0, ws, nws, stream) == 0
+                assert sv.sv_verify_layer(Lh, bss[k], y, logits, sv.SV_HEAD_LOGITS_STATS, ws, nws, stream) == 0
                 accept(k)
 
             kv_all.copy_(batch.kv_len.expand_as(kv_all))
@@ -758,7 +763,7 @@ def tree_bench(args):
                    "verify_tok_s": round(T / ms * 1e3, 1), "emitted_tok_s": round(B * emitted / ms * 1e3, 1)}
             rows.append(row)
             log(json.dumps(row))
-            del probs, q, ws, x, y
+            del logits, q, ws, x, y
         del kcs, vcs
         torch.cuda.empty_cache()
     out = {"tree": True, "shape": args.tree_shape_name, "ctx": ctx, "depth": depth, "parents": tpar,

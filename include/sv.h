@@ -345,7 +345,10 @@ sv_status sv_accept_commit_noalloc(int32_t B, int32_t V, int32_t mode, const int
  * from R (or from trunc(fl32(p_v * 2^32)), the bonus row) by the inverse-CDF
  * rule of sv_accept_commit.  On a chain (one child per node) this is exactly
  * sv_accept_commit.  Greedy mode follows the child whose token is argmax p_v
- * (lowest index on ties); q, u_acc, u_samp may be NULL.
+ * (lowest index on ties); q, u_acc, u_samp may be NULL.  Either mode may be
+ * or'ed with SV_ACCEPT_FROM_LOGITS: p is then the output of an
+ * SV_HEAD_LOGITS_STATS head call over the tree pass, and every probability
+ * is formed from it as sv_accept_commit forms it (bit-identical results).
  * Outputs: accepted[i] = depth of the last accepted node, next_token[i],
  * kv_len[i] += accepted[i] + 1, path (device int32 [B][64]): the accepted node
  * at each depth (path[i][0] = 0), -1 past the end.  A tree with a bad parent

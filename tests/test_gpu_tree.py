@@ -124,8 +124,10 @@ def _rows(rng, n, V, scale=3.0):
     return (e / e.sum(1, keepdims=True)).astype(np.float32)
 
 
-def _run_tree_accept(parents, tokens, p, q, ua, us, ctx, greedy):
-    B, V = len(parents), p.shape[1]
+def _run_tree_accept(parents, tokens, p, q, ua, us, ctx, greedy, from_logits=False):
+    """p: host probabilities [T][V], or (from_logits) the head's device output
+    of logits and row statistics."""
+    B, V = len(parents), q.shape[1]
     gam = [len(x) - 1 for x in parents]
     dev = lambda a, dt: torch.as_tensor(np.ascontiguousarray(a), dtype=dt, device="cuda")  # noqa: E731
     par = dev(np.concatenate([np.asarray(x) for x in parents]), torch.int32)
@@ -138,7 +140,10 @@ def _run_tree_accept(parents, tokens, p, q, ua, us, ctx, greedy):
     n = sv.sv_accept_tree_workspace_bytes(B, V, gam)
     ws = tg.workspace(n)
     mode = sv.SV_ACCEPT_GREEDY if greedy else sv.SV_ACCEPT_STOCHASTIC
-    st = sv.sv_accept_tree(B, V, mode, gam, par, tok, dev(p, torch.float32), dev(q, torch.float32),
+    if from_logits:
+        mode |= sv.SV_ACCEPT_FROM_LOGITS
+    pd = p if from_logits else dev(p, torch.float32)
+    st = sv.sv_accept_tree(B, V, mode, gam, par, tok, pd, dev(q, torch.float32),
                            dev(ua, torch.float32), dev(us, torch.float32), kv, acc, nxt, path, err, ws,
                            n, tg.stream_handle())
     assert st == sv.SV_OK
@@ -233,6 +238,48 @@ def test_tree_accept_bit_exact_spines(V):
             ends[kids] = ends.get(kids, 0) + 1
     say(f"tree accept spines V={V}: walks ending at nodes of 0/1/2/3+ children: {ends}")
     assert ends.get(0, 0) > 0 and ends.get(2, 0) > 0
+
+
+@pytest.mark.parametrize("vocab", [20011, 151936])
+@pytest.mark.parametrize("greedy", [False, True])
+def test_tree_accept_from_logits(vocab, greedy):
+    """Acceptance from the head's logits and row statistics
+    (SV_ACCEPT_FROM_LOGITS, no probability rows materialised) decides exactly
+    as from the head's probabilities, which match the oracle; spines, a
+    random tree and a lone root, over several vocabulary chunks (20011: the
+    scalar path, 151936: 16-byte loads)."""
+    shape = Shape(512, 8, 2, 128, 1024, vocab)
+    rng = np.random.default_rng(70 + greedy)
+    parents = [spine_tree(8), random_tree(rng, 20), spine_tree(4, 4), [-1]]
+    sizes = [len(par) for par in parents]
+    wl = custom_workload(shape, "bf16", [n - 1 for n in sizes], [5] * len(sizes), seed=71)
+    head = GpuHead(wl, packed=True)
+    y = tg.to_dev(hidden_states(wl.T, shape.d, 72))
+    pr = head.run(y)
+    lgs = head.run(y, flags=sv.SV_HEAD_LOGITS_STATS)
+    torch.cuda.synchronize()
+    p = pr.cpu().numpy()
+    q = (0.6 * p + 0.4 * _rows(rng, wl.T, vocab, 2.0)).astype(np.float32)
+    q /= q.sum(1, keepdims=True)
+    tokens = np.zeros(wl.T, np.int64)
+    r0 = 0
+    for par in parents:
+        for j in range(1, len(par)):
+            row = q[r0 + par[j]].astype(np.float64)
+            tokens[r0 + j] = int(rng.choice(vocab, p=row / row.sum()))
+        r0 += len(par)
+    ua = (rng.integers(0, GRID, size=wl.T) / GRID).astype(np.float32)
+    us = (rng.integers(0, GRID, size=len(sizes)) / GRID).astype(np.float32)
+    ctx = [5] * len(sizes)
+    got_p = _run_tree_accept(parents, tokens, p, q, ua, us, ctx, greedy)
+    got_l = _run_tree_accept(parents, tokens, lgs, q, ua, us, ctx, greedy, from_logits=True)
+    want = OT.tree_accept(parents, tokens, p, q, ua, us, ctx, greedy=greedy)
+    for k in range(4):
+        np.testing.assert_array_equal(got_l[k], got_p[k])
+    np.testing.assert_array_equal(got_p[0], want[0])
+    np.testing.assert_array_equal(got_p[1], want[1])
+    assert got_l[4] == 0
+    say(f"tree accept from logits V={vocab} greedy={greedy}: accepted {got_l[0].tolist()} next {got_l[1].tolist()}")
 
 
 def test_tree_commit_moves_accepted_rows():

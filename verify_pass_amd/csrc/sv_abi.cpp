@@ -1009,6 +1009,8 @@ extern "C" sv_status sv_accept_tree(int32_t B, int32_t V, int32_t mode, const in
                                     int32_t *kv_len, int32_t *accepted, int32_t *next_token, int32_t *path,
                                     int32_t *err_flag, void *workspace, size_t workspace_bytes,
                                     void *stream) {
+  const bool from_logits = (mode & SV_ACCEPT_FROM_LOGITS) != 0;
+  mode &= ~SV_ACCEPT_FROM_LOGITS;
   if (mode != SV_ACCEPT_STOCHASTIC && mode != SV_ACCEPT_GREEDY) return SV_ERR_INVALID_ARG;
   long long T = 0;
   size_t bytes = 0;
@@ -1025,6 +1027,7 @@ extern "C" sv_status sv_accept_tree(int32_t B, int32_t V, int32_t mode, const in
   a.parent = parent;
   a.tokens = tokens;
   a.p = p;
+  a.row_ms = from_logits ? p + (size_t)T * V : nullptr;
   a.q = q;
   a.u_acc = u_acc;
   a.u_samp = u_samp;

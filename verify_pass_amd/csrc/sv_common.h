@@ -323,7 +323,8 @@ struct TreeAcceptParams {
   int B, V, greedy;
   const int *parent;      // [T] parent node of each stacked node (roots: any)
   const int *tokens;      // [T] token of each node (roots: ignored)
-  const float *p;         // [T][V] target rows
+  const float *p;         // [T][V] target rows: probabilities, or logits when row_ms is set
+  const float *row_ms;    // [T][2] (max, sum of exp(logit - max)) of each logits row, or null
   const float *q;         // [T][V] draft distribution of each node's children
   const float *u_acc;     // [T] one uniform per node (its own test)
   const float *u_samp;    // [B]

@@ -253,10 +253,25 @@ __device__ u64 block_exscan(u64 v, u64 *total, RedShared &sh) {
   return before + inc - v;
 }
 
+// Probabilities of one row as the rule reads them: the entries themselves,
+// or (logits rows) formed from the logits and the row's (max, sum) exactly as
+// the head's softmax finish forms them.
+struct PX {
+  bool on;
+  float Mk, S;
+  __device__ __forceinline__ float operator()(float v) const { return on ? prob_of_logit(v, Mk, S) : v; }
+};
+__device__ __forceinline__ PX px_of(const TreeAcceptParams &p, int row) {
+  if (!p.row_ms) return PX{false, 0.f, 1.f};
+  return PX{true, p.row_ms[2 * row] * kLog2eF, p.row_ms[2 * row + 1]};
+}
+
 // Calls f(x, p(x), q(x)) on this thread's share of [x0, x1), x0 a chunk start
-// (q(x) = 0 without q).  vec: all of the thread's float4 loads first.
+// (q(x) = 0 without q; p(x) through xf).  vec: all of the thread's float4
+// loads first.
 template <class F>
-__device__ __forceinline__ void chunk_for(const float *pr, const float *qr, int x0, int x1, bool vec, F &&f) {
+__device__ __forceinline__ void chunk_for(const float *pr, const float *qr, int x0, int x1, bool vec, const PX &xf,
+                                          F &&f) {
   if (vec) {
     const float4 *p4 = reinterpret_cast<const float4 *>(pr);
     const float4 *q4 = reinterpret_cast<const float4 *>(qr);
@@ -272,13 +287,13 @@ __device__ __forceinline__ void chunk_for(const float *pr, const float *qr, int 
     for (int k = 0; k < kVec; ++k) {
       const int x = x0 / 4 + threadIdx.x + k * kThreads;
       if (x >= x1 / 4) continue;
-      f(4 * x, pv[k].x, qv[k].x);
-      f(4 * x + 1, pv[k].y, qv[k].y);
-      f(4 * x + 2, pv[k].z, qv[k].z);
-      f(4 * x + 3, pv[k].w, qv[k].w);
+      f(4 * x, xf(pv[k].x), qv[k].x);
+      f(4 * x + 1, xf(pv[k].y), qv[k].y);
+      f(4 * x + 2, xf(pv[k].z), qv[k].z);
+      f(4 * x + 3, xf(pv[k].w), qv[k].w);
     }
   } else {
-    for (int x = x0 + threadIdx.x; x < x1; x += kThreads) f(x, pr[x], qr ? qr[x] : 0.f);
+    for (int x = x0 + threadIdx.x; x < x1; x += kThreads) f(x, xf(pr[x]), qr ? qr[x] : 0.f);
   }
 }
 
@@ -306,10 +321,10 @@ __global__ __launch_bounds__(kThreads) void tree_sums_kernel(TreeAcceptParams p,
   float mv = -INFINITY;
   int mi = 0x7fffffff;
   if (p.greedy) {
-    chunk_for(pr, nullptr, x0, x1, w.vec != 0, [&](int x, float pe, float) { amax(mv, mi, pe, x); });
+    chunk_for(pr, nullptr, x0, x1, w.vec != 0, px_of(p, r), [&](int x, float pe, float) { amax(mv, mi, pe, x); });
   } else {
     if (!w.need[r]) return;  // flagged by the first walk pass
-    chunk_for(pr, p.q + (size_t)r * V, x0, x1, w.vec != 0, [&](int, float pe, float qe) {
+    chunk_for(pr, p.q + (size_t)r * V, x0, x1, w.vec != 0, px_of(p, r), [&](int, float pe, float qe) {
       s0 += weight_of(pe);
       s1 += weight_of(pe - qe);
       sq += weight_of(qe);
@@ -369,11 +384,11 @@ __device__ U128 walk_sum128(U128 v, WalkShared &sh) {
 }
 
 // argmax of row[0, V), lowest index on ties
-__device__ int walk_argmax(const float *row, int V, WalkShared &sh) {
+__device__ int walk_argmax(const float *row, const PX &xf, int V, WalkShared &sh) {
   const int tid = threadIdx.x;
   float bv = -INFINITY;
   int bi = 0x7FFFFFFF;
-  for (int x = tid; x < V; x += kThreads) amax(bv, bi, row[x], x);
+  for (int x = tid; x < V; x += kThreads) amax(bv, bi, xf(row[x]), x);
   sh.amax_v[tid] = bv;
   sh.amax_i[tid] = bi;
   __syncthreads();
@@ -435,6 +450,7 @@ __device__ int walk_node_alone(const TreeAcceptParams &p, WalkShared &sh, int i,
                                u64 *R, int *y) {
   const int tid = threadIdx.x, V = p.V;
   const float *pv = p.p + (size_t)(qs + v) * V;
+  const PX xf = px_of(p, qs + v);
   const float *qv = p.q + (size_t)(qs + v) * V;
   bool have_r = false;  // R holds the residual of the rejected children
   u64 S = 0, SQ = 0;
@@ -442,7 +458,7 @@ __device__ int walk_node_alone(const TreeAcceptParams &p, WalkShared &sh, int i,
   for (int c = sh.first_kid[v]; c >= 0; c = sh.next_sib[c]) {
     const int d = sh.tok[c];
     if (!have_r) {
-      if (tid == 0) sh.ok = (p.u_acc[qs + c] * qv[d] < pv[d]) ? 1 : 0;
+      if (tid == 0) sh.ok = (p.u_acc[qs + c] * qv[d] < xf(pv[d])) ? 1 : 0;
     } else {
       if (!sq_ready) {
         u64 part = 0;
@@ -465,7 +481,7 @@ __device__ int walk_node_alone(const TreeAcceptParams &p, WalkShared &sh, int i,
     if (!have_r) {
       u64 part = 0;
       for (int x = tid; x < V; x += kThreads) {
-        const u64 wx = weight_of(pv[x] - qv[x]);
+        const u64 wx = weight_of(xf(pv[x]) - qv[x]);
         R[x] = wx;
         part += wx;
       }
@@ -488,7 +504,7 @@ __device__ int walk_node_alone(const TreeAcceptParams &p, WalkShared &sh, int i,
     if (S == 0) {  // empty residual: back to the target row
       u64 part = 0;
       for (int x = tid; x < V; x += kThreads) {
-        const u64 wx = weight_of(pv[x]);
+        const u64 wx = weight_of(xf(pv[x]));
         R[x] = wx;
         part += wx;
       }
@@ -499,7 +515,7 @@ __device__ int walk_node_alone(const TreeAcceptParams &p, WalkShared &sh, int i,
   // rejections, so R is set)
   __syncthreads();  // R complete before the segment scan reads it
   if (S == 0) {
-    *y = walk_argmax(pv, V, sh);
+    *y = walk_argmax(pv, xf, V, sh);
   } else {
     u64 t = static_cast<u64>(floor(static_cast<double>(p.u_samp[i]) * static_cast<double>(S)));
     if (t > S - 1) t = S - 1;
@@ -575,7 +591,7 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeAcceptParams p,
     if (!p.greedy && j > 0) {
       const size_t at = (size_t)(qs + sh.par[j]) * V + sh.tok[j];
       sh.ua[j] = p.u_acc[qs + j];
-      sh.pd[j] = p.p[at];
+      sh.pd[j] = px_of(p, qs + sh.par[j])(p.p[at]);
       sh.qd[j] = p.q[at];
     }
   }
@@ -721,7 +737,7 @@ __global__ __launch_bounds__(kThreads) void tree_resid2_kernel(TreeAcceptParams 
   if (dd.mode != kDrawR2) return;
   const int V = p.V, x0 = c * kChunk, x1 = min(V, x0 + kChunk);
   U128 acc{0ull, 0ull};
-  chunk_for(p.p + (size_t)dd.row * V, p.q + (size_t)dd.row * V, x0, x1, w.vec != 0,
+  chunk_for(p.p + (size_t)dd.row * V, p.q + (size_t)dd.row * V, x0, x1, w.vec != 0, px_of(p, dd.row),
             [&](int, float pe, float qe) {
               const u64 r1 = dd.p1 ? weight_of(pe) : weight_of(pe - qe);
               acc = add128(acc, resid2_raw(r1, dd.sq, qe, dd.s1));
@@ -741,7 +757,7 @@ __global__ __launch_bounds__(kThreads) void tree_draw_sums_kernel(TreeAcceptPara
   float mv = -INFINITY;
   int mi = 0x7fffffff;
   const float *qr = dd.mode == kDrawP ? nullptr : p.q + (size_t)dd.row * V;
-  chunk_for(p.p + (size_t)dd.row * V, qr, x0, x1, w.vec != 0, [&](int x, float pe, float qe) {
+  chunk_for(p.p + (size_t)dd.row * V, qr, x0, x1, w.vec != 0, px_of(p, dd.row), [&](int x, float pe, float qe) {
     sres += f(pe, qe);
     sp += weight_of(pe);
     amax(mv, mi, pe, x);
@@ -802,6 +818,7 @@ __global__ __launch_bounds__(kThreads) void tree_pick_kernel(TreeAcceptParams p,
     // exact scan of that chunk: each thread a contiguous segment
     const int cx0 = s_hit * kChunk, cn = min(V, cx0 + kChunk) - cx0;
     const float *pr = p.p + (size_t)dd.row * V + cx0;
+    const PX xf = px_of(p, dd.row);
     const float *qr = (ur && dd.mode != kDrawP) ? p.q + (size_t)dd.row * V + cx0 : nullptr;
     const bool vec = w.vec != 0;
     int per = (cn + kThreads - 1) / kThreads;  // <= kPer
@@ -822,16 +839,16 @@ __global__ __launch_bounds__(kThreads) void tree_pick_kernel(TreeAcceptParams p,
 #pragma unroll
       for (int k = 0; k < kVec; ++k) {
         const bool in = k < n4;
-        wv[4 * k] = in ? f(pv[k].x, qv[k].x) : 0ull;
-        wv[4 * k + 1] = in ? f(pv[k].y, qv[k].y) : 0ull;
-        wv[4 * k + 2] = in ? f(pv[k].z, qv[k].z) : 0ull;
-        wv[4 * k + 3] = in ? f(pv[k].w, qv[k].w) : 0ull;
+        wv[4 * k] = in ? f(xf(pv[k].x), qv[k].x) : 0ull;
+        wv[4 * k + 1] = in ? f(xf(pv[k].y), qv[k].y) : 0ull;
+        wv[4 * k + 2] = in ? f(xf(pv[k].z), qv[k].z) : 0ull;
+        wv[4 * k + 3] = in ? f(xf(pv[k].w), qv[k].w) : 0ull;
       }
     } else {
 #pragma unroll
       for (int k = 0; k < kPer; ++k) {
         const int x = lo + k;
-        wv[k] = x < hi ? f(pr[x], qr ? qr[x] : 0.f) : 0ull;
+        wv[k] = x < hi ? f(xf(pr[x]), qr ? qr[x] : 0.f) : 0ull;
       }
     }
 #pragma unroll
