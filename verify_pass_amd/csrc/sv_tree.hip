@@ -12,7 +12,9 @@
 // token is drawn from R (or from trunc(fl32(p_v * 2^32)), the bonus row) by
 // the integer inverse CDF.  Every decision is exact integer arithmetic or one
 // fp32 compare, so any thread and workgroup layout decides the same.  Greedy
-// mode follows the child whose token is argmax p_v.
+// mode follows the child whose token is argmax p_v.  The target rows may be
+// logits with each row's (max, sum of exponentials): every entry read is then
+// turned into the probability the head's softmax finish would have written.
 //
 // The walk itself touches a few entries per node; what costs is the
 // vocabulary-long sums behind a rejection and the draw.  Those run on grids
