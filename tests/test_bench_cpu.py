@@ -43,3 +43,29 @@ def test_step_model_fit_recovers_constants():
     ftw, fk, fc = bench.fit_step_model(bs, ts, n)
     assert abs(ftw - tw) / tw < 1e-3 and abs(fc - c) / c < 1e-3
     assert abs(fk - k) / k < 5e-2
+
+
+def test_tree_shape_is_a_spine_with_one_extra_candidate_per_level():
+    from oracle import tree as OT
+    for depth in (1, 2, 5, 8, 16):
+        par = bench.tree_shape(depth)
+        assert len(par) == 2 * depth
+        dep = OT.depths(par)          # also checks topological order
+        assert dep.max() == depth
+        kids = [OT.children(par, v) for v in range(len(par))]
+        chain = [0] + [v for v in range(1, len(par)) if kids[v] or dep[v] == depth]
+        assert [int(dep[v]) for v in chain] == list(range(depth + 1))
+        for v in chain[:-1]:
+            # two candidates at every level but the last, the chain going on through the first
+            assert len(kids[v]) == (2 if dep[v] < depth - 1 else 1)
+            assert kids[v][0] == chain[int(dep[v]) + 1]
+            assert all(not kids[c] for c in kids[v][1:])
+    assert bench.tree_shape(8) == [-1, 0, 0, 1, 1, 3, 3, 5, 5, 7, 7, 9, 9, 11, 11, 13]
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], capture_output=True, text=True,
+                       cwd=bench.os.path.dirname(bench.os.path.abspath(bench.__file__)), timeout=300)
+    assert r.returncode == 2 and "one GPU" in r.stderr and not r.stdout
