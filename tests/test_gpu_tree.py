@@ -240,6 +240,29 @@ def test_tree_accept_bit_exact_spines(V):
     assert ends.get(0, 0) > 0 and ends.get(2, 0) > 0
 
 
+@pytest.mark.parametrize("V", [20003, 151936])
+def test_tree_accept_bit_exact_many_rejections(V):
+    """Candidates drawn uniformly over the vocabulary, so most tests reject:
+    nodes of four to seven children run the residual through further updates
+    (the workgroup-alone path: 128-bit products and shifts) before a later
+    candidate passes or the draw; bit for bit against the oracle."""
+    rng = np.random.default_rng(80 + V % 2)
+    parents = [spine_tree(3, 6), spine_tree(2, 4), [-1, 0, 0, 0, 0, 0, 0, 0], spine_tree(4)]
+    past_second = 0  # nodes settled by a third or later candidate, or after rejecting three or more
+    for _ in range(2):
+        got = _tree_accept_case(rng, None, V, False, draft_from_q=False, parents=parents)
+        for i, par in enumerate(parents):
+            path = got[3][i, :got[0][i] + 1].tolist()
+            for k, v in enumerate(path):
+                kids = OT.children(par, v)
+                if k + 1 < len(path):
+                    past_second += kids.index(path[k + 1]) >= 2
+                else:
+                    past_second += len(kids) >= 3
+    say(f"tree accept, uniform drafts V={V}: {past_second} nodes settled past their second candidate")
+    assert past_second >= 3
+
+
 @pytest.mark.parametrize("vocab", [20011, 151936])
 @pytest.mark.parametrize("greedy", [False, True])
 def test_tree_accept_from_logits(vocab, greedy):
