@@ -240,6 +240,19 @@ def test_tree_accept_bit_exact_spines(V):
     assert ends.get(0, 0) > 0 and ends.get(2, 0) > 0
 
 
+def test_tree_accept_bit_exact_sixteen_trees():
+    """Sixteen trees at V = 151936 (304 chunk workgroups per grid, more than
+    one round of CUs): spines, a bushy spine and a small binary tree, in both
+    modes, bit for bit against the oracle."""
+    V, B = 151936, 16
+    rng = np.random.default_rng(106)
+    shapes = [spine_tree(8), spine_tree(4, 4), spine_tree(3), [-1, 0, 0, 1, 1, 2, 2]]
+    parents = [shapes[k % len(shapes)] for k in range(B)]
+    for greedy in (False, True):
+        got = _tree_accept_case(rng, None, V, greedy, mix=0.5, parents=parents)
+        say(f"tree accept B={B} V={V} greedy={greedy}: accepted {got[0].tolist()}")
+
+
 @pytest.mark.parametrize("V", [20003, 151936])
 def test_tree_accept_bit_exact_many_rejections(V):
     """Candidates drawn uniformly over the vocabulary, so most tests reject:
