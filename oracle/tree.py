@@ -54,7 +54,7 @@ import numpy as np
 
 from .accept import draw_integer_cdf, integer_weights, passes
 from .formats import bf16_to_f64, matrix_f64, round_bf16
-from .verify import LayerOut, attend, rms_norm, rope, silu
+from .verify import LayerOut, attend, dequantize_int8, quantize_int8_row, rms_norm, rope, silu
 
 __all__ = ["depths", "ancestor_masks", "children", "tree_decoder_layer", "tree_accept",
            "compact_rows"]
@@ -92,12 +92,15 @@ def children(parent, v: int) -> list:
 
 
 def tree_decoder_layer(shape, w, x, parents, ctx, kcache, vcache, *, eps=1e-6,
-                       theta=10000.0) -> LayerOut:
+                       theta=10000.0, kscale=None, vscale=None) -> LayerOut:
     """One decoder layer over the stacked tree nodes of every sequence
     (sequence i owns stacked rows q_start[i] .. q_start[i] + n_i - 1, node j of
     its tree at row q_start[i] + j).  Inputs as verify.decoder_layer; the
     appended keys and values are returned in node order (cache rows
-    ctx_i + j), bf16-rounded as the cache stores them."""
+    ctx_i + j), bf16-rounded as the cache stores them.  kscale / vscale
+    given: int8 caches, read and appended as verify.decoder_layer does
+    (a cached vector is code * scale; an appended one is rounded to bf16,
+    then stored as its int8 code and scale)."""
     W = {n: (m if isinstance(m, np.ndarray) else matrix_f64(m)) for n, m in w.items()}
     x = np.asarray(x)
     x = bf16_to_f64(x) if x.dtype == np.uint16 else x.astype(np.float64)
@@ -109,6 +112,13 @@ def tree_decoder_layer(shape, w, x, parents, ctx, kcache, vcache, *, eps=1e-6,
     k = (h @ W["wk"].T).reshape(T, hk, hd)
     v = (h @ W["wv"].T).reshape(T, hk, hd)
     o = np.zeros((T, hq, hd))
+    int8 = kscale is not None
+    if int8:
+        def store(a):
+            codes, sc = quantize_int8_row(round_bf16(a))
+            return dequantize_int8(codes, sc)
+    else:
+        store = round_bf16
     k_new, v_new = {}, {}
     r0 = 0
     for i, par in enumerate(parents):
@@ -118,13 +128,19 @@ def tree_decoder_layer(shape, w, x, parents, ctx, kcache, vcache, *, eps=1e-6,
         anc = ancestor_masks(par)
         kk = np.empty((hk, c + n, hd))
         vv = np.empty((hk, c + n, hd))
-        kk[:, :c] = bf16_to_f64(kcache[i, :, :c])
-        vv[:, :c] = bf16_to_f64(vcache[i, :, :c])
+        if int8:
+            kk[:, :c] = np.asarray(kcache[i, :, :c], np.float64) * \
+                np.asarray(kscale[i, :, :c], np.float32).astype(np.float64)[..., None]
+            vv[:, :c] = np.asarray(vcache[i, :, :c], np.float64) * \
+                np.asarray(vscale[i, :, :c], np.float32).astype(np.float64)[..., None]
+        else:
+            kk[:, :c] = bf16_to_f64(kcache[i, :, :c])
+            vv[:, :c] = bf16_to_f64(vcache[i, :, :c])
         for j in range(n):
             pos = c + int(dep[j])
             for g in range(hk):
-                kk[g, c + j] = round_bf16(rope(k[r0 + j, g], pos, theta))
-                vv[g, c + j] = round_bf16(v[r0 + j, g])
+                kk[g, c + j] = store(rope(k[r0 + j, g], pos, theta))
+                vv[g, c + j] = store(v[r0 + j, g])
         k_new[i], v_new[i] = kk[:, c:].copy(), vv[:, c:].copy()
         for j in range(n):
             pos = c + int(dep[j])

@@ -10,7 +10,7 @@ import torch
 
 from gpu_helpers import TOL, GpuDecoder, GpuHead, OF, OV, dev_bf16_to_f64, rel_rows, say, sv, tg
 from oracle import tree as OT
-from workloads import Shape, custom_workload, hidden_states, kv_cache, layer_weights
+from workloads import Shape, custom_workload, hidden_states, kv_cache, kv_cache_int8, layer_weights
 
 pytestmark = pytest.mark.gpu
 GRID = 1 << 24
@@ -83,6 +83,52 @@ def test_tree_verify_parity(name, shape, wtype, sizes, ctx):
         vg = OF.bf16_to_f64(batch.v_logical(i)[:, c:c + n])
         assert rel_rows(kg.reshape(-1, hd), ref.k_new[i].reshape(-1, hd)) < TOL[wtype]
         assert rel_rows(vg.reshape(-1, hd), ref.v_new[i].reshape(-1, hd)) < TOL[wtype]
+
+
+INT8_CASES = [
+    # (name, shape, tree sizes, ctx): up to 16 query rows per KV head (the
+    # key-split kernel) and up to 96 (the query-tiled kernel)
+    ("gqa4-rows16", Shape(512, 8, 2, 128, 1024, 3000), [4, 3, 1], [300, 17, 0]),
+    ("gqa4-rows96", Shape(512, 8, 2, 128, 1024, 3000), [24, 9, 2], [700, 33, 257]),
+]
+
+
+@pytest.mark.parametrize("name,shape,sizes,ctx", INT8_CASES, ids=[c[0] for c in INT8_CASES])
+def test_tree_verify_over_int8_caches(name, shape, sizes, ctx):
+    """Tree verify (ancestor masks, positions ctx + depth) over int8 caches:
+    layer outputs and the appended keys and values (code times scale)
+    against the oracle's int8 form."""
+    rng = np.random.default_rng(len(name))
+    parents = [random_tree(rng, n) for n in sizes]
+    gamma = [n - 1 for n in sizes]
+    wl = custom_workload(shape, "bf16", gamma, ctx, seed=77)
+    W = layer_weights(shape, "bf16", wl.seed)
+    mats = {k: tg.upload_matrix(v, packed=True) for k, v in W.items()}
+    L = tg.decoder_struct(shape, "bf16", mats, packed=True)
+    k8, ks, v8, vs = kv_cache_int8(shape, wl.ctx, wl.cap, wl.seed)
+    batch = tg.DeviceBatch(gamma, ctx, wl.cap, kcache=k8, vcache=v8, kscale=ks, vscale=vs,
+                           tree_parents=parents)
+    bs = batch.struct()
+    n = sv.sv_verify_layer_workspace_bytes(L, bs)
+    ws = tg.workspace(n)
+    xh = hidden_states(wl.T, shape.d, wl.seed)
+    y = torch.empty_like(tg.to_dev(xh))
+    assert sv.sv_verify_layer(L, bs, tg.to_dev(xh), y, 0, ws, n, tg.stream_handle()) == sv.SV_OK
+    torch.cuda.synchronize()
+    assert batch.err.item() == 0
+    ref = OT.tree_decoder_layer(shape, W, xh, parents, ctx, k8, v8, kscale=ks, vscale=vs)
+    err = rel_rows(dev_bf16_to_f64(y), ref.y)
+    say(f"tree verify {name} over int8 caches: y rel err {err:.2e}")
+    assert err < TOL["bf16"]
+    hd = shape.hd
+    for i, c in enumerate(ctx):
+        m = sizes[i]
+        kd = batch.k_logical(i)[:, c:c + m].astype(np.float64) * \
+            batch.ks[i].cpu().numpy()[:, c:c + m].astype(np.float64)[..., None]
+        vd = batch.v_logical(i)[:, c:c + m].astype(np.float64) * \
+            batch.vs[i].cpu().numpy()[:, c:c + m].astype(np.float64)[..., None]
+        assert rel_rows(kd.reshape(-1, hd), ref.k_new[i].reshape(-1, hd)) < TOL["bf16"]
+        assert rel_rows(vd.reshape(-1, hd), ref.v_new[i].reshape(-1, hd)) < TOL["bf16"]
 
 
 def test_chain_beyond_64_rows_per_kv_head():

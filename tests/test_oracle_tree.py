@@ -1,9 +1,10 @@
 """Token-tree oracle pins.
 
 1. Structure: depths and ancestor masks of a hand-drawn tree.
-2. Verify: a chain tree is exactly the linear verify pass; every node of a
-   branching tree equals the linear pass over its own root path (a node sees
-   only its ancestors), so siblings do not affect each other.
+2. Verify: a chain tree is exactly the linear verify pass (also over int8
+   caches); every node of a branching tree equals the linear pass over its
+   own root path (a node sees only its ancestors, also over int8 caches), so
+   siblings do not affect each other.
 3. Accept: on a chain the tree rule is the linear rule bit for bit (both
    modes); with several children drawn i.i.d. from the parent's draft
    distribution the first emitted token is distributed as the target row,
@@ -16,7 +17,7 @@ import pytest
 from oracle import accept as OA
 from oracle import tree as OT
 from oracle import verify as OV
-from workloads import Shape, hidden_states, kv_cache, layer_weights
+from workloads import Shape, hidden_states, kv_cache, kv_cache_int8, layer_weights
 
 SMALL = Shape(d=128, n_q=4, n_kv=2, hd=32, ffn=192, vocab=300)
 GRID = 1 << 24
@@ -58,6 +59,40 @@ def test_chain_tree_is_the_linear_pass():
     for i in range(len(gamma)):
         np.testing.assert_array_equal(tre.k_new[i], lin.k_new[i])
         np.testing.assert_array_equal(tre.v_new[i], lin.v_new[i])
+
+
+def test_chain_tree_over_int8_caches_is_the_linear_pass():
+    gamma, ctx = [3, 0, 5], [17, 4, 40]
+    parents = [[-1] + list(range(g)) for g in gamma]
+    W, _, _, x = _layer_inputs(parents, ctx, 4)
+    cap = (max(c + g + 1 for c, g in zip(ctx, gamma)) + 31) // 32 * 32
+    k8, ks, v8, vs = kv_cache_int8(SMALL, np.asarray(ctx), cap, 4)
+    lin = OV.decoder_layer(SMALL, W, x, gamma, ctx, k8, v8, kscale=ks, vscale=vs)
+    tre = OT.tree_decoder_layer(SMALL, W, x, parents, ctx, k8, v8, kscale=ks, vscale=vs)
+    np.testing.assert_array_equal(tre.y, lin.y)
+    for i in range(len(gamma)):
+        np.testing.assert_array_equal(tre.k_new[i], lin.k_new[i])
+        np.testing.assert_array_equal(tre.v_new[i], lin.v_new[i])
+    # and the int8 caches change the result
+    plain = OT.tree_decoder_layer(SMALL, W, x, parents, ctx, *_layer_inputs(parents, ctx, 4)[1:3])
+    assert np.abs(plain.y - tre.y).max() > 0
+
+
+def test_every_node_over_int8_caches_equals_the_linear_pass_over_its_root_path():
+    par = [-1, 0, 0, 1, 1, 2, 4, 6, 0]
+    ctx = [23]
+    W, _, _, x = _layer_inputs([par], ctx, 6)
+    k8, ks, v8, vs = kv_cache_int8(SMALL, np.asarray(ctx), 64, 6)
+    tre = OT.tree_decoder_layer(SMALL, W, x, [par], ctx, k8, v8, kscale=ks, vscale=vs)
+    for j in range(len(par)):
+        path, v = [], j
+        while v >= 0:
+            path.append(v)
+            v = par[v] if v > 0 else -1
+        path = path[::-1]
+        lin = OV.decoder_layer(SMALL, W, x[path], [len(path) - 1], ctx, k8, v8, kscale=ks, vscale=vs)
+        np.testing.assert_allclose(tre.y[j], lin.y[-1], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(tre.k_new[0][:, j], lin.k_new[0][:, -1], rtol=0, atol=0)
 
 
 def test_every_node_equals_the_linear_pass_over_its_root_path():
