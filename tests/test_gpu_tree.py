@@ -131,6 +131,45 @@ def test_tree_verify_over_int8_caches(name, shape, sizes, ctx):
         assert rel_rows(vd.reshape(-1, hd), ref.v_new[i].reshape(-1, hd)) < TOL["bf16"]
 
 
+def test_tree_verify_at_the_size_limits():
+    """A 64-node tree and a 64-node chain (the ancestor masks' limit) at a
+    GQA group of 2: 128 query rows per KV head, the attention kernels'
+    limit; one tree starts from an empty cache."""
+    shape = Shape(256, 4, 2, 64, 512, 1000)
+    rng = np.random.default_rng(111)
+    parents = [random_tree(rng, 64), [-1] + list(range(63))]
+    ctx = [100, 0]
+    wl, batch, y, ref = _tree_layer(shape, "bf16", parents, ctx, seed=112, packed=True)
+    err = rel_rows(dev_bf16_to_f64(y), ref.y)
+    say(f"tree verify at 64 nodes, 128 rows per KV head: y rel err {err:.2e}")
+    assert err < TOL["bf16"]
+
+
+@pytest.mark.parametrize("greedy", [False, True])
+def test_tree_accept_full_depth_chain(greedy):
+    """A 64-node chain whose every draft passes (drafts from q = p, or the
+    argmax in greedy mode): accepted depth 63, every path slot filled, the
+    bonus token drawn at the last node; bit for bit against the oracle."""
+    rng = np.random.default_rng(113 + greedy)
+    V = 5003
+    par = [-1] + list(range(63))
+    p = _rows(rng, 64, V)
+    tokens = np.zeros(64, np.int64)
+    for j in range(1, 64):
+        row = p[j - 1].astype(np.float64)
+        tokens[j] = int(np.argmax(row)) if greedy else int(rng.choice(V, p=row / row.sum()))
+    ua = (rng.integers(0, GRID, size=64) / GRID).astype(np.float32)
+    us = np.array([0.61], np.float32)
+    got = _run_tree_accept([par], tokens, p, p.copy(), ua, us, [9], greedy)
+    want = OT.tree_accept([par], tokens, p, p.copy(), ua, us, [9], greedy=greedy)
+    assert int(want[0][0]) == 63 and len(want[3][0]) == 64
+    np.testing.assert_array_equal(got[0], want[0])
+    np.testing.assert_array_equal(got[1], want[1])
+    np.testing.assert_array_equal(got[2], want[2])
+    np.testing.assert_array_equal(got[3][0], want[3][0])
+    assert got[4] == 0
+
+
 def test_chain_beyond_64_rows_per_kv_head():
     """Linear drafts with 96 query rows per KV head (the eight-wave kernel)."""
     shape = Shape(512, 8, 2, 128, 1024, 3000)
