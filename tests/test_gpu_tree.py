@@ -338,6 +338,17 @@ def test_tree_accept_bit_exact_sixteen_trees():
         say(f"tree accept B={B} V={V} greedy={greedy}: accepted {got[0].tolist()}")
 
 
+@pytest.mark.parametrize("greedy", [False, True])
+def test_tree_accept_bit_exact_256_trees(greedy):
+    """The largest batch (256 trees of 1 to 8 nodes, small vocabulary): every
+    sequence's row range comes from the launch's start table at its full
+    size, bit for bit against the oracle."""
+    rng = np.random.default_rng(120 + greedy)
+    sizes = [int(v) for v in rng.integers(1, 9, size=256)]
+    got = _tree_accept_case(rng, sizes, 301, greedy, mix=0.6)
+    say(f"tree accept B=256 greedy={greedy}: mean accepted depth {got[0].mean():.2f}")
+
+
 @pytest.mark.parametrize("V", [20003, 151936])
 def test_tree_accept_bit_exact_many_rejections(V):
     """Candidates drawn uniformly over the vocabulary, so most tests reject:
