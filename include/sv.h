@@ -372,6 +372,18 @@ sv_status sv_tree_commit_kv(int32_t B, int32_t n_kv_heads, int32_t head_dim, int
                             const int32_t *kv_len, const int32_t *accepted, const int32_t *path,
                             void *const *k_cache, void *const *v_cache, void *stream);
 
+/* The same moves for int8 caches (sv_batch with SV_KV_INT8: codes in the
+ * bf16 layouts, one byte per value; k_scale / v_scale: per sequence, fp32
+ * [n_kv][kv_cap], one scale per cached vector): each moved vector's codes
+ * and scale.  Defined by the same passages as sv_tree_commit_kv, with the
+ * caches of "Why Static Batching Wastes an RX 9070 XT Agent Swarm and
+ * Continuous Batching Wins It Back", section "The catch is prefill, and it
+ * points back at admission" (quantised KV). */
+sv_status sv_tree_commit_kv_int8(int32_t B, int32_t n_kv_heads, int32_t head_dim, int32_t kv_cap,
+                                 const int32_t *kv_len, const int32_t *accepted, const int32_t *path,
+                                 void *const *k_cache, void *const *v_cache, void *const *k_scale,
+                                 void *const *v_scale, void *stream);
+
 /* Iteration-level batching (host only).
  *
  * Defined by: "Why Static Batching Wastes an RX 9070 XT Agent Swarm and

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _declared():
     txt = open(os.path.join(ROOT, "include", "sv.h")).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"\b(sv_[a-z_]+)\s*\(", txt)))
+    return sorted(set(re.findall(r"\b(sv_[a-z0-9_]+)\s*\(", txt)))
 
 
 def test_exports_every_declared_symbol():

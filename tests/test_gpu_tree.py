@@ -436,6 +436,33 @@ def test_tree_commit_moves_accepted_rows():
         np.testing.assert_array_equal(batch.v_logical(i), OT.compact_rows(vc[i], int(ctx[i]), paths[i]))
 
 
+def test_tree_commit_moves_int8_rows_and_scales():
+    """The commit's moves on int8 caches: each accepted node's key and value
+    codes and their scales move to ctx + depth (hd 64 and 128)."""
+    for shape in (Shape(512, 8, 2, 128, 1024, 3000), Shape(256, 4, 2, 64, 512, 1000)):
+        B, cap = 3, 96
+        ctx = np.array([10, 40, 3])
+        acc = np.array([3, 0, 2])
+        paths = [[0, 2, 5, 9], [0], [0, 1, 4]]
+        k8, ks, v8, vs = kv_cache_int8(shape, ctx + 20, cap, 78)
+        batch = tg.DeviceBatch([0] * B, list(ctx), cap, kcache=k8, vcache=v8, kscale=ks, vscale=vs)
+        kv_after = torch.tensor(ctx + acc + 1, dtype=torch.int32, device="cuda")
+        pm = np.full((B, 64), -1, np.int32)
+        for i, pth in enumerate(paths):
+            pm[i, :len(pth)] = pth
+        assert sv.sv_tree_commit_kv_int8(B, shape.n_kv, shape.hd, cap, kv_after,
+                                         torch.tensor(acc, dtype=torch.int32, device="cuda"),
+                                         torch.tensor(pm, device="cuda"), batch.kptr, batch.vptr, batch.ksptr,
+                                         batch.vsptr, tg.stream_handle()) == sv.SV_OK
+        torch.cuda.synchronize()
+        for i in range(B):
+            c = int(ctx[i])
+            np.testing.assert_array_equal(batch.k_logical(i), OT.compact_rows(k8[i], c, paths[i]))
+            np.testing.assert_array_equal(batch.v_logical(i), OT.compact_rows(v8[i], c, paths[i]))
+            np.testing.assert_array_equal(batch.ks[i].cpu().numpy(), OT.compact_rows(ks[i][..., None], c, paths[i])[..., 0])
+            np.testing.assert_array_equal(batch.vs[i].cpu().numpy(), OT.compact_rows(vs[i][..., None], c, paths[i])[..., 0])
+
+
 def test_tree_round_end_to_end():
     """Tree verify of a lone sequence (a 20-node tree, 80 query rows per KV
     head), the LM head over its nodes, tree acceptance on the GPU's

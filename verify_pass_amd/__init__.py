@@ -99,6 +99,8 @@ _SIGNATURES = [
      [C.c_int32, C.c_int32, C.c_int32, C.POINTER(C.c_int32)] + [C.c_void_p] * 14),
     ("sv_tree_commit_kv", C.c_int32,
      [C.c_int32, C.c_int32, C.c_int32, C.c_int32] + [C.c_void_p] * 6),
+    ("sv_tree_commit_kv_int8", C.c_int32,
+     [C.c_int32, C.c_int32, C.c_int32, C.c_int32] + [C.c_void_p] * 8),
     ("sv_accept_position_counts", C.c_int32,
      [C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]),
     ("sv_packed_matrix_bytes", C.c_int32,
@@ -225,6 +227,13 @@ def sv_tree_commit_kv(B, n_kv_heads, head_dim, kv_cap, kv_len, accepted, path, k
                       stream) -> int:
     return _lib.sv_tree_commit_kv(B, n_kv_heads, head_dim, kv_cap, _ptr(kv_len), _ptr(accepted),
                                   _ptr(path), _ptr(k_cache), _ptr(v_cache), _ptr(stream))
+
+
+def sv_tree_commit_kv_int8(B, n_kv_heads, head_dim, kv_cap, kv_len, accepted, path, k_cache, v_cache,
+                           k_scale, v_scale, stream) -> int:
+    return _lib.sv_tree_commit_kv_int8(B, n_kv_heads, head_dim, kv_cap, _ptr(kv_len), _ptr(accepted),
+                                       _ptr(path), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                                       _ptr(v_scale), _ptr(stream))
 
 
 def sv_accept_position_counts(B, n_pos, gamma, accepted, counts, stream) -> int:

@@ -1047,13 +1047,17 @@ extern "C" sv_status sv_accept_tree(int32_t B, int32_t V, int32_t mode, const in
   return launch_tree_accept(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
-extern "C" sv_status sv_tree_commit_kv(int32_t B, int32_t n_kv_heads, int32_t head_dim, int32_t kv_cap,
-                                       const int32_t *kv_len, const int32_t *accepted, const int32_t *path,
-                                       void *const *k_cache, void *const *v_cache, void *stream) {
+namespace {
+sv_status tree_commit(int32_t B, int32_t n_kv_heads, int32_t head_dim, int32_t kv_cap, const int32_t *kv_len,
+                      const int32_t *accepted, const int32_t *path, void *const *k_cache, void *const *v_cache,
+                      void *const *k_scale, void *const *v_scale, void *stream) {
   if (B < 0 || n_kv_heads <= 0 || head_dim <= 0 || kv_cap <= 0 || kv_cap % 32) return SV_ERR_INVALID_ARG;
   if (B == 0) return SV_OK;
   if (!kv_len || !accepted || !path || !k_cache || !v_cache) return SV_ERR_INVALID_ARG;
   TreeCommitParams c;
+  c.kv8 = k_scale != nullptr;
+  c.ksc = k_scale;
+  c.vsc = v_scale;
   c.B = B;
   c.hkv = n_kv_heads;
   c.hd = head_dim;
@@ -1065,6 +1069,23 @@ extern "C" sv_status sv_tree_commit_kv(int32_t B, int32_t n_kv_heads, int32_t he
   c.vc = v_cache;
   (void)hipGetLastError();
   return launch_tree_commit(c, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+}  // namespace
+
+extern "C" sv_status sv_tree_commit_kv(int32_t B, int32_t n_kv_heads, int32_t head_dim, int32_t kv_cap,
+                                       const int32_t *kv_len, const int32_t *accepted, const int32_t *path,
+                                       void *const *k_cache, void *const *v_cache, void *stream) {
+  return tree_commit(B, n_kv_heads, head_dim, kv_cap, kv_len, accepted, path, k_cache, v_cache, nullptr, nullptr,
+                     stream);
+}
+
+extern "C" sv_status sv_tree_commit_kv_int8(int32_t B, int32_t n_kv_heads, int32_t head_dim, int32_t kv_cap,
+                                            const int32_t *kv_len, const int32_t *accepted, const int32_t *path,
+                                            void *const *k_cache, void *const *v_cache, void *const *k_scale,
+                                            void *const *v_scale, void *stream) {
+  if (B > 0 && (!k_scale || !v_scale)) return SV_ERR_INVALID_ARG;
+  return tree_commit(B, n_kv_heads, head_dim, kv_cap, kv_len, accepted, path, k_cache, v_cache, k_scale, v_scale,
+                     stream);
 }
 
 extern "C" sv_status sv_accept_position_counts(int32_t B, int32_t n_pos, const int32_t *gamma,

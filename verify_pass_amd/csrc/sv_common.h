@@ -343,6 +343,9 @@ struct TreeCommitParams {
   const int *kv_len, *accepted, *path;
   void *const *kc;
   void *const *vc;
+  int kv8;              // int8 caches: one byte per value, and the scales below
+  void *const *ksc;     // [B] fp32 [hkv][kv_cap] scale of each cached key (int8 caches)
+  void *const *vsc;     // [B] the same for the values
 };
 
 hipError_t launch_tree_accept(const TreeAcceptParams &p, hipStream_t s);

@@ -877,15 +877,19 @@ __global__ __launch_bounds__(kThreads) void tree_pick_kernel(TreeAcceptParams p,
   if (tid == 0) p.next_token[i] = result;
 }
 
-// Row moves of the commit, one workgroup per (sequence, KV head).
-__global__ __launch_bounds__(kThreads) void tree_commit_kernel(TreeCommitParams p) {
-  const int i = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+// Row moves of the commit, one workgroup per (sequence, KV head); T is the
+// cache element (bf16 bits, or int8 codes whose per-vector scales move too).
+template <class T>
+__device__ __forceinline__ void commit_rows(const TreeCommitParams &p, int i, int h) {
+  const int tid = threadIdx.x;
   const int a = p.accepted[i];
   if (a <= 0) return;
   const int ctx = p.kv_len[i] - a - 1;
   const int *path = p.path + (size_t)i * kMaxTreeNodes;
-  uint16_t *kc = static_cast<uint16_t *>(p.kc[i]) + (size_t)h * p.kv_cap * p.hd;
-  uint16_t *vc = static_cast<uint16_t *>(p.vc[i]) + (size_t)h * p.hd * p.kv_cap;
+  T *kc = static_cast<T *>(p.kc[i]) + (size_t)h * p.kv_cap * p.hd;
+  T *vc = static_cast<T *>(p.vc[i]) + (size_t)h * p.hd * p.kv_cap;
+  float *ks = p.kv8 ? static_cast<float *>(p.ksc[i]) + (size_t)h * p.kv_cap : nullptr;
+  float *vs = p.kv8 ? static_cast<float *>(p.vsc[i]) + (size_t)h * p.kv_cap : nullptr;
   for (int k = 1; k <= a && k < kMaxTreeNodes; ++k) {
     const int node = path[k];
     const int src = ctx + node, dst = ctx + k;
@@ -896,9 +900,20 @@ __global__ __launch_bounds__(kThreads) void tree_commit_kernel(TreeCommitParams 
         // values in 32-position blocks: (position, column) at (pos / 32 * hd + column) * 32 + pos % 32
         vc[((size_t)(dst >> 5) * p.hd + c) * 32 + (dst & 31)] = vc[((size_t)(src >> 5) * p.hd + c) * 32 + (src & 31)];
       }
+      if (ks && tid == 0) {
+        ks[dst] = ks[src];
+        vs[dst] = vs[src];
+      }
     }
     __syncthreads();  // depth k lands before depth k + 1 reads
   }
+}
+
+__global__ __launch_bounds__(kThreads) void tree_commit_kernel(TreeCommitParams p) {
+  if (p.kv8)
+    commit_rows<int8_t>(p, blockIdx.x, blockIdx.y);
+  else
+    commit_rows<uint16_t>(p, blockIdx.x, blockIdx.y);
 }
 
 }  // namespace
