@@ -65,6 +65,8 @@ CASES = [
     ("gqa5-rows120", Shape(640, 10, 2, 128, 1280, 2000), "bf16", [24, 2], [300, 1100]),
     ("gqa4-keysplit-rows16", Shape(512, 8, 2, 128, 1024, 3000), "bf16", [4, 3, 2], [100, 513, 5]),
     ("hd64-gqa2-int4", Shape(512, 8, 4, 64, 1024, 3000), "int4", [17, 6], [64, 2000]),
+    # fp32 weights (the small model's precision: hi + lo bf16 halves), no GQA
+    ("tiny-f32", Shape(256, 4, 4, 64, 1024, 1024), "f32", [9, 5, 1], [128, 3, 40]),
 ]
 
 
