@@ -18,7 +18,7 @@
 //
 // The walk itself touches a few entries per node; what costs is the
 // vocabulary-long sums behind a rejection and the draw.  Those run on grids
-// of vocabulary chunks (8192 entries, one workgroup each).  Stochastic mode,
+// of vocabulary chunks (4096 entries, one workgroup each).  Stochastic mode,
 // six launches:
 //   walk 1 (sequences): one workgroup per tree gathers every node's own test
 //          inputs once and walks down in LDS.  It ends on a draw from p_v (a
@@ -55,7 +55,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kPer = 32;                 // chunk entries per thread
+constexpr int kPer = 16;                 // chunk entries per thread
 constexpr int kChunk = kThreads * kPer;  // vocabulary chunk of one workgroup
 constexpr int kVec = kPer / 4;           // float4 loads per thread and row over a chunk
 constexpr float kTwo32 = 4294967296.0f;
